@@ -1,0 +1,275 @@
+"""Seeded synthetic inputs for the sparse MoE FFN layer.
+
+This module is shared by the tests, the bench and the CPU oracle's callers. It draws
+inputs only; it evaluates no part of the layer.  Two input-construction steps look at
+router logits, and both are documented where they happen:
+
+* gap enforcement: a token row is redrawn until the k+1 largest fp64 router logits are
+  separated by more than ``gap`` (so that fp32-vs-fp64 accumulation can never change
+  which experts a row selects);
+* the capped-Zipf router bias of the prefill workload is calibrated on pure noise so
+  that the expected share of rows selecting the expert of rank r is
+  ``min(1, c * r**-s)``.
+
+Neither step selects experts for any evaluated token nor computes a routing weight.
+
+Every tensor is drawn from its own counter-keyed stream
+``numpy.random.Generator(PCG64([seed, tensor_code, expert]))`` so that one expert of a
+large layer can be regenerated on its own.  bf16 tensors are produced by rounding the
+fp32 draw to nearest-even and are stored as their uint16 bit patterns.
+
+Shapes follow the row-major ``[out, in]`` convention of the Hugging Face layouts shown
+in "Phase 19: MoE - gpt-oss-20b" (measured tensor layout) and the merged 3-D expert
+tensors of "Llama Forward Pass" (Mixture of Experts, expert weight formats):
+``w_router[E,d]``, ``w_gate/w_up[E,ff,d]``, ``w_down[E,d,ff]``, ``w_gate_up[E,2ff,d]``
+(rows interleaved gate, up, gate, up, ...), shared ``ws_gate/ws_up[ffs,d]``,
+``ws_down[d,ffs]``, ``ws_gate_inp[d]``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import functools
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+# Stream codes: one independent stream per (tensor, expert).
+_CODE = {
+    "w_router": 1, "b_router": 2, "w_gate": 3, "w_up": 4, "w_down": 5,
+    "w_gate_up": 6, "b_gate_up": 7, "b_down": 8, "ws_gate": 9, "ws_up": 10,
+    "ws_down": 11, "ws_gate_inp": 12, "x": 20, "x_redraw": 21,
+}
+
+ROUTE_SOFTMAX_TOPK_RENORM = "softmax_topk_renorm"
+ROUTE_TOPK_SOFTMAX = "topk_softmax"
+ACT_SWIGLU = "swiglu"
+ACT_SWIGLU_OAI = "swiglu_oai"
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerSpec:
+    name: str
+    d: int
+    n_expert: int
+    ff: int
+    k: int
+    shared_ff: int
+    dtype: str                      # "f32" or "bf16": dtype of x, every weight and y
+    route: str = ROUTE_SOFTMAX_TOPK_RENORM
+    act: str = ACT_SWIGLU
+    route_scale: float = 1.0
+    oai_alpha: float = 1.702
+    oai_limit: float = 7.0
+    router_std: float = 0.1
+    weight_std: float = 0.02
+    router_bias: str = "none"       # "none" | "normal" | "zipf"
+    router_bias_std: float = 0.1
+    zipf_s: float = 1.1
+    bias_std: float = 0.02          # expert biases of the clamped variant
+
+
+# The workloads.  Distributions: x ~ N(0,1); expert and shared weights ~ N(0, weight_std);
+# router ~ N(0, router_std); router_std = 1/sqrt(d) makes logits ~ N(0,1).
+SPECS = {
+    "tiny_f32": LayerSpec("tiny_f32", d=256, n_expert=8, ff=512, k=2, shared_ff=0,
+                          dtype="f32", router_std=0.1),
+    "qwen": LayerSpec("qwen", d=2048, n_expert=256, ff=512, k=8, shared_ff=512,
+                      dtype="bf16", router_std=1.0 / math.sqrt(2048)),
+    "qwen_zipf": LayerSpec("qwen_zipf", d=2048, n_expert=256, ff=512, k=8, shared_ff=512,
+                           dtype="bf16", router_std=1.0 / math.sqrt(2048), router_bias="zipf"),
+    "gptoss": LayerSpec("gptoss", d=2880, n_expert=32, ff=2880, k=4, shared_ff=0,
+                        dtype="bf16", route=ROUTE_TOPK_SOFTMAX, act=ACT_SWIGLU_OAI,
+                        router_std=1.0 / math.sqrt(2880), router_bias="normal",
+                        router_bias_std=0.1),
+    "mixtral": LayerSpec("mixtral", d=4096, n_expert=8, ff=14336, k=2, shared_ff=0,
+                         dtype="bf16", router_std=1.0 / math.sqrt(4096)),
+}
+
+
+def spec(name: str, **overrides) -> LayerSpec:
+    """A named workload, optionally with fields replaced (smaller d, other k, ...)."""
+    return dataclasses.replace(SPECS[name], **overrides)
+
+
+# ----------------------------------------------------------------------------- bf16 bits
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to the nearest bf16 (ties to even); returns uint16 bit patterns."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    rounded = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def storage_to_f32(a: np.ndarray) -> np.ndarray:
+    """fp32 view of a stored tensor (bf16 bits are widened exactly)."""
+    return bf16_bits_to_f32(a) if a.dtype == np.uint16 else np.asarray(a, dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------- draws
+
+def _rng(*key: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64([int(v) for v in key]))
+
+
+def _draw(seed: int, code: str, idx: int, shape, std: float) -> np.ndarray:
+    a = _rng(seed, _CODE[code], idx).standard_normal(shape, dtype=np.float32)
+    a *= np.float32(std)
+    return a
+
+
+def _store(a: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(a) if dtype == "bf16" else a
+
+
+def _stacked(seed: int, code: str, E: int, shape, std: float, dtype: str,
+             experts=None) -> np.ndarray:
+    """[E, *shape] tensor, expert e from stream (seed, code, e); others left zero."""
+    out = np.zeros((E,) + tuple(shape), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    todo = range(E) if experts is None else sorted(set(int(e) for e in experts))
+
+    def one(e):
+        out[e] = _store(_draw(seed, code, e, shape, std), dtype)
+
+    workers = min(len(todo), max(1, min(16, os.cpu_count() or 1)))
+    if workers > 1 and out.nbytes > (8 << 20):
+        with ThreadPoolExecutor(workers) as pool:
+            list(pool.map(one, todo))
+    else:
+        for e in todo:
+            one(e)
+    return out
+
+
+def make_layer(sp: LayerSpec, seed: int = 0, experts=None) -> dict:
+    """All parameters of one layer, in storage form (uint16 bf16 bits or float32).
+
+    ``experts`` restricts which routed experts are drawn (the others stay zero); the
+    router, biases and shared expert are always drawn.  The returned dict also carries
+    the layer's scalar fields so that it fully describes the layer.
+    """
+    E, d, ff, ffs, dt = sp.n_expert, sp.d, sp.ff, sp.shared_ff, sp.dtype
+    L = {
+        "name": sp.name, "d": d, "n_expert": E, "ff": ff, "k": sp.k, "shared_ff": ffs,
+        "dtype": dt, "route": sp.route, "act": sp.act, "route_scale": sp.route_scale,
+        "oai_alpha": sp.oai_alpha, "oai_limit": sp.oai_limit,
+    }
+    L["w_router"] = _store(_draw(seed, "w_router", 0, (E, d), sp.router_std), dt)
+    if sp.router_bias == "normal":
+        L["b_router"] = _draw(seed, "b_router", 0, (E,), sp.router_bias_std)
+    elif sp.router_bias == "zipf":
+        L["b_router"] = zipf_router_bias(E, sp.k, sp.zipf_s)
+    else:
+        L["b_router"] = None
+    if sp.act == ACT_SWIGLU:
+        L["w_gate"] = _stacked(seed, "w_gate", E, (ff, d), sp.weight_std, dt, experts)
+        L["w_up"] = _stacked(seed, "w_up", E, (ff, d), sp.weight_std, dt, experts)
+        L["w_gate_up"] = L["b_gate_up"] = L["b_down"] = None
+    else:
+        L["w_gate_up"] = _stacked(seed, "w_gate_up", E, (2 * ff, d), sp.weight_std, dt, experts)
+        L["b_gate_up"] = _stacked(seed, "b_gate_up", E, (2 * ff,), sp.bias_std, dt, experts)
+        L["b_down"] = _stacked(seed, "b_down", E, (d,), sp.bias_std, dt, experts)
+        L["w_gate"] = L["w_up"] = None
+    L["w_down"] = _stacked(seed, "w_down", E, (d, ff), sp.weight_std, dt, experts)
+    if ffs > 0:
+        L["ws_gate"] = _store(_draw(seed, "ws_gate", 0, (ffs, d), sp.weight_std), dt)
+        L["ws_up"] = _store(_draw(seed, "ws_up", 0, (ffs, d), sp.weight_std), dt)
+        L["ws_down"] = _store(_draw(seed, "ws_down", 0, (d, ffs), sp.weight_std), dt)
+        L["ws_gate_inp"] = _store(_draw(seed, "ws_gate_inp", 0, (d,), sp.weight_std), dt)
+    else:
+        L["ws_gate"] = L["ws_up"] = L["ws_down"] = L["ws_gate_inp"] = None
+    return L
+
+
+# ----------------------------------------------------------------------------- tokens
+
+def _router_logits_f64(x_store: np.ndarray, L: dict) -> np.ndarray:
+    """fp64 router logits, used only to reject token rows with near-ties."""
+    z = storage_to_f32(x_store).astype(np.float64) @ storage_to_f32(L["w_router"]).astype(np.float64).T
+    if L["b_router"] is not None:
+        z += L["b_router"].astype(np.float64)
+    return z
+
+
+def _bad_rows(z: np.ndarray, k: int, gap: float) -> np.ndarray:
+    m = min(k + 1, z.shape[1])
+    top = -np.sort(-z, axis=1)[:, :m]
+    if m < 2:
+        return np.zeros(z.shape[0], dtype=bool)
+    return np.any(top[:, :-1] - top[:, 1:] <= gap, axis=1)
+
+
+def make_tokens(L: dict, T: int, seed: int = 0, gap: float = 1e-3, max_attempts: int = 200) -> np.ndarray:
+    """x[T, d] ~ N(0,1) in the layer's storage dtype, with every row's k+1 largest fp64
+    logits separated by more than ``gap``.  A failing row t is redrawn from stream
+    (seed, x_redraw, t, attempt).  ``gap <= 0`` disables the check."""
+    d, k, dt = L["d"], L["k"], L["dtype"]
+    x = _store(_rng(seed, _CODE["x"], T).standard_normal((T, d), dtype=np.float32), dt)
+    if gap <= 0 or T == 0:
+        return x
+    bad = np.nonzero(_bad_rows(_router_logits_f64(x, L), k, gap))[0]
+    attempt = 0
+    while bad.size:
+        attempt += 1
+        if attempt > max_attempts:
+            raise RuntimeError(f"gap enforcement failed for {bad.size} rows")
+        for t in bad:
+            x[t] = _store(_rng(seed, _CODE["x_redraw"], int(t), attempt)
+                          .standard_normal((1, d), dtype=np.float32), dt)[0]
+        still = _bad_rows(_router_logits_f64(x[bad], L), k, gap)
+        bad = bad[still]
+    return x
+
+
+# ----------------------------------------------------------------------------- Zipf bias
+
+def zipf_targets(E: int, k: int, s: float) -> np.ndarray:
+    """Target share of rows selecting the expert of rank r: q_r = min(1, c r^-s),
+    with c fixed by sum(q) = k (an expert appears at most once per row)."""
+    r = np.arange(1, E + 1, dtype=np.float64)
+    lo, hi = 0.0, float(k) * 10
+    for _ in range(200):
+        c = 0.5 * (lo + hi)
+        if np.minimum(1.0, c * r ** -s).sum() > k:
+            hi = c
+        else:
+            lo = c
+    return np.minimum(1.0, 0.5 * (lo + hi) * r ** -s)
+
+
+@functools.lru_cache(maxsize=8)
+def _zipf_bias_by_rank(E: int, k: int, s: float, rows: int, iters: int) -> np.ndarray:
+    q = zipf_targets(E, k, s)
+    noise = _rng(1, 0).standard_normal((rows, E), dtype=np.float32)
+    b = np.zeros(E)
+    for _ in range(iters):
+        z = noise + b.astype(np.float32)
+        kth = -np.partition(-z, k - 1, axis=1)[:, k - 1:k]
+        share = (z >= kth).sum(axis=0) / rows
+        b += 0.3 * (np.log(q) - np.log(np.maximum(share, 0.25 / rows)))
+        b -= b[1:].max()
+        b[0] = max(b[0], 3.0)
+    return b
+
+
+def zipf_router_bias(E: int, k: int, s: float = 1.1, rows: int = 32768, iters: int = 60) -> np.ndarray:
+    """fp32 router bias giving a capped-Zipf(s) expected load when logits are ~N(0,1).
+    Calibrated by a damped fixed-point update on N(0,1) noise (stream 1); ranks are
+    assigned to expert ids by a seeded permutation (stream 2)."""
+    by_rank = _zipf_bias_by_rank(E, k, float(s), rows, iters)
+    perm = _rng(2, 0).permutation(E)          # expert id of each rank
+    b = np.empty(E)
+    b[perm] = by_rank
+    return b.astype(np.float32)
+
+
+def zipf_rank_of_expert(E: int) -> np.ndarray:
+    perm = _rng(2, 0).permutation(E)
+    rank = np.empty(E, dtype=np.int64)
+    rank[perm] = np.arange(E)
+    return rank

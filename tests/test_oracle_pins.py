@@ -1,0 +1,304 @@
+"""Pins of the fp64 oracle against facts fixed outside the oracle itself: closed forms,
+special cases that reduce to library routines, brute force on tiny inputs, invariants,
+and the worked example printed on the "Engine" (Cherenkov) page.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term, a wrong
+sign or index, a transposed operand, swapped gate/up) fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.special as sps
+import torch
+import torch.nn.functional as F
+
+import oracle
+from sparse_mixture_experts_amd import synth
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def tiny_layer(d=16, E=6, ff=8, k=2, ffs=0, route="softmax_topk_renorm", act="swiglu",
+               seed=0, dtype="f32", router_std=0.5, bias="none", scale=1.0):
+    sp = synth.LayerSpec("t", d=d, n_expert=E, ff=ff, k=k, shared_ff=ffs, dtype=dtype,
+                         route=route, act=act, router_std=router_std, weight_std=0.3,
+                         router_bias=bias, router_bias_std=0.3, bias_std=0.3, route_scale=scale)
+    return synth.make_layer(sp, seed=seed)
+
+
+def t64(a):
+    return torch.from_numpy(oracle.widen(a))
+
+
+def torch_swiglu(x, wg, wu, wd):
+    """Plain SwiGLU MLP with torch's own silu (a library routine), in fp64 on the CPU."""
+    return (F.silu(t64(x) @ t64(wg).T) * (t64(x) @ t64(wu).T)) @ t64(wd).T
+
+
+# ----------------------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("route", ["softmax_topk_renorm", "topk_softmax"])
+def test_routing_weights_sum_to_one(route):
+    # "Llama Forward Pass", Mixture of Experts: renormalised weights sum to 1.
+    L = tiny_layer(E=8, k=3, route=route, d=32)
+    x = synth.make_tokens(L, 64, seed=1)
+    _, w, _ = oracle.route(L, x)
+    assert np.all(w > 0)
+    assert np.max(np.abs(w.sum(axis=1) - 1.0)) <= 1e-12
+
+
+def test_route_scale_multiplies_after_renorm():
+    L = tiny_layer(E=8, k=3, d=32, scale=2.5)
+    x = synth.make_tokens(L, 16, seed=1)
+    _, w, _ = oracle.route(L, x)
+    assert np.max(np.abs(w.sum(axis=1) - 2.5)) <= 1e-12
+
+
+def test_mode_a_equals_mode_b_identity():
+    # With renormalisation and scale 1 the full-softmax denominator cancels.
+    rng = np.random.default_rng(0)
+    z = rng.standard_normal((200, 32)) * 3
+    idx = oracle.topk_select(z, 5)
+    a = oracle.weights_softmax_topk_renorm(z, idx)
+    b = oracle.weights_topk_softmax(z, idx)
+    assert np.max(np.abs(a - b)) <= 1e-14
+
+
+@pytest.mark.parametrize("route", ["softmax_topk_renorm", "topk_softmax"])
+def test_two_expert_weights_closed_form(route):
+    # k = 2: the first weight is the logistic function of the logit gap (scipy's expit).
+    rng = np.random.default_rng(1)
+    z = rng.standard_normal((100, 7))
+    idx = oracle.topk_select(z, 2)
+    if route == "softmax_topk_renorm":
+        w = oracle.weights_softmax_topk_renorm(z, idx)
+    else:
+        w = oracle.weights_topk_softmax(z, idx)
+    gap = np.take_along_axis(z, idx[:, :1], 1) - np.take_along_axis(z, idx[:, 1:2], 1)
+    assert np.max(np.abs(w[:, 0] - sps.expit(gap[:, 0]))) <= 1e-15
+    assert np.max(np.abs(w[:, 1] - sps.expit(-gap[:, 0]))) <= 1e-15
+
+
+@pytest.mark.parametrize("E", [3, 5, 8])
+def test_topk_matches_subset_brute_force(E):
+    rng = np.random.default_rng(E)
+    for trial in range(40):
+        # half the trials use small integers so that ties occur
+        z = rng.integers(-3, 4, size=E).astype(float) if trial % 2 else rng.standard_normal(E)
+        for k in range(1, E + 1):
+            got = oracle.topk_select(z[None, :], k)[0].tolist()
+            assert got == oracle.brute_topk(z, k), (z, k)
+
+
+def test_topk_ties_lowest_index_and_descending_order():
+    z = np.array([[0.5, 2.0, 2.0, -1.0, 2.0, 0.5]])
+    assert oracle.topk_select(z, 4)[0].tolist() == [1, 2, 4, 0]
+
+
+def test_all_tie_router():
+    # W_r = 0, b = 0: logits exactly equal; experts 0..k-1 in order, weight 1/k each.
+    L = tiny_layer(E=8, k=3, d=16)
+    L["w_router"] = np.zeros_like(L["w_router"])
+    x = synth.make_tokens(L, 5, gap=0)
+    idx, w, _ = oracle.route(L, x)
+    assert (idx == np.array([0, 1, 2])).all()
+    assert np.max(np.abs(w - 1.0 / 3.0)) <= 1e-16
+
+
+# ----------------------------------------------------------------------------- experts
+
+def test_textbook_single_expert_is_plain_swiglu_mlp():
+    # E = 1, k = 1, no shared expert: the layer is the SwiGLU MLP of "Llama Forward
+    # Pass", SwiGLU FFN.  Reference: torch's silu in fp64.
+    L = tiny_layer(E=1, k=1, d=24, ff=40)
+    x = synth.make_tokens(L, 7, gap=0)
+    ref = torch_swiglu(x, L["w_gate"][0], L["w_up"][0], L["w_down"][0]).numpy()
+    got = oracle.moe_forward(L, x)
+    assert np.max(np.abs(got - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+def test_one_hot_router_reproduces_single_expert():
+    L = tiny_layer(E=6, k=1, d=16, ff=12)
+    L["w_router"] = np.zeros_like(L["w_router"])
+    b = np.zeros(6, dtype=np.float32)
+    b[4] = 100.0
+    L["b_router"] = b
+    x = synth.make_tokens(L, 9, gap=0)
+    idx, w, _ = oracle.route(L, x)
+    assert (idx[:, 0] == 4).all() and (w == 1.0).all()
+    ref = torch_swiglu(x, L["w_gate"][4], L["w_up"][4], L["w_down"][4]).numpy()
+    assert np.max(np.abs(oracle.moe_forward(L, x) - ref)) <= 1e-14 * np.max(np.abs(ref))
+
+
+def test_dense_equivalence_k_equals_E():
+    # k = E: every expert sees every token and out = sum_e p_e FFN_e(x) + shared,
+    # evaluated here with einsum over all experts, no routing or permutation.
+    E, d, ff, ffs = 5, 12, 10, 6
+    L = tiny_layer(E=E, k=E, d=d, ff=ff, ffs=ffs)
+    x = synth.make_tokens(L, 11, gap=0)
+    counts, *_ = oracle.permute(oracle.route(L, x)[0], E)
+    assert (counts == 11).all()
+    X = oracle.widen(x)
+    z = X @ oracle.widen(L["w_router"]).T
+    p = sps.softmax(z, axis=1)
+    g = np.einsum("td,efd->tef", X, oracle.widen(L["w_gate"]))
+    u = np.einsum("td,efd->tef", X, oracle.widen(L["w_up"]))
+    h = F.silu(torch.from_numpy(g)).numpy() * u
+    y = np.einsum("tef,edf->ted", h, oracle.widen(L["w_down"]))
+    sh = torch_swiglu(x, L["ws_gate"], L["ws_up"], L["ws_down"]).numpy()
+    gate = sps.expit(X @ oracle.widen(L["ws_gate_inp"]))
+    ref = np.einsum("te,ted->td", p, y) + gate[:, None] * sh
+    assert np.max(np.abs(oracle.moe_forward(L, x) - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_identical_experts_give_single_ffn_for_any_router():
+    L = tiny_layer(E=6, k=3, d=16, ff=8, ffs=4)
+    for n in ("w_gate", "w_up", "w_down"):
+        L[n][:] = L[n][0]
+    x = synth.make_tokens(L, 8, seed=3)
+    ffn = torch_swiglu(x, L["w_gate"][0], L["w_up"][0], L["w_down"][0]).numpy()
+    sh = torch_swiglu(x, L["ws_gate"], L["ws_up"], L["ws_down"]).numpy()
+    gate = sps.expit(oracle.widen(x) @ oracle.widen(L["ws_gate_inp"]))
+    ref = ffn + gate[:, None] * sh
+    assert np.max(np.abs(oracle.moe_forward(L, x) - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_shared_gate_zero_is_half():
+    # w_sg = 0 gives sigmoid(0) = 0.5 exactly; routed experts with W_d = 0 add nothing.
+    L = tiny_layer(E=4, k=2, d=16, ff=8, ffs=12)
+    L["ws_gate_inp"] = np.zeros_like(L["ws_gate_inp"])
+    L["w_down"] = np.zeros_like(L["w_down"])
+    x = synth.make_tokens(L, 6)
+    ref = 0.5 * torch_swiglu(x, L["ws_gate"], L["ws_up"], L["ws_down"]).numpy()
+    assert np.array_equal(oracle.route(L, x)[2], np.zeros(6))
+    assert np.max(np.abs(oracle.moe_forward(L, x) - ref)) <= 1e-15 * np.max(np.abs(ref))
+
+
+def test_oai_up_plus_one_and_bias_inside_sum():
+    # Up rows zero and up bias -1 make (up + 1) = 0, so h = 0 and every expert returns
+    # its down bias: out = sum_j w_j b_d[s_j] ("Phase 19", Experts).
+    L = tiny_layer(E=5, k=2, d=16, ff=8, route="topk_softmax", act="swiglu_oai", bias="normal")
+    L["w_gate_up"][:, 1::2, :] = 0
+    L["b_gate_up"][:, 1::2] = -1.0
+    x = synth.make_tokens(L, 7)
+    idx, w, _ = oracle.route(L, x)
+    bd = oracle.widen(L["b_down"])
+    ref = np.einsum("tj,tjd->td", w, bd[idx])
+    assert np.max(np.abs(oracle.moe_forward(L, x) - ref)) <= 1e-15 * np.max(np.abs(ref))
+
+
+def test_oai_clamps_and_interleave():
+    # One expert, x = e_0, W_d = I: out = h.  Row 2f of gate_up is gate f, row 2f+1 is
+    # up f.  Gate is clamped only from above at 7, up to [-7, 7].
+    g = [10.0, 7.0, 1.0, -8.0, 0.5]
+    u = [10.0, -10.0, 0.5, -0.5, 3.0]
+    ff = d = len(g)
+    wgu = np.zeros((1, 2 * ff, d), dtype=np.float32)
+    wgu[0, 0::2, 0] = g
+    wgu[0, 1::2, 0] = u
+    L = {"d": d, "n_expert": 1, "ff": ff, "k": 1, "shared_ff": 0, "route": "topk_softmax",
+         "act": "swiglu_oai", "oai_alpha": 1.702, "oai_limit": 7.0,
+         "w_router": np.zeros((1, d), np.float32), "b_router": None,
+         "w_gate_up": wgu, "b_gate_up": np.zeros((1, 2 * ff), np.float32),
+         "w_down": np.eye(d, dtype=np.float32)[None], "b_down": np.zeros((1, d), np.float32)}
+    x = np.zeros((1, d), np.float32)
+    x[0, 0] = 1.0
+    a = 1.702
+    expected = [
+        (7.0 + 1.0) * 7.0 * sps.expit(a * 7.0),     # gate 10 -> 7, up 10 -> 7
+        (-7.0 + 1.0) * 7.0 * sps.expit(a * 7.0),    # gate at the limit, up -10 -> -7
+        (0.5 + 1.0) * 1.0 * sps.expit(a * 1.0),
+        (-0.5 + 1.0) * -8.0 * sps.expit(-8.0 * a),  # no lower clamp on the gate
+        (3.0 + 1.0) * 0.5 * sps.expit(0.5 * a),
+    ]
+    got = oracle.moe_forward(L, x)[0]
+    assert np.max(np.abs(got - np.array(expected))) <= 1e-14
+
+
+# ----------------------------------------------------------------------------- grouping
+
+def test_permute_against_library_sort():
+    rng = np.random.default_rng(5)
+    T, E, k = 40, 9, 3
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    counts, offsets, perm_token, perm_inv = oracle.permute(idx, E)
+    assert (counts == np.bincount(idx.reshape(-1), minlength=E)).all()
+    assert offsets[0] == 0 and (np.diff(offsets) == counts).all()
+    tok = np.repeat(np.arange(T), k)
+    order = np.lexsort((tok, idx.reshape(-1)))        # expert-major, then token
+    assert (perm_token == tok[order]).all()
+    flat_inv = np.empty(T * k, dtype=np.int64)
+    flat_inv[order] = np.arange(T * k)
+    assert (perm_inv.reshape(-1) == flat_inv).all()
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(route="softmax_topk_renorm", act="swiglu", ffs=0),
+    dict(route="softmax_topk_renorm", act="swiglu", ffs=4, scale=1.5),
+    dict(route="topk_softmax", act="swiglu_oai", ffs=0, bias="normal"),
+    dict(route="softmax_topk_renorm", act="swiglu", ffs=0, bias="normal"),
+])
+def test_grouped_oracle_matches_scalar_brute_force(cfg):
+    L = tiny_layer(E=5, k=2, d=6, ff=4, **cfg)
+    L["oai_limit"] = 0.4          # small weights: a small limit makes the clamps bite
+    x = synth.make_tokens(L, 4, seed=2)
+    ref = oracle.brute_forward(L, x)
+    got = oracle.moe_forward(L, x)
+    assert np.max(np.abs(got - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+def test_grouped_equals_per_token_definition():
+    L = tiny_layer(E=8, k=3, d=32, ff=16, ffs=8)
+    x = synth.make_tokens(L, 30, seed=4)
+    a = oracle.moe_forward(L, x)
+    b = oracle.moe_forward_tokens(L, x)
+    assert np.max(np.abs(a - b)) <= 1e-13 * np.max(np.abs(b))
+
+
+def test_relabelling_invariance():
+    L = tiny_layer(E=7, k=3, d=16, ff=8, ffs=4, bias="normal")
+    x = synth.make_tokens(L, 12, seed=6)
+    perm = np.random.default_rng(9).permutation(7)
+    P = dict(L)
+    for n in ("w_router", "b_router", "w_gate", "w_up", "w_down"):
+        P[n] = L[n][perm]
+    c0, *_ = oracle.permute(oracle.route(L, x)[0], 7)
+    c1, *_ = oracle.permute(oracle.route(P, x)[0], 7)
+    assert (c1 == c0[perm]).all()
+    assert np.max(np.abs(oracle.moe_forward(P, x) - oracle.moe_forward(L, x))) <= 1e-13
+
+
+def test_token_independence():
+    L = tiny_layer(E=8, k=2, d=16, ff=8, ffs=4)
+    x = synth.make_tokens(L, 10, seed=8)
+    full = oracle.moe_forward(L, x)
+    for t in (0, 3, 9):
+        assert np.max(np.abs(oracle.moe_forward(L, x[t:t + 1])[0] - full[t])) <= 1e-14
+
+
+def test_empty_batch():
+    L = tiny_layer()
+    assert oracle.moe_forward(L, np.zeros((0, 16), np.float32)).shape == (0, 16)
+
+
+def test_address_table_example(golden_dir):
+    with open(os.path.join(golden_dir, "cherenkov_address_table.json")) as f:
+        g = json.load(f)
+    m = g["mapping"]
+    idx = np.array([[m[e] for e in r["experts"]] for r in g["rows"]])
+    w = np.array([r["weights"] for r in g["rows"]])
+    active, wmap = oracle.active_union(idx, w, g["n_expert"])
+    assert active.tolist() == [m[e] for e in g["expected_union"]]
+    for name, row in g["expected_wmap"].items():
+        assert wmap[active.tolist().index(m[name])].tolist() == row
+
+
+def test_activation_special_values():
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    assert oracle.sigmoid(np.array([0.0]))[0] == 0.5
+    big = np.array([50.0])
+    assert oracle.silu(big)[0] == 50.0
+    v = np.linspace(-6, 6, 101)
+    assert np.allclose(oracle.silu(v), F.silu(torch.from_numpy(v)).numpy(), rtol=0, atol=1e-15)
