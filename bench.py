@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse MoE FFN layer on one MI355X, through the C ABI.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-sweep]
+
+A step is one ``moe_forward`` (router, top-k, grouping, expert FFNs, combine) over one
+batch of synthetic tokens already resident in HBM.  To keep the 256 MB Infinity Cache
+from serving "HBM" reads, steps rotate over several device copies of the layer weights
+and over several pre-generated token batches.
+
+The printed JSON line carries the headline workload (Qwen3.5-MoE-shaped decode, T=64);
+``sweep`` holds the other decode batches and the prefill batch.  ``roofline`` is for
+the dominant stage (the expert FFN launches: plan + up-projection + down-projection),
+timed with events on the launch stream in a separate pass of the same steps split at
+the C-ABI calls.  ``cpu_baseline`` is the fp64 oracle on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12             # B/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15       # FLOP/s, dense bf16
+VALU_F32_PEAK = 157.3e12
+
+# name -> (layer spec name, T)
+WORKLOADS = {
+    "qwen_decode_t1": ("qwen", 1),
+    "qwen_decode_t8": ("qwen", 8),
+    "qwen_decode_t64": ("qwen", 64),
+    "qwen_prefill_t8192": ("qwen_zipf", 8192),
+    "gptoss_t1": ("gptoss", 1),
+    "gptoss_t4096": ("gptoss", 4096),
+    "mixtral_t16": ("mixtral", 16),
+    "mixtral_t16384": ("mixtral", 16384),
+    "tiny_f32_t16": ("tiny_f32", 16),
+}
+DEFAULT = "qwen_decode_t64"
+DEFAULT_SWEEP = ["qwen_decode_t1", "qwen_decode_t8", "qwen_prefill_t8192"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- work model
+
+def elem_bytes(L):
+    return 2 if L["dtype"] == "bf16" else 4
+
+
+def expert_weight_bytes(L):
+    """Bytes of one routed expert's parameters."""
+    s, d, ff = elem_bytes(L), L["d"], L["ff"]
+    if L["act"] == "swiglu":
+        return 3 * d * ff * s
+    b = 2 * ff * s + (d * s if L.get("b_down") is not None else 0)
+    return 3 * d * ff * s + b
+
+
+def shared_bytes(L):
+    return (3 * L["d"] * L["shared_ff"] + L["d"]) * elem_bytes(L) if L["shared_ff"] else 0
+
+
+def layer_bytes(L, T, U):
+    """Algorithmic HBM bytes of one forward: active experts, shared expert, router, x, y."""
+    s = elem_bytes(L)
+    router = L["n_expert"] * L["d"] * s + (L["n_expert"] * 4 if L.get("b_router") is not None else 0)
+    return U * expert_weight_bytes(L) + shared_bytes(L) + router + 2 * T * L["d"] * s
+
+
+def stage_bytes(L, T, U):
+    """Algorithmic bytes of the expert FFN stage: active + shared expert weights, x."""
+    s = elem_bytes(L)
+    return U * expert_weight_bytes(L) + 3 * L["d"] * L["shared_ff"] * s + T * L["d"] * s
+
+
+def layer_flops(L, T):
+    d, ff, k = L["d"], L["ff"], L["k"]
+    routed = 2 * T * k * 3 * d * ff
+    shared = 2 * T * 3 * d * L["shared_ff"]
+    router = 2 * T * L["n_expert"] * d
+    return routed + shared + router
+
+
+def stage_flops(L, T):
+    return 2 * T * L["k"] * 3 * L["d"] * L["ff"] + 2 * T * 3 * L["d"] * L["shared_ff"]
+
+
+# ----------------------------------------------------------------------------- timing
+
+def time_workload(name, steps, warmup, layer_cache):
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_amd.moe as moe
+    from sparse_mixture_experts_amd import synth
+
+    spec_name, T = WORKLOADS[name]
+    L = layer_cache.get(spec_name)
+    if L is None:
+        t0 = time.time()
+        base = "qwen" if spec_name == "qwen_zipf" and "qwen" in layer_cache else None
+        if base:
+            L = dict(layer_cache["qwen"])
+            L["b_router"] = synth.zipf_router_bias(L["n_expert"], L["k"], 1.1)
+            L["name"] = "qwen_zipf"
+        else:
+            L = synth.make_layer(synth.spec(spec_name), seed=0)
+        layer_cache[spec_name] = L
+        log(f"[{name}] layer generated in {time.time() - t0:.1f}s")
+    decode = T <= 64
+    # Decode touches a small, batch-dependent slice of the weights: 4 weight copies and
+    # 16 token batches keep consecutive steps off each other's cache lines.  Prefill
+    # streams every expert once per step, far beyond the 256 MB Infinity Cache.
+    n_copies = 4 if decode else 1
+    n_batches = 16 if decode else 2
+    t0 = time.time()
+    xs_np = [synth.make_tokens(L, T, seed=1000 + i) for i in range(n_batches)]
+    log(f"[{name}] {n_batches} token batches in {time.time() - t0:.1f}s; {n_copies} weight copies")
+
+    lay0 = moe.Layer.from_arrays(L)
+    layers = [lay0]
+    for _ in range(n_copies - 1):
+        tens = {k: (v.clone() if v is not None else None) for k, v in lay0.tensors.items()}
+        layers.append(moe.Layer(L["d"], L["n_expert"], L["ff"], L["k"], L["shared_ff"], L["dtype"],
+                                L["route"], L["act"], L["route_scale"], L["oai_alpha"],
+                                L["oai_limit"], **tens))
+    xs = [moe.to_device(x) for x in xs_np]
+    ws = moe.workspace(lay0, T)
+    y = torch.empty((T, L["d"]), dtype=lay0.torch_dtype, device="cuda")
+
+    # realised active experts per batch (from the library's own routing)
+    U = []
+    for x in xs:
+        idx, _, _ = moe.route(lay0, x, ws)
+        U.append(int(torch.unique(idx).numel()))
+    U_mean = sum(U) / len(U)
+
+    def step(i):
+        moe.forward(layers[i % n_copies], xs[i % n_batches], ws, out=y)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(steps):
+        ev[i][0].record()
+        step(warmup + i)
+        ev[i][1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    ms_step = total_ms / steps
+
+    # Stage pass: the same steps split at the C-ABI calls, events around the expert FFN.
+    plans = []
+    for x in xs:
+        idx, w, sg = moe.route(lay0, x, ws)
+        off, pt, pi = moe.permute(idx, L["n_expert"])
+        plans.append((off, pt))
+    rows = T * L["k"] + (T if L["shared_ff"] else 0)
+    yp = torch.empty((rows, L["d"]), dtype=torch.float32, device="cuda")
+    lib, stream = moe.lib(), moe._stream()
+
+    def stage(i):
+        lay, x = layers[i % n_copies], xs[i % n_batches]
+        off, pt = plans[i % n_batches]
+        st = lib.moe_expert_ffn(lay.ref(), x.data_ptr(), T, off.data_ptr(), pt.data_ptr(),
+                                yp.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        assert st == 0, st
+
+    for i in range(warmup):
+        stage(i)
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        sev[i][0].record()
+        stage(warmup + i)
+        sev[i][1].record()
+    torch.cuda.synchronize()
+    stage_ms = sum(a.elapsed_time(b) for a, b in sev) / steps
+
+    res = {
+        "workload": name, "T": T, "layer": spec_name, "dtype": L["dtype"],
+        "ms_per_step": ms_step, "ms_p10": per[len(per) // 10], "ms_median": statistics.median(per),
+        "ms_p90": per[(9 * len(per)) // 10], "tokens_per_s": T / (ms_step / 1e3),
+        "active_experts_mean": U_mean, "weight_copies": n_copies, "token_batches": n_batches,
+        "stage_ms": stage_ms,
+    }
+    if decode:
+        lb = layer_bytes(L, T, U_mean)
+        sb = stage_bytes(L, T, U_mean)
+        res["layer_bytes"] = lb
+        res["layer_hbm_frac"] = lb / (ms_step / 1e3) / HBM_PEAK
+        res["roofline"] = {"bound": "hbm", "achieved": sb / (stage_ms / 1e3) / 1e9,
+                           "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                           "frac": sb / (stage_ms / 1e3) / HBM_PEAK, "traffic": None,
+                           "kernel": "expert FFN stage (plan + up + down)",
+                           "algorithmic_bytes": sb}
+    else:
+        fl = layer_flops(L, T)
+        sf = stage_flops(L, T)
+        peak = MFMA_BF16_PEAK if L["dtype"] == "bf16" else VALU_F32_PEAK
+        res["layer_flops"] = fl
+        res["layer_mfma_frac"] = fl / (ms_step / 1e3) / peak
+        res["roofline"] = {"bound": "mfma", "achieved": sf / (stage_ms / 1e3) / 1e12,
+                           "peak": peak / 1e12, "unit": "TFLOP/s",
+                           "frac": sf / (stage_ms / 1e3) / peak, "traffic": None,
+                           "kernel": "expert FFN stage (plan + up + down)",
+                           "algorithmic_flops": sf}
+    log(f"[{name}] {ms_step * 1e3:.1f} us/step, {res['tokens_per_s']:.0f} tok/s, "
+        f"stage {stage_ms * 1e3:.1f} us, roofline frac {res['roofline']['frac']:.3f}")
+    del layers, xs, ws, y, yp, plans
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(name, layer_cache, max_tokens=64):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle
+    from sparse_mixture_experts_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    spec_name, T = WORKLOADS[name]
+    L = layer_cache.get(spec_name) or synth.make_layer(synth.spec(spec_name), seed=0)
+    n = min(T, max_tokens)
+    x = synth.make_tokens(L, n, seed=1000)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.moe_forward(L, x)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"value": n / med, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} tokens of {name}, median of 3 full oracle calls "
+                      f"({med:.2f} s each, bf16->fp64 weight widening included)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--sweep", default=",".join(DEFAULT_SWEEP),
+                    help="comma-separated extra workloads reported under 'sweep'")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from sparse_mixture_experts_amd import moe
+    moe.lib()
+
+    cache = {}
+    main_res = time_workload(args.workload, args.steps, args.warmup, cache)
+    sweep = []
+    if not args.no_sweep:
+        for w in [s for s in args.sweep.split(",") if s and s != args.workload]:
+            sweep.append(time_workload(w, max(5, min(args.steps, 20)) if WORKLOADS[w][1] > 64 else args.steps,
+                                       min(args.warmup, 5), cache))
+    cpu = None if args.no_cpu else cpu_baseline(args.workload, cache)
+
+    spec_name, T = WORKLOADS[args.workload]
+    out = {
+        "metric": "MoE-layer tokens/s + % HBM roofline (decode T=1..64) / % MFMA peak (T=8192)",
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if main_res["dtype"] == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "layer": spec_name, "tokens": T,
+                   "layer_hbm_frac": main_res.get("layer_hbm_frac"),
+                   "active_experts_mean": main_res["active_experts_mean"],
+                   "ms_median": main_res["ms_median"], "ms_p10": main_res["ms_p10"],
+                   "ms_p90": main_res["ms_p90"]},
+        "roofline": main_res["roofline"],
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

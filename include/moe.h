@@ -1,0 +1,177 @@
+/*
+ * moe.h -- C ABI of libsmoe.so, the sparse mixture-of-experts FFN layer on one
+ * MI355X (gfx950).
+ *
+ * The layer (per token t, input x[t] of width d):
+ *   z      = W_r x (+ b_r)                                   router logits, E of them
+ *   S, w   = the k experts with the largest logits and their routing weights
+ *   out    = sum_j w_j FFN_{S_j}(x) (+ sigmoid(w_sg . x) FFN_shared(x))
+ * as defined on "Qwen3.5-MoE Model Implementation" (section "MoE routing": router,
+ * top-8, renormalisation, SwiGLU experts, sigmoid-gated shared expert, combine with
+ * the residual left to the caller), "Llama Forward Pass" (section "Mixture of
+ * Experts (Mixtral)") and "Phase 19: MoE - gpt-oss-20b" (section 2, Router and
+ * Experts: top-k before softmax with a router bias; interleaved, clamped
+ * (up + 1) * gate * sigmoid(alpha * gate) experts with biases).  The grouped
+ * evaluation (tokens grouped by expert, gathered, projected, scattered back) is the
+ * one described on "Engine" (Cherenkov), section "Prefill".
+ *
+ * Conventions (every entry point):
+ *  - Every pointer argument and every pointer inside moe_layer is DEVICE memory
+ *    unless stated otherwise; the moe_layer struct itself and size_t* out-arguments
+ *    are HOST memory.  The caller owns all memory; the library borrows it for the
+ *    duration of the enqueued work and never allocates, frees or synchronises.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls
+ *    only enqueue kernels; results are valid once the stream's work has completed.
+ *  - Tensors are dense, row-major, with no padding.  Weights are [out, in]
+ *    (the input dimension is contiguous).
+ *  - Argument checks happen on the host before anything is enqueued.  On any error
+ *    the call returns without enqueuing work and without writing any output.
+ *    T == 0 is a no-op that returns MOE_OK.
+ *  - Results are deterministic: no floating-point atomics, fixed reduction orders.
+ *  - The functions hold no state and may be called from several host threads.
+ */
+#ifndef SMOE_MOE_H
+#define SMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+enum {
+    MOE_OK = 0,
+    MOE_ERR_ARG = 1,          /* null required pointer, bad enum, k < 1, k > E, T < 0, ... */
+    MOE_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels handle (see below)    */
+    MOE_ERR_WORKSPACE = 3,    /* workspace smaller than the size query returned           */
+    MOE_ERR_DEVICE = 4        /* a HIP launch failed (hipGetLastError after enqueue)      */
+};
+
+/* dtype of x, y and every weight except the router bias (always fp32). */
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* Routing mode.
+ *  SOFTMAX_TOPK_RENORM ("Qwen3.5-MoE Model Implementation", MoE routing; "Llama Forward
+ *    Pass", Mixture of Experts): p = softmax(z) over all E experts, S = top-k, weights
+ *    w_j = route_scale * p_{S_j} / sum_j' p_{S_j'}.
+ *  TOPK_SOFTMAX ("Phase 19: MoE - gpt-oss-20b", Router): S = top-k of z, weights
+ *    w = softmax over the k selected logits (route_scale is ignored).
+ *  In both modes S is ordered by descending logit and ties go to the lower expert
+ *  index; a router bias, when given, is added to z before selection. */
+enum { MOE_ROUTE_SOFTMAX_TOPK_RENORM = 0, MOE_ROUTE_TOPK_SOFTMAX = 1 };
+
+/* Expert activation.
+ *  SWIGLU: h = silu(W_g x) * (W_u x), y = W_d h ("Llama Forward Pass", SwiGLU FFN).
+ *  SWIGLU_OAI ("Phase 19: MoE - gpt-oss-20b", Experts): v = W_gu x + b_gu with rows of
+ *    W_gu interleaved (row 2m = gate m, row 2m+1 = up m); gate = min(v_2m, limit);
+ *    up = clamp(v_2m+1, -limit, limit); h = (up + 1) * gate * sigmoid(alpha * gate);
+ *    y = W_d h + b_d (the down bias is inside the routing-weighted sum). */
+enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 };
+
+/* Kernel path.  AUTO: the decode GEMV path for T <= 64, the grouped MFMA path above.
+ * DECODE / GROUPED force one path at any T (GROUPED requires MOE_BF16). */
+enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_GROUPED = 2 };
+
+/* One MoE layer.  Fixed layout: 9 int32, 3 float, then 12 pointers (offset 48). No
+ * field depends on a build flag.  All pointers are device memory, 16-byte aligned
+ * (b_router, b_gate_up, b_down: element-aligned suffices). */
+typedef struct moe_layer {
+    int32_t d;            /* model width; multiple of 64                               */
+    int32_t n_expert;     /* E, 1..512                                                 */
+    int32_t ff;           /* expert hidden width; multiple of 64                       */
+    int32_t k;            /* experts per token, 1..min(E, 32)                          */
+    int32_t shared_ff;    /* shared expert hidden width; 0 = no shared expert; %64==0  */
+    int32_t dtype;        /* MOE_F32 | MOE_BF16                                        */
+    int32_t route;        /* MOE_ROUTE_*                                               */
+    int32_t act;          /* MOE_ACT_*                                                 */
+    int32_t path;         /* MOE_PATH_*                                                */
+    float route_scale;    /* expert weight scale of mode SOFTMAX_TOPK_RENORM (1.0)     */
+    float oai_alpha;      /* 1.702 for SWIGLU_OAI                                      */
+    float oai_limit;      /* 7.0 for SWIGLU_OAI                                        */
+    const void* w_router;     /* [E, d]                                                */
+    const float* b_router;    /* [E] fp32, or NULL                                     */
+    const void* w_gate;       /* SWIGLU: [E, ff, d]                                    */
+    const void* w_up;         /* SWIGLU: [E, ff, d]                                    */
+    const void* w_gate_up;    /* SWIGLU_OAI: [E, 2*ff, d], rows gate,up interleaved    */
+    const void* b_gate_up;    /* SWIGLU_OAI: [E, 2*ff]                                 */
+    const void* w_down;       /* [E, d, ff]                                            */
+    const void* b_down;       /* SWIGLU_OAI: [E, d] or NULL                            */
+    const void* ws_gate;      /* shared expert: [shared_ff, d]                         */
+    const void* ws_up;        /* shared expert: [shared_ff, d]                         */
+    const void* ws_down;      /* shared expert: [d, shared_ff]                         */
+    const void* ws_gate_inp;  /* shared expert sigmoid gate vector: [d]                */
+} moe_layer;
+
+/* ABI version of this header (bumped on any layout or signature change). */
+int32_t moe_abi_version(void);
+
+/* Static description of a status code.  Never NULL. */
+const char* moe_status_string(moe_status s);
+
+/* Workspace bytes needed by moe_route, moe_expert_ffn and moe_forward for this layer
+ * and up to T tokens (one size covers all three).  Writes *bytes (host).  Errors:
+ * MOE_ERR_ARG / MOE_ERR_UNSUPPORTED as for moe_forward. */
+moe_status moe_workspace_size(const moe_layer* L, int32_t T, size_t* bytes);
+
+/* Router and top-k ("Qwen3.5-MoE Model Implementation", MoE routing; "Phase 19",
+ * Router).
+ *   x           [T, d] in L->dtype
+ *   topk_idx    [T, k] int32 out: selected experts, descending logit, ties -> lower id
+ *   topk_w      [T, k] fp32 out: routing weights of the layer's mode
+ *   shared_gate [T] fp32 out: w_sg . x (the sigmoid's input), or NULL; must be NULL
+ *               when the layer has no shared expert
+ *   ws          device workspace of at least moe_workspace_size(L, T) bytes */
+moe_status moe_route(const moe_layer* L, const void* x, int32_t T, int32_t* topk_idx,
+                     float* topk_w, float* shared_gate, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Workspace bytes needed by moe_permute. */
+moe_status moe_permute_workspace_size(int32_t T, int32_t k, int32_t E, size_t* bytes);
+
+/* Group the T*k (token, slot) pairs by expert ("Engine", Prefill: tokens grouped by
+ * expert).
+ *   topk_idx        [T, k] int32 in, entries in [0, E), distinct within a row
+ *   expert_offsets  [E+1] int32 out: exclusive prefix sum of per-expert counts
+ *   perm_token      [T*k] int32 out: token of grouped row r (expert-major rows, tokens
+ *                   ascending inside an expert)
+ *   perm_inv        [T*k] int32 out: grouped row of (t, j), at index t*k + j
+ * Entries outside [0, E) are ignored (not counted; their perm_inv is -1). */
+moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                       int32_t* expert_offsets, int32_t* perm_token, int32_t* perm_inv,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFNs over the grouped rows ("Qwen3.5-MoE Model Implementation", MoE
+ * routing: SwiGLU experts and the shared expert; "Phase 19", Experts).
+ *   expert_offsets, perm_token  as produced by moe_permute for this T and k
+ *   y_perm  [T*k + (shared_ff ? T : 0), d] fp32 out: row r < T*k holds
+ *           FFN_e(x[perm_token[r]]) for the expert e owning row r (down bias included,
+ *           routing weight NOT applied); row T*k + t holds the shared expert's output
+ *           for token t without its sigmoid gate. */
+moe_status moe_expert_ffn(const moe_layer* L, const void* x, int32_t T,
+                          const int32_t* expert_offsets, const int32_t* perm_token,
+                          float* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine ("Qwen3.5-MoE Model Implementation", MoE routing: out = moe_out +
+ * shexp_out, no residual):
+ *   y[t] = sum_{j<k} topk_w[t,j] * y_perm[perm_inv[t*k+j]]
+ *          (+ sigmoid(shared_gate[t]) * y_perm[T*k + t])
+ * summed in fp32 in the order j = 0..k-1, then the shared term; y [T, d] in L->dtype.
+ * shared_gate must be non-NULL exactly when the layer has a shared expert. */
+moe_status moe_combine(const moe_layer* L, const float* y_perm, const int32_t* perm_inv,
+                       const float* topk_w, const float* shared_gate, int32_t T, void* y,
+                       void* stream);
+
+/* The whole layer: route, group, expert FFNs, combine.  x [T, d] and y [T, d] in
+ * L->dtype (y must not alias x); ws of at least moe_workspace_size(L, T) bytes.
+ * Unsupported: d, ff or shared_ff not a multiple of 64; E > 512; k > 32;
+ * MOE_PATH_GROUPED with MOE_F32. */
+moe_status moe_forward(const moe_layer* L, const void* x, int32_t T, void* y, void* ws,
+                       size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMOE_MOE_H */

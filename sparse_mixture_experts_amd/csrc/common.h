@@ -1,0 +1,91 @@
+// Device helpers shared by the kernels of libsmoe.so (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smoe {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 <-> fp32
+// bf16 values are carried as raw uint16 bits; widening is exact.
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+// Element type tags: the kernels are templated on the storage type of weights and
+// activations.  VEC = elements per 16-byte load.
+struct BF16 { using storage = uint16_t; static constexpr int VEC = 8; };
+struct F32  { using storage = float;    static constexpr int VEC = 4; };
+
+// Unpack one 16-byte vector into VEC floats.
+template <typename TT> __device__ __forceinline__ void unpack16(const uint4& v, float* out);
+template <> __device__ __forceinline__ void unpack16<BF16>(const uint4& v, float* o) {
+    o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+    o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+}
+template <> __device__ __forceinline__ void unpack16<F32>(const uint4& v, float* o) {
+    o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// Streaming load for weights that are read once per call.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Load N consecutive elements of type TT starting at p as floats (N a multiple of VEC).
+template <typename TT, int N>
+__device__ __forceinline__ void load_as_f32(const typename TT::storage* p, float* out) {
+#pragma unroll
+    for (int i = 0; i < N / TT::VEC; ++i) unpack16<TT>(ld16(p + i * TT::VEC), out + i * TT::VEC);
+}
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
+
+// ---------------------------------------------------------------- block scan
+// Exclusive prefix sum of one int per thread over the whole block (blockDim.x <= 1024,
+// a multiple of 64).  `tmp` must hold blockDim.x / 64 ints of LDS.  Returns the
+// exclusive prefix; *total receives the block total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        int o = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) tmp[wave] = incl;
+    __syncthreads();
+    int wave_base = 0, all = 0;
+    for (int w = 0; w < nw; ++w) {
+        int s = tmp[w];
+        if (w < wave) wave_base += s;
+        all += s;
+    }
+    __syncthreads();
+    *total = all;
+    return wave_base + incl - v;
+}
+
+}  // namespace smoe

@@ -1,0 +1,255 @@
+// C ABI of libsmoe.so: argument checks, workspace layout, and the stream-ordered
+// sequence of launches of each entry point.  Every check happens on the host before
+// any HIP call, so a rejected call enqueues nothing and writes nothing.
+#include <math.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace smoe {
+namespace {
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxK = 32;
+constexpr int32_t kMaxTokens = 1 << 22;
+constexpr int kDecodeMaxT = 64;  // MOE_PATH_AUTO takes the GEMV path up to this T
+constexpr int kTileM = 64;  // M-tile size recorded in the group plan
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte offsets of every scratch buffer inside the caller's workspace.
+struct Layout {
+    size_t logits, idx, w, sg, counts, base, offsets, perm_token, perm_inv, groups, meta, H, yperm;
+    size_t total;
+    int ld, hstride, rows;
+};
+
+Layout layout_for(const moe_layer& L, int T) {
+    Layout o{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += round_up(bytes ? bytes : 1, 256);
+        return at;
+    };
+    const bool shared = L.shared_ff > 0;
+    const size_t tk = (size_t)T * L.k;
+    const size_t n_chunks = ((size_t)T + kPermChunk - 1) / kPermChunk;
+    o.ld = L.n_expert + (shared ? 1 : 0);
+    o.hstride = L.ff > L.shared_ff ? L.ff : L.shared_ff;
+    o.rows = (int)(tk + (shared ? T : 0));
+    o.logits = take((size_t)T * o.ld * 4);
+    o.idx = take(tk * 4);
+    o.w = take(tk * 4);
+    o.sg = take((size_t)T * 4);
+    o.counts = take(n_chunks * L.n_expert * 4);
+    o.base = take(n_chunks * L.n_expert * 4);
+    o.offsets = take(((size_t)L.n_expert + 1) * 4);
+    o.perm_token = take(tk * 4);
+    o.perm_inv = take(tk * 4);
+    o.groups = take(((size_t)L.n_expert + 1) * sizeof(Group));
+    o.meta = take(sizeof(PlanMeta));
+    o.H = take((size_t)o.rows * o.hstride * 4);
+    o.yperm = take((size_t)o.rows * L.d * 4);
+    o.total = off;
+    return o;
+}
+
+template <typename P>
+inline P* at(void* ws, size_t off) {
+    return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+moe_status check_layer(const moe_layer* L) {
+    if (!L) return MOE_ERR_ARG;
+    if (L->d <= 0 || L->n_expert <= 0 || L->ff <= 0 || L->k < 1 || L->k > L->n_expert ||
+        L->shared_ff < 0)
+        return MOE_ERR_ARG;
+    if (L->dtype != MOE_F32 && L->dtype != MOE_BF16) return MOE_ERR_ARG;
+    if (L->route != MOE_ROUTE_SOFTMAX_TOPK_RENORM && L->route != MOE_ROUTE_TOPK_SOFTMAX) return MOE_ERR_ARG;
+    if (L->act != MOE_ACT_SWIGLU && L->act != MOE_ACT_SWIGLU_OAI) return MOE_ERR_ARG;
+    if (L->path != MOE_PATH_AUTO && L->path != MOE_PATH_DECODE && L->path != MOE_PATH_GROUPED)
+        return MOE_ERR_ARG;
+    if (!isfinite(L->route_scale) || !isfinite(L->oai_alpha) || !isfinite(L->oai_limit))
+        return MOE_ERR_ARG;
+    if (!L->w_router || !L->w_down) return MOE_ERR_ARG;
+    if (L->act == MOE_ACT_SWIGLU && (!L->w_gate || !L->w_up)) return MOE_ERR_ARG;
+    if (L->act == MOE_ACT_SWIGLU_OAI && (!L->w_gate_up || !L->b_gate_up)) return MOE_ERR_ARG;
+    if (L->shared_ff > 0 && (!L->ws_gate || !L->ws_up || !L->ws_down || !L->ws_gate_inp))
+        return MOE_ERR_ARG;
+    if (L->d % 64 || L->ff % 64 || L->shared_ff % 64) return MOE_ERR_UNSUPPORTED;
+    if (L->n_expert > kMaxExperts || L->k > kMaxK) return MOE_ERR_UNSUPPORTED;
+    if (L->path == MOE_PATH_GROUPED && L->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    const void* vec_ptrs[] = {L->w_router, L->w_gate, L->w_up, L->w_gate_up, L->w_down,
+                              L->ws_gate, L->ws_up, L->ws_down, L->ws_gate_inp};
+    for (const void* p : vec_ptrs)
+        if (!aligned(p, 16)) return MOE_ERR_UNSUPPORTED;
+    const size_t es = L->dtype == MOE_BF16 ? 2 : 4;
+    if (!aligned(L->b_router, 4) || !aligned(L->b_gate_up, es) || !aligned(L->b_down, es))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status check_tokens(int32_t T) {
+    if (T < 0) return MOE_ERR_ARG;
+    if (T > kMaxTokens) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+inline moe_status status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+#define SMOE_TRY(expr)                          \
+    do {                                        \
+        hipError_t err_ = (expr);               \
+        if (err_ != hipSuccess) return MOE_ERR_DEVICE; \
+    } while (0)
+
+moe_status run_experts(const moe_layer& L, const void* x, int T, const int32_t* offsets,
+                       const int32_t* perm_token, float* y_perm, void* ws, const Layout& o,
+                       hipStream_t s) {
+    Group* groups = at<Group>(ws, o.groups);
+    PlanMeta* meta = at<PlanMeta>(ws, o.meta);
+    SMOE_TRY(launch_plan(offsets, L.n_expert, T, L.k, L.shared_ff > 0, kTileM, groups, meta, s));
+    SMOE_TRY(launch_expert_gemv(L, x, T, perm_token, groups, meta, at<float>(ws, o.H), o.hstride,
+                                y_perm, s));
+    return MOE_OK;
+}
+
+}  // namespace
+}  // namespace smoe
+
+using namespace smoe;
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return 1; }
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape, alignment or dtype/path combination";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_DEVICE: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+moe_status moe_workspace_size(const moe_layer* L, int32_t T, size_t* bytes) {
+    moe_status st = check_layer(L);
+    if (st != MOE_OK) return st;
+    if ((st = check_tokens(T)) != MOE_OK) return st;
+    if (!bytes) return MOE_ERR_ARG;
+    *bytes = layout_for(*L, T).total;
+    return MOE_OK;
+}
+
+moe_status moe_route(const moe_layer* L, const void* x, int32_t T, int32_t* topk_idx,
+                     float* topk_w, float* shared_gate, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_layer(L);
+    if (st != MOE_OK) return st;
+    if ((st = check_tokens(T)) != MOE_OK) return st;
+    if (shared_gate && L->shared_ff == 0) return MOE_ERR_ARG;
+    if (T == 0) return MOE_OK;
+    if (!x || !topk_idx || !topk_w || !ws) return MOE_ERR_ARG;
+    if (!aligned(x, 16)) return MOE_ERR_UNSUPPORTED;
+    const Layout o = layout_for(*L, T);
+    if (ws_bytes < o.total) return MOE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    float* logits = at<float>(ws, o.logits);
+    SMOE_TRY(launch_router_logits(*L, x, T, logits, o.ld, s));
+    SMOE_TRY(launch_topk(*L, logits, o.ld, T, topk_idx, topk_w, shared_gate, s));
+    return MOE_OK;
+}
+
+moe_status moe_permute_workspace_size(int32_t T, int32_t k, int32_t E, size_t* bytes) {
+    if (T < 0 || k < 1 || E < 1 || k > E || !bytes) return MOE_ERR_ARG;
+    if (E > kMaxExperts || k > kMaxK || T > kMaxTokens) return MOE_ERR_UNSUPPORTED;
+    const size_t n_chunks = ((size_t)T + kPermChunk - 1) / kPermChunk;
+    *bytes = 2 * round_up(n_chunks * E * 4 + 4, 256);
+    return MOE_OK;
+}
+
+moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                       int32_t* expert_offsets, int32_t* perm_token, int32_t* perm_inv, void* ws,
+                       size_t ws_bytes, void* stream) {
+    size_t need = 0;
+    moe_status st = moe_permute_workspace_size(T, k, E, &need);
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (!topk_idx || !expert_offsets || !perm_token || !perm_inv || !ws) return MOE_ERR_ARG;
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    int32_t* counts = static_cast<int32_t*>(ws);
+    int32_t* base = at<int32_t>(ws, need / 2);
+    return status_of(launch_permute(topk_idx, T, k, E, expert_offsets, perm_token, perm_inv, counts,
+                                    base, s));
+}
+
+moe_status moe_expert_ffn(const moe_layer* L, const void* x, int32_t T,
+                          const int32_t* expert_offsets, const int32_t* perm_token, float* y_perm,
+                          void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_layer(L);
+    if (st != MOE_OK) return st;
+    if ((st = check_tokens(T)) != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (!x || !expert_offsets || !perm_token || !y_perm || !ws) return MOE_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(y_perm, 16)) return MOE_ERR_UNSUPPORTED;
+    const Layout o = layout_for(*L, T);
+    if (ws_bytes < o.total) return MOE_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    return run_experts(*L, x, T, expert_offsets, perm_token, y_perm, ws, o,
+                       static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_combine(const moe_layer* L, const float* y_perm, const int32_t* perm_inv,
+                       const float* topk_w, const float* shared_gate, int32_t T, void* y,
+                       void* stream) {
+    moe_status st = check_layer(L);
+    if (st != MOE_OK) return st;
+    if ((st = check_tokens(T)) != MOE_OK) return st;
+    if ((shared_gate != nullptr) != (L->shared_ff > 0)) return MOE_ERR_ARG;
+    if (T == 0) return MOE_OK;
+    if (!y_perm || !perm_inv || !topk_w || !y) return MOE_ERR_ARG;
+    if (!aligned(y_perm, 16) || !aligned(y, 16)) return MOE_ERR_UNSUPPORTED;
+    (void)hipGetLastError();
+    return status_of(launch_combine(*L, y_perm, perm_inv, topk_w, shared_gate, T, y,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward(const moe_layer* L, const void* x, int32_t T, void* y, void* ws,
+                       size_t ws_bytes, void* stream) {
+    moe_status st = check_layer(L);
+    if (st != MOE_OK) return st;
+    if ((st = check_tokens(T)) != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (!x || !y || !ws) return MOE_ERR_ARG;
+    if (x == y) return MOE_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 16)) return MOE_ERR_UNSUPPORTED;
+    const Layout o = layout_for(*L, T);
+    if (ws_bytes < o.total) return MOE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const bool shared = L->shared_ff > 0;
+    float* logits = at<float>(ws, o.logits);
+    int32_t* idx = at<int32_t>(ws, o.idx);
+    float* w = at<float>(ws, o.w);
+    float* sg = shared ? at<float>(ws, o.sg) : nullptr;
+    int32_t* offsets = at<int32_t>(ws, o.offsets);
+    int32_t* perm_token = at<int32_t>(ws, o.perm_token);
+    int32_t* perm_inv = at<int32_t>(ws, o.perm_inv);
+    float* y_perm = at<float>(ws, o.yperm);
+    SMOE_TRY(launch_router_logits(*L, x, T, logits, o.ld, s));
+    SMOE_TRY(launch_topk(*L, logits, o.ld, T, idx, w, sg, s));
+    SMOE_TRY(launch_permute(idx, T, L->k, L->n_expert, offsets, perm_token, perm_inv,
+                            at<int32_t>(ws, o.counts), at<int32_t>(ws, o.base), s));
+    st = run_experts(*L, x, T, offsets, perm_token, y_perm, ws, o, s);
+    if (st != MOE_OK) return st;
+    SMOE_TRY(launch_combine(*L, y_perm, perm_inv, w, sg, T, y, s));
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,237 @@
+"""Thin ctypes binding of libsmoe.so (declared in include/moe.h).
+
+Argument marshalling only: torch tensors provide device memory and the current HIP
+stream; every step of the layer runs in the library's kernels.  There is no fallback:
+if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsmoe.so")
+
+MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_ROUTE_SOFTMAX_TOPK_RENORM, MOE_ROUTE_TOPK_SOFTMAX = 0, 1
+MOE_ACT_SWIGLU, MOE_ACT_SWIGLU_OAI = 0, 1
+MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_GROUPED = 0, 1, 2
+
+_ROUTE = {"softmax_topk_renorm": MOE_ROUTE_SOFTMAX_TOPK_RENORM, "topk_softmax": MOE_ROUTE_TOPK_SOFTMAX}
+_ACT = {"swiglu": MOE_ACT_SWIGLU, "swiglu_oai": MOE_ACT_SWIGLU_OAI}
+_PATH = {"auto": MOE_PATH_AUTO, "decode": MOE_PATH_DECODE, "grouped": MOE_PATH_GROUPED}
+
+_P = ctypes.c_void_p
+
+
+class MoeLayer(ctypes.Structure):
+    """Mirror of ``moe_layer`` (9 int32, 3 float, 12 pointers at byte offset 48)."""
+    _fields_ = [
+        ("d", ctypes.c_int32), ("n_expert", ctypes.c_int32), ("ff", ctypes.c_int32),
+        ("k", ctypes.c_int32), ("shared_ff", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("route", ctypes.c_int32), ("act", ctypes.c_int32), ("path", ctypes.c_int32),
+        ("route_scale", ctypes.c_float), ("oai_alpha", ctypes.c_float), ("oai_limit", ctypes.c_float),
+        ("w_router", _P), ("b_router", _P), ("w_gate", _P), ("w_up", _P),
+        ("w_gate_up", _P), ("b_gate_up", _P), ("w_down", _P), ("b_down", _P),
+        ("ws_gate", _P), ("ws_up", _P), ("ws_down", _P), ("ws_gate_inp", _P),
+    ]
+
+
+POINTER_FIELDS = [f for f, t in MoeLayer._fields_ if t is _P]
+EXPORTS = ["moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
+           "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn", "moe_combine",
+           "moe_forward"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_mixture_experts_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, sz, vp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+        pl = ctypes.POINTER(MoeLayer)
+        L.moe_abi_version.restype = i32
+        L.moe_abi_version.argtypes = []
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [i32]
+        L.moe_workspace_size.restype = i32
+        L.moe_workspace_size.argtypes = [pl, i32, ctypes.POINTER(sz)]
+        L.moe_route.restype = i32
+        L.moe_route.argtypes = [pl, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_permute_workspace_size.restype = i32
+        L.moe_permute_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+        L.moe_permute.restype = i32
+        L.moe_permute.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_ffn.restype = i32
+        L.moe_expert_ffn.argtypes = [pl, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_combine.restype = i32
+        L.moe_combine.argtypes = [pl, vp, vp, vp, vp, i32, vp, vp]
+        L.moe_forward.restype = i32
+        L.moe_forward.argtypes = [pl, vp, i32, vp, vp, sz, vp]
+        if L.moe_abi_version() != 1:
+            raise RuntimeError("libsmoe.so ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != MOE_OK:
+        raise MoeError(status, what)
+
+
+# ----------------------------------------------------------------------------- torch side
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def to_device(a: np.ndarray | None, device="cuda"):
+    """A stored numpy tensor (uint16 bf16 bits or float32) as a torch tensor on device."""
+    if a is None:
+        return None
+    torch = _torch()
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+class Layer:
+    """A layer's parameters resident on the device plus the ``moe_layer`` struct that
+    points at them.  Holds references so the tensors outlive the struct."""
+
+    def __init__(self, d, n_expert, ff, k, shared_ff, dtype, route, act, route_scale=1.0,
+                 oai_alpha=1.702, oai_limit=7.0, path="auto", **tensors):
+        self.tensors = dict(tensors)
+        self.d, self.n_expert, self.ff, self.k, self.shared_ff = d, n_expert, ff, k, shared_ff
+        self.dtype = dtype
+        s = MoeLayer()
+        s.d, s.n_expert, s.ff, s.k, s.shared_ff = d, n_expert, ff, k, shared_ff
+        s.dtype = MOE_BF16 if dtype == "bf16" else MOE_F32
+        s.route, s.act, s.path = _ROUTE[route], _ACT[act], _PATH[path]
+        s.route_scale, s.oai_alpha, s.oai_limit = route_scale, oai_alpha, oai_limit
+        for name in POINTER_FIELDS:
+            setattr(s, name, _ptr(self.tensors.get(name)))
+        self.struct = s
+
+    @classmethod
+    def from_arrays(cls, L: dict, device="cuda", path="auto"):
+        """From a layer dict of the input generator (numpy storage arrays)."""
+        tensors = {n: to_device(L.get(n), device) for n in POINTER_FIELDS}
+        return cls(L["d"], L["n_expert"], L["ff"], L["k"], L["shared_ff"], L["dtype"], L["route"],
+                   L["act"], L.get("route_scale", 1.0), L.get("oai_alpha", 1.702),
+                   L.get("oai_limit", 7.0), path=path, **tensors)
+
+    def with_path(self, path: str) -> "Layer":
+        other = Layer.__new__(Layer)
+        other.__dict__.update(self.__dict__)
+        other.struct = MoeLayer.from_buffer_copy(self.struct)
+        other.struct.path = _PATH[path]
+        return other
+
+    @property
+    def torch_dtype(self):
+        torch = _torch()
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def workspace_size(layer: Layer, T: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_size(layer.ref(), int(T), ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def workspace(layer: Layer, T: int, device="cuda"):
+    torch = _torch()
+    return torch.empty(max(workspace_size(layer, T), 1), dtype=torch.uint8, device=device)
+
+
+def route(layer: Layer, x, ws=None):
+    """(topk_idx int32 [T,k], topk_w fp32 [T,k], shared_gate fp32 [T] or None)."""
+    torch = _torch()
+    T = x.shape[0]
+    ws = workspace(layer, T, x.device) if ws is None else ws
+    idx = torch.empty((T, layer.k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, layer.k), dtype=torch.float32, device=x.device)
+    sg = torch.empty(T, dtype=torch.float32, device=x.device) if layer.shared_ff else None
+    _check(lib().moe_route(layer.ref(), _ptr(x), T, _ptr(idx), _ptr(w), _ptr(sg), _ptr(ws),
+                           ws.numel(), _stream()), "moe_route")
+    return idx, w, sg
+
+
+def permute(topk_idx, n_expert: int):
+    """(expert_offsets [E+1], perm_token [T*k], perm_inv [T*k]) int32."""
+    torch = _torch()
+    T, k = topk_idx.shape
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_permute_workspace_size(T, k, n_expert, ctypes.byref(n)), "moe_permute_workspace_size")
+    ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=topk_idx.device)
+    off = torch.empty(n_expert + 1, dtype=torch.int32, device=topk_idx.device)
+    pt = torch.empty(T * k, dtype=torch.int32, device=topk_idx.device)
+    pi = torch.empty(T * k, dtype=torch.int32, device=topk_idx.device)
+    _check(lib().moe_permute(_ptr(topk_idx.contiguous()), T, k, n_expert, _ptr(off), _ptr(pt), _ptr(pi),
+                             _ptr(ws), ws.numel(), _stream()), "moe_permute")
+    return off, pt, pi
+
+
+def expert_ffn(layer: Layer, x, expert_offsets, perm_token, ws=None):
+    """y_perm fp32 [T*k (+T), d]."""
+    torch = _torch()
+    T = x.shape[0]
+    rows = T * layer.k + (T if layer.shared_ff else 0)
+    ws = workspace(layer, T, x.device) if ws is None else ws
+    y = torch.empty((rows, layer.d), dtype=torch.float32, device=x.device)
+    _check(lib().moe_expert_ffn(layer.ref(), _ptr(x), T, _ptr(expert_offsets), _ptr(perm_token),
+                                _ptr(y), _ptr(ws), ws.numel(), _stream()), "moe_expert_ffn")
+    return y
+
+
+def combine(layer: Layer, y_perm, perm_inv, topk_w, shared_gate):
+    torch = _torch()
+    T = topk_w.shape[0]
+    y = torch.empty((T, layer.d), dtype=layer.torch_dtype, device=topk_w.device)
+    _check(lib().moe_combine(layer.ref(), _ptr(y_perm), _ptr(perm_inv), _ptr(topk_w), _ptr(shared_gate),
+                             T, _ptr(y), _stream()), "moe_combine")
+    return y
+
+
+def forward(layer: Layer, x, ws=None, out=None):
+    """The whole layer: y [T, d] in the layer dtype."""
+    torch = _torch()
+    T = x.shape[0]
+    ws = workspace(layer, T, x.device) if ws is None else ws
+    y = torch.empty((T, layer.d), dtype=layer.torch_dtype, device=x.device) if out is None else out
+    _check(lib().moe_forward(layer.ref(), _ptr(x), T, _ptr(y), _ptr(ws), ws.numel(), _stream()),
+           "moe_forward")
+    return y

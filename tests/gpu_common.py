@@ -1,0 +1,55 @@
+"""Shared helpers of the GPU parity tests: seeded cases, uploads and the tolerance rule.
+
+Tolerance (whole-tensor rule): max |got - ref| <= rtol * max |ref| with rtol = 2e-2 for
+bf16 weights (fp32 accumulation) and 1e-4 for fp32.  Routing indices and grouping are
+compared bit-exactly; routing weights within 1e-6 absolute, the shared-gate input within
+1e-4 absolute.
+"""
+import functools
+import sys
+
+import numpy as np
+
+import oracle
+from sparse_mixture_experts_amd import synth
+
+RTOL = {"bf16": 2e-2, "f32": 1e-4}
+W_ATOL = 1e-6
+SG_ATOL = 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = np.max(np.abs(ref)) if ref.size else 0.0
+    if ref.size == 0:
+        return 0.0
+    return float(np.max(np.abs(got - ref)) / (scale if scale > 0 else 1.0))
+
+
+def assert_close(got, ref, dtype, what=""):
+    e = rel_err(got, ref)
+    assert e <= RTOL[dtype], f"{what}: max|err|/max|ref| = {e:.3e} > {RTOL[dtype]}"
+    return e
+
+
+@functools.lru_cache(maxsize=4)
+def layer_arrays(name: str, seed: int = 0, **overrides):
+    return synth.make_layer(synth.spec(name, **dict(overrides)), seed=seed)
+
+
+def case(name, T, seed=0, **overrides):
+    L = layer_arrays(name, seed, **overrides)
+    x = synth.make_tokens(L, T, seed=seed + 100)
+    return L, x
+
+
+def to_numpy_y(y):
+    """A device output tensor as fp64 numpy (bf16 widened exactly)."""
+    import torch
+    return y.detach().to("cpu", torch.float64).numpy()

@@ -1,0 +1,155 @@
+"""The C ABI without a GPU: the library loads, exports every function include/moe.h
+declares, the struct layout matches, and every argument error is reported before any
+HIP call (fake, never-dereferenced pointers are enough)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_mixture_experts_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # 64 KiB-aligned address; the library must never touch it in these tests
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_]+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail("libsmoe.so is not built")
+    return moe.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) == 9, names
+    assert sorted(moe.EXPORTS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout(lib):
+    assert ctypes.sizeof(moe.MoeLayer) == 48 + 12 * 8
+    assert moe.MoeLayer.route_scale.offset == 36
+    assert moe.MoeLayer.w_router.offset == 48
+    assert moe.MoeLayer.ws_gate_inp.offset == 48 + 11 * 8
+
+
+def fake_layer(**kw):
+    s = moe.MoeLayer()
+    s.d, s.n_expert, s.ff, s.k, s.shared_ff = 256, 8, 512, 2, 0
+    s.dtype, s.route, s.act, s.path = moe.MOE_BF16, 0, 0, 0
+    s.route_scale, s.oai_alpha, s.oai_limit = 1.0, 1.702, 7.0
+    s.w_router = s.w_gate = s.w_up = s.w_down = FAKE
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def ws_size(lib, s, T):
+    n = ctypes.c_size_t(0)
+    st = lib.moe_workspace_size(ctypes.byref(s), T, ctypes.byref(n))
+    return st, n.value
+
+
+def fwd(lib, s, T=4, x=FAKE, y=FAKE * 2, ws=FAKE * 3, nbytes=1 << 40):
+    return lib.moe_forward(ctypes.byref(s), x, T, y, ws, nbytes, None)
+
+
+def test_status_strings(lib):
+    assert moe.status_string(0) == "ok"
+    assert "workspace" in moe.status_string(3)
+    assert moe.status_string(99) == "unknown status"
+
+
+def test_workspace_size_grows_with_T(lib):
+    s = fake_layer()
+    st0, n0 = ws_size(lib, s, 1)
+    st1, n1 = ws_size(lib, s, 1000)
+    assert st0 == st1 == 0 and 0 < n0 < n1
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("k", 0, moe.MOE_ERR_ARG), ("k", 9, moe.MOE_ERR_ARG), ("d", 0, moe.MOE_ERR_ARG),
+    ("n_expert", -1, moe.MOE_ERR_ARG), ("shared_ff", -64, moe.MOE_ERR_ARG),
+    ("dtype", 5, moe.MOE_ERR_ARG), ("route", 2, moe.MOE_ERR_ARG), ("act", 7, moe.MOE_ERR_ARG),
+    ("path", 3, moe.MOE_ERR_ARG), ("w_router", None, moe.MOE_ERR_ARG),
+    ("w_gate", None, moe.MOE_ERR_ARG), ("w_down", None, moe.MOE_ERR_ARG),
+    ("route_scale", float("nan"), moe.MOE_ERR_ARG),
+    ("shared_ff", 512, moe.MOE_ERR_ARG),            # shared expert without its pointers
+    ("d", 200, moe.MOE_ERR_UNSUPPORTED), ("ff", 100, moe.MOE_ERR_UNSUPPORTED),
+    ("w_up", FAKE + 2, moe.MOE_ERR_UNSUPPORTED),    # misaligned weights
+    ("b_router", FAKE + 2, moe.MOE_ERR_UNSUPPORTED),
+])
+def test_layer_errors(lib, field, value, status):
+    s = fake_layer(**{field: value})
+    assert fwd(lib, s) == status
+    assert ws_size(lib, s, 4)[0] == status
+
+
+def test_too_many_experts_or_k(lib):
+    assert fwd(lib, fake_layer(n_expert=1024, k=2)) == moe.MOE_ERR_UNSUPPORTED
+    assert fwd(lib, fake_layer(n_expert=64, k=33)) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_oai_needs_fused_weights(lib):
+    s = fake_layer(act=moe.MOE_ACT_SWIGLU_OAI)
+    assert fwd(lib, s) == moe.MOE_ERR_ARG
+    s = fake_layer(act=moe.MOE_ACT_SWIGLU_OAI, w_gate_up=FAKE, b_gate_up=FAKE)
+    assert ws_size(lib, s, 4)[0] == 0
+
+
+def test_grouped_path_needs_bf16(lib):
+    assert fwd(lib, fake_layer(dtype=moe.MOE_F32, path=moe.MOE_PATH_GROUPED)) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_forward_argument_errors(lib):
+    s = fake_layer()
+    assert fwd(lib, s, T=-1) == moe.MOE_ERR_ARG
+    assert fwd(lib, s, T=0) == moe.MOE_OK                     # no-op, nothing launched
+    assert fwd(lib, s, T=0, x=None, y=None, ws=None) == moe.MOE_OK
+    assert fwd(lib, s, x=None) == moe.MOE_ERR_ARG
+    assert fwd(lib, s, y=None) == moe.MOE_ERR_ARG
+    assert fwd(lib, s, ws=None) == moe.MOE_ERR_ARG
+    assert fwd(lib, s, x=FAKE, y=FAKE) == moe.MOE_ERR_ARG      # y aliases x
+    assert fwd(lib, s, x=FAKE + 8) == moe.MOE_ERR_UNSUPPORTED  # misaligned x
+    assert fwd(lib, s, T=1 << 23) == moe.MOE_ERR_UNSUPPORTED
+    _, need = ws_size(lib, s, 4)
+    assert fwd(lib, s, nbytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_forward(None, FAKE, 4, FAKE * 2, FAKE * 3, 1 << 40, None) == moe.MOE_ERR_ARG
+
+
+def test_route_permute_ffn_combine_argument_errors(lib):
+    s = fake_layer()
+    L = ctypes.byref(s)
+    # shared_gate output for a layer without a shared expert
+    assert lib.moe_route(L, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == moe.MOE_ERR_ARG
+    assert lib.moe_route(L, FAKE, 4, None, FAKE, None, FAKE, 1 << 40, None) == moe.MOE_ERR_ARG
+    assert lib.moe_route(L, FAKE, 4, FAKE, FAKE, None, FAKE, 10, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_route(L, FAKE, 0, None, None, None, None, 0, None) == moe.MOE_OK
+    n = ctypes.c_size_t(0)
+    assert lib.moe_permute_workspace_size(4, 3, 2, ctypes.byref(n)) == moe.MOE_ERR_ARG    # k > E
+    assert lib.moe_permute_workspace_size(4, 2, 8, ctypes.byref(n)) == moe.MOE_OK
+    assert lib.moe_permute(FAKE, 4, 2, 8, FAKE, FAKE, FAKE, FAKE, n.value - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_permute(None, 4, 2, 8, FAKE, FAKE, FAKE, FAKE, n.value, None) == moe.MOE_ERR_ARG
+    assert lib.moe_permute(FAKE, -2, 2, 8, FAKE, FAKE, FAKE, FAKE, n.value, None) == moe.MOE_ERR_ARG
+    assert lib.moe_expert_ffn(L, FAKE, 4, None, FAKE, FAKE, FAKE, 1 << 40, None) == moe.MOE_ERR_ARG
+    assert lib.moe_expert_ffn(L, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 10, None) == moe.MOE_ERR_WORKSPACE
+    # combine: shared_gate must be given exactly when the layer has a shared expert
+    assert lib.moe_combine(L, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None) == moe.MOE_ERR_ARG
+    assert lib.moe_combine(L, FAKE, FAKE, None, None, 4, FAKE, None) == moe.MOE_ERR_ARG
+    sh = fake_layer(shared_ff=512, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, ws_gate_inp=FAKE)
+    assert lib.moe_combine(ctypes.byref(sh), FAKE, FAKE, FAKE, None, 4, FAKE, None) == moe.MOE_ERR_ARG
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(moe, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        moe.lib()

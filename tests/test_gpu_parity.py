@@ -1,0 +1,309 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+Small shapes span several blocks/tiles with ragged tails; the full workload shapes are
+covered further down (routing on every token, outputs on every token or on a seeded
+sample when the oracle would take too long).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_mixture_experts_amd import synth
+
+from gpu_common import (SG_ATOL, W_ATOL, assert_close, case, layer_arrays, rel_err, say,
+                        to_numpy_y)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_mixture_experts_amd import moe
+    moe.lib()
+
+
+def moe_mod():
+    from sparse_mixture_experts_amd import moe
+    return moe
+
+
+_DEV = {}
+
+
+def dev_layer(name, seed=0, path="auto", **ov):
+    key = (name, seed, tuple(sorted(ov.items())))
+    if key not in _DEV:
+        if len(_DEV) > 2:
+            _DEV.clear()
+            torch.cuda.empty_cache()
+        _DEV[key] = moe_mod().Layer.from_arrays(layer_arrays(name, seed, **ov))
+    lay = _DEV[key]
+    return lay if path == "auto" else lay.with_path(path)
+
+
+def xdev(x):
+    return moe_mod().to_device(x)
+
+
+# Small shapes: several blocks per kernel and ragged tails (T not a multiple of 4/64).
+SMALL = [
+    ("tiny_f32", {}, [1, 16, 77]),
+    ("qwen", dict(d=512, n_expert=64, ff=192, shared_ff=128), [1, 5, 64, 150]),
+    ("qwen_zipf", dict(d=512, ff=128, shared_ff=192), [300]),
+    ("gptoss", dict(d=320, n_expert=16, ff=192), [1, 7, 100]),
+    ("mixtral", dict(d=256, ff=448), [3, 130]),
+]
+SMALL_CASES = [(n, ov, T) for n, ov, Ts in SMALL for T in Ts]
+
+
+def _id(c):
+    n, ov, T = c
+    return f"{n}-T{T}"
+
+
+@pytest.mark.parametrize("c", SMALL_CASES, ids=_id)
+def test_route(c):
+    name, ov, T = c
+    say("route", name, ov, T)
+    L, x = case(name, T, **ov)
+    lay = dev_layer(name, **ov)
+    idx, w, sg = moe_mod().route(lay, xdev(x))
+    torch.cuda.synchronize()
+    ridx, rw, rsg = oracle.route(L, x)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.max(np.abs(w.cpu().numpy() - rw)) <= W_ATOL
+    if rsg is not None:
+        assert np.max(np.abs(sg.cpu().numpy() - rsg)) <= SG_ATOL
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 8, 256), (64, 8, 256), (65, 8, 256), (1000, 4, 32),
+                                   (4097, 2, 8), (300, 8, 8), (200, 3, 500)])
+def test_permute(T, k, E):
+    say("permute", T, k, E)
+    rng = np.random.default_rng(T * 7 + E)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    off, pt, pi = moe_mod().permute(torch.from_numpy(idx).cuda(), E)
+    torch.cuda.synchronize()
+    counts, roff, rpt, rpi = oracle.permute(idx.astype(np.int64), E)
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(pt.cpu().numpy(), rpt)
+    assert np.array_equal(pi.cpu().numpy(), rpi.reshape(-1))
+
+
+def test_permute_ignores_out_of_range_ids():
+    E, k, T = 16, 2, 70
+    rng = np.random.default_rng(3)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    idx[5, 1] = -3
+    idx[66, 0] = E + 4
+    off, pt, pi = moe_mod().permute(torch.from_numpy(idx).cuda(), E)
+    pi = pi.cpu().numpy()
+    assert pi[5 * k + 1] == -1 and pi[66 * k] == -1
+    assert off.cpu().numpy()[-1] == T * k - 2
+    valid = np.ones(T * k, bool)
+    valid[[5 * k + 1, 66 * k]] = False
+    ref_counts = np.bincount(idx.reshape(-1)[valid], minlength=E)
+    assert np.array_equal(np.diff(off.cpu().numpy()), ref_counts)
+    assert np.array_equal(pt.cpu().numpy()[pi[valid]], np.repeat(np.arange(T), k)[valid])
+
+
+@pytest.mark.parametrize("c", SMALL_CASES, ids=_id)
+def test_expert_ffn(c):
+    name, ov, T = c
+    say("expert_ffn", name, ov, T)
+    L, x = case(name, T, **ov)
+    lay = dev_layer(name, **ov)
+    ridx, _, _ = oracle.route(L, x)
+    _, roff, rpt, _ = oracle.permute(ridx, L["n_expert"])
+    y = moe_mod().expert_ffn(lay, xdev(x), torch.from_numpy(roff.astype(np.int32)).cuda(),
+                            torch.from_numpy(rpt.astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.expert_rows(L, x, roff, rpt)
+    assert_close(y.cpu().numpy(), ref, L["dtype"], "y_perm")
+
+
+@pytest.mark.parametrize("c", SMALL_CASES, ids=_id)
+def test_combine_fed_oracle_rows(c):
+    name, ov, T = c
+    say("combine", name, ov, T)
+    L, x = case(name, T, **ov)
+    lay = dev_layer(name, **ov)
+    ridx, rw, rsg = oracle.route(L, x)
+    _, roff, rpt, rpi = oracle.permute(ridx, L["n_expert"])
+    yp = oracle.expert_rows(L, x, roff, rpt)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    y = moe_mod().combine(lay, f32(yp), torch.from_numpy(rpi.reshape(-1).astype(np.int32)).cuda(),
+                         f32(rw), None if rsg is None else f32(rsg))
+    torch.cuda.synchronize()
+    # inputs rounded to fp32: compare against the oracle's combine of the same rounded rows
+    ref = oracle.combine(yp.astype(np.float32).astype(np.float64), rpi, rw.astype(np.float32),
+                         None if rsg is None else rsg.astype(np.float32))
+    assert_close(to_numpy_y(y), ref, L["dtype"], "combine")
+
+
+@pytest.mark.parametrize("path", ["auto", "decode", "grouped"])
+@pytest.mark.parametrize("c", SMALL_CASES, ids=_id)
+def test_forward(c, path):
+    name, ov, T = c
+    if path == "grouped" and name == "tiny_f32":
+        pytest.skip("grouped path is bf16-only")
+    say("forward", name, ov, T, path)
+    L, x = case(name, T, **ov)
+    lay = dev_layer(name, path=path, **ov)
+    y = moe_mod().forward(lay, xdev(x))
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward(L, x)
+    e = assert_close(to_numpy_y(y), ref, L["dtype"], "y")
+    say(f"  rel err {e:.2e}")
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+def test_zero_tokens():
+    lay = dev_layer("tiny_f32")
+    x = torch.empty((0, 256), dtype=torch.float32, device="cuda")
+    y = moe_mod().forward(lay, x, ws=torch.empty(1, dtype=torch.uint8, device="cuda"))
+    assert y.shape == (0, 256)
+
+
+def _custom(L):
+    return moe_mod().Layer.from_arrays(L)
+
+
+def test_k_equals_E_dense_case():
+    L = dict(layer_arrays("tiny_f32", k=8))
+    x = synth.make_tokens(L, 33, seed=4)
+    y = moe_mod().forward(_custom(L), xdev(x))
+    assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "f32", "k=E")
+
+
+def test_one_expert_takes_every_token():
+    L = dict(layer_arrays("qwen", d=256, n_expert=32, ff=128, shared_ff=64))
+    L["w_router"] = np.zeros_like(L["w_router"])
+    b = np.zeros(32, np.float32)
+    b[13] = 100.0
+    L["b_router"] = b
+    L["k"] = 1
+    x = synth.make_tokens(L, 200, seed=5, gap=0)
+    for path in ("decode", "grouped"):
+        lay = _custom(L).with_path(path)
+        idx, w, _ = moe_mod().route(lay, xdev(x))
+        assert (idx.cpu().numpy() == 13).all() and (w.cpu().numpy() == 1.0).all()
+        y = moe_mod().forward(lay, xdev(x))
+        assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "bf16", path)
+
+
+def test_all_tie_router_bit_exact():
+    L = dict(layer_arrays("qwen", d=256, n_expert=32, ff=128, shared_ff=64))
+    L["w_router"] = np.zeros_like(L["w_router"])
+    x = synth.make_tokens(L, 9, seed=6, gap=0)
+    idx, w, _ = moe_mod().route(_custom(L), xdev(x))
+    assert (idx.cpu().numpy() == np.arange(8)).all()
+    assert (w.cpu().numpy() == np.float32(1.0 / 8)).all()
+
+
+def test_identical_experts():
+    L = dict(layer_arrays("qwen", d=256, n_expert=16, ff=128, shared_ff=64))
+    for n in ("w_gate", "w_up", "w_down"):
+        L[n] = np.broadcast_to(L[n][:1], L[n].shape).copy()
+    x = synth.make_tokens(L, 40, seed=7)
+    y = moe_mod().forward(_custom(L), xdev(x))
+    assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "bf16", "identical experts")
+
+
+def test_oai_clamp_coverage():
+    # Larger gate_up weights so that |gate|, |up| exceed the limit often.
+    sp = synth.spec("gptoss", d=320, n_expert=16, ff=192, weight_std=0.1)
+    L = synth.make_layer(sp, seed=3)
+    x = synth.make_tokens(L, 50, seed=8)
+    xf = synth.storage_to_f32(x).astype(np.float64)
+    v = xf @ synth.storage_to_f32(L["w_gate_up"][0]).astype(np.float64).T
+    assert (v[:, 0::2] > 7).mean() > 0.05 and (np.abs(v[:, 1::2]) > 7).mean() > 0.05
+    for path in ("decode", "grouped"):
+        y = moe_mod().forward(_custom(L).with_path(path), xdev(x))
+        assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "bf16", "clamp " + path)
+
+
+def test_deterministic():
+    L, x = case("qwen", 64, d=512, n_expert=64, ff=192, shared_ff=128)
+    lay = dev_layer("qwen", d=512, n_expert=64, ff=192, shared_ff=128)
+    for path in ("decode", "grouped"):
+        a = moe_mod().forward(lay.with_path(path), xdev(x))
+        b = moe_mod().forward(lay.with_path(path), xdev(x))
+        assert torch.equal(a, b)
+
+
+def test_batch_invariance():
+    # Rows of a batch equal the same tokens run alone (the batched-decode check of the
+    # "Llama Forward Pass" page, applied to the MoE layer).
+    ov = dict(d=512, n_expert=64, ff=192, shared_ff=128)
+    L, x = case("qwen", 100, **ov)
+    lay = dev_layer("qwen", **ov)
+    full = moe_mod().forward(lay, xdev(x))
+    idx_full, _, _ = moe_mod().route(lay, xdev(x))
+    for t in (0, 37, 99):
+        one = moe_mod().forward(lay, xdev(x[t:t + 1]))
+        idx_one, _, _ = moe_mod().route(lay, xdev(x[t:t + 1]))
+        assert torch.equal(idx_one[0], idx_full[t])
+        assert rel_err(to_numpy_y(one)[0], to_numpy_y(full)[t]) <= 2e-2
+
+
+# ----------------------------------------------------------------------------- full sizes
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_full_qwen_decode(T):
+    say("full qwen decode", T)
+    L, x = case("qwen", T)
+    lay = dev_layer("qwen")
+    idx, w, sg = moe_mod().route(lay, xdev(x))
+    y = moe_mod().forward(lay, xdev(x))
+    torch.cuda.synchronize()
+    ridx, rw, rsg = oracle.route(L, x)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.max(np.abs(w.cpu().numpy() - rw)) <= W_ATOL
+    assert np.max(np.abs(sg.cpu().numpy() - rsg)) <= SG_ATOL
+    e = assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "bf16", "y")
+    say(f"  rel err {e:.2e}")
+
+
+def test_full_qwen_prefill_zipf():
+    T = 8192
+    say("full qwen prefill", T)
+    L, x = case("qwen_zipf", T)
+    lay = dev_layer("qwen_zipf")
+    idx, w, sg = moe_mod().route(lay, xdev(x))
+    y = moe_mod().forward(lay, xdev(x))
+    torch.cuda.synchronize()
+    ridx, rw, rsg = oracle.route(L, x)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.max(np.abs(w.cpu().numpy() - rw)) <= W_ATOL
+    counts = np.bincount(ridx.reshape(-1), minlength=256)
+    say("  counts min/median/max", counts.min(), int(np.median(counts)), counts.max())
+    e = assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "bf16", "y")
+    say(f"  rel err {e:.2e}")
+
+
+@pytest.mark.parametrize("name,T,sample", [("gptoss", 1, None), ("gptoss", 4096, 256),
+                                           ("mixtral", 16, None), ("mixtral", 16384, 256)])
+def test_full_other_layers(name, T, sample):
+    say("full", name, T)
+    L, x = case(name, T)
+    lay = dev_layer(name)
+    idx, w, _ = moe_mod().route(lay, xdev(x))
+    y = moe_mod().forward(lay, xdev(x))
+    torch.cuda.synchronize()
+    ridx, rw, _ = oracle.route(L, x)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.max(np.abs(w.cpu().numpy() - rw)) <= W_ATOL
+    yn = to_numpy_y(y)
+    if sample is None:
+        ref, got = oracle.moe_forward(L, x), yn
+    else:
+        tok = np.sort(np.random.default_rng(11).choice(T, sample, replace=False))
+        ref, got = oracle.moe_forward(L, x[tok]), yn[tok]
+    e = assert_close(got, ref, "bf16", "y")
+    say(f"  rel err {e:.2e}")
