@@ -61,7 +61,60 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
 }
 
+// Rows already carry their routing weight (and the shared rows their sigmoid gate):
+// y[t] = sum_{j<k} Y[perm_inv[t,j]] (+ Y[T*k + t]), fp32 sum in the same fixed order.
+template <typename TT>
+__global__ __launch_bounds__(256) void combine_sum_kernel(const uint16_t* __restrict__ y_rows,
+                                                          const int32_t* __restrict__ perm_inv, int T,
+                                                          int k, int d, int shared,
+                                                          typename TT::storage* __restrict__ y) {
+    const int t = blockIdx.x;
+    const int tk = T * k;
+    __shared__ int rows[33];
+    if (threadIdx.x < k) {
+        const int r = perm_inv[(size_t)t * k + threadIdx.x];
+        rows[threadIdx.x] = (r >= 0 && r < tk) ? r : -1;
+    }
+    if (threadIdx.x == 0) rows[k] = shared ? tk + t : -1;
+    __syncthreads();
+    for (int i = threadIdx.x * 8; i < d; i += blockDim.x * 8) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j <= k; ++j) {
+            const int r = rows[j];
+            if (r < 0) continue;
+            float v[8];
+            unpack16<BF16>(ld16(y_rows + (size_t)r * d + i), v);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] += v[q];
+        }
+        if constexpr (sizeof(typename TT::storage) == 2) {
+            uint4 o;
+            o.x = uint32_t(f32_to_bf16(acc[0])) | (uint32_t(f32_to_bf16(acc[1])) << 16);
+            o.y = uint32_t(f32_to_bf16(acc[2])) | (uint32_t(f32_to_bf16(acc[3])) << 16);
+            o.z = uint32_t(f32_to_bf16(acc[4])) | (uint32_t(f32_to_bf16(acc[5])) << 16);
+            o.w = uint32_t(f32_to_bf16(acc[6])) | (uint32_t(f32_to_bf16(acc[7])) << 16);
+            *reinterpret_cast<uint4*>(y + (size_t)t * d + i) = o;
+        } else {
+            float4* o = reinterpret_cast<float4*>(y + (size_t)t * d + i);
+            o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_combine_sum(const moe_layer& L, const uint16_t* y_rows, const int32_t* perm_inv,
+                              int T, void* y, hipStream_t s) {
+    const int shared = L.shared_ff > 0 ? 1 : 0;
+    if (L.dtype == MOE_BF16)
+        combine_sum_kernel<BF16><<<T, 256, 0, s>>>(y_rows, perm_inv, T, L.k, L.d, shared,
+                                                   static_cast<uint16_t*>(y));
+    else
+        combine_sum_kernel<F32><<<T, 256, 0, s>>>(y_rows, perm_inv, T, L.k, L.d, shared,
+                                                  static_cast<float*>(y));
+    return hipGetLastError();
+}
 
 hipError_t launch_combine(const moe_layer& L, const float* y_perm, const int32_t* perm_inv,
                           const float* w, const float* shared_gate, int T, void* y, hipStream_t s) {

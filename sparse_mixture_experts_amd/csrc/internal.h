@@ -11,6 +11,8 @@ namespace smoe {
 
 // Tokens per permute chunk: one 64-bit token mask per expert and chunk.
 constexpr int kPermChunk = 64;
+// Rows per M-tile of the grouped MFMA kernels.
+constexpr int kGroupTileM = 128;
 
 // One group of grouped rows handled by the expert kernels: expert e (-1 = shared
 // expert), its first grouped row, its row count and its first M-tile.
@@ -30,13 +32,27 @@ inline int max_groups(int E, int T, int k, bool shared) {
 
 hipError_t launch_router_logits(const moe_layer& L, const void* x, int T, float* logits, int ld,
                                 hipStream_t s);
+// row_w (optional, [T*k (+T)]): per grouped row routing weight, and sigmoid of the
+// shared gate for the shared rows T*k + t; lets the down GEMM apply the weights.
 hipError_t launch_topk(const moe_layer& L, const float* logits, int ld, int T, int32_t* idx,
-                       float* w, float* shared_gate, hipStream_t s);
+                       float* w, float* shared_gate, float* row_w, hipStream_t s);
+hipError_t launch_decode_route(const moe_layer& L, const float* logits, int ld, int T, int32_t* idx,
+                               float* w, float* shared_gate, int32_t* offsets, int32_t* perm_token,
+                               int32_t* perm_inv, float* row_w, int tile_m, Group* groups,
+                               PlanMeta* meta, int32_t* tile_map, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
                           int32_t* perm_token, int32_t* perm_inv, int32_t* counts, int32_t* base,
-                          hipStream_t s);
+                          const float* w, float* row_w, hipStream_t s);
 hipError_t launch_plan(const int32_t* offsets, int E, int T, int k, bool shared, int tile_m,
-                       Group* groups, PlanMeta* meta, hipStream_t s);
+                       Group* groups, PlanMeta* meta, int32_t* tile_map, hipStream_t s);
+int grouped_max_mtiles(int E, int T, int k, bool shared);
+hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
+                              const Group* groups, const PlanMeta* meta, const int32_t* tile_map,
+                              uint16_t* H, int hstride, const float* row_w, void* y, bool y_bf16,
+                              hipStream_t s);
+// Combine of pre-weighted bf16 rows: y[t] = sum_j Y[perm_inv[t,j]] (+ Y[T*k + t]).
+hipError_t launch_combine_sum(const moe_layer& L, const uint16_t* y_rows, const int32_t* perm_inv,
+                              int T, void* y, hipStream_t s);
 hipError_t launch_expert_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                               const Group* groups, const PlanMeta* meta, float* H, int hstride,
                               float* y_perm, hipStream_t s);

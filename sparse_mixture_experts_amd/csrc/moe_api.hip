@@ -13,14 +13,15 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxK = 32;
 constexpr int32_t kMaxTokens = 1 << 22;
 constexpr int kDecodeMaxT = 64;  // MOE_PATH_AUTO takes the GEMV path up to this T
-constexpr int kTileM = 64;  // M-tile size recorded in the group plan
+constexpr int kTileM = kGroupTileM;  // M-tile size recorded in the group plan
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Byte offsets of every scratch buffer inside the caller's workspace.
 struct Layout {
-    size_t logits, idx, w, sg, counts, base, offsets, perm_token, perm_inv, groups, meta, H, yperm;
+    size_t logits, idx, w, sg, counts, base, offsets, perm_token, perm_inv, groups, meta, tile_map,
+        row_w, H, yperm;
     size_t total;
     int ld, hstride, rows;
 };
@@ -50,6 +51,9 @@ Layout layout_for(const moe_layer& L, int T) {
     o.perm_inv = take(tk * 4);
     o.groups = take(((size_t)L.n_expert + 1) * sizeof(Group));
     o.meta = take(sizeof(PlanMeta));
+    o.tile_map = take((size_t)grouped_max_mtiles(L.n_expert, T, L.k, shared) * 4);
+    o.row_w = take((size_t)o.rows * 4);
+    // H: fp32 on the GEMV path, bf16 on the grouped path (same region).
     o.H = take((size_t)o.rows * o.hstride * 4);
     o.yperm = take((size_t)o.rows * L.d * 4);
     o.total = off;
@@ -105,14 +109,33 @@ inline moe_status status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MO
         if (err_ != hipSuccess) return MOE_ERR_DEVICE; \
     } while (0)
 
+// The grouped MFMA path (bf16 only) or the decode GEMV path.
+bool use_grouped(const moe_layer& L, int T) {
+    if (L.dtype != MOE_BF16) return false;
+    if (L.path == MOE_PATH_GROUPED) return true;
+    return L.path == MOE_PATH_AUTO && T > kDecodeMaxT;
+}
+
+// Expert FFNs over the grouped rows.  `planned`: the group list is already in the
+// workspace (the fused decode routing kernel wrote it).  Grouped path: `row_w` non-null
+// scales each row by its routing weight and `y_bf16` stores bf16 rows; the GEMV path
+// always writes unweighted fp32 rows.
 moe_status run_experts(const moe_layer& L, const void* x, int T, const int32_t* offsets,
-                       const int32_t* perm_token, float* y_perm, void* ws, const Layout& o,
-                       hipStream_t s) {
+                       const int32_t* perm_token, void* y_rows, const float* row_w, bool y_bf16,
+                       void* ws, const Layout& o, bool planned, hipStream_t s) {
     Group* groups = at<Group>(ws, o.groups);
     PlanMeta* meta = at<PlanMeta>(ws, o.meta);
-    SMOE_TRY(launch_plan(offsets, L.n_expert, T, L.k, L.shared_ff > 0, kTileM, groups, meta, s));
-    SMOE_TRY(launch_expert_gemv(L, x, T, perm_token, groups, meta, at<float>(ws, o.H), o.hstride,
-                                y_perm, s));
+    int32_t* tile_map = at<int32_t>(ws, o.tile_map);
+    if (!planned)
+        SMOE_TRY(launch_plan(offsets, L.n_expert, T, L.k, L.shared_ff > 0, kTileM, groups, meta,
+                             tile_map, s));
+    if (use_grouped(L, T)) {
+        SMOE_TRY(launch_grouped_ffn(L, x, T, perm_token, groups, meta, tile_map, at<uint16_t>(ws, o.H),
+                                    o.hstride, row_w, y_rows, y_bf16, s));
+    } else {
+        SMOE_TRY(launch_expert_gemv(L, x, T, perm_token, groups, meta, at<float>(ws, o.H), o.hstride,
+                                    static_cast<float*>(y_rows), s));
+    }
     return MOE_OK;
 }
 
@@ -160,7 +183,7 @@ moe_status moe_route(const moe_layer* L, const void* x, int32_t T, int32_t* topk
     (void)hipGetLastError();
     float* logits = at<float>(ws, o.logits);
     SMOE_TRY(launch_router_logits(*L, x, T, logits, o.ld, s));
-    SMOE_TRY(launch_topk(*L, logits, o.ld, T, topk_idx, topk_w, shared_gate, s));
+    SMOE_TRY(launch_topk(*L, logits, o.ld, T, topk_idx, topk_w, shared_gate, nullptr, s));
     return MOE_OK;
 }
 
@@ -186,7 +209,7 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
     int32_t* counts = static_cast<int32_t*>(ws);
     int32_t* base = at<int32_t>(ws, need / 2);
     return status_of(launch_permute(topk_idx, T, k, E, expert_offsets, perm_token, perm_inv, counts,
-                                    base, s));
+                                    base, nullptr, nullptr, s));
 }
 
 moe_status moe_expert_ffn(const moe_layer* L, const void* x, int32_t T,
@@ -201,7 +224,7 @@ moe_status moe_expert_ffn(const moe_layer* L, const void* x, int32_t T,
     const Layout o = layout_for(*L, T);
     if (ws_bytes < o.total) return MOE_ERR_WORKSPACE;
     (void)hipGetLastError();
-    return run_experts(*L, x, T, expert_offsets, perm_token, y_perm, ws, o,
+    return run_experts(*L, x, T, expert_offsets, perm_token, y_perm, nullptr, false, ws, o, false,
                        static_cast<hipStream_t>(stream));
 }
 
@@ -241,14 +264,27 @@ moe_status moe_forward(const moe_layer* L, const void* x, int32_t T, void* y, vo
     int32_t* offsets = at<int32_t>(ws, o.offsets);
     int32_t* perm_token = at<int32_t>(ws, o.perm_token);
     int32_t* perm_inv = at<int32_t>(ws, o.perm_inv);
-    float* y_perm = at<float>(ws, o.yperm);
+    const bool grouped = use_grouped(*L, T);
+    // Grouped path: rows carry their routing weight and are stored in bf16.
+    float* row_w = grouped ? at<float>(ws, o.row_w) : nullptr;
+    void* y_rows = at<void>(ws, o.yperm);
     SMOE_TRY(launch_router_logits(*L, x, T, logits, o.ld, s));
-    SMOE_TRY(launch_topk(*L, logits, o.ld, T, idx, w, sg, s));
-    SMOE_TRY(launch_permute(idx, T, L->k, L->n_expert, offsets, perm_token, perm_inv,
-                            at<int32_t>(ws, o.counts), at<int32_t>(ws, o.base), s));
-    st = run_experts(*L, x, T, offsets, perm_token, y_perm, ws, o, s);
+    const bool fused_route = T <= kPermChunk;
+    if (fused_route) {
+        SMOE_TRY(launch_decode_route(*L, logits, o.ld, T, idx, w, sg, offsets, perm_token, perm_inv,
+                                     row_w, kTileM, at<Group>(ws, o.groups), at<PlanMeta>(ws, o.meta),
+                                     at<int32_t>(ws, o.tile_map), s));
+    } else {
+        SMOE_TRY(launch_topk(*L, logits, o.ld, T, idx, w, sg, row_w, s));
+        SMOE_TRY(launch_permute(idx, T, L->k, L->n_expert, offsets, perm_token, perm_inv,
+                                at<int32_t>(ws, o.counts), at<int32_t>(ws, o.base), w, row_w, s));
+    }
+    st = run_experts(*L, x, T, offsets, perm_token, y_rows, row_w, grouped, ws, o, fused_route, s);
     if (st != MOE_OK) return st;
-    SMOE_TRY(launch_combine(*L, y_perm, perm_inv, w, sg, T, y, s));
+    if (grouped)
+        SMOE_TRY(launch_combine_sum(*L, static_cast<const uint16_t*>(y_rows), perm_inv, T, y, s));
+    else
+        SMOE_TRY(launch_combine(*L, static_cast<const float*>(y_rows), perm_inv, w, sg, T, y, s));
     return MOE_OK;
 }
 

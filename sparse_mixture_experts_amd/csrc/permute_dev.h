@@ -1,0 +1,92 @@
+// Device helpers of the expert grouping, shared by the permute kernels and the fused
+// decode routing kernel.  See permute.hip for the method.
+#pragma once
+
+#include "common.h"
+#include "internal.h"
+
+namespace smoe {
+
+constexpr int kMaxE = 512;
+
+__device__ __forceinline__ void build_masks(const int32_t* __restrict__ idx, int T, int k, int E,
+                                            int chunk, unsigned long long* mask) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
+    __syncthreads();
+    const int t0 = chunk * kPermChunk;
+    const int n = min(kPermChunk, T - t0) * k;
+    for (int p = threadIdx.x; p < n; p += blockDim.x) {
+        const int tl = p / k;
+        const int e = idx[(size_t)t0 * k + p];
+        if (e >= 0 && e < E) atomicOr(&mask[e], 1ull << tl);
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void scatter_chunk(const int32_t* __restrict__ idx, int T, int k, int E,
+                                              int chunk, const unsigned long long* mask,
+                                              const int32_t* base_row, int32_t* __restrict__ perm_token,
+                                              int32_t* __restrict__ perm_inv, const float* __restrict__ w,
+                                              float* __restrict__ row_w) {
+    const int t0 = chunk * kPermChunk;
+    const int n = min(kPermChunk, T - t0) * k;
+    for (int p = threadIdx.x; p < n; p += blockDim.x) {
+        const int tl = p / k;
+        const size_t flat = (size_t)t0 * k + p;
+        const int e = idx[flat];
+        if (e >= 0 && e < E) {
+            const int rank = __popcll(mask[e] & ((1ull << tl) - 1ull));
+            const int pos = base_row[e] + rank;
+            perm_token[pos] = t0 + tl;
+            perm_inv[flat] = pos;
+            if (row_w) row_w[pos] = w[flat];
+        } else {
+            perm_inv[flat] = -1;
+        }
+    }
+}
+
+// Group list for the expert kernels: every non-empty expert in ascending id, then the
+// shared expert (e = -1) over rows T*k .. T*k+T-1.  tile0 = first M-tile of the group
+// when groups are cut into tiles of tile_m rows; tile_map (optional) gets the group of
+// every M-tile (at most tile_cap entries).
+// Runs on one block with blockDim.x >= E; `tmp` holds blockDim.x / 64 ints of LDS.
+__device__ __forceinline__ void plan_block(const int32_t* offsets, int E, int T, int k, int shared,
+                                           int tile_m, Group* __restrict__ groups,
+                                           PlanMeta* __restrict__ meta, int32_t* __restrict__ tile_map,
+                                           int tile_cap, int* tmp) {
+    const int e = threadIdx.x;
+    // Offsets may come from the caller: clamp them so every group stays inside the
+    // T*k grouped rows whatever they hold.
+    const int tk = T * k;
+    const int row0 = e < E ? min(max(offsets[e], 0), tk) : 0;
+    const int n = e < E ? min(max(offsets[e + 1] - row0, 0), tk - row0) : 0;
+    const int flag = n > 0 ? 1 : 0;
+    const int tiles = n > 0 ? (n + tile_m - 1) / tile_m : 0;
+    int n_active, n_tiles;
+    const int pos = block_exclusive_scan(flag, tmp, &n_active);
+    const int tile0 = block_exclusive_scan(tiles, tmp, &n_tiles);
+    if (flag) {
+        groups[pos] = Group{e, row0, n, tile0};
+        if (tile_map)
+            for (int i = 0; i < tiles && tile0 + i < tile_cap; ++i) tile_map[tile0 + i] = pos;
+    }
+    if (e == 0) {
+        int ng = n_active, nt = n_tiles;
+        if (shared) {
+            groups[ng] = Group{-1, T * k, T, nt};
+            const int st = (T + tile_m - 1) / tile_m;
+            if (tile_map)
+                for (int i = 0; i < st && nt + i < tile_cap; ++i) tile_map[nt + i] = ng;
+            ++ng;
+            nt += st;
+        }
+        meta->n_groups = ng;
+        // Offsets from a caller may overlap; never hand out tiles beyond the map.
+        meta->n_tiles = min(nt, tile_cap);
+        meta->pad0 = meta->pad1 = 0;
+    }
+}
+
+
+}  // namespace smoe

@@ -8,13 +8,14 @@
 #include <math.h>
 
 #include "internal.h"
+#include "permute_dev.h"
+#include "route_dev.h"
 #include "rowdot.h"
 
 namespace smoe {
 namespace {
 
-constexpr int kRouterTokChunk = 64;  // tokens per block along grid.y
-constexpr int kRouterNT = 4;         // tokens per rows_dot call
+constexpr int kRouterNT = 4;  // tokens per rows_dot call
 
 // One wave per router row (rows 0..E-1 are experts, row E the shared gate vector),
 // looping over a chunk of tokens.  Writes logits[t * ld + row].
@@ -22,13 +23,13 @@ template <int KB, typename TT>
 __global__ __launch_bounds__(256) void router_gemv_kernel(
     const typename TT::storage* __restrict__ x, const typename TT::storage* __restrict__ w_router,
     const float* __restrict__ b_router, const typename TT::storage* __restrict__ w_sg, int T, int d,
-    int E, int n_rows, float* __restrict__ logits, int ld) {
+    int E, int n_rows, int tok_chunk, float* __restrict__ logits, int ld) {
     const int row = blockIdx.x * 4 + threadIdx.x / kWave;
     if (row >= n_rows) return;
     const typename TT::storage* const wr[1] = {row < E ? w_router + (size_t)row * d : w_sg};
     const float bias = (row < E && b_router) ? b_router[row] : 0.0f;
-    const int t_end = min(T, (int)(blockIdx.y + 1) * kRouterTokChunk);
-    for (int t0 = blockIdx.y * kRouterTokChunk; t0 < t_end; t0 += kRouterNT) {
+    const int t_end = min(T, (int)(blockIdx.y + 1) * tok_chunk);
+    for (int t0 = blockIdx.y * tok_chunk; t0 < t_end; t0 += kRouterNT) {
         const int nt = min(kRouterNT, t_end - t0);
         const typename TT::storage* ar[kRouterNT];
 #pragma unroll
@@ -43,65 +44,77 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(
     }
 }
 
-// Does (va, ia) rank before (vb, ib)?  Larger logit first, ties to the lower index.
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
-}
-
-constexpr int kMaxPerLane = 8;  // E <= 512
-
 // One wave per token: k rounds of a wave arg-max by xor shuffles, then the weights.
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int ld, int T,
                                                    int E, int k, int mode, float scale,
                                                    int32_t* __restrict__ idx_out,
                                                    float* __restrict__ w_out,
-                                                   float* __restrict__ sg_out) {
+                                                   float* __restrict__ sg_out,
+                                                   float* __restrict__ row_w) {
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
     if (t >= T) return;
-    const int lane = lane_id();
     const float* z = logits + (size_t)t * ld;
-    float v[kMaxPerLane];
-    int id[kMaxPerLane];
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + i * kWave;
-        v[i] = e < E ? z[e] : -INFINITY;
-        id[i] = e < E ? e : INT32_MAX;
-    }
-    float my_v = -INFINITY;
-    int my_i = 0;
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int bi = INT32_MAX;
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-            if (ranks_before(v[i], id[i], bv, bi)) { bv = v[i]; bi = id[i]; }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, kWave);
-            const int oi = __shfl_xor(bi, off, kWave);
-            if (ranks_before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-        }
-        // Non-finite logits can leave no candidate: keep the index in range.
-        if (bi >= E) bi = 0;
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-            if (id[i] == bi) { v[i] = -INFINITY; id[i] = INT32_MAX; }
-        if (lane == j) { my_v = bv; my_i = bi; }
-    }
-    // Weights over the selected logits: exp(z_j - z_0) / sum_j' exp(z_j' - z_0).  In
-    // mode SOFTMAX_TOPK_RENORM the full-softmax denominator cancels in the
-    // renormalisation, so both modes share this form; mode A then applies the scale.
-    const float zmax = __shfl(my_v, 0, kWave);
-    const float ex = lane < k ? expf(my_v - zmax) : 0.0f;
-    const float den = wave_sum(ex);
+    int my_i;
+    float my_w;
+    topk_wave(z, E, k, mode, scale, &my_i, &my_w);
+    const int lane = lane_id();
     if (lane < k) {
-        float w = ex / den;
-        if (mode == MOE_ROUTE_SOFTMAX_TOPK_RENORM) w *= scale;
         idx_out[(size_t)t * k + lane] = my_i;
-        w_out[(size_t)t * k + lane] = w;
+        w_out[(size_t)t * k + lane] = my_w;
     }
-    if (sg_out && lane == 0) sg_out[t] = z[E];
+    if (sg_out && lane == 0) {
+        sg_out[t] = z[E];
+        if (row_w) row_w[(size_t)T * k + t] = 1.0f / (1.0f + expf(-z[E]));
+    }
+}
+
+// Decode (T <= 64): top-k of every token, the expert grouping and the group plan in one
+// block of 1024 threads, so that routing costs one launch after the logits.
+__global__ __launch_bounds__(1024) void decode_route_kernel(
+    const float* __restrict__ logits, int ld, int T, int E, int k, int mode, float scale,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, float* __restrict__ sg_out,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token, int32_t* __restrict__ perm_inv,
+    float* __restrict__ row_w, int shared, int tile_m, Group* __restrict__ groups,
+    PlanMeta* __restrict__ meta, int32_t* __restrict__ tile_map, int tile_cap) {
+    __shared__ float s_w[kPermChunk * 32];
+    __shared__ int32_t s_idx[kPermChunk * 32];
+    __shared__ unsigned long long mask[kMaxE];
+    __shared__ int32_t base_row[kMaxE + 1];
+    __shared__ int tmp[1024 / kWave];
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    for (int t = wave; t < T; t += 1024 / kWave) {
+        const float* z = logits + (size_t)t * ld;
+        int my_i;
+        float my_w;
+        topk_wave(z, E, k, mode, scale, &my_i, &my_w);
+        if (lane < k) {
+            idx_out[(size_t)t * k + lane] = my_i;
+            w_out[(size_t)t * k + lane] = my_w;
+            s_idx[t * k + lane] = my_i;
+            s_w[t * k + lane] = my_w;
+        }
+        if (sg_out && lane == 0) {
+            sg_out[t] = z[E];
+            if (row_w) row_w[T * k + t] = 1.0f / (1.0f + expf(-z[E]));
+        }
+    }
+    __syncthreads();
+    build_masks(s_idx, T, k, E, 0, mask);
+    const int e = threadIdx.x;
+    const int cnt = e < E ? __popcll(mask[e]) : 0;
+    int total;
+    const int off = block_exclusive_scan(cnt, tmp, &total);
+    if (e < E) {
+        base_row[e] = off;
+        offsets[e] = off;
+    }
+    if (e == 0) {
+        base_row[E] = total;
+        offsets[E] = total;
+    }
+    __syncthreads();
+    scatter_chunk(s_idx, T, k, E, 0, mask, base_row, perm_token, perm_inv, s_w, row_w);
+    plan_block(base_row, E, T, k, shared, tile_m, groups, meta, tile_map, tile_cap, tmp);
 }
 
 template <typename TT>
@@ -109,7 +122,10 @@ hipError_t launch_router_t(const moe_layer& L, const void* x, int T, float* logi
                            hipStream_t s) {
     using S = typename TT::storage;
     const int n_rows = L.n_expert + (L.shared_ff > 0 ? 1 : 0);
-    dim3 grid((n_rows + 3) / 4, (T + kRouterTokChunk - 1) / kRouterTokChunk);
+    // Small batches: one 4-token chunk per block row, so that every wave issues its
+    // loads at once; large batches: 64 tokens per block to reuse the router row.
+    const int tok_chunk = T <= 256 ? kRouterNT : 64;
+    dim3 grid((n_rows + 3) / 4, (T + tok_chunk - 1) / tok_chunk);
     const S* xs = static_cast<const S*>(x);
     const S* wr = static_cast<const S*>(L.w_router);
     const S* wsg = static_cast<const S*>(L.ws_gate_inp);
@@ -117,7 +133,8 @@ hipError_t launch_router_t(const moe_layer& L, const void* x, int T, float* logi
 #define SMOE_ROUTER_CASE(KB)                                                                   \
     case KB:                                                                                   \
         router_gemv_kernel<KB, TT><<<grid, 256, 0, s>>>(xs, wr, L.b_router, wsg, T, L.d,        \
-                                                        L.n_expert, n_rows, logits, ld);       \
+                                                        L.n_expert, n_rows, tok_chunk, logits, \
+                                                        ld);                                   \
         break;
         SMOE_ROUTER_CASE(1)
         SMOE_ROUTER_CASE(2)
@@ -130,6 +147,17 @@ hipError_t launch_router_t(const moe_layer& L, const void* x, int T, float* logi
 
 }  // namespace
 
+hipError_t launch_decode_route(const moe_layer& L, const float* logits, int ld, int T, int32_t* idx,
+                               float* w, float* shared_gate, int32_t* offsets, int32_t* perm_token,
+                               int32_t* perm_inv, float* row_w, int tile_m, Group* groups,
+                               PlanMeta* meta, int32_t* tile_map, hipStream_t s) {
+    decode_route_kernel<<<1, 1024, 0, s>>>(logits, ld, T, L.n_expert, L.k, L.route, L.route_scale, idx,
+                                           w, shared_gate, offsets, perm_token, perm_inv, row_w,
+                                           L.shared_ff > 0 ? 1 : 0, tile_m, groups, meta, tile_map,
+                                           grouped_max_mtiles(L.n_expert, T, L.k, L.shared_ff > 0));
+    return hipGetLastError();
+}
+
 hipError_t launch_router_logits(const moe_layer& L, const void* x, int T, float* logits, int ld,
                                 hipStream_t s) {
     return L.dtype == MOE_BF16 ? launch_router_t<BF16>(L, x, T, logits, ld, s)
@@ -137,9 +165,9 @@ hipError_t launch_router_logits(const moe_layer& L, const void* x, int T, float*
 }
 
 hipError_t launch_topk(const moe_layer& L, const float* logits, int ld, int T, int32_t* idx,
-                       float* w, float* shared_gate, hipStream_t s) {
+                       float* w, float* shared_gate, float* row_w, hipStream_t s) {
     topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, ld, T, L.n_expert, L.k, L.route,
-                                             L.route_scale, idx, w, shared_gate);
+                                             L.route_scale, idx, w, shared_gate, row_w);
     return hipGetLastError();
 }
 
