@@ -50,12 +50,19 @@ struct DownArgs {
     int hstride, d, ff, ffs;
 };
 
-template <int KB, typename TT, bool OAI>
+// Group handled by grid row y.  With a shared expert (always the last group, and the
+// one with the most rows) grid row 0 takes it, so its longer work starts first.
+__device__ __forceinline__ int group_of_row(int y, int n_groups, bool has_shared) {
+    return has_shared ? (y == 0 ? n_groups - 1 : y - 1) : y;
+}
+
+// RESIDENT: the whole K axis fits one KB-chunk register batch (chosen at launch).
+template <int KB, typename TT, bool OAI, bool RESIDENT>
 __global__ __launch_bounds__(256) void expert_up_gemv_kernel(UpArgs a) {
     using S = typename TT::storage;
     const PlanMeta meta = *a.meta;
     if ((int)blockIdx.y >= meta.n_groups) return;
-    const Group g = a.groups[blockIdx.y];
+    const Group g = a.groups[group_of_row(blockIdx.y, meta.n_groups, a.ffs > 0)];
     const bool shared = g.e < 0;
     const int ffg = shared ? a.ffs : a.ff;
     const int f0 = (blockIdx.x * 4 + threadIdx.x / kWave) * 2;
@@ -93,6 +100,10 @@ __global__ __launch_bounds__(256) void expert_up_gemv_kernel(UpArgs a) {
     }
     const S* x = static_cast<const S*>(a.x);
     const int lane = lane_id();
+    // Whole K in one register batch: stream the 4 weight rows once and loop over every
+    // row of the group from registers.
+    uint4 wv[RESIDENT ? KB : 1][4];
+    if constexpr (RESIDENT) load_w_batch<4, KB, TT, true>(wrc, a.d, 0, wv);
     for (int tb = 0; tb < g.n; tb += kNT) {
         const int nt = min(kNT, g.n - tb);
         const S* ar[kNT];
@@ -105,10 +116,12 @@ __global__ __launch_bounds__(256) void expert_up_gemv_kernel(UpArgs a) {
         }
         const S* const arc[kNT] = {ar[0], ar[1], ar[2], ar[3]};
         float acc[4][kNT] = {};
-        rows_dot<4, kNT, KB, TT, TT, true>(wrc, arc, nt, a.d, acc);
+        if constexpr (RESIDENT) dot_w_batch<4, kNT, KB, TT, TT>(wv, arc, nt, a.d, 0, acc);
+        else rows_dot<4, kNT, KB, TT, TT, true>(wrc, arc, nt, a.d, acc);
         float h[2][kNT];
 #pragma unroll
         for (int t = 0; t < kNT; ++t) {
+            if (t >= nt) continue;
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
                 if (oai) {
@@ -132,12 +145,12 @@ __global__ __launch_bounds__(256) void expert_up_gemv_kernel(UpArgs a) {
     }
 }
 
-template <int KB, typename TT, bool OAI>
+template <int KB, typename TT, bool OAI, bool RESIDENT>
 __global__ __launch_bounds__(256) void expert_down_gemv_kernel(DownArgs a) {
     using S = typename TT::storage;
     const PlanMeta meta = *a.meta;
     if ((int)blockIdx.y >= meta.n_groups) return;
-    const Group g = a.groups[blockIdx.y];
+    const Group g = a.groups[group_of_row(blockIdx.y, meta.n_groups, a.ffs > 0)];
     const bool shared = g.e < 0;
     const int K = shared ? a.ffs : a.ff;
     const int i0 = (blockIdx.x * 4 + threadIdx.x / kWave) * 4;
@@ -154,6 +167,8 @@ __global__ __launch_bounds__(256) void expert_down_gemv_kernel(DownArgs a) {
         }
     }
     const int lane = lane_id();
+    uint4 wv[RESIDENT ? KB : 1][4];
+    if constexpr (RESIDENT) load_w_batch<4, KB, TT, true>(wr, K, 0, wv);
     for (int tb = 0; tb < g.n; tb += kNT) {
         const int nt = min(kNT, g.n - tb);
         const float* ar[kNT];
@@ -161,12 +176,15 @@ __global__ __launch_bounds__(256) void expert_down_gemv_kernel(DownArgs a) {
         for (int t = 0; t < kNT; ++t) ar[t] = a.H + (size_t)(g.row0 + min(tb + t, g.n - 1)) * a.hstride;
         const float* const arc[kNT] = {ar[0], ar[1], ar[2], ar[3]};
         float acc[4][kNT] = {};
-        rows_dot<4, kNT, KB, TT, F32, true>(wr, arc, nt, K, acc);
+        if constexpr (RESIDENT) dot_w_batch<4, kNT, KB, TT, F32>(wv, arc, nt, K, 0, acc);
+        else rows_dot<4, kNT, KB, TT, F32, true>(wr, arc, nt, K, acc);
         float out[4][kNT];
 #pragma unroll
-        for (int t = 0; t < kNT; ++t)
+        for (int t = 0; t < kNT; ++t) {
+            if (t >= nt) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) out[r][t] = wave_sum(acc[r][t]) + bias[r];
+        }
 #pragma unroll
         for (int t = 0; t < kNT; ++t)
 #pragma unroll
@@ -185,9 +203,13 @@ hipError_t launch_t(const moe_layer& L, const void* x, int T, const int32_t* per
              L.ws_gate, L.ws_up, H, hstride, T, L.d, L.ff, L.shared_ff, L.oai_alpha, L.oai_limit};
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
     dim3 gu((ffmax + 7) / 8, gmax);
+    const bool up_res = chunks(L.d, TT::VEC) <= 8;
     switch (pick_kb(L.d, TT::VEC)) {
-#define SMOE_UP_CASE(KB) \
-    case KB: expert_up_gemv_kernel<KB, TT, OAI><<<gu, 256, 0, s>>>(u); break;
+#define SMOE_UP_CASE(KB)                                                                      \
+    case KB:                                                                                  \
+        if (up_res) expert_up_gemv_kernel<KB, TT, OAI, true><<<gu, 256, 0, s>>>(u);           \
+        else expert_up_gemv_kernel<KB, TT, OAI, false><<<gu, 256, 0, s>>>(u);                 \
+        break;
         SMOE_UP_CASE(1)
         SMOE_UP_CASE(2)
         SMOE_UP_CASE(4)
@@ -196,9 +218,13 @@ hipError_t launch_t(const moe_layer& L, const void* x, int T, const int32_t* per
     }
     DownArgs dn{H, groups, meta, L.w_down, L.b_down, L.ws_down, y_perm, hstride, L.d, L.ff, L.shared_ff};
     dim3 gd((L.d + 15) / 16, gmax);
+    const bool dn_res = chunks(ffmax, TT::VEC) <= 8;
     switch (pick_kb(ffmax, TT::VEC)) {
-#define SMOE_DOWN_CASE(KB) \
-    case KB: expert_down_gemv_kernel<KB, TT, OAI><<<gd, 256, 0, s>>>(dn); break;
+#define SMOE_DOWN_CASE(KB)                                                                    \
+    case KB:                                                                                  \
+        if (dn_res) expert_down_gemv_kernel<KB, TT, OAI, true><<<gd, 256, 0, s>>>(dn);        \
+        else expert_down_gemv_kernel<KB, TT, OAI, false><<<gd, 256, 0, s>>>(dn);              \
+        break;
         SMOE_DOWN_CASE(1)
         SMOE_DOWN_CASE(2)
         SMOE_DOWN_CASE(4)

@@ -86,55 +86,88 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* lds, int row, int col
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(lds + row * LDS_STRIDE + col));
 }
 
+// One pipeline step on K-slice kt, using LDS buffer / register set B (= kt & 1, a
+// compile-time constant so the register arrays are never indexed dynamically).
+template <int B>
+__device__ __forceinline__ void pipeline_step(const uint16_t* const (&a_rows)[4],
+                                              const uint16_t* const (&b_rows)[4], int kt, int nk,
+                                              const int (&brow)[4], uint4 (&ra)[2][4], uint4 (&rb)[2][4],
+                                              uint16_t (&sA)[2][BM * LDS_STRIDE],
+                                              uint16_t (&sB)[2][BN * LDS_STRIDE], floatx4 (&acc)[4][4]) {
+    const int lane = lane_id();
+    const int wm = (threadIdx.x / kWave) >> 1;
+    const int fr = lane & 15, fk = (lane >> 4) * 8;
+    if (kt + 2 < nk) {
+        load_slice(a_rows, (kt + 2) * BK, ra[B]);
+        load_slice(b_rows, (kt + 2) * BK, rb[B]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+        bf16x8 af[4], bfr[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) af[mi] = lds_frag(sA[B], wm * 64 + mi * 16 + fr, kk + fk);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) bfr[ni] = lds_frag(sB[B], brow[ni] + fr, kk + fk);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+        store_slice(sA[B ^ 1], ra[B ^ 1]);
+        store_slice(sB[B ^ 1], rb[B ^ 1]);
+    }
+    __syncthreads();
+}
+
 // acc[mi][ni] += A[64 wave rows] x B[4 x 16 rows given by brow[ni]]^T over K.
+// Slice s (K range [s*BK, (s+1)*BK)) is loaded into registers two steps before it is
+// used (register set s & 1), written to LDS buffer s & 1 one step before, and consumed
+// from LDS: each global load has two steps of MFMA work to arrive.
 __device__ __forceinline__ void mainloop(const uint16_t* const (&a_rows)[4], const uint16_t* const (&b_rows)[4],
                                          int K, const int (&brow)[4], floatx4 (&acc)[4][4]) {
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDS_STRIDE];
     __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDS_STRIDE];
-    const int lane = lane_id();
-    const int wm = (threadIdx.x / kWave) >> 1;
-    const int fr = lane & 15, fk = (lane >> 4) * 8;
-    uint4 ra[4], rb[4];
-    load_slice(a_rows, 0, ra);
-    load_slice(b_rows, 0, rb);
-    store_slice(sA[0], ra);
-    store_slice(sB[0], rb);
-    __syncthreads();
     const int nk = K / BK;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) {
-            load_slice(a_rows, (kt + 1) * BK, ra);
-            load_slice(b_rows, (kt + 1) * BK, rb);
-        }
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
-            bf16x8 af[4], bfr[4];
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) af[mi] = lds_frag(sA[buf], wm * 64 + mi * 16 + fr, kk + fk);
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) bfr[ni] = lds_frag(sB[buf], brow[ni] + fr, kk + fk);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
-        }
-        if (kt + 1 < nk) {
-            store_slice(sA[buf ^ 1], ra);
-            store_slice(sB[buf ^ 1], rb);
-        }
-        __syncthreads();
+    uint4 ra[2][4], rb[2][4];
+    load_slice(a_rows, 0, ra[0]);
+    load_slice(b_rows, 0, rb[0]);
+    if (nk > 1) {
+        load_slice(a_rows, BK, ra[1]);
+        load_slice(b_rows, BK, rb[1]);
     }
+    store_slice(sA[0], ra[0]);
+    store_slice(sB[0], rb[0]);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+        pipeline_step<0>(a_rows, b_rows, kt, nk, brow, ra, rb, sA, sB, acc);
+        if (kt + 1 < nk) pipeline_step<1>(a_rows, b_rows, kt + 1, nk, brow, ra, rb, sA, sB, acc);
+    }
+}
+
+// XCD-aware tile order.  Workgroups are dispatched to the 8 XCDs round-robin by block
+// id, and each XCD has its own L2.  Block b runs slot b / 8 of XCD b % 8; every XCD owns
+// a contiguous range of M-tiles (groups are contiguous in tile order, so an expert spans
+// at most a few XCDs) and runs all N-tiles of one M-tile back to back.  The gathered A
+// tile is then fetched into one L2 and reused by all N-tiles, and an expert's weight
+// slices are reused by its consecutive M-tiles inside the same L2.
+constexpr int kXcds = 8;
+
+inline int grid_blocks(int max_mtiles, int n_ntiles) {
+    return kXcds * ((max_mtiles + kXcds - 1) / kXcds) * n_ntiles;
 }
 
 // Resolve this block's (group, first row, N-tile).  Returns false if the block is idle.
 __device__ __forceinline__ bool locate(const PlanMeta* meta, const int32_t* tile_map, const Group* groups,
                                        int n_ntiles, Group& g, int& m0, int& nt) {
     const int n_tiles = meta->n_tiles;
-    const int mt = blockIdx.x / n_ntiles;
-    nt = blockIdx.x % n_ntiles;
-    if (mt >= n_tiles) return false;
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    const int per_xcd = (n_tiles + kXcds - 1) / kXcds;
+    const int local = slot / n_ntiles;
+    const int mt = xcd * per_xcd + local;
+    nt = slot % n_ntiles;
+    if (local >= per_xcd || mt >= n_tiles) return false;
     g = groups[tile_map[mt]];
     m0 = (mt - g.tile0) * BM;
     return true;
@@ -269,7 +302,61 @@ __global__ __launch_bounds__(kThreads, 2) void gg_down_kernel(DownArgs a) {
     }
 }
 
+// Router logits of a large batch on MFMA: logits[t, e] = x[t] . W_r[e] (+ b[e]) for
+// e < E ("Qwen3.5-MoE Model Implementation", MoE routing; "Phase 19: MoE - gpt-oss-20b",
+// Router).  Same tiling as the down kernel: 128 tokens x 128 experts per block.
+__global__ __launch_bounds__(kThreads, 2) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint16_t* __restrict__ w_router,
+                                                                  const float* __restrict__ b_router,
+                                                                  int T, int d, int E, int n_ntiles,
+                                                                  float* __restrict__ logits, int ld) {
+    const int m0 = (blockIdx.x / n_ntiles) * BM;
+    const int n0 = (blockIdx.x % n_ntiles) * BN;
+    const int r0 = threadIdx.x >> 3;
+    const uint16_t* a_rows[4];
+    const uint16_t* b_rows[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a_rows[i] = x + (size_t)min(m0 + r0 + 32 * i, T - 1) * d;
+        b_rows[i] = w_router + (size_t)min(n0 + r0 + 32 * i, E - 1) * d;
+    }
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int brow[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
+    floatx4 acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* const (&ar)[4] = a_rows;
+    const uint16_t* const (&br)[4] = b_rows;
+    mainloop(ar, br, d, brow, acc);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+        const int n = n0 + wn * 64 + ni * 16 + (lane & 15);
+        if (n >= E) continue;
+        const float bias = b_router ? b_router[n] : 0.0f;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = m0 + wm * 64 + mi * 16 + 4 * (lane >> 4) + i;
+                if (m < T) logits[(size_t)m * ld + n] = acc[mi][ni][i] + bias;
+            }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_router_mfma(const moe_layer& L, const void* x, int T, float* logits, int ld,
+                              hipStream_t s) {
+    const int nn = (L.n_expert + BN - 1) / BN;
+    const int nm = (T + BM - 1) / BM;
+    router_mfma_kernel<<<nm * nn, kThreads, 0, s>>>(static_cast<const uint16_t*>(x),
+                                                    static_cast<const uint16_t*>(L.w_router), L.b_router, T,
+                                                    L.d, L.n_expert, nn, logits, ld);
+    return hipGetLastError();
+}
 
 int grouped_max_mtiles(int E, int T, int k, bool shared) {
     const long long tk = (long long)T * k;
@@ -290,7 +377,7 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
              static_cast<const uint16_t*>(L.w_gate_up), static_cast<const uint16_t*>(L.b_gate_up),
              static_cast<const uint16_t*>(L.ws_gate), static_cast<const uint16_t*>(L.ws_up), H, hstride, T,
              L.d, L.ff, L.shared_ff, ffmax / 64, L.oai_alpha, L.oai_limit};
-    const dim3 gu((unsigned)mt * (ffmax / 64));
+    const dim3 gu((unsigned)grid_blocks(mt, ffmax / 64));
     if (L.act == MOE_ACT_SWIGLU_OAI)
         gg_up_kernel<true><<<gu, kThreads, 0, s>>>(u);
     else
@@ -299,7 +386,7 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
     DownArgs dn{H, groups, meta, tile_map, static_cast<const uint16_t*>(L.w_down),
                 static_cast<const uint16_t*>(L.b_down), static_cast<const uint16_t*>(L.ws_down), row_w, y,
                 hstride, L.d, L.ff, L.shared_ff, nn};
-    const dim3 gd((unsigned)mt * nn);
+    const dim3 gd((unsigned)grid_blocks(mt, nn));
     if (y_bf16)
         gg_down_kernel<uint16_t><<<gd, kThreads, 0, s>>>(dn);
     else

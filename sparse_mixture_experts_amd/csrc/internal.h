@@ -34,8 +34,13 @@ hipError_t launch_router_logits(const moe_layer& L, const void* x, int T, float*
                                 hipStream_t s);
 // row_w (optional, [T*k (+T)]): per grouped row routing weight, and sigmoid of the
 // shared gate for the shared rows T*k + t; lets the down GEMM apply the weights.
+// Router logits on MFMA (bf16, experts only: the shared-gate column is left to top-k).
+hipError_t launch_router_mfma(const moe_layer& L, const void* x, int T, float* logits, int ld,
+                              hipStream_t s);
+// x_sg (optional, bf16 x): top-k computes the shared-gate input w_sg . x itself instead of
+// reading logits column E.
 hipError_t launch_topk(const moe_layer& L, const float* logits, int ld, int T, int32_t* idx,
-                       float* w, float* shared_gate, float* row_w, hipStream_t s);
+                       float* w, float* shared_gate, float* row_w, const void* x_sg, hipStream_t s);
 hipError_t launch_decode_route(const moe_layer& L, const float* logits, int ld, int T, int32_t* idx,
                                float* w, float* shared_gate, int32_t* offsets, int32_t* perm_token,
                                int32_t* perm_inv, float* row_w, int tile_m, Group* groups,

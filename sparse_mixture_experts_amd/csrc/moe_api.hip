@@ -45,7 +45,7 @@ Layout layout_for(const moe_layer& L, int T) {
     o.w = take(tk * 4);
     o.sg = take((size_t)T * 4);
     o.counts = take(n_chunks * L.n_expert * 4);
-    o.base = take(n_chunks * L.n_expert * 4);
+    o.base = take((n_chunks + 1) * L.n_expert * 4);
     o.offsets = take(((size_t)L.n_expert + 1) * 4);
     o.perm_token = take(tk * 4);
     o.perm_inv = take(tk * 4);
@@ -116,6 +116,17 @@ bool use_grouped(const moe_layer& L, int T) {
     return L.path == MOE_PATH_AUTO && T > kDecodeMaxT;
 }
 
+// Large bf16 batches compute the router logits on MFMA (experts only; top-k then forms
+// the shared-gate input itself); otherwise the GEMV router fills every column.
+bool router_on_mfma(const moe_layer& L, int T) { return use_grouped(L, T) && T > kPermChunk; }
+bool router_leaves_shared_gate(const moe_layer& L, int T) {
+    return router_on_mfma(L, T) && L.shared_ff > 0;
+}
+hipError_t run_router(const moe_layer& L, const void* x, int T, float* logits, int ld, hipStream_t s) {
+    return router_on_mfma(L, T) ? launch_router_mfma(L, x, T, logits, ld, s)
+                                : launch_router_logits(L, x, T, logits, ld, s);
+}
+
 // Expert FFNs over the grouped rows.  `planned`: the group list is already in the
 // workspace (the fused decode routing kernel wrote it).  Grouped path: `row_w` non-null
 // scales each row by its routing weight and `y_bf16` stores bf16 rows; the GEMV path
@@ -182,8 +193,9 @@ moe_status moe_route(const moe_layer* L, const void* x, int32_t T, int32_t* topk
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     float* logits = at<float>(ws, o.logits);
-    SMOE_TRY(launch_router_logits(*L, x, T, logits, o.ld, s));
-    SMOE_TRY(launch_topk(*L, logits, o.ld, T, topk_idx, topk_w, shared_gate, nullptr, s));
+    SMOE_TRY(run_router(*L, x, T, logits, o.ld, s));
+    SMOE_TRY(launch_topk(*L, logits, o.ld, T, topk_idx, topk_w, shared_gate, nullptr,
+                         router_leaves_shared_gate(*L, T) ? x : nullptr, s));
     return MOE_OK;
 }
 
@@ -191,7 +203,7 @@ moe_status moe_permute_workspace_size(int32_t T, int32_t k, int32_t E, size_t* b
     if (T < 0 || k < 1 || E < 1 || k > E || !bytes) return MOE_ERR_ARG;
     if (E > kMaxExperts || k > kMaxK || T > kMaxTokens) return MOE_ERR_UNSUPPORTED;
     const size_t n_chunks = ((size_t)T + kPermChunk - 1) / kPermChunk;
-    *bytes = 2 * round_up(n_chunks * E * 4 + 4, 256);
+    *bytes = round_up(n_chunks * E * 4, 256) + round_up((n_chunks + 1) * E * 4, 256);
     return MOE_OK;
 }
 
@@ -206,8 +218,9 @@ moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
     if (ws_bytes < need) return MOE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
+    const size_t n_chunks = ((size_t)T + kPermChunk - 1) / kPermChunk;
     int32_t* counts = static_cast<int32_t*>(ws);
-    int32_t* base = at<int32_t>(ws, need / 2);
+    int32_t* base = at<int32_t>(ws, round_up(n_chunks * E * 4, 256));
     return status_of(launch_permute(topk_idx, T, k, E, expert_offsets, perm_token, perm_inv, counts,
                                     base, nullptr, nullptr, s));
 }
@@ -268,14 +281,15 @@ moe_status moe_forward(const moe_layer* L, const void* x, int32_t T, void* y, vo
     // Grouped path: rows carry their routing weight and are stored in bf16.
     float* row_w = grouped ? at<float>(ws, o.row_w) : nullptr;
     void* y_rows = at<void>(ws, o.yperm);
-    SMOE_TRY(launch_router_logits(*L, x, T, logits, o.ld, s));
+    SMOE_TRY(run_router(*L, x, T, logits, o.ld, s));
     const bool fused_route = T <= kPermChunk;
     if (fused_route) {
         SMOE_TRY(launch_decode_route(*L, logits, o.ld, T, idx, w, sg, offsets, perm_token, perm_inv,
                                      row_w, kTileM, at<Group>(ws, o.groups), at<PlanMeta>(ws, o.meta),
                                      at<int32_t>(ws, o.tile_map), s));
     } else {
-        SMOE_TRY(launch_topk(*L, logits, o.ld, T, idx, w, sg, row_w, s));
+        SMOE_TRY(launch_topk(*L, logits, o.ld, T, idx, w, sg, row_w,
+                             router_leaves_shared_gate(*L, T) ? x : nullptr, s));
         SMOE_TRY(launch_permute(idx, T, L->k, L->n_expert, offsets, perm_token, perm_inv,
                                 at<int32_t>(ws, o.counts), at<int32_t>(ws, o.base), w, row_w, s));
     }

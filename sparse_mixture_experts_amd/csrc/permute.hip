@@ -4,9 +4,9 @@
 //
 // Tokens are cut into chunks of 64.  For each chunk and expert an LDS 64-bit mask marks
 // the chunk's tokens that selected the expert (LDS atomic OR: order-free, so the
-// result is deterministic).  counts = popcount(mask); an exclusive scan over
-// (expert, chunk) gives every chunk's base row per expert; the rank of token t inside
-// its chunk is popcount(mask & bits below t).  A token selects an expert at most once,
+// result is deterministic).  counts = popcount(mask); a scan down each expert's column
+// of chunk counts plus a scan of the expert totals give every chunk's base row per
+// expert; the rank of token t inside its chunk is popcount(mask & bits below t).  A token selects an expert at most once,
 // so this rank is exactly the stable (token-ascending) position.
 //
 // Also here: the plan kernel that turns expert offsets into the list of non-empty
@@ -28,40 +28,52 @@ __global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __res
         counts[(size_t)blockIdx.x * E + e] = __popcll(mask[e]);
 }
 
-// Pass 2 (one block of 512 threads, E <= 512): base[chunk][e] = offsets[e] + rows of
-// expert e in earlier chunks; offsets[E+1] = exclusive scan of the expert totals.
-__global__ __launch_bounds__(512) void permute_scan_kernel(const int32_t* __restrict__ counts,
-                                                           int n_chunks, int E, int32_t* __restrict__ base,
-                                                           int32_t* __restrict__ offsets) {
-    __shared__ int tmp[512 / kWave];
-    const int e = threadIdx.x;
-    int run = 0;
-    if (e < E)
-        for (int c = 0; c < n_chunks; ++c) {
-            const int v = counts[(size_t)c * E + e];
-            base[(size_t)c * E + e] = run;
-            run += v;
-        }
-    int total;
-    const int off = block_exclusive_scan(e < E ? run : 0, tmp, &total);
-    if (e < E) {
-        offsets[e] = off;
-        for (int c = 0; c < n_chunks; ++c) base[(size_t)c * E + e] += off;
+// Pass 2 (one block per expert e): base[chunk][e] = rows of expert e in earlier chunks
+// (a block-wide scan down the column), and totals[e] = rows of expert e (row n_chunks
+// of `base`).
+__global__ __launch_bounds__(256) void permute_colscan_kernel(const int32_t* __restrict__ counts,
+                                                              int n_chunks, int E, int32_t* __restrict__ base) {
+    __shared__ int tmp[256 / kWave];
+    const int e = blockIdx.x;
+    int carry = 0;
+    for (int c0 = 0; c0 < n_chunks; c0 += blockDim.x) {
+        const int c = c0 + threadIdx.x;
+        const int v = c < n_chunks ? counts[(size_t)c * E + e] : 0;
+        int total;
+        const int excl = block_exclusive_scan(v, tmp, &total);
+        if (c < n_chunks) base[(size_t)c * E + e] = carry + excl;
+        carry += total;
     }
-    if (e == 0) offsets[E] = total;
+    if (threadIdx.x == 0) base[(size_t)n_chunks * E + e] = carry;
 }
 
 // Pass 3 (several chunks): stable scatter.
+// Every block first turns the expert totals into offsets (exclusive scan over E <= 512
+// in LDS, two experts per thread); block 0 also writes them out.
 __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t* __restrict__ idx, int T,
-                                                              int k, int E, const int32_t* __restrict__ base,
+                                                              int k, int E, int n_chunks,
+                                                              const int32_t* __restrict__ base,
+                                                              int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ perm_token,
                                                               int32_t* __restrict__ perm_inv,
                                                               const float* __restrict__ w,
                                                               float* __restrict__ row_w) {
     __shared__ unsigned long long mask[kMaxE];
     __shared__ int32_t base_row[kMaxE];
+    __shared__ int tmp[256 / kWave];
     build_masks(idx, T, k, E, blockIdx.x, mask);
-    for (int e = threadIdx.x; e < E; e += blockDim.x) base_row[e] = base[(size_t)blockIdx.x * E + e];
+    const int32_t* totals = base + (size_t)n_chunks * E;
+    const int e0 = 2 * threadIdx.x;
+    const int v0 = e0 < E ? totals[e0] : 0, v1 = e0 + 1 < E ? totals[e0 + 1] : 0;
+    int all;
+    const int off0 = block_exclusive_scan(v0 + v1, tmp, &all);
+    if (e0 < E) base_row[e0] = off0 + base[(size_t)blockIdx.x * E + e0];
+    if (e0 + 1 < E) base_row[e0 + 1] = off0 + v0 + base[(size_t)blockIdx.x * E + e0 + 1];
+    if (blockIdx.x == 0) {
+        if (e0 < E) offsets[e0] = off0;
+        if (e0 + 1 < E) offsets[e0 + 1] = off0 + v0;
+        if (threadIdx.x == 0) offsets[E] = all;
+    }
     __syncthreads();
     scatter_chunk(idx, T, k, E, blockIdx.x, mask, base_row, perm_token, perm_inv, w, row_w);
 }
@@ -109,8 +121,9 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
         return hipGetLastError();
     }
     permute_count_kernel<<<n_chunks, 256, 0, s>>>(idx, T, k, E, counts);
-    permute_scan_kernel<<<1, 512, 0, s>>>(counts, n_chunks, E, base, offsets);
-    permute_scatter_kernel<<<n_chunks, 256, 0, s>>>(idx, T, k, E, base, perm_token, perm_inv, w, row_w);
+    permute_colscan_kernel<<<E, 256, 0, s>>>(counts, n_chunks, E, base);
+    permute_scatter_kernel<<<n_chunks, 256, 0, s>>>(idx, T, k, E, n_chunks, base, offsets, perm_token,
+                                                    perm_inv, w, row_w);
     return hipGetLastError();
 }
 

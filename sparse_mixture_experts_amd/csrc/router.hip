@@ -50,7 +50,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    int32_t* __restrict__ idx_out,
                                                    float* __restrict__ w_out,
                                                    float* __restrict__ sg_out,
-                                                   float* __restrict__ row_w) {
+                                                   float* __restrict__ row_w,
+                                                   const uint16_t* __restrict__ x_sg,
+                                                   const uint16_t* __restrict__ w_sg, int d) {
     const int t = blockIdx.x * 4 + threadIdx.x / kWave;
     if (t >= T) return;
     const float* z = logits + (size_t)t * ld;
@@ -62,9 +64,26 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
         idx_out[(size_t)t * k + lane] = my_i;
         w_out[(size_t)t * k + lane] = my_w;
     }
-    if (sg_out && lane == 0) {
-        sg_out[t] = z[E];
-        if (row_w) row_w[(size_t)T * k + t] = 1.0f / (1.0f + expf(-z[E]));
+    if (sg_out) {
+        float a;
+        if (x_sg) {  // shared-gate input w_sg . x[t], bf16 products, fp32 sum
+            float acc = 0.0f;
+            const uint16_t* xr = x_sg + (size_t)t * d;
+            for (int i = lane * 8; i < d; i += kWave * 8) {
+                float xv[8], wv[8];
+                unpack16<BF16>(ld16(xr + i), xv);
+                unpack16<BF16>(ld16(w_sg + i), wv);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc = fmaf(xv[q], wv[q], acc);
+            }
+            a = wave_sum(acc);
+        } else {
+            a = z[E];
+        }
+        if (lane == 0) {
+            sg_out[t] = a;
+            if (row_w) row_w[(size_t)T * k + t] = 1.0f / (1.0f + expf(-a));
+        }
     }
 }
 
@@ -165,9 +184,11 @@ hipError_t launch_router_logits(const moe_layer& L, const void* x, int T, float*
 }
 
 hipError_t launch_topk(const moe_layer& L, const float* logits, int ld, int T, int32_t* idx,
-                       float* w, float* shared_gate, float* row_w, hipStream_t s) {
+                       float* w, float* shared_gate, float* row_w, const void* x_sg, hipStream_t s) {
     topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, ld, T, L.n_expert, L.k, L.route,
-                                             L.route_scale, idx, w, shared_gate, row_w);
+                                             L.route_scale, idx, w, shared_gate, row_w,
+                                             static_cast<const uint16_t*>(x_sg),
+                                             static_cast<const uint16_t*>(L.ws_gate_inp), L.d);
     return hipGetLastError();
 }
 
