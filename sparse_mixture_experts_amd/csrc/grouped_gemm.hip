@@ -1,25 +1,36 @@
-// Grouped GEMMs of the expert FFNs on bf16 MFMA (the prefill path).
+// Grouped GEMMs of the expert FFNs on bf16 MFMA (the prefill path), and the dense router
+// GEMM of large batches.
 //
 // "Engine" (Cherenkov), Prefill: tokens are grouped by expert, gathered, projected and
 // scattered back; its kernels use token tiles, half-precision weights and float
 // accumulation.  Here every group (one expert's rows, or the shared expert over all
 // tokens) is cut into 128-row M-tiles; a block computes one 128-row tile against one
-// slice of the expert's weights with v_mfma_f32_16x16x32_bf16 and fp32 accumulation.
+// 256-row slice of the expert's weights with v_mfma_f32_16x16x32_bf16 and fp32
+// accumulation.
 //
-// Up kernel: rows of x gathered through perm_token, times the 64 gate rows and the 64
-// matching up rows of a 64-unit slice of the hidden layer (for the clamped variant the
+// Up kernel: rows of x gathered through perm_token, times the 128 gate rows and the 128
+// matching up rows of a 128-unit slice of the hidden layer (for the clamped variant the
 // interleaved gate_up rows are de-interleaved while staging), then the activation of
 // "Qwen3.5-MoE Model Implementation" (silu(gate) * up) or of "Phase 19: MoE -
 // gpt-oss-20b", Experts (biases, clamps, (up + 1) * gate * sigmoid(alpha * gate)) in
 // the epilogue; H is stored in bf16.
-// Down kernel: H rows times a 128-column slice of W_d (+ down bias), optionally scaled
+// Down kernel: H rows times a 256-column slice of W_d (+ down bias), optionally scaled
 // by each row's routing weight (or the shared expert's sigmoid gate) so that the
 // combine is a plain sum; output bf16 or fp32.
 //
-// Block: 256 threads = 4 waves in a 2 x 2 grid, each wave a 64 x 64 output tile =
-// 4 x 4 MFMA tiles.  K advances 64 per step through a double-buffered LDS stage: the
-// next step's global loads are issued before the current step's MFMAs.  LDS rows are
-// padded to 72 bf16 (144 B) so the 16-row fragment reads hit distinct banks.
+// Grouped block: 512 threads = 8 waves in a 2 x 4 grid, each wave a 64 x 64 output tile =
+// 4 x 4 MFMA tiles.  K advances 64 per step through a 3-stage LDS ring filled straight
+// from global memory by global_load_lds_dwordx4 (no register round trip, no LDS store
+// instructions); slice s is issued two steps before it is used, and one barrier per step
+// both publishes slice s and frees the stage that the next issue overwrites.
+// LDS rows are 128 bytes (64 bf16, 8 chunks of 16 B) with chunk c of row r stored at
+// c ^ ((r >> 1) & 7): 16 rows read at one chunk touch 64 distinct banks.  A wave's direct
+// load writes 64 consecutive 16-byte slots (8 rows), so each lane fetches the global
+// chunk that belongs in its slot.  Epilogues go through LDS so that every lane stores
+// whole 16-byte chunks of output rows.
+//
+// The router GEMM (128 tokens x 128 experts per block) keeps a 4-wave, register-staged
+// pipeline: with E = 256 experts a 256-wide tile would leave too few blocks.
 #include "common.h"
 #include "internal.h"
 
@@ -28,12 +39,155 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int BM = kGroupTileM;  // rows per M-tile
-constexpr int BN = 128;          // weight rows per block
-constexpr int BK = 64;           // K per pipeline step
-constexpr int LDS_STRIDE = BK + 8;
-constexpr int kThreads = 256;
+
+__device__ __forceinline__ float ld_bf16(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// LDS row layouts.  Rows of 64 bf16 (8 chunks of 16 B): chunk c of row r at
+// c ^ ((r >> 1) & 7).  Rows of 32 bf16 (4 chunks): chunk c of row r at c ^ ((r >> 2) & 3).
+// Either way 16 rows read at one logical chunk cover 64 distinct banks.
+template <int KW>
+__device__ __forceinline__ int swz(int r, int c) {
+    if constexpr (KW == 64) return r * 64 + ((c ^ ((r >> 1) & 7)) << 3);
+    else return r * 32 + ((c ^ ((r >> 2) & 3)) << 3);
+}
+
+template <int KW>
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* lds, int row, int chunk) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(lds + swz<KW>(row, chunk)));
+}
+
+template <int MI, int NI>
+__device__ __forceinline__ void zero(floatx4 (&acc)[MI][NI]) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = floatx4{0.f, 0.f, 0.f, 0.f};
+}
+
+// 32 K of one wave's 64 x 64 tile: 4 A and 4 B fragments from LDS, 16 MFMAs.
+// Fragment layout of v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16 of its
+// 16-row block and the 8 K values of chunk (l / 16); A and B use the same chunk map, so
+// the order of K inside the 32 does not matter.
+template <int KW>
+__device__ __forceinline__ void mfma_k32(const uint16_t* sa, const uint16_t* sb, int arow0,
+                                         const int (&brow)[4], int kc, floatx4 (&acc)[4][4]) {
+    const int lane = lane_id();
+    const int fr = lane & 15, fc = lane >> 4;
+    bf16x8 af[4], bfr[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) af[mi] = lds_frag<KW>(sa, arow0 + mi * 16 + fr, kc + fc);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) bfr[ni] = lds_frag<KW>(sb, brow[ni] + fr, kc + fc);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt: no wait): this lane's vector-memory ops but the
+// newest N are done, and all of its LDS ops are.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (whose release would
+// drain the direct loads still in flight); the memory clobber keeps the compiler from
+// moving LDS accesses across it.  Ordering of the direct LDS loads is by wait_vm_lgkm.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// =====================================================================================
+// Grouped GEMM: 8 waves, 128 x 256 block tile, direct-to-LDS 3-stage ring, K = 32 per
+// step (64-byte LDS rows), 72 KB of LDS per block so that two blocks share a CU.
+// =====================================================================================
+constexpr int GBN = 256;
+constexpr int GBK = 32;
+constexpr int kGThreads = 512;
+constexpr int kStages = 3;
+constexpr int kRowsPerSeg = 1024 / (GBK * 2);  // LDS rows per 1 KB direct-load segment
+constexpr int kChunksPerRow = GBK / 8;
+constexpr int kSegA = BM / kRowsPerSeg;         // segments per A slice
+constexpr int kSegB = GBN / kRowsPerSeg;        // ... per B slice
+constexpr int kLoadsA = kSegA / 8, kLoadsB = kSegB / 8;  // per wave (8 waves)
+constexpr int kLoads = kLoadsA + kLoadsB;                  // direct loads per lane per slice
+
+constexpr int kUpStage = 128 + 8;       // bf16 H tile 128 x 128
+constexpr int kDownStageH = GBN + 8;    // bf16 output tile 128 x 256
+constexpr int kDownStageF = GBN / 2 + 4;  // fp32 output tile, one 128-column half at a time
+
+struct GSmem {
+    union {
+        struct {
+            uint16_t a[kStages][BM * GBK];
+            uint16_t b[kStages][GBN * GBK];
+        } k;
+        uint16_t up[BM * kUpStage];
+        uint16_t down_h[BM * kDownStageH];
+        float down_f[BM * kDownStageF];
+    };
+};
+
+// Source pointers of this lane's direct loads: A segments w + 8j, B segments w + 8j
+// (segment s holds tile rows s * kRowsPerSeg ..).  row_a / row_b map a tile row to its
+// global row.
+struct LoadPlan {
+    const uint16_t* src[kLoads];
+};
+
+template <typename RowA, typename RowB>
+__device__ __forceinline__ LoadPlan make_plan(RowA row_a, RowB row_b) {
+    LoadPlan p;
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const bool is_a = j < kLoadsA;
+        const int seg = wave + 8 * (is_a ? j : j - kLoadsA);
+        const int r = seg * kRowsPerSeg + lane / kChunksPerRow;
+        const int slot = lane % kChunksPerRow;
+        const int c = slot ^ ((r >> 2) & 3);  // logical chunk that belongs in this slot
+        p.src[j] = (is_a ? row_a(r) : row_b(r)) + c * 8;
+    }
+    return p;
+}
+
+__device__ __forceinline__ void issue_slice(GSmem& sm, const LoadPlan& p, int stage, int k0) {
+    const int wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const bool is_a = j < kLoadsA;
+        const int seg = wave + 8 * (is_a ? j : j - kLoadsA);
+        uint16_t* dst = is_a ? &sm.k.a[stage][seg * 512] : &sm.k.b[stage][seg * 512];  // 1 KB
+        __builtin_amdgcn_global_load_lds(p.src[j] + k0, (lds_ptr_t)dst, 16, 0, 0);
+    }
+}
+
+// acc += A[wave rows] x B[rows brow[ni] + 0..15]^T over K.  Step kt: wait for this lane's
+// loads of slice kt, barrier (everyone's slice kt has landed and everyone has finished
+// step kt-1, whose stage the next issue reuses), issue slice kt+2 (clamped near the end,
+// so the body stays uniform), compute slice kt.  Ends with all loads drained and a
+// barrier, so the caller may reuse the LDS.
+__device__ __forceinline__ void grouped_mainloop(GSmem& sm, const LoadPlan& p, int K, int arow0,
+                                                 const int (&brow)[4], floatx4 (&acc)[4][4]) {
+    const int nk = K / GBK;
+    issue_slice(sm, p, 0, 0);
+    issue_slice(sm, p, 1, min(1, nk - 1) * GBK);
+    int st = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vm_lgkm<kLoads>();
+        lds_barrier();
+        const int pre = st == 0 ? 2 : st - 1;  // (kt + 2) % 3
+        issue_slice(sm, p, pre, min(kt + 2, nk - 1) * GBK);
+        mfma_k32<GBK>(sm.k.a[st], sm.k.b[st], arow0, brow, 0, acc);
+        st = st == 2 ? 0 : st + 1;
+    }
+    wait_vm_lgkm<0>();
+    __syncthreads();
+}
 
 struct UpArgs {
     const uint16_t* x;
@@ -65,87 +219,6 @@ struct DownArgs {
     int hstride, d, ff, ffs, n_ntiles;
 };
 
-__device__ __forceinline__ float ld_bf16(const uint16_t* p) { return bf16_to_f32(*p); }
-
-// Stage one BK-wide slice: this thread's 4 rows (tile rows tid/8 + 32 i) at chunk tid%8.
-__device__ __forceinline__ void load_slice(const uint16_t* const (&rows)[4], int k0, uint4 (&r)[4]) {
-    const int c = (threadIdx.x & 7) * 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = ld16(rows[i] + k0 + c);
-}
-
-__device__ __forceinline__ void store_slice(uint16_t* lds, const uint4 (&r)[4]) {
-    const int c = (threadIdx.x & 7) * 8;
-    const int r0 = threadIdx.x >> 3;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4*>(lds + (r0 + 32 * i) * LDS_STRIDE + c) = r[i];
-}
-
-__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* lds, int row, int col) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(lds + row * LDS_STRIDE + col));
-}
-
-// One pipeline step on K-slice kt, using LDS buffer / register set B (= kt & 1, a
-// compile-time constant so the register arrays are never indexed dynamically).
-template <int B>
-__device__ __forceinline__ void pipeline_step(const uint16_t* const (&a_rows)[4],
-                                              const uint16_t* const (&b_rows)[4], int kt, int nk,
-                                              const int (&brow)[4], uint4 (&ra)[2][4], uint4 (&rb)[2][4],
-                                              uint16_t (&sA)[2][BM * LDS_STRIDE],
-                                              uint16_t (&sB)[2][BN * LDS_STRIDE], floatx4 (&acc)[4][4]) {
-    const int lane = lane_id();
-    const int wm = (threadIdx.x / kWave) >> 1;
-    const int fr = lane & 15, fk = (lane >> 4) * 8;
-    if (kt + 2 < nk) {
-        load_slice(a_rows, (kt + 2) * BK, ra[B]);
-        load_slice(b_rows, (kt + 2) * BK, rb[B]);
-    }
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-        bf16x8 af[4], bfr[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) af[mi] = lds_frag(sA[B], wm * 64 + mi * 16 + fr, kk + fk);
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) bfr[ni] = lds_frag(sB[B], brow[ni] + fr, kk + fk);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-        store_slice(sA[B ^ 1], ra[B ^ 1]);
-        store_slice(sB[B ^ 1], rb[B ^ 1]);
-    }
-    __syncthreads();
-}
-
-// acc[mi][ni] += A[64 wave rows] x B[4 x 16 rows given by brow[ni]]^T over K.
-// Slice s (K range [s*BK, (s+1)*BK)) is loaded into registers two steps before it is
-// used (register set s & 1), written to LDS buffer s & 1 one step before, and consumed
-// from LDS: each global load has two steps of MFMA work to arrive.
-__device__ __forceinline__ void mainloop(const uint16_t* const (&a_rows)[4], const uint16_t* const (&b_rows)[4],
-                                         int K, const int (&brow)[4], floatx4 (&acc)[4][4]) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDS_STRIDE];
-    const int nk = K / BK;
-    uint4 ra[2][4], rb[2][4];
-    load_slice(a_rows, 0, ra[0]);
-    load_slice(b_rows, 0, rb[0]);
-    if (nk > 1) {
-        load_slice(a_rows, BK, ra[1]);
-        load_slice(b_rows, BK, rb[1]);
-    }
-    store_slice(sA[0], ra[0]);
-    store_slice(sB[0], rb[0]);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-        pipeline_step<0>(a_rows, b_rows, kt, nk, brow, ra, rb, sA, sB, acc);
-        if (kt + 1 < nk) pipeline_step<1>(a_rows, b_rows, kt + 1, nk, brow, ra, rb, sA, sB, acc);
-    }
-}
-
 // XCD-aware tile order.  Workgroups are dispatched to the 8 XCDs round-robin by block
 // id, and each XCD has its own L2.  Block b runs slot b / 8 of XCD b % 8; every XCD owns
 // a contiguous range of M-tiles (groups are contiguous in tile order, so an expert spans
@@ -174,55 +247,51 @@ __device__ __forceinline__ bool locate(const PlanMeta* meta, const int32_t* tile
 }
 
 template <bool OAI>
-__global__ __launch_bounds__(kThreads, 2) void gg_up_kernel(UpArgs a) {
+__global__ __launch_bounds__(kGThreads, 2) void gg_up_kernel(UpArgs a) {
+    __shared__ GSmem sm;
     Group g;
     int m0, nt;
     if (!locate(a.meta, a.tile_map, a.groups, a.n_ntiles, g, m0, nt)) return;
     const bool shared = g.e < 0;
     const int ffg = shared ? a.ffs : a.ff;
-    const int f0 = nt * 64;
+    const int f0 = nt * 128;
     if (f0 >= ffg) return;
     const bool oai = OAI && !shared;
     const size_t d = a.d;
-    const int r0 = threadIdx.x >> 3;
 
-    const uint16_t* a_rows[4];
-    const uint16_t* b_rows[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = min(m0 + r0 + 32 * i, g.n - 1);  // ragged tail: re-read the last row
+    // Tile rows of A: gathered token rows (ragged tail re-reads the last row).  Tile rows
+    // of B: 0..127 gate units f0.., 128..255 up units f0.. (units past ffg re-read the last).
+    auto row_a = [&](int r) {
+        const int m = min(m0 + r, g.n - 1);
         int tok = shared ? m : a.perm_token[g.row0 + m];
         tok = min(max(tok, 0), a.T - 1);
-        a_rows[i] = a.x + (size_t)tok * d;
-        const int j = r0 + 32 * (i & 1);  // hidden unit within the slice
-        const bool up = i >= 2;
-        if (oai) {
-            b_rows[i] = a.w_gate_up + ((size_t)g.e * 2 * a.ff + 2 * (f0 + j) + (up ? 1 : 0)) * d;
-        } else {
-            const uint16_t* base = shared ? (up ? a.ws_up : a.ws_gate)
-                                          : (up ? a.w_up : a.w_gate) + (size_t)g.e * a.ff * d;
-            b_rows[i] = base + (size_t)(f0 + j) * d;
-        }
-    }
+        return a.x + (size_t)tok * d;
+    };
+    auto row_b = [&](int r) {
+        const bool up = r >= 128;
+        const int f = min(f0 + (r & 127), ffg - 1);
+        if (oai) return a.w_gate_up + ((size_t)g.e * 2 * a.ff + 2 * f + (up ? 1 : 0)) * d;
+        const uint16_t* base = shared ? (up ? a.ws_up : a.ws_gate)
+                                      : (up ? a.w_up : a.w_gate) + (size_t)g.e * a.ff * d;
+        return base + (size_t)f * d;
+    };
+    const LoadPlan plan = make_plan(row_a, row_b);
     const int lane = lane_id(), wave = threadIdx.x / kWave;
-    const int wm = wave >> 1, wn = wave & 1;
-    // B tile rows: 0..63 gate units, 64..127 up units; wave n-tiles 0,1 gate, 2,3 up.
-    const int brow[4] = {wn * 32, wn * 32 + 16, 64 + wn * 32, 64 + wn * 32 + 16};
+    const int wm = wave >> 2, wn = wave & 3;
+    // Wave n-tiles 0,1 are gate units wn*32.., 2,3 the matching up units.
+    const int brow[4] = {wn * 32, wn * 32 + 16, 128 + wn * 32, 128 + wn * 32 + 16};
     floatx4 acc[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t* const (&ar)[4] = a_rows;
-    const uint16_t* const (&br)[4] = b_rows;
-    mainloop(ar, br, a.d, brow, acc);
+    zero(acc);
+    grouped_mainloop(sm, plan, a.d, wm * 64, brow, acc);
 
-    // Epilogue: lane holds D[4*(lane/16) + i][lane%16] of each 16x16 tile.
+    // Epilogue: lane holds D[4*(lane/16) + i][lane%16] of each 16x16 tile.  Activation,
+    // bf16, staged in LDS as the 128 x 128 H tile.
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
-        const int f = f0 + wn * 32 + ni * 16 + (lane & 15);
+        const int fl = wn * 32 + ni * 16 + (lane & 15);
         float bg = 0.f, bu = 0.f;
         if (oai) {
+            const int f = min(f0 + fl, ffg - 1);
             bg = ld_bf16(a.b_gate_up + (size_t)g.e * 2 * a.ff + 2 * f);
             bu = ld_bf16(a.b_gate_up + (size_t)g.e * 2 * a.ff + 2 * f + 1);
         }
@@ -230,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 2) void gg_up_kernel(UpArgs a) {
         for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int m = m0 + wm * 64 + mi * 16 + 4 * (lane >> 4) + i;
+                const int ml = wm * 64 + mi * 16 + 4 * (lane >> 4) + i;
                 float gv = acc[mi][ni][i], uv = acc[mi][ni + 2][i], h;
                 if (oai) {
                     gv = fminf(gv + bg, a.limit);
@@ -239,41 +308,43 @@ __global__ __launch_bounds__(kThreads, 2) void gg_up_kernel(UpArgs a) {
                 } else {
                     h = gv * sigmoidf_(gv) * uv;
                 }
-                if (m < g.n) a.H[(size_t)(g.row0 + m) * a.hstride + f] = f32_to_bf16(h);
+                sm.up[ml * kUpStage + fl] = f32_to_bf16(h);
             }
         }
+    }
+    __syncthreads();
+    // 128 rows x 16 chunks; 512 threads = 32 rows per pass.
+    const int c = threadIdx.x & 15;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int ml = (threadIdx.x >> 4) + 32 * p;
+        if (m0 + ml < g.n && f0 + c * 8 < ffg)
+            *reinterpret_cast<uint4*>(a.H + (size_t)(g.row0 + m0 + ml) * a.hstride + f0 + c * 8) =
+                *reinterpret_cast<const uint4*>(sm.up + ml * kUpStage + c * 8);
     }
 }
 
 template <typename TY>
-__global__ __launch_bounds__(kThreads, 2) void gg_down_kernel(DownArgs a) {
+__global__ __launch_bounds__(kGThreads, 2) void gg_down_kernel(DownArgs a) {
+    __shared__ GSmem sm;
     Group g;
     int m0, nt;
     if (!locate(a.meta, a.tile_map, a.groups, a.n_ntiles, g, m0, nt)) return;
     const bool shared = g.e < 0;
     const int K = shared ? a.ffs : a.ff;
-    const int n0 = nt * BN;
-    const int r0 = threadIdx.x >> 3;
-    const uint16_t* a_rows[4];
-    const uint16_t* b_rows[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = min(m0 + r0 + 32 * i, g.n - 1);
-        a_rows[i] = a.H + (size_t)(g.row0 + m) * a.hstride;
-        const int n = min(n0 + r0 + 32 * i, a.d - 1);  // partial last N-tile: re-read
-        b_rows[i] = shared ? a.ws_down + (size_t)n * K : a.w_down + ((size_t)g.e * a.d + n) * K;
-    }
+    const int n0 = nt * GBN;
+    auto row_a = [&](int r) { return a.H + (size_t)(g.row0 + min(m0 + r, g.n - 1)) * a.hstride; };
+    auto row_b = [&](int r) {
+        const int n = min(n0 + r, a.d - 1);  // partial last N-tile: re-read
+        return shared ? a.ws_down + (size_t)n * K : a.w_down + ((size_t)g.e * a.d + n) * K;
+    };
+    const LoadPlan plan = make_plan(row_a, row_b);
     const int lane = lane_id(), wave = threadIdx.x / kWave;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int brow[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
     floatx4 acc[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t* const (&ar)[4] = a_rows;
-    const uint16_t* const (&br)[4] = b_rows;
-    mainloop(ar, br, K, brow, acc);
+    zero(acc);
+    grouped_mainloop(sm, plan, K, wm * 64, brow, acc);
 
     float rw[4][4];
 #pragma unroll
@@ -283,35 +354,111 @@ __global__ __launch_bounds__(kThreads, 2) void gg_down_kernel(DownArgs a) {
             const int m = min(m0 + wm * 64 + mi * 16 + 4 * (lane >> 4) + i, g.n - 1);
             rw[mi][i] = a.row_w ? a.row_w[g.row0 + m] : 1.0f;
         }
+    constexpr bool kHalf = sizeof(TY) == 2;
+    // bf16: the whole 128 x 256 tile is staged at once; fp32: two 128-column halves (the
+    // waves with wn < 2, then the others), each followed by coalesced 16-byte stores.
+    constexpr int kHalves = kHalf ? 1 : 2;
+    constexpr int kCols = GBN / kHalves;
+    constexpr int kStride = kHalf ? kDownStageH : kDownStageF;
+    constexpr int kChunks = kCols * (int)sizeof(TY) / 16;
+    constexpr int kPer = 16 / (int)sizeof(TY);
+    constexpr int kRowsPerPass = kGThreads / kChunks;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-        const int n = n0 + wn * 64 + ni * 16 + (lane & 15);
-        if (n >= a.d) continue;
-        const float bias = (!shared && a.b_down) ? ld_bf16(a.b_down + (size_t)g.e * a.d + n) : 0.0f;
+    for (int h = 0; h < kHalves; ++h) {
+        if (kHalves == 1 || (wn >> 1) == h) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+            for (int ni = 0; ni < 4; ++ni) {
+                const int nl = wn * 64 + ni * 16 + (lane & 15);
+                const int n = min(n0 + nl, a.d - 1);
+                const float bias = (!shared && a.b_down) ? ld_bf16(a.b_down + (size_t)g.e * a.d + n) : 0.0f;
+                const int sc = nl - h * kCols;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = m0 + wm * 64 + mi * 16 + 4 * (lane >> 4) + i;
-                if (m >= g.n) continue;
-                const float v = (acc[mi][ni][i] + bias) * rw[mi][i];
-                const size_t o = (size_t)(g.row0 + m) * a.d + n;
-                if constexpr (sizeof(TY) == 2) static_cast<uint16_t*>(a.y)[o] = f32_to_bf16(v);
-                else static_cast<float*>(a.y)[o] = v;
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int ml = wm * 64 + mi * 16 + 4 * (lane >> 4) + i;
+                        const float v = (acc[mi][ni][i] + bias) * rw[mi][i];
+                        if constexpr (kHalf) sm.down_h[ml * kStride + sc] = f32_to_bf16(v);
+                        else sm.down_f[ml * kStride + sc] = v;
+                    }
             }
+        }
+        __syncthreads();
+        const int c = threadIdx.x % kChunks;
+#pragma unroll
+        for (int p = 0; p < BM / kRowsPerPass; ++p) {
+            const int ml = threadIdx.x / kChunks + kRowsPerPass * p;
+            const int n = n0 + h * kCols + c * kPer;
+            if (m0 + ml < g.n && n < a.d) {
+                TY* dst = static_cast<TY*>(a.y) + (size_t)(g.row0 + m0 + ml) * a.d + n;
+                uint4 v;
+                if constexpr (kHalf) v = *reinterpret_cast<const uint4*>(sm.down_h + ml * kStride + c * kPer);
+                else v = *reinterpret_cast<const uint4*>(sm.down_f + ml * kStride + c * kPer);
+                *reinterpret_cast<uint4*>(dst) = v;
+            }
+        }
+        if (h + 1 < kHalves) __syncthreads();
     }
+}
+
+// =====================================================================================
+// Router GEMM: 4 waves, 128 x 128 block tile, register-staged double-buffered LDS.
+// =====================================================================================
+constexpr int RBN = 128;
+constexpr int RBK = 64;
+constexpr int kRThreads = 256;
+
+struct RSmem {
+    uint16_t a[2][BM * RBK];
+    uint16_t b[2][RBN * RBK];
+};
+
+// This thread's 4 rows (tile rows tid/8 + 32 i) at chunk tid%8.
+__device__ __forceinline__ void load_slice(const uint16_t* const (&rows)[4], int k0, uint4 (&r)[4]) {
+    const int c = (threadIdx.x & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = ld16(rows[i] + k0 + c);
+}
+
+__device__ __forceinline__ void store_slice(uint16_t* lds, const uint4 (&r)[4]) {
+    const int c = threadIdx.x & 7;
+    const int r0 = threadIdx.x >> 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(lds + swz<RBK>(r0 + 32 * i, c)) = r[i];
+}
+
+// One step on K-slice kt with buffer / register set B (compile-time, so register arrays
+// are never indexed dynamically).  Straight-line on purpose: the prefetch (slice kt+2,
+// clamped) and the store (slice kt+1; a dead store into the idle buffer on the last step)
+// are unconditional, and a scheduling fence keeps the prefetch above the store, so the
+// wait before the store leaves this step's prefetch in flight.
+template <int B>
+__device__ __forceinline__ void router_step(RSmem& sm, const uint16_t* const (&a_rows)[4],
+                                            const uint16_t* const (&b_rows)[4], int kt, int nk, int arow0,
+                                            const int (&brow)[4], uint4 (&ra)[2][4], uint4 (&rb)[2][4],
+                                            floatx4 (&acc)[4][4]) {
+    const int pre = min(kt + 2, nk - 1) * RBK;
+    load_slice(a_rows, pre, ra[B]);
+    load_slice(b_rows, pre, rb[B]);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_k32<RBK>(sm.a[B], sm.b[B], arow0, brow, 0, acc);
+    mfma_k32<RBK>(sm.a[B], sm.b[B], arow0, brow, 4, acc);
+    store_slice(sm.a[B ^ 1], ra[B ^ 1]);
+    store_slice(sm.b[B ^ 1], rb[B ^ 1]);
+    __syncthreads();
 }
 
 // Router logits of a large batch on MFMA: logits[t, e] = x[t] . W_r[e] (+ b[e]) for
 // e < E ("Qwen3.5-MoE Model Implementation", MoE routing; "Phase 19: MoE - gpt-oss-20b",
-// Router).  Same tiling as the down kernel: 128 tokens x 128 experts per block.
-__global__ __launch_bounds__(kThreads, 2) void router_mfma_kernel(const uint16_t* __restrict__ x,
-                                                                  const uint16_t* __restrict__ w_router,
-                                                                  const float* __restrict__ b_router,
-                                                                  int T, int d, int E, int n_ntiles,
-                                                                  float* __restrict__ logits, int ld) {
+// Router).
+__global__ __launch_bounds__(kRThreads, 2) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                   const uint16_t* __restrict__ w_router,
+                                                                   const float* __restrict__ b_router,
+                                                                   int T, int d, int E, int n_ntiles,
+                                                                   float* __restrict__ logits, int ld) {
+    __shared__ RSmem sm;
     const int m0 = (blockIdx.x / n_ntiles) * BM;
-    const int n0 = (blockIdx.x % n_ntiles) * BN;
+    const int n0 = (blockIdx.x % n_ntiles) * RBN;
     const int r0 = threadIdx.x >> 3;
     const uint16_t* a_rows[4];
     const uint16_t* b_rows[4];
@@ -324,13 +471,24 @@ __global__ __launch_bounds__(kThreads, 2) void router_mfma_kernel(const uint16_t
     const int wm = wave >> 1, wn = wave & 1;
     const int brow[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
     floatx4 acc[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = floatx4{0.f, 0.f, 0.f, 0.f};
+    zero(acc);
     const uint16_t* const (&ar)[4] = a_rows;
     const uint16_t* const (&br)[4] = b_rows;
-    mainloop(ar, br, d, brow, acc);
+    const int nk = d / RBK;
+    uint4 ra[2][4], rb[2][4];
+    load_slice(ar, 0, ra[0]);
+    load_slice(br, 0, rb[0]);
+    load_slice(ar, min(1, nk - 1) * RBK, ra[1]);
+    load_slice(br, min(1, nk - 1) * RBK, rb[1]);
+    store_slice(sm.a[0], ra[0]);
+    store_slice(sm.b[0], rb[0]);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        router_step<0>(sm, ar, br, kt, nk, wm * 64, brow, ra, rb, acc);
+        router_step<1>(sm, ar, br, kt + 1, nk, wm * 64, brow, ra, rb, acc);
+    }
+    if (kt < nk) router_step<0>(sm, ar, br, kt, nk, wm * 64, brow, ra, rb, acc);
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
         const int n = n0 + wn * 64 + ni * 16 + (lane & 15);
@@ -350,11 +508,11 @@ __global__ __launch_bounds__(kThreads, 2) void router_mfma_kernel(const uint16_t
 
 hipError_t launch_router_mfma(const moe_layer& L, const void* x, int T, float* logits, int ld,
                               hipStream_t s) {
-    const int nn = (L.n_expert + BN - 1) / BN;
+    const int nn = (L.n_expert + RBN - 1) / RBN;
     const int nm = (T + BM - 1) / BM;
-    router_mfma_kernel<<<nm * nn, kThreads, 0, s>>>(static_cast<const uint16_t*>(x),
-                                                    static_cast<const uint16_t*>(L.w_router), L.b_router, T,
-                                                    L.d, L.n_expert, nn, logits, ld);
+    router_mfma_kernel<<<nm * nn, kRThreads, 0, s>>>(static_cast<const uint16_t*>(x),
+                                                     static_cast<const uint16_t*>(L.w_router), L.b_router,
+                                                     T, L.d, L.n_expert, nn, logits, ld);
     return hipGetLastError();
 }
 
@@ -372,25 +530,26 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
     const bool shared = L.shared_ff > 0;
     const int mt = grouped_max_mtiles(L.n_expert, T, L.k, shared);
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
+    const int nn_up = (ffmax + 127) / 128;
     UpArgs u{static_cast<const uint16_t*>(x), perm_token, groups, meta, tile_map,
              static_cast<const uint16_t*>(L.w_gate), static_cast<const uint16_t*>(L.w_up),
              static_cast<const uint16_t*>(L.w_gate_up), static_cast<const uint16_t*>(L.b_gate_up),
              static_cast<const uint16_t*>(L.ws_gate), static_cast<const uint16_t*>(L.ws_up), H, hstride, T,
-             L.d, L.ff, L.shared_ff, ffmax / 64, L.oai_alpha, L.oai_limit};
-    const dim3 gu((unsigned)grid_blocks(mt, ffmax / 64));
+             L.d, L.ff, L.shared_ff, nn_up, L.oai_alpha, L.oai_limit};
+    const dim3 gu((unsigned)grid_blocks(mt, nn_up));
     if (L.act == MOE_ACT_SWIGLU_OAI)
-        gg_up_kernel<true><<<gu, kThreads, 0, s>>>(u);
+        gg_up_kernel<true><<<gu, kGThreads, 0, s>>>(u);
     else
-        gg_up_kernel<false><<<gu, kThreads, 0, s>>>(u);
-    const int nn = (L.d + BN - 1) / BN;
+        gg_up_kernel<false><<<gu, kGThreads, 0, s>>>(u);
+    const int nn = (L.d + GBN - 1) / GBN;
     DownArgs dn{H, groups, meta, tile_map, static_cast<const uint16_t*>(L.w_down),
                 static_cast<const uint16_t*>(L.b_down), static_cast<const uint16_t*>(L.ws_down), row_w, y,
                 hstride, L.d, L.ff, L.shared_ff, nn};
     const dim3 gd((unsigned)grid_blocks(mt, nn));
     if (y_bf16)
-        gg_down_kernel<uint16_t><<<gd, kThreads, 0, s>>>(dn);
+        gg_down_kernel<uint16_t><<<gd, kGThreads, 0, s>>>(dn);
     else
-        gg_down_kernel<float><<<gd, kThreads, 0, s>>>(dn);
+        gg_down_kernel<float><<<gd, kGThreads, 0, s>>>(dn);
     return hipGetLastError();
 }
 
