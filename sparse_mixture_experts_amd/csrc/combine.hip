@@ -21,27 +21,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int k, int d, typename TT::storage* __restrict__ y) {
     const int t = blockIdx.x;
     const int tk = T * k;
-    __shared__ int rows[32];
-    __shared__ float wts[32];
+    __shared__ int rows[40];  // k <= 32, read in batches of 8
+    __shared__ float wts[40];
     __shared__ float sg;
-    if (threadIdx.x < k) {
-        const int r = perm_inv[(size_t)t * k + threadIdx.x];
+    if (threadIdx.x < 40) {
+        int r = -1;
+        float wv = 0.0f;
+        if (threadIdx.x < k) {
+            r = perm_inv[(size_t)t * k + threadIdx.x];
+            wv = w[(size_t)t * k + threadIdx.x];
+        }
         rows[threadIdx.x] = (r >= 0 && r < tk) ? r : -1;
-        wts[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+        wts[threadIdx.x] = wv;
     }
     if (threadIdx.x == 0) sg = shared_gate ? 1.0f / (1.0f + expf(-shared_gate[t])) : 0.0f;
     __syncthreads();
     for (int i = threadIdx.x * 4; i < d; i += blockDim.x * 4) {
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < k; ++j) {
-            const int r = rows[j];
-            if (r < 0) continue;
-            const float4 v = *reinterpret_cast<const float4*>(y_perm + (size_t)r * d + i);
-            const float wj = wts[j];
-            acc.x = fmaf(wj, v.x, acc.x);
-            acc.y = fmaf(wj, v.y, acc.y);
-            acc.z = fmaf(wj, v.z, acc.z);
-            acc.w = fmaf(wj, v.w, acc.w);
+        // Up to 8 rows per batch, all loads issued before the FMAs; a missing row (-1)
+        // reads row 0 with weight 0.
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            float4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int r = (j0 + u < k) ? rows[j0 + u] : -1;
+                v[u] = *reinterpret_cast<const float4*>(y_perm + (size_t)max(r, 0) * d + i);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const bool ok = j0 + u < k && rows[j0 + u] >= 0;
+                const float wj = ok ? wts[j0 + u] : 0.0f;
+                acc.x = fmaf(wj, v[u].x, acc.x);
+                acc.y = fmaf(wj, v[u].y, acc.y);
+                acc.z = fmaf(wj, v[u].z, acc.z);
+                acc.w = fmaf(wj, v[u].w, acc.w);
+            }
         }
         if (shared_gate) {
             const float4 v = *reinterpret_cast<const float4*>(y_perm + (size_t)(tk + t) * d + i);
@@ -70,22 +84,37 @@ __global__ __launch_bounds__(256) void combine_sum_kernel(const uint16_t* __rest
                                                           typename TT::storage* __restrict__ y) {
     const int t = blockIdx.x;
     const int tk = T * k;
-    __shared__ int rows[33];
-    if (threadIdx.x < k) {
-        const int r = perm_inv[(size_t)t * k + threadIdx.x];
-        rows[threadIdx.x] = (r >= 0 && r < tk) ? r : -1;
+    __shared__ int rows[40];  // k + 1 <= 33 rows, read in batches of 8
+    if (threadIdx.x < 40) {
+        int r = -1;
+        if (threadIdx.x < k) {
+            r = perm_inv[(size_t)t * k + threadIdx.x];
+            r = (r >= 0 && r < tk) ? r : -1;
+        } else if (threadIdx.x == k && shared) {
+            r = tk + t;
+        }
+        rows[threadIdx.x] = r;
     }
-    if (threadIdx.x == 0) rows[k] = shared ? tk + t : -1;
     __syncthreads();
     for (int i = threadIdx.x * 8; i < d; i += blockDim.x * 8) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j <= k; ++j) {
-            const int r = rows[j];
-            if (r < 0) continue;
-            float v[8];
-            unpack16<BF16>(ld16(y_rows + (size_t)r * d + i), v);
+        // Rows j = 0..k (k+1 = shared), up to 8 per batch with the loads issued first; a
+        // missing row reads row 0 and is not added.
+        for (int j0 = 0; j0 <= k; j0 += 8) {
+            uint4 v[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc[q] += v[q];
+            for (int u = 0; u < 8; ++u) {
+                const int r = (j0 + u <= k) ? rows[j0 + u] : -1;
+                v[u] = ld16(y_rows + (size_t)max(r, 0) * d + i);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (j0 + u > k || rows[j0 + u] < 0) continue;
+                float f[8];
+                unpack16<BF16>(v[u], f);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[q] += f[q];
+            }
         }
         if constexpr (sizeof(typename TT::storage) == 2) {
             uint4 o;

@@ -15,8 +15,6 @@
 namespace smoe {
 namespace {
 
-constexpr int kRouterNT = 4;  // tokens per rows_dot call
-
 // One wave per router row (rows 0..E-1 are experts, row E the shared gate vector),
 // looping over a chunk of tokens.  Writes logits[t * ld + row].
 template <int KB, typename TT>
@@ -26,22 +24,8 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(
     int E, int n_rows, int tok_chunk, float* __restrict__ logits, int ld) {
     const int row = blockIdx.x * 4 + threadIdx.x / kWave;
     if (row >= n_rows) return;
-    const typename TT::storage* const wr[1] = {row < E ? w_router + (size_t)row * d : w_sg};
-    const float bias = (row < E && b_router) ? b_router[row] : 0.0f;
-    const int t_end = min(T, (int)(blockIdx.y + 1) * tok_chunk);
-    for (int t0 = blockIdx.y * tok_chunk; t0 < t_end; t0 += kRouterNT) {
-        const int nt = min(kRouterNT, t_end - t0);
-        const typename TT::storage* ar[kRouterNT];
-#pragma unroll
-        for (int t = 0; t < kRouterNT; ++t) ar[t] = x + (size_t)min(t0 + t, T - 1) * d;
-        float acc[1][kRouterNT] = {};
-        rows_dot<1, kRouterNT, KB, TT, TT>(wr, ar, nt, d, acc);
-#pragma unroll
-        for (int t = 0; t < kRouterNT; ++t) {
-            const float z = wave_sum(acc[0][t]);
-            if (lane_id() == 0 && t < nt) logits[(size_t)(t0 + t) * ld + row] = z + bias;
-        }
-    }
+    const int t0 = blockIdx.y * tok_chunk;
+    router_row_wave<KB, TT>(x, w_router, b_router, w_sg, T, d, E, row, t0, min(T, t0 + tok_chunk), logits, ld);
 }
 
 // One wave per token: k rounds of a wave arg-max by xor shuffles, then the weights.
