@@ -63,29 +63,57 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
 
-// ---------------------------------------------------------------- block scan
-// Exclusive prefix sum of one int per thread over the whole block (blockDim.x <= 1024,
-// a multiple of 64).  `tmp` must hold blockDim.x / 64 ints of LDS.  Returns the
-// exclusive prefix; *total receives the block total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+// ---------------------------------------------------------------- scans
+// Inclusive prefix sum over the wave through DPP: shifts right by 1, 2, 4 and 8 lanes
+// inside each 16-lane row (lanes without a source add the zero `old`), then the row
+// broadcasts add row 0's total into row 1, row 2's into row 3, and rows 0-1's into rows
+// 2-3.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+    return v;
+}
+
+// Exclusive prefix sums of N ints per thread over the whole block (blockDim.x <= 1024, a
+// multiple of 64), all N in one pass.  `tmp` must hold N * blockDim.x / 64 ints of LDS.
+// excl[i] receives the exclusive prefix of v[i], total[i] the block total.
+template <int N>
+__device__ __forceinline__ void block_exclusive_scan_n(const int (&v)[N], int* tmp, int (&excl)[N],
+                                                       int (&total)[N]) {
     const int lane = lane_id(), wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
-    int incl = v;
+    int incl[N];
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        int o = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += o;
-    }
-    if (lane == kWave - 1) tmp[wave] = incl;
-    __syncthreads();
-    int wave_base = 0, all = 0;
-    for (int w = 0; w < nw; ++w) {
-        int s = tmp[w];
-        if (w < wave) wave_base += s;
-        all += s;
+    for (int i = 0; i < N; ++i) {
+        incl[i] = wave_inclusive_sum(v[i]);
+        if (lane == kWave - 1) tmp[i * nw + wave] = incl[i];
     }
     __syncthreads();
-    *total = all;
-    return wave_base + incl - v;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        int wave_base = 0, all = 0;
+        for (int w = 0; w < nw; ++w) {
+            const int s = tmp[i * nw + w];
+            if (w < wave) wave_base += s;
+            all += s;
+        }
+        excl[i] = wave_base + incl[i] - v[i];
+        total[i] = all;
+    }
+    __syncthreads();
+}
+
+// One value per thread: returns the exclusive prefix, *total the block total.  `tmp` must
+// hold blockDim.x / 64 ints of LDS.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+    const int in[1] = {v};
+    int ex[1], tot[1];
+    block_exclusive_scan_n<1>(in, tmp, ex, tot);
+    *total = tot[0];
+    return ex[0];
 }
 
 }  // namespace smoe

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(512) void plan_kernel(const int32_t* __restrict__ o
                                                    int k, int shared, int tile_m, Group* __restrict__ groups,
                                                    PlanMeta* __restrict__ meta,
                                                    int32_t* __restrict__ tile_map, int tile_cap) {
-    __shared__ int tmp[512 / kWave];
+    __shared__ int tmp[2 * 512 / kWave];
     plan_block(offsets, E, T, k, shared, tile_m, groups, meta, tile_map, tile_cap, tmp);
 }
 

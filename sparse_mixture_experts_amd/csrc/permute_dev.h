@@ -50,7 +50,7 @@ __device__ __forceinline__ void scatter_chunk(const int32_t* __restrict__ idx, i
 // shared expert (e = -1) over rows T*k .. T*k+T-1.  tile0 = first M-tile of the group
 // when groups are cut into tiles of tile_m rows; tile_map (optional) gets the group of
 // every M-tile (at most tile_cap entries).
-// Runs on one block with blockDim.x >= E; `tmp` holds blockDim.x / 64 ints of LDS.
+// Runs on one block with blockDim.x >= E; `tmp` holds 2 * blockDim.x / 64 ints of LDS.
 __device__ __forceinline__ void plan_block(const int32_t* offsets, int E, int T, int k, int shared,
                                            int tile_m, Group* __restrict__ groups,
                                            PlanMeta* __restrict__ meta, int32_t* __restrict__ tile_map,
@@ -63,9 +63,10 @@ __device__ __forceinline__ void plan_block(const int32_t* offsets, int E, int T,
     const int n = e < E ? min(max(offsets[e + 1] - row0, 0), tk - row0) : 0;
     const int flag = n > 0 ? 1 : 0;
     const int tiles = n > 0 ? (n + tile_m - 1) / tile_m : 0;
-    int n_active, n_tiles;
-    const int pos = block_exclusive_scan(flag, tmp, &n_active);
-    const int tile0 = block_exclusive_scan(tiles, tmp, &n_tiles);
+    const int in[2] = {flag, tiles};
+    int ex[2], tot[2];
+    block_exclusive_scan_n<2>(in, tmp, ex, tot);
+    const int pos = ex[0], tile0 = ex[1], n_active = tot[0], n_tiles = tot[1];
     if (flag) {
         groups[pos] = Group{e, row0, n, tile0};
         if (tile_map)

@@ -39,87 +39,89 @@ __device__ __forceinline__ void router_row_wave(const typename TT::storage* __re
     }
 }
 
-// Does (va, ia) rank before (vb, ib)?  Larger logit first, ties to the lower index.
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
+// Order-preserving 32-bit key of a logit: unsigned comparison of keys is the float order
+// (-0 and +0 share one key, as they compare equal).  NaN gets key 1, below every other
+// value (-inf included) and above key 0, which marks retired and absent entries.
+__device__ __forceinline__ unsigned logit_key(float v) {
+    v = v + 0.0f;  // -0 -> +0
+    unsigned u = __float_as_uint(v);
+    u ^= static_cast<unsigned>(static_cast<int>(u) >> 31) | 0x80000000u;
+    return v != v ? 1u : u;
 }
 
-// Lane moves inside 16-lane rows (DPP): quad permutes [1,0,3,2] and [2,3,0,1], the
-// half-row mirror (lane i <- 7-i within 8) and the row mirror (lane i <- 15-i).
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+__device__ __forceinline__ float key_logit(unsigned key) {
+    const unsigned u = (key >> 31) ? (key & 0x7FFFFFFFu) : ~key;
+    return key == 1u ? __uint_as_float(0x7FC00000u) : __uint_as_float(u);
 }
 
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& v, int& i) {
-    const float ov = __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
-    const int oi = dpp_i<CTRL>(i);
-    if (ranks_before(ov, oi, v, i)) {
-        v = ov;
-        i = oi;
-    }
+// Lane-to-lane max through DPP.  The zero `old` operand is the identity of unsigned max,
+// which lets the compiler fold each move into one v_max_u32_dpp.  Inside 16-lane rows:
+// quad permutes [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors leave every
+// lane with its row's max; the two row broadcasts (lane 15 into rows 1 and 3, lane 31
+// into rows 2 and 3) carry the wave max to lane 63.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ unsigned dpp_max(unsigned m) {
+    return max(m, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(m), CTRL, ROW_MASK,
+                                                                      0xF, false)));
 }
 
-// Wave-wide best (value, index) under ranks_before, returned to every lane: four DPP
-// steps make each 16-lane row uniform, then the four row winners are read and compared.
-// The order is strict (indices are distinct), so both sides of every step agree.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-    argmax_step<0xB1>(v, i);
-    argmax_step<0x4E>(v, i);
-    argmax_step<0x141>(v, i);
-    argmax_step<0x140>(v, i);
-    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r) {
-        const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
-        const int ri = __builtin_amdgcn_readlane(i, 16 * r);
-        if (ranks_before(rv, ri, bv, bi)) {
-            bv = rv;
-            bi = ri;
-        }
-    }
-    v = bv;
-    i = bi;
+__device__ __forceinline__ unsigned wave_max_key(unsigned m) {
+    m = dpp_max<0xB1>(m);
+    m = dpp_max<0x4E>(m);
+    m = dpp_max<0x141>(m);
+    m = dpp_max<0x140>(m);
+    m = dpp_max<0x142, 0xA>(m);
+    m = dpp_max<0x143, 0xC>(m);
+    return static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(m), 63));
 }
 
-constexpr int kMaxPerLane = 8;  // E <= 512
-
-// Called by a whole wave for one token's logits z[0..E).  Lane j < k receives the j-th
-// selected expert (descending logit, ties to the lower index) and its weight.
-// Selection: k rounds; each lane keeps the best of its E/64 logits, a wave arg-max finds
-// the wave's best, whose owner retires it.
+// Top-k of one token's logits z[0..E) on one wave (E <= 64 * PL).  Lane j < k returns
+// the j-th selected expert (descending logit, ties to the lower index) and its weight.
+// Selection: k rounds of a wave max over the keys; the lowest expert index holding the
+// max (ballot per register slot, expert = lane + 64 * slot) is taken and retired.
 // Weights: exp(z_j - z_0) / sum_j' exp(z_j' - z_0) over the k selected.  In mode
 // SOFTMAX_TOPK_RENORM the full-softmax denominator cancels in the renormalisation, so
 // both modes share this form; that mode then applies the expert weight scale.
-__device__ __forceinline__ void topk_wave(const float* z, int E, int k, int mode, float scale,
-                                          int* out_i, float* out_w) {
+// Requires 1 <= k <= min(E, 64).
+template <int PL>
+__device__ __forceinline__ void topk_wave_pl(const float* z, int E, int k, int mode, float scale,
+                                             int* out_i, float* out_w) {
     const int lane = lane_id();
-    float v[kMaxPerLane];
-    int id[kMaxPerLane];
+    unsigned key[PL];
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < PL; ++i) {
         const int e = lane + i * kWave;
-        v[i] = e < E ? z[e] : -INFINITY;
-        id[i] = e < E ? e : INT32_MAX;
+        key[i] = e < E ? logit_key(z[e]) : 0u;
     }
-    float my_v = -INFINITY;
+    unsigned my_key = 0;
     int my_i = 0;
     for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int bi = INT32_MAX;
+        unsigned m = key[0];
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-            if (ranks_before(v[i], id[i], bv, bi)) { bv = v[i]; bi = id[i]; }
-        wave_argmax(bv, bi);
-        // Non-finite logits can leave no candidate: keep the index in range.
-        if (bi >= E) bi = 0;
+        for (int i = 1; i < PL; ++i) m = max(m, key[i]);
+        m = wave_max_key(m);
+        int slot = 0;
+        unsigned long long owners = 0;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-            if (id[i] == bi) { v[i] = -INFINITY; id[i] = INT32_MAX; }
-        if (lane == j) { my_v = bv; my_i = bi; }
+        for (int i = PL - 1; i >= 0; --i) {
+            const unsigned long long b = __ballot(key[i] == m);
+            if (b) {
+                slot = i;
+                owners = b;
+            }
+        }
+        const int owner = __builtin_ctzll(owners);
+        const bool mine = lane == owner;
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+            if (i == slot && mine) key[i] = 0u;
+        if (lane == j) {
+            my_key = m;
+            my_i = owner + slot * kWave;
+        }
     }
+    if (my_i >= E) my_i = 0;  // unreachable for k <= E; keeps the index in range
+    const float my_v = key_logit(my_key);
     const float zmax = __shfl(my_v, 0, kWave);
     const float ex = lane < k ? expf(my_v - zmax) : 0.0f;
     const float den = wave_sum(ex);
@@ -127,6 +129,16 @@ __device__ __forceinline__ void topk_wave(const float* z, int E, int k, int mode
     if (mode == MOE_ROUTE_SOFTMAX_TOPK_RENORM) w *= scale;
     *out_i = my_i;
     *out_w = w;
+}
+
+constexpr int kMaxPerLane = 8;  // E <= 512
+
+__device__ __forceinline__ void topk_wave(const float* z, int E, int k, int mode, float scale, int* out_i,
+                                          float* out_w) {
+    if (E <= kWave) topk_wave_pl<1>(z, E, k, mode, scale, out_i, out_w);
+    else if (E <= 2 * kWave) topk_wave_pl<2>(z, E, k, mode, scale, out_i, out_w);
+    else if (E <= 4 * kWave) topk_wave_pl<4>(z, E, k, mode, scale, out_i, out_w);
+    else topk_wave_pl<kMaxPerLane>(z, E, k, mode, scale, out_i, out_w);
 }
 
 }  // namespace smoe

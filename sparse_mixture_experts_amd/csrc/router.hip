@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(
     router_row_wave<KB, TT>(x, w_router, b_router, w_sg, T, d, E, row, t0, min(T, t0 + tok_chunk), logits, ld);
 }
 
-// One wave per token: k rounds of a wave arg-max by xor shuffles, then the weights.
+// One wave per token: the wave top-k, the weights, and the shared-expert gate input.
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int ld, int T,
                                                    int E, int k, int mode, float scale,
                                                    int32_t* __restrict__ idx_out,
@@ -71,21 +71,28 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     }
 }
 
-// Decode (T <= 64): top-k of every token, the expert grouping and the group plan in one
-// block of 1024 threads, so that routing costs one launch after the logits.
+// Decode (T <= 64): the expert grouping and the group plan in one block of 1024 threads,
+// after the top-k of every token, done here (topk_here, one wave per token) for small T or
+// beforehand by topk_kernel, whose blocks spread the tokens over many compute units.
 __global__ __launch_bounds__(1024) void decode_route_kernel(
     const float* __restrict__ logits, int ld, int T, int E, int k, int mode, float scale,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, float* __restrict__ sg_out,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token, int32_t* __restrict__ perm_inv,
     float* __restrict__ row_w, int shared, int tile_m, Group* __restrict__ groups,
-    PlanMeta* __restrict__ meta, int32_t* __restrict__ tile_map, int tile_cap) {
+    PlanMeta* __restrict__ meta, int32_t* __restrict__ tile_map, int tile_cap, int topk_here) {
     __shared__ float s_w[kPermChunk * 32];
     __shared__ int32_t s_idx[kPermChunk * 32];
     __shared__ unsigned long long mask[kMaxE];
     __shared__ int32_t base_row[kMaxE + 1];
-    __shared__ int tmp[1024 / kWave];
+    __shared__ int tmp[2 * 1024 / kWave];
     const int lane = lane_id(), wave = threadIdx.x / kWave;
-    for (int t = wave; t < T; t += 1024 / kWave) {
+    if (!topk_here) {  // top-k already done by topk_kernel: idx_out / w_out hold it
+        for (int p = threadIdx.x; p < T * k; p += blockDim.x) {
+            s_idx[p] = idx_out[p];
+            s_w[p] = w_out[p];
+        }
+    }
+    for (int t = wave; topk_here && t < T; t += 1024 / kWave) {
         const float* z = logits + (size_t)t * ld;
         int my_i;
         float my_w;
@@ -154,10 +161,17 @@ hipError_t launch_decode_route(const moe_layer& L, const float* logits, int ld, 
                                float* w, float* shared_gate, int32_t* offsets, int32_t* perm_token,
                                int32_t* perm_inv, float* row_w, int tile_m, Group* groups,
                                PlanMeta* meta, int32_t* tile_map, hipStream_t s) {
+    // One block holds 16 waves: beyond 16 tokens the top-k runs as its own launch.
+    const bool topk_here = T <= 1024 / kWave;
+    if (!topk_here) {
+        const hipError_t e = launch_topk(L, logits, ld, T, idx, w, shared_gate, row_w, nullptr, s);
+        if (e != hipSuccess) return e;
+    }
     decode_route_kernel<<<1, 1024, 0, s>>>(logits, ld, T, L.n_expert, L.k, L.route, L.route_scale, idx,
                                            w, shared_gate, offsets, perm_token, perm_inv, row_w,
                                            L.shared_ff > 0 ? 1 : 0, tile_m, groups, meta, tile_map,
-                                           grouped_max_mtiles(L.n_expert, T, L.k, L.shared_ff > 0));
+                                           grouped_max_mtiles(L.n_expert, T, L.k, L.shared_ff > 0),
+                                           topk_here ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -200,13 +200,54 @@ def test_one_expert_takes_every_token():
         assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "bf16", path)
 
 
-def test_all_tie_router_bit_exact():
+@pytest.mark.parametrize("T", [9, 40, 200])
+def test_all_tie_router_bit_exact(T):
+    # T = 9: top-k inside the decode routing block; 40: its own launch; 200: MFMA router.
     L = dict(layer_arrays("qwen", d=256, n_expert=32, ff=128, shared_ff=64))
     L["w_router"] = np.zeros_like(L["w_router"])
-    x = synth.make_tokens(L, 9, seed=6, gap=0)
+    x = synth.make_tokens(L, T, seed=6, gap=0)
     idx, w, _ = moe_mod().route(_custom(L), xdev(x))
     assert (idx.cpu().numpy() == np.arange(8)).all()
     assert (w.cpu().numpy() == np.float32(1.0 / 8)).all()
+
+
+@pytest.mark.parametrize("T", [5, 40, 300])
+def test_masked_experts(T):
+    # A router bias of -inf masks all experts but two: top-4 takes those two, then the
+    # two lowest-index masked experts with weight exactly 0.
+    L = dict(layer_arrays("gptoss", d=320, n_expert=16, ff=192))
+    b = np.full(16, -np.inf, np.float32)
+    b[[3, 11]] = 0.0
+    L["b_router"] = b
+    # Keep tokens whose two live logits differ by more than 1e-3 (the usual gap rule).
+    x = synth.make_tokens(L, 2 * T + 8, seed=9, gap=0)
+    z = oracle.router_logits(L, x)
+    x = x[np.abs(z[:, 3] - z[:, 11]) > 1e-3][:T]
+    assert x.shape[0] == T
+    lay = _custom(L)
+    idx, w, _ = moe_mod().route(lay, xdev(x))
+    ridx, rw, _ = oracle.route(L, x)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert (np.sort(ridx[:, 2:], axis=1) == [0, 1]).all()
+    assert (w.cpu().numpy()[:, 2:] == 0).all()
+    assert np.max(np.abs(w.cpu().numpy() - rw)) <= W_ATOL
+    y = moe_mod().forward(lay, xdev(x))
+    assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "bf16", "masked experts")
+
+
+@pytest.mark.parametrize("T", [3, 40, 300])
+def test_nan_logits_rank_last(T):
+    # A token whose input holds a NaN has NaN logits only; NaN ranks below every number
+    # and ties go to the lower index, so its picks are experts 0..k-1 (the oracle's
+    # stable sort puts NaN last as well).  Other tokens are unaffected.
+    L = dict(layer_arrays("qwen", d=256, n_expert=32, ff=128, shared_ff=64))
+    x = synth.make_tokens(L, T, seed=10).copy()
+    x[1, 17] = 0x7FC0  # bf16 quiet NaN
+    idx, _, _ = moe_mod().route(_custom(L), xdev(x))
+    ridx, _, _ = oracle.route(L, x)
+    got = idx.cpu().numpy()
+    assert (ridx[1] == np.arange(8)).all()
+    assert np.array_equal(got, ridx)
 
 
 def test_identical_experts():
