@@ -50,6 +50,112 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# ----------------------------------------------------------------------------- HBM traffic
+# Measured HBM bytes per launch of the timed stage come from two rocprofv3 counter runs
+# of this script (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled by what
+# the same counter reads for a plain read+write kernel of known size run at the end of
+# those runs (--copy-calibration).  `--summarize-pmc` turns the two counter CSVs into
+# profiles/<workload>_hbm_traffic.md; a normal run reports the recorded figure only while
+# the kernel sources still hash to the value recorded with it.
+
+CALIB_BYTES = 256 << 20
+STAGE_KERNELS = ("expert_up_gemv_kernel", "expert_down_gemv_kernel", "plan_kernel",
+                 "gg_up_kernel", "gg_down_kernel<float>")
+
+
+def kernel_source_hash():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "sparse_mixture_experts_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "moe.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
+
+
+def recorded_traffic(workload):
+    """Bytes per stage launch recorded for this workload, or None (absent or stale)."""
+    try:
+        with open(traffic_file(workload)) as fh:
+            for line in fh:
+                if line.startswith("traffic_json: "):
+                    rec = json.loads(line[len("traffic_json: "):])
+                    if rec.get("csrc_hash") == kernel_source_hash():
+                        return rec["bytes_per_launch"]
+                    return None
+    except OSError:
+        pass
+    return None
+
+
+def _short_kernel(name):
+    n = name.replace("(anonymous namespace)::", "").replace("smoe::", "")
+    if n.startswith("void "):
+        n = n[5:]
+    return n.split("(")[0]
+
+
+def summarize_pmc(fetch_csv, write_csv, workload, out_path, command):
+    import csv
+    import collections
+    per = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = collections.defaultdict(list)
+        calib = []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                n = _short_kernel(r["Kernel_Name"])
+                v = float(r["Counter_Value"])
+                if "neg_kernel" in r["Kernel_Name"] or "NegFunctor" in r["Kernel_Name"]:
+                    calib.append(v)
+                else:
+                    vals[n].append(v)
+        if not calib:
+            raise SystemExit(f"{path}: no calibration dispatches (run with --copy-calibration)")
+        factor = statistics.median(calib) * 1024.0 / CALIB_BYTES
+        per[counter] = (vals, factor, len(calib))
+    kernels = sorted(set(per["FETCH_SIZE"][0]) | set(per["WRITE_SIZE"][0]))
+    rows, total = [], 0.0
+    for n in kernels:
+        f = per["FETCH_SIZE"][0].get(n, [])
+        w = per["WRITE_SIZE"][0].get(n, [])
+        fb = (sum(f) / len(f) * 1024.0 / per["FETCH_SIZE"][1]) if f else 0.0
+        wb = (sum(w) / len(w) * 1024.0 / per["WRITE_SIZE"][1]) if w else 0.0
+        stage = any(n.startswith(k) or k in n for k in STAGE_KERNELS)
+        if stage:
+            total += fb + wb
+        rows.append((n, len(f), fb, wb, stage))
+    lines = [f"# HBM traffic per launch: {workload}", "",
+             "Commands (from the repository root, one MI355X; one counter per run):", "", "```"]
+    lines += command.split("\n")
+    lines += ["```", "",
+              f"Calibration: torch.neg over {CALIB_BYTES >> 20} MiB fp32 (reads and writes exactly "
+              f"that much).  FETCH_SIZE reads {per['FETCH_SIZE'][1]:.4f} x the true bytes "
+              f"({per['FETCH_SIZE'][2]} dispatches), WRITE_SIZE {per['WRITE_SIZE'][1]:.4f} x; "
+              "every figure below is divided by its factor.", "",
+              "| kernel | dispatches | fetched MB/launch | written MB/launch | in timed stage |",
+              "|---|---|---|---|---|"]
+    for n, c, fb, wb, st in rows:
+        if "rocclr" in n or "rocprim" in n:
+            continue
+        lines.append(f"| `{n[:80]}` | {c} | {fb / 1e6:.2f} | {wb / 1e6:.2f} | {'yes' if st else ''} |")
+    lines += ["", f"Timed stage (expert FFN launches): {total / 1e6:.2f} MB of HBM traffic per launch.", "",
+              "traffic_json: " + json.dumps({"workload": workload, "bytes_per_launch": total,
+                                             "csrc_hash": kernel_source_hash()})]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out_path}: {total / 1e6:.2f} MB per stage launch")
+
+
 # ----------------------------------------------------------------------------- work model
 
 def elem_bytes(L):
@@ -206,7 +312,7 @@ def time_workload(name, steps, warmup, layer_cache):
         res["layer_hbm_frac"] = lb / (ms_step / 1e3) / HBM_PEAK
         res["roofline"] = {"bound": "hbm", "achieved": sb / (stage_ms / 1e3) / 1e9,
                            "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                           "frac": sb / (stage_ms / 1e3) / HBM_PEAK, "traffic": None,
+                           "frac": sb / (stage_ms / 1e3) / HBM_PEAK, "traffic": recorded_traffic(name),
                            "kernel": "expert FFN stage (plan + up + down)",
                            "algorithmic_bytes": sb}
     else:
@@ -217,7 +323,7 @@ def time_workload(name, steps, warmup, layer_cache):
         res["layer_mfma_frac"] = fl / (ms_step / 1e3) / peak
         res["roofline"] = {"bound": "mfma", "achieved": sf / (stage_ms / 1e3) / 1e12,
                            "peak": peak / 1e12, "unit": "TFLOP/s",
-                           "frac": sf / (stage_ms / 1e3) / peak, "traffic": None,
+                           "frac": sf / (stage_ms / 1e3) / peak, "traffic": recorded_traffic(name),
                            "kernel": "expert FFN stage (plan + up + down)",
                            "algorithmic_flops": sf}
     log(f"[{name}] {ms_step * 1e3:.1f} us/step, {res['tokens_per_s']:.0f} tok/s, "
@@ -263,7 +369,18 @@ def main():
                     help="comma-separated extra workloads reported under 'sweep'")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with three read+write passes of 256 MiB (torch.neg) that calibrate "
+                         "the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/<workload>_hbm_traffic.md from two counter CSVs (no GPU)")
+    ap.add_argument("--pmc-command", default="", help="command lines quoted in that summary")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                      traffic_file(args.workload), args.pmc_command)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -286,6 +403,13 @@ def main():
             sweep.append(time_workload(w, max(5, min(args.steps, 20)) if WORKLOADS[w][1] > 64 else args.steps,
                                        min(args.warmup, 5), cache))
     cpu = None if args.no_cpu else cpu_baseline(args.workload, cache)
+    if args.copy_calibration:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     spec_name, T = WORKLOADS[args.workload]
     out = {

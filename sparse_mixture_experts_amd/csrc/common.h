@@ -61,7 +61,98 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Wave index in the block, marked wave-uniform so that addresses built from it stay in
+// scalar registers.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
+
 __device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
+
+// ---------------------------------------------------------------- wave reduce-scatter
+// Butterfly sum of N values per lane across the wave (N a power of two, 1..64), in
+// 63 lane exchanges for N = 64 instead of 6 per value.  Step b (lane bit 5 down to 0)
+// pairs each lane with the lane differing in bit b -- through v_permlane32_swap and
+// v_permlane16_swap for bits 5 and 4, through DPP row mirror, half-row mirror and quad
+// permutes for bits 3..0 (those partners also differ in lower bits, which no earlier
+// step has used) -- and, while more than one value remains, each lane keeps the half of
+// the values named by its bit and adds its partner's copy of that half.  On return every
+// lane holds the wave total of value index lane >> (6 - log2 N).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int B>
+__device__ __forceinline__ void lane_pair_swap(float& a, float& b) {
+    // After the swap, a + b sums the lower-half value in lanes with bit B clear and the
+    // upper-half value in lanes with bit B set, each with its partner's copy.
+    if constexpr (B == 5) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        a = __uint_as_float(r[0]);
+        b = __uint_as_float(r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        a = __uint_as_float(r[0]);
+        b = __uint_as_float(r[1]);
+    }
+}
+
+template <int B>
+constexpr int lane_pair_dpp() {
+    return B == 3 ? 0x140 : B == 2 ? 0x141 : B == 1 ? 0x4E : 0xB1;
+}
+
+template <int B, int H>
+__device__ __forceinline__ void butterfly_split(float* v) {
+    if constexpr (B >= 4) {
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+            float a = v[i], b = v[H + i];
+            lane_pair_swap<B>(a, b);
+            v[i] = a + b;
+        }
+    } else {
+        const bool upper = (lane_id() >> B) & 1;
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+            const float keep = upper ? v[H + i] : v[i];
+            const float give = upper ? v[i] : v[H + i];
+            v[i] = keep + dpp_f32<lane_pair_dpp<B>()>(give);
+        }
+    }
+}
+
+template <int B>
+__device__ __forceinline__ float butterfly_full(float x) {
+    if constexpr (B >= 4) {
+        float a = x, b = x;
+        lane_pair_swap<B>(a, b);
+        return a + b;
+    } else {
+        return x + dpp_f32<lane_pair_dpp<B>()>(x);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ float wave_reduce_scatter(float (&v)[N]) {
+    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N must be a power of two <= 64");
+    if constexpr (N >= 2) butterfly_split<5, N / 2>(v);
+    if constexpr (N >= 4) butterfly_split<4, N / 4>(v);
+    if constexpr (N >= 8) butterfly_split<3, N / 8>(v);
+    if constexpr (N >= 16) butterfly_split<2, N / 16>(v);
+    if constexpr (N >= 32) butterfly_split<1, N / 32>(v);
+    if constexpr (N >= 64) butterfly_split<0, N / 64>(v);
+    float x = v[0];
+    if constexpr (N < 2) x = butterfly_full<5>(x);
+    if constexpr (N < 4) x = butterfly_full<4>(x);
+    if constexpr (N < 8) x = butterfly_full<3>(x);
+    if constexpr (N < 16) x = butterfly_full<2>(x);
+    if constexpr (N < 32) x = butterfly_full<1>(x);
+    if constexpr (N < 64) x = butterfly_full<0>(x);
+    return x;
+}
+
+// log2 of a power of two, at compile time.
+constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
 
 // ---------------------------------------------------------------- scans
 // Inclusive prefix sum over the wave through DPP: shifts right by 1, 2, 4 and 8 lanes

@@ -5,11 +5,11 @@
 // token.  "Phase 19: MoE - gpt-oss-20b", Experts: fused interleaved gate_up with bias,
 // clamps, (up + 1) * gate * sigmoid(alpha * gate), down with bias.
 //
-// up_item: a wave owns 2 hidden units f, f+1 of one group: it streams the 4 weight rows
-// (gate f, gate f+1, up f, up f+1 -- or the 4 interleaved gate_up rows) and dots them
-// with the group's rows of x, then applies the activation and writes H[row, f..f+1] in
-// fp32.  down_item: a wave owns 4 output dims i..i+3 of one group: it streams the 4 rows
-// of W_d and dots them with the group's rows of H, writing Y_perm[row, i..i+3].
+// up_item: a wave owns U hidden units f.. of one group: it streams their 2U weight rows
+// (gate and up, or the interleaved gate_up rows) and dots them with the group's rows of
+// x, then applies the activation and writes H[row, f..] in fp32.  down_item: a wave owns NR output dims i.. of one group: it streams those NR rows
+// of W_d and dots them with the group's rows of H, writing Y_perm[row, i..].  Each
+// 4-row step ends in one butterfly reduce-scatter of all the wave's partial sums.
 #pragma once
 
 #include "internal.h"
@@ -44,133 +44,165 @@ struct GemvDown {
     int hstride, d, ff, ffs;
 };
 
-// One wave: hidden units f0, f0+1 (f0 even, f0 < the group's hidden width) of group g,
+// One wave: hidden units f0 .. f0+U-1 of group g (those below the group's hidden width),
 // for every row of the group.  RESIDENT: the whole K axis fits one KB-chunk register
-// batch, so the 4 weight rows are streamed once and every row is served from registers.
-template <int KB, typename TT, bool OAI, bool RESIDENT>
+// batch, so the 2U weight rows are streamed once and every row is served from registers.
+template <int KB, typename TT, bool OAI, bool RESIDENT, int U, bool EXACT>
 __device__ __forceinline__ void up_item(const GemvUp& a, const Group& g, int f0) {
     using S = typename TT::storage;
+    constexpr int NR = 2 * U;
     const bool shared = g.e < 0;
     const size_t d = a.d;
+    const int ffg = shared ? a.ffs : a.ff;
     // The shared expert is always a plain SwiGLU, also in a layer of clamped experts.
     const bool oai = OAI && !shared;
-    const S* wr[4];
+    // Weight rows: gate f0.., then up f0.. (two matrices), or the interleaved gate_up rows
+    // gate f0, up f0, gate f0+1, ... (one matrix).  Units past the width repeat the last.
+    const S* wr[NR];
     if (oai) {
-        const S* base = static_cast<const S*>(a.w_gate_up) + ((size_t)g.e * 2 * a.ff + 2 * f0) * d;
-        // rows: gate f0, up f0, gate f0+1, up f0+1
-        for (int r = 0; r < 4; ++r) wr[r] = base + r * d;
+        const S* base = static_cast<const S*>(a.w_gate_up) + (size_t)g.e * 2 * a.ff * d;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) wr[r] = base + (size_t)(2 * min(f0 + r / 2, ffg - 1) + (r & 1)) * d;
     } else {
         const S* gb = shared ? static_cast<const S*>(a.ws_gate) : static_cast<const S*>(a.w_gate) + (size_t)g.e * a.ff * d;
         const S* ub = shared ? static_cast<const S*>(a.ws_up) : static_cast<const S*>(a.w_up) + (size_t)g.e * a.ff * d;
-        // rows: gate f0, gate f0+1, up f0, up f0+1
-        wr[0] = gb + f0 * d;
-        wr[1] = gb + (f0 + 1) * d;
-        wr[2] = ub + f0 * d;
-        wr[3] = ub + (f0 + 1) * d;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            wr[u] = gb + (size_t)min(f0 + u, ffg - 1) * d;
+            wr[U + u] = ub + (size_t)min(f0 + u, ffg - 1) * d;
+        }
     }
-    const S* const wrc[4] = {wr[0], wr[1], wr[2], wr[3]};
-    float bg[2] = {0.f, 0.f}, bu[2] = {0.f, 0.f};
-    if (oai) {
-        const S* b = static_cast<const S*>(a.b_gate_up) + (size_t)g.e * 2 * a.ff + 2 * f0;
-        for (int f = 0; f < 2; ++f) {
-            if constexpr (sizeof(S) == 2) {
-                bg[f] = bf16_to_f32(b[2 * f]);
-                bu[f] = bf16_to_f32(b[2 * f + 1]);
-            } else {
-                bg[f] = b[2 * f];
-                bu[f] = b[2 * f + 1];
-            }
+    const S* const (&wrc)[NR] = wr;
+    // After the reduction lane l holds value (t * NR + r) = l >> SH: token t = l >> 4 (one
+    // 16-lane row per token), weight row r = (l >> SH) % NR.  The up row matching a gate
+    // row sits U values on (two matrices) or 1 value on (interleaved): fetched by a DPP
+    // row shift of (U << SH) or (1 << SH) lanes.
+    constexpr int N = NR * kNT;
+    constexpr int SH = 6 - ilog2(N);
+    const int lane = lane_id();
+    const int my_t = lane >> 4, my_r = (lane >> SH) % NR;
+    const bool gate_lane = oai ? (my_r & 1) == 0 : my_r < U;
+    const int my_f = oai ? my_r / 2 : my_r;  // unit offset of a gate lane
+    const bool writer = gate_lane && (lane & ((1 << SH) - 1)) == 0 && f0 + my_f < ffg;
+    float bg = 0.f, bu = 0.f;
+    if (oai && writer) {
+        const S* b = static_cast<const S*>(a.b_gate_up) + (size_t)g.e * 2 * a.ff + 2 * (f0 + my_f);
+        if constexpr (sizeof(S) == 2) {
+            bg = bf16_to_f32(b[0]);
+            bu = bf16_to_f32(b[1]);
+        } else {
+            bg = b[0];
+            bu = b[1];
         }
     }
     const S* x = static_cast<const S*>(a.x);
-    const int lane = lane_id();
-    // Whole K in one register batch: stream the 4 weight rows once and loop over every
-    // row of the group from registers.
-    uint4 wv[RESIDENT ? KB : 1][4];
-    if constexpr (RESIDENT) load_w_batch<4, KB, TT, true>(wrc, a.d, 0, wv);
-    for (int tb = 0; tb < g.n; tb += kNT) {
+    // Token of row tb + (lane % kNT), one vector load per step, issued before the weight
+    // loads so that waiting for it does not wait for them.
+    auto step_tokens = [&](int tb) {
+        const int r = min(tb + (lane & (kNT - 1)), g.n - 1);
+        const int tok = shared ? r : a.perm_token[g.row0 + r];
+        return min(max(tok, 0), a.T - 1);
+    };
+    auto step = [&](int tb, int tok_v, const uint4 (&wv)[RESIDENT ? KB : 1][NR]) {
         const int nt = min(kNT, g.n - tb);
         const S* ar[kNT];
 #pragma unroll
-        for (int t = 0; t < kNT; ++t) {
-            const int r = min(tb + t, g.n - 1);
-            int tok = shared ? r : a.perm_token[g.row0 + r];
-            tok = min(max(tok, 0), a.T - 1);
-            ar[t] = x + (size_t)tok * d;
-        }
-        const S* const arc[kNT] = {ar[0], ar[1], ar[2], ar[3]};
-        float acc[4][kNT] = {};
-        if constexpr (RESIDENT) dot_w_batch<4, kNT, KB, TT, TT>(wv, arc, nt, a.d, 0, acc);
-        else rows_dot<4, kNT, KB, TT, TT, true>(wrc, arc, nt, a.d, acc);
-        float h[2][kNT];
-#pragma unroll
-        for (int t = 0; t < kNT; ++t) {
-            if (t >= nt) continue;
-#pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                if (oai) {
-                    float gv = wave_sum(acc[2 * f][t]) + bg[f];
-                    float uv = wave_sum(acc[2 * f + 1][t]) + bu[f];
-                    gv = fminf(gv, a.limit);
-                    uv = fminf(fmaxf(uv, -a.limit), a.limit);
-                    h[f][t] = (uv + 1.0f) * gv * sigmoidf_(a.alpha * gv);
-                } else {
-                    const float gv = wave_sum(acc[f][t]);
-                    const float uv = wave_sum(acc[2 + f][t]);
-                    h[f][t] = gv * sigmoidf_(gv) * uv;
-                }
-            }
-        }
+        for (int t = 0; t < kNT; ++t) ar[t] = x + (size_t)__builtin_amdgcn_readlane(tok_v, t) * d;
+        const S* const (&arc)[kNT] = ar;
+        float acc[NR][kNT] = {};
+        if constexpr (RESIDENT) dot_w_batch<NR, kNT, KB, TT, TT, EXACT>(wv, arc, nt, a.d, 0, acc);
+        else rows_dot<NR, kNT, KB, TT, TT, true, EXACT>(wrc, arc, nt, a.d, acc);
+        float v[N];
 #pragma unroll
         for (int t = 0; t < kNT; ++t)
 #pragma unroll
-            for (int f = 0; f < 2; ++f)
-                if (lane == f + 2 * t && t < nt) a.H[(size_t)(g.row0 + tb + t) * a.hstride + f0 + f] = h[f][t];
-    }
+            for (int r = 0; r < NR; ++r) v[t * NR + r] = acc[r][t];
+        const float sum = wave_reduce_scatter<N>(v);
+        const float up_two = __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x100 + (U << SH), 0xF, 0xF, false));
+        const float up_one = __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x100 + (1 << SH), 0xF, 0xF, false));
+        float h;
+        if (oai) {
+            float gv = sum + bg;
+            float uv = up_one + bu;
+            gv = fminf(gv, a.limit);
+            uv = fminf(fmaxf(uv, -a.limit), a.limit);
+            h = (uv + 1.0f) * gv * sigmoidf_(a.alpha * gv);
+        } else {
+            h = sum * sigmoidf_(sum) * up_two;
+        }
+        if (writer && my_t < nt) a.H[(size_t)(g.row0 + tb + my_t) * a.hstride + f0 + my_f] = h;
+    };
+    // The first step runs outside the loop: straight-line code lets the compiler wait for
+    // the token load alone (not the weights behind it) before the activation loads.
+    const int tok0 = step_tokens(0);
+    uint4 wv[RESIDENT ? KB : 1][NR];
+    if constexpr (RESIDENT) load_w_batch<NR, KB, TT, true, EXACT>(wrc, a.d, 0, wv);
+    __builtin_amdgcn_sched_barrier(0);  // the token's readlanes stay behind the weight loads
+    step(0, tok0, wv);
+    for (int tb = kNT; tb < g.n; tb += kNT) step(tb, step_tokens(tb), wv);
 }
 
-// One wave: output dims i0..i0+3 (i0 < d, d a multiple of 4) of group g, for every row.
-template <int KB, typename TT, bool OAI, bool RESIDENT>
+// Hidden units per up-projection wave.  Four units (8 weight rows, x re-read half as
+// often) measured slower at 64 decode tokens than two: the larger register batch halves
+// the waves in flight.
+constexpr int kUpUnits = 2;
+
+// One wave: output dims i0 .. i0+NR-1 of group g (those below d), for every row, NT
+// rows of H per step.
+template <int KB, typename TT, bool OAI, bool RESIDENT, int NR, int NT, bool EXACT>
 __device__ __forceinline__ void down_item(const GemvDown& a, const Group& g, int i0) {
     using S = typename TT::storage;
     const bool shared = g.e < 0;
     const int K = shared ? a.ffs : a.ff;
-    const S* base = shared ? static_cast<const S*>(a.ws_down) + (size_t)i0 * K
-                           : static_cast<const S*>(a.w_down) + ((size_t)g.e * a.d + i0) * K;
-    const S* const wr[4] = {base, base + K, base + 2 * (size_t)K, base + 3 * (size_t)K};
-    float bias[4] = {0.f, 0.f, 0.f, 0.f};
-    if (OAI && !shared && a.b_down) {
-        const S* b = static_cast<const S*>(a.b_down) + (size_t)g.e * a.d + i0;
-        for (int r = 0; r < 4; ++r) {
-            if constexpr (sizeof(S) == 2) bias[r] = bf16_to_f32(b[r]);
-            else bias[r] = b[r];
-        }
-    }
+    const S* base = shared ? static_cast<const S*>(a.ws_down) : static_cast<const S*>(a.w_down) + (size_t)g.e * a.d * K;
+    const S* wr[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) wr[r] = base + (size_t)min(i0 + r, a.d - 1) * K;
+    const S* const (&wrc)[NR] = wr;
+    // After the reduction lane l holds value (t * NR + r) = l >> SH.
+    constexpr int N = NR * NT;
+    constexpr int SH = 6 - ilog2(N);
     const int lane = lane_id();
-    uint4 wv[RESIDENT ? KB : 1][4];
-    if constexpr (RESIDENT) load_w_batch<4, KB, TT, true>(wr, K, 0, wv);
-    for (int tb = 0; tb < g.n; tb += kNT) {
-        const int nt = min(kNT, g.n - tb);
-        const float* ar[kNT];
+    const int my_t = (lane >> SH) / NR, my_i = i0 + (lane >> SH) % NR;
+    const bool writer = (lane & ((1 << SH) - 1)) == 0 && my_i < a.d;
+    float bias = 0.f;
+    if (OAI && !shared && a.b_down && my_i < a.d) {
+        const S* b = static_cast<const S*>(a.b_down) + (size_t)g.e * a.d + my_i;
+        if constexpr (sizeof(S) == 2) bias = bf16_to_f32(*b);
+        else bias = *b;
+    }
+    uint4 wv[RESIDENT ? KB : 1][NR];
+    if constexpr (RESIDENT) load_w_batch<NR, KB, TT, true, EXACT>(wrc, K, 0, wv);
+    for (int tb = 0; tb < g.n; tb += NT) {
+        const int nt = min(NT, g.n - tb);
+        const float* ar[NT];
 #pragma unroll
-        for (int t = 0; t < kNT; ++t) ar[t] = a.H + (size_t)(g.row0 + min(tb + t, g.n - 1)) * a.hstride;
-        const float* const arc[kNT] = {ar[0], ar[1], ar[2], ar[3]};
-        float acc[4][kNT] = {};
-        if constexpr (RESIDENT) dot_w_batch<4, kNT, KB, TT, F32>(wv, arc, nt, K, 0, acc);
-        else rows_dot<4, kNT, KB, TT, F32, true>(wr, arc, nt, K, acc);
-        float out[4][kNT];
+        for (int t = 0; t < NT; ++t) ar[t] = a.H + (size_t)(g.row0 + min(tb + t, g.n - 1)) * a.hstride;
+        const float* const (&arc)[NT] = ar;
+        float acc[NR][NT] = {};
+        if constexpr (RESIDENT) dot_w_batch<NR, NT, KB, TT, F32, EXACT>(wv, arc, nt, K, 0, acc);
+        else rows_dot<NR, NT, KB, TT, F32, true, EXACT>(wrc, arc, nt, K, acc);
+        float v[N];
 #pragma unroll
-        for (int t = 0; t < kNT; ++t) {
-            if (t >= nt) continue;
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) out[r][t] = wave_sum(acc[r][t]) + bias[r];
-        }
-#pragma unroll
-        for (int t = 0; t < kNT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (lane == r + 4 * t && t < nt) a.y[(size_t)(g.row0 + tb + t) * a.d + i0 + r] = out[r][t];
+            for (int r = 0; r < NR; ++r) v[t * NR + r] = acc[r][t];
+        const float out = wave_reduce_scatter<N>(v) + bias;
+        if (writer && my_t < nt) a.y[(size_t)(g.row0 + tb + my_t) * a.d + my_i] = out;
     }
 }
+
+// Output rows per down-projection wave for "wide" launches: 16 when the K axis is one
+// register chunk per lane, fewer for longer axes so that the weight batch stays at 64
+// registers or below.  Launches over very few groups use 4 rows per wave instead, for
+// more waves in flight.
+template <int KB>
+constexpr int down_rows_wide() { return KB == 1 ? 16 : KB == 2 ? 8 : 4; }
+
+// H rows per down-projection step: 2 beside 16 weight rows (register budget), else 4.
+template <int NR>
+constexpr int down_step_rows() { return NR >= 16 ? 2 : kNT; }
 
 }  // namespace smoe

@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(
     const typename TT::storage* __restrict__ x, const typename TT::storage* __restrict__ w_router,
     const float* __restrict__ b_router, const typename TT::storage* __restrict__ w_sg, int T, int d,
     int E, int n_rows, int tok_chunk, float* __restrict__ logits, int ld) {
-    const int row = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int row = blockIdx.x * 4 + wave_id();
     if (row >= n_rows) return;
     const int t0 = blockIdx.y * tok_chunk;
     router_row_wave<KB, TT>(x, w_router, b_router, w_sg, T, d, E, row, t0, min(T, t0 + tok_chunk), logits, ld);
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    float* __restrict__ row_w,
                                                    const uint16_t* __restrict__ x_sg,
                                                    const uint16_t* __restrict__ w_sg, int d) {
-    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int t = blockIdx.x * 4 + wave_id();
     if (t >= T) return;
     const float* z = logits + (size_t)t * ld;
     int my_i;

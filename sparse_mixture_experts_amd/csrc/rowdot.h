@@ -6,54 +6,112 @@
 
 namespace smoe {
 
-// acc[r][t] += sum_i W_r[i] * A_t[i] over i < K, for NR weight rows and up to NT
-// activation rows, computed by one wave.  The K axis is cut into 16-byte chunks of W
-// (TW::VEC elements); lane l takes chunks l, l+64, l+128, ...  KB chunks per lane are
-// loaded into registers before any arithmetic so that NR*KB independent 16-byte loads
-// per lane are in flight.  STREAM_W marks the W loads non-temporal (for weights read
-// once per call).  Tokens t >= nt are skipped.
-// The partial sums are per lane; the caller reduces them across the wave.
-template <int NR, int NT, int KB, typename TW, typename TA, bool STREAM_W = false>
-__device__ __forceinline__ void rows_dot(const typename TW::storage* const (&w)[NR],
-                                         const typename TA::storage* const (&a)[NT], int nt,
-                                         int K, float (&acc)[NR][NT]) {
-    constexpr int V = TW::VEC;
-    static_assert(V % TA::VEC == 0, "activation loads must tile the weight vector");
-    const int lane = lane_id();
-    const int nchunk = (K / V + kWave - 1) / kWave;
-    for (int c0 = 0; c0 < nchunk; c0 += KB) {
-        uint4 wv[KB][NR];
+// The value itself, hidden from the optimiser: widening of register-resident weights is
+// then done where it is written, not hoisted out of the row loop (which would hold the
+// fp32 copy -- twice the registers).  The asm also pins instruction order, so every load
+// of a step is issued before the first use of this.
+__device__ __forceinline__ uint4 opaque(uint4 v) {
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+    return v;
+}
+
+// One lane's activation chunk of V elements, as loaded (16-byte pieces, not widened).
+template <typename TA, int V>
+struct ARaw {
+    static constexpr int Q = (V * (int)sizeof(typename TA::storage) + 15) / 16;
+    uint4 q[Q];
+};
+
+template <typename TA, int V>
+__device__ __forceinline__ void load_a(const typename TA::storage* p, ARaw<TA, V>& r) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int e0 = ((c0 + kb) * kWave + lane) * V;
+    for (int i = 0; i < ARaw<TA, V>::Q; ++i) r.q[i] = ld16(p + i * TA::VEC);
+}
+
+template <typename TA, int V>
+__device__ __forceinline__ void widen_a(const ARaw<TA, V>& r, float (&f)[V]) {
+#pragma unroll
+    for (int i = 0; i < ARaw<TA, V>::Q; ++i) unpack16<TA>(r.q[i], f + i * TA::VEC);
+}
+
+// acc[r][t] += W_r . A_t over one 16-byte weight chunk per row (V = TW::VEC elements),
+// from registers.  The operand with fewer rows is widened to fp32 in full first and the
+// other one row at a time, which keeps the fewest floats live: weights first for
+// NR <= NT, activations first for taller weight blocks.
+template <int NR, int NT, typename TW, typename TA>
+__device__ __forceinline__ void fma_chunk(const uint4 (&wv)[NR], const ARaw<TA, TW::VEC> (&av)[NT],
+                                          float (&acc)[NR][NT]) {
+    constexpr int V = TW::VEC;
+    if constexpr (NR <= NT) {
+        float wf[NR][V];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) unpack16<TW>(opaque(wv[r]), wf[r]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            float af[V];
+            widen_a<TA, V>(av[t], af);
 #pragma unroll
             for (int r = 0; r < NR; ++r)
-                wv[kb][r] = (e0 < K) ? (STREAM_W ? ld16_stream(w[r] + e0) : ld16(w[r] + e0))
-                                      : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < V; ++v) acc[r][t] = fmaf(wf[r][v], af[v], acc[r][t]);
         }
+    } else {
+        float af[NT][V];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int e0 = ((c0 + kb) * kWave + lane) * V;
-            if (e0 >= K) continue;
-            float wf[NR][V];
+        for (int t = 0; t < NT; ++t) widen_a<TA, V>(av[t], af[t]);
 #pragma unroll
-            for (int r = 0; r < NR; ++r) unpack16<TW>(wv[kb][r], wf[r]);
+        for (int r = 0; r < NR; ++r) {
+            float wf[V];
+            unpack16<TW>(opaque(wv[r]), wf);
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                if (t >= nt) continue;
-                float af[V];
-                load_as_f32<TA, V>(a[t] + e0, af);
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int r = 0; r < NR; ++r)
+                for (int v = 0; v < V; ++v) acc[r][t] = fmaf(wf[v], af[t][v], acc[r][t]);
+        }
+    }
+}
+
+// All-ones for a lane whose chunk starting at element e0 lies inside K, else zero, hidden
+// from the optimiser: zeroing a loaded chunk with it cannot be turned back into an
+// exec-masked load behind a branch (after which the compiler no longer counts the loads
+// in flight and, at its next wait, waits for all of them).
+__device__ __forceinline__ unsigned in_range_mask(int e0, int K) {
+    unsigned m = e0 < K ? ~0u : 0u;
+    asm("" : "+v"(m));
+    return m;
+}
+
+__device__ __forceinline__ uint4 and_mask(uint4 q, unsigned m) {
+    return make_uint4(q.x & m, q.y & m, q.z & m, q.w & m);
+}
+
+// Activation chunks of NT rows for the KB-chunk batch starting at chunk c0.  EXACT: every
+// chunk of the batch lies inside K; otherwise chunks past K read the last in-range chunk
+// and are zeroed (K >= V).
+template <int NT, int KB, typename TW, typename TA, bool EXACT>
+__device__ __forceinline__ void load_a_batch(const typename TA::storage* const (&a)[NT], int K, int c0,
+                                             ARaw<TA, TW::VEC> (&av)[KB][NT]) {
+    constexpr int V = TW::VEC;
+    const int lane = lane_id();
 #pragma unroll
-                    for (int v = 0; v < V; ++v) acc[r][t] = fmaf(wf[r][v], af[v], acc[r][t]);
+    for (int kb = 0; kb < KB; ++kb) {
+        const int e0 = ((c0 + kb) * kWave + lane) * V;
+        const int ec = EXACT ? e0 : min(e0, K - V);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            load_a<TA, V>(a[t] + ec, av[kb][t]);
+            if constexpr (!EXACT) {
+                const unsigned m = in_range_mask(e0, K);
+#pragma unroll
+                for (int i = 0; i < ARaw<TA, V>::Q; ++i) av[kb][t].q[i] = and_mask(av[kb][t].q[i], m);
             }
         }
     }
 }
 
-// Weights of NR rows held in registers: the KB-chunk batch starting at chunk c0.
-template <int NR, int KB, typename TW, bool STREAM_W>
+// Weights of NR rows held in registers: the KB-chunk batch starting at chunk c0 (EXACT
+// and the tail as for load_a_batch).
+template <int NR, int KB, typename TW, bool STREAM_W, bool EXACT>
 __device__ __forceinline__ void load_w_batch(const typename TW::storage* const (&w)[NR], int K, int c0,
                                              uint4 (&wv)[KB][NR]) {
     constexpr int V = TW::VEC;
@@ -61,38 +119,56 @@ __device__ __forceinline__ void load_w_batch(const typename TW::storage* const (
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
         const int e0 = ((c0 + kb) * kWave + lane) * V;
+        const int ec = EXACT ? e0 : min(e0, K - V);
 #pragma unroll
-        for (int r = 0; r < NR; ++r)
-            wv[kb][r] = (e0 < K) ? (STREAM_W ? ld16_stream(w[r] + e0) : ld16(w[r] + e0))
-                                  : make_uint4(0, 0, 0, 0);
-    }
-}
-
-// acc[r][t] += W-batch (registers) . A_t over the batch's K range, tokens t < nt.
-template <int NR, int NT, int KB, typename TW, typename TA>
-__device__ __forceinline__ void dot_w_batch(const uint4 (&wv)[KB][NR], const typename TA::storage* const (&a)[NT],
-                                            int nt, int K, int c0, float (&acc)[NR][NT]) {
-    constexpr int V = TW::VEC;
-    const int lane = lane_id();
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        const int e0 = ((c0 + kb) * kWave + lane) * V;
-        if (e0 >= K) continue;
-        float wf[NR][V];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) unpack16<TW>(wv[kb][r], wf[r]);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t >= nt) continue;
-            float af[V];
-            load_as_f32<TA, V>(a[t] + e0, af);
-#pragma unroll
-            for (int r = 0; r < NR; ++r)
-#pragma unroll
-                for (int v = 0; v < V; ++v) acc[r][t] = fmaf(wf[r][v], af[v], acc[r][t]);
+        for (int r = 0; r < NR; ++r) {
+            const uint4 q = STREAM_W ? ld16_stream(w[r] + ec) : ld16(w[r] + ec);
+            if constexpr (EXACT) wv[kb][r] = q;
+            else wv[kb][r] = and_mask(q, in_range_mask(e0, K));
         }
     }
 }
+
+// acc[r][t] += sum_i W_r[i] * A_t[i] over i < K, for NR weight rows and NT activation
+// rows, computed by one wave.  The K axis is cut into 16-byte chunks of W (TW::VEC
+// elements); lane l takes chunks l, l+64, l+128, ...  Per batch of KB chunks, all
+// NR*KB weight loads and NT*KB activation loads of a lane are issued before any
+// arithmetic.  STREAM_W marks the W loads non-temporal (for weights read once per call).
+// EXACT: K is a multiple of the batch span (64 * KB chunks), so no chunk needs a bound.
+// Every a[t] must be readable over K (callers repeat their last row to fill NT); sums of
+// rows t >= nt are computed and left for the caller to drop.
+// The partial sums are per lane; the caller reduces them across the wave.
+template <int NR, int NT, int KB, typename TW, typename TA, bool STREAM_W = false, bool EXACT = false>
+__device__ __forceinline__ void rows_dot(const typename TW::storage* const (&w)[NR],
+                                         const typename TA::storage* const (&a)[NT], int nt,
+                                         int K, float (&acc)[NR][NT]) {
+    static_assert(TW::VEC % TA::VEC == 0, "activation loads must tile the weight vector");
+    (void)nt;
+    const int nchunk = (K / TW::VEC + kWave - 1) / kWave;
+    for (int c0 = 0; c0 < nchunk; c0 += KB) {
+        uint4 wv[KB][NR];
+        ARaw<TA, TW::VEC> av[KB][NT];
+        load_w_batch<NR, KB, TW, STREAM_W, EXACT>(w, K, c0, wv);
+        load_a_batch<NT, KB, TW, TA, EXACT>(a, K, c0, av);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) fma_chunk<NR, NT, TW, TA>(wv[kb], av[kb], acc);
+    }
+}
+
+// acc[r][t] += W-batch (registers) . A_t over the batch's K range (same contract on a[t],
+// nt and EXACT as rows_dot).  Chunks past K hold zero weights and activations.
+template <int NR, int NT, int KB, typename TW, typename TA, bool EXACT = false>
+__device__ __forceinline__ void dot_w_batch(const uint4 (&wv)[KB][NR], const typename TA::storage* const (&a)[NT],
+                                            int nt, int K, int c0, float (&acc)[NR][NT]) {
+    (void)nt;
+    ARaw<TA, TW::VEC> av[KB][NT];
+    load_a_batch<NT, KB, TW, TA, EXACT>(a, K, c0, av);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) fma_chunk<NR, NT, TW, TA>(wv[kb], av[kb], acc);
+}
+
+// Is K a whole number of KB-chunk batches (64 lanes x KB chunks of `vec` elements)?
+inline bool exact_k(int K, int vec, int kb) { return K % (kWave * vec * kb) == 0; }
 
 // 16-byte chunks per lane along a K axis of the given length.
 inline int chunks(int K, int vec) { return (K / vec + 63) / 64; }
