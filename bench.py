@@ -255,20 +255,27 @@ def time_workload(name, steps, warmup, layer_cache):
 
     for i in range(warmup):
         step(i)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # Timed region: exactly `steps` forwards back to back, bracketed by synchronisation;
+    # nothing else is enqueued between them.
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for i in range(steps):
-        ev[i][0].record()
         step(warmup + i)
-        ev[i][1].record()
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    per = sorted(a.elapsed_time(b) for a, b in ev)
     ms_step = total_ms / steps
+    # Per-step spread, from a separate pass with an event pair around each step (the event
+    # packets themselves add a few microseconds per step, so this pass is not the value).
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record()
+        step(warmup + steps + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
 
     # Stage pass: the same steps split at the C-ABI calls, events around the expert FFN.
     plans = []
@@ -362,8 +369,10 @@ def cpu_baseline(name, layer_cache, max_tokens=64):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # Decode steps take ~0.05-0.3 ms: 200 timed steps after 50 warm-up steps keep the clocks
+    # at their steady state (30 steps after 10 read ~10% slow) and still finish in seconds.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--sweep", default=",".join(DEFAULT_SWEEP),
                     help="comma-separated extra workloads reported under 'sweep'")
@@ -400,8 +409,9 @@ def main():
     sweep = []
     if not args.no_sweep:
         for w in [s for s in args.sweep.split(",") if s and s != args.workload]:
-            sweep.append(time_workload(w, max(5, min(args.steps, 20)) if WORKLOADS[w][1] > 64 else args.steps,
-                                       min(args.warmup, 5), cache))
+            big = WORKLOADS[w][1] > 64  # ~1 ms steps: fewer of them
+            sweep.append(time_workload(w, max(5, min(args.steps, 50)) if big else args.steps,
+                                       min(args.warmup, 20) if big else args.warmup, cache))
     cpu = None if args.no_cpu else cpu_baseline(args.workload, cache)
     if args.copy_calibration:
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")

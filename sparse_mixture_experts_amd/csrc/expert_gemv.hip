@@ -55,7 +55,8 @@ hipError_t launch_t(const moe_layer& L, const void* x, int T, const int32_t* per
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
     const bool up_res = chunks(L.d, TT::VEC) <= 8;
     const dim3 gu((ffmax + 4 * kUpUnits - 1) / (4 * kUpUnits), gmax);
-    switch (pick_kb(L.d, TT::VEC)) {
+    // Rows longer than one 8-chunk batch stream in batches of 4 chunks per lane.
+    switch (up_res ? pick_kb(L.d, TT::VEC) : 4) {
 #define SMOE_UP_LAUNCH(KB, RES, EX) \
     expert_up_gemv_kernel<KB, TT, OAI, RES, kUpUnits, EX><<<gu, 256, 0, s>>>(u, meta)
 #define SMOE_UP_CASE(KB)                                                                       \
@@ -85,7 +86,7 @@ hipError_t launch_t(const moe_layer& L, const void* x, int T, const int32_t* per
     const auto dn_exact = [&](int kb) {
         return exact_k(L.ff, TT::VEC, kb) && (L.shared_ff == 0 || exact_k(L.shared_ff, TT::VEC, kb));
     };
-    switch (pick_kb(ffmax, TT::VEC)) {
+    switch (dn_res ? pick_kb(ffmax, TT::VEC) : 4) {
 #define SMOE_DOWN_LAUNCH(KB, NR, RES, EX)                                                      \
     expert_down_gemv_kernel<KB, TT, OAI, RES, NR, EX>                                          \
         <<<dim3((L.d + 4 * (NR) - 1) / (4 * (NR)), gmax), 256, 0, s>>>(dn, meta)

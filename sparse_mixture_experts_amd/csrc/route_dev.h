@@ -12,30 +12,48 @@
 namespace smoe {
 
 constexpr int kRouterNT = 4;  // tokens per rows_dot call
+constexpr int kRouterNR = 4;  // router rows per wave
 
-// One wave: router row `row` (rows 0..E-1 are experts, row E the shared-gate vector) over
-// tokens [t0, t_end), written to logits[t * ld + row] (+ the expert's bias).
+// One wave: router rows row0 .. row0+3 (rows 0..E-1 are experts, row E the shared-gate
+// vector; rows past n_rows repeat the last and are not written) over tokens
+// [t0, t_end), written to logits[t * ld + row] (+ the expert's bias).
 template <int KB, typename TT>
-__device__ __forceinline__ void router_row_wave(const typename TT::storage* __restrict__ x,
-                                                const typename TT::storage* __restrict__ w_router,
-                                                const float* __restrict__ b_router,
-                                                const typename TT::storage* __restrict__ w_sg, int T, int d,
-                                                int E, int row, int t0, int t_end, float* __restrict__ logits,
-                                                int ld) {
-    const typename TT::storage* const wr[1] = {row < E ? w_router + (size_t)row * d : w_sg};
-    const float bias = (row < E && b_router) ? b_router[row] : 0.0f;
-    for (; t0 < t_end; t0 += kRouterNT) {
-        const int nt = min(kRouterNT, t_end - t0);
-        const typename TT::storage* ar[kRouterNT];
+__device__ __forceinline__ void router_rows_wave(const typename TT::storage* __restrict__ x,
+                                                 const typename TT::storage* __restrict__ w_router,
+                                                 const float* __restrict__ b_router,
+                                                 const typename TT::storage* __restrict__ w_sg, int T, int d,
+                                                 int E, int n_rows, int row0, int t0, int t_end,
+                                                 float* __restrict__ logits, int ld) {
+    using S = typename TT::storage;
+    constexpr int NR = kRouterNR, NT = kRouterNT, N = NR * NT;
+    constexpr int SH = 6 - ilog2(N);
+    const S* wr[NR];
 #pragma unroll
-        for (int t = 0; t < kRouterNT; ++t) ar[t] = x + (size_t)min(t0 + t, T - 1) * d;
-        float acc[1][kRouterNT] = {};
-        rows_dot<1, kRouterNT, KB, TT, TT>(wr, ar, nt, d, acc);
+    for (int r = 0; r < NR; ++r) {
+        const int row = min(row0 + r, n_rows - 1);
+        wr[r] = row < E ? w_router + (size_t)row * d : w_sg;
+    }
+    const S* const (&wrc)[NR] = wr;
+    // After the reduction lane l holds value (t * NR + r) = l >> SH.
+    const int lane = lane_id();
+    const int my_t = (lane >> SH) / NR, my_row = row0 + (lane >> SH) % NR;
+    const bool writer = (lane & ((1 << SH) - 1)) == 0 && my_row < n_rows;
+    const float bias = (writer && my_row < E && b_router) ? b_router[my_row] : 0.0f;
+    for (; t0 < t_end; t0 += NT) {
+        const int nt = min(NT, t_end - t0);
+        const S* ar[NT];
 #pragma unroll
-        for (int t = 0; t < kRouterNT; ++t) {
-            const float z = wave_sum(acc[0][t]);
-            if (lane_id() == 0 && t < nt) logits[(size_t)(t0 + t) * ld + row] = z + bias;
-        }
+        for (int t = 0; t < NT; ++t) ar[t] = x + (size_t)min(t0 + t, T - 1) * d;
+        const S* const (&arc)[NT] = ar;
+        float acc[NR][NT] = {};
+        rows_dot<NR, NT, KB, TT, TT>(wrc, arc, nt, d, acc);
+        float v[N];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) v[t * NR + r] = acc[r][t];
+        const float z = wave_reduce_scatter<N>(v);
+        if (writer && my_t < nt) logits[(size_t)(t0 + my_t) * ld + my_row] = z + bias;
     }
 }
 

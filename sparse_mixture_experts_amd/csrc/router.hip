@@ -15,17 +15,18 @@
 namespace smoe {
 namespace {
 
-// One wave per router row (rows 0..E-1 are experts, row E the shared gate vector),
+// Four router rows per wave (rows 0..E-1 are experts, row E the shared gate vector),
 // looping over a chunk of tokens.  Writes logits[t * ld + row].
 template <int KB, typename TT>
 __global__ __launch_bounds__(256) void router_gemv_kernel(
     const typename TT::storage* __restrict__ x, const typename TT::storage* __restrict__ w_router,
     const float* __restrict__ b_router, const typename TT::storage* __restrict__ w_sg, int T, int d,
     int E, int n_rows, int tok_chunk, float* __restrict__ logits, int ld) {
-    const int row = blockIdx.x * 4 + wave_id();
-    if (row >= n_rows) return;
+    const int row0 = (blockIdx.x * 4 + wave_id()) * kRouterNR;
+    if (row0 >= n_rows) return;
     const int t0 = blockIdx.y * tok_chunk;
-    router_row_wave<KB, TT>(x, w_router, b_router, w_sg, T, d, E, row, t0, min(T, t0 + tok_chunk), logits, ld);
+    router_rows_wave<KB, TT>(x, w_router, b_router, w_sg, T, d, E, n_rows, row0, t0, min(T, t0 + tok_chunk),
+                             logits, ld);
 }
 
 // One wave per token: the wave top-k, the weights, and the shared-expert gate input.
@@ -135,11 +136,12 @@ hipError_t launch_router_t(const moe_layer& L, const void* x, int T, float* logi
     // Small batches: one 4-token chunk per block row, so that every wave issues its
     // loads at once; large batches: 64 tokens per block to reuse the router row.
     const int tok_chunk = T <= 256 ? kRouterNT : 64;
-    dim3 grid((n_rows + 3) / 4, (T + tok_chunk - 1) / tok_chunk);
+    dim3 grid((n_rows + 4 * kRouterNR - 1) / (4 * kRouterNR), (T + tok_chunk - 1) / tok_chunk);
     const S* xs = static_cast<const S*>(x);
     const S* wr = static_cast<const S*>(L.w_router);
     const S* wsg = static_cast<const S*>(L.ws_gate_inp);
-    switch (pick_kb(L.d, TT::VEC)) {
+    // Weight batches of at most 4 chunks per lane (longer rows loop over batches).
+    switch (min(pick_kb(L.d, TT::VEC), 4)) {
 #define SMOE_ROUTER_CASE(KB)                                                                   \
     case KB:                                                                                   \
         router_gemv_kernel<KB, TT><<<grid, 256, 0, s>>>(xs, wr, L.b_router, wsg, T, L.d,        \
@@ -149,7 +151,6 @@ hipError_t launch_router_t(const moe_layer& L, const void* x, int T, float* logi
         SMOE_ROUTER_CASE(1)
         SMOE_ROUTER_CASE(2)
         SMOE_ROUTER_CASE(4)
-        SMOE_ROUTER_CASE(8)
 #undef SMOE_ROUTER_CASE
     }
     return hipGetLastError();

@@ -129,6 +129,33 @@ __device__ __forceinline__ void load_w_batch(const typename TW::storage* const (
     }
 }
 
+// Activation chunks per load sub-batch: at most 16 16-byte pieces (64 registers).
+template <int NT, int KB, typename TW, typename TA>
+constexpr int act_sub_batch() {
+    constexpr int per_chunk = NT * ARaw<TA, TW::VEC>::Q;
+    constexpr int n = 16 / per_chunk;
+    return n < 1 ? 1 : (n > KB ? KB : n);
+}
+
+// acc[r][t] += W-batch (registers) . A_t over the batch's K range (same contract on a[t],
+// nt and EXACT as rows_dot).  Chunks past K hold zero weights and activations.  The
+// activations are loaded in sub-batches of at most 64 registers, each loaded in full
+// before its arithmetic.
+template <int NR, int NT, int KB, typename TW, typename TA, bool EXACT = false>
+__device__ __forceinline__ void dot_w_batch(const uint4 (&wv)[KB][NR], const typename TA::storage* const (&a)[NT],
+                                            int nt, int K, int c0, float (&acc)[NR][NT]) {
+    (void)nt;
+    constexpr int KBA = act_sub_batch<NT, KB, TW, TA>();
+    static_assert(KB % KBA == 0, "sub-batches must tile the chunk batch");
+#pragma unroll
+    for (int k0 = 0; k0 < KB; k0 += KBA) {
+        ARaw<TA, TW::VEC> av[KBA][NT];
+        load_a_batch<NT, KBA, TW, TA, EXACT>(a, K, c0 + k0, av);
+#pragma unroll
+        for (int kb = 0; kb < KBA; ++kb) fma_chunk<NR, NT, TW, TA>(wv[k0 + kb], av[kb], acc);
+    }
+}
+
 // acc[r][t] += sum_i W_r[i] * A_t[i] over i < K, for NR weight rows and NT activation
 // rows, computed by one wave.  The K axis is cut into 16-byte chunks of W (TW::VEC
 // elements); lane l takes chunks l, l+64, l+128, ...  Per batch of KB chunks, all
@@ -147,24 +174,9 @@ __device__ __forceinline__ void rows_dot(const typename TW::storage* const (&w)[
     const int nchunk = (K / TW::VEC + kWave - 1) / kWave;
     for (int c0 = 0; c0 < nchunk; c0 += KB) {
         uint4 wv[KB][NR];
-        ARaw<TA, TW::VEC> av[KB][NT];
         load_w_batch<NR, KB, TW, STREAM_W, EXACT>(w, K, c0, wv);
-        load_a_batch<NT, KB, TW, TA, EXACT>(a, K, c0, av);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) fma_chunk<NR, NT, TW, TA>(wv[kb], av[kb], acc);
+        dot_w_batch<NR, NT, KB, TW, TA, EXACT>(wv, a, nt, K, c0, acc);
     }
-}
-
-// acc[r][t] += W-batch (registers) . A_t over the batch's K range (same contract on a[t],
-// nt and EXACT as rows_dot).  Chunks past K hold zero weights and activations.
-template <int NR, int NT, int KB, typename TW, typename TA, bool EXACT = false>
-__device__ __forceinline__ void dot_w_batch(const uint4 (&wv)[KB][NR], const typename TA::storage* const (&a)[NT],
-                                            int nt, int K, int c0, float (&acc)[NR][NT]) {
-    (void)nt;
-    ARaw<TA, TW::VEC> av[KB][NT];
-    load_a_batch<NT, KB, TW, TA, EXACT>(a, K, c0, av);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) fma_chunk<NR, NT, TW, TA>(wv[kb], av[kb], acc);
 }
 
 // Is K a whole number of KB-chunk batches (64 lanes x KB chunks of `vec` elements)?
