@@ -18,16 +18,16 @@
 // by each row's routing weight (or the shared expert's sigmoid gate) so that the
 // combine is a plain sum; output bf16 or fp32.
 //
-// Grouped block: 512 threads = 8 waves in a 2 x 4 grid, each wave a 64 x 64 output tile =
-// 4 x 4 MFMA tiles.  K advances 64 per step through a 3-stage LDS ring filled straight
-// from global memory by global_load_lds_dwordx4 (no register round trip, no LDS store
-// instructions); slice s is issued two steps before it is used, and one barrier per step
-// both publishes slice s and frees the stage that the next issue overwrites.
-// LDS rows are 128 bytes (64 bf16, 8 chunks of 16 B) with chunk c of row r stored at
-// c ^ ((r >> 1) & 7): 16 rows read at one chunk touch 64 distinct banks.  A wave's direct
-// load writes 64 consecutive 16-byte slots (8 rows), so each lane fetches the global
-// chunk that belongs in its slot.  Epilogues go through LDS so that every lane stores
-// whole 16-byte chunks of output rows.
+// Grouped block: 512 threads = 8 waves in a 2 x 4 grid over a 128 x 256 output tile, each
+// wave a 64 x 64 tile = 4 x 4 MFMA tiles.  K advances 32 per step through a 3-stage LDS
+// ring filled straight from global memory by global_load_lds_dwordx4 (no register round
+// trip, no LDS store instructions); slice s is issued two steps before it is used, and one
+// barrier per step both publishes slice s and frees the stage that the next issue
+// overwrites.  Ring rows are 64 bytes (32 bf16, 4 chunks of 16 B) with chunk c of row r
+// stored at c ^ ((r >> 2) & 3): 16 rows read at one logical chunk touch 64 distinct banks.
+// A wave's direct load writes 64 consecutive 16-byte slots (16 rows), so each lane fetches
+// the global chunk that belongs in its slot.  Epilogues go through LDS so that every lane
+// stores whole 16-byte chunks of output rows.
 //
 // The router GEMM (128 tokens x 128 experts per block) keeps a 4-wave, register-staged
 // pipeline: with E = 256 experts a 256-wide tile would leave too few blocks.
