@@ -33,39 +33,12 @@
 // pipeline: with E = 256 experts a 256-wide tile would leave too few blocks.
 #include "common.h"
 #include "internal.h"
+#include "mfma_dev.h"
 
 namespace smoe {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 constexpr int BM = kGroupTileM;  // rows per M-tile
-
-__device__ __forceinline__ float ld_bf16(const uint16_t* p) { return bf16_to_f32(*p); }
-
-// LDS row layouts.  Rows of 64 bf16 (8 chunks of 16 B): chunk c of row r at
-// c ^ ((r >> 1) & 7).  Rows of 32 bf16 (4 chunks): chunk c of row r at c ^ ((r >> 2) & 3).
-// Either way 16 rows read at one logical chunk cover 64 distinct banks.
-template <int KW>
-__device__ __forceinline__ int swz(int r, int c) {
-    if constexpr (KW == 64) return r * 64 + ((c ^ ((r >> 1) & 7)) << 3);
-    else return r * 32 + ((c ^ ((r >> 2) & 3)) << 3);
-}
-
-template <int KW>
-__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* lds, int row, int chunk) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(lds + swz<KW>(row, chunk)));
-}
-
-template <int MI, int NI>
-__device__ __forceinline__ void zero(floatx4 (&acc)[MI][NI]) {
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = floatx4{0.f, 0.f, 0.f, 0.f};
-}
 
 // 32 K of one wave's 64 x 64 tile: 4 A and 4 B fragments from LDS, 16 MFMAs.
 // Fragment layout of v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16 of its
@@ -87,19 +60,6 @@ __device__ __forceinline__ void mfma_k32(const uint16_t* sa, const uint16_t* sb,
         for (int ni = 0; ni < 4; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
 }
-
-// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt: no wait): this lane's vector-memory ops but the
-// newest N are done, and all of its LDS ops are.
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads (whose release would
-// drain the direct loads still in flight); the memory clobber keeps the compiler from
-// moving LDS accesses across it.  Ordering of the direct LDS loads is by wait_vm_lgkm.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // =====================================================================================
 // Grouped GEMM: 8 waves, 128 x 256 block tile, direct-to-LDS 3-stage ring, K = 32 per
@@ -132,6 +92,9 @@ struct GSmem {
     };
 };
 
+// Blocks that fit one CU's 160 KB of LDS (at most 2).
+constexpr int kGBlocksPerCU = sizeof(GSmem) * 2 <= 160 * 1024 ? 2 : 1;
+
 // Source pointers of this lane's direct loads: A segments w + 8j, B segments w + 8j
 // (segment s holds tile rows s * kRowsPerSeg ..).  row_a / row_b map a tile row to its
 // global row.
@@ -149,7 +112,7 @@ __device__ __forceinline__ LoadPlan make_plan(RowA row_a, RowB row_b) {
         const int seg = wave + 8 * (is_a ? j : j - kLoadsA);
         const int r = seg * kRowsPerSeg + lane / kChunksPerRow;
         const int slot = lane % kChunksPerRow;
-        const int c = slot ^ ((r >> 2) & 3);  // logical chunk that belongs in this slot
+        const int c = swz_chunk<GBK>(r, slot);  // logical chunk that belongs in this slot (the map is an involution)
         p.src[j] = (is_a ? row_a(r) : row_b(r)) + c * 8;
     }
     return p;
@@ -182,7 +145,8 @@ __device__ __forceinline__ void grouped_mainloop(GSmem& sm, const LoadPlan& p, i
         lds_barrier();
         const int pre = st == 0 ? 2 : st - 1;  // (kt + 2) % 3
         issue_slice(sm, p, pre, min(kt + 2, nk - 1) * GBK);
-        mfma_k32<GBK>(sm.k.a[st], sm.k.b[st], arow0, brow, 0, acc);
+#pragma unroll
+        for (int kc = 0; kc < GBK / 8; kc += 4) mfma_k32<GBK>(sm.k.a[st], sm.k.b[st], arow0, brow, kc, acc);
         st = st == 2 ? 0 : st + 1;
     }
     wait_vm_lgkm<0>();
@@ -194,7 +158,7 @@ struct UpArgs {
     const int32_t* perm_token;
     const Group* groups;
     const PlanMeta* meta;
-    const int32_t* tile_map;
+    const TileDesc* tiles;
     const uint16_t* w_gate;     // [E, ff, d]
     const uint16_t* w_up;
     const uint16_t* w_gate_up;  // [E, 2ff, d]
@@ -210,7 +174,7 @@ struct DownArgs {
     const uint16_t* H;
     const Group* groups;
     const PlanMeta* meta;
-    const int32_t* tile_map;
+    const TileDesc* tiles;
     const uint16_t* w_down;   // [E, d, ff]
     const uint16_t* b_down;   // [E, d] or null
     const uint16_t* ws_down;  // [d, ffs]
@@ -232,7 +196,7 @@ inline int grid_blocks(int max_mtiles, int n_ntiles) {
 }
 
 // Resolve this block's (group, first row, N-tile).  Returns false if the block is idle.
-__device__ __forceinline__ bool locate(const PlanMeta* meta, const int32_t* tile_map, const Group* groups,
+__device__ __forceinline__ bool locate(const PlanMeta* meta, const TileDesc* tiles, const Group* groups,
                                        int n_ntiles, Group& g, int& m0, int& nt) {
     const int n_tiles = meta->n_tiles;
     const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
@@ -241,17 +205,17 @@ __device__ __forceinline__ bool locate(const PlanMeta* meta, const int32_t* tile
     const int mt = xcd * per_xcd + local;
     nt = slot % n_ntiles;
     if (local >= per_xcd || mt >= n_tiles) return false;
-    g = groups[tile_map[mt]];
+    g = groups[tiles[mt].group];
     m0 = (mt - g.tile0) * BM;
     return true;
 }
 
 template <bool OAI>
-__global__ __launch_bounds__(kGThreads, 2) void gg_up_kernel(UpArgs a) {
+__global__ __launch_bounds__(kGThreads, kGBlocksPerCU) void gg_up_kernel(UpArgs a) {
     __shared__ GSmem sm;
     Group g;
     int m0, nt;
-    if (!locate(a.meta, a.tile_map, a.groups, a.n_ntiles, g, m0, nt)) return;
+    if (!locate(a.meta, a.tiles, a.groups, a.n_ntiles, g, m0, nt)) return;
     const bool shared = g.e < 0;
     const int ffg = shared ? a.ffs : a.ff;
     const int f0 = nt * 128;
@@ -325,11 +289,11 @@ __global__ __launch_bounds__(kGThreads, 2) void gg_up_kernel(UpArgs a) {
 }
 
 template <typename TY>
-__global__ __launch_bounds__(kGThreads, 2) void gg_down_kernel(DownArgs a) {
+__global__ __launch_bounds__(kGThreads, kGBlocksPerCU) void gg_down_kernel(DownArgs a) {
     __shared__ GSmem sm;
     Group g;
     int m0, nt;
-    if (!locate(a.meta, a.tile_map, a.groups, a.n_ntiles, g, m0, nt)) return;
+    if (!locate(a.meta, a.tiles, a.groups, a.n_ntiles, g, m0, nt)) return;
     const bool shared = g.e < 0;
     const int K = shared ? a.ffs : a.ff;
     const int n0 = nt * GBN;
@@ -524,14 +488,14 @@ int grouped_max_mtiles(int E, int T, int k, bool shared) {
 }
 
 hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
-                              const Group* groups, const PlanMeta* meta, const int32_t* tile_map,
+                              const Group* groups, const PlanMeta* meta, const TileDesc* tiles,
                               uint16_t* H, int hstride, const float* row_w, void* y, bool y_bf16,
                               hipStream_t s) {
     const bool shared = L.shared_ff > 0;
     const int mt = grouped_max_mtiles(L.n_expert, T, L.k, shared);
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
     const int nn_up = (ffmax + 127) / 128;
-    UpArgs u{static_cast<const uint16_t*>(x), perm_token, groups, meta, tile_map,
+    UpArgs u{static_cast<const uint16_t*>(x), perm_token, groups, meta, tiles,
              static_cast<const uint16_t*>(L.w_gate), static_cast<const uint16_t*>(L.w_up),
              static_cast<const uint16_t*>(L.w_gate_up), static_cast<const uint16_t*>(L.b_gate_up),
              static_cast<const uint16_t*>(L.ws_gate), static_cast<const uint16_t*>(L.ws_up), H, hstride, T,
@@ -542,7 +506,7 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
     else
         gg_up_kernel<false><<<gu, kGThreads, 0, s>>>(u);
     const int nn = (L.d + GBN - 1) / GBN;
-    DownArgs dn{H, groups, meta, tile_map, static_cast<const uint16_t*>(L.w_down),
+    DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down),
                 static_cast<const uint16_t*>(L.b_down), static_cast<const uint16_t*>(L.ws_down), row_w, y,
                 hstride, L.d, L.ff, L.shared_ff, nn};
     const dim3 gd((unsigned)grid_blocks(mt, nn));

@@ -25,6 +25,12 @@ struct PlanMeta {
     int32_t n_groups, n_tiles, pad0, pad1;
 };
 
+// One M-tile of the grouped kernels: expert e (-1 = shared), first grouped row, rows
+// (1 .. kGroupTileM), index of its group in the group list.
+struct TileDesc {
+    int32_t e, row0, n, group;
+};
+
 inline int max_groups(int E, int T, int k, bool shared) {
     long long tk = (long long)T * k;
     return int((tk < E ? tk : E) + (shared ? 1 : 0));
@@ -44,15 +50,15 @@ hipError_t launch_topk(const moe_layer& L, const float* logits, int ld, int T, i
 hipError_t launch_decode_route(const moe_layer& L, const float* logits, int ld, int T, int32_t* idx,
                                float* w, float* shared_gate, int32_t* offsets, int32_t* perm_token,
                                int32_t* perm_inv, float* row_w, int tile_m, Group* groups,
-                               PlanMeta* meta, int32_t* tile_map, hipStream_t s);
+                               PlanMeta* meta, TileDesc* tiles, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
                           int32_t* perm_token, int32_t* perm_inv, int32_t* counts, int32_t* base,
                           const float* w, float* row_w, hipStream_t s);
 hipError_t launch_plan(const int32_t* offsets, int E, int T, int k, bool shared, int tile_m,
-                       Group* groups, PlanMeta* meta, int32_t* tile_map, hipStream_t s);
+                       Group* groups, PlanMeta* meta, TileDesc* tiles, hipStream_t s);
 int grouped_max_mtiles(int E, int T, int k, bool shared);
 hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
-                              const Group* groups, const PlanMeta* meta, const int32_t* tile_map,
+                              const Group* groups, const PlanMeta* meta, const TileDesc* tiles,
                               uint16_t* H, int hstride, const float* row_w, void* y, bool y_bf16,
                               hipStream_t s);
 // Combine of pre-weighted bf16 rows: y[t] = sum_j Y[perm_inv[t,j]] (+ Y[T*k + t]).
@@ -63,5 +69,6 @@ hipError_t launch_expert_gemv(const moe_layer& L, const void* x, int T, const in
                               float* y_perm, hipStream_t s);
 hipError_t launch_combine(const moe_layer& L, const float* y_perm, const int32_t* perm_inv,
                           const float* w, const float* shared_gate, int T, void* y, hipStream_t s);
+
 
 }  // namespace smoe

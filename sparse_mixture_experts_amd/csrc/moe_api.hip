@@ -20,7 +20,7 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 
 // Byte offsets of every scratch buffer inside the caller's workspace.
 struct Layout {
-    size_t logits, idx, w, sg, counts, base, offsets, perm_token, perm_inv, groups, meta, tile_map,
+    size_t logits, idx, w, sg, counts, base, offsets, perm_token, perm_inv, groups, meta, tiles,
         row_w, H, yperm;
     size_t total;
     int ld, hstride, rows;
@@ -51,7 +51,7 @@ Layout layout_for(const moe_layer& L, int T) {
     o.perm_inv = take(tk * 4);
     o.groups = take(((size_t)L.n_expert + 1) * sizeof(Group));
     o.meta = take(sizeof(PlanMeta));
-    o.tile_map = take((size_t)grouped_max_mtiles(L.n_expert, T, L.k, shared) * 4);
+    o.tiles = take((size_t)grouped_max_mtiles(L.n_expert, T, L.k, shared) * sizeof(TileDesc));
     o.row_w = take((size_t)o.rows * 4);
     // H: fp32 on the GEMV path, bf16 on the grouped path (same region).
     o.H = take((size_t)o.rows * o.hstride * 4);
@@ -136,12 +136,12 @@ moe_status run_experts(const moe_layer& L, const void* x, int T, const int32_t* 
                        void* ws, const Layout& o, bool planned, hipStream_t s) {
     Group* groups = at<Group>(ws, o.groups);
     PlanMeta* meta = at<PlanMeta>(ws, o.meta);
-    int32_t* tile_map = at<int32_t>(ws, o.tile_map);
+    TileDesc* tiles = at<TileDesc>(ws, o.tiles);
     if (!planned)
         SMOE_TRY(launch_plan(offsets, L.n_expert, T, L.k, L.shared_ff > 0, kTileM, groups, meta,
-                             tile_map, s));
+                             tiles, s));
     if (use_grouped(L, T)) {
-        SMOE_TRY(launch_grouped_ffn(L, x, T, perm_token, groups, meta, tile_map, at<uint16_t>(ws, o.H),
+        SMOE_TRY(launch_grouped_ffn(L, x, T, perm_token, groups, meta, tiles, at<uint16_t>(ws, o.H),
                                     o.hstride, row_w, y_rows, y_bf16, s));
     } else {
         SMOE_TRY(launch_expert_gemv(L, x, T, perm_token, groups, meta, at<float>(ws, o.H), o.hstride,
@@ -286,7 +286,7 @@ moe_status moe_forward(const moe_layer* L, const void* x, int32_t T, void* y, vo
     if (fused_route) {
         SMOE_TRY(launch_decode_route(*L, logits, o.ld, T, idx, w, sg, offsets, perm_token, perm_inv,
                                      row_w, kTileM, at<Group>(ws, o.groups), at<PlanMeta>(ws, o.meta),
-                                     at<int32_t>(ws, o.tile_map), s));
+                                     at<TileDesc>(ws, o.tiles), s));
     } else {
         SMOE_TRY(launch_topk(*L, logits, o.ld, T, idx, w, sg, row_w,
                              router_leaves_shared_gate(*L, T) ? x : nullptr, s));

@@ -105,9 +105,9 @@ __global__ __launch_bounds__(512) void permute_single_kernel(const int32_t* __re
 __global__ __launch_bounds__(512) void plan_kernel(const int32_t* __restrict__ offsets, int E, int T,
                                                    int k, int shared, int tile_m, Group* __restrict__ groups,
                                                    PlanMeta* __restrict__ meta,
-                                                   int32_t* __restrict__ tile_map, int tile_cap) {
+                                                   TileDesc* __restrict__ tiles, int tile_cap) {
     __shared__ int tmp[2 * 512 / kWave];
-    plan_block(offsets, E, T, k, shared, tile_m, groups, meta, tile_map, tile_cap, tmp);
+    plan_block(offsets, E, T, k, shared, tile_m, groups, meta, tiles, tile_cap, tmp);
 }
 
 }  // namespace
@@ -128,8 +128,8 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
 }
 
 hipError_t launch_plan(const int32_t* offsets, int E, int T, int k, bool shared, int tile_m,
-                       Group* groups, PlanMeta* meta, int32_t* tile_map, hipStream_t s) {
-    plan_kernel<<<1, 512, 0, s>>>(offsets, E, T, k, shared ? 1 : 0, tile_m, groups, meta, tile_map,
+                       Group* groups, PlanMeta* meta, TileDesc* tiles, hipStream_t s) {
+    plan_kernel<<<1, 512, 0, s>>>(offsets, E, T, k, shared ? 1 : 0, tile_m, groups, meta, tiles,
                                   grouped_max_mtiles(E, T, k, shared));
     return hipGetLastError();
 }

@@ -48,12 +48,12 @@ __device__ __forceinline__ void scatter_chunk(const int32_t* __restrict__ idx, i
 
 // Group list for the expert kernels: every non-empty expert in ascending id, then the
 // shared expert (e = -1) over rows T*k .. T*k+T-1.  tile0 = first M-tile of the group
-// when groups are cut into tiles of tile_m rows; tile_map (optional) gets the group of
+// when groups are cut into tiles of tile_m rows; tiles (optional) gets the descriptor of
 // every M-tile (at most tile_cap entries).
 // Runs on one block with blockDim.x >= E; `tmp` holds 2 * blockDim.x / 64 ints of LDS.
 __device__ __forceinline__ void plan_block(const int32_t* offsets, int E, int T, int k, int shared,
                                            int tile_m, Group* __restrict__ groups,
-                                           PlanMeta* __restrict__ meta, int32_t* __restrict__ tile_map,
+                                           PlanMeta* __restrict__ meta, TileDesc* __restrict__ tiles_out,
                                            int tile_cap, int* tmp) {
     const int e = threadIdx.x;
     // Offsets may come from the caller: clamp them so every group stays inside the
@@ -69,16 +69,18 @@ __device__ __forceinline__ void plan_block(const int32_t* offsets, int E, int T,
     const int pos = ex[0], tile0 = ex[1], n_active = tot[0], n_tiles = tot[1];
     if (flag) {
         groups[pos] = Group{e, row0, n, tile0};
-        if (tile_map)
-            for (int i = 0; i < tiles && tile0 + i < tile_cap; ++i) tile_map[tile0 + i] = pos;
+        if (tiles_out)
+            for (int i = 0; i < tiles && tile0 + i < tile_cap; ++i)
+                tiles_out[tile0 + i] = TileDesc{e, row0 + i * tile_m, min(tile_m, n - i * tile_m), pos};
     }
     if (e == 0) {
         int ng = n_active, nt = n_tiles;
         if (shared) {
             groups[ng] = Group{-1, T * k, T, nt};
             const int st = (T + tile_m - 1) / tile_m;
-            if (tile_map)
-                for (int i = 0; i < st && nt + i < tile_cap; ++i) tile_map[nt + i] = ng;
+            if (tiles_out)
+                for (int i = 0; i < st && nt + i < tile_cap; ++i)
+                    tiles_out[nt + i] = TileDesc{-1, T * k + i * tile_m, min(tile_m, T - i * tile_m), ng};
             ++ng;
             nt += st;
         }

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(1024) void decode_route_kernel(
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, float* __restrict__ sg_out,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token, int32_t* __restrict__ perm_inv,
     float* __restrict__ row_w, int shared, int tile_m, Group* __restrict__ groups,
-    PlanMeta* __restrict__ meta, int32_t* __restrict__ tile_map, int tile_cap, int topk_here) {
+    PlanMeta* __restrict__ meta, TileDesc* __restrict__ tiles, int tile_cap, int topk_here) {
     __shared__ float s_w[kPermChunk * 32];
     __shared__ int32_t s_idx[kPermChunk * 32];
     __shared__ unsigned long long mask[kMaxE];
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(1024) void decode_route_kernel(
     }
     __syncthreads();
     scatter_chunk(s_idx, T, k, E, 0, mask, base_row, perm_token, perm_inv, s_w, row_w);
-    plan_block(base_row, E, T, k, shared, tile_m, groups, meta, tile_map, tile_cap, tmp);
+    plan_block(base_row, E, T, k, shared, tile_m, groups, meta, tiles, tile_cap, tmp);
 }
 
 template <typename TT>
@@ -161,7 +161,7 @@ hipError_t launch_router_t(const moe_layer& L, const void* x, int T, float* logi
 hipError_t launch_decode_route(const moe_layer& L, const float* logits, int ld, int T, int32_t* idx,
                                float* w, float* shared_gate, int32_t* offsets, int32_t* perm_token,
                                int32_t* perm_inv, float* row_w, int tile_m, Group* groups,
-                               PlanMeta* meta, int32_t* tile_map, hipStream_t s) {
+                               PlanMeta* meta, TileDesc* tiles, hipStream_t s) {
     // One block holds 16 waves: beyond 16 tokens the top-k runs as its own launch.
     const bool topk_here = T <= 1024 / kWave;
     if (!topk_here) {
@@ -170,7 +170,7 @@ hipError_t launch_decode_route(const moe_layer& L, const float* logits, int ld, 
     }
     decode_route_kernel<<<1, 1024, 0, s>>>(logits, ld, T, L.n_expert, L.k, L.route, L.route_scale, idx,
                                            w, shared_gate, offsets, perm_token, perm_inv, row_w,
-                                           L.shared_ff > 0 ? 1 : 0, tile_m, groups, meta, tile_map,
+                                           L.shared_ff > 0 ? 1 : 0, tile_m, groups, meta, tiles,
                                            grouped_max_mtiles(L.n_expert, T, L.k, L.shared_ff > 0),
                                            topk_here ? 1 : 0);
     return hipGetLastError();

@@ -53,6 +53,8 @@ def xdev(x):
 SMALL = [
     ("tiny_f32", {}, [1, 16, 77]),
     ("qwen", dict(d=512, n_expert=64, ff=192, shared_ff=128), [1, 5, 64, 150]),
+    # Shared expert as wide as the routed ones, whole 256-column N-tiles.
+    ("qwen", dict(d=512, n_expert=64, ff=256, shared_ff=256), [1, 5, 150, 300]),
     ("qwen_zipf", dict(d=512, ff=128, shared_ff=192), [300]),
     ("gptoss", dict(d=320, n_expert=16, ff=192), [1, 7, 100]),
     ("mixtral", dict(d=256, ff=448), [3, 130]),
@@ -62,7 +64,7 @@ SMALL_CASES = [(n, ov, T) for n, ov, Ts in SMALL for T in Ts]
 
 def _id(c):
     n, ov, T = c
-    return f"{n}-T{T}"
+    return f"{n}-ff{ov['ff']}-T{T}" if "ff" in ov else f"{n}-T{T}"
 
 
 @pytest.mark.parametrize("c", SMALL_CASES, ids=_id)
@@ -352,3 +354,31 @@ def test_full_other_layers(name, T, sample):
         ref, got = oracle.moe_forward(L, x[tok]), yn[tok]
     e = assert_close(got, ref, "bf16", "y")
     say(f"  rel err {e:.2e}")
+
+
+def test_grouped_many_tiles():
+    # 4096 tokens, 64 experts of 256 units, shared expert: ~290 M-tiles x 2 N-tiles, more
+    # tiles than blocks in flight and several M-tiles per expert.  Rows of the expert stage
+    # (fp32) and the layer output are compared on a seeded sample of tokens.
+    ov = dict(d=512, n_expert=64, ff=256, shared_ff=256)
+    T = 4096
+    say("grouped many tiles", ov, T)
+    L, x = case("qwen", T, **ov)
+    lay = dev_layer("qwen", **ov)
+    ridx, rw, rsg = oracle.route(L, x)
+    idx, _, _ = moe_mod().route(lay, xdev(x))
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    _, roff, rpt, rinv = oracle.permute(ridx, L["n_expert"])
+    yp = moe_mod().expert_ffn(lay, xdev(x), torch.from_numpy(roff.astype(np.int32)).cuda(),
+                             torch.from_numpy(rpt.astype(np.int32)).cuda()).cpu().numpy()
+    y = to_numpy_y(moe_mod().forward(lay, xdev(x)))
+    tok = np.sort(np.random.default_rng(12).choice(T, 192, replace=False))
+    # Expert rows of the sampled tokens: their k routed rows and their shared row.
+    rows = np.concatenate([rinv[tok].reshape(-1), T * L["k"] + tok])
+    ref_rows = np.concatenate([
+        np.stack([oracle.expert_apply(L, int(ridx[t, j]), oracle.widen(x[t:t + 1]))[0]
+                  for t in tok for j in range(L["k"])]),
+        oracle.swiglu_ffn(oracle.widen(x[tok]), oracle.widen(L["ws_gate"]), oracle.widen(L["ws_up"]),
+                          oracle.widen(L["ws_down"]))])
+    assert_close(yp[rows], ref_rows, "bf16", "expert rows")
+    assert_close(y[tok], oracle.moe_forward(L, x[tok]), "bf16", "y")
