@@ -92,4 +92,57 @@ __device__ __forceinline__ void plan_block(const int32_t* offsets, int E, int T,
 }
 
 
+// Grouping, group list and M-tile descriptors of at most 64 routed rows (T * k <= 64,
+// tile_m >= 64) by one wave, for the decode routing kernel.  Lane p holds entry p (token
+// p / k, slot p % k, expert idx[p]); the order is the same as the chunked path's:
+// ascending expert, then ascending p (ascending token).  A radix rank over the expert id
+// bits (ballots from the top bit down) gives each entry the number of entries with a
+// smaller expert and, among those with the same expert, the ones before it.  Each group
+// holds at most 64 rows, so it is one M-tile.  Out-of-range ids get perm_inv = -1.
+__device__ __forceinline__ void group_wave_small(const int32_t* idx, const float* w, int T, int k, int E,
+                                                 int shared, int32_t* __restrict__ perm_token,
+                                                 int32_t* __restrict__ perm_inv, float* __restrict__ row_w,
+                                                 Group* __restrict__ groups, PlanMeta* __restrict__ meta,
+                                                 TileDesc* __restrict__ tiles, int tile_cap) {
+    const int lane = lane_id();
+    const int n = T * k;
+    const bool valid = lane < n;
+    const int e = valid ? idx[lane] : -1;
+    const bool ok = valid && e >= 0 && e < E;
+    unsigned long long eq = __ballot(ok), less = 0ull;
+#pragma unroll
+    for (int b = 9; b >= 0; --b) {  // E <= 512 < 2^10
+        const bool bit = (e >> b) & 1;
+        const unsigned long long B = __ballot(ok && bit);
+        less = bit ? (less | (eq & ~B)) : less;
+        eq = bit ? (eq & B) : (eq & ~B);
+    }
+    const unsigned long long below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(less) + __popcll(eq & below);
+    const bool first = ok && (eq & below) == 0ull;
+    const unsigned long long firsts = __ballot(first);
+    const int gi = __popcll(firsts & less);
+    if (ok) {
+        perm_token[rank] = lane / k;
+        if (row_w) row_w[rank] = w[lane];
+    }
+    if (valid) perm_inv[lane] = ok ? rank : -1;
+    if (first) {
+        const int cnt = __popcll(eq);
+        groups[gi] = Group{e, rank, cnt, gi};
+        if (tiles && gi < tile_cap) tiles[gi] = TileDesc{e, rank, cnt, gi};
+    }
+    if (lane == 0) {
+        int ng = __popcll(firsts);
+        if (shared) {
+            groups[ng] = Group{-1, n, T, ng};
+            if (tiles && ng < tile_cap) tiles[ng] = TileDesc{-1, n, T, ng};
+            ++ng;
+        }
+        meta->n_groups = ng;
+        meta->n_tiles = min(ng, tile_cap);
+        meta->pad0 = meta->pad1 = 0;
+    }
+}
+
 }  // namespace smoe

@@ -12,12 +12,12 @@
 namespace smoe {
 
 constexpr int kRouterNT = 4;  // tokens per rows_dot call
-constexpr int kRouterNR = 4;  // router rows per wave
+constexpr int kRouterNR = 4;  // router rows per wave (a few tokens: 1, for more waves)
 
-// One wave: router rows row0 .. row0+3 (rows 0..E-1 are experts, row E the shared-gate
+// One wave: router rows row0 .. row0+NR-1 (rows 0..E-1 are experts, row E the shared-gate
 // vector; rows past n_rows repeat the last and are not written) over tokens
 // [t0, t_end), written to logits[t * ld + row] (+ the expert's bias).
-template <int KB, typename TT>
+template <int KB, typename TT, int NR>
 __device__ __forceinline__ void router_rows_wave(const typename TT::storage* __restrict__ x,
                                                  const typename TT::storage* __restrict__ w_router,
                                                  const float* __restrict__ b_router,
@@ -25,7 +25,7 @@ __device__ __forceinline__ void router_rows_wave(const typename TT::storage* __r
                                                  int E, int n_rows, int row0, int t0, int t_end,
                                                  float* __restrict__ logits, int ld) {
     using S = typename TT::storage;
-    constexpr int NR = kRouterNR, NT = kRouterNT, N = NR * NT;
+    constexpr int NT = kRouterNT, N = NR * NT;
     constexpr int SH = 6 - ilog2(N);
     const S* wr[NR];
 #pragma unroll

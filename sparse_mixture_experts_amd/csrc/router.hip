@@ -15,17 +15,17 @@
 namespace smoe {
 namespace {
 
-// Four router rows per wave (rows 0..E-1 are experts, row E the shared gate vector),
+// NR router rows per wave (rows 0..E-1 are experts, row E the shared gate vector),
 // looping over a chunk of tokens.  Writes logits[t * ld + row].
-template <int KB, typename TT>
+template <int KB, typename TT, int NR>
 __global__ __launch_bounds__(256) void router_gemv_kernel(
     const typename TT::storage* __restrict__ x, const typename TT::storage* __restrict__ w_router,
     const float* __restrict__ b_router, const typename TT::storage* __restrict__ w_sg, int T, int d,
     int E, int n_rows, int tok_chunk, float* __restrict__ logits, int ld) {
-    const int row0 = (blockIdx.x * 4 + wave_id()) * kRouterNR;
+    const int row0 = (blockIdx.x * 4 + wave_id()) * NR;
     if (row0 >= n_rows) return;
     const int t0 = blockIdx.y * tok_chunk;
-    router_rows_wave<KB, TT>(x, w_router, b_router, w_sg, T, d, E, n_rows, row0, t0, min(T, t0 + tok_chunk),
+    router_rows_wave<KB, TT, NR>(x, w_router, b_router, w_sg, T, d, E, n_rows, row0, t0, min(T, t0 + tok_chunk),
                              logits, ld);
 }
 
@@ -110,6 +110,13 @@ __global__ __launch_bounds__(1024) void decode_route_kernel(
         }
     }
     __syncthreads();
+    if (T * k <= kWave && tile_m >= kWave) {
+        // One wave groups every routed row; expert offsets are not needed by the forward.
+        if (wave == 0)
+            group_wave_small(s_idx, s_w, T, k, E, shared, perm_token, perm_inv, row_w, groups, meta, tiles,
+                             tile_cap);
+        return;
+    }
     build_masks(s_idx, T, k, E, 0, mask);
     const int e = threadIdx.x;
     const int cnt = e < E ? __popcll(mask[e]) : 0;
@@ -134,24 +141,31 @@ hipError_t launch_router_t(const moe_layer& L, const void* x, int T, float* logi
     using S = typename TT::storage;
     const int n_rows = L.n_expert + (L.shared_ff > 0 ? 1 : 0);
     // Small batches: one 4-token chunk per block row, so that every wave issues its
-    // loads at once; large batches: 64 tokens per block to reuse the router row.
+    // loads at once; large batches: 64 tokens per block to reuse the router row.  Up to
+    // two chunks of tokens, one row per wave: four times the waves to stream the matrix.
     const int tok_chunk = T <= 256 ? kRouterNT : 64;
-    dim3 grid((n_rows + 4 * kRouterNR - 1) / (4 * kRouterNR), (T + tok_chunk - 1) / tok_chunk);
+    const bool one_row = T <= 2 * kRouterNT;
+    const int nr = one_row ? 1 : kRouterNR;
+    dim3 grid((n_rows + 4 * nr - 1) / (4 * nr), (T + tok_chunk - 1) / tok_chunk);
     const S* xs = static_cast<const S*>(x);
     const S* wr = static_cast<const S*>(L.w_router);
     const S* wsg = static_cast<const S*>(L.ws_gate_inp);
     // Weight batches of at most 4 chunks per lane (longer rows loop over batches).
     switch (min(pick_kb(L.d, TT::VEC), 4)) {
+#define SMOE_ROUTER_LAUNCH(KB, NR)                                                             \
+    router_gemv_kernel<KB, TT, NR><<<grid, 256, 0, s>>>(xs, wr, L.b_router, wsg, T, L.d,        \
+                                                        L.n_expert, n_rows, tok_chunk, logits, \
+                                                        ld)
 #define SMOE_ROUTER_CASE(KB)                                                                   \
     case KB:                                                                                   \
-        router_gemv_kernel<KB, TT><<<grid, 256, 0, s>>>(xs, wr, L.b_router, wsg, T, L.d,        \
-                                                        L.n_expert, n_rows, tok_chunk, logits, \
-                                                        ld);                                   \
+        if (one_row) SMOE_ROUTER_LAUNCH(KB, 1);                                                \
+        else SMOE_ROUTER_LAUNCH(KB, kRouterNR);                                                \
         break;
         SMOE_ROUTER_CASE(1)
         SMOE_ROUTER_CASE(2)
         SMOE_ROUTER_CASE(4)
 #undef SMOE_ROUTER_CASE
+#undef SMOE_ROUTER_LAUNCH
     }
     return hipGetLastError();
 }
