@@ -19,14 +19,17 @@
 // combine is a plain sum; output bf16 or fp32.
 //
 // Grouped block: 512 threads = 8 waves in a 2 x 4 grid over a 128 x 256 output tile, each
-// wave a 64 x 64 tile = 4 x 4 MFMA tiles.  K advances 32 per step through a 3-stage LDS
-// ring filled straight from global memory by global_load_lds_dwordx4 (no register round
-// trip, no LDS store instructions); slice s is issued two steps before it is used, and one
-// barrier per step both publishes slice s and frees the stage that the next issue
-// overwrites.  Ring rows are 64 bytes (32 bf16, 4 chunks of 16 B) with chunk c of row r
-// stored at c ^ ((r >> 2) & 3): 16 rows read at one logical chunk touch 64 distinct banks.
-// A wave's direct load writes 64 consecutive 16-byte slots (16 rows), so each lane fetches
-// the global chunk that belongs in its slot.  Epilogues go through LDS so that every lane
+// wave a 64 x 64 tile = 4 x 4 MFMA tiles.  K advances one slice (64 for the up kernel,
+// 32 for the down kernel) per step through a 3-stage LDS ring filled straight from global
+// memory by global_load_lds_dwordx4 (no register round trip, no LDS store instructions);
+// slice s is issued two steps before it is used, and one barrier per step both publishes
+// slice s and frees the stage that the next issue overwrites.  Ring rows of 64 bf16
+// (8 chunks of 16 B) store chunk c of row r at c ^ ((r >> 1) & 7), rows of 32 bf16 at
+// c ^ ((r >> 2) & 3): 16 rows read at one logical chunk touch 64 distinct banks.  A wave's
+// direct load writes 64 consecutive 16-byte slots (8 or 16 rows), so each lane fetches the
+// global chunk that belongs in its slot.  Whole 128-byte rows per slice halve the L2
+// requests of 64-byte rows (each request returns a full cache line); that pays in the up
+// kernel's long K loop.  Epilogues go through LDS so that every lane
 // stores whole 16-byte chunks of output rows.
 //
 // The router GEMM (128 tokens x 128 experts per block) keeps a 4-wave, register-staged
@@ -62,29 +65,37 @@ __device__ __forceinline__ void mfma_k32(const uint16_t* sa, const uint16_t* sb,
 }
 
 // =====================================================================================
-// Grouped GEMM: 8 waves, 128 x 256 block tile, direct-to-LDS 3-stage ring, K = 32 per
-// step (64-byte LDS rows), 72 KB of LDS per block so that two blocks share a CU.
+// Grouped GEMM: 8 waves, 128 x 256 block tile, direct-to-LDS 3-stage ring of K-slices
+// KW wide.  Up: KW = 64 (128-byte LDS rows, whole cache lines per row; 144 KB of LDS, one
+// block per CU).  Down (K = ff, a few slices per tile): KW = 32 (72 KB, two blocks per
+// CU, so one block's prologue and epilogue overlap the other's main loop).
 // =====================================================================================
 constexpr int GBN = 256;
-constexpr int GBK = 32;
 constexpr int kGThreads = 512;
 constexpr int kStages = 3;
-constexpr int kRowsPerSeg = 1024 / (GBK * 2);  // LDS rows per 1 KB direct-load segment
-constexpr int kChunksPerRow = GBK / 8;
-constexpr int kSegA = BM / kRowsPerSeg;         // segments per A slice
-constexpr int kSegB = GBN / kRowsPerSeg;        // ... per B slice
-constexpr int kLoadsA = kSegA / 8, kLoadsB = kSegB / 8;  // per wave (8 waves)
-constexpr int kLoads = kLoadsA + kLoadsB;                  // direct loads per lane per slice
+constexpr int kUpKW = 64;
+constexpr int kDownKW = 32;
+
+template <int KW>
+struct Ring {
+    static constexpr int kRowsPerSeg = 1024 / (KW * 2);  // LDS rows per 1 KB direct-load segment
+    static constexpr int kChunksPerRow = KW / 8;
+    static constexpr int kSegA = BM / kRowsPerSeg;        // segments per A slice
+    static constexpr int kSegB = GBN / kRowsPerSeg;       // ... per B slice
+    static constexpr int kLoadsA = kSegA / 8, kLoadsB = kSegB / 8;  // per wave (8 waves)
+    static constexpr int kLoads = kLoadsA + kLoadsB;                  // direct loads per lane per slice
+};
 
 constexpr int kUpStage = 128 + 8;       // bf16 H tile 128 x 128
 constexpr int kDownStageH = GBN + 8;    // bf16 output tile 128 x 256
 constexpr int kDownStageF = GBN / 2 + 4;  // fp32 output tile, one 128-column half at a time
 
+template <int KW>
 struct GSmem {
     union {
         struct {
-            uint16_t a[kStages][BM * GBK];
-            uint16_t b[kStages][GBN * GBK];
+            uint16_t a[kStages][BM * KW];
+            uint16_t b[kStages][GBN * KW];
         } k;
         uint16_t up[BM * kUpStage];
         uint16_t down_h[BM * kDownStageH];
@@ -93,37 +104,42 @@ struct GSmem {
 };
 
 // Blocks that fit one CU's 160 KB of LDS (at most 2).
-constexpr int kGBlocksPerCU = sizeof(GSmem) * 2 <= 160 * 1024 ? 2 : 1;
+template <int KW>
+constexpr int blocks_per_cu() { return sizeof(GSmem<KW>) * 2 <= 160 * 1024 ? 2 : 1; }
 
 // Source pointers of this lane's direct loads: A segments w + 8j, B segments w + 8j
 // (segment s holds tile rows s * kRowsPerSeg ..).  row_a / row_b map a tile row to its
 // global row.
+template <int KW>
 struct LoadPlan {
-    const uint16_t* src[kLoads];
+    const uint16_t* src[Ring<KW>::kLoads];
 };
 
-template <typename RowA, typename RowB>
-__device__ __forceinline__ LoadPlan make_plan(RowA row_a, RowB row_b) {
-    LoadPlan p;
+template <int KW, typename RowA, typename RowB>
+__device__ __forceinline__ LoadPlan<KW> make_plan(RowA row_a, RowB row_b) {
+    using R = Ring<KW>;
+    LoadPlan<KW> p;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-        const bool is_a = j < kLoadsA;
-        const int seg = wave + 8 * (is_a ? j : j - kLoadsA);
-        const int r = seg * kRowsPerSeg + lane / kChunksPerRow;
-        const int slot = lane % kChunksPerRow;
-        const int c = swz_chunk<GBK>(r, slot);  // logical chunk that belongs in this slot (the map is an involution)
+    for (int j = 0; j < R::kLoads; ++j) {
+        const bool is_a = j < R::kLoadsA;
+        const int seg = wave + 8 * (is_a ? j : j - R::kLoadsA);
+        const int r = seg * R::kRowsPerSeg + lane / R::kChunksPerRow;
+        const int slot = lane % R::kChunksPerRow;
+        const int c = swz_chunk<KW>(r, slot);  // logical chunk that belongs in this slot (the map is an involution)
         p.src[j] = (is_a ? row_a(r) : row_b(r)) + c * 8;
     }
     return p;
 }
 
-__device__ __forceinline__ void issue_slice(GSmem& sm, const LoadPlan& p, int stage, int k0) {
+template <int KW>
+__device__ __forceinline__ void issue_slice(GSmem<KW>& sm, const LoadPlan<KW>& p, int stage, int k0) {
+    using R = Ring<KW>;
     const int wave = threadIdx.x / kWave;
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-        const bool is_a = j < kLoadsA;
-        const int seg = wave + 8 * (is_a ? j : j - kLoadsA);
+    for (int j = 0; j < R::kLoads; ++j) {
+        const bool is_a = j < R::kLoadsA;
+        const int seg = wave + 8 * (is_a ? j : j - R::kLoadsA);
         uint16_t* dst = is_a ? &sm.k.a[stage][seg * 512] : &sm.k.b[stage][seg * 512];  // 1 KB
         __builtin_amdgcn_global_load_lds(p.src[j] + k0, (lds_ptr_t)dst, 16, 0, 0);
     }
@@ -134,19 +150,20 @@ __device__ __forceinline__ void issue_slice(GSmem& sm, const LoadPlan& p, int st
 // step kt-1, whose stage the next issue reuses), issue slice kt+2 (clamped near the end,
 // so the body stays uniform), compute slice kt.  Ends with all loads drained and a
 // barrier, so the caller may reuse the LDS.
-__device__ __forceinline__ void grouped_mainloop(GSmem& sm, const LoadPlan& p, int K, int arow0,
+template <int KW>
+__device__ __forceinline__ void grouped_mainloop(GSmem<KW>& sm, const LoadPlan<KW>& p, int K, int arow0,
                                                  const int (&brow)[4], floatx4 (&acc)[4][4]) {
-    const int nk = K / GBK;
+    const int nk = K / KW;
     issue_slice(sm, p, 0, 0);
-    issue_slice(sm, p, 1, min(1, nk - 1) * GBK);
+    issue_slice(sm, p, 1, min(1, nk - 1) * KW);
     int st = 0;
     for (int kt = 0; kt < nk; ++kt) {
-        wait_vm_lgkm<kLoads>();
+        wait_vm_lgkm<Ring<KW>::kLoads>();
         lds_barrier();
         const int pre = st == 0 ? 2 : st - 1;  // (kt + 2) % 3
-        issue_slice(sm, p, pre, min(kt + 2, nk - 1) * GBK);
+        issue_slice(sm, p, pre, min(kt + 2, nk - 1) * KW);
 #pragma unroll
-        for (int kc = 0; kc < GBK / 8; kc += 4) mfma_k32<GBK>(sm.k.a[st], sm.k.b[st], arow0, brow, kc, acc);
+        for (int kc = 0; kc < KW / 8; kc += 4) mfma_k32<KW>(sm.k.a[st], sm.k.b[st], arow0, brow, kc, acc);
         st = st == 2 ? 0 : st + 1;
     }
     wait_vm_lgkm<0>();
@@ -211,8 +228,8 @@ __device__ __forceinline__ bool locate(const PlanMeta* meta, const TileDesc* til
 }
 
 template <bool OAI>
-__global__ __launch_bounds__(kGThreads, kGBlocksPerCU) void gg_up_kernel(UpArgs a) {
-    __shared__ GSmem sm;
+__global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kernel(UpArgs a) {
+    __shared__ GSmem<kUpKW> sm;
     Group g;
     int m0, nt;
     if (!locate(a.meta, a.tiles, a.groups, a.n_ntiles, g, m0, nt)) return;
@@ -239,7 +256,7 @@ __global__ __launch_bounds__(kGThreads, kGBlocksPerCU) void gg_up_kernel(UpArgs 
                                       : (up ? a.w_up : a.w_gate) + (size_t)g.e * a.ff * d;
         return base + (size_t)f * d;
     };
-    const LoadPlan plan = make_plan(row_a, row_b);
+    const LoadPlan<kUpKW> plan = make_plan<kUpKW>(row_a, row_b);
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int wm = wave >> 2, wn = wave & 3;
     // Wave n-tiles 0,1 are gate units wn*32.., 2,3 the matching up units.
@@ -289,8 +306,8 @@ __global__ __launch_bounds__(kGThreads, kGBlocksPerCU) void gg_up_kernel(UpArgs 
 }
 
 template <typename TY>
-__global__ __launch_bounds__(kGThreads, kGBlocksPerCU) void gg_down_kernel(DownArgs a) {
-    __shared__ GSmem sm;
+__global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_kernel(DownArgs a) {
+    __shared__ GSmem<kDownKW> sm;
     Group g;
     int m0, nt;
     if (!locate(a.meta, a.tiles, a.groups, a.n_ntiles, g, m0, nt)) return;
@@ -302,7 +319,7 @@ __global__ __launch_bounds__(kGThreads, kGBlocksPerCU) void gg_down_kernel(DownA
         const int n = min(n0 + r, a.d - 1);  // partial last N-tile: re-read
         return shared ? a.ws_down + (size_t)n * K : a.w_down + ((size_t)g.e * a.d + n) * K;
     };
-    const LoadPlan plan = make_plan(row_a, row_b);
+    const LoadPlan<kDownKW> plan = make_plan<kDownKW>(row_a, row_b);
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int wm = wave >> 2, wn = wave & 3;
     const int brow[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
