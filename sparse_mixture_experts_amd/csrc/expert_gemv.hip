@@ -19,27 +19,19 @@
 namespace smoe {
 namespace {
 
-// Group handled by grid row y.  With a shared expert (always the last group, and the
-// one with the most rows) grid row 0 takes it, so its longer work starts first.
-__device__ __forceinline__ int group_of_row(int y, int n_groups, bool has_shared) {
-    return has_shared ? (y == 0 ? n_groups - 1 : y - 1) : y;
-}
-
 template <int KB, typename TT, bool OAI, bool RESIDENT, int U, bool EXACT>
-__global__ __launch_bounds__(256) void expert_up_gemv_kernel(GemvUp a, const PlanMeta* meta_p) {
-    const PlanMeta meta = *meta_p;
-    if ((int)blockIdx.y >= meta.n_groups) return;
-    const Group g = a.groups[group_of_row(blockIdx.y, meta.n_groups, a.ffs > 0)];
+__global__ __launch_bounds__(256) void expert_up_gemv_kernel(GemvUp a, const PlanMeta* meta) {
+    Group g;
+    if (!gemv_group(a.groups, meta, a.ffs > 0, a.T, a.tk, g)) return;
     const int ffg = g.e < 0 ? a.ffs : a.ff;
     const int f0 = (blockIdx.x * 4 + wave_id()) * U;
     if (f0 < ffg) up_item<KB, TT, OAI, RESIDENT, U, EXACT>(a, g, f0);
 }
 
 template <int KB, typename TT, bool OAI, bool RESIDENT, int NR, bool EXACT>
-__global__ __launch_bounds__(256) void expert_down_gemv_kernel(GemvDown a, const PlanMeta* meta_p) {
-    const PlanMeta meta = *meta_p;
-    if ((int)blockIdx.y >= meta.n_groups) return;
-    const Group g = a.groups[group_of_row(blockIdx.y, meta.n_groups, a.ffs > 0)];
+__global__ __launch_bounds__(256) void expert_down_gemv_kernel(GemvDown a, const PlanMeta* meta) {
+    Group g;
+    if (!gemv_group(a.groups, meta, a.ffs > 0, a.T, a.tk, g)) return;
     const int i0 = (blockIdx.x * 4 + wave_id()) * NR;
     if (i0 < a.d) down_item<KB, TT, OAI, RESIDENT, NR, down_step_rows<NR>(), EXACT>(a, g, i0);
 }
@@ -51,7 +43,7 @@ hipError_t launch_t(const moe_layer& L, const void* x, int T, const int32_t* per
     const bool shared = L.shared_ff > 0;
     const int gmax = max_groups(L.n_expert, T, L.k, shared);
     GemvUp u{x, perm_token, groups, L.w_gate, L.w_up, L.w_gate_up, L.b_gate_up,
-             L.ws_gate, L.ws_up, H, hstride, T, L.d, L.ff, L.shared_ff, L.oai_alpha, L.oai_limit};
+             L.ws_gate, L.ws_up, H, hstride, T, T * L.k, L.d, L.ff, L.shared_ff, L.oai_alpha, L.oai_limit};
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
     const bool up_res = chunks(L.d, TT::VEC) <= 8;
     const dim3 gu((ffmax + 4 * kUpUnits - 1) / (4 * kUpUnits), gmax);
@@ -76,7 +68,7 @@ hipError_t launch_t(const moe_layer& L, const void* x, int T, const int32_t* per
 #undef SMOE_UP_CASE
 #undef SMOE_UP_LAUNCH
     }
-    GemvDown dn{H, groups, L.w_down, L.b_down, L.ws_down, y_perm, hstride, L.d, L.ff, L.shared_ff};
+    GemvDown dn{H, groups, L.w_down, L.b_down, L.ws_down, y_perm, hstride, T, T * L.k, L.d, L.ff, L.shared_ff};
     const bool dn_res = chunks(ffmax, TT::VEC) <= 8;
     // Fewer than 64 possible groups (T*k + shared below 64 rows): 4 rows per wave, for
     // more waves in flight.

@@ -30,7 +30,7 @@ struct GemvUp {
     const void* ws_gate;    // shared [ffs, d]
     const void* ws_up;
     float* H;
-    int hstride, T, d, ff, ffs;
+    int hstride, T, tk, d, ff, ffs;  // tk = T * k routed rows
     float alpha, limit;
 };
 
@@ -41,8 +41,32 @@ struct GemvDown {
     const void* b_down;   // OAI [E, d] or null
     const void* ws_down;  // [d, ffs]
     float* y;
-    int hstride, d, ff, ffs;
+    int hstride, T, tk, d, ff, ffs;
 };
+
+// Group of grid row blockIdx.y.  The shared expert (when there is one) is the last group
+// of the list and always holds rows tk .. tk+T-1; grid row 0 takes it, built here without
+// a load, so that its longer work starts first.  Grid row y > 0 (or y without a shared
+// expert) takes routed group y - 1 (or y).  The group entry and the group count are
+// loaded together, before the count is checked (the list has room for every grid row),
+// so the two reads cost one memory latency.  Returns false for rows past the count.
+__device__ __forceinline__ bool gemv_group(const Group* groups, const PlanMeta* meta, bool has_shared,
+                                           int T, int tk, Group& g) {
+    const int y = blockIdx.y;
+    const int gi = has_shared ? max(y - 1, 0) : y;
+    // Loaded on every row, so that nothing branches before the loads are issued; both
+    // values are needed at the asm, so the compiler may not sink either load past a check.
+    const Group cand = groups[gi];
+    const int n_groups = meta->n_groups;
+    asm volatile("" ::"s"(cand.e), "s"(cand.row0), "s"(cand.n), "s"(n_groups));
+    if (has_shared && y == 0) {
+        g = Group{-1, tk, T, 0};
+        return true;
+    }
+    if (gi >= n_groups - (has_shared ? 1 : 0)) return false;
+    g = cand;
+    return true;
+}
 
 // One wave: hidden units f0 .. f0+U-1 of group g (those below the group's hidden width),
 // for every row of the group.  RESIDENT: the whole K axis fits one KB-chunk register
@@ -100,7 +124,8 @@ __device__ __forceinline__ void up_item(const GemvUp& a, const Group& g, int f0)
     // loads so that waiting for it does not wait for them.
     auto step_tokens = [&](int tb) {
         const int r = min(tb + (lane & (kNT - 1)), g.n - 1);
-        const int tok = shared ? r : a.perm_token[g.row0 + r];
+        // Shared rows are the tokens in order; with one token every row is token 0.
+        const int tok = (shared || a.T == 1) ? r : a.perm_token[g.row0 + r];
         return min(max(tok, 0), a.T - 1);
     };
     auto step = [&](int tb, int tok_v, const uint4 (&wv)[RESIDENT ? KB : 1][NR]) {
