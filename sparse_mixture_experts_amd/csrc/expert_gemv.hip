@@ -36,10 +36,79 @@ __global__ __launch_bounds__(256) void expert_down_gemv_kernel(GemvDown a, const
     if (i0 < a.d) down_item<KB, TT, OAI, RESIDENT, NR, down_step_rows<NR>(), EXACT>(a, g, i0);
 }
 
+// One token: the down projection of every pick and of the shared expert, and the
+// weighted combine, in one kernel.  Block b owns output dims i0 = b*NR .. i0+NR-1.  Wave
+// j < k takes the token's j-th pick (expert idx[j], weight w[j], hidden row perm_inv[j]);
+// wave k (when there is a shared expert) takes hidden row k with weight sigmoid(gate).
+// Each wave leaves its NR dot products (+ the down bias) in LDS; the first NR threads then
+// sum them in the combine's fixed order, picks 0..k-1 and then the shared expert: the
+// separate down GEMV and combine compute the same sums (up to the order of the cross-lane
+// reduction of each dot product).
+constexpr int kToken1MaxWaves = 16;
+constexpr int kToken1Rows = 4;
+
+template <int KB, typename TT, bool OAI, int NR, bool EXACT>
+__global__ __launch_bounds__(kToken1MaxWaves * kWave) void token1_down_combine_kernel(
+    GemvDown a, const int32_t* __restrict__ idx, const float* __restrict__ w,
+    const int32_t* __restrict__ perm_inv, const float* __restrict__ shared_gate, int E, int k,
+    typename TT::storage* __restrict__ y) {
+    using S = typename TT::storage;
+    __shared__ float part[kToken1MaxWaves][NR];
+    __shared__ float wts[kToken1MaxWaves];
+    const int j = wave_id(), lane = lane_id();
+    const bool shared = j >= k;
+    const int i0 = blockIdx.x * NR;
+    int e = 0, row = k;
+    float weight;
+    if (shared) {
+        weight = 1.0f / (1.0f + expf(-shared_gate[0]));
+    } else {
+        // A pick without a valid hidden row contributes nothing (its weight is zero).
+        const int ei = idx[j], r = perm_inv[j];
+        const bool ok = ei >= 0 && ei < E && r >= 0 && r < k;
+        e = ok ? ei : 0;
+        row = ok ? r : 0;
+        weight = ok ? w[j] : 0.0f;
+    }
+    const int K = shared ? a.ffs : a.ff;
+    const S* base = shared ? static_cast<const S*>(a.ws_down) : static_cast<const S*>(a.w_down) + (size_t)e * a.d * K;
+    const S* wr[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) wr[r] = base + (size_t)min(i0 + r, a.d - 1) * K;
+    const S* const (&wrc)[NR] = wr;
+    const float* ar[1] = {a.H + (size_t)row * a.hstride};
+    const float* const (&arc)[1] = ar;
+    float acc[NR][1] = {};
+    rows_dot<NR, 1, KB, TT, F32, true, EXACT>(wrc, arc, 1, K, acc);
+    float v[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) v[r] = acc[r][0];
+    // After the reduction lane l holds row l >> SH.
+    constexpr int SH = 6 - ilog2(NR);
+    const float sum = wave_reduce_scatter<NR>(v);
+    const int my_r = lane >> SH;
+    float bias = 0.0f;
+    if (OAI && !shared && a.b_down && i0 + my_r < a.d) {
+        const S* b = static_cast<const S*>(a.b_down) + (size_t)e * a.d + i0 + my_r;
+        if constexpr (sizeof(S) == 2) bias = bf16_to_f32(*b);
+        else bias = *b;
+    }
+    if ((lane & ((1 << SH) - 1)) == 0) part[j][my_r] = sum + bias;
+    if (lane == 0) wts[j] = weight;
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < NR && i0 + t < a.d) {
+        const int nw = blockDim.x / kWave;
+        float o = 0.0f;
+        for (int jj = 0; jj < nw; ++jj) o = fmaf(wts[jj], part[jj][t], o);
+        if constexpr (sizeof(S) == 2) y[i0 + t] = f32_to_bf16(o);
+        else y[i0 + t] = o;
+    }
+}
+
 template <typename TT, bool OAI>
-hipError_t launch_t(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
-                    const Group* groups, const PlanMeta* meta, float* H, int hstride, float* y_perm,
-                    hipStream_t s) {
+hipError_t launch_up_t(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
+                       const Group* groups, const PlanMeta* meta, float* H, int hstride, hipStream_t s) {
     const bool shared = L.shared_ff > 0;
     const int gmax = max_groups(L.n_expert, T, L.k, shared);
     GemvUp u{x, perm_token, groups, L.w_gate, L.w_up, L.w_gate_up, L.b_gate_up,
@@ -68,6 +137,15 @@ hipError_t launch_t(const moe_layer& L, const void* x, int T, const int32_t* per
 #undef SMOE_UP_CASE
 #undef SMOE_UP_LAUNCH
     }
+    return hipGetLastError();
+}
+
+template <typename TT, bool OAI>
+hipError_t launch_down_t(const moe_layer& L, int T, const Group* groups, const PlanMeta* meta, const float* H,
+                         int hstride, float* y_perm, hipStream_t s) {
+    const bool shared = L.shared_ff > 0;
+    const int gmax = max_groups(L.n_expert, T, L.k, shared);
+    const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
     GemvDown dn{H, groups, L.w_down, L.b_down, L.ws_down, y_perm, hstride, T, T * L.k, L.d, L.ff, L.shared_ff};
     const bool dn_res = chunks(ffmax, TT::VEC) <= 8;
     // Fewer than 64 possible groups (T*k + shared below 64 rows): 4 rows per wave, for
@@ -109,17 +187,77 @@ hipError_t launch_t(const moe_layer& L, const void* x, int T, const int32_t* per
     return hipGetLastError();
 }
 
+
+template <typename TT, bool OAI>
+hipError_t launch_token1_t(const moe_layer& L, const Group* groups, const float* H, int hstride,
+                           const int32_t* idx, const float* w, const int32_t* perm_inv,
+                           const float* shared_gate, void* y, hipStream_t s) {
+    const bool shared = L.shared_ff > 0;
+    GemvDown dn{H, groups, L.w_down, L.b_down, L.ws_down, nullptr, hstride, 1, L.k, L.d, L.ff, L.shared_ff};
+    const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
+    const dim3 grid((L.d + kToken1Rows - 1) / kToken1Rows);
+    const dim3 block((L.k + (shared ? 1 : 0)) * kWave);
+    auto* yo = static_cast<typename TT::storage*>(y);
+    const auto exact = [&](int kb) {
+        return exact_k(L.ff, TT::VEC, kb) && (L.shared_ff == 0 || exact_k(L.shared_ff, TT::VEC, kb));
+    };
+    // Weight batches of at most 2 chunks per lane: the block may hold 16 waves, which
+    // leaves 128 registers per lane.
+    switch (min(pick_kb(ffmax, TT::VEC), 2)) {
+#define SMOE_T1_CASE(KB)                                                                        \
+    case KB:                                                                                    \
+        if (exact(KB))                                                                          \
+            token1_down_combine_kernel<KB, TT, OAI, kToken1Rows, true>                          \
+                <<<grid, block, 0, s>>>(dn, idx, w, perm_inv, shared_gate, L.n_expert, L.k, yo); \
+        else                                                                                    \
+            token1_down_combine_kernel<KB, TT, OAI, kToken1Rows, false>                         \
+                <<<grid, block, 0, s>>>(dn, idx, w, perm_inv, shared_gate, L.n_expert, L.k, yo); \
+        break;
+        SMOE_T1_CASE(1)
+        SMOE_T1_CASE(2)
+#undef SMOE_T1_CASE
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_expert_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                               const Group* groups, const PlanMeta* meta, float* H, int hstride,
                               float* y_perm, hipStream_t s) {
+    const hipError_t e = launch_expert_up_gemv(L, x, T, perm_token, groups, meta, H, hstride, s);
+    if (e != hipSuccess) return e;
     const bool oai = L.act == MOE_ACT_SWIGLU_OAI;
     if (L.dtype == MOE_BF16)
-        return oai ? launch_t<BF16, true>(L, x, T, perm_token, groups, meta, H, hstride, y_perm, s)
-                   : launch_t<BF16, false>(L, x, T, perm_token, groups, meta, H, hstride, y_perm, s);
-    return oai ? launch_t<F32, true>(L, x, T, perm_token, groups, meta, H, hstride, y_perm, s)
-               : launch_t<F32, false>(L, x, T, perm_token, groups, meta, H, hstride, y_perm, s);
+        return oai ? launch_down_t<BF16, true>(L, T, groups, meta, H, hstride, y_perm, s)
+                   : launch_down_t<BF16, false>(L, T, groups, meta, H, hstride, y_perm, s);
+    return oai ? launch_down_t<F32, true>(L, T, groups, meta, H, hstride, y_perm, s)
+               : launch_down_t<F32, false>(L, T, groups, meta, H, hstride, y_perm, s);
+}
+
+hipError_t launch_expert_up_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
+                                 const Group* groups, const PlanMeta* meta, float* H, int hstride,
+                                 hipStream_t s) {
+    const bool oai = L.act == MOE_ACT_SWIGLU_OAI;
+    if (L.dtype == MOE_BF16)
+        return oai ? launch_up_t<BF16, true>(L, x, T, perm_token, groups, meta, H, hstride, s)
+                   : launch_up_t<BF16, false>(L, x, T, perm_token, groups, meta, H, hstride, s);
+    return oai ? launch_up_t<F32, true>(L, x, T, perm_token, groups, meta, H, hstride, s)
+               : launch_up_t<F32, false>(L, x, T, perm_token, groups, meta, H, hstride, s);
+}
+
+bool token1_fits(const moe_layer& L) { return L.k + (L.shared_ff > 0 ? 1 : 0) <= kToken1MaxWaves; }
+
+hipError_t launch_token1_down_combine(const moe_layer& L, const Group* groups, const float* H, int hstride,
+                                      const int32_t* idx, const float* w, const int32_t* perm_inv,
+                                      const float* shared_gate, void* y, hipStream_t s) {
+    if (!token1_fits(L)) return hipErrorInvalidValue;
+    const bool oai = L.act == MOE_ACT_SWIGLU_OAI;
+    if (L.dtype == MOE_BF16)
+        return oai ? launch_token1_t<BF16, true>(L, groups, H, hstride, idx, w, perm_inv, shared_gate, y, s)
+                   : launch_token1_t<BF16, false>(L, groups, H, hstride, idx, w, perm_inv, shared_gate, y, s);
+    return oai ? launch_token1_t<F32, true>(L, groups, H, hstride, idx, w, perm_inv, shared_gate, y, s)
+               : launch_token1_t<F32, false>(L, groups, H, hstride, idx, w, perm_inv, shared_gate, y, s);
 }
 
 }  // namespace smoe

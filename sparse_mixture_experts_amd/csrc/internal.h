@@ -67,6 +67,16 @@ hipError_t launch_combine_sum(const moe_layer& L, const uint16_t* y_rows, const 
 hipError_t launch_expert_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                               const Group* groups, const PlanMeta* meta, float* H, int hstride,
                               float* y_perm, hipStream_t s);
+// Up GEMV alone (H rows), for callers that finish the layer themselves.
+hipError_t launch_expert_up_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
+                                 const Group* groups, const PlanMeta* meta, float* H, int hstride,
+                                 hipStream_t s);
+// One token (T = 1): down GEMVs of all picks and the shared expert plus the weighted
+// combine, written straight to y.  Needs k (+1 with a shared expert) <= 16.
+bool token1_fits(const moe_layer& L);
+hipError_t launch_token1_down_combine(const moe_layer& L, const Group* groups, const float* H, int hstride,
+                                      const int32_t* idx, const float* w, const int32_t* perm_inv,
+                                      const float* shared_gate, void* y, hipStream_t s);
 hipError_t launch_combine(const moe_layer& L, const float* y_perm, const int32_t* perm_inv,
                           const float* w, const float* shared_gate, int T, void* y, hipStream_t s);
 

@@ -293,6 +293,15 @@ moe_status moe_forward(const moe_layer* L, const void* x, int32_t T, void* y, vo
         SMOE_TRY(launch_permute(idx, T, L->k, L->n_expert, offsets, perm_token, perm_inv,
                                 at<int32_t>(ws, o.counts), at<int32_t>(ws, o.base), w, row_w, s));
     }
+    if (T == 1 && !grouped && token1_fits(*L)) {
+        // One token: the routing kernel has planned the groups; up GEMV, then the down
+        // GEMVs and the combine in one kernel.
+        SMOE_TRY(launch_expert_up_gemv(*L, x, T, perm_token, at<Group>(ws, o.groups), at<PlanMeta>(ws, o.meta),
+                                       at<float>(ws, o.H), o.hstride, s));
+        SMOE_TRY(launch_token1_down_combine(*L, at<Group>(ws, o.groups), at<float>(ws, o.H), o.hstride, idx, w,
+                                            perm_inv, sg, y, s));
+        return MOE_OK;
+    }
     st = run_experts(*L, x, T, offsets, perm_token, y_rows, row_w, grouped, ws, o, fused_route, s);
     if (st != MOE_OK) return st;
     if (grouped)

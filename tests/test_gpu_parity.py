@@ -57,7 +57,7 @@ SMALL = [
     ("qwen", dict(d=512, n_expert=64, ff=256, shared_ff=256), [1, 5, 150, 300]),
     ("qwen_zipf", dict(d=512, ff=128, shared_ff=192), [300]),
     ("gptoss", dict(d=320, n_expert=16, ff=192), [1, 7, 100]),
-    ("mixtral", dict(d=256, ff=448), [3, 130]),
+    ("mixtral", dict(d=256, ff=448), [1, 3, 130]),
 ]
 SMALL_CASES = [(n, ov, T) for n, ov, Ts in SMALL for T in Ts]
 
