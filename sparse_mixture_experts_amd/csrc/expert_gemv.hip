@@ -15,6 +15,7 @@
 // Grids are sized for the largest possible number of groups; blocks beyond the
 // device-side group count return at once, so no host synchronisation is needed.
 #include "gemv_items.h"
+#include "route_dev.h"
 
 namespace smoe {
 namespace {
@@ -36,9 +37,42 @@ __global__ __launch_bounds__(256) void expert_down_gemv_kernel(GemvDown a, const
     if (i0 < a.d) down_item<KB, TT, OAI, RESIDENT, NR, down_step_rows<NR>(), EXACT>(a, g, i0);
 }
 
+// One token: routing and the up projection in one kernel.  Grid row 0 (with a shared
+// expert) is the shared expert, hidden row k, and starts streaming at once; grid row y
+// of a pick j = y - 1 (or y) runs the token's top-k on every wave (the same wave top-k as
+// the routing kernels) and takes its j-th pick, hidden row j.  Block 0 of each pick row
+// records the pick (idx[j], w[j]) for the down kernel.
+template <int KB, typename TT, bool OAI, bool RESIDENT, int U, bool EXACT>
+__global__ __launch_bounds__(256) void token1_up_kernel(GemvUp a, const float* __restrict__ logits, int E,
+                                                        int k, int mode, float scale, int32_t* __restrict__ idx,
+                                                        float* __restrict__ w) {
+    const bool has_shared = a.ffs > 0;
+    const int y = blockIdx.y;
+    const int f0 = (blockIdx.x * 4 + wave_id()) * U;
+    Group g;
+    if (has_shared && y == 0) {
+        g = Group{-1, k, 1, 0};
+    } else {
+        if (f0 >= a.ff) return;  // never block 0's first wave, which records the pick
+        const int j = has_shared ? y - 1 : y;
+        int my_i;
+        float my_w;
+        topk_wave(logits, E, k, mode, scale, &my_i, &my_w);
+        if (blockIdx.x == 0 && wave_id() == 0 && lane_id() == j) {
+            idx[j] = my_i;
+            w[j] = my_w;
+        }
+        const int e = __builtin_amdgcn_readlane(my_i, j);
+        g = Group{min(max(e, 0), E - 1), j, 1, 0};
+    }
+    const int ffg = g.e < 0 ? a.ffs : a.ff;
+    if (f0 < ffg) up_item<KB, TT, OAI, RESIDENT, U, EXACT>(a, g, f0);
+}
+
 // One token: the down projection of every pick and of the shared expert, and the
 // weighted combine, in one kernel.  Block b owns output dims i0 = b*NR .. i0+NR-1.  Wave
-// j < k takes the token's j-th pick (expert idx[j], weight w[j], hidden row perm_inv[j]);
+// j < k takes the token's j-th pick (expert idx[j], weight w[j], hidden row perm_inv[j],
+// or row j without perm_inv);
 // wave k (when there is a shared expert) takes hidden row k with weight sigmoid(gate).
 // Each wave leaves its NR dot products (+ the down bias) in LDS; the first NR threads then
 // sum them in the combine's fixed order, picks 0..k-1 and then the shared expert: the
@@ -64,7 +98,7 @@ __global__ __launch_bounds__(kToken1MaxWaves * kWave) void token1_down_combine_k
         weight = 1.0f / (1.0f + expf(-shared_gate[0]));
     } else {
         // A pick without a valid hidden row contributes nothing (its weight is zero).
-        const int ei = idx[j], r = perm_inv[j];
+        const int ei = idx[j], r = perm_inv ? perm_inv[j] : j;
         const bool ok = ei >= 0 && ei < E && r >= 0 && r < k;
         e = ok ? ei : 0;
         row = ok ? r : 0;
@@ -189,6 +223,39 @@ hipError_t launch_down_t(const moe_layer& L, int T, const Group* groups, const P
 
 
 template <typename TT, bool OAI>
+hipError_t launch_token1_up_t(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,
+                              float* H, int hstride, hipStream_t s) {
+    const bool shared = L.shared_ff > 0;
+    GemvUp u{x, nullptr, nullptr, L.w_gate, L.w_up, L.w_gate_up, L.b_gate_up,
+             L.ws_gate, L.ws_up, H, hstride, 1, L.k, L.d, L.ff, L.shared_ff, L.oai_alpha, L.oai_limit};
+    const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
+    const bool up_res = chunks(L.d, TT::VEC) <= 8;
+    const dim3 gu((ffmax + 4 * kUpUnits - 1) / (4 * kUpUnits), L.k + (shared ? 1 : 0));
+    switch (up_res ? pick_kb(L.d, TT::VEC) : 4) {
+#define SMOE_UP_LAUNCH(KB, RES, EX)                                                              \
+    token1_up_kernel<KB, TT, OAI, RES, kUpUnits, EX>                                             \
+        <<<gu, 256, 0, s>>>(u, logits, L.n_expert, L.k, L.route, L.route_scale, idx, w)
+#define SMOE_UP_CASE(KB)                                                                       \
+    case KB:                                                                                   \
+        if (exact_k(L.d, TT::VEC, KB)) {                                                       \
+            if (up_res) SMOE_UP_LAUNCH(KB, true, true);                                        \
+            else SMOE_UP_LAUNCH(KB, false, true);                                              \
+        } else {                                                                               \
+            if (up_res) SMOE_UP_LAUNCH(KB, true, false);                                       \
+            else SMOE_UP_LAUNCH(KB, false, false);                                             \
+        }                                                                                      \
+        break;
+        SMOE_UP_CASE(1)
+        SMOE_UP_CASE(2)
+        SMOE_UP_CASE(4)
+        SMOE_UP_CASE(8)
+#undef SMOE_UP_CASE
+#undef SMOE_UP_LAUNCH
+    }
+    return hipGetLastError();
+}
+
+template <typename TT, bool OAI>
 hipError_t launch_token1_t(const moe_layer& L, const Group* groups, const float* H, int hstride,
                            const int32_t* idx, const float* w, const int32_t* perm_inv,
                            const float* shared_gate, void* y, hipStream_t s) {
@@ -244,6 +311,17 @@ hipError_t launch_expert_up_gemv(const moe_layer& L, const void* x, int T, const
                    : launch_up_t<BF16, false>(L, x, T, perm_token, groups, meta, H, hstride, s);
     return oai ? launch_up_t<F32, true>(L, x, T, perm_token, groups, meta, H, hstride, s)
                : launch_up_t<F32, false>(L, x, T, perm_token, groups, meta, H, hstride, s);
+}
+
+hipError_t launch_token1_up(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,
+                            float* H, int hstride, hipStream_t s) {
+    if (!token1_fits(L)) return hipErrorInvalidValue;
+    const bool oai = L.act == MOE_ACT_SWIGLU_OAI;
+    if (L.dtype == MOE_BF16)
+        return oai ? launch_token1_up_t<BF16, true>(L, x, logits, idx, w, H, hstride, s)
+                   : launch_token1_up_t<BF16, false>(L, x, logits, idx, w, H, hstride, s);
+    return oai ? launch_token1_up_t<F32, true>(L, x, logits, idx, w, H, hstride, s)
+               : launch_token1_up_t<F32, false>(L, x, logits, idx, w, H, hstride, s);
 }
 
 bool token1_fits(const moe_layer& L) { return L.k + (L.shared_ff > 0 ? 1 : 0) <= kToken1MaxWaves; }

@@ -71,9 +71,13 @@ hipError_t launch_expert_gemv(const moe_layer& L, const void* x, int T, const in
 hipError_t launch_expert_up_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                                  const Group* groups, const PlanMeta* meta, float* H, int hstride,
                                  hipStream_t s);
-// One token (T = 1): down GEMVs of all picks and the shared expert plus the weighted
-// combine, written straight to y.  Needs k (+1 with a shared expert) <= 16.
+// One token (T = 1): top-k on the router logits fused into the up GEMV (hidden row j for
+// pick j, row k for the shared expert; the picks go to idx / w), then the down GEMVs of
+// all picks and the shared expert plus the weighted combine, written straight to y
+// (perm_inv null: hidden row j for pick j).  Needs k (+1 with a shared expert) <= 16.
 bool token1_fits(const moe_layer& L);
+hipError_t launch_token1_up(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,
+                            float* H, int hstride, hipStream_t s);
 hipError_t launch_token1_down_combine(const moe_layer& L, const Group* groups, const float* H, int hstride,
                                       const int32_t* idx, const float* w, const int32_t* perm_inv,
                                       const float* shared_gate, void* y, hipStream_t s);

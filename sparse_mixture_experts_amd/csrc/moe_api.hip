@@ -282,6 +282,14 @@ moe_status moe_forward(const moe_layer* L, const void* x, int32_t T, void* y, vo
     float* row_w = grouped ? at<float>(ws, o.row_w) : nullptr;
     void* y_rows = at<void>(ws, o.yperm);
     SMOE_TRY(run_router(*L, x, T, logits, o.ld, s));
+    if (T == 1 && !grouped && token1_fits(*L)) {
+        // One token: top-k inside the up GEMV, then the down GEMVs and the combine in one
+        // kernel (no grouping: hidden row j holds pick j).
+        SMOE_TRY(launch_token1_up(*L, x, logits, idx, w, at<float>(ws, o.H), o.hstride, s));
+        SMOE_TRY(launch_token1_down_combine(*L, at<Group>(ws, o.groups), at<float>(ws, o.H), o.hstride, idx, w,
+                                            nullptr, shared ? logits + L->n_expert : nullptr, y, s));
+        return MOE_OK;
+    }
     const bool fused_route = T <= kPermChunk;
     if (fused_route) {
         SMOE_TRY(launch_decode_route(*L, logits, o.ld, T, idx, w, sg, offsets, perm_token, perm_inv,
@@ -292,15 +300,6 @@ moe_status moe_forward(const moe_layer* L, const void* x, int32_t T, void* y, vo
                              router_leaves_shared_gate(*L, T) ? x : nullptr, s));
         SMOE_TRY(launch_permute(idx, T, L->k, L->n_expert, offsets, perm_token, perm_inv,
                                 at<int32_t>(ws, o.counts), at<int32_t>(ws, o.base), w, row_w, s));
-    }
-    if (T == 1 && !grouped && token1_fits(*L)) {
-        // One token: the routing kernel has planned the groups; up GEMV, then the down
-        // GEMVs and the combine in one kernel.
-        SMOE_TRY(launch_expert_up_gemv(*L, x, T, perm_token, at<Group>(ws, o.groups), at<PlanMeta>(ws, o.meta),
-                                       at<float>(ws, o.H), o.hstride, s));
-        SMOE_TRY(launch_token1_down_combine(*L, at<Group>(ws, o.groups), at<float>(ws, o.H), o.hstride, idx, w,
-                                            perm_inv, sg, y, s));
-        return MOE_OK;
     }
     st = run_experts(*L, x, T, offsets, perm_token, y_rows, row_w, grouped, ws, o, fused_route, s);
     if (st != MOE_OK) return st;
