@@ -374,6 +374,44 @@ def cpu_baseline(name, layer_cache, max_tokens=64):
                       f"({med:.2f} s each, {sum(times):.1f} s in all, bf16->fp64 weight widening included)"}
 
 
+def vendor_gemm_reference():
+    """Context for the prefill MFMA fraction: the vendor GEMM library (hipBLASLt through
+    torch.mm / torch.bmm) on the expert shapes of the Qwen T=8192 layer, without the
+    gather, the Zipf skew or the fused activation.  Times are HIP-event means of 20 calls
+    after 5 warm-up calls; bf16 in, fp32 accumulation."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    rows = 8192 * 8 + 8192  # routed rows + shared rows
+    cases = [("dense up: all rows, one weight matrix", None, rows, 2048, 1024),
+             ("dense down: all rows, one weight matrix", None, rows, 512, 2048),
+             ("batched up: 256 experts x 288 rows", 256, 288, 2048, 1024),
+             ("batched down: 256 experts x 288 rows", 256, 288, 512, 2048)]
+    out = []
+    for name, E, M, K, N in cases:
+        if E is None:
+            a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+            b = torch.randn(N, K, device="cuda", dtype=torch.bfloat16, generator=g)
+            fn, flops = (lambda: torch.mm(a, b.t())), 2.0 * M * N * K
+        else:
+            a = torch.randn(E, M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+            b = torch.randn(E, K, N, device="cuda", dtype=torch.bfloat16, generator=g).contiguous()
+            fn, flops = (lambda: torch.bmm(a, b)), 2.0 * E * M * N * K
+        for _ in range(5):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        tf = flops / (ms * 1e-3) / 1e12
+        out.append({"case": name, "us": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                    "mfma_frac": round(tf * 1e12 / MFMA_BF16_PEAK, 3)})
+        del a, b
+    print(json.dumps({"vendor_gemm_reference": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -392,6 +430,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/<workload>_hbm_traffic.md from two counter CSVs (no GPU)")
     ap.add_argument("--pmc-command", default="", help="command lines quoted in that summary")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time torch.mm / torch.bmm (hipBLASLt) on the Qwen prefill expert shapes and exit")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -409,6 +449,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.vendor_gemm:
+        vendor_gemm_reference()
+        return
     from sparse_mixture_experts_amd import moe
     moe.lib()
 
