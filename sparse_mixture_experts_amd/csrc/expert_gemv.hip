@@ -69,11 +69,11 @@ __global__ __launch_bounds__(256) void token1_up_kernel(GemvUp a, const float* _
     if (f0 < ffg) up_item<KB, TT, OAI, RESIDENT, U, EXACT>(a, g, f0);
 }
 
-// One token: the down projection of every pick and of the shared expert, and the
-// weighted combine, in one kernel.  Block b owns output dims i0 = b*NR .. i0+NR-1.  Wave
-// j < k takes the token's j-th pick (expert idx[j], weight w[j], hidden row perm_inv[j],
-// or row j without perm_inv);
-// wave k (when there is a shared expert) takes hidden row k with weight sigmoid(gate).
+// A few tokens: the down projection of every pick and of the shared expert, and the
+// weighted combine, in one kernel.  Block (b, t) owns output dims i0 = b*NR .. i0+NR-1 of
+// token t.  Wave j < k takes the token's j-th pick (expert idx[t*k+j], weight w[t*k+j],
+// hidden row perm_inv[t*k+j], or row j for a single token without perm_inv); wave k (when
+// there is a shared expert) takes hidden row T*k + t with weight sigmoid(gate[t]).
 // Each wave leaves its NR dot products (+ the down bias) in LDS; the first NR threads then
 // sum them in the combine's fixed order, picks 0..k-1 and then the shared expert: the
 // separate down GEMV and combine compute the same sums (up to the order of the cross-lane
@@ -84,25 +84,26 @@ constexpr int kToken1Rows = 4;
 template <int KB, typename TT, bool OAI, int NR, bool EXACT>
 __global__ __launch_bounds__(kToken1MaxWaves * kWave) void token1_down_combine_kernel(
     GemvDown a, const int32_t* __restrict__ idx, const float* __restrict__ w,
-    const int32_t* __restrict__ perm_inv, const float* __restrict__ shared_gate, int E, int k,
+    const int32_t* __restrict__ perm_inv, const float* __restrict__ shared_gate, int gate_ld, int E, int k,
     typename TT::storage* __restrict__ y) {
     using S = typename TT::storage;
     __shared__ float part[kToken1MaxWaves][NR];
     __shared__ float wts[kToken1MaxWaves];
     const int j = wave_id(), lane = lane_id();
     const bool shared = j >= k;
-    const int i0 = blockIdx.x * NR;
-    int e = 0, row = k;
+    const int i0 = blockIdx.x * NR, t = blockIdx.y;
+    int e = 0, row = a.tk + t;
     float weight;
     if (shared) {
-        weight = 1.0f / (1.0f + expf(-shared_gate[0]));
+        weight = 1.0f / (1.0f + expf(-shared_gate[(size_t)t * gate_ld]));
     } else {
         // A pick without a valid hidden row contributes nothing (its weight is zero).
-        const int ei = idx[j], r = perm_inv ? perm_inv[j] : j;
-        const bool ok = ei >= 0 && ei < E && r >= 0 && r < k;
+        const int p = t * k + j;
+        const int ei = idx[p], r = perm_inv ? perm_inv[p] : j;
+        const bool ok = ei >= 0 && ei < E && r >= 0 && r < a.tk;
         e = ok ? ei : 0;
         row = ok ? r : 0;
-        weight = ok ? w[j] : 0.0f;
+        weight = ok ? w[p] : 0.0f;
     }
     const int K = shared ? a.ffs : a.ff;
     const S* base = shared ? static_cast<const S*>(a.ws_down) : static_cast<const S*>(a.w_down) + (size_t)e * a.d * K;
@@ -130,13 +131,13 @@ __global__ __launch_bounds__(kToken1MaxWaves * kWave) void token1_down_combine_k
     if ((lane & ((1 << SH) - 1)) == 0) part[j][my_r] = sum + bias;
     if (lane == 0) wts[j] = weight;
     __syncthreads();
-    const int t = threadIdx.x;
-    if (t < NR && i0 + t < a.d) {
+    const int tid = threadIdx.x;
+    if (tid < NR && i0 + tid < a.d) {
         const int nw = blockDim.x / kWave;
         float o = 0.0f;
-        for (int jj = 0; jj < nw; ++jj) o = fmaf(wts[jj], part[jj][t], o);
-        if constexpr (sizeof(S) == 2) y[i0 + t] = f32_to_bf16(o);
-        else y[i0 + t] = o;
+        for (int jj = 0; jj < nw; ++jj) o = fmaf(wts[jj], part[jj][tid], o);
+        if constexpr (sizeof(S) == 2) y[(size_t)t * a.d + i0 + tid] = f32_to_bf16(o);
+        else y[(size_t)t * a.d + i0 + tid] = o;
     }
 }
 
@@ -256,13 +257,13 @@ hipError_t launch_token1_up_t(const moe_layer& L, const void* x, const float* lo
 }
 
 template <typename TT, bool OAI>
-hipError_t launch_token1_t(const moe_layer& L, const Group* groups, const float* H, int hstride,
-                           const int32_t* idx, const float* w, const int32_t* perm_inv,
-                           const float* shared_gate, void* y, hipStream_t s) {
+hipError_t launch_token1_t(const moe_layer& L, int T, const float* H, int hstride, const int32_t* idx,
+                           const float* w, const int32_t* perm_inv, const float* shared_gate, int gate_ld,
+                           void* y, hipStream_t s) {
     const bool shared = L.shared_ff > 0;
-    GemvDown dn{H, groups, L.w_down, L.b_down, L.ws_down, nullptr, hstride, 1, L.k, L.d, L.ff, L.shared_ff};
+    GemvDown dn{H, nullptr, L.w_down, L.b_down, L.ws_down, nullptr, hstride, T, T * L.k, L.d, L.ff, L.shared_ff};
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
-    const dim3 grid((L.d + kToken1Rows - 1) / kToken1Rows);
+    const dim3 grid((L.d + kToken1Rows - 1) / kToken1Rows, T);
     const dim3 block((L.k + (shared ? 1 : 0)) * kWave);
     auto* yo = static_cast<typename TT::storage*>(y);
     const auto exact = [&](int kb) {
@@ -275,10 +276,10 @@ hipError_t launch_token1_t(const moe_layer& L, const Group* groups, const float*
     case KB:                                                                                    \
         if (exact(KB))                                                                          \
             token1_down_combine_kernel<KB, TT, OAI, kToken1Rows, true>                          \
-                <<<grid, block, 0, s>>>(dn, idx, w, perm_inv, shared_gate, L.n_expert, L.k, yo); \
+                <<<grid, block, 0, s>>>(dn, idx, w, perm_inv, shared_gate, gate_ld, L.n_expert, L.k, yo); \
         else                                                                                    \
             token1_down_combine_kernel<KB, TT, OAI, kToken1Rows, false>                         \
-                <<<grid, block, 0, s>>>(dn, idx, w, perm_inv, shared_gate, L.n_expert, L.k, yo); \
+                <<<grid, block, 0, s>>>(dn, idx, w, perm_inv, shared_gate, gate_ld, L.n_expert, L.k, yo); \
         break;
         SMOE_T1_CASE(1)
         SMOE_T1_CASE(2)
@@ -326,16 +327,16 @@ hipError_t launch_token1_up(const moe_layer& L, const void* x, const float* logi
 
 bool token1_fits(const moe_layer& L) { return L.k + (L.shared_ff > 0 ? 1 : 0) <= kToken1MaxWaves; }
 
-hipError_t launch_token1_down_combine(const moe_layer& L, const Group* groups, const float* H, int hstride,
-                                      const int32_t* idx, const float* w, const int32_t* perm_inv,
-                                      const float* shared_gate, void* y, hipStream_t s) {
-    if (!token1_fits(L)) return hipErrorInvalidValue;
+hipError_t launch_token_down_combine(const moe_layer& L, int T, const float* H, int hstride, const int32_t* idx,
+                                     const float* w, const int32_t* perm_inv, const float* shared_gate,
+                                     int gate_ld, void* y, hipStream_t s) {
+    if (!token1_fits(L) || T < 1 || (!perm_inv && T != 1)) return hipErrorInvalidValue;
     const bool oai = L.act == MOE_ACT_SWIGLU_OAI;
     if (L.dtype == MOE_BF16)
-        return oai ? launch_token1_t<BF16, true>(L, groups, H, hstride, idx, w, perm_inv, shared_gate, y, s)
-                   : launch_token1_t<BF16, false>(L, groups, H, hstride, idx, w, perm_inv, shared_gate, y, s);
-    return oai ? launch_token1_t<F32, true>(L, groups, H, hstride, idx, w, perm_inv, shared_gate, y, s)
-               : launch_token1_t<F32, false>(L, groups, H, hstride, idx, w, perm_inv, shared_gate, y, s);
+        return oai ? launch_token1_t<BF16, true>(L, T, H, hstride, idx, w, perm_inv, shared_gate, gate_ld, y, s)
+                   : launch_token1_t<BF16, false>(L, T, H, hstride, idx, w, perm_inv, shared_gate, gate_ld, y, s);
+    return oai ? launch_token1_t<F32, true>(L, T, H, hstride, idx, w, perm_inv, shared_gate, gate_ld, y, s)
+               : launch_token1_t<F32, false>(L, T, H, hstride, idx, w, perm_inv, shared_gate, gate_ld, y, s);
 }
 
 }  // namespace smoe

@@ -72,15 +72,16 @@ hipError_t launch_expert_up_gemv(const moe_layer& L, const void* x, int T, const
                                  const Group* groups, const PlanMeta* meta, float* H, int hstride,
                                  hipStream_t s);
 // One token (T = 1): top-k on the router logits fused into the up GEMV (hidden row j for
-// pick j, row k for the shared expert; the picks go to idx / w), then the down GEMVs of
-// all picks and the shared expert plus the weighted combine, written straight to y
-// (perm_inv null: hidden row j for pick j).  Needs k (+1 with a shared expert) <= 16.
+// pick j, row k for the shared expert; the picks go to idx / w).  A few tokens: the down
+// GEMVs of every pick and of the shared expert plus the weighted combine, written straight
+// to y; hidden rows perm_inv[t*k+j] (null for one token: row j) and T*k + t (shared, gate
+// shared_gate[t * gate_ld]).  Both need k (+1 with a shared expert) <= 16.
 bool token1_fits(const moe_layer& L);
 hipError_t launch_token1_up(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,
                             float* H, int hstride, hipStream_t s);
-hipError_t launch_token1_down_combine(const moe_layer& L, const Group* groups, const float* H, int hstride,
-                                      const int32_t* idx, const float* w, const int32_t* perm_inv,
-                                      const float* shared_gate, void* y, hipStream_t s);
+hipError_t launch_token_down_combine(const moe_layer& L, int T, const float* H, int hstride, const int32_t* idx,
+                                     const float* w, const int32_t* perm_inv, const float* shared_gate,
+                                     int gate_ld, void* y, hipStream_t s);
 hipError_t launch_combine(const moe_layer& L, const float* y_perm, const int32_t* perm_inv,
                           const float* w, const float* shared_gate, int T, void* y, hipStream_t s);
 

@@ -14,6 +14,8 @@ constexpr int kMaxK = 32;
 constexpr int32_t kMaxTokens = 1 << 22;
 constexpr int kDecodeMaxT = 64;  // MOE_PATH_AUTO takes the GEMV path up to this T
 constexpr int kTileM = kGroupTileM;  // M-tile size recorded in the group plan
+// Largest batch whose down projection runs per token, fused with the combine.
+constexpr int kTokenDownMaxT = 8;
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -286,8 +288,8 @@ moe_status moe_forward(const moe_layer* L, const void* x, int32_t T, void* y, vo
         // One token: top-k inside the up GEMV, then the down GEMVs and the combine in one
         // kernel (no grouping: hidden row j holds pick j).
         SMOE_TRY(launch_token1_up(*L, x, logits, idx, w, at<float>(ws, o.H), o.hstride, s));
-        SMOE_TRY(launch_token1_down_combine(*L, at<Group>(ws, o.groups), at<float>(ws, o.H), o.hstride, idx, w,
-                                            nullptr, shared ? logits + L->n_expert : nullptr, y, s));
+        SMOE_TRY(launch_token_down_combine(*L, 1, at<float>(ws, o.H), o.hstride, idx, w, nullptr,
+                                           shared ? logits + L->n_expert : nullptr, o.ld, y, s));
         return MOE_OK;
     }
     const bool fused_route = T <= kPermChunk;
@@ -300,6 +302,14 @@ moe_status moe_forward(const moe_layer* L, const void* x, int32_t T, void* y, vo
                              router_leaves_shared_gate(*L, T) ? x : nullptr, s));
         SMOE_TRY(launch_permute(idx, T, L->k, L->n_expert, offsets, perm_token, perm_inv,
                                 at<int32_t>(ws, o.counts), at<int32_t>(ws, o.base), w, row_w, s));
+    }
+    if (fused_route && !grouped && T <= kTokenDownMaxT && token1_fits(*L)) {
+        // A few tokens: up GEMV over the groups, then per token the down GEMVs of its picks
+        // and the combine in one kernel.
+        SMOE_TRY(launch_expert_up_gemv(*L, x, T, perm_token, at<Group>(ws, o.groups), at<PlanMeta>(ws, o.meta),
+                                       at<float>(ws, o.H), o.hstride, s));
+        SMOE_TRY(launch_token_down_combine(*L, T, at<float>(ws, o.H), o.hstride, idx, w, perm_inv, sg, 1, y, s));
+        return MOE_OK;
     }
     st = run_experts(*L, x, T, offsets, perm_token, y_rows, row_w, grouped, ws, o, fused_route, s);
     if (st != MOE_OK) return st;

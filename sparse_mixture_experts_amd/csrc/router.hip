@@ -142,9 +142,9 @@ hipError_t launch_router_t(const moe_layer& L, const void* x, int T, float* logi
     const int n_rows = L.n_expert + (L.shared_ff > 0 ? 1 : 0);
     // Small batches: one 4-token chunk per block row, so that every wave issues its
     // loads at once; large batches: 64 tokens per block to reuse the router row.  Up to
-    // two chunks of tokens, one row per wave: four times the waves to stream the matrix.
+    // 64 tokens (decode batches), one row per wave: four times the waves in flight.
     const int tok_chunk = T <= 256 ? kRouterNT : 64;
-    const bool one_row = T <= 2 * kRouterNT;
+    const bool one_row = T <= 64;
     const int nr = one_row ? 1 : kRouterNR;
     dim3 grid((n_rows + 4 * nr - 1) / (4 * nr), (T + tok_chunk - 1) / tok_chunk);
     const S* xs = static_cast<const S*>(x);
