@@ -21,6 +21,9 @@ The passages followed:
   ``gate_up`` with bias, gate clamped from above, up clamped on both sides,
   ``glu = gate * sigmoid(alpha * gate)``, ``h = (up + 1) * glu``, down projection with
   bias, weighted sum with the routing scores.
+* "Llama Forward Pass", section "Key Operations", RMSNorm, and "Qwen3.5-MoE Model
+  Implementation", section "Architecture" (post-attention norm -> MoE FFN -> residual):
+  the layer shell around the block (``moe_shell``).
 * "Engine" (Cherenkov), section "Prefill": tokens grouped by expert, gathered,
   projected and scattered back -- the grouped evaluation below; section "Address
   tables": the union of the experts a batch selects, with a zero weight where a row did
@@ -267,6 +270,51 @@ def moe_forward_tokens(L: dict, x, tokens=None) -> np.ndarray:
         if sh is not None:
             out[i] += sh[i]
     return out
+
+
+# ----------------------------------------------------------------------------- layer shell
+
+def rmsnorm(x, weight, eps: float) -> np.ndarray:
+    """RMSNorm ("Llama Forward Pass", Key Operations, RMSNorm; "Phase 19: MoE -
+    gpt-oss-20b", section 2, RMSNorm, eps 1e-5): every row divided by the square root of
+    the mean of its squares plus eps, then multiplied elementwise by the weight."""
+    xf = widen(x)
+    wf = widen(weight)
+    mean_sq = np.mean(xf * xf, axis=1, keepdims=True)
+    return xf / np.sqrt(mean_sq + eps) * wf[None, :]
+
+
+def round_to_bf16(a: np.ndarray) -> np.ndarray:
+    """fp64 values rounded to the nearest bf16 value (8 significant bits, ties to even),
+    returned as fp64.  Finite values in the normal bf16 range only (the normalised
+    activations this is used on are far from under- and overflow)."""
+    a = np.asarray(a, dtype=np.float64)
+    _, e = np.frexp(a)                   # a = m * 2**e, 0.5 <= |m| < 1
+    ulp = np.ldexp(1.0, e - 8)           # spacing of 8-bit significands at that exponent
+    return np.round(a / ulp) * ulp       # np.round: half to even
+
+
+def store_activation(a: np.ndarray, dtype: str):
+    """The normalised activation in the layer's storage form: bf16 bit patterns (uint16)
+    for a bf16 layer, float32 otherwise.  Reading taken: the norm's output is stored in
+    the dtype of the layer's activations before the MoE block reads it, as a separate
+    norm kernel would store it."""
+    if dtype == "bf16":
+        r = round_to_bf16(a).astype(np.float32)          # exact: 8-bit significands fit fp32
+        return (r.view(np.uint32) >> 16).astype(np.uint16)
+    return np.asarray(a, dtype=np.float32)
+
+
+def moe_shell(L: dict, h, norm_w, eps: float) -> np.ndarray:
+    """The FFN half of a decoder layer around the MoE block ("Qwen3.5-MoE Model
+    Implementation", Architecture: post-attention norm, then the shared-MoE FFN, then the
+    residual add): out = h + MoE(RMSNorm(h)), the normalised rows stored in the layer's
+    dtype first."""
+    hf = widen(h)
+    if hf.shape[0] == 0:
+        return np.zeros((0, L["d"]))
+    xn = store_activation(rmsnorm(h, norm_w, eps), L["dtype"])
+    return hf + moe_forward(L, xn)
 
 
 # ----------------------------------------------------------------------------- decode view

@@ -39,7 +39,8 @@ import numpy as np
 _CODE = {
     "w_router": 1, "b_router": 2, "w_gate": 3, "w_up": 4, "w_down": 5,
     "w_gate_up": 6, "b_gate_up": 7, "b_down": 8, "ws_gate": 9, "ws_up": 10,
-    "ws_down": 11, "ws_gate_inp": 12, "x": 20, "x_redraw": 21,
+    "ws_down": 11, "ws_gate_inp": 12, "x": 20, "x_redraw": 21, "norm_w": 30, "h": 31,
+    "h_redraw": 32,
 }
 
 ROUTE_SOFTMAX_TOPK_RENORM = "softmax_topk_renorm"
@@ -208,22 +209,54 @@ def make_tokens(L: dict, T: int, seed: int = 0, gap: float = 1e-3, max_attempts:
     """x[T, d] ~ N(0,1) in the layer's storage dtype, with every row's k+1 largest fp64
     logits separated by more than ``gap``.  A failing row t is redrawn from stream
     (seed, x_redraw, t, attempt).  ``gap <= 0`` disables the check."""
+    return _gapped_rows(L, T, seed, "x", "x_redraw", gap, max_attempts, None, None)
+
+
+def _row_scales(T: int) -> np.ndarray:
+    # Powers of two, so scaled bf16 rows stay exact: 1/4, 1/2, 1, 2, 4, 1/4, ...
+    return np.ldexp(np.float32(1.0), (np.arange(T) % 5) - 2).astype(np.float32)
+
+
+def _gapped_rows(L, T, seed, code, redraw, gap, max_attempts, scales, router_view):
     d, k, dt = L["d"], L["k"], L["dtype"]
-    x = _store(_rng(seed, _CODE["x"], T).standard_normal((T, d), dtype=np.float32), dt)
+
+    def draw(stream, shape, rows):
+        a = stream.standard_normal(shape, dtype=np.float32)
+        if scales is not None:
+            a *= scales[rows][:, None]
+        return _store(a, dt)
+
+    x = draw(_rng(seed, _CODE[code], T), (T, d), np.arange(T))
     if gap <= 0 or T == 0:
         return x
-    bad = np.nonzero(_bad_rows(_router_logits_f64(x, L), k, gap))[0]
+    view = router_view if router_view is not None else (lambda rows: rows)
+    bad = np.nonzero(_bad_rows(_router_logits_f64(view(x), L), k, gap))[0]
     attempt = 0
     while bad.size:
         attempt += 1
         if attempt > max_attempts:
             raise RuntimeError(f"gap enforcement failed for {bad.size} rows")
         for t in bad:
-            x[t] = _store(_rng(seed, _CODE["x_redraw"], int(t), attempt)
-                          .standard_normal((1, d), dtype=np.float32), dt)[0]
-        still = _bad_rows(_router_logits_f64(x[bad], L), k, gap)
+            x[t] = draw(_rng(seed, _CODE[redraw], int(t), attempt), (1, d), np.array([t]))[0]
+        still = _bad_rows(_router_logits_f64(view(x[bad]), L), k, gap)
         bad = bad[still]
     return x
+
+
+def make_norm_weight(L: dict, seed: int = 0) -> np.ndarray:
+    """RMSNorm weight [d] ~ N(1, 0.1^2) in the layer's storage dtype."""
+    a = 1.0 + 0.1 * _rng(seed, _CODE["norm_w"], 0).standard_normal(L["d"], dtype=np.float32)
+    return _store(a.astype(np.float32), L["dtype"])
+
+
+def make_hidden(L: dict, T: int, seed: int = 0, gap: float = 1e-3, router_view=None,
+                max_attempts: int = 200) -> np.ndarray:
+    """Hidden rows h[T, d] for the layer shell: N(0,1) rows scaled by 1/4, 1/2, 1, 2, 4 in
+    turn (powers of two, exact in bf16), so the norm sees several magnitudes.
+    ``router_view`` (optional) maps stored rows to the stored rows the router reads --
+    the caller's normalisation; rows whose fp64 logits of that view have near-ties (k+1
+    largest within ``gap``) are redrawn.  This module does no normalisation itself."""
+    return _gapped_rows(L, T, seed, "h", "h_redraw", gap, max_attempts, _row_scales(T), router_view)
 
 
 # ----------------------------------------------------------------------------- Zipf bias

@@ -302,3 +302,68 @@ def test_activation_special_values():
     assert oracle.silu(big)[0] == 50.0
     v = np.linspace(-6, 6, 101)
     assert np.allclose(oracle.silu(v), F.silu(torch.from_numpy(v)).numpy(), rtol=0, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- layer shell
+
+def test_rmsnorm_worked_example():
+    # Row [3, 4]: mean square 12.5, root 3.5355339..., so 3 and 4 map to the hand-computed
+    # values below ("Llama Forward Pass", Key Operations, RMSNorm, with eps 0 and weight 1).
+    out = oracle.rmsnorm(np.array([[3.0, 4.0]], dtype=np.float32), np.ones(2, np.float32), 0.0)
+    assert np.allclose(out, [[0.848528137423857, 1.131370849898476]], rtol=0, atol=1e-15)
+    # eps enters under the root: a constant row 0.01 with eps 1e-4 gives 0.01 / sqrt(2e-4).
+    c = oracle.rmsnorm(np.full((1, 8), 0.01), np.ones(8), 1e-4)
+    assert np.allclose(c, 0.7071067811865476, rtol=0, atol=1e-15)
+    assert np.all(oracle.rmsnorm(np.zeros((2, 8)), np.ones(8), 1e-5) == 0)
+
+
+def test_rmsnorm_invariants():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 64)) * np.array([[0.1], [1.0], [3.0], [10.0], [0.5]])
+    one = np.ones(64)
+    y = oracle.rmsnorm(x, one, 0.0)
+    assert np.allclose(np.mean(y * y, axis=1), 1.0, rtol=0, atol=1e-13)  # per row, not per column
+    assert np.allclose(oracle.rmsnorm(7.5 * x, one, 0.0), y, rtol=0, atol=1e-13)
+    assert np.allclose(oracle.rmsnorm(-x, one, 0.0), -y, rtol=0, atol=1e-15)
+    w = rng.standard_normal(64)
+    assert np.allclose(oracle.rmsnorm(x, w, 0.0), y * w[None, :], rtol=0, atol=1e-13)
+    # torch's own RMSNorm (a library routine) on the same rows
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (64,), torch.from_numpy(w), eps=1e-5)
+    assert np.allclose(oracle.rmsnorm(x, w, 1e-5), ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_round_to_bf16():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties go to the even significand (1);
+    # 1 + 3 * 2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6: even is 1 + 2^-6.
+    v = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 3 * 2.0 ** -8, 0.0])
+    assert list(oracle.round_to_bf16(v)) == [1.0, 1 + 2.0 ** -6, -1.0, 3 * 2.0 ** -8, 0.0]
+    # fp32 values: agree with torch's fp32 -> bf16 conversion and with the input module's
+    a = np.random.default_rng(4).standard_normal(4096).astype(np.float32) * 3
+    t = torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_to_bf16(a.astype(np.float64)), t)
+    bits = oracle.store_activation(a.astype(np.float64), "bf16")
+    assert bits.dtype == np.uint16 and np.array_equal(bits, synth.f32_to_bf16_bits(a))
+    assert oracle.store_activation(np.array([1.5]), "f32").dtype == np.float32
+
+
+@pytest.mark.parametrize("act,ffs", [("swiglu", 4), ("swiglu_oai", 0)])
+def test_moe_shell(act, ffs):
+    L = tiny_layer(d=16, E=6, ff=8, k=2, ffs=ffs, act=act,
+                   route="softmax_topk_renorm" if act == "swiglu" else "topk_softmax", dtype="bf16")
+    w = synth.make_norm_weight(L, seed=2)
+    rng = np.random.default_rng(5)
+    h = synth.f32_to_bf16_bits((rng.standard_normal((7, 16)) * 3).astype(np.float32))
+    out = oracle.moe_shell(L, h, w, 1e-5)
+    # The residual: experts whose outputs are zero leave h unchanged.
+    Lz = dict(L)
+    for n in ("w_down", "ws_down", "b_down"):
+        if Lz.get(n) is not None:
+            Lz[n] = np.zeros_like(Lz[n])
+    assert np.array_equal(oracle.moe_shell(Lz, h, w, 1e-5), oracle.widen(h))
+    # The block reads the stored normalised rows: the shell minus h equals the layer's
+    # token-by-token definition on those rows, built from torch's RMSNorm and bf16 cast.
+    hn = torch.nn.functional.rms_norm(torch.from_numpy(oracle.widen(h)), (16,),
+                                      torch.from_numpy(oracle.widen(w)), eps=1e-5)
+    xn = synth.f32_to_bf16_bits(hn.to(torch.bfloat16).to(torch.float32).numpy())
+    assert np.allclose(out - oracle.widen(h), oracle.moe_forward_tokens(L, xn), rtol=0, atol=1e-12)
+    assert oracle.moe_shell(L, h[:0], w, 1e-5).shape == (0, 16)
