@@ -110,8 +110,8 @@ int32_t moe_abi_version(void);
 /* Static description of a status code.  Never NULL. */
 const char* moe_status_string(moe_status s);
 
-/* Workspace bytes needed by moe_route, moe_expert_ffn and moe_forward for this layer
- * and up to T tokens (one size covers all three).  Writes *bytes (host).  Errors:
+/* Workspace bytes needed by moe_route, moe_expert_ffn, moe_forward and
+ * moe_forward_shell for this layer and up to T tokens (one size covers all of them).  Writes *bytes (host).  Errors:
  * MOE_ERR_ARG / MOE_ERR_UNSUPPORTED as for moe_forward. */
 moe_status moe_workspace_size(const moe_layer* L, int32_t T, size_t* bytes);
 
@@ -169,6 +169,23 @@ moe_status moe_combine(const moe_layer* L, const float* y_perm, const int32_t* p
  * MOE_PATH_GROUPED with MOE_F32. */
 moe_status moe_forward(const moe_layer* L, const void* x, int32_t T, void* y, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* The FFN half of a decoder layer around the block ("Qwen3.5-MoE Model Implementation",
+ * Architecture: post-attention norm, shared-MoE FFN, residual add; RMSNorm as in "Llama
+ * Forward Pass", Key Operations):
+ *     out[t] = h[t] + MoE(RMSNorm(h[t]) * norm_w),  RMSNorm(v) = v / sqrt(mean(v^2) + eps).
+ * The normalised rows are computed in fp32 and stored in L->dtype (bf16: rounded to
+ * nearest even) in the workspace; the block reads them as moe_forward reads x, and the
+ * residual is added to the fp32 sum before the output is stored.
+ *   h       [T, d] in L->dtype (the layer input and the residual)
+ *   norm_w  [d] in L->dtype, 16-byte aligned
+ *   eps     finite, >= 0 (the pages use 1e-5)
+ *   out     [T, d] in L->dtype; may equal h (in-place residual update), must not overlap
+ *           it otherwise
+ *   ws      as for moe_forward: moe_workspace_size(L, T) bytes cover this call too
+ * Errors as moe_forward; MOE_ERR_ARG for a negative or non-finite eps. */
+moe_status moe_forward_shell(const moe_layer* L, const void* h, int32_t T, const void* norm_w, float eps,
+                             void* out, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,10 +1,11 @@
 // Weighted combine ("Qwen3.5-MoE Model Implementation", MoE routing: out = moe_out +
-// shexp_out, the residual left to the caller; "Phase 19: MoE - gpt-oss-20b", Experts:
-// out = sum over the selected experts of score * y_e).
+// shexp_out, the residual left to the caller of the block; "Phase 19: MoE - gpt-oss-20b",
+// Experts: out = sum over the selected experts of score * y_e).
 //
 // y[t] = sum_{j<k} w[t,j] * Y_perm[perm_inv[t,j]] (+ sigmoid(a[t]) * Y_perm[T*k + t]),
 // accumulated in fp32 in the fixed order j = 0..k-1 then the shared term, so results
-// do not depend on scheduling.
+// do not depend on scheduling.  The layer shell (same page, Architecture: the MoE FFN
+// followed by the residual add) passes its input rows as `residual`, added last.
 #include <math.h>
 
 #include "common.h"
@@ -18,7 +19,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ perm_inv,
                                                       const float* __restrict__ w,
                                                       const float* __restrict__ shared_gate, int T,
-                                                      int k, int d, typename TT::storage* __restrict__ y) {
+                                                      int k, int d,
+                                                      const typename TT::storage* __restrict__ residual,
+                                                      typename TT::storage* __restrict__ y) {
     const int t = blockIdx.x;
     const int tk = T * k;
     __shared__ int rows[40];  // k <= 32, read in batches of 8
@@ -64,6 +67,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             acc.z = fmaf(sg, v.z, acc.z);
             acc.w = fmaf(sg, v.w, acc.w);
         }
+        if (residual) {  // read before y is written: y may alias it
+            float r[4];
+            if constexpr (sizeof(typename TT::storage) == 2) {
+                const uint2 q = *reinterpret_cast<const uint2*>(residual + (size_t)t * d + i);
+                r[0] = bf16_lo(q.x); r[1] = bf16_hi(q.x); r[2] = bf16_lo(q.y); r[3] = bf16_hi(q.y);
+            } else {
+                const float4 q = *reinterpret_cast<const float4*>(residual + (size_t)t * d + i);
+                r[0] = q.x; r[1] = q.y; r[2] = q.z; r[3] = q.w;
+            }
+            acc.x += r[0];
+            acc.y += r[1];
+            acc.z += r[2];
+            acc.w += r[3];
+        }
         if constexpr (sizeof(typename TT::storage) == 2) {
             uint2 o;
             o.x = uint32_t(f32_to_bf16(acc.x)) | (uint32_t(f32_to_bf16(acc.y)) << 16);
@@ -81,6 +98,7 @@ template <typename TT>
 __global__ __launch_bounds__(256) void combine_sum_kernel(const uint16_t* __restrict__ y_rows,
                                                           const int32_t* __restrict__ perm_inv, int T,
                                                           int k, int d, int shared,
+                                                          const typename TT::storage* __restrict__ residual,
                                                           typename TT::storage* __restrict__ y) {
     const int t = blockIdx.x;
     const int tk = T * k;
@@ -116,6 +134,18 @@ __global__ __launch_bounds__(256) void combine_sum_kernel(const uint16_t* __rest
                 for (int q = 0; q < 8; ++q) acc[q] += f[q];
             }
         }
+        if (residual) {  // read before y is written: y may alias it
+            float r[8];
+            const typename TT::storage* rp = residual + (size_t)t * d + i;
+            if constexpr (sizeof(typename TT::storage) == 2) {
+                unpack16<BF16>(ld16(rp), r);
+            } else {
+                unpack16<F32>(ld16(rp), r);
+                unpack16<F32>(ld16(rp + 4), r + 4);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] += r[q];
+        }
         if constexpr (sizeof(typename TT::storage) == 2) {
             uint4 o;
             o.x = uint32_t(f32_to_bf16(acc[0])) | (uint32_t(f32_to_bf16(acc[1])) << 16);
@@ -134,25 +164,27 @@ __global__ __launch_bounds__(256) void combine_sum_kernel(const uint16_t* __rest
 }  // namespace
 
 hipError_t launch_combine_sum(const moe_layer& L, const uint16_t* y_rows, const int32_t* perm_inv,
-                              int T, void* y, hipStream_t s) {
+                              int T, const void* residual, void* y, hipStream_t s) {
     const int shared = L.shared_ff > 0 ? 1 : 0;
     if (L.dtype == MOE_BF16)
         combine_sum_kernel<BF16><<<T, 256, 0, s>>>(y_rows, perm_inv, T, L.k, L.d, shared,
+                                                   static_cast<const uint16_t*>(residual),
                                                    static_cast<uint16_t*>(y));
     else
         combine_sum_kernel<F32><<<T, 256, 0, s>>>(y_rows, perm_inv, T, L.k, L.d, shared,
-                                                  static_cast<float*>(y));
+                                                  static_cast<const float*>(residual), static_cast<float*>(y));
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const moe_layer& L, const float* y_perm, const int32_t* perm_inv,
-                          const float* w, const float* shared_gate, int T, void* y, hipStream_t s) {
+                          const float* w, const float* shared_gate, int T, const void* residual, void* y,
+                          hipStream_t s) {
     if (L.dtype == MOE_BF16)
         combine_kernel<BF16><<<T, 256, 0, s>>>(y_perm, perm_inv, w, shared_gate, T, L.k, L.d,
-                                               static_cast<uint16_t*>(y));
+                                               static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(y));
     else
         combine_kernel<F32><<<T, 256, 0, s>>>(y_perm, perm_inv, w, shared_gate, T, L.k, L.d,
-                                              static_cast<float*>(y));
+                                              static_cast<const float*>(residual), static_cast<float*>(y));
     return hipGetLastError();
 }
 

@@ -85,7 +85,7 @@ template <int KB, typename TT, bool OAI, int NR, bool EXACT>
 __global__ __launch_bounds__(kToken1MaxWaves * kWave) void token1_down_combine_kernel(
     GemvDown a, const int32_t* __restrict__ idx, const float* __restrict__ w,
     const int32_t* __restrict__ perm_inv, const float* __restrict__ shared_gate, int gate_ld, int E, int k,
-    typename TT::storage* __restrict__ y) {
+    const typename TT::storage* __restrict__ residual, typename TT::storage* __restrict__ y) {
     using S = typename TT::storage;
     __shared__ float part[kToken1MaxWaves][NR];
     __shared__ float wts[kToken1MaxWaves];
@@ -136,8 +136,13 @@ __global__ __launch_bounds__(kToken1MaxWaves * kWave) void token1_down_combine_k
         const int nw = blockDim.x / kWave;
         float o = 0.0f;
         for (int jj = 0; jj < nw; ++jj) o = fmaf(wts[jj], part[jj][tid], o);
-        if constexpr (sizeof(S) == 2) y[(size_t)t * a.d + i0 + tid] = f32_to_bf16(o);
-        else y[(size_t)t * a.d + i0 + tid] = o;
+        const size_t at = (size_t)t * a.d + i0 + tid;
+        if (residual) {  // read before y is written: y may alias it
+            if constexpr (sizeof(S) == 2) o += bf16_to_f32(residual[at]);
+            else o += residual[at];
+        }
+        if constexpr (sizeof(S) == 2) y[at] = f32_to_bf16(o);
+        else y[at] = o;
     }
 }
 
@@ -259,13 +264,14 @@ hipError_t launch_token1_up_t(const moe_layer& L, const void* x, const float* lo
 template <typename TT, bool OAI>
 hipError_t launch_token1_t(const moe_layer& L, int T, const float* H, int hstride, const int32_t* idx,
                            const float* w, const int32_t* perm_inv, const float* shared_gate, int gate_ld,
-                           void* y, hipStream_t s) {
+                           const void* residual, void* y, hipStream_t s) {
     const bool shared = L.shared_ff > 0;
     GemvDown dn{H, nullptr, L.w_down, L.b_down, L.ws_down, nullptr, hstride, T, T * L.k, L.d, L.ff, L.shared_ff};
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
     const dim3 grid((L.d + kToken1Rows - 1) / kToken1Rows, T);
     const dim3 block((L.k + (shared ? 1 : 0)) * kWave);
     auto* yo = static_cast<typename TT::storage*>(y);
+    const auto* ro = static_cast<const typename TT::storage*>(residual);
     const auto exact = [&](int kb) {
         return exact_k(L.ff, TT::VEC, kb) && (L.shared_ff == 0 || exact_k(L.shared_ff, TT::VEC, kb));
     };
@@ -276,10 +282,10 @@ hipError_t launch_token1_t(const moe_layer& L, int T, const float* H, int hstrid
     case KB:                                                                                    \
         if (exact(KB))                                                                          \
             token1_down_combine_kernel<KB, TT, OAI, kToken1Rows, true>                          \
-                <<<grid, block, 0, s>>>(dn, idx, w, perm_inv, shared_gate, gate_ld, L.n_expert, L.k, yo); \
+                <<<grid, block, 0, s>>>(dn, idx, w, perm_inv, shared_gate, gate_ld, L.n_expert, L.k, ro, yo); \
         else                                                                                    \
             token1_down_combine_kernel<KB, TT, OAI, kToken1Rows, false>                         \
-                <<<grid, block, 0, s>>>(dn, idx, w, perm_inv, shared_gate, gate_ld, L.n_expert, L.k, yo); \
+                <<<grid, block, 0, s>>>(dn, idx, w, perm_inv, shared_gate, gate_ld, L.n_expert, L.k, ro, yo); \
         break;
         SMOE_T1_CASE(1)
         SMOE_T1_CASE(2)
@@ -329,14 +335,14 @@ bool token1_fits(const moe_layer& L) { return L.k + (L.shared_ff > 0 ? 1 : 0) <=
 
 hipError_t launch_token_down_combine(const moe_layer& L, int T, const float* H, int hstride, const int32_t* idx,
                                      const float* w, const int32_t* perm_inv, const float* shared_gate,
-                                     int gate_ld, void* y, hipStream_t s) {
+                                     int gate_ld, const void* residual, void* y, hipStream_t s) {
     if (!token1_fits(L) || T < 1 || (!perm_inv && T != 1)) return hipErrorInvalidValue;
     const bool oai = L.act == MOE_ACT_SWIGLU_OAI;
     if (L.dtype == MOE_BF16)
-        return oai ? launch_token1_t<BF16, true>(L, T, H, hstride, idx, w, perm_inv, shared_gate, gate_ld, y, s)
-                   : launch_token1_t<BF16, false>(L, T, H, hstride, idx, w, perm_inv, shared_gate, gate_ld, y, s);
-    return oai ? launch_token1_t<F32, true>(L, T, H, hstride, idx, w, perm_inv, shared_gate, gate_ld, y, s)
-               : launch_token1_t<F32, false>(L, T, H, hstride, idx, w, perm_inv, shared_gate, gate_ld, y, s);
+        return oai ? launch_token1_t<BF16, true>(L, T, H, hstride, idx, w, perm_inv, shared_gate, gate_ld, residual, y, s)
+                   : launch_token1_t<BF16, false>(L, T, H, hstride, idx, w, perm_inv, shared_gate, gate_ld, residual, y, s);
+    return oai ? launch_token1_t<F32, true>(L, T, H, hstride, idx, w, perm_inv, shared_gate, gate_ld, residual, y, s)
+               : launch_token1_t<F32, false>(L, T, H, hstride, idx, w, perm_inv, shared_gate, gate_ld, residual, y, s);
 }
 
 }  // namespace smoe

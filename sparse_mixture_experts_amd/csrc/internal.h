@@ -63,7 +63,7 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
                               hipStream_t s);
 // Combine of pre-weighted bf16 rows: y[t] = sum_j Y[perm_inv[t,j]] (+ Y[T*k + t]).
 hipError_t launch_combine_sum(const moe_layer& L, const uint16_t* y_rows, const int32_t* perm_inv,
-                              int T, void* y, hipStream_t s);
+                              int T, const void* residual, void* y, hipStream_t s);
 hipError_t launch_expert_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                               const Group* groups, const PlanMeta* meta, float* H, int hstride,
                               float* y_perm, hipStream_t s);
@@ -81,9 +81,14 @@ hipError_t launch_token1_up(const moe_layer& L, const void* x, const float* logi
                             float* H, int hstride, hipStream_t s);
 hipError_t launch_token_down_combine(const moe_layer& L, int T, const float* H, int hstride, const int32_t* idx,
                                      const float* w, const int32_t* perm_inv, const float* shared_gate,
-                                     int gate_ld, void* y, hipStream_t s);
+                                     int gate_ld, const void* residual, void* y, hipStream_t s);
+// residual (optional, [T, d] in the layer's dtype) is added to every output row.
 hipError_t launch_combine(const moe_layer& L, const float* y_perm, const int32_t* perm_inv,
-                          const float* w, const float* shared_gate, int T, void* y, hipStream_t s);
+                          const float* w, const float* shared_gate, int T, const void* residual, void* y,
+                          hipStream_t s);
+// xn[t] = RMSNorm(h[t]) * w in the layer's dtype (the layer shell's norm).
+hipError_t launch_rmsnorm(const moe_layer& L, const void* h, int T, const void* w, float eps, void* xn,
+                          hipStream_t s);
 
 
 }  // namespace smoe

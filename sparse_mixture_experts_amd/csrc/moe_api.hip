@@ -23,7 +23,7 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 // Byte offsets of every scratch buffer inside the caller's workspace.
 struct Layout {
     size_t logits, idx, w, sg, counts, base, offsets, perm_token, perm_inv, groups, meta, tiles,
-        row_w, H, yperm;
+        row_w, H, yperm, xn;
     size_t total;
     int ld, hstride, rows;
 };
@@ -58,6 +58,8 @@ Layout layout_for(const moe_layer& L, int T) {
     // H: fp32 on the GEMV path, bf16 on the grouped path (same region).
     o.H = take((size_t)o.rows * o.hstride * 4);
     o.yperm = take((size_t)o.rows * L.d * 4);
+    // Normalised rows of the layer shell, in the layer's dtype.
+    o.xn = take((size_t)T * L.d * (L.dtype == MOE_BF16 ? 2 : 4));
     o.total = off;
     return o;
 }
@@ -152,6 +154,60 @@ moe_status run_experts(const moe_layer& L, const void* x, int T, const int32_t* 
     return MOE_OK;
 }
 
+// The layer after the argument checks: route, group, expert FFNs, combine (plus
+// residual[t] when it is non-null), reading x and writing y.
+moe_status forward_body(const moe_layer* L, const void* x, int32_t T, const void* residual, void* y, void* ws,
+                        const Layout& o, hipStream_t s) {
+    const bool shared = L->shared_ff > 0;
+    float* logits = at<float>(ws, o.logits);
+    int32_t* idx = at<int32_t>(ws, o.idx);
+    float* w = at<float>(ws, o.w);
+    float* sg = shared ? at<float>(ws, o.sg) : nullptr;
+    int32_t* offsets = at<int32_t>(ws, o.offsets);
+    int32_t* perm_token = at<int32_t>(ws, o.perm_token);
+    int32_t* perm_inv = at<int32_t>(ws, o.perm_inv);
+    const bool grouped = use_grouped(*L, T);
+    // Grouped path: rows carry their routing weight and are stored in bf16.
+    float* row_w = grouped ? at<float>(ws, o.row_w) : nullptr;
+    void* y_rows = at<void>(ws, o.yperm);
+    SMOE_TRY(run_router(*L, x, T, logits, o.ld, s));
+    if (T == 1 && !grouped && token1_fits(*L)) {
+        // One token: top-k inside the up GEMV, then the down GEMVs and the combine in one
+        // kernel (no grouping: hidden row j holds pick j).
+        SMOE_TRY(launch_token1_up(*L, x, logits, idx, w, at<float>(ws, o.H), o.hstride, s));
+        SMOE_TRY(launch_token_down_combine(*L, 1, at<float>(ws, o.H), o.hstride, idx, w, nullptr,
+                                           shared ? logits + L->n_expert : nullptr, o.ld, residual, y, s));
+        return MOE_OK;
+    }
+    const bool fused_route = T <= kPermChunk;
+    if (fused_route) {
+        SMOE_TRY(launch_decode_route(*L, logits, o.ld, T, idx, w, sg, offsets, perm_token, perm_inv,
+                                     row_w, kTileM, at<Group>(ws, o.groups), at<PlanMeta>(ws, o.meta),
+                                     at<TileDesc>(ws, o.tiles), s));
+    } else {
+        SMOE_TRY(launch_topk(*L, logits, o.ld, T, idx, w, sg, row_w,
+                             router_leaves_shared_gate(*L, T) ? x : nullptr, s));
+        SMOE_TRY(launch_permute(idx, T, L->k, L->n_expert, offsets, perm_token, perm_inv,
+                                at<int32_t>(ws, o.counts), at<int32_t>(ws, o.base), w, row_w, s));
+    }
+    if (fused_route && !grouped && T <= kTokenDownMaxT && token1_fits(*L)) {
+        // A few tokens: up GEMV over the groups, then per token the down GEMVs of its picks
+        // and the combine in one kernel.
+        SMOE_TRY(launch_expert_up_gemv(*L, x, T, perm_token, at<Group>(ws, o.groups), at<PlanMeta>(ws, o.meta),
+                                       at<float>(ws, o.H), o.hstride, s));
+        SMOE_TRY(launch_token_down_combine(*L, T, at<float>(ws, o.H), o.hstride, idx, w, perm_inv, sg, 1, residual,
+                                           y, s));
+        return MOE_OK;
+    }
+    const moe_status st = run_experts(*L, x, T, offsets, perm_token, y_rows, row_w, grouped, ws, o, fused_route, s);
+    if (st != MOE_OK) return st;
+    if (grouped)
+        SMOE_TRY(launch_combine_sum(*L, static_cast<const uint16_t*>(y_rows), perm_inv, T, residual, y, s));
+    else
+        SMOE_TRY(launch_combine(*L, static_cast<const float*>(y_rows), perm_inv, w, sg, T, residual, y, s));
+    return MOE_OK;
+}
+
 }  // namespace
 }  // namespace smoe
 
@@ -159,7 +215,7 @@ using namespace smoe;
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 const char* moe_status_string(moe_status s) {
     switch (s) {
@@ -254,7 +310,7 @@ moe_status moe_combine(const moe_layer* L, const float* y_perm, const int32_t* p
     if (!y_perm || !perm_inv || !topk_w || !y) return MOE_ERR_ARG;
     if (!aligned(y_perm, 16) || !aligned(y, 16)) return MOE_ERR_UNSUPPORTED;
     (void)hipGetLastError();
-    return status_of(launch_combine(*L, y_perm, perm_inv, topk_w, shared_gate, T, y,
+    return status_of(launch_combine(*L, y_perm, perm_inv, topk_w, shared_gate, T, nullptr, y,
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -271,53 +327,32 @@ moe_status moe_forward(const moe_layer* L, const void* x, int32_t T, void* y, vo
     if (ws_bytes < o.total) return MOE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    const bool shared = L->shared_ff > 0;
-    float* logits = at<float>(ws, o.logits);
-    int32_t* idx = at<int32_t>(ws, o.idx);
-    float* w = at<float>(ws, o.w);
-    float* sg = shared ? at<float>(ws, o.sg) : nullptr;
-    int32_t* offsets = at<int32_t>(ws, o.offsets);
-    int32_t* perm_token = at<int32_t>(ws, o.perm_token);
-    int32_t* perm_inv = at<int32_t>(ws, o.perm_inv);
-    const bool grouped = use_grouped(*L, T);
-    // Grouped path: rows carry their routing weight and are stored in bf16.
-    float* row_w = grouped ? at<float>(ws, o.row_w) : nullptr;
-    void* y_rows = at<void>(ws, o.yperm);
-    SMOE_TRY(run_router(*L, x, T, logits, o.ld, s));
-    if (T == 1 && !grouped && token1_fits(*L)) {
-        // One token: top-k inside the up GEMV, then the down GEMVs and the combine in one
-        // kernel (no grouping: hidden row j holds pick j).
-        SMOE_TRY(launch_token1_up(*L, x, logits, idx, w, at<float>(ws, o.H), o.hstride, s));
-        SMOE_TRY(launch_token_down_combine(*L, 1, at<float>(ws, o.H), o.hstride, idx, w, nullptr,
-                                           shared ? logits + L->n_expert : nullptr, o.ld, y, s));
-        return MOE_OK;
-    }
-    const bool fused_route = T <= kPermChunk;
-    if (fused_route) {
-        SMOE_TRY(launch_decode_route(*L, logits, o.ld, T, idx, w, sg, offsets, perm_token, perm_inv,
-                                     row_w, kTileM, at<Group>(ws, o.groups), at<PlanMeta>(ws, o.meta),
-                                     at<TileDesc>(ws, o.tiles), s));
-    } else {
-        SMOE_TRY(launch_topk(*L, logits, o.ld, T, idx, w, sg, row_w,
-                             router_leaves_shared_gate(*L, T) ? x : nullptr, s));
-        SMOE_TRY(launch_permute(idx, T, L->k, L->n_expert, offsets, perm_token, perm_inv,
-                                at<int32_t>(ws, o.counts), at<int32_t>(ws, o.base), w, row_w, s));
-    }
-    if (fused_route && !grouped && T <= kTokenDownMaxT && token1_fits(*L)) {
-        // A few tokens: up GEMV over the groups, then per token the down GEMVs of its picks
-        // and the combine in one kernel.
-        SMOE_TRY(launch_expert_up_gemv(*L, x, T, perm_token, at<Group>(ws, o.groups), at<PlanMeta>(ws, o.meta),
-                                       at<float>(ws, o.H), o.hstride, s));
-        SMOE_TRY(launch_token_down_combine(*L, T, at<float>(ws, o.H), o.hstride, idx, w, perm_inv, sg, 1, y, s));
-        return MOE_OK;
-    }
-    st = run_experts(*L, x, T, offsets, perm_token, y_rows, row_w, grouped, ws, o, fused_route, s);
+    return forward_body(L, x, T, nullptr, y, ws, o, s);
+}
+
+moe_status moe_forward_shell(const moe_layer* L, const void* h, int32_t T, const void* norm_w, float eps,
+                             void* out, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_layer(L);
     if (st != MOE_OK) return st;
-    if (grouped)
-        SMOE_TRY(launch_combine_sum(*L, static_cast<const uint16_t*>(y_rows), perm_inv, T, y, s));
-    else
-        SMOE_TRY(launch_combine(*L, static_cast<const float*>(y_rows), perm_inv, w, sg, T, y, s));
-    return MOE_OK;
+    if ((st = check_tokens(T)) != MOE_OK) return st;
+    if (!isfinite(eps) || eps < 0.0f) return MOE_ERR_ARG;
+    if (T == 0) return MOE_OK;
+    if (!h || !norm_w || !out || !ws) return MOE_ERR_ARG;
+    // out may be h itself, but may not overlap it partially.
+    const size_t row_bytes = (size_t)T * L->d * (L->dtype == MOE_BF16 ? 2 : 4);
+    const uintptr_t hb = reinterpret_cast<uintptr_t>(h), ob = reinterpret_cast<uintptr_t>(out);
+    if (hb != ob && hb < ob + row_bytes && ob < hb + row_bytes) return MOE_ERR_ARG;
+    if (!aligned(h, 16) || !aligned(out, 16) || !aligned(ws, 16) || !aligned(norm_w, 16))
+        return MOE_ERR_UNSUPPORTED;
+    const Layout o = layout_for(*L, T);
+    if (ws_bytes < o.total) return MOE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    void* xn = at<void>(ws, o.xn);
+    SMOE_TRY(launch_rmsnorm(*L, h, T, norm_w, eps, xn, s));
+    // h is read again only by the final kernel, element by element before out is
+    // written there, so out may alias h.
+    return forward_body(L, xn, T, h, out, ws, o, s);
 }
 
 }  // extern "C"

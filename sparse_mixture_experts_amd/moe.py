@@ -41,9 +41,10 @@ class MoeLayer(ctypes.Structure):
 
 
 POINTER_FIELDS = [f for f, t in MoeLayer._fields_ if t is _P]
+ABI_VERSION = 2
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward"]
+           "moe_forward", "moe_forward_shell"]
 
 
 class MoeError(RuntimeError):
@@ -83,7 +84,9 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [pl, vp, vp, vp, vp, i32, vp, vp]
         L.moe_forward.restype = i32
         L.moe_forward.argtypes = [pl, vp, i32, vp, vp, sz, vp]
-        if L.moe_abi_version() != 1:
+        L.moe_forward_shell.restype = i32
+        L.moe_forward_shell.argtypes = [pl, vp, i32, vp, ctypes.c_float, vp, vp, sz, vp]
+        if L.moe_abi_version() != ABI_VERSION:
             raise RuntimeError("libsmoe.so ABI version mismatch")
         _lib = L
     return _lib
@@ -234,4 +237,16 @@ def forward(layer: Layer, x, ws=None, out=None):
     y = torch.empty((T, layer.d), dtype=layer.torch_dtype, device=x.device) if out is None else out
     _check(lib().moe_forward(layer.ref(), _ptr(x), T, _ptr(y), _ptr(ws), ws.numel(), _stream()),
            "moe_forward")
+    return y
+
+
+def forward_shell(layer: Layer, h, norm_w, eps: float = 1e-5, ws=None, out=None):
+    """out = h + MoE(RMSNorm(h) * norm_w) [T, d] in the layer dtype; ``out`` may be ``h``
+    itself (in-place residual update)."""
+    torch = _torch()
+    T = h.shape[0]
+    ws = workspace(layer, T, h.device) if ws is None else ws
+    y = torch.empty((T, layer.d), dtype=layer.torch_dtype, device=h.device) if out is None else out
+    _check(lib().moe_forward_shell(layer.ref(), _ptr(h), T, _ptr(norm_w), float(eps), _ptr(y), _ptr(ws),
+                                   ws.numel(), _stream()), "moe_forward_shell")
     return y

@@ -250,13 +250,18 @@ def make_norm_weight(L: dict, seed: int = 0) -> np.ndarray:
 
 
 def make_hidden(L: dict, T: int, seed: int = 0, gap: float = 1e-3, router_view=None,
-                max_attempts: int = 200) -> np.ndarray:
+                scale: float = 1.0, max_attempts: int = 200) -> np.ndarray:
     """Hidden rows h[T, d] for the layer shell: N(0,1) rows scaled by 1/4, 1/2, 1, 2, 4 in
-    turn (powers of two, exact in bf16), so the norm sees several magnitudes.
+    turn, times ``scale`` (all powers of two, exact in bf16), so the norm sees several
+    magnitudes.
     ``router_view`` (optional) maps stored rows to the stored rows the router reads --
     the caller's normalisation; rows whose fp64 logits of that view have near-ties (k+1
     largest within ``gap``) are redrawn.  This module does no normalisation itself."""
-    return _gapped_rows(L, T, seed, "h", "h_redraw", gap, max_attempts, _row_scales(T), router_view)
+    m, _ = math.frexp(scale)
+    if scale <= 0 or m != 0.5:
+        raise ValueError("scale must be a power of two")
+    return _gapped_rows(L, T, seed, "h", "h_redraw", gap, max_attempts,
+                        (_row_scales(T) * np.float32(scale)).astype(np.float32), router_view)
 
 
 # ----------------------------------------------------------------------------- Zipf bias

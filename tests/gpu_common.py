@@ -55,3 +55,22 @@ def to_numpy_y(y):
     """A device output tensor as fp64 numpy (bf16 widened exactly)."""
     import torch
     return y.detach().to("cpu", torch.float64).numpy()
+
+
+# Half an ulp of the output, relative to the value: bf16 keeps 8 significant bits, fp32 24.
+OUT_ULP = {"bf16": 2.0 ** -8, "f32": 2.0 ** -23}
+
+
+def assert_shell_close(got, ref, h, dtype, what=""):
+    """Layer-shell outputs: the block's part (ref - h) is held to the usual rule, relative
+    to its own largest magnitude, and each element may also carry the rounding of the
+    residual sum to the output dtype (half an ulp of the value)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    part = ref - np.asarray(h, dtype=np.float64)
+    scale = np.max(np.abs(part)) if part.size else 0.0
+    allow = RTOL[dtype] * scale + OUT_ULP[dtype] * np.abs(ref)
+    err = np.abs(got - ref)
+    worst = float(np.max(err / np.maximum(allow, 1e-300))) if err.size else 0.0
+    assert worst <= 1.0, f"{what}: error reaches {worst:.3f} of the allowance"
+    return float(np.max(err) / scale) if scale > 0 else 0.0

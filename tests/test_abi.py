@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -153,3 +153,24 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         moe.lib()
+
+
+def shell(lib, s, T=4, h=FAKE, w=FAKE * 4, eps=1e-5, out=FAKE * 2, ws=FAKE * 3, nbytes=1 << 40):
+    return lib.moe_forward_shell(ctypes.byref(s), h, T, w, eps, out, ws, nbytes, None)
+
+
+def test_shell_argument_errors(lib):
+    s = fake_layer()
+    assert shell(lib, s, T=0) == moe.MOE_OK
+    assert shell(lib, s, T=-1) == moe.MOE_ERR_ARG
+    assert shell(lib, s, eps=-1.0) == moe.MOE_ERR_ARG
+    assert shell(lib, s, eps=float("nan")) == moe.MOE_ERR_ARG
+    assert shell(lib, s, eps=float("inf")) == moe.MOE_ERR_ARG
+    for name in ("h", "w", "out", "ws"):
+        assert shell(lib, s, **{name: None}) == moe.MOE_ERR_ARG, name
+    assert shell(lib, s, out=FAKE + 256) == moe.MOE_ERR_ARG        # overlaps h partially
+    assert shell(lib, s, w=FAKE * 4 + 8) == moe.MOE_ERR_UNSUPPORTED  # misaligned norm weight
+    assert shell(lib, s, h=FAKE + 8, out=FAKE * 2 + 8) == moe.MOE_ERR_UNSUPPORTED
+    _, need = ws_size(lib, s, 4)
+    assert shell(lib, s, nbytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_forward_shell(None, FAKE, 4, FAKE, 1e-5, FAKE * 2, FAKE * 3, 1 << 40, None) == moe.MOE_ERR_ARG

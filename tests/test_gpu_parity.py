@@ -10,8 +10,8 @@ import pytest
 import oracle
 from sparse_mixture_experts_amd import synth
 
-from gpu_common import (SG_ATOL, W_ATOL, assert_close, case, layer_arrays, rel_err, say,
-                        to_numpy_y)
+from gpu_common import (SG_ATOL, W_ATOL, assert_close, assert_shell_close, case, layer_arrays, rel_err,
+                        say, to_numpy_y)
 
 pytestmark = pytest.mark.gpu
 
@@ -382,3 +382,71 @@ def test_grouped_many_tiles():
                           oracle.widen(L["ws_down"]))])
     assert_close(yp[rows], ref_rows, "bf16", "expert rows")
     assert_close(y[tok], oracle.moe_forward(L, x[tok]), "bf16", "y")
+
+
+# ----------------------------------------------------------------------------- layer shell
+
+EPS = 1e-5
+SHELL = [
+    ("tiny_f32", {}, [1, 16, 77]),
+    ("qwen", dict(d=512, n_expert=64, ff=192, shared_ff=128), [1, 5, 64, 150]),
+    ("gptoss", dict(d=320, n_expert=16, ff=192), [1, 7, 100]),
+]
+SHELL_CASES = [(n, ov, T) for n, ov, Ts in SHELL for T in Ts]
+
+
+def shell_case(name, T, **ov):
+    L = layer_arrays(name, 0, **ov)
+    w = synth.make_norm_weight(L, seed=7)
+
+    def view(rows):
+        return oracle.store_activation(oracle.rmsnorm(rows, w, EPS), L["dtype"])
+
+    # bf16: small residual magnitudes keep the block's part visible after the rounding of
+    # the sum; the rows still span a factor 16 for the norm.
+    scale = 2.0 ** -4 if L["dtype"] == "bf16" else 1.0
+    h = synth.make_hidden(L, T, seed=8, router_view=view, scale=scale)
+    return L, w, h
+
+
+@pytest.mark.parametrize("path", ["auto", "grouped"])
+@pytest.mark.parametrize("c", SHELL_CASES, ids=_id)
+def test_forward_shell(c, path):
+    name, ov, T = c
+    if path == "grouped" and name == "tiny_f32":
+        pytest.skip("grouped path is bf16-only")
+    say("shell", name, ov, T, path)
+    L, w, h = shell_case(name, T, **ov)
+    lay = dev_layer(name, path=path, **ov)
+    out = moe_mod().forward_shell(lay, xdev(h), xdev(w), EPS)
+    torch.cuda.synchronize()
+    ref = oracle.moe_shell(L, h, w, EPS)
+    e = assert_shell_close(to_numpy_y(out), ref, oracle.widen(h), L["dtype"], "shell")
+    say(f"  block part rel err {e:.2e}")
+
+
+@pytest.mark.parametrize("T", [1, 5, 64, 150])
+def test_forward_shell_in_place(T):
+    ov = dict(d=512, n_expert=64, ff=192, shared_ff=128)
+    say("shell in place", T)
+    L, w, h = shell_case("qwen", T, **ov)
+    lay = dev_layer("qwen", **ov)
+    wd = xdev(w)
+    apart = moe_mod().forward_shell(lay, xdev(h), wd, EPS)
+    hd = xdev(h)
+    same = moe_mod().forward_shell(lay, hd, wd, EPS, out=hd)
+    torch.cuda.synchronize()
+    assert same.data_ptr() == hd.data_ptr()
+    assert torch.equal(same, apart)
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_full_qwen_shell(T):
+    say("full qwen shell", T)
+    L, w, h = shell_case("qwen", T)
+    lay = dev_layer("qwen")
+    out = moe_mod().forward_shell(lay, xdev(h), xdev(w), EPS)
+    torch.cuda.synchronize()
+    ref = oracle.moe_shell(L, h, w, EPS)
+    e = assert_shell_close(to_numpy_y(out), ref, oracle.widen(h), "bf16", "shell")
+    say(f"  block part rel err {e:.2e}")
