@@ -12,7 +12,9 @@ The printed JSON line carries the headline workload (Qwen3.5-MoE-shaped decode, 
 ``sweep`` holds the other decode batches and the prefill batch.  ``roofline`` is for
 the dominant stage (the expert FFN launches: plan + up-projection + down-projection),
 timed with events on the launch stream in a separate pass of the same steps split at
-the C-ABI calls.  ``cpu_baseline`` is the fp64 oracle on the host cores.
+the C-ABI calls.  ``shell_ms_per_step`` times ``moe_forward_shell`` (RMSNorm in front,
+residual add at the end) on the same batches.  ``cpu_baseline`` is the fp64 oracle on
+the host cores.
 """
 from __future__ import annotations
 
@@ -283,6 +285,23 @@ def time_workload(name, steps, warmup, layer_cache):
     torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) for a, b in ev)
 
+    # The layer shell (moe_forward_shell: RMSNorm in front, residual add at the end) on the
+    # same batches, timed the same way.
+    norm_w = moe.to_device(synth.make_norm_weight(L, seed=0))
+
+    def shell_step(i):
+        moe.forward_shell(layers[i % n_copies], xs[i % n_batches], norm_w, 1e-5, ws, out=y)
+
+    for i in range(warmup):
+        shell_step(i)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(steps):
+        shell_step(warmup + i)
+    t_end.record()
+    torch.cuda.synchronize()
+    shell_ms = t_start.elapsed_time(t_end) / steps
+
     # Stage pass: the same steps split at the C-ABI calls, events around the expert FFN.
     plans = []
     for x in xs:
@@ -316,7 +335,7 @@ def time_workload(name, steps, warmup, layer_cache):
         "ms_per_step": ms_step, "ms_p10": per[len(per) // 10], "ms_median": statistics.median(per),
         "ms_p90": per[(9 * len(per)) // 10], "tokens_per_s": T / (ms_step / 1e3),
         "active_experts_mean": U_mean, "weight_copies": n_copies, "token_batches": n_batches,
-        "stage_ms": stage_ms,
+        "stage_ms": stage_ms, "shell_ms_per_step": shell_ms,
     }
     if decode:
         lb = layer_bytes(L, T, U_mean)
@@ -340,7 +359,8 @@ def time_workload(name, steps, warmup, layer_cache):
                            "kernel": "expert FFN stage (plan + up + down)",
                            "algorithmic_flops": sf}
     log(f"[{name}] {ms_step * 1e3:.1f} us/step, {res['tokens_per_s']:.0f} tok/s, "
-        f"stage {stage_ms * 1e3:.1f} us, roofline frac {res['roofline']['frac']:.3f}")
+        f"stage {stage_ms * 1e3:.1f} us, roofline frac {res['roofline']['frac']:.3f}, "
+        f"shell {shell_ms * 1e3:.1f} us/step")
     del layers, xs, ws, y, yp, plans
     torch.cuda.empty_cache()
     return res
@@ -490,7 +510,7 @@ def main():
                    "layer_hbm_frac": main_res.get("layer_hbm_frac"),
                    "active_experts_mean": main_res["active_experts_mean"],
                    "ms_median": main_res["ms_median"], "ms_p10": main_res["ms_p10"],
-                   "ms_p90": main_res["ms_p90"]},
+                   "ms_p90": main_res["ms_p90"], "shell_ms_per_step": main_res["shell_ms_per_step"]},
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
         "sweep": sweep,

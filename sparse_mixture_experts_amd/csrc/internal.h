@@ -36,8 +36,18 @@ inline int max_groups(int E, int T, int k, bool shared) {
     return int((tk < E ? tk : E) + (shared ? 1 : 0));
 }
 
+// RMSNorm fused in front of the router GEMV (the layer shell): x is then the un-normalised
+// input h; the router reads RMSNorm(h) * w and writes it to xn [T, d] in the layer dtype.
+// Only for batches of at most 256 tokens (chunks of 4 tokens) whose 4 rows fit 64 KB of LDS.
+struct RouterNorm {
+    const void* w;
+    float eps;
+    void* xn;
+};
+constexpr size_t kRouterNormMaxLds = 64 * 1024;
+bool router_norm_fits(const moe_layer& L);
 hipError_t launch_router_logits(const moe_layer& L, const void* x, int T, float* logits, int ld,
-                                hipStream_t s);
+                                hipStream_t s, const RouterNorm* norm = nullptr);
 // row_w (optional, [T*k (+T)]): per grouped row routing weight, and sigmoid of the
 // shared gate for the shared rows T*k + t; lets the down GEMM apply the weights.
 // Router logits on MFMA (bf16, experts only: the shared-gate column is left to top-k).

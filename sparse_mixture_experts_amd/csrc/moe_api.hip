@@ -126,7 +126,9 @@ bool router_on_mfma(const moe_layer& L, int T) { return use_grouped(L, T) && T >
 bool router_leaves_shared_gate(const moe_layer& L, int T) {
     return router_on_mfma(L, T) && L.shared_ff > 0;
 }
-hipError_t run_router(const moe_layer& L, const void* x, int T, float* logits, int ld, hipStream_t s) {
+hipError_t run_router(const moe_layer& L, const void* x, int T, float* logits, int ld, hipStream_t s,
+                      const RouterNorm* norm = nullptr) {
+    if (norm) return launch_router_logits(L, x, T, logits, ld, s, norm);
     return router_on_mfma(L, T) ? launch_router_mfma(L, x, T, logits, ld, s)
                                 : launch_router_logits(L, x, T, logits, ld, s);
 }
@@ -155,9 +157,11 @@ moe_status run_experts(const moe_layer& L, const void* x, int T, const int32_t* 
 }
 
 // The layer after the argument checks: route, group, expert FFNs, combine (plus
-// residual[t] when it is non-null), reading x and writing y.
+// residual[t] when it is non-null), reading x and writing y.  With `norm` the router
+// reads residual (the shell's h), normalises it and writes the rows the experts read to
+// x (= norm->xn).
 moe_status forward_body(const moe_layer* L, const void* x, int32_t T, const void* residual, void* y, void* ws,
-                        const Layout& o, hipStream_t s) {
+                        const Layout& o, hipStream_t s, const RouterNorm* norm = nullptr) {
     const bool shared = L->shared_ff > 0;
     float* logits = at<float>(ws, o.logits);
     int32_t* idx = at<int32_t>(ws, o.idx);
@@ -170,7 +174,7 @@ moe_status forward_body(const moe_layer* L, const void* x, int32_t T, const void
     // Grouped path: rows carry their routing weight and are stored in bf16.
     float* row_w = grouped ? at<float>(ws, o.row_w) : nullptr;
     void* y_rows = at<void>(ws, o.yperm);
-    SMOE_TRY(run_router(*L, x, T, logits, o.ld, s));
+    SMOE_TRY(run_router(*L, norm ? residual : x, T, logits, o.ld, s, norm));
     if (T == 1 && !grouped && token1_fits(*L)) {
         // One token: top-k inside the up GEMV, then the down GEMVs and the combine in one
         // kernel (no grouping: hidden row j holds pick j).
@@ -349,9 +353,14 @@ moe_status moe_forward_shell(const moe_layer* L, const void* h, int32_t T, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     void* xn = at<void>(ws, o.xn);
+    // h is read by the norm (or the router that normalises) and then only by the final
+    // kernel, element by element before out is written there, so out may alias h.
+    if (T <= kDecodeMaxT && !router_on_mfma(*L, T) && router_norm_fits(*L)) {
+        // Decode batches: the router GEMV normalises its token chunk itself.
+        const RouterNorm norm{norm_w, eps, xn};
+        return forward_body(L, xn, T, h, out, ws, o, s, &norm);
+    }
     SMOE_TRY(launch_rmsnorm(*L, h, T, norm_w, eps, xn, s));
-    // h is read again only by the final kernel, element by element before out is
-    // written there, so out may alias h.
     return forward_body(L, xn, T, h, out, ws, o, s);
 }
 

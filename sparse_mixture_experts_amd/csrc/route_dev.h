@@ -16,14 +16,15 @@ constexpr int kRouterNR = 4;  // router rows per wave (a few tokens: 1, for more
 
 // One wave: router rows row0 .. row0+NR-1 (rows 0..E-1 are experts, row E the shared-gate
 // vector; rows past n_rows repeat the last and are not written) over tokens
-// [t0, t_end), written to logits[t * ld + row] (+ the expert's bias).
+// [t0, t_end), written to logits[t * ld + row] (+ the expert's bias).  Token t's row is
+// x + (t - x_first) * d.
 template <int KB, typename TT, int NR>
 __device__ __forceinline__ void router_rows_wave(const typename TT::storage* __restrict__ x,
                                                  const typename TT::storage* __restrict__ w_router,
                                                  const float* __restrict__ b_router,
                                                  const typename TT::storage* __restrict__ w_sg, int T, int d,
                                                  int E, int n_rows, int row0, int t0, int t_end,
-                                                 float* __restrict__ logits, int ld) {
+                                                 float* __restrict__ logits, int ld, int x_first = 0) {
     using S = typename TT::storage;
     constexpr int NT = kRouterNT, N = NR * NT;
     constexpr int SH = 6 - ilog2(N);
@@ -43,7 +44,7 @@ __device__ __forceinline__ void router_rows_wave(const typename TT::storage* __r
         const int nt = min(NT, t_end - t0);
         const S* ar[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) ar[t] = x + (size_t)min(t0 + t, T - 1) * d;
+        for (int t = 0; t < NT; ++t) ar[t] = x + (size_t)(min(t0 + t, T - 1) - x_first) * d;
         const S* const (&arc)[NT] = ar;
         float acc[NR][NT] = {};
         rows_dot<NR, NT, KB, TT, TT>(wrc, arc, nt, d, acc);

@@ -8,6 +8,7 @@
 #include <math.h>
 
 #include "internal.h"
+#include "norm_dev.h"
 #include "permute_dev.h"
 #include "route_dev.h"
 #include "rowdot.h"
@@ -27,6 +28,30 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(
     const int t0 = blockIdx.y * tok_chunk;
     router_rows_wave<KB, TT, NR>(x, w_router, b_router, w_sg, T, d, E, n_rows, row0, t0, min(T, t0 + tok_chunk),
                              logits, ld);
+}
+
+// The same over the RMSNorm of the rows (the layer shell, chunks of kRouterNT tokens):
+// wave w first normalises token t0 + w of h into LDS (and, in the blocks of grid column
+// 0, into xn for the expert kernels), then the block's router rows read the LDS rows.
+template <int KB, typename TT, int NR>
+__global__ __launch_bounds__(256) void router_norm_gemv_kernel(
+    const typename TT::storage* __restrict__ h, const typename TT::storage* __restrict__ norm_w, float eps,
+    typename TT::storage* __restrict__ xn, const typename TT::storage* __restrict__ w_router,
+    const float* __restrict__ b_router, const typename TT::storage* __restrict__ w_sg, int T, int d, int E,
+    int n_rows, float* __restrict__ logits, int ld) {
+    using S = typename TT::storage;
+    extern __shared__ uint4 smem_rows[];  // kRouterNT rows of d elements
+    S* xs = reinterpret_cast<S*>(smem_rows);
+    const int t0 = blockIdx.y * kRouterNT;
+    const int w = wave_id(), t = t0 + w;
+    if (t < T)
+        rmsnorm_row_wave<TT>(h + (size_t)t * d, norm_w, eps, d, xs + (size_t)w * d,
+                             blockIdx.x == 0 ? xn + (size_t)t * d : nullptr);
+    __syncthreads();
+    const int row0 = (blockIdx.x * 4 + w) * NR;
+    if (row0 >= n_rows) return;
+    router_rows_wave<KB, TT, NR>(xs, w_router, b_router, w_sg, T, d, E, n_rows, row0, t0, min(T, t0 + kRouterNT),
+                                 logits, ld, t0);
 }
 
 // One wave per token: the wave top-k, the weights, and the shared-expert gate input.
@@ -137,7 +162,7 @@ __global__ __launch_bounds__(1024) void decode_route_kernel(
 
 template <typename TT>
 hipError_t launch_router_t(const moe_layer& L, const void* x, int T, float* logits, int ld,
-                           hipStream_t s) {
+                           const RouterNorm* norm, hipStream_t s) {
     using S = typename TT::storage;
     const int n_rows = L.n_expert + (L.shared_ff > 0 ? 1 : 0);
     // Small batches: one 4-token chunk per block row, so that every wave issues its
@@ -149,13 +174,23 @@ hipError_t launch_router_t(const moe_layer& L, const void* x, int T, float* logi
     dim3 grid((n_rows + 4 * nr - 1) / (4 * nr), (T + tok_chunk - 1) / tok_chunk);
     const S* xs = static_cast<const S*>(x);
     const S* wr = static_cast<const S*>(L.w_router);
+    // The normalising variant works on chunks of kRouterNT tokens held in LDS.
+    if (norm && (tok_chunk != kRouterNT || !router_norm_fits(L))) return hipErrorInvalidValue;
+    const size_t norm_lds = norm ? (size_t)kRouterNT * L.d * sizeof(S) : 0;
     const S* wsg = static_cast<const S*>(L.ws_gate_inp);
     // Weight batches of at most 4 chunks per lane (longer rows loop over batches).
     switch (min(pick_kb(L.d, TT::VEC), 4)) {
 #define SMOE_ROUTER_LAUNCH(KB, NR)                                                             \
-    router_gemv_kernel<KB, TT, NR><<<grid, 256, 0, s>>>(xs, wr, L.b_router, wsg, T, L.d,        \
-                                                        L.n_expert, n_rows, tok_chunk, logits, \
-                                                        ld)
+    do {                                                                                       \
+        if (norm)                                                                              \
+            router_norm_gemv_kernel<KB, TT, NR><<<grid, 256, norm_lds, s>>>(                   \
+                xs, static_cast<const S*>(norm->w), norm->eps, static_cast<S*>(norm->xn), wr,   \
+                L.b_router, wsg, T, L.d, L.n_expert, n_rows, logits, ld);                     \
+        else                                                                                   \
+            router_gemv_kernel<KB, TT, NR><<<grid, 256, 0, s>>>(xs, wr, L.b_router, wsg, T,     \
+                                                                L.d, L.n_expert, n_rows,       \
+                                                                tok_chunk, logits, ld);        \
+    } while (0)
 #define SMOE_ROUTER_CASE(KB)                                                                   \
     case KB:                                                                                   \
         if (one_row) SMOE_ROUTER_LAUNCH(KB, 1);                                                \
@@ -191,9 +226,13 @@ hipError_t launch_decode_route(const moe_layer& L, const float* logits, int ld, 
 }
 
 hipError_t launch_router_logits(const moe_layer& L, const void* x, int T, float* logits, int ld,
-                                hipStream_t s) {
-    return L.dtype == MOE_BF16 ? launch_router_t<BF16>(L, x, T, logits, ld, s)
-                               : launch_router_t<F32>(L, x, T, logits, ld, s);
+                                hipStream_t s, const RouterNorm* norm) {
+    return L.dtype == MOE_BF16 ? launch_router_t<BF16>(L, x, T, logits, ld, norm, s)
+                               : launch_router_t<F32>(L, x, T, logits, ld, norm, s);
+}
+
+bool router_norm_fits(const moe_layer& L) {
+    return (size_t)kRouterNT * L.d * (L.dtype == MOE_BF16 ? 2 : 4) <= kRouterNormMaxLds;
 }
 
 hipError_t launch_topk(const moe_layer& L, const float* logits, int ld, int T, int32_t* idx,
