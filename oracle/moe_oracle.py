@@ -21,6 +21,8 @@ The passages followed:
   ``gate_up`` with bias, gate clamped from above, up clamped on both sides,
   ``glu = gate * sigmoid(alpha * gate)``, ``h = (up + 1) * glu``, down projection with
   bias, weighted sum with the routing scores.
+* "Phase 19: MoE - gpt-oss-20b", section 3 and the tensor layout: MXFP4 expert weights
+  (32 FP4 codes and one E8M0 scale per block), dequantised before use.
 * "Llama Forward Pass", section "Key Operations", RMSNorm, and "Qwen3.5-MoE Model
   Implementation", section "Architecture" (post-attention norm -> MoE FFN -> residual):
   the layer shell around the block (``moe_shell``).
@@ -56,9 +58,35 @@ def widen(a) -> np.ndarray | None:
     return a.astype(np.float64)
 
 
+# FP4 (E2M1) code table of the OCP Microscaling formats: sign bit 3, two exponent bits
+# (bias 1), one mantissa bit; exponent 0 holds 0 and the subnormal 0.5.  The gpt-oss page
+# names the table (fp4_lut) without printing it.
+FP4_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                     -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+
+
+def mxfp4_dequant(blocks, scales) -> np.ndarray:
+    """MXFP4 weights ("Phase 19: MoE - gpt-oss-20b", section 3, MXFP4 dequantisation, and
+    the measured tensor layout): ``blocks[..., nblk, 16]`` uint8 hold 32 FP4 codes per 16
+    bytes, the low nibble of byte i being element 2i and the high nibble element 2i+1;
+    ``scales[..., nblk]`` uint8 are E8M0 exponents shared by the block's 32 elements;
+    value = fp4(code) * 2^(scale - 127) (scale 255 is NaN).  Returns fp64
+    ``[..., nblk * 32]``."""
+    b = np.asarray(blocks, dtype=np.uint8)
+    sc = np.asarray(scales, dtype=np.int64)
+    codes = np.stack([b & 0x0F, b >> 4], axis=-1).reshape(b.shape[:-1] + (32,))
+    mult = np.where(sc == 255, np.nan, np.ldexp(1.0, sc - 127))
+    vals = FP4_E2M1[codes] * mult[..., None]
+    return vals.reshape(b.shape[:-2] + (b.shape[-2] * 32,))
+
+
 def _expert(L: dict, name: str, e: int) -> np.ndarray | None:
     t = L.get(name)
-    return None if t is None else widen(t[e])
+    if t is None:
+        return None
+    if L.get("expert_format") == "mxfp4" and name in ("w_gate_up", "w_down"):
+        return mxfp4_dequant(t[e], L[name + "_scales"][e])
+    return widen(t[e])
 
 
 # ----------------------------------------------------------------------------- router
@@ -348,8 +376,11 @@ def brute_topk(zrow, k):
 
 
 def brute_forward(L: dict, x) -> np.ndarray:
-    """Scalar Python loops over the whole layer for tiny shapes (d, ff <= 16, E <= 6)."""
+    """Scalar Python loops over the whole layer for tiny shapes (d, ff <= 16, E <= 6), dense
+    expert weights only."""
     import math
+    if L.get("expert_format", "dense") != "dense":
+        raise ValueError("brute_forward takes dense expert weights")
     xf = widen(x)
     T, d = xf.shape
     E, k, ff = L["n_expert"], L["k"], L["ff"]

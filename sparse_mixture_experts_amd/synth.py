@@ -40,7 +40,7 @@ _CODE = {
     "w_router": 1, "b_router": 2, "w_gate": 3, "w_up": 4, "w_down": 5,
     "w_gate_up": 6, "b_gate_up": 7, "b_down": 8, "ws_gate": 9, "ws_up": 10,
     "ws_down": 11, "ws_gate_inp": 12, "x": 20, "x_redraw": 21, "norm_w": 30, "h": 31,
-    "h_redraw": 32,
+    "h_redraw": 32, "w_gate_up_scales": 40, "w_down_scales": 41,
 }
 
 ROUTE_SOFTMAX_TOPK_RENORM = "softmax_topk_renorm"
@@ -69,6 +69,7 @@ class LayerSpec:
     router_bias_std: float = 0.1
     zipf_s: float = 1.1
     bias_std: float = 0.02          # expert biases of the clamped variant
+    experts: str = "dense"          # "dense" | "mxfp4" (gate_up / down of the clamped variant)
 
 
 # The workloads.  Distributions: x ~ N(0,1); expert and shared weights ~ N(0, weight_std);
@@ -84,6 +85,11 @@ SPECS = {
                         dtype="bf16", route=ROUTE_TOPK_SOFTMAX, act=ACT_SWIGLU_OAI,
                         router_std=1.0 / math.sqrt(2880), router_bias="normal",
                         router_bias_std=0.1),
+    # The same layer with MXFP4 gate_up / down weights, as the checkpoint stores them.
+    "gptoss_mx": LayerSpec("gptoss_mx", d=2880, n_expert=32, ff=2880, k=4, shared_ff=0,
+                           dtype="bf16", route=ROUTE_TOPK_SOFTMAX, act=ACT_SWIGLU_OAI,
+                           router_std=1.0 / math.sqrt(2880), router_bias="normal",
+                           router_bias_std=0.1, experts="mxfp4"),
     "mixtral": LayerSpec("mixtral", d=4096, n_expert=8, ff=14336, k=2, shared_ff=0,
                          dtype="bf16", router_std=1.0 / math.sqrt(4096)),
 }
@@ -147,6 +153,21 @@ def _stacked(seed: int, code: str, E: int, shape, std: float, dtype: str,
     return out
 
 
+def _mxfp4_stacked(seed: int, code: str, E: int, rows: int, K: int, std: float, experts=None):
+    """MXFP4 tensors [E, rows, K/32, 16] uint8 (two uniformly drawn FP4 codes per byte) and
+    their E8M0 scales [E, rows, K/32] uint8, drawn around the exponent that gives values
+    of standard deviation ~std (FP4 codes drawn uniformly have rms 2.93)."""
+    nblk = K // 32
+    e0 = 127 + int(round(math.log2(std / 2.93)))
+    blocks = np.zeros((E, rows, nblk, 16), dtype=np.uint8)
+    scales = np.zeros((E, rows, nblk), dtype=np.uint8)
+    for e in (range(E) if experts is None else experts):
+        g = _rng(seed, _CODE[code], e)
+        blocks[e] = g.integers(0, 256, size=(rows, nblk, 16), dtype=np.uint8)
+        scales[e] = (e0 + g.integers(-1, 2, size=(rows, nblk))).astype(np.uint8)
+    return blocks, scales
+
+
 def make_layer(sp: LayerSpec, seed: int = 0, experts=None) -> dict:
     """All parameters of one layer, in storage form (uint16 bf16 bits or float32).
 
@@ -172,11 +193,19 @@ def make_layer(sp: LayerSpec, seed: int = 0, experts=None) -> dict:
         L["w_up"] = _stacked(seed, "w_up", E, (ff, d), sp.weight_std, dt, experts)
         L["w_gate_up"] = L["b_gate_up"] = L["b_down"] = None
     else:
-        L["w_gate_up"] = _stacked(seed, "w_gate_up", E, (2 * ff, d), sp.weight_std, dt, experts)
         L["b_gate_up"] = _stacked(seed, "b_gate_up", E, (2 * ff,), sp.bias_std, dt, experts)
         L["b_down"] = _stacked(seed, "b_down", E, (d,), sp.bias_std, dt, experts)
         L["w_gate"] = L["w_up"] = None
-    L["w_down"] = _stacked(seed, "w_down", E, (d, ff), sp.weight_std, dt, experts)
+    L["expert_format"] = sp.experts
+    if sp.experts == "mxfp4":
+        if sp.act != ACT_SWIGLU_OAI or dt != "bf16" or d % 32 or ff % 32:
+            raise ValueError("MXFP4 experts: clamped variant, bf16, widths multiple of 32")
+        for name, rows, K in (("w_gate_up", 2 * ff, d), ("w_down", d, ff)):
+            L[name], L[name + "_scales"] = _mxfp4_stacked(seed, name, E, rows, K, sp.weight_std, experts)
+    else:
+        if sp.act == ACT_SWIGLU_OAI:
+            L["w_gate_up"] = _stacked(seed, "w_gate_up", E, (2 * ff, d), sp.weight_std, dt, experts)
+        L["w_down"] = _stacked(seed, "w_down", E, (d, ff), sp.weight_std, dt, experts)
     if ffs > 0:
         L["ws_gate"] = _store(_draw(seed, "ws_gate", 0, (ffs, d), sp.weight_std), dt)
         L["ws_up"] = _store(_draw(seed, "ws_up", 0, (ffs, d), sp.weight_std), dt)

@@ -367,3 +367,48 @@ def test_moe_shell(act, ffs):
     xn = synth.f32_to_bf16_bits(hn.to(torch.bfloat16).to(torch.float32).numpy())
     assert np.allclose(out - oracle.widen(h), oracle.moe_forward_tokens(L, xn), rtol=0, atol=1e-12)
     assert oracle.moe_shell(L, h[:0], w, 1e-5).shape == (0, 16)
+
+
+# ----------------------------------------------------------------------------- MXFP4
+
+def test_fp4_table_from_bit_fields():
+    # E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0; exponent 0 is the
+    # subnormal range m * 0.5.
+    for c in range(16):
+        s, e, m = c >> 3, (c >> 1) & 3, c & 1
+        mag = 0.5 * m if e == 0 else 2.0 ** (e - 1) * (1 + 0.5 * m)
+        assert oracle.FP4_E2M1[c] == (-mag if s else mag), c
+
+
+def test_mxfp4_block_layout_and_scale():
+    blocks = np.zeros((1, 2, 16), dtype=np.uint8)
+    blocks[0, 0, 0] = 0x21      # element 0: code 1 (0.5), element 1: code 2 (1.0)
+    blocks[0, 0, 1] = 0x43      # element 2: code 3 (1.5), element 3: code 4 (2.0)
+    blocks[0, 0, 15] = 0xF9     # element 30: code 9 (-0.5), element 31: code 15 (-6)
+    blocks[0, 1, 0] = 0x07      # second block, element 32: code 7 (6.0)
+    v = oracle.mxfp4_dequant(blocks, np.array([[127, 129]], dtype=np.uint8))
+    assert v.shape == (1, 64)
+    assert list(v[0, :4]) == [0.5, 1.0, 1.5, 2.0]
+    assert list(v[0, 30:32]) == [-0.5, -6.0]
+    assert v[0, 32] == 6.0 * 4 and v[0, 33] == 0.0      # scale 129 = 2^2
+    assert np.all(v[0, 4:30] == 0)
+    w = oracle.mxfp4_dequant(blocks[:, :1], np.array([[120]], dtype=np.uint8))
+    assert w[0, 1] == 2.0 ** -7
+    assert np.isnan(oracle.mxfp4_dequant(blocks[:, :1], np.array([[255]], dtype=np.uint8))).all()
+
+
+def test_mxfp4_layer_equals_dequantised_bf16_layer():
+    # Every FP4 value times a power of two is a bf16 value, so the MXFP4 layer must give
+    # exactly what the dense bf16 layer holding the dequantised weights gives.
+    sp = synth.spec("gptoss_mx", d=64, n_expert=6, ff=64, k=2)
+    L = synth.make_layer(sp, seed=3)
+    D = dict(L)
+    D["expert_format"] = "dense"
+    for n in ("w_gate_up", "w_down"):
+        deq = oracle.mxfp4_dequant(L[n], L[n + "_scales"])
+        D[n] = synth.f32_to_bf16_bits(deq.astype(np.float32))
+        assert np.array_equal(oracle.widen(D[n]), deq)
+        del D[n + "_scales"]
+    x = synth.make_tokens(L, 9, seed=4)
+    assert np.array_equal(oracle.moe_forward(L, x), oracle.moe_forward(D, x))
+    assert np.allclose(oracle.moe_forward(L, x), oracle.moe_forward_tokens(L, x), rtol=0, atol=1e-12)
