@@ -246,7 +246,7 @@ def time_workload(name, steps, warmup, layer_cache):
         tens = {k: (v.clone() if v is not None else None) for k, v in lay0.tensors.items()}
         layers.append(moe.Layer(L["d"], L["n_expert"], L["ff"], L["k"], L["shared_ff"], L["dtype"],
                                 L["route"], L["act"], L["route_scale"], L["oai_alpha"],
-                                L["oai_limit"], **tens))
+                                L["oai_limit"], expert_format=L.get("expert_format", "dense"), **tens))
     xs = [moe.to_device(x) for x in xs_np]
     ws = moe.workspace(lay0, T)
     y = torch.empty((T, L["d"]), dtype=lay0.torch_dtype, device="cuda")

@@ -71,12 +71,25 @@ enum { MOE_ROUTE_SOFTMAX_TOPK_RENORM = 0, MOE_ROUTE_TOPK_SOFTMAX = 1 };
 enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 };
 
 /* Kernel path.  AUTO: the decode GEMV path for T <= 64, the grouped MFMA path above.
- * DECODE / GROUPED force one path at any T (GROUPED requires MOE_BF16). */
+ * DECODE / GROUPED force one path at any T (GROUPED requires MOE_BF16 and dense experts). */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_GROUPED = 2 };
 
-/* One MoE layer.  Fixed layout: 9 int32, 3 float, then 12 pointers (offset 48). No
- * field depends on a build flag.  All pointers are device memory, 16-byte aligned
- * (b_router, b_gate_up, b_down: element-aligned suffices). */
+/* Storage of the routed experts' gate_up and down weights.
+ *  DENSE: in `dtype`, as described at each field.
+ *  MXFP4 ("Phase 19: MoE - gpt-oss-20b", section 3 and the measured tensor layout):
+ *    w_gate_up = blocks [E, 2*ff, d/32, 16] uint8 with scales w_gate_up_scales
+ *    [E, 2*ff, d/32] uint8, and w_down = blocks [E, d, ff/32, 16] uint8 with scales
+ *    w_down_scales [E, d, ff/32] uint8.  Each 16-byte block holds the 32 FP4 (E2M1,
+ *    OCP Microscaling) codes of 32 consecutive inputs, the low nibble of byte i being
+ *    element 2i; each scale is an E8M0 exponent: value = fp4(code) * 2^(scale - 127).
+ *    Requires MOE_BF16, MOE_ACT_SWIGLU_OAI and no shared expert; runs on the GEMV path
+ *    at every T (MOE_PATH_GROUPED is unsupported).  Biases, router, x and y stay bf16. */
+enum { MOE_EXPERTS_DENSE = 0, MOE_EXPERTS_MXFP4 = 1 };
+
+/* One MoE layer.  Fixed layout: 9 int32, 3 float, then 12 pointers (offset 48), then
+ * 2 int32 and 2 pointers (offset 144).  No field depends on a build flag.  All pointers
+ * are device memory, 16-byte aligned (b_router, b_gate_up, b_down and the MXFP4 scales:
+ * element-aligned suffices). */
 typedef struct moe_layer {
     int32_t d;            /* model width; multiple of 64                               */
     int32_t n_expert;     /* E, 1..512                                                 */
@@ -102,6 +115,10 @@ typedef struct moe_layer {
     const void* ws_up;        /* shared expert: [shared_ff, d]                         */
     const void* ws_down;      /* shared expert: [d, shared_ff]                         */
     const void* ws_gate_inp;  /* shared expert sigmoid gate vector: [d]                */
+    int32_t expert_format;    /* MOE_EXPERTS_*                                         */
+    int32_t reserved0;        /* 0                                                     */
+    const uint8_t* w_gate_up_scales;  /* MXFP4: [E, 2*ff, d/32] E8M0, else NULL        */
+    const uint8_t* w_down_scales;     /* MXFP4: [E, d, ff/32] E8M0, else NULL          */
 } moe_layer;
 
 /* ABI version of this header (bumped on any layout or signature change). */

@@ -299,6 +299,8 @@ hipError_t launch_token1_t(const moe_layer& L, int T, const float* H, int hstrid
 hipError_t launch_expert_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                               const Group* groups, const PlanMeta* meta, float* H, int hstride,
                               float* y_perm, hipStream_t s) {
+    if (L.expert_format == MOE_EXPERTS_MXFP4)
+        return launch_expert_gemv_mx(L, x, T, perm_token, groups, meta, H, hstride, y_perm, s);
     const hipError_t e = launch_expert_up_gemv(L, x, T, perm_token, groups, meta, H, hstride, s);
     if (e != hipSuccess) return e;
     const bool oai = L.act == MOE_ACT_SWIGLU_OAI;

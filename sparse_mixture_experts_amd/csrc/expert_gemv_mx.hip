@@ -1,0 +1,267 @@
+// Expert FFN GEMVs over MXFP4 expert weights (the decode path of a gpt-oss-shaped layer
+// stored as its checkpoint stores it).
+//
+// "Phase 19: MoE - gpt-oss-20b", section 3 and the measured tensor layout: gate_up
+// [E, 2ff, d/32, 16] and down [E, d, ff/32, 16] uint8 blocks, each 16-byte block the 32
+// FP4 (E2M1) codes of 32 consecutive inputs (low nibble first) sharing one E8M0 scale;
+// value = fp4(code) * 2^(scale - 127).  Experts as in section 2: interleaved gate/up
+// rows with biases, gate clamped from above, up clamped both ways, (up + 1) * gate *
+// sigmoid(alpha * gate), down projection with bias.
+//
+// The weights are never expanded in memory: each lane loads whole 16-byte blocks plus
+// their scale byte (0.53 bytes per weight instead of 2) and gfx950's scaled conversions
+// expand them in registers, two codes per instruction, to bf16 pairs that meet the bf16
+// activations in v_dot2 (fp32 accumulation).  H rows are stored in bf16 here, as on the
+// grouped path.  Lane l takes blocks l, l+64, ... of a row.
+#include "gemv_items.h"
+
+namespace smoe {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// 2^(s - 127) as a float: the E8M0 scale.  s = 0 is 2^-127 (a subnormal float), s = 255
+// is NaN.
+__device__ __forceinline__ float e8m0_scale(uint32_t s) {
+    const uint32_t bits = s == 0 ? 0x00400000u : (s == 255 ? 0x7FC00000u : s << 23);
+    return __uint_as_float(bits);
+}
+
+// Two bf16 (or fp32) weights of byte B of a code word, times the block's scale.
+template <int B>
+__device__ __forceinline__ bf16x2_t fp4_pair_bf16(uint32_t cw, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, B);
+}
+// acc += the 8 products of code word cw (elements 8w .. 8w+7 of the block) with the bf16
+// activations xw holding the same elements.
+__device__ __forceinline__ float word_dot_bf16(uint32_t cw, float scale, const uint4& xw, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(fp4_pair_bf16<0>(cw, scale), __builtin_bit_cast(bf16x2_t, xw.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(fp4_pair_bf16<1>(cw, scale), __builtin_bit_cast(bf16x2_t, xw.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(fp4_pair_bf16<2>(cw, scale), __builtin_bit_cast(bf16x2_t, xw.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(fp4_pair_bf16<3>(cw, scale), __builtin_bit_cast(bf16x2_t, xw.w), acc, false);
+    return acc;
+}
+
+// acc += sum over the block's 32 elements of w * x, w the block (codes + scale), x the
+// 32 bf16 activations in four 16-byte pieces.
+__device__ __forceinline__ float block_dot_bf16(const uint4& codes, float scale, const uint4 (&xq)[4], float acc) {
+    acc = word_dot_bf16(codes.x, scale, xq[0], acc);
+    acc = word_dot_bf16(codes.y, scale, xq[1], acc);
+    acc = word_dot_bf16(codes.z, scale, xq[2], acc);
+    acc = word_dot_bf16(codes.w, scale, xq[3], acc);
+    return acc;
+}
+
+constexpr int kMxUnits = 2;   // hidden units per up wave (4 interleaved rows)
+constexpr int kMxUpNT = 2;    // group rows per up step
+constexpr int kMxDownNR = 4;  // output dims per down wave
+constexpr int kMxDownNT = 2;  // H rows per down step
+constexpr int kMxNB = 2;      // blocks per lane and row held at once (K up to 4096)
+
+struct MxArgs {
+    const uint16_t* x;          // [T, d] bf16
+    const int32_t* perm_token;
+    const Group* groups;
+    const uint8_t* w_gate_up;   // blocks [E, 2ff, d/32, 16]
+    const uint8_t* s_gate_up;   // [E, 2ff, d/32]
+    const uint16_t* b_gate_up;  // [E, 2ff] bf16
+    const uint8_t* w_down;      // blocks [E, d, ff/32, 16]
+    const uint8_t* s_down;      // [E, d, ff/32]
+    const uint16_t* b_down;     // [E, d] bf16 or null
+    uint16_t* H;                // bf16 [rows, hstride]
+    float* y;
+    int hstride, T, tk, d, ff;
+    float alpha, limit;
+};
+
+// Block i of this lane (block index lane + 64 i) of `rows` weight rows: codes and scale;
+// blocks past nblk read block 0 with zero codes (value +0).
+template <int NR, int NB>
+__device__ __forceinline__ void load_mx_rows(const uint8_t* const (&wrow)[NR], const uint8_t* const (&srow)[NR],
+                                             int nblk, uint4 (&codes)[NR][NB], float (&scale)[NR][NB]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int b = lane + kWave * i;
+        const int bc = b < nblk ? b : 0;
+        const unsigned m = in_range_mask(b, nblk);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            codes[r][i] = and_mask(ld16(wrow[r] + (size_t)bc * 16), m);
+            scale[r][i] = e8m0_scale(srow[r][bc]);
+        }
+    }
+}
+
+// One wave: hidden units f0, f0+1 of routed group g (interleaved rows 2f0 .. 2f0+3), every
+// row of the group, kMxUpNT rows per step.
+template <int NB>
+__device__ __forceinline__ void mx_up_item(const MxArgs& a, const Group& g, int f0) {
+    constexpr int NR = 2 * kMxUnits, NT = kMxUpNT, N = NR * NT;
+    constexpr int SH = 6 - ilog2(N);
+    const int nblk = a.d / 32;
+    const size_t row_blocks = (size_t)nblk;
+    const uint8_t* wrow[NR];
+    const uint8_t* srow[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int f = min(f0 + r / 2, a.ff - 1);
+        const size_t R = (size_t)g.e * 2 * a.ff + 2 * f + (r & 1);
+        wrow[r] = a.w_gate_up + R * row_blocks * 16;
+        srow[r] = a.s_gate_up + R * row_blocks;
+    }
+    const uint8_t* const (&wc)[NR] = wrow;
+    const uint8_t* const (&sc)[NR] = srow;
+    uint4 codes[NR][NB];
+    float scale[NR][NB];
+    load_mx_rows<NR, NB>(wc, sc, nblk, codes, scale);
+    // After the reduction lane l holds value v = t * NR + r = l >> SH; the up row of gate
+    // row r sits one value on, 1 << SH lanes higher in the same 16-lane row.
+    const int lane = lane_id();
+    const int my_t = (lane >> SH) / NR, my_r = (lane >> SH) % NR;
+    const int my_f = f0 + my_r / 2;
+    const bool writer = (my_r & 1) == 0 && (lane & ((1 << SH) - 1)) == 0 && my_f < a.ff;
+    float bg = 0.f, bu = 0.f;
+    if (writer) {
+        const uint16_t* b = a.b_gate_up + (size_t)g.e * 2 * a.ff + 2 * my_f;
+        bg = bf16_to_f32(b[0]);
+        bu = bf16_to_f32(b[1]);
+    }
+    for (int tb = 0; tb < g.n; tb += NT) {
+        const int nt = min(NT, g.n - tb);
+        float acc[NR][NT] = {};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int rr = min(tb + t, g.n - 1);
+            const int tok = min(max(a.T == 1 ? 0 : a.perm_token[g.row0 + rr], 0), a.T - 1);
+            const uint16_t* xr = a.x + (size_t)tok * a.d;
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int b = lane + kWave * i;
+                const int bc = b < nblk ? b : 0;
+                uint4 xq[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xq[q] = ld16(xr + (size_t)bc * 32 + q * 8);
+#pragma unroll
+                for (int r = 0; r < NR; ++r) acc[r][t] = block_dot_bf16(codes[r][i], scale[r][i], xq, acc[r][t]);
+            }
+        }
+        float v[N];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) v[t * NR + r] = acc[r][t];
+        const float sum = wave_reduce_scatter<N>(v);
+        const float up = __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x100 + (1 << SH), 0xF, 0xF, false));
+        if (writer && my_t < nt) {
+            float gv = fminf(sum + bg, a.limit);
+            float uv = fminf(fmaxf(up + bu, -a.limit), a.limit);
+            a.H[(size_t)(g.row0 + tb + my_t) * a.hstride + my_f] =
+                f32_to_bf16((uv + 1.0f) * gv * sigmoidf_(a.alpha * gv));
+        }
+    }
+}
+
+// One wave: output dims i0 .. i0+NR-1 of routed group g, kMxDownNT H rows per step.
+template <int NB>
+__device__ __forceinline__ void mx_down_item(const MxArgs& a, const Group& g, int i0) {
+    constexpr int NR = kMxDownNR, NT = kMxDownNT, N = NR * NT;
+    constexpr int SH = 6 - ilog2(N);
+    const int nblk = a.ff / 32;
+    const uint8_t* wrow[NR];
+    const uint8_t* srow[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const size_t R = (size_t)g.e * a.d + min(i0 + r, a.d - 1);
+        wrow[r] = a.w_down + R * nblk * 16;
+        srow[r] = a.s_down + R * nblk;
+    }
+    const uint8_t* const (&wc)[NR] = wrow;
+    const uint8_t* const (&sc)[NR] = srow;
+    uint4 codes[NR][NB];
+    float scale[NR][NB];
+    load_mx_rows<NR, NB>(wc, sc, nblk, codes, scale);
+    // After the reduction lane l holds value v = t * NR + r = l >> SH.
+    const int lane = lane_id();
+    const int my_t = (lane >> SH) / NR, my_i = i0 + (lane >> SH) % NR;
+    const bool writer = (lane & ((1 << SH) - 1)) == 0 && my_i < a.d;
+    const float bias = (writer && a.b_down) ? bf16_to_f32(a.b_down[(size_t)g.e * a.d + my_i]) : 0.0f;
+    for (int tb = 0; tb < g.n; tb += NT) {
+        const int nt = min(NT, g.n - tb);
+        float acc[NR][NT] = {};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint16_t* hr = a.H + (size_t)(g.row0 + min(tb + t, g.n - 1)) * a.hstride;
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int b = lane + kWave * i;
+                const int bc = b < nblk ? b : 0;
+                uint4 hq[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) hq[q] = ld16(hr + (size_t)bc * 32 + q * 8);
+#pragma unroll
+                for (int r = 0; r < NR; ++r) acc[r][t] = block_dot_bf16(codes[r][i], scale[r][i], hq, acc[r][t]);
+            }
+        }
+        float v[N];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) v[t * NR + r] = acc[r][t];
+        const float sum = wave_reduce_scatter<N>(v);
+        if (writer && my_t < nt) a.y[(size_t)(g.row0 + tb + my_t) * a.d + my_i] = sum + bias;
+    }
+}
+
+// Grid row y takes routed group y (there is no shared expert with MXFP4 experts).
+__device__ __forceinline__ bool mx_group(const MxArgs& a, const PlanMeta* meta, Group& g) {
+    return gemv_group(a.groups, meta, false, a.T, a.tk, g);
+}
+
+template <int NB>
+__global__ __launch_bounds__(256) void expert_up_gemv_mx_kernel(MxArgs a, const PlanMeta* meta) {
+    Group g;
+    if (!mx_group(a, meta, g)) return;
+    const int f0 = (blockIdx.x * 4 + wave_id()) * kMxUnits;
+    if (f0 < a.ff) mx_up_item<NB>(a, g, f0);
+}
+
+template <int NB>
+__global__ __launch_bounds__(256) void expert_down_gemv_mx_kernel(MxArgs a, const PlanMeta* meta) {
+    Group g;
+    if (!mx_group(a, meta, g)) return;
+    const int i0 = (blockIdx.x * 4 + wave_id()) * kMxDownNR;
+    if (i0 < a.d) mx_down_item<NB>(a, g, i0);
+}
+
+int blocks_per_lane(int K) { return (K / 32 + kWave - 1) / kWave; }
+
+}  // namespace
+
+bool mx_fits(const moe_layer& L) {
+    return blocks_per_lane(L.d) <= kMxNB && blocks_per_lane(L.ff) <= kMxNB && L.d % 32 == 0 && L.ff % 32 == 0;
+}
+
+hipError_t launch_expert_gemv_mx(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
+                                 const Group* groups, const PlanMeta* meta, float* H, int hstride, float* y_perm,
+                                 hipStream_t s) {
+    if (!mx_fits(L)) return hipErrorInvalidValue;
+    MxArgs a{static_cast<const uint16_t*>(x), perm_token, groups,
+             static_cast<const uint8_t*>(L.w_gate_up), L.w_gate_up_scales, static_cast<const uint16_t*>(L.b_gate_up),
+             static_cast<const uint8_t*>(L.w_down), L.w_down_scales, static_cast<const uint16_t*>(L.b_down),
+             reinterpret_cast<uint16_t*>(H), y_perm, hstride, T, T * L.k, L.d, L.ff, L.oai_alpha, L.oai_limit};
+    const int gmax = max_groups(L.n_expert, T, L.k, false);
+    const dim3 gu((L.ff + 4 * kMxUnits - 1) / (4 * kMxUnits), gmax);
+    const dim3 gd((L.d + 4 * kMxDownNR - 1) / (4 * kMxDownNR), gmax);
+    if (blocks_per_lane(L.d) == 1) expert_up_gemv_mx_kernel<1><<<gu, 256, 0, s>>>(a, meta);
+    else expert_up_gemv_mx_kernel<2><<<gu, 256, 0, s>>>(a, meta);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (blocks_per_lane(L.ff) == 1) expert_down_gemv_mx_kernel<1><<<gd, 256, 0, s>>>(a, meta);
+    else expert_down_gemv_mx_kernel<2><<<gd, 256, 0, s>>>(a, meta);
+    return hipGetLastError();
+}
+
+}  // namespace smoe

@@ -77,6 +77,13 @@ hipError_t launch_combine_sum(const moe_layer& L, const uint16_t* y_rows, const 
 hipError_t launch_expert_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                               const Group* groups, const PlanMeta* meta, float* H, int hstride,
                               float* y_perm, hipStream_t s);
+// GEMVs over MXFP4 expert weights (up then down; H in bf16 in the fp32 H region;
+// unweighted fp32 rows), for layers with MOE_EXPERTS_MXFP4; mx_fits: the widths the
+// kernels take (K <= 4096).
+bool mx_fits(const moe_layer& L);
+hipError_t launch_expert_gemv_mx(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
+                                 const Group* groups, const PlanMeta* meta, float* H, int hstride, float* y_perm,
+                                 hipStream_t s);
 // Up GEMV alone (H rows), for callers that finish the layer themselves.
 hipError_t launch_expert_up_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                                  const Group* groups, const PlanMeta* meta, float* H, int hstride,

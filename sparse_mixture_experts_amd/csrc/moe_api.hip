@@ -89,6 +89,14 @@ moe_status check_layer(const moe_layer* L) {
     if (L->d % 64 || L->ff % 64 || L->shared_ff % 64) return MOE_ERR_UNSUPPORTED;
     if (L->n_expert > kMaxExperts || L->k > kMaxK) return MOE_ERR_UNSUPPORTED;
     if (L->path == MOE_PATH_GROUPED && L->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (L->expert_format != MOE_EXPERTS_DENSE && L->expert_format != MOE_EXPERTS_MXFP4) return MOE_ERR_ARG;
+    if (L->reserved0 != 0) return MOE_ERR_ARG;
+    if (L->expert_format == MOE_EXPERTS_MXFP4) {
+        if (!L->w_gate_up_scales || !L->w_down_scales) return MOE_ERR_ARG;
+        if (L->dtype != MOE_BF16 || L->act != MOE_ACT_SWIGLU_OAI || L->shared_ff != 0 ||
+            L->path == MOE_PATH_GROUPED || !mx_fits(*L))
+            return MOE_ERR_UNSUPPORTED;
+    }
     const void* vec_ptrs[] = {L->w_router, L->w_gate, L->w_up, L->w_gate_up, L->w_down,
                               L->ws_gate, L->ws_up, L->ws_down, L->ws_gate_inp};
     for (const void* p : vec_ptrs)
@@ -113,9 +121,9 @@ inline moe_status status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MO
         if (err_ != hipSuccess) return MOE_ERR_DEVICE; \
     } while (0)
 
-// The grouped MFMA path (bf16 only) or the decode GEMV path.
+// The grouped MFMA path (bf16, dense experts) or the decode GEMV path.
 bool use_grouped(const moe_layer& L, int T) {
-    if (L.dtype != MOE_BF16) return false;
+    if (L.dtype != MOE_BF16 || L.expert_format != MOE_EXPERTS_DENSE) return false;
     if (L.path == MOE_PATH_GROUPED) return true;
     return L.path == MOE_PATH_AUTO && T > kDecodeMaxT;
 }
@@ -175,7 +183,8 @@ moe_status forward_body(const moe_layer* L, const void* x, int32_t T, const void
     float* row_w = grouped ? at<float>(ws, o.row_w) : nullptr;
     void* y_rows = at<void>(ws, o.yperm);
     SMOE_TRY(run_router(*L, norm ? residual : x, T, logits, o.ld, s, norm));
-    if (T == 1 && !grouped && token1_fits(*L)) {
+    const bool dense = L->expert_format == MOE_EXPERTS_DENSE;
+    if (T == 1 && !grouped && dense && token1_fits(*L)) {
         // One token: top-k inside the up GEMV, then the down GEMVs and the combine in one
         // kernel (no grouping: hidden row j holds pick j).
         SMOE_TRY(launch_token1_up(*L, x, logits, idx, w, at<float>(ws, o.H), o.hstride, s));
@@ -194,7 +203,7 @@ moe_status forward_body(const moe_layer* L, const void* x, int32_t T, const void
         SMOE_TRY(launch_permute(idx, T, L->k, L->n_expert, offsets, perm_token, perm_inv,
                                 at<int32_t>(ws, o.counts), at<int32_t>(ws, o.base), w, row_w, s));
     }
-    if (fused_route && !grouped && T <= kTokenDownMaxT && token1_fits(*L)) {
+    if (fused_route && !grouped && dense && T <= kTokenDownMaxT && token1_fits(*L)) {
         // A few tokens: up GEMV over the groups, then per token the down GEMVs of its picks
         // and the combine in one kernel.
         SMOE_TRY(launch_expert_up_gemv(*L, x, T, perm_token, at<Group>(ws, o.groups), at<PlanMeta>(ws, o.meta),
@@ -219,7 +228,7 @@ using namespace smoe;
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 2; }
+int32_t moe_abi_version(void) { return 3; }
 
 const char* moe_status_string(moe_status s) {
     switch (s) {

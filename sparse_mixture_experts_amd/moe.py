@@ -19,16 +19,19 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_ROUTE_SOFTMAX_TOPK_RENORM, MOE_ROUTE_TOPK_SOFTMAX = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_SWIGLU_OAI = 0, 1
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_GROUPED = 0, 1, 2
+MOE_EXPERTS_DENSE, MOE_EXPERTS_MXFP4 = 0, 1
 
 _ROUTE = {"softmax_topk_renorm": MOE_ROUTE_SOFTMAX_TOPK_RENORM, "topk_softmax": MOE_ROUTE_TOPK_SOFTMAX}
 _ACT = {"swiglu": MOE_ACT_SWIGLU, "swiglu_oai": MOE_ACT_SWIGLU_OAI}
 _PATH = {"auto": MOE_PATH_AUTO, "decode": MOE_PATH_DECODE, "grouped": MOE_PATH_GROUPED}
+_EXPERTS = {"dense": MOE_EXPERTS_DENSE, "mxfp4": MOE_EXPERTS_MXFP4}
 
 _P = ctypes.c_void_p
 
 
 class MoeLayer(ctypes.Structure):
-    """Mirror of ``moe_layer`` (9 int32, 3 float, 12 pointers at byte offset 48)."""
+    """Mirror of ``moe_layer`` (9 int32, 3 float, 12 pointers at byte offset 48, then 2
+    int32 and 2 pointers at offset 144)."""
     _fields_ = [
         ("d", ctypes.c_int32), ("n_expert", ctypes.c_int32), ("ff", ctypes.c_int32),
         ("k", ctypes.c_int32), ("shared_ff", ctypes.c_int32), ("dtype", ctypes.c_int32),
@@ -37,11 +40,13 @@ class MoeLayer(ctypes.Structure):
         ("w_router", _P), ("b_router", _P), ("w_gate", _P), ("w_up", _P),
         ("w_gate_up", _P), ("b_gate_up", _P), ("w_down", _P), ("b_down", _P),
         ("ws_gate", _P), ("ws_up", _P), ("ws_down", _P), ("ws_gate_inp", _P),
+        ("expert_format", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("w_gate_up_scales", _P), ("w_down_scales", _P),
     ]
 
 
 POINTER_FIELDS = [f for f, t in MoeLayer._fields_ if t is _P]
-ABI_VERSION = 2
+ABI_VERSION = 3
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_forward", "moe_forward_shell"]
@@ -124,6 +129,8 @@ def to_device(a: np.ndarray | None, device="cuda"):
     torch = _torch()
     if a.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    if a.dtype == np.uint8:
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
 
@@ -132,7 +139,7 @@ class Layer:
     points at them.  Holds references so the tensors outlive the struct."""
 
     def __init__(self, d, n_expert, ff, k, shared_ff, dtype, route, act, route_scale=1.0,
-                 oai_alpha=1.702, oai_limit=7.0, path="auto", **tensors):
+                 oai_alpha=1.702, oai_limit=7.0, path="auto", expert_format="dense", **tensors):
         self.tensors = dict(tensors)
         self.d, self.n_expert, self.ff, self.k, self.shared_ff = d, n_expert, ff, k, shared_ff
         self.dtype = dtype
@@ -141,6 +148,8 @@ class Layer:
         s.dtype = MOE_BF16 if dtype == "bf16" else MOE_F32
         s.route, s.act, s.path = _ROUTE[route], _ACT[act], _PATH[path]
         s.route_scale, s.oai_alpha, s.oai_limit = route_scale, oai_alpha, oai_limit
+        s.expert_format = _EXPERTS[expert_format]
+        self.expert_format = expert_format
         for name in POINTER_FIELDS:
             setattr(s, name, _ptr(self.tensors.get(name)))
         self.struct = s
@@ -151,7 +160,8 @@ class Layer:
         tensors = {n: to_device(L.get(n), device) for n in POINTER_FIELDS}
         return cls(L["d"], L["n_expert"], L["ff"], L["k"], L["shared_ff"], L["dtype"], L["route"],
                    L["act"], L.get("route_scale", 1.0), L.get("oai_alpha", 1.702),
-                   L.get("oai_limit", 7.0), path=path, **tensors)
+                   L.get("oai_limit", 7.0), path=path, expert_format=L.get("expert_format", "dense"),
+                   **tensors)
 
     def with_path(self, path: str) -> "Layer":
         other = Layer.__new__(Layer)

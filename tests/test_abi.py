@@ -35,10 +35,13 @@ def test_exports_every_declared_function(lib):
 
 
 def test_struct_layout(lib):
-    assert ctypes.sizeof(moe.MoeLayer) == 48 + 12 * 8
     assert moe.MoeLayer.route_scale.offset == 36
     assert moe.MoeLayer.w_router.offset == 48
     assert moe.MoeLayer.ws_gate_inp.offset == 48 + 11 * 8
+    assert moe.MoeLayer.expert_format.offset == 144
+    assert moe.MoeLayer.w_gate_up_scales.offset == 152
+    assert moe.MoeLayer.w_down_scales.offset == 160
+    assert ctypes.sizeof(moe.MoeLayer) == 168
 
 
 def fake_layer(**kw):
@@ -174,3 +177,19 @@ def test_shell_argument_errors(lib):
     _, need = ws_size(lib, s, 4)
     assert shell(lib, s, nbytes=need - 1) == moe.MOE_ERR_WORKSPACE
     assert lib.moe_forward_shell(None, FAKE, 4, FAKE, 1e-5, FAKE * 2, FAKE * 3, 1 << 40, None) == moe.MOE_ERR_ARG
+
+
+def test_mxfp4_layer_checks(lib):
+    mx = dict(expert_format=moe.MOE_EXPERTS_MXFP4, act=moe.MOE_ACT_SWIGLU_OAI, w_gate_up=FAKE,
+              b_gate_up=FAKE, w_gate_up_scales=FAKE * 5, w_down_scales=FAKE * 6)
+    assert ws_size(lib, fake_layer(**mx), 4)[0] == moe.MOE_OK
+    assert ws_size(lib, fake_layer(**dict(mx, w_down_scales=None)), 4)[0] == moe.MOE_ERR_ARG
+    assert ws_size(lib, fake_layer(**dict(mx, expert_format=7)), 4)[0] == moe.MOE_ERR_ARG
+    assert ws_size(lib, fake_layer(**dict(mx, reserved0=1)), 4)[0] == moe.MOE_ERR_ARG
+    assert ws_size(lib, fake_layer(**dict(mx, dtype=moe.MOE_F32)), 4)[0] == moe.MOE_ERR_UNSUPPORTED
+    assert ws_size(lib, fake_layer(**dict(mx, act=moe.MOE_ACT_SWIGLU, w_gate=FAKE, w_up=FAKE)), 4)[0] \
+        == moe.MOE_ERR_UNSUPPORTED
+    assert ws_size(lib, fake_layer(**dict(mx, path=moe.MOE_PATH_GROUPED)), 4)[0] == moe.MOE_ERR_UNSUPPORTED
+    assert ws_size(lib, fake_layer(**dict(mx, d=8192)), 4)[0] == moe.MOE_ERR_UNSUPPORTED  # K > 4096
+    sh = dict(mx, shared_ff=64, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, ws_gate_inp=FAKE)
+    assert ws_size(lib, fake_layer(**sh), 4)[0] == moe.MOE_ERR_UNSUPPORTED

@@ -335,7 +335,9 @@ def test_full_qwen_prefill_zipf():
 
 
 @pytest.mark.parametrize("name,T,sample", [("gptoss", 1, None), ("gptoss", 4096, 256),
-                                           ("mixtral", 16, None), ("mixtral", 16384, 256)])
+                                           ("mixtral", 16, None), ("mixtral", 16384, 256),
+                                           ("gptoss_mx", 1, None), ("gptoss_mx", 64, None),
+                                           ("gptoss_mx", 1000, 128)])
 def test_full_other_layers(name, T, sample):
     say("full", name, T)
     L, x = case(name, T)
@@ -450,3 +452,55 @@ def test_full_qwen_shell(T):
     ref = oracle.moe_shell(L, h, w, EPS)
     e = assert_shell_close(to_numpy_y(out), ref, oracle.widen(h), "bf16", "shell")
     say(f"  block part rel err {e:.2e}")
+
+
+# ----------------------------------------------------------------------------- MXFP4 experts
+
+MX_SMALL = [dict(d=320, n_expert=16, ff=192), dict(d=4096, n_expert=8, ff=128, k=2)]
+
+
+@pytest.mark.parametrize("T", [1, 7, 100])
+@pytest.mark.parametrize("ov", MX_SMALL, ids=["d320", "d4096"])
+def test_mxfp4_forward(ov, T):
+    say("mxfp4 forward", ov, T)
+    L, x = case("gptoss_mx", T, **ov)
+    lay = dev_layer("gptoss_mx", **ov)
+    y = moe_mod().forward(lay, xdev(x))
+    torch.cuda.synchronize()
+    e = assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "bf16", "y")
+    say(f"  rel err {e:.2e}")
+
+
+def test_mxfp4_expert_ffn_rows():
+    # The expert stage alone through the ABI: unweighted rows of every (token, pick) pair.
+    ov = MX_SMALL[0]
+    L, x = case("gptoss_mx", 37, **ov)
+    lay = dev_layer("gptoss_mx", **ov)
+    idx, _, _ = moe_mod().route(lay, xdev(x))
+    off, pt, pi = moe_mod().permute(idx, L["n_expert"])
+    yp = moe_mod().expert_ffn(lay, xdev(x), off, pt)
+    torch.cuda.synchronize()
+    ridx, _, _ = oracle.route(L, x)
+    _, roff, rpt, _ = oracle.permute(ridx, L["n_expert"])
+    assert np.array_equal(off.cpu().numpy(), roff) and np.array_equal(pt.cpu().numpy(), rpt)
+    ref = oracle.expert_rows(L, x, roff, rpt)
+    assert_close(to_numpy_y(yp), ref, "bf16", "rows")
+
+
+def test_mxfp4_shell():
+    ov = MX_SMALL[0]
+    for T in (1, 64, 100):
+        L, w, h = shell_case("gptoss_mx", T, **ov)
+        lay = dev_layer("gptoss_mx", **ov)
+        out = moe_mod().forward_shell(lay, xdev(h), xdev(w), EPS)
+        torch.cuda.synchronize()
+        ref = oracle.moe_shell(L, h, w, EPS)
+        assert_shell_close(to_numpy_y(out), ref, oracle.widen(h), "bf16", f"mx shell T={T}")
+
+
+def test_mxfp4_grouped_path_unsupported():
+    lay = dev_layer("gptoss_mx", **MX_SMALL[0])
+    x = xdev(case("gptoss_mx", 4, **MX_SMALL[0])[1])
+    with pytest.raises(moe_mod().MoeError) as ei:
+        moe_mod().forward(lay.with_path("grouped"), x)
+    assert ei.value.status == moe_mod().MOE_ERR_UNSUPPORTED
