@@ -40,6 +40,9 @@ WORKLOADS = {
     "qwen_prefill_t8192": ("qwen_zipf", 8192),
     "gptoss_t1": ("gptoss", 1),
     "gptoss_t4096": ("gptoss", 4096),
+    "gptoss_t64": ("gptoss", 64),
+    "gptoss_mx_t1": ("gptoss_mx", 1),
+    "gptoss_mx_t64": ("gptoss_mx", 64),
     "mixtral_t16": ("mixtral", 16),
     "mixtral_t16384": ("mixtral", 16384),
     "tiny_f32_t16": ("tiny_f32", 16),
@@ -171,12 +174,14 @@ def elem_bytes(L):
 
 
 def expert_weight_bytes(L):
-    """Bytes of one routed expert's parameters."""
+    """Bytes of one routed expert's parameters (MXFP4: 16 code bytes and one scale byte
+    per 32 weights)."""
     s, d, ff = elem_bytes(L), L["d"], L["ff"]
+    w = 3 * d * ff * 17 // 32 if L.get("expert_format") == "mxfp4" else 3 * d * ff * s
     if L["act"] == "swiglu":
-        return 3 * d * ff * s
+        return w
     b = 2 * ff * s + (d * s if L.get("b_down") is not None else 0)
-    return 3 * d * ff * s + b
+    return w + b
 
 
 def shared_bytes(L):

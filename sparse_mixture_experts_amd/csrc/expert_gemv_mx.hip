@@ -33,24 +33,40 @@ template <int B>
 __device__ __forceinline__ bf16x2_t fp4_pair_bf16(uint32_t cw, float scale) {
     return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, B);
 }
-// acc += the 8 products of code word cw (elements 8w .. 8w+7 of the block) with the bf16
-// activations xw holding the same elements.
-__device__ __forceinline__ float word_dot_bf16(uint32_t cw, float scale, const uint4& xw, float acc) {
-    acc = __builtin_amdgcn_fdot2_f32_bf16(fp4_pair_bf16<0>(cw, scale), __builtin_bit_cast(bf16x2_t, xw.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(fp4_pair_bf16<1>(cw, scale), __builtin_bit_cast(bf16x2_t, xw.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(fp4_pair_bf16<2>(cw, scale), __builtin_bit_cast(bf16x2_t, xw.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(fp4_pair_bf16<3>(cw, scale), __builtin_bit_cast(bf16x2_t, xw.w), acc, false);
-    return acc;
+// The same for NT activation rows at once: each converted pair serves every row.
+template <int NT>
+__device__ __forceinline__ void word_dot_bf16_rows(uint32_t cw, float scale, const uint4 (&xw)[NT], float (&acc)[NT]) {
+    const bf16x2_t p0 = fp4_pair_bf16<0>(cw, scale), p1 = fp4_pair_bf16<1>(cw, scale);
+    const bf16x2_t p2 = fp4_pair_bf16<2>(cw, scale), p3 = fp4_pair_bf16<3>(cw, scale);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        float a = acc[t];
+        a = __builtin_amdgcn_fdot2_f32_bf16(p0, __builtin_bit_cast(bf16x2_t, xw[t].x), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(p1, __builtin_bit_cast(bf16x2_t, xw[t].y), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(p2, __builtin_bit_cast(bf16x2_t, xw[t].z), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(p3, __builtin_bit_cast(bf16x2_t, xw[t].w), a, false);
+        acc[t] = a;
+    }
 }
 
-// acc += sum over the block's 32 elements of w * x, w the block (codes + scale), x the
-// 32 bf16 activations in four 16-byte pieces.
-__device__ __forceinline__ float block_dot_bf16(const uint4& codes, float scale, const uint4 (&xq)[4], float acc) {
-    acc = word_dot_bf16(codes.x, scale, xq[0], acc);
-    acc = word_dot_bf16(codes.y, scale, xq[1], acc);
-    acc = word_dot_bf16(codes.z, scale, xq[2], acc);
-    acc = word_dot_bf16(codes.w, scale, xq[3], acc);
-    return acc;
+// acc[t] += sum over the block's 32 elements of w * x_t for NT activation rows x_t (each
+// 32 bf16 in four 16-byte pieces): every FP4 pair is converted once for all rows.
+template <int NT>
+__device__ __forceinline__ void block_dot_bf16_rows(const uint4& codes, float scale, const uint4 (&xq)[NT][4],
+                                                    float (&acc)[NT]) {
+    uint4 xw[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xw[t] = xq[t][0];
+    word_dot_bf16_rows<NT>(codes.x, scale, xw, acc);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xw[t] = xq[t][1];
+    word_dot_bf16_rows<NT>(codes.y, scale, xw, acc);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xw[t] = xq[t][2];
+    word_dot_bf16_rows<NT>(codes.z, scale, xw, acc);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xw[t] = xq[t][3];
+    word_dot_bf16_rows<NT>(codes.w, scale, xw, acc);
 }
 
 constexpr int kMxUnits = 2;   // hidden units per up wave (4 interleaved rows)
@@ -58,6 +74,8 @@ constexpr int kMxUpNT = 2;    // group rows per up step
 constexpr int kMxDownNR = 4;  // output dims per down wave
 constexpr int kMxDownNT = 2;  // H rows per down step
 constexpr int kMxNB = 2;      // blocks per lane and row held at once (K up to 4096)
+
+__device__ const uint16_t kZeroBf16 = 0;
 
 struct MxArgs {
     const uint16_t* x;          // [T, d] bf16
@@ -75,23 +93,29 @@ struct MxArgs {
     float alpha, limit;
 };
 
-// Block i of this lane (block index lane + 64 i) of `rows` weight rows: codes and scale;
-// blocks past nblk read block 0 with zero codes (value +0).
+// Block i of this lane (block index lane + 64 i) of `rows` weight rows: codes and the raw
+// scale byte.  Nothing is done with them here, so that no wait for these loads comes
+// before the activation loads are issued; blocks past nblk read block 0 and are given a
+// zero scale where they are used (mx_scale).
 template <int NR, int NB>
 __device__ __forceinline__ void load_mx_rows(const uint8_t* const (&wrow)[NR], const uint8_t* const (&srow)[NR],
-                                             int nblk, uint4 (&codes)[NR][NB], float (&scale)[NR][NB]) {
+                                             int nblk, uint4 (&codes)[NR][NB], uint32_t (&sbyte)[NR][NB]) {
     const int lane = lane_id();
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         const int b = lane + kWave * i;
         const int bc = b < nblk ? b : 0;
-        const unsigned m = in_range_mask(b, nblk);
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            codes[r][i] = and_mask(ld16(wrow[r] + (size_t)bc * 16), m);
-            scale[r][i] = e8m0_scale(srow[r][bc]);
+            codes[r][i] = ld16(wrow[r] + (size_t)bc * 16);
+            sbyte[r][i] = srow[r][bc];
         }
     }
+}
+
+// The block's scale, or 0 for a block past the row (its codes were block 0's).
+__device__ __forceinline__ float mx_scale(uint32_t sbyte, int b, int nblk) {
+    return b < nblk ? e8m0_scale(sbyte) : 0.0f;
 }
 
 // One wave: hidden units f0, f0+1 of routed group g (interleaved rows 2f0 .. 2f0+3), every
@@ -113,39 +137,58 @@ __device__ __forceinline__ void mx_up_item(const MxArgs& a, const Group& g, int 
     }
     const uint8_t* const (&wc)[NR] = wrow;
     const uint8_t* const (&sc)[NR] = srow;
+    // Token of each row of a step (unconditional loads: perm_token always holds the group's
+    // rows; with one token the row is token 0).  The first step's are loaded before the
+    // weights: vector loads complete in issue order, so a token index loaded after the
+    // weights could only be used once the weights had arrived.
+    // Lane l loads the token of row tb + l % NT: a per-lane load keeps the value in a
+    // vector register, read out with readlane only where the activation addresses need it.
+    const int lane = lane_id();
+    auto step_tokens = [&](int tb) { return a.perm_token[g.row0 + min(tb + (lane & (NT - 1)), g.n - 1)]; };
+    const int tok0 = step_tokens(0);
+    __builtin_amdgcn_sched_barrier(0);
     uint4 codes[NR][NB];
-    float scale[NR][NB];
-    load_mx_rows<NR, NB>(wc, sc, nblk, codes, scale);
+    uint32_t sbyte[NR][NB];
+    load_mx_rows<NR, NB>(wc, sc, nblk, codes, sbyte);
     // After the reduction lane l holds value v = t * NR + r = l >> SH; the up row of gate
     // row r sits one value on, 1 << SH lanes higher in the same 16-lane row.
-    const int lane = lane_id();
     const int my_t = (lane >> SH) / NR, my_r = (lane >> SH) % NR;
     const int my_f = f0 + my_r / 2;
     const bool writer = (my_r & 1) == 0 && (lane & ((1 << SH) - 1)) == 0 && my_f < a.ff;
-    float bg = 0.f, bu = 0.f;
-    if (writer) {
-        const uint16_t* b = a.b_gate_up + (size_t)g.e * 2 * a.ff + 2 * my_f;
-        bg = bf16_to_f32(b[0]);
-        bu = bf16_to_f32(b[1]);
-    }
+    // Every lane loads a bias pair (branch-free, clamped): a load behind a branch would make
+    // the compiler wait for all loads in flight at the join.
+    const uint32_t bpair = *reinterpret_cast<const uint32_t*>(a.b_gate_up + (size_t)g.e * 2 * a.ff +
+                                                              2 * min(my_f, a.ff - 1));
     for (int tb = 0; tb < g.n; tb += NT) {
         const int nt = min(NT, g.n - tb);
         float acc[NR][NT] = {};
+        const int tok_v = tb == 0 ? tok0 : step_tokens(tb);
+        const uint16_t* xr[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const int rr = min(tb + t, g.n - 1);
-            const int tok = min(max(a.T == 1 ? 0 : a.perm_token[g.row0 + rr], 0), a.T - 1);
-            const uint16_t* xr = a.x + (size_t)tok * a.d;
+            const int tok = __builtin_amdgcn_readlane(tok_v, t);
+            xr[t] = a.x + (size_t)min(max(a.T == 1 ? 0 : tok, 0), a.T - 1) * a.d;
+        }
+        // All activation loads of the step first; then the codes pass an opaque asm, so
+        // that their conversion is neither hoisted out of the loop (which would wait for
+        // the weights before the first activation load and hold 4x the registers) nor
+        // moved above the activation loads.
+        uint4 xq[NB][NT][4];
 #pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const int b = lane + kWave * i;
-                const int bc = b < nblk ? b : 0;
-                uint4 xq[4];
+        for (int i = 0; i < NB; ++i) {
+            const int b = lane + kWave * i;
+            const int bc = b < nblk ? b : 0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) xq[q] = ld16(xr + (size_t)bc * 32 + q * 8);
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int r = 0; r < NR; ++r) acc[r][t] = block_dot_bf16(codes[r][i], scale[r][i], xq, acc[r][t]);
-            }
+                for (int q = 0; q < 4; ++q) xq[i][t][q] = ld16(xr[t] + (size_t)bc * 32 + q * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int b = lane + kWave * i;
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                block_dot_bf16_rows<NT>(opaque(codes[r][i]), mx_scale(sbyte[r][i], b, nblk), xq[i], acc[r]);
         }
         float v[N];
 #pragma unroll
@@ -156,8 +199,8 @@ __device__ __forceinline__ void mx_up_item(const MxArgs& a, const Group& g, int 
         const float up = __int_as_float(
             __builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x100 + (1 << SH), 0xF, 0xF, false));
         if (writer && my_t < nt) {
-            float gv = fminf(sum + bg, a.limit);
-            float uv = fminf(fmaxf(up + bu, -a.limit), a.limit);
+            float gv = fminf(sum + bf16_lo(bpair), a.limit);
+            float uv = fminf(fmaxf(up + bf16_hi(bpair), -a.limit), a.limit);
             a.H[(size_t)(g.row0 + tb + my_t) * a.hstride + my_f] =
                 f32_to_bf16((uv + 1.0f) * gv * sigmoidf_(a.alpha * gv));
         }
@@ -181,29 +224,38 @@ __device__ __forceinline__ void mx_down_item(const MxArgs& a, const Group& g, in
     const uint8_t* const (&wc)[NR] = wrow;
     const uint8_t* const (&sc)[NR] = srow;
     uint4 codes[NR][NB];
-    float scale[NR][NB];
-    load_mx_rows<NR, NB>(wc, sc, nblk, codes, scale);
+    uint32_t sbyte[NR][NB];
+    load_mx_rows<NR, NB>(wc, sc, nblk, codes, sbyte);
     // After the reduction lane l holds value v = t * NR + r = l >> SH.
     const int lane = lane_id();
     const int my_t = (lane >> SH) / NR, my_i = i0 + (lane >> SH) % NR;
     const bool writer = (lane & ((1 << SH) - 1)) == 0 && my_i < a.d;
-    const float bias = (writer && a.b_down) ? bf16_to_f32(a.b_down[(size_t)g.e * a.d + my_i]) : 0.0f;
+    // Branch-free bias load (see mx_up_item); a layer without down bias reads a zero.
+    const uint16_t* bd = a.b_down ? a.b_down + (size_t)g.e * a.d + min(my_i, a.d - 1) : &kZeroBf16;
+    const float bias = bf16_to_f32(*bd);
     for (int tb = 0; tb < g.n; tb += NT) {
         const int nt = min(NT, g.n - tb);
         float acc[NR][NT] = {};
+        const uint16_t* hr[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const uint16_t* hr = a.H + (size_t)(g.row0 + min(tb + t, g.n - 1)) * a.hstride;
+        for (int t = 0; t < NT; ++t) hr[t] = a.H + (size_t)(g.row0 + min(tb + t, g.n - 1)) * a.hstride;
+        // As in mx_up_item: the step's H loads first, then the codes through an opaque asm.
+        uint4 hq[NB][NT][4];
 #pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const int b = lane + kWave * i;
-                const int bc = b < nblk ? b : 0;
-                uint4 hq[4];
+        for (int i = 0; i < NB; ++i) {
+            const int b = lane + kWave * i;
+            const int bc = b < nblk ? b : 0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) hq[q] = ld16(hr + (size_t)bc * 32 + q * 8);
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int r = 0; r < NR; ++r) acc[r][t] = block_dot_bf16(codes[r][i], scale[r][i], hq, acc[r][t]);
-            }
+                for (int q = 0; q < 4; ++q) hq[i][t][q] = ld16(hr[t] + (size_t)bc * 32 + q * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int b = lane + kWave * i;
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                block_dot_bf16_rows<NT>(opaque(codes[r][i]), mx_scale(sbyte[r][i], b, nblk), hq[i], acc[r]);
         }
         float v[N];
 #pragma unroll
