@@ -20,21 +20,22 @@
 namespace smoe {
 namespace {
 
-template <int KB, typename TT, bool OAI, bool RESIDENT, int U, bool EXACT>
+// NT: group rows per step (1 for one token: every group then has one row).
+template <int KB, typename TT, bool OAI, bool RESIDENT, int U, bool EXACT, int NT>
 __global__ __launch_bounds__(256) void expert_up_gemv_kernel(GemvUp a, const PlanMeta* meta) {
     Group g;
     if (!gemv_group(a.groups, meta, a.ffs > 0, a.T, a.tk, g)) return;
     const int ffg = g.e < 0 ? a.ffs : a.ff;
     const int f0 = (blockIdx.x * 4 + wave_id()) * U;
-    if (f0 < ffg) up_item<KB, TT, OAI, RESIDENT, U, EXACT>(a, g, f0);
+    if (f0 < ffg) up_item<KB, TT, OAI, RESIDENT, U, EXACT, NT>(a, g, f0);
 }
 
-template <int KB, typename TT, bool OAI, bool RESIDENT, int NR, bool EXACT>
+template <int KB, typename TT, bool OAI, bool RESIDENT, int NR, bool EXACT, int NT>
 __global__ __launch_bounds__(256) void expert_down_gemv_kernel(GemvDown a, const PlanMeta* meta) {
     Group g;
     if (!gemv_group(a.groups, meta, a.ffs > 0, a.T, a.tk, g)) return;
     const int i0 = (blockIdx.x * 4 + wave_id()) * NR;
-    if (i0 < a.d) down_item<KB, TT, OAI, RESIDENT, NR, down_step_rows<NR>(), EXACT>(a, g, i0);
+    if (i0 < a.d) down_item<KB, TT, OAI, RESIDENT, NR, NT, EXACT>(a, g, i0);
 }
 
 // One token: routing and the up projection in one kernel.  Grid row 0 (with a shared
@@ -66,7 +67,8 @@ __global__ __launch_bounds__(256) void token1_up_kernel(GemvUp a, const float* _
         g = Group{min(max(e, 0), E - 1), j, 1, 0};
     }
     const int ffg = g.e < 0 ? a.ffs : a.ff;
-    if (f0 < ffg) up_item<KB, TT, OAI, RESIDENT, U, EXACT>(a, g, f0);
+    // Every group holds the one token: one row per step.
+    if (f0 < ffg) up_item<KB, TT, OAI, RESIDENT, U, EXACT, 1>(a, g, f0);
 }
 
 // A few tokens: the down projection of every pick and of the shared expert, and the
@@ -155,11 +157,22 @@ hipError_t launch_up_t(const moe_layer& L, const void* x, int T, const int32_t* 
              L.ws_gate, L.ws_up, H, hstride, T, T * L.k, L.d, L.ff, L.shared_ff, L.oai_alpha, L.oai_limit};
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
     const bool up_res = chunks(L.d, TT::VEC) <= 8;
-    const dim3 gu((ffmax + 4 * kUpUnits - 1) / (4 * kUpUnits), gmax);
-    // Rows longer than one 8-chunk batch stream in batches of 4 chunks per lane.
-    switch (up_res ? pick_kb(L.d, TT::VEC) : 4) {
-#define SMOE_UP_LAUNCH(KB, RES, EX) \
-    expert_up_gemv_kernel<KB, TT, OAI, RES, kUpUnits, EX><<<gu, 256, 0, s>>>(u, meta)
+    // Rows longer than one 8-chunk batch stream in batches of 4 chunks per lane.  One
+    // token: one row per step, and one hidden unit per wave for rows of 8 chunks per lane
+    // (the resident weights are used once, so fewer registers buy more waves).
+    const int kb = up_res ? pick_kb(L.d, TT::VEC) : 4;
+    const bool one = T == 1;
+    const int units = one && kb == 8 ? 1 : kUpUnits;
+    const dim3 gu((ffmax + 4 * units - 1) / (4 * units), gmax);
+    switch (kb) {
+#define SMOE_UP_LAUNCH(KB, RES, EX)                                                            \
+    do {                                                                                       \
+        if (one)                                                                               \
+            expert_up_gemv_kernel<KB, TT, OAI, RES, KB == 8 ? 1 : kUpUnits, EX, 1>             \
+                <<<gu, 256, 0, s>>>(u, meta);                                                  \
+        else                                                                                   \
+            expert_up_gemv_kernel<KB, TT, OAI, RES, kUpUnits, EX, kNT><<<gu, 256, 0, s>>>(u, meta); \
+    } while (0)
 #define SMOE_UP_CASE(KB)                                                                       \
     case KB:                                                                                   \
         if (exact_k(L.d, TT::VEC, KB)) {                                                       \
@@ -198,8 +211,14 @@ hipError_t launch_down_t(const moe_layer& L, int T, const Group* groups, const P
     };
     switch (dn_res ? pick_kb(ffmax, TT::VEC) : 4) {
 #define SMOE_DOWN_LAUNCH(KB, NR, RES, EX)                                                      \
-    expert_down_gemv_kernel<KB, TT, OAI, RES, NR, EX>                                          \
-        <<<dim3((L.d + 4 * (NR) - 1) / (4 * (NR)), gmax), 256, 0, s>>>(dn, meta)
+    do {                                                                                       \
+        const dim3 gd((L.d + 4 * (NR) - 1) / (4 * (NR)), gmax);                               \
+        if (T == 1)                                                                            \
+            expert_down_gemv_kernel<KB, TT, OAI, RES, NR, EX, 1><<<gd, 256, 0, s>>>(dn, meta);   \
+        else                                                                                   \
+            expert_down_gemv_kernel<KB, TT, OAI, RES, NR, EX, down_step_rows<NR>()>            \
+                <<<gd, 256, 0, s>>>(dn, meta);                                                 \
+    } while (0)
 #define SMOE_DOWN_NR(KB, NR)                                                                   \
     if (dn_exact(KB)) {                                                                        \
         if (dn_res) SMOE_DOWN_LAUNCH(KB, NR, true, true);                                      \
@@ -236,10 +255,14 @@ hipError_t launch_token1_up_t(const moe_layer& L, const void* x, const float* lo
              L.ws_gate, L.ws_up, H, hstride, 1, L.k, L.d, L.ff, L.shared_ff, L.oai_alpha, L.oai_limit};
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
     const bool up_res = chunks(L.d, TT::VEC) <= 8;
-    const dim3 gu((ffmax + 4 * kUpUnits - 1) / (4 * kUpUnits), L.k + (shared ? 1 : 0));
-    switch (up_res ? pick_kb(L.d, TT::VEC) : 4) {
+    // One token gives the resident weights no reuse: rows of 8 chunks per lane take one
+    // hidden unit per wave (64 weight registers) for more waves in flight.
+    const int kb = up_res ? pick_kb(L.d, TT::VEC) : 4;
+    const int units = kb == 8 ? 1 : kUpUnits;
+    const dim3 gu((ffmax + 4 * units - 1) / (4 * units), L.k + (shared ? 1 : 0));
+    switch (kb) {
 #define SMOE_UP_LAUNCH(KB, RES, EX)                                                              \
-    token1_up_kernel<KB, TT, OAI, RES, kUpUnits, EX>                                             \
+    token1_up_kernel<KB, TT, OAI, RES, KB == 8 ? 1 : kUpUnits, EX>                               \
         <<<gu, 256, 0, s>>>(u, logits, L.n_expert, L.k, L.route, L.route_scale, idx, w)
 #define SMOE_UP_CASE(KB)                                                                       \
     case KB:                                                                                   \

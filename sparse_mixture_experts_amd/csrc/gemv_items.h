@@ -71,7 +71,18 @@ __device__ __forceinline__ bool gemv_group(const Group* groups, const PlanMeta* 
 // One wave: hidden units f0 .. f0+U-1 of group g (those below the group's hidden width),
 // for every row of the group.  RESIDENT: the whole K axis fits one KB-chunk register
 // batch, so the 2U weight rows are streamed once and every row is served from registers.
-template <int KB, typename TT, bool OAI, bool RESIDENT, int U, bool EXACT>
+// v of the lane SHIFT lanes higher: a DPP row shift inside 16-lane rows (lanes whose
+// source lies outside their row get 0; callers only use lanes whose source is inside),
+// a bpermute for shifts of a whole row or more.
+template <int SHIFT>
+__device__ __forceinline__ float lanes_down(float v) {
+    if constexpr (SHIFT < 16)
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + SHIFT, 0xF, 0xF, false));
+    else
+        return __shfl_down(v, SHIFT, kWave);
+}
+
+template <int KB, typename TT, bool OAI, bool RESIDENT, int U, bool EXACT, int NT = kNT>
 __device__ __forceinline__ void up_item(const GemvUp& a, const Group& g, int f0) {
     using S = typename TT::storage;
     constexpr int NR = 2 * U;
@@ -97,14 +108,13 @@ __device__ __forceinline__ void up_item(const GemvUp& a, const Group& g, int f0)
         }
     }
     const S* const (&wrc)[NR] = wr;
-    // After the reduction lane l holds value (t * NR + r) = l >> SH: token t = l >> 4 (one
-    // 16-lane row per token), weight row r = (l >> SH) % NR.  The up row matching a gate
-    // row sits U values on (two matrices) or 1 value on (interleaved): fetched by a DPP
-    // row shift of (U << SH) or (1 << SH) lanes.
-    constexpr int N = NR * kNT;
+    // After the reduction lane l holds value (t * NR + r) = l >> SH: row t of the step,
+    // weight row r = (l >> SH) % NR.  The up row matching a gate row sits U values on (two
+    // matrices) or 1 value on (interleaved), (U << SH) or (1 << SH) lanes higher.
+    constexpr int N = NR * NT;
     constexpr int SH = 6 - ilog2(N);
     const int lane = lane_id();
-    const int my_t = lane >> 4, my_r = (lane >> SH) % NR;
+    const int my_t = (lane >> SH) / NR, my_r = (lane >> SH) % NR;
     const bool gate_lane = oai ? (my_r & 1) == 0 : my_r < U;
     const int my_f = oai ? my_r / 2 : my_r;  // unit offset of a gate lane
     const bool writer = gate_lane && (lane & ((1 << SH) - 1)) == 0 && f0 + my_f < ffg;
@@ -120,33 +130,31 @@ __device__ __forceinline__ void up_item(const GemvUp& a, const Group& g, int f0)
         }
     }
     const S* x = static_cast<const S*>(a.x);
-    // Token of row tb + (lane % kNT), one vector load per step, issued before the weight
+    // Token of row tb + (lane % NT), one vector load per step, issued before the weight
     // loads so that waiting for it does not wait for them.
     auto step_tokens = [&](int tb) {
-        const int r = min(tb + (lane & (kNT - 1)), g.n - 1);
+        const int r = min(tb + (lane & (NT - 1)), g.n - 1);
         // Shared rows are the tokens in order; with one token every row is token 0.
         const int tok = (shared || a.T == 1) ? r : a.perm_token[g.row0 + r];
         return min(max(tok, 0), a.T - 1);
     };
     auto step = [&](int tb, int tok_v, const uint4 (&wv)[RESIDENT ? KB : 1][NR]) {
-        const int nt = min(kNT, g.n - tb);
-        const S* ar[kNT];
+        const int nt = min(NT, g.n - tb);
+        const S* ar[NT];
 #pragma unroll
-        for (int t = 0; t < kNT; ++t) ar[t] = x + (size_t)__builtin_amdgcn_readlane(tok_v, t) * d;
-        const S* const (&arc)[kNT] = ar;
-        float acc[NR][kNT] = {};
-        if constexpr (RESIDENT) dot_w_batch<NR, kNT, KB, TT, TT, EXACT>(wv, arc, nt, a.d, 0, acc);
-        else rows_dot<NR, kNT, KB, TT, TT, true, EXACT>(wrc, arc, nt, a.d, acc);
+        for (int t = 0; t < NT; ++t) ar[t] = x + (size_t)__builtin_amdgcn_readlane(tok_v, t) * d;
+        const S* const (&arc)[NT] = ar;
+        float acc[NR][NT] = {};
+        if constexpr (RESIDENT) dot_w_batch<NR, NT, KB, TT, TT, EXACT>(wv, arc, nt, a.d, 0, acc);
+        else rows_dot<NR, NT, KB, TT, TT, true, EXACT>(wrc, arc, nt, a.d, acc);
         float v[N];
 #pragma unroll
-        for (int t = 0; t < kNT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < NR; ++r) v[t * NR + r] = acc[r][t];
         const float sum = wave_reduce_scatter<N>(v);
-        const float up_two = __int_as_float(
-            __builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x100 + (U << SH), 0xF, 0xF, false));
-        const float up_one = __int_as_float(
-            __builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x100 + (1 << SH), 0xF, 0xF, false));
+        const float up_two = lanes_down<(U << SH)>(sum);
+        const float up_one = lanes_down<(1 << SH)>(sum);
         float h;
         if (oai) {
             float gv = sum + bg;
@@ -166,7 +174,7 @@ __device__ __forceinline__ void up_item(const GemvUp& a, const Group& g, int f0)
     if constexpr (RESIDENT) load_w_batch<NR, KB, TT, true, EXACT>(wrc, a.d, 0, wv);
     __builtin_amdgcn_sched_barrier(0);  // the token's readlanes stay behind the weight loads
     step(0, tok0, wv);
-    for (int tb = kNT; tb < g.n; tb += kNT) step(tb, step_tokens(tb), wv);
+    for (int tb = NT; tb < g.n; tb += NT) step(tb, step_tokens(tb), wv);
 }
 
 // Hidden units per up-projection wave.  Four units (8 weight rows, x re-read half as
