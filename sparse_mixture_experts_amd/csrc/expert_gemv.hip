@@ -159,7 +159,9 @@ hipError_t launch_up_t(const moe_layer& L, const void* x, int T, const int32_t* 
     const bool up_res = chunks(L.d, TT::VEC) <= 8;
     // Rows longer than one 8-chunk batch stream in batches of 4 chunks per lane.  One
     // token: one row per step, and one hidden unit per wave for rows of 8 chunks per lane
-    // (the resident weights are used once, so fewer registers buy more waves).
+    // (the resident weights are used once, so fewer registers buy more waves).  Decode
+    // batches (groups of a row or two): two rows per step, which measured faster than
+    // four at 8 and 64 tokens (fewer registers, no duplicated rows); larger batches four.
     const int kb = up_res ? pick_kb(L.d, TT::VEC) : 4;
     const bool one = T == 1;
     const int units = one && kb == 8 ? 1 : kUpUnits;
@@ -170,6 +172,8 @@ hipError_t launch_up_t(const moe_layer& L, const void* x, int T, const int32_t* 
         if (one)                                                                               \
             expert_up_gemv_kernel<KB, TT, OAI, RES, KB == 8 ? 1 : kUpUnits, EX, 1>             \
                 <<<gu, 256, 0, s>>>(u, meta);                                                  \
+        else if (T <= 64)                                                                      \
+            expert_up_gemv_kernel<KB, TT, OAI, RES, kUpUnits, EX, 2><<<gu, 256, 0, s>>>(u, meta); \
         else                                                                                   \
             expert_up_gemv_kernel<KB, TT, OAI, RES, kUpUnits, EX, kNT><<<gu, 256, 0, s>>>(u, meta); \
     } while (0)
