@@ -227,15 +227,16 @@ __device__ __forceinline__ void down_item(const GemvDown& a, const Group& g, int
     }
 }
 
-// Output rows per down-projection wave for "wide" launches: 16 when the K axis is one
-// register chunk per lane, fewer for longer axes so that the weight batch stays at 64
-// registers or below.  Launches over very few groups use 4 rows per wave instead, for
-// more waves in flight.
+// Output rows per down-projection wave for "wide" launches: 8 (a K axis of one or two
+// register chunks per lane; 16 and 4 measured slower at 64 decode tokens), 4 for longer
+// axes so that the weight batch stays at 64 registers or below.  Launches over very few
+// groups use 4 rows per wave instead, for more waves in flight.
 template <int KB>
-constexpr int down_rows_wide() { return KB == 1 ? 16 : KB == 2 ? 8 : 4; }
+constexpr int down_rows_wide() { return KB <= 2 ? 8 : 4; }
 
-// H rows per down-projection step: 2 beside 16 weight rows (register budget), else 4.
+// H rows per down-projection step: 2 beside 8 or more weight rows (decode groups hold a
+// row or two; fewer registers), else 4.
 template <int NR>
-constexpr int down_step_rows() { return NR >= 16 ? 2 : kNT; }
+constexpr int down_step_rows() { return NR >= 8 ? 2 : kNT; }
 
 }  // namespace smoe
