@@ -20,11 +20,17 @@
 namespace smoe {
 namespace {
 
-// NT: group rows per step (1 for one token: every group then has one row).
-template <int KB, typename TT, bool OAI, bool RESIDENT, int U, bool EXACT, int NT>
-__global__ __launch_bounds__(256) void expert_up_gemv_kernel(GemvUp a, const PlanMeta* meta) {
+// NT: group rows per step (1 for one token: every group then has one row).  PLAN: the
+// wave finds its group from the expert offsets and the kernel writes the list for the down
+// kernel (used for one token, where a separate planning launch costs more than the scan).
+template <int KB, typename TT, bool OAI, bool RESIDENT, int U, bool EXACT, int NT, bool PLAN = false>
+__global__ __launch_bounds__(256) void expert_up_gemv_kernel(GemvUp a, const PlanMeta* meta, GemvPlan plan) {
     Group g;
-    if (!gemv_group(a.groups, meta, a.ffs > 0, a.T, a.tk, g)) return;
+    if constexpr (PLAN) {
+        if (!plan_group(plan, a.ffs > 0, a.T, a.tk, g)) return;
+    } else {
+        if (!gemv_group(a.groups, meta, a.ffs > 0, a.T, a.tk, g)) return;
+    }
     const int ffg = g.e < 0 ? a.ffs : a.ff;
     const int f0 = (blockIdx.x * 4 + wave_id()) * U;
     if (f0 < ffg) up_item<KB, TT, OAI, RESIDENT, U, EXACT, NT>(a, g, f0);
@@ -150,7 +156,8 @@ __global__ __launch_bounds__(kToken1MaxWaves * kWave) void token1_down_combine_k
 
 template <typename TT, bool OAI>
 hipError_t launch_up_t(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
-                       const Group* groups, const PlanMeta* meta, float* H, int hstride, hipStream_t s) {
+                       const Group* groups, const PlanMeta* meta, float* H, int hstride, const GemvPlan& plan,
+                       hipStream_t s) {
     const bool shared = L.shared_ff > 0;
     const int gmax = max_groups(L.n_expert, T, L.k, shared);
     GemvUp u{x, perm_token, groups, L.w_gate, L.w_up, L.w_gate_up, L.b_gate_up,
@@ -164,18 +171,22 @@ hipError_t launch_up_t(const moe_layer& L, const void* x, int T, const int32_t* 
     // four at 8 and 64 tokens (fewer registers, no duplicated rows); larger batches four.
     const int kb = up_res ? pick_kb(L.d, TT::VEC) : 4;
     const bool one = T == 1;
+    if (plan.offsets && !one) return hipErrorInvalidValue;  // the in-kernel list is for one token
     const int units = one && kb == 8 ? 1 : kUpUnits;
     const dim3 gu((ffmax + 4 * units - 1) / (4 * units), gmax);
     switch (kb) {
 #define SMOE_UP_LAUNCH(KB, RES, EX)                                                            \
     do {                                                                                       \
-        if (one)                                                                               \
+        if (one && plan.offsets)                                                               \
+            expert_up_gemv_kernel<KB, TT, OAI, RES, KB == 8 ? 1 : kUpUnits, EX, 1, true>       \
+                <<<gu, 256, 0, s>>>(u, meta, plan);                                            \
+        else if (one)                                                                          \
             expert_up_gemv_kernel<KB, TT, OAI, RES, KB == 8 ? 1 : kUpUnits, EX, 1>             \
-                <<<gu, 256, 0, s>>>(u, meta);                                                  \
+                <<<gu, 256, 0, s>>>(u, meta, plan);                                            \
         else if (T <= 64)                                                                      \
-            expert_up_gemv_kernel<KB, TT, OAI, RES, kUpUnits, EX, 2><<<gu, 256, 0, s>>>(u, meta); \
+            expert_up_gemv_kernel<KB, TT, OAI, RES, kUpUnits, EX, 2><<<gu, 256, 0, s>>>(u, meta, plan); \
         else                                                                                   \
-            expert_up_gemv_kernel<KB, TT, OAI, RES, kUpUnits, EX, kNT><<<gu, 256, 0, s>>>(u, meta); \
+            expert_up_gemv_kernel<KB, TT, OAI, RES, kUpUnits, EX, kNT><<<gu, 256, 0, s>>>(u, meta, plan); \
     } while (0)
 #define SMOE_UP_CASE(KB)                                                                       \
     case KB:                                                                                   \
@@ -324,13 +335,22 @@ hipError_t launch_token1_t(const moe_layer& L, int T, const float* H, int hstrid
 }  // namespace
 
 hipError_t launch_expert_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
-                              const Group* groups, const PlanMeta* meta, float* H, int hstride,
-                              float* y_perm, hipStream_t s) {
-    if (L.expert_format == MOE_EXPERTS_MXFP4)
+                              Group* groups, PlanMeta* meta, float* H, int hstride, float* y_perm,
+                              const int32_t* plan_offsets, hipStream_t s) {
+    if (L.expert_format == MOE_EXPERTS_MXFP4) {
+        if (plan_offsets) return hipErrorInvalidValue;
         return launch_expert_gemv_mx(L, x, T, perm_token, groups, meta, H, hstride, y_perm, s);
-    const hipError_t e = launch_expert_up_gemv(L, x, T, perm_token, groups, meta, H, hstride, s);
-    if (e != hipSuccess) return e;
+    }
+    const GemvPlan plan{plan_offsets, L.n_expert, groups, meta};
     const bool oai = L.act == MOE_ACT_SWIGLU_OAI;
+    hipError_t e;
+    if (L.dtype == MOE_BF16)
+        e = oai ? launch_up_t<BF16, true>(L, x, T, perm_token, groups, meta, H, hstride, plan, s)
+                : launch_up_t<BF16, false>(L, x, T, perm_token, groups, meta, H, hstride, plan, s);
+    else
+        e = oai ? launch_up_t<F32, true>(L, x, T, perm_token, groups, meta, H, hstride, plan, s)
+                : launch_up_t<F32, false>(L, x, T, perm_token, groups, meta, H, hstride, plan, s);
+    if (e != hipSuccess) return e;
     if (L.dtype == MOE_BF16)
         return oai ? launch_down_t<BF16, true>(L, T, groups, meta, H, hstride, y_perm, s)
                    : launch_down_t<BF16, false>(L, T, groups, meta, H, hstride, y_perm, s);
@@ -341,12 +361,13 @@ hipError_t launch_expert_gemv(const moe_layer& L, const void* x, int T, const in
 hipError_t launch_expert_up_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                                  const Group* groups, const PlanMeta* meta, float* H, int hstride,
                                  hipStream_t s) {
+    const GemvPlan plan{nullptr, L.n_expert, nullptr, nullptr};
     const bool oai = L.act == MOE_ACT_SWIGLU_OAI;
     if (L.dtype == MOE_BF16)
-        return oai ? launch_up_t<BF16, true>(L, x, T, perm_token, groups, meta, H, hstride, s)
-                   : launch_up_t<BF16, false>(L, x, T, perm_token, groups, meta, H, hstride, s);
-    return oai ? launch_up_t<F32, true>(L, x, T, perm_token, groups, meta, H, hstride, s)
-               : launch_up_t<F32, false>(L, x, T, perm_token, groups, meta, H, hstride, s);
+        return oai ? launch_up_t<BF16, true>(L, x, T, perm_token, groups, meta, H, hstride, plan, s)
+                   : launch_up_t<BF16, false>(L, x, T, perm_token, groups, meta, H, hstride, plan, s);
+    return oai ? launch_up_t<F32, true>(L, x, T, perm_token, groups, meta, H, hstride, plan, s)
+               : launch_up_t<F32, false>(L, x, T, perm_token, groups, meta, H, hstride, plan, s);
 }
 
 hipError_t launch_token1_up(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,

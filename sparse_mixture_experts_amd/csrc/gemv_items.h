@@ -71,6 +71,90 @@ __device__ __forceinline__ bool gemv_group(const Group* groups, const PlanMeta* 
 // One wave: hidden units f0 .. f0+U-1 of group g (those below the group's hidden width),
 // for every row of the group.  RESIDENT: the whole K axis fits one KB-chunk register
 // batch, so the 2U weight rows are streamed once and every row is served from registers.
+// The group list built inside the up kernel instead of by a separate planning launch
+// (expert offsets from the caller): where the offsets are, and where the list and its
+// count go for the down kernel.
+struct GemvPlan {
+    const int32_t* offsets;  // [E + 1], or null: the list is already built
+    int E;
+    Group* groups;
+    PlanMeta* meta;
+};
+
+// Routed group gi of the expert offsets, found by one wave: the gi-th expert (ascending
+// id) with rows, its rows clamped to 0 .. tk the same way as the planning kernel does.
+// Lane l scans experts l*epl .. l*epl+epl-1 (epl = ceil(E / 64) <= 8); a wave prefix sum
+// of the per-lane counts names the lane that holds group gi.  Returns the number of
+// routed groups; g is set when gi is below it.  gi must be wave-uniform.
+__device__ __forceinline__ int offsets_group(const int32_t* __restrict__ offsets, int E, int tk, int gi,
+                                             Group& g) {
+    const int epl = (E + kWave - 1) / kWave;
+    const int e0 = lane_id() * epl;
+    int o[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) o[i] = offsets[min(e0 + i, E)];
+    const auto rows_of = [&](int i, int& r0, int& n) {
+        r0 = min(max(o[i], 0), tk);
+        n = (i < epl && e0 + i < E) ? min(max(o[i + 1] - r0, 0), tk - r0) : 0;
+    };
+    unsigned flags = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int r0, n;
+        rows_of(i, r0, n);
+        flags |= (n > 0 ? 1u : 0u) << i;
+    }
+    const int cnt = __popc(flags);
+    const int incl = wave_inclusive_sum(cnt);
+    const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+    const int excl = incl - cnt;
+    const unsigned long long holder = __ballot(gi >= excl && gi < incl);
+    if (holder == 0ull) return total;
+    const int src = __ffsll((long long)holder) - 1;
+    int t = gi - excl, pe = 0, pr = 0, pn = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int r0, n;
+        rows_of(i, r0, n);
+        if ((flags >> i) & 1u) {
+            if (t == 0) {
+                pe = e0 + i;
+                pr = r0;
+                pn = n;
+            }
+            --t;
+        }
+    }
+    g = Group{__builtin_amdgcn_readlane(pe, src), __builtin_amdgcn_readlane(pr, src),
+              __builtin_amdgcn_readlane(pn, src), 0};
+    return total;
+}
+
+// gemv_group for a kernel that builds the list itself from p.offsets (same grid-row
+// order).  Thread 0 of block 0 of each grid row records its routed group, and grid row 0
+// the shared group and the count, for the down kernel that follows.
+__device__ __forceinline__ bool plan_group(const GemvPlan& p, bool has_shared, int T, int tk, Group& g) {
+    const int y = blockIdx.y;
+    const int gi = has_shared ? max(y - 1, 0) : y;
+    Group cand{0, 0, 0, 0};
+    const int n_routed = offsets_group(p.offsets, p.E, tk, gi, cand);
+    const bool shared_row = has_shared && y == 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (y == 0) {
+            *p.meta = PlanMeta{n_routed + (has_shared ? 1 : 0), 0, 0, 0};
+            if (has_shared) p.groups[n_routed] = Group{-1, tk, T, 0};
+        }
+        if (!shared_row && gi < n_routed) p.groups[gi] = cand;
+    }
+    if (shared_row) {
+        g = Group{-1, tk, T, 0};
+        return true;
+    }
+    if (gi >= n_routed) return false;
+    g = cand;
+    return true;
+}
+
 // v of the lane SHIFT lanes higher: a DPP row shift inside 16-lane rows (lanes whose
 // source lies outside their row get 0; callers only use lanes whose source is inside),
 // a bpermute for shifts of a whole row or more.

@@ -74,9 +74,12 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
 // Combine of pre-weighted bf16 rows: y[t] = sum_j Y[perm_inv[t,j]] (+ Y[T*k + t]).
 hipError_t launch_combine_sum(const moe_layer& L, const uint16_t* y_rows, const int32_t* perm_inv,
                               int T, const void* residual, void* y, hipStream_t s);
+// Decode GEMVs (up then down; fp32 H and unweighted fp32 rows).  With plan_offsets (the
+// expert offsets; dense experts and one token only) the up kernel builds the group list
+// and count into groups / meta itself, so no planning launch has to come first.
 hipError_t launch_expert_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
-                              const Group* groups, const PlanMeta* meta, float* H, int hstride,
-                              float* y_perm, hipStream_t s);
+                              Group* groups, PlanMeta* meta, float* H, int hstride, float* y_perm,
+                              const int32_t* plan_offsets, hipStream_t s);
 // GEMVs over MXFP4 expert weights (up then down; H in bf16 in the fp32 H region;
 // unweighted fp32 rows), for layers with MOE_EXPERTS_MXFP4; mx_fits: the widths the
 // kernels take (K <= 4096).

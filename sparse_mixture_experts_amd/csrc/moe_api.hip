@@ -151,15 +151,20 @@ moe_status run_experts(const moe_layer& L, const void* x, int T, const int32_t* 
     Group* groups = at<Group>(ws, o.groups);
     PlanMeta* meta = at<PlanMeta>(ws, o.meta);
     TileDesc* tiles = at<TileDesc>(ws, o.tiles);
-    if (!planned)
+    const bool grouped = use_grouped(L, T);
+    // One token on the dense GEMVs: the up kernel finds its groups from the offsets itself
+    // (a planning launch costs more than that scan there; at more tokens the scan in front
+    // of every wave's loads costs more than the launch).
+    const bool plan_in_up = !planned && !grouped && T == 1 && L.expert_format == MOE_EXPERTS_DENSE;
+    if (!planned && !plan_in_up)
         SMOE_TRY(launch_plan(offsets, L.n_expert, T, L.k, L.shared_ff > 0, kTileM, groups, meta,
                              tiles, s));
-    if (use_grouped(L, T)) {
+    if (grouped) {
         SMOE_TRY(launch_grouped_ffn(L, x, T, perm_token, groups, meta, tiles, at<uint16_t>(ws, o.H),
                                     o.hstride, row_w, y_rows, y_bf16, s));
     } else {
         SMOE_TRY(launch_expert_gemv(L, x, T, perm_token, groups, meta, at<float>(ws, o.H), o.hstride,
-                                    static_cast<float*>(y_rows), s));
+                                    static_cast<float*>(y_rows), plan_in_up ? offsets : nullptr, s));
     }
     return MOE_OK;
 }

@@ -131,6 +131,24 @@ def test_expert_ffn(c, path):
     assert_close(y.cpu().numpy(), ref, L["dtype"], "y_perm")
 
 
+@pytest.mark.parametrize("E,T", [(100, 1), (512, 1), (512, 40)])
+def test_expert_ffn_expert_counts(E, T):
+    # At one token the decode up GEMV finds each group from the expert offsets itself, one
+    # wave scanning ceil(E / 64) experts per lane: a partial last lane (E = 100) and eight
+    # experts per lane (the largest E), with most experts empty.  T = 40 takes the list
+    # from the planning kernel.
+    ov = dict(d=256, n_expert=E, ff=64, shared_ff=64)
+    say("expert_ffn expert counts", ov, T)
+    L, x = case("qwen", T, **ov)
+    lay = dev_layer("qwen", path="decode", **ov)
+    ridx, _, _ = oracle.route(L, x)
+    _, roff, rpt, _ = oracle.permute(ridx, L["n_expert"])
+    y = moe_mod().expert_ffn(lay, xdev(x), torch.from_numpy(roff.astype(np.int32)).cuda(),
+                             torch.from_numpy(rpt.astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy(), oracle.expert_rows(L, x, roff, rpt), L["dtype"], "y_perm")
+
+
 @pytest.mark.parametrize("c", SMALL_CASES, ids=_id)
 def test_combine_fed_oracle_rows(c):
     name, ov, T = c
