@@ -12,7 +12,10 @@ namespace {
 constexpr int kMaxExperts = 512;
 constexpr int kMaxK = 32;
 constexpr int32_t kMaxTokens = 1 << 22;
-constexpr int kDecodeMaxT = 64;  // MOE_PATH_AUTO takes the GEMV path up to this T
+constexpr int kDecodeMaxT = 64;  // MOE_PATH_AUTO takes the grouped path above this T
+// ... and at or below it when the expected rows per active expert reach this many: the
+// GEMVs' per-row arithmetic then outgrows their weight stream, MFMA tiles do not.
+constexpr double kGroupedMinRows = 4.0;
 constexpr int kTileM = kGroupTileM;  // M-tile size recorded in the group plan
 // Largest batch whose down projection runs per token, fused with the combine.
 constexpr int kTokenDownMaxT = 8;
@@ -122,10 +125,16 @@ inline moe_status status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MO
     } while (0)
 
 // The grouped MFMA path (bf16, dense experts) or the decode GEMV path.
+// Expected number of distinct experts that T tokens select, k each, if every expert were
+// equally likely: E * (1 - (1 - k/E)^T).
+double expected_active(int E, int k, int T) { return E * (1.0 - pow(1.0 - (double)k / E, (double)T)); }
+
 bool use_grouped(const moe_layer& L, int T) {
     if (L.dtype != MOE_BF16 || L.expert_format != MOE_EXPERTS_DENSE) return false;
     if (L.path == MOE_PATH_GROUPED) return true;
-    return L.path == MOE_PATH_AUTO && T > kDecodeMaxT;
+    if (L.path != MOE_PATH_AUTO) return false;
+    if (T > kDecodeMaxT) return true;
+    return (double)T * L.k >= kGroupedMinRows * expected_active(L.n_expert, L.k, T);
 }
 
 // Large bf16 batches compute the router logits on MFMA (experts only; top-k then forms

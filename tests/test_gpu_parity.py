@@ -302,6 +302,23 @@ def test_deterministic():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("T,expect", [(4, "decode"), (12, "decode"), (16, "grouped"), (40, "grouped")])
+def test_auto_path_rows_per_expert(T, expect):
+    # AUTO takes the grouped MFMA path at or below 64 tokens once the expected rows per
+    # active expert, T*k / (E * (1 - (1 - k/E)^T)), reach 4 (E = 8, k = 2: from T = 16 on);
+    # the paths round differently, so the output matches the forced path bit for bit.
+    ov = dict(d=256, ff=448)
+    say("auto path", T, expect)
+    L, x = case("mixtral", T, **ov)
+    lay = dev_layer("mixtral", **ov)
+    auto = moe_mod().forward(lay, xdev(x))
+    forced = moe_mod().forward(lay.with_path(expect), xdev(x))
+    other = moe_mod().forward(lay.with_path("grouped" if expect == "decode" else "decode"), xdev(x))
+    assert torch.equal(auto, forced)
+    assert not torch.equal(auto, other)
+    assert_close(to_numpy_y(auto), oracle.moe_forward(L, x), "bf16", "y")
+
+
 def test_batch_invariance():
     # Rows of a batch equal the same tokens run alone (the batched-decode check of the
     # "Llama Forward Pass" page, applied to the MoE layer).
