@@ -201,7 +201,10 @@ hipError_t launch_up_t(const moe_layer& L, const void* x, int T, const int32_t* 
         SMOE_UP_CASE(1)
         SMOE_UP_CASE(2)
         SMOE_UP_CASE(4)
+        SMOE_UP_CASE(6)
         SMOE_UP_CASE(8)
+        default:
+            return hipErrorInvalidValue;
 #undef SMOE_UP_CASE
 #undef SMOE_UP_LAUNCH
     }
@@ -253,7 +256,10 @@ hipError_t launch_down_t(const moe_layer& L, int T, const Group* groups, const P
         SMOE_DOWN_CASE(1)
         SMOE_DOWN_CASE(2)
         SMOE_DOWN_CASE(4)
+        SMOE_DOWN_CASE(6)
         SMOE_DOWN_CASE(8)
+        default:
+            return hipErrorInvalidValue;
 #undef SMOE_DOWN_CASE
 #undef SMOE_DOWN_NR
 #undef SMOE_DOWN_LAUNCH
@@ -292,7 +298,10 @@ hipError_t launch_token1_up_t(const moe_layer& L, const void* x, const float* lo
         SMOE_UP_CASE(1)
         SMOE_UP_CASE(2)
         SMOE_UP_CASE(4)
+        SMOE_UP_CASE(6)
         SMOE_UP_CASE(8)
+        default:
+            return hipErrorInvalidValue;
 #undef SMOE_UP_CASE
 #undef SMOE_UP_LAUNCH
     }
@@ -327,6 +336,8 @@ hipError_t launch_token1_t(const moe_layer& L, int T, const float* H, int hstrid
         break;
         SMOE_T1_CASE(1)
         SMOE_T1_CASE(2)
+        default:
+            return hipErrorInvalidValue;
 #undef SMOE_T1_CASE
     }
     return hipGetLastError();

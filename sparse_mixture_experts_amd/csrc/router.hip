@@ -199,6 +199,8 @@ hipError_t launch_router_t(const moe_layer& L, const void* x, int T, float* logi
         SMOE_ROUTER_CASE(1)
         SMOE_ROUTER_CASE(2)
         SMOE_ROUTER_CASE(4)
+        default:
+            return hipErrorInvalidValue;
 #undef SMOE_ROUTER_CASE
 #undef SMOE_ROUTER_LAUNCH
     }

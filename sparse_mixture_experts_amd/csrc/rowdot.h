@@ -129,12 +129,15 @@ __device__ __forceinline__ void load_w_batch(const typename TW::storage* const (
     }
 }
 
-// Activation chunks per load sub-batch: at most 16 16-byte pieces (64 registers).
+// Activation chunks per load sub-batch: the largest divisor of KB that keeps it at most
+// 16 16-byte pieces (64 registers).
 template <int NT, int KB, typename TW, typename TA>
 constexpr int act_sub_batch() {
     constexpr int per_chunk = NT * ARaw<TA, TW::VEC>::Q;
-    constexpr int n = 16 / per_chunk;
-    return n < 1 ? 1 : (n > KB ? KB : n);
+    int n = 16 / per_chunk;
+    if (n > KB) n = KB;
+    while (n > 1 && KB % n != 0) --n;
+    return n < 1 ? 1 : n;
 }
 
 // acc[r][t] += W-batch (registers) . A_t over the batch's K range (same contract on a[t],
@@ -185,13 +188,15 @@ inline bool exact_k(int K, int vec, int kb) { return K % (kWave * vec * kb) == 0
 // 16-byte chunks per lane along a K axis of the given length.
 inline int chunks(int K, int vec) { return (K / vec + 63) / 64; }
 
-// Chunk-batch size for a K axis of the given length: the smallest of 1, 2, 4, 8 that
-// covers it in one batch, capped at 8 (longer axes loop over batches).
+// Chunk-batch size for a K axis of the given length: the smallest of 1, 2, 4, 6, 8 that
+// covers it in one batch, capped at 8 (longer axes loop over batches).  6 serves axes of
+// 5-6 chunks per lane (K = 2880 in bf16 is 5.6) with a quarter fewer padded chunks than 8.
 inline int pick_kb(int K, int vec) {
     int nchunk = (K / vec + 63) / 64;
     if (nchunk <= 1) return 1;
     if (nchunk <= 2) return 2;
     if (nchunk <= 4) return 4;
+    if (nchunk <= 6) return 6;
     return 8;
 }
 

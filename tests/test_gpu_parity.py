@@ -57,6 +57,10 @@ SMALL = [
     ("qwen", dict(d=512, n_expert=64, ff=256, shared_ff=256), [1, 5, 150, 300]),
     ("qwen_zipf", dict(d=512, ff=128, shared_ff=192), [300]),
     ("gptoss", dict(d=320, n_expert=16, ff=192), [1, 7, 100]),
+    # K of 5.5 16-byte chunks per lane (a 6-chunk batch with a masked tail), on the up
+    # projection (d) and on the down projection (ff).
+    ("gptoss", dict(d=2816, n_expert=8, ff=192), [1, 5]),
+    ("gptoss", dict(d=320, n_expert=8, ff=2816), [1, 5]),
     ("mixtral", dict(d=256, ff=448), [1, 3, 130]),
 ]
 SMALL_CASES = [(n, ov, T) for n, ov, Ts in SMALL for T in Ts]
@@ -64,7 +68,8 @@ SMALL_CASES = [(n, ov, T) for n, ov, Ts in SMALL for T in Ts]
 
 def _id(c):
     n, ov, T = c
-    return f"{n}-ff{ov['ff']}-T{T}" if "ff" in ov else f"{n}-T{T}"
+    dims = "".join(f"-{key}{ov[key]}" for key in ("d", "ff") if key in ov)
+    return f"{n}{dims}-T{T}"
 
 
 @pytest.mark.parametrize("c", SMALL_CASES, ids=_id)
@@ -428,6 +433,10 @@ SHELL = [
     ("tiny_f32", {}, [1, 16, 77]),
     ("qwen", dict(d=512, n_expert=64, ff=192, shared_ff=128), [1, 5, 64, 150]),
     ("gptoss", dict(d=320, n_expert=16, ff=192), [1, 7, 100]),
+    # K of 5.5 16-byte chunks per lane (a 6-chunk batch with a masked tail), on the up
+    # projection (d) and on the down projection (ff).
+    ("gptoss", dict(d=2816, n_expert=8, ff=192), [1, 5]),
+    ("gptoss", dict(d=320, n_expert=8, ff=2816), [1, 5]),
 ]
 SHELL_CASES = [(n, ov, T) for n, ov, Ts in SHELL for T in Ts]
 
