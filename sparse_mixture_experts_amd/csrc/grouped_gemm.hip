@@ -196,8 +196,9 @@ struct DownArgs {
     const uint16_t* b_down;   // [E, d] or null
     const uint16_t* ws_down;  // [d, ffs]
     const float* row_w;       // per grouped row weight, or null (unweighted)
-    void* y;                  // [rows, d], bf16 or fp32
+    void* y;                  // [rows, d], bf16 or fp32; with ksplit > 1 fp32 [ksplit][rows][d]
     int hstride, d, ff, ffs, n_ntiles;
+    int ksplit, rows;         // K slices per tile (each block sums K / ksplit), grouped rows
 };
 
 // XCD-aware tile order.  Workgroups are dispatched to the 8 XCDs round-robin by block
@@ -305,19 +306,27 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kerne
     }
 }
 
+// With ksplit > 1 (few tiles: decode-sized batches of layers with few experts) the K axis
+// of every tile is cut into ksplit slices, one block each (N-tile-major: the slices of an
+// N-tile are consecutive block slots), and each block stores its raw fp32 sums to slice
+// plane ks of y; splitk_reduce_kernel adds the planes, the bias and the routing weight.
 template <typename TY>
 __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_kernel(DownArgs a) {
     __shared__ GSmem<kDownKW> sm;
     Group g;
     int m0, nt;
-    if (!locate(a.meta, a.tiles, a.groups, a.n_ntiles, g, m0, nt)) return;
+    if (!locate(a.meta, a.tiles, a.groups, a.n_ntiles * a.ksplit, g, m0, nt)) return;
+    const int ks = nt % a.ksplit;
+    nt /= a.ksplit;
     const bool shared = g.e < 0;
-    const int K = shared ? a.ffs : a.ff;
+    const int Kfull = shared ? a.ffs : a.ff;
+    const int K = Kfull / a.ksplit;  // the host picks ksplit so that slices are whole K-steps
+    const int kb = ks * K;
     const int n0 = nt * GBN;
-    auto row_a = [&](int r) { return a.H + (size_t)(g.row0 + min(m0 + r, g.n - 1)) * a.hstride; };
+    auto row_a = [&](int r) { return a.H + (size_t)(g.row0 + min(m0 + r, g.n - 1)) * a.hstride + kb; };
     auto row_b = [&](int r) {
         const int n = min(n0 + r, a.d - 1);  // partial last N-tile: re-read
-        return shared ? a.ws_down + (size_t)n * K : a.w_down + ((size_t)g.e * a.d + n) * K;
+        return (shared ? a.ws_down + (size_t)n * Kfull : a.w_down + ((size_t)g.e * a.d + n) * Kfull) + kb;
     };
     const LoadPlan<kDownKW> plan = make_plan<kDownKW>(row_a, row_b);
     const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -371,7 +380,7 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
             const int ml = threadIdx.x / kChunks + kRowsPerPass * p;
             const int n = n0 + h * kCols + c * kPer;
             if (m0 + ml < g.n && n < a.d) {
-                TY* dst = static_cast<TY*>(a.y) + (size_t)(g.row0 + m0 + ml) * a.d + n;
+                TY* dst = static_cast<TY*>(a.y) + ((size_t)ks * a.rows + g.row0 + m0 + ml) * a.d + n;
                 uint4 v;
                 if constexpr (kHalf) v = *reinterpret_cast<const uint4*>(sm.down_h + ml * kStride + c * kPer);
                 else v = *reinterpret_cast<const uint4*>(sm.down_f + ml * kStride + c * kPer);
@@ -379,6 +388,49 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
             }
         }
         if (h + 1 < kHalves) __syncthreads();
+    }
+}
+
+// Sum of the ksplit fp32 planes of split-K down tiles, in plane order, plus the down bias,
+// times the row's routing weight: the same value the unsplit epilogue stores, summed in
+// another order.  Block (c, i) takes M-tile i of the tile map and 1024 output columns
+// from c * 1024, four per thread, row after row.
+template <typename TY>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int ksplit, int rows,
+                                                           const PlanMeta* __restrict__ meta,
+                                                           const TileDesc* __restrict__ tiles,
+                                                           const uint16_t* __restrict__ b_down,
+                                                           const float* __restrict__ row_w, TY* __restrict__ y,
+                                                           int d) {
+    if ((int)blockIdx.y >= meta->n_tiles) return;
+    const TileDesc td = tiles[blockIdx.y];
+    const int n = blockIdx.x * 1024 + threadIdx.x * 4;
+    if (n >= d) return;
+    float bias[4] = {0.f, 0.f, 0.f, 0.f};
+    if (td.e >= 0 && b_down) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bias[j] = ld_bf16(b_down + (size_t)td.e * d + n + j);
+    }
+    for (int m = 0; m < td.n; ++m) {
+        const size_t row = (size_t)td.row0 + m;
+        float4 acc = *reinterpret_cast<const float4*>(part + row * d + n);
+        for (int s = 1; s < ksplit; ++s) {
+            const float4 v = *reinterpret_cast<const float4*>(part + ((size_t)s * rows + row) * d + n);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        const float rw = row_w ? row_w[row] : 1.0f;
+        const float o[4] = {(acc.x + bias[0]) * rw, (acc.y + bias[1]) * rw, (acc.z + bias[2]) * rw,
+                            (acc.w + bias[3]) * rw};
+        if constexpr (sizeof(TY) == 2) {
+            const uint2 pk = make_uint2(uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16),
+                                        uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16));
+            *reinterpret_cast<uint2*>(y + row * d + n) = pk;
+        } else {
+            *reinterpret_cast<float4*>(y + row * d + n) = make_float4(o[0], o[1], o[2], o[3]);
+        }
     }
 }
 
@@ -507,7 +559,7 @@ int grouped_max_mtiles(int E, int T, int k, bool shared) {
 hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                               const Group* groups, const PlanMeta* meta, const TileDesc* tiles,
                               uint16_t* H, int hstride, const float* row_w, void* y, bool y_bf16,
-                              hipStream_t s) {
+                              int ksplit, float* partial, hipStream_t s) {
     const bool shared = L.shared_ff > 0;
     const int mt = grouped_max_mtiles(L.n_expert, T, L.k, shared);
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
@@ -523,9 +575,27 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
     else
         gg_up_kernel<false><<<gu, kGThreads, 0, s>>>(u);
     const int nn = (L.d + GBN - 1) / GBN;
-    DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down),
-                static_cast<const uint16_t*>(L.b_down), static_cast<const uint16_t*>(L.ws_down), row_w, y,
-                hstride, L.d, L.ff, L.shared_ff, nn};
+    const int rows = T * L.k + (shared ? T : 0);
+    const auto* b_down = static_cast<const uint16_t*>(L.b_down);
+    if (ksplit > 1) {
+        if (!partial || (L.ff / ksplit) % kDownKW || (shared && (L.shared_ff / ksplit) % kDownKW) ||
+            L.ff % ksplit || L.shared_ff % ksplit)
+            return hipErrorInvalidValue;
+        DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down), nullptr,
+                    static_cast<const uint16_t*>(L.ws_down), nullptr, partial, hstride, L.d, L.ff, L.shared_ff,
+                    nn, ksplit, rows};
+        gg_down_kernel<float><<<dim3((unsigned)grid_blocks(mt, nn * ksplit)), kGThreads, 0, s>>>(dn);
+        const dim3 gr((unsigned)((L.d + 1023) / 1024), (unsigned)mt);
+        if (y_bf16)
+            splitk_reduce_kernel<uint16_t><<<gr, 256, 0, s>>>(partial, ksplit, rows, meta, tiles, b_down, row_w,
+                                                              static_cast<uint16_t*>(y), L.d);
+        else
+            splitk_reduce_kernel<float><<<gr, 256, 0, s>>>(partial, ksplit, rows, meta, tiles, b_down, row_w,
+                                                           static_cast<float*>(y), L.d);
+        return hipGetLastError();
+    }
+    DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down), b_down,
+                static_cast<const uint16_t*>(L.ws_down), row_w, y, hstride, L.d, L.ff, L.shared_ff, nn, 1, rows};
     const dim3 gd((unsigned)grid_blocks(mt, nn));
     if (y_bf16)
         gg_down_kernel<uint16_t><<<gd, kGThreads, 0, s>>>(dn);

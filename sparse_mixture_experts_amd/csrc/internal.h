@@ -67,10 +67,12 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
 hipError_t launch_plan(const int32_t* offsets, int E, int T, int k, bool shared, int tile_m,
                        Group* groups, PlanMeta* meta, TileDesc* tiles, hipStream_t s);
 int grouped_max_mtiles(int E, int T, int k, bool shared);
+// Grouped up + down.  ksplit > 1: the down projection cuts each tile's K axis into that
+// many slices, summing them through `partial` (fp32, ksplit * rows * d floats).
 hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                               const Group* groups, const PlanMeta* meta, const TileDesc* tiles,
                               uint16_t* H, int hstride, const float* row_w, void* y, bool y_bf16,
-                              hipStream_t s);
+                              int ksplit, float* partial, hipStream_t s);
 // Combine of pre-weighted bf16 rows: y[t] = sum_j Y[perm_inv[t,j]] (+ Y[T*k + t]).
 hipError_t launch_combine_sum(const moe_layer& L, const uint16_t* y_rows, const int32_t* perm_inv,
                               int T, const void* residual, void* y, hipStream_t s);

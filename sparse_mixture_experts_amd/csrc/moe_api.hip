@@ -16,6 +16,10 @@ constexpr int kDecodeMaxT = 64;  // MOE_PATH_AUTO takes the grouped path above t
 // ... and at or below it when the expected rows per active expert reach this many: the
 // GEMVs' per-row arithmetic then outgrows their weight stream, MFMA tiles do not.
 constexpr double kGroupedMinRows = 4.0;
+// Split-K of the grouped down projection at decode-sized batches: at most this many K
+// slices per tile, chosen to bring the expected down blocks up to two per CU (256 CUs).
+constexpr int kMaxKSplit = 4;
+constexpr double kTargetDownBlocks = 512.0;
 constexpr int kTileM = kGroupTileM;  // M-tile size recorded in the group plan
 // Largest batch whose down projection runs per token, fused with the combine.
 constexpr int kTokenDownMaxT = 8;
@@ -26,7 +30,7 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 // Byte offsets of every scratch buffer inside the caller's workspace.
 struct Layout {
     size_t logits, idx, w, sg, counts, base, offsets, perm_token, perm_inv, groups, meta, tiles,
-        row_w, H, yperm, xn;
+        row_w, H, yperm, xn, partial;
     size_t total;
     int ld, hstride, rows;
 };
@@ -63,6 +67,9 @@ Layout layout_for(const moe_layer& L, int T) {
     o.yperm = take((size_t)o.rows * L.d * 4);
     // Normalised rows of the layer shell, in the layer's dtype.
     o.xn = take((size_t)T * L.d * (L.dtype == MOE_BF16 ? 2 : 4));
+    // fp32 planes of the split-K down projection (decode-sized bf16 batches only).
+    const bool split_possible = T <= kDecodeMaxT && L.dtype == MOE_BF16 && L.expert_format == MOE_EXPERTS_DENSE;
+    o.partial = take(split_possible ? (size_t)kMaxKSplit * o.rows * L.d * 4 : 0);
     o.total = off;
     return o;
 }
@@ -124,11 +131,11 @@ inline moe_status status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MO
         if (err_ != hipSuccess) return MOE_ERR_DEVICE; \
     } while (0)
 
-// The grouped MFMA path (bf16, dense experts) or the decode GEMV path.
 // Expected number of distinct experts that T tokens select, k each, if every expert were
 // equally likely: E * (1 - (1 - k/E)^T).
 double expected_active(int E, int k, int T) { return E * (1.0 - pow(1.0 - (double)k / E, (double)T)); }
 
+// The grouped MFMA path (bf16, dense experts) or the decode GEMV path.
 bool use_grouped(const moe_layer& L, int T) {
     if (L.dtype != MOE_BF16 || L.expert_format != MOE_EXPERTS_DENSE) return false;
     if (L.path == MOE_PATH_GROUPED) return true;
@@ -139,6 +146,20 @@ bool use_grouped(const moe_layer& L, int T) {
 
 // Large bf16 batches compute the router logits on MFMA (experts only; top-k then forms
 // the shared-gate input itself); otherwise the GEMV router fills every column.
+// K slices per tile of the grouped down projection.  Up to 64 tokens a group holds at most
+// 64 rows, so every active expert is one M-tile; with few of them (layers with few experts)
+// the down grid would leave CUs idle.  The slices must be whole 32-wide K-steps of both the
+// routed and the shared expert's K.
+int down_ksplit(const moe_layer& L, int T) {
+    if (T > kDecodeMaxT) return 1;
+    const double tiles = expected_active(L.n_expert, L.k, T) + (L.shared_ff > 0 ? 1 : 0);
+    const double blocks = tiles * ((L.d + 255) / 256);
+    int s = (int)ceil(kTargetDownBlocks / blocks);
+    s = s < kMaxKSplit ? s : kMaxKSplit;
+    while (s > 1 && (L.ff % (32 * s) || (L.shared_ff > 0 && L.shared_ff % (32 * s)))) --s;
+    return s > 1 ? s : 1;
+}
+
 bool router_on_mfma(const moe_layer& L, int T) { return use_grouped(L, T) && T > kPermChunk; }
 bool router_leaves_shared_gate(const moe_layer& L, int T) {
     return router_on_mfma(L, T) && L.shared_ff > 0;
@@ -169,8 +190,10 @@ moe_status run_experts(const moe_layer& L, const void* x, int T, const int32_t* 
         SMOE_TRY(launch_plan(offsets, L.n_expert, T, L.k, L.shared_ff > 0, kTileM, groups, meta,
                              tiles, s));
     if (grouped) {
+        const int ksplit = down_ksplit(L, T);
         SMOE_TRY(launch_grouped_ffn(L, x, T, perm_token, groups, meta, tiles, at<uint16_t>(ws, o.H),
-                                    o.hstride, row_w, y_rows, y_bf16, s));
+                                    o.hstride, row_w, y_rows, y_bf16, ksplit,
+                                    ksplit > 1 ? at<float>(ws, o.partial) : nullptr, s));
     } else {
         SMOE_TRY(launch_expert_gemv(L, x, T, perm_token, groups, meta, at<float>(ws, o.H), o.hstride,
                                     static_cast<float*>(y_rows), plan_in_up ? offsets : nullptr, s));
