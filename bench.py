@@ -65,7 +65,7 @@ def log(*a):
 
 CALIB_BYTES = 256 << 20
 STAGE_KERNELS = ("expert_up_gemv_kernel", "expert_down_gemv_kernel", "plan_kernel",
-                 "gg_up_kernel", "gg_down_kernel<float>")
+                 "gg_up_kernel", "gg_down_kernel<float>", "splitk_reduce_kernel<float>")
 
 
 def kernel_source_hash():

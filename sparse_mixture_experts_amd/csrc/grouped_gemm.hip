@@ -393,8 +393,10 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
 
 // Sum of the ksplit fp32 planes of split-K down tiles, in plane order, plus the down bias,
 // times the row's routing weight: the same value the unsplit epilogue stores, summed in
-// another order.  Block (c, i) takes M-tile i of the tile map and 1024 output columns
-// from c * 1024, four per thread, row after row.
+// another order.  Block (c, i, m) takes row m of M-tile i of the tile map and 1024 output
+// columns from c * 1024, four per thread; every plane's load is issued before the sum.
+constexpr int kMaxSplitPlanes = 4;
+
 template <typename TY>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int ksplit, int rows,
                                                            const PlanMeta* __restrict__ meta,
@@ -404,33 +406,39 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                            int d) {
     if ((int)blockIdx.y >= meta->n_tiles) return;
     const TileDesc td = tiles[blockIdx.y];
+    const int m = blockIdx.z;
     const int n = blockIdx.x * 1024 + threadIdx.x * 4;
-    if (n >= d) return;
+    if (m >= td.n || n >= d) return;
+    const size_t row = (size_t)td.row0 + m;
+    float4 v[kMaxSplitPlanes];
+#pragma unroll
+    for (int s = 0; s < kMaxSplitPlanes; ++s)
+        v[s] = s < ksplit ? *reinterpret_cast<const float4*>(part + ((size_t)s * rows + row) * d + n)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
     float bias[4] = {0.f, 0.f, 0.f, 0.f};
     if (td.e >= 0 && b_down) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) bias[j] = ld_bf16(b_down + (size_t)td.e * d + n + j);
     }
-    for (int m = 0; m < td.n; ++m) {
-        const size_t row = (size_t)td.row0 + m;
-        float4 acc = *reinterpret_cast<const float4*>(part + row * d + n);
-        for (int s = 1; s < ksplit; ++s) {
-            const float4 v = *reinterpret_cast<const float4*>(part + ((size_t)s * rows + row) * d + n);
-            acc.x += v.x;
-            acc.y += v.y;
-            acc.z += v.z;
-            acc.w += v.w;
+    const float rw = row_w ? row_w[row] : 1.0f;
+    float4 acc = v[0];
+#pragma unroll
+    for (int s = 1; s < kMaxSplitPlanes; ++s) {
+        if (s < ksplit) {
+            acc.x += v[s].x;
+            acc.y += v[s].y;
+            acc.z += v[s].z;
+            acc.w += v[s].w;
         }
-        const float rw = row_w ? row_w[row] : 1.0f;
-        const float o[4] = {(acc.x + bias[0]) * rw, (acc.y + bias[1]) * rw, (acc.z + bias[2]) * rw,
-                            (acc.w + bias[3]) * rw};
-        if constexpr (sizeof(TY) == 2) {
-            const uint2 pk = make_uint2(uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16),
-                                        uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16));
-            *reinterpret_cast<uint2*>(y + row * d + n) = pk;
-        } else {
-            *reinterpret_cast<float4*>(y + row * d + n) = make_float4(o[0], o[1], o[2], o[3]);
-        }
+    }
+    const float o[4] = {(acc.x + bias[0]) * rw, (acc.y + bias[1]) * rw, (acc.z + bias[2]) * rw,
+                        (acc.w + bias[3]) * rw};
+    if constexpr (sizeof(TY) == 2) {
+        const uint2 pk = make_uint2(uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16),
+                                    uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16));
+        *reinterpret_cast<uint2*>(y + row * d + n) = pk;
+    } else {
+        *reinterpret_cast<float4*>(y + row * d + n) = make_float4(o[0], o[1], o[2], o[3]);
     }
 }
 
@@ -578,14 +586,16 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
     const int rows = T * L.k + (shared ? T : 0);
     const auto* b_down = static_cast<const uint16_t*>(L.b_down);
     if (ksplit > 1) {
-        if (!partial || (L.ff / ksplit) % kDownKW || (shared && (L.shared_ff / ksplit) % kDownKW) ||
-            L.ff % ksplit || L.shared_ff % ksplit)
+        // The reduce grid has a z-slice per tile row: min(BM, T*k) covers every row of a tile
+        // (a group never holds more than the T*k routed rows).
+        if (!partial || ksplit > kMaxSplitPlanes || (L.ff / ksplit) % kDownKW ||
+            (shared && (L.shared_ff / ksplit) % kDownKW) || L.ff % ksplit || L.shared_ff % ksplit)
             return hipErrorInvalidValue;
         DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down), nullptr,
                     static_cast<const uint16_t*>(L.ws_down), nullptr, partial, hstride, L.d, L.ff, L.shared_ff,
                     nn, ksplit, rows};
         gg_down_kernel<float><<<dim3((unsigned)grid_blocks(mt, nn * ksplit)), kGThreads, 0, s>>>(dn);
-        const dim3 gr((unsigned)((L.d + 1023) / 1024), (unsigned)mt);
+        const dim3 gr((unsigned)((L.d + 1023) / 1024), (unsigned)mt, (unsigned)min(BM, T * L.k));
         if (y_bf16)
             splitk_reduce_kernel<uint16_t><<<gr, 256, 0, s>>>(partial, ksplit, rows, meta, tiles, b_down, row_w,
                                                               static_cast<uint16_t*>(y), L.d);
