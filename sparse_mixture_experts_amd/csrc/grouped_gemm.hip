@@ -204,25 +204,36 @@ struct DownArgs {
 // XCD-aware tile order.  Workgroups are dispatched to the 8 XCDs round-robin by block
 // id, and each XCD has its own L2.  Block b runs slot b / 8 of XCD b % 8; every XCD owns
 // a contiguous range of M-tiles (groups are contiguous in tile order, so an expert spans
-// at most a few XCDs) and runs all N-tiles of one M-tile back to back.  The gathered A
-// tile is then fetched into one L2 and reused by all N-tiles, and an expert's weight
-// slices are reused by its consecutive M-tiles inside the same L2.
+// at most a few XCDs) and walks it in groups of kGroupM M-tiles: all N-tiles of a group,
+// N-tile by N-tile, each N-tile over the group's M-tiles.  The blocks in flight on one XCD
+// (32 to 64) then share a few gathered A tiles and a few weight slices in its L2.  With
+// a single M-tile per step of the walk, a layer with wide experts (tens of N-tiles) would
+// stream a different weight slice into every block and re-read each expert's weights
+// from HBM once per M-tile.
 constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
 
 inline int grid_blocks(int max_mtiles, int n_ntiles) {
     return kXcds * ((max_mtiles + kXcds - 1) / kXcds) * n_ntiles;
 }
 
 // Resolve this block's (group, first row, N-tile).  Returns false if the block is idle.
+// Slots of one XCD: group q = slot / (kGroupM * n_ntiles) holds that XCD's M-tiles
+// q*kGroupM .. +gm-1 (gm = kGroupM but for the last group); inside it slot s takes N-tile
+// s / gm of M-tile s % gm.  The grid has ceil(max_mtiles / 8) * n_ntiles slots per XCD,
+// which covers every (M-tile, N-tile) pair of the XCD's range exactly once.
 __device__ __forceinline__ bool locate(const PlanMeta* meta, const TileDesc* tiles, const Group* groups,
                                        int n_ntiles, Group& g, int& m0, int& nt) {
     const int n_tiles = meta->n_tiles;
     const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
     const int per_xcd = (n_tiles + kXcds - 1) / kXcds;
-    const int local = slot / n_ntiles;
+    const int q = slot / (kGroupM * n_ntiles), s = slot % (kGroupM * n_ntiles);
+    const int gm = min(kGroupM, per_xcd - q * kGroupM);
+    if (gm <= 0) return false;
+    nt = s / gm;
+    const int local = q * kGroupM + s % gm;
     const int mt = xcd * per_xcd + local;
-    nt = slot % n_ntiles;
-    if (local >= per_xcd || mt >= n_tiles) return false;
+    if (nt >= n_ntiles || mt >= n_tiles) return false;
     g = groups[tiles[mt].group];
     m0 = (mt - g.tile0) * BM;
     return true;
