@@ -147,9 +147,12 @@ __device__ __forceinline__ void issue_slice(GSmem<KW>& sm, const LoadPlan<KW>& p
 
 // acc += A[wave rows] x B[rows brow[ni] + 0..15]^T over K.  Step kt: wait for this lane's
 // loads of slice kt, barrier (everyone's slice kt has landed and everyone has finished
-// step kt-1, whose stage the next issue reuses), issue slice kt+2 (clamped near the end,
-// so the body stays uniform), compute slice kt.  Ends with all loads drained and a
-// barrier, so the caller may reuse the LDS.
+// step kt-1, whose stage the next issue reuses), compute slice kt, then issue slice kt+2
+// (clamped near the end, so the body stays uniform).  Issuing the loads behind the
+// step's LDS reads and MFMAs instead of in front of them measured ~20% faster per step in
+// a probe of this loop (L2-resident operands): the fragment reads start right after the
+// barrier instead of queueing behind the direct loads' LDS writes.  Ends with all loads
+// drained and a barrier, so the caller may reuse the LDS.
 template <int KW>
 __device__ __forceinline__ void grouped_mainloop(GSmem<KW>& sm, const LoadPlan<KW>& p, int K, int arow0,
                                                  const int (&brow)[4], floatx4 (&acc)[4][4]) {
@@ -160,10 +163,10 @@ __device__ __forceinline__ void grouped_mainloop(GSmem<KW>& sm, const LoadPlan<K
     for (int kt = 0; kt < nk; ++kt) {
         wait_vm_lgkm<Ring<KW>::kLoads>();
         lds_barrier();
-        const int pre = st == 0 ? 2 : st - 1;  // (kt + 2) % 3
-        issue_slice(sm, p, pre, min(kt + 2, nk - 1) * KW);
 #pragma unroll
         for (int kc = 0; kc < KW / 8; kc += 4) mfma_k32<KW>(sm.k.a[st], sm.k.b[st], arow0, brow, kc, acc);
+        const int pre = st == 0 ? 2 : st - 1;  // (kt + 2) % 3
+        issue_slice(sm, p, pre, min(kt + 2, nk - 1) * KW);
         st = st == 2 ? 0 : st + 1;
     }
     wait_vm_lgkm<0>();
