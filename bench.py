@@ -43,6 +43,7 @@ WORKLOADS = {
     "gptoss_t64": ("gptoss", 64),
     "gptoss_mx_t1": ("gptoss_mx", 1),
     "gptoss_mx_t64": ("gptoss_mx", 64),
+    "gptoss_mx_t4096": ("gptoss_mx", 4096),
     "mixtral_t16": ("mixtral", 16),
     "mixtral_t16384": ("mixtral", 16384),
     "tiny_f32_t16": ("tiny_f32", 16),

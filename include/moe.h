@@ -71,10 +71,9 @@ enum { MOE_ROUTE_SOFTMAX_TOPK_RENORM = 0, MOE_ROUTE_TOPK_SOFTMAX = 1 };
 enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 };
 
 /* Kernel path.  AUTO: the grouped MFMA path for T > 64, and also for smaller batches
- * (bf16, dense experts) whose expected rows per active expert reach 4, taking
- * E * (1 - (1 - k/E)^T) distinct experts as for uniform routing; else the decode GEMV
- * path.  DECODE / GROUPED force one path at any T (GROUPED requires MOE_BF16 and dense
- * experts). */
+ * (bf16) whose expected rows per active expert reach 4, taking E * (1 - (1 - k/E)^T)
+ * distinct experts as for uniform routing; else the decode GEMV path.  DECODE / GROUPED
+ * force one path at any T (GROUPED requires MOE_BF16). */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_GROUPED = 2 };
 
 /* Storage of the routed experts' gate_up and down weights.
@@ -85,8 +84,10 @@ enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_GROUPED = 2 };
  *    w_down_scales [E, d, ff/32] uint8.  Each 16-byte block holds the 32 FP4 (E2M1,
  *    OCP Microscaling) codes of 32 consecutive inputs, the low nibble of byte i being
  *    element 2i; each scale is an E8M0 exponent: value = fp4(code) * 2^(scale - 127).
- *    Requires MOE_BF16, MOE_ACT_SWIGLU_OAI and no shared expert; runs on the GEMV path
- *    at every T (MOE_PATH_GROUPED is unsupported).  Biases, router, x and y stay bf16. */
+ *    Requires MOE_BF16, MOE_ACT_SWIGLU_OAI, no shared expert and d, ff <= 4096.  The
+ *    GEMV path expands the blocks in registers; the grouped path expands each K-slice of
+ *    a weight tile into LDS as bf16 for the bf16 MFMA (activations stay bf16).  Biases,
+ *    router, x and y stay bf16. */
 enum { MOE_EXPERTS_DENSE = 0, MOE_EXPERTS_MXFP4 = 1 };
 
 /* One MoE layer.  Fixed layout: 9 int32, 3 float, then 12 pointers (offset 48), then

@@ -14,26 +14,14 @@
 // activations in v_dot2 (fp32 accumulation).  H rows are stored in bf16 here, as on the
 // grouped path.  Lane l takes blocks l, l+64, ... of a row.
 #include "gemv_items.h"
+#include "mxfp4_dev.h"
 
 namespace smoe {
 namespace {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
 
-// 2^(s - 127) as a float: the E8M0 scale.  s = 0 is 2^-127 (a subnormal float), s = 255
-// is NaN.
-__device__ __forceinline__ float e8m0_scale(uint32_t s) {
-    const uint32_t bits = s == 0 ? 0x00400000u : (s == 255 ? 0x7FC00000u : s << 23);
-    return __uint_as_float(bits);
-}
-
-// Two bf16 (or fp32) weights of byte B of a code word, times the block's scale.
-template <int B>
-__device__ __forceinline__ bf16x2_t fp4_pair_bf16(uint32_t cw, float scale) {
-    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, B);
-}
-// The same for NT activation rows at once: each converted pair serves every row.
+// A code word's 8 weights against NT activation rows at once: each converted pair
+// serves every row.
 template <int NT>
 __device__ __forceinline__ void word_dot_bf16_rows(uint32_t cw, float scale, const uint4 (&xw)[NT], float (&acc)[NT]) {
     const bf16x2_t p0 = fp4_pair_bf16<0>(cw, scale), p1 = fp4_pair_bf16<1>(cw, scale);

@@ -37,6 +37,7 @@
 #include "common.h"
 #include "internal.h"
 #include "mfma_dev.h"
+#include "mxfp4_dev.h"
 
 namespace smoe {
 namespace {
@@ -115,7 +116,9 @@ struct LoadPlan {
     const uint16_t* src[Ring<KW>::kLoads];
 };
 
-template <int KW, typename RowA, typename RowB>
+// A_ONLY: B comes from MXFP4 blocks through registers (mx_load / mx_store), so only the A
+// segments are direct loads; row_b is not called.
+template <int KW, bool A_ONLY = false, typename RowA, typename RowB>
 __device__ __forceinline__ LoadPlan<KW> make_plan(RowA row_a, RowB row_b) {
     using R = Ring<KW>;
     LoadPlan<KW> p;
@@ -127,17 +130,18 @@ __device__ __forceinline__ LoadPlan<KW> make_plan(RowA row_a, RowB row_b) {
         const int r = seg * R::kRowsPerSeg + lane / R::kChunksPerRow;
         const int slot = lane % R::kChunksPerRow;
         const int c = swz_chunk<KW>(r, slot);  // logical chunk that belongs in this slot (the map is an involution)
-        p.src[j] = (is_a ? row_a(r) : row_b(r)) + c * 8;
+        if (A_ONLY && !is_a) p.src[j] = nullptr;
+        else p.src[j] = (is_a ? row_a(r) : row_b(r)) + c * 8;
     }
     return p;
 }
 
-template <int KW>
+template <int KW, bool A_ONLY = false>
 __device__ __forceinline__ void issue_slice(GSmem<KW>& sm, const LoadPlan<KW>& p, int stage, int k0) {
     using R = Ring<KW>;
     const int wave = threadIdx.x / kWave;
 #pragma unroll
-    for (int j = 0; j < R::kLoads; ++j) {
+    for (int j = 0; j < (A_ONLY ? R::kLoadsA : R::kLoads); ++j) {
         const bool is_a = j < R::kLoadsA;
         const int seg = wave + 8 * (is_a ? j : j - R::kLoadsA);
         uint16_t* dst = is_a ? &sm.k.a[stage][seg * 512] : &sm.k.b[stage][seg * 512];  // 1 KB
@@ -173,6 +177,89 @@ __device__ __forceinline__ void grouped_mainloop(GSmem<KW>& sm, const LoadPlan<K
     __syncthreads();
 }
 
+// MXFP4 weights ("Phase 19: MoE - gpt-oss-20b", section 3): B rows are 16-byte blocks of
+// 32 FP4 codes with one E8M0 scale byte each.  They cannot be direct-loaded into the bf16
+// ring, so each thread loads its share of a K-slice into registers -- row threadIdx.x / 2
+// of the N-tile, half threadIdx.x & 1 of the slice's KW codes (KW / 4 bytes) and the
+// block's scale -- and one step later expands it with gfx950's scaled FP4 conversion into
+// the slice's bf16 LDS rows (same swizzled layout as the direct loads).  The weights then
+// cost 0.53 bytes each from memory instead of 2.
+struct MxRow {
+    const uint8_t* codes;   // the row's first block
+    const uint8_t* scales;  // the row's first scale byte
+};
+
+template <int KW>
+struct MxRegs {
+    uint32_t w[KW / 16];  // KW / 2 codes
+    uint32_t s;           // scale byte
+};
+constexpr int kMxLoads = 2;  // vector loads per thread per slice (codes, scale)
+
+template <int KW>
+__device__ __forceinline__ MxRegs<KW> mx_load(const MxRow& m, int k0) {
+    const int h = threadIdx.x & 1;
+    MxRegs<KW> r;
+    if constexpr (KW == 64) {  // two blocks per row slice: one each
+        const int blk = k0 / 32 + h;
+        const uint4 q = ld16(m.codes + (size_t)blk * 16);
+        r.w[0] = q.x;
+        r.w[1] = q.y;
+        r.w[2] = q.z;
+        r.w[3] = q.w;
+        r.s = m.scales[blk];
+    } else {  // one block per row slice: half of it each
+        static_assert(KW == 32, "MXFP4 slices are one or two blocks wide");
+        const int blk = k0 / 32;
+        const uint2 q = *reinterpret_cast<const uint2*>(m.codes + (size_t)blk * 16 + 8 * h);
+        r.w[0] = q.x;
+        r.w[1] = q.y;
+        r.s = m.scales[blk];
+    }
+    return r;
+}
+
+template <int KW>
+__device__ __forceinline__ void mx_store(GSmem<KW>& sm, int stage, const MxRegs<KW>& r) {
+    const int row = threadIdx.x >> 1, h = threadIdx.x & 1;
+    const float scale = e8m0_scale(r.s);
+#pragma unroll
+    for (int i = 0; i < KW / 16; ++i)
+        *reinterpret_cast<uint4*>(&sm.k.b[stage][swz<KW>(row, h * (KW / 16) + i)]) = fp4_word_bf16x8(r.w[i], scale);
+}
+
+// The main loop with B from MXFP4 blocks.  Slice s: A direct-loaded two steps ahead as
+// above; B loaded into registers two steps ahead and expanded into LDS at the end of step
+// s - 1 (its stage held slice s - 3, finished by every wave at the barrier of step s - 1).
+// The wait before each step allows the newest slice's loads (A and B registers) in
+// flight; the expansion itself waits for its registers, which also completes the A
+// loads issued before them.
+template <int KW>
+__device__ __forceinline__ void grouped_mainloop_mx(GSmem<KW>& sm, const LoadPlan<KW>& p, const MxRow& mb, int K,
+                                                    int arow0, const int (&brow)[4], floatx4 (&acc)[4][4]) {
+    const int nk = K / KW;
+    issue_slice<KW, true>(sm, p, 0, 0);
+    const MxRegs<KW> first = mx_load<KW>(mb, 0);
+    issue_slice<KW, true>(sm, p, 1, min(1, nk - 1) * KW);
+    MxRegs<KW> nxt = mx_load<KW>(mb, min(1, nk - 1) * KW);
+    mx_store(sm, 0, first);
+    int st = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vm_lgkm<Ring<KW>::kLoadsA + kMxLoads>();
+        lds_barrier();
+#pragma unroll
+        for (int kc = 0; kc < KW / 8; kc += 4) mfma_k32<KW>(sm.k.a[st], sm.k.b[st], arow0, brow, kc, acc);
+        const int nx = st == 2 ? 0 : st + 1;   // (kt + 1) % 3
+        mx_store(sm, nx, nxt);                 // B of slice kt+1 (clamped re-load on the last step)
+        const int pre = st == 0 ? 2 : st - 1;  // (kt + 2) % 3
+        issue_slice<KW, true>(sm, p, pre, min(kt + 2, nk - 1) * KW);
+        nxt = mx_load<KW>(mb, min(kt + 2, nk - 1) * KW);
+        st = nx;
+    }
+    wait_vm_lgkm<0>();
+    __syncthreads();
+}
+
 struct UpArgs {
     const uint16_t* x;
     const int32_t* perm_token;
@@ -185,6 +272,8 @@ struct UpArgs {
     const uint16_t* b_gate_up;  // [E, 2ff]
     const uint16_t* ws_gate;    // [ffs, d]
     const uint16_t* ws_up;
+    const uint8_t* mx_w;        // MXFP4 gate_up blocks [E, 2ff, d/32, 16], or null
+    const uint8_t* mx_s;        // ... and scales [E, 2ff, d/32]
     uint16_t* H;                // bf16 [rows, hstride]
     int hstride, T, d, ff, ffs, n_ntiles;
     float alpha, limit;
@@ -198,6 +287,8 @@ struct DownArgs {
     const uint16_t* w_down;   // [E, d, ff]
     const uint16_t* b_down;   // [E, d] or null
     const uint16_t* ws_down;  // [d, ffs]
+    const uint8_t* mx_w;      // MXFP4 down blocks [E, d, ff/32, 16], or null
+    const uint8_t* mx_s;      // ... and scales [E, d, ff/32]
     const float* row_w;       // per grouped row weight, or null (unweighted)
     void* y;                  // [rows, d], bf16 or fp32; with ksplit > 1 fp32 [ksplit][rows][d]
     int hstride, d, ff, ffs, n_ntiles;
@@ -242,7 +333,8 @@ __device__ __forceinline__ bool locate(const PlanMeta* meta, const TileDesc* til
     return true;
 }
 
-template <bool OAI>
+// MX: gate_up weights as MXFP4 blocks (a.mx_w, a.mx_s; clamped variant, no shared expert).
+template <bool OAI, bool MX>
 __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kernel(UpArgs a) {
     __shared__ GSmem<kUpKW> sm;
     Group g;
@@ -271,14 +363,24 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kerne
                                       : (up ? a.w_up : a.w_gate) + (size_t)g.e * a.ff * d;
         return base + (size_t)f * d;
     };
-    const LoadPlan<kUpKW> plan = make_plan<kUpKW>(row_a, row_b);
+    const LoadPlan<kUpKW> plan = make_plan<kUpKW, MX>(row_a, row_b);
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int wm = wave >> 2, wn = wave & 3;
     // Wave n-tiles 0,1 are gate units wn*32.., 2,3 the matching up units.
     const int brow[4] = {wn * 32, wn * 32 + 16, 128 + wn * 32, 128 + wn * 32 + 16};
     floatx4 acc[4][4];
     zero(acc);
-    grouped_mainloop(sm, plan, a.d, wm * 64, brow, acc);
+    if constexpr (MX) {
+        // This thread's B row (tile row threadIdx.x / 2), in the interleaved gate_up rows.
+        const int r = threadIdx.x >> 1;
+        const int f = min(f0 + (r & 127), ffg - 1);
+        const size_t R = (size_t)max(g.e, 0) * 2 * a.ff + 2 * f + (r >= 128 ? 1 : 0);
+        const size_t nblk = d / 32;
+        const MxRow mb{a.mx_w + R * nblk * 16, a.mx_s + R * nblk};
+        grouped_mainloop_mx(sm, plan, mb, a.d, wm * 64, brow, acc);
+    } else {
+        grouped_mainloop(sm, plan, a.d, wm * 64, brow, acc);
+    }
 
     // Epilogue: lane holds D[4*(lane/16) + i][lane%16] of each 16x16 tile.  Activation,
     // bf16, staged in LDS as the 128 x 128 H tile.
@@ -324,7 +426,8 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kerne
 // of every tile is cut into ksplit slices, one block each (N-tile-major: the slices of an
 // N-tile are consecutive block slots), and each block stores its raw fp32 sums to slice
 // plane ks of y; splitk_reduce_kernel adds the planes, the bias and the routing weight.
-template <typename TY>
+// MX: down weights as MXFP4 blocks (a.mx_w, a.mx_s).
+template <typename TY, bool MX>
 __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_kernel(DownArgs a) {
     __shared__ GSmem<kDownKW> sm;
     Group g;
@@ -342,13 +445,22 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
         const int n = min(n0 + r, a.d - 1);  // partial last N-tile: re-read
         return (shared ? a.ws_down + (size_t)n * Kfull : a.w_down + ((size_t)g.e * a.d + n) * Kfull) + kb;
     };
-    const LoadPlan<kDownKW> plan = make_plan<kDownKW>(row_a, row_b);
+    const LoadPlan<kDownKW> plan = make_plan<kDownKW, MX>(row_a, row_b);
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int wm = wave >> 2, wn = wave & 3;
     const int brow[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
     floatx4 acc[4][4];
     zero(acc);
-    grouped_mainloop(sm, plan, K, wm * 64, brow, acc);
+    if constexpr (MX) {
+        // This thread's B row (tile row threadIdx.x / 2) of W_d, from this split's first block.
+        const int n = min(n0 + (int)(threadIdx.x >> 1), a.d - 1);
+        const size_t R = (size_t)max(g.e, 0) * a.d + n;
+        const size_t nblk = Kfull / 32;
+        const MxRow mb{a.mx_w + (R * nblk + kb / 32) * 16, a.mx_s + R * nblk + kb / 32};
+        grouped_mainloop_mx(sm, plan, mb, K, wm * 64, brow, acc);
+    } else {
+        grouped_mainloop(sm, plan, K, wm * 64, brow, acc);
+    }
 
     float rw[4][4];
 #pragma unroll
@@ -586,16 +698,25 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
     const int mt = grouped_max_mtiles(L.n_expert, T, L.k, shared);
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
     const int nn_up = (ffmax + 127) / 128;
+    // MXFP4 experts: the clamped variant without a shared expert (checked by the caller);
+    // w_gate_up / w_down hold the FP4 blocks, the *_scales fields their E8M0 scales.
+    const bool mx = L.expert_format == MOE_EXPERTS_MXFP4;
+    if (mx && (L.act != MOE_ACT_SWIGLU_OAI || shared || L.d % 64 || L.ff % 32)) return hipErrorInvalidValue;
     UpArgs u{static_cast<const uint16_t*>(x), perm_token, groups, meta, tiles,
              static_cast<const uint16_t*>(L.w_gate), static_cast<const uint16_t*>(L.w_up),
              static_cast<const uint16_t*>(L.w_gate_up), static_cast<const uint16_t*>(L.b_gate_up),
-             static_cast<const uint16_t*>(L.ws_gate), static_cast<const uint16_t*>(L.ws_up), H, hstride, T,
-             L.d, L.ff, L.shared_ff, nn_up, L.oai_alpha, L.oai_limit};
+             static_cast<const uint16_t*>(L.ws_gate), static_cast<const uint16_t*>(L.ws_up),
+             mx ? static_cast<const uint8_t*>(L.w_gate_up) : nullptr, mx ? L.w_gate_up_scales : nullptr, H,
+             hstride, T, L.d, L.ff, L.shared_ff, nn_up, L.oai_alpha, L.oai_limit};
     const dim3 gu((unsigned)grid_blocks(mt, nn_up));
-    if (L.act == MOE_ACT_SWIGLU_OAI)
-        gg_up_kernel<true><<<gu, kGThreads, 0, s>>>(u);
+    if (mx)
+        gg_up_kernel<true, true><<<gu, kGThreads, 0, s>>>(u);
+    else if (L.act == MOE_ACT_SWIGLU_OAI)
+        gg_up_kernel<true, false><<<gu, kGThreads, 0, s>>>(u);
     else
-        gg_up_kernel<false><<<gu, kGThreads, 0, s>>>(u);
+        gg_up_kernel<false, false><<<gu, kGThreads, 0, s>>>(u);
+    const uint8_t* mx_dw = mx ? static_cast<const uint8_t*>(L.w_down) : nullptr;
+    const uint8_t* mx_ds = mx ? L.w_down_scales : nullptr;
     const int nn = (L.d + GBN - 1) / GBN;
     const int rows = T * L.k + (shared ? T : 0);
     const auto* b_down = static_cast<const uint16_t*>(L.b_down);
@@ -606,9 +727,11 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
             (shared && (L.shared_ff / ksplit) % kDownKW) || L.ff % ksplit || L.shared_ff % ksplit)
             return hipErrorInvalidValue;
         DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down), nullptr,
-                    static_cast<const uint16_t*>(L.ws_down), nullptr, partial, hstride, L.d, L.ff, L.shared_ff,
-                    nn, ksplit, rows};
-        gg_down_kernel<float><<<dim3((unsigned)grid_blocks(mt, nn * ksplit)), kGThreads, 0, s>>>(dn);
+                    static_cast<const uint16_t*>(L.ws_down), mx_dw, mx_ds, nullptr, partial, hstride, L.d, L.ff,
+                    L.shared_ff, nn, ksplit, rows};
+        const dim3 gs((unsigned)grid_blocks(mt, nn * ksplit));
+        if (mx) gg_down_kernel<float, true><<<gs, kGThreads, 0, s>>>(dn);
+        else gg_down_kernel<float, false><<<gs, kGThreads, 0, s>>>(dn);
         const dim3 gr((unsigned)((L.d + 1023) / 1024), (unsigned)mt, (unsigned)min(BM, T * L.k));
         if (y_bf16)
             splitk_reduce_kernel<uint16_t><<<gr, 256, 0, s>>>(partial, ksplit, rows, meta, tiles, b_down, row_w,
@@ -619,12 +742,16 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
         return hipGetLastError();
     }
     DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down), b_down,
-                static_cast<const uint16_t*>(L.ws_down), row_w, y, hstride, L.d, L.ff, L.shared_ff, nn, 1, rows};
+                static_cast<const uint16_t*>(L.ws_down), mx_dw, mx_ds, row_w, y, hstride, L.d, L.ff, L.shared_ff,
+                nn, 1, rows};
     const dim3 gd((unsigned)grid_blocks(mt, nn));
-    if (y_bf16)
-        gg_down_kernel<uint16_t><<<gd, kGThreads, 0, s>>>(dn);
-    else
-        gg_down_kernel<float><<<gd, kGThreads, 0, s>>>(dn);
+    if (mx) {
+        if (y_bf16) gg_down_kernel<uint16_t, true><<<gd, kGThreads, 0, s>>>(dn);
+        else gg_down_kernel<float, true><<<gd, kGThreads, 0, s>>>(dn);
+    } else {
+        if (y_bf16) gg_down_kernel<uint16_t, false><<<gd, kGThreads, 0, s>>>(dn);
+        else gg_down_kernel<float, false><<<gd, kGThreads, 0, s>>>(dn);
+    }
     return hipGetLastError();
 }
 

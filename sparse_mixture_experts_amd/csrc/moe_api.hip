@@ -68,7 +68,7 @@ Layout layout_for(const moe_layer& L, int T) {
     // Normalised rows of the layer shell, in the layer's dtype.
     o.xn = take((size_t)T * L.d * (L.dtype == MOE_BF16 ? 2 : 4));
     // fp32 planes of the split-K down projection (decode-sized bf16 batches only).
-    const bool split_possible = T <= kDecodeMaxT && L.dtype == MOE_BF16 && L.expert_format == MOE_EXPERTS_DENSE;
+    const bool split_possible = T <= kDecodeMaxT && L.dtype == MOE_BF16;
     o.partial = take(split_possible ? (size_t)kMaxKSplit * o.rows * L.d * 4 : 0);
     o.total = off;
     return o;
@@ -103,8 +103,7 @@ moe_status check_layer(const moe_layer* L) {
     if (L->reserved0 != 0) return MOE_ERR_ARG;
     if (L->expert_format == MOE_EXPERTS_MXFP4) {
         if (!L->w_gate_up_scales || !L->w_down_scales) return MOE_ERR_ARG;
-        if (L->dtype != MOE_BF16 || L->act != MOE_ACT_SWIGLU_OAI || L->shared_ff != 0 ||
-            L->path == MOE_PATH_GROUPED || !mx_fits(*L))
+        if (L->dtype != MOE_BF16 || L->act != MOE_ACT_SWIGLU_OAI || L->shared_ff != 0 || !mx_fits(*L))
             return MOE_ERR_UNSUPPORTED;
     }
     const void* vec_ptrs[] = {L->w_router, L->w_gate, L->w_up, L->w_gate_up, L->w_down,
@@ -135,9 +134,9 @@ inline moe_status status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MO
 // equally likely: E * (1 - (1 - k/E)^T).
 double expected_active(int E, int k, int T) { return E * (1.0 - pow(1.0 - (double)k / E, (double)T)); }
 
-// The grouped MFMA path (bf16, dense experts) or the decode GEMV path.
+// The grouped MFMA path (bf16; dense or MXFP4 experts) or the decode GEMV path.
 bool use_grouped(const moe_layer& L, int T) {
-    if (L.dtype != MOE_BF16 || L.expert_format != MOE_EXPERTS_DENSE) return false;
+    if (L.dtype != MOE_BF16) return false;
     if (L.path == MOE_PATH_GROUPED) return true;
     if (L.path != MOE_PATH_AUTO) return false;
     if (T > kDecodeMaxT) return true;

@@ -189,7 +189,7 @@ def test_mxfp4_layer_checks(lib):
     assert ws_size(lib, fake_layer(**dict(mx, dtype=moe.MOE_F32)), 4)[0] == moe.MOE_ERR_UNSUPPORTED
     assert ws_size(lib, fake_layer(**dict(mx, act=moe.MOE_ACT_SWIGLU, w_gate=FAKE, w_up=FAKE)), 4)[0] \
         == moe.MOE_ERR_UNSUPPORTED
-    assert ws_size(lib, fake_layer(**dict(mx, path=moe.MOE_PATH_GROUPED)), 4)[0] == moe.MOE_ERR_UNSUPPORTED
+    assert ws_size(lib, fake_layer(**dict(mx, path=moe.MOE_PATH_GROUPED)), 4)[0] == moe.MOE_OK
     assert ws_size(lib, fake_layer(**dict(mx, d=8192)), 4)[0] == moe.MOE_ERR_UNSUPPORTED  # K > 4096
     sh = dict(mx, shared_ff=64, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, ws_gate_inp=FAKE)
     assert ws_size(lib, fake_layer(**sh), 4)[0] == moe.MOE_ERR_UNSUPPORTED

@@ -542,9 +542,31 @@ def test_mxfp4_shell():
         assert_shell_close(to_numpy_y(out), ref, oracle.widen(h), "bf16", f"mx shell T={T}")
 
 
-def test_mxfp4_grouped_path_unsupported():
-    lay = dev_layer("gptoss_mx", **MX_SMALL[0])
-    x = xdev(case("gptoss_mx", 4, **MX_SMALL[0])[1])
-    with pytest.raises(moe_mod().MoeError) as ei:
-        moe_mod().forward(lay.with_path("grouped"), x)
-    assert ei.value.status == moe_mod().MOE_ERR_UNSUPPORTED
+@pytest.mark.parametrize("T", [1, 7, 100, 300])
+@pytest.mark.parametrize("ov", MX_SMALL, ids=["d320", "d4096"])
+def test_mxfp4_grouped_forward(ov, T):
+    # The grouped MFMA path with the FP4 blocks expanded into LDS (forced at every T; T=7
+    # takes split-K down tiles), against the oracle on the dequantised weights.
+    say("mxfp4 grouped forward", ov, T)
+    L, x = case("gptoss_mx", T, **ov)
+    lay = dev_layer("gptoss_mx", **ov)
+    y = moe_mod().forward(lay.with_path("grouped"), xdev(x))
+    torch.cuda.synchronize()
+    e = assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "bf16", "y")
+    say(f"  rel err {e:.2e}")
+
+
+def test_mxfp4_grouped_expert_ffn_rows():
+    # Unweighted expert rows of the grouped path (fp32 output tiles), several M-tiles per
+    # expert and a ragged last tile.
+    ov = MX_SMALL[0]
+    L, x = case("gptoss_mx", 333, **ov)
+    lay = dev_layer("gptoss_mx", **ov).with_path("grouped")
+    idx, _, _ = moe_mod().route(lay, xdev(x))
+    off, pt, _ = moe_mod().permute(idx, L["n_expert"])
+    yp = moe_mod().expert_ffn(lay, xdev(x), off, pt)
+    torch.cuda.synchronize()
+    ridx, _, _ = oracle.route(L, x)
+    _, roff, rpt, _ = oracle.permute(ridx, L["n_expert"])
+    assert np.array_equal(off.cpu().numpy(), roff) and np.array_equal(pt.cpu().numpy(), rpt)
+    assert_close(to_numpy_y(yp), oracle.expert_rows(L, x, roff, rpt), "bf16", "rows")
