@@ -65,8 +65,9 @@ def log(*a):
 # the kernel sources still hash to the value recorded with it.
 
 CALIB_BYTES = 256 << 20
+# Kernels of the timed stage (name prefixes; the grouped down kernel writes fp32 rows there).
 STAGE_KERNELS = ("expert_up_gemv_kernel", "expert_down_gemv_kernel", "plan_kernel",
-                 "gg_up_kernel", "gg_down_kernel<float>", "splitk_reduce_kernel<float>")
+                 "gg_up_kernel", "gg_down_kernel<float", "splitk_reduce_kernel<float")
 
 
 def kernel_source_hash():
@@ -142,7 +143,7 @@ def summarize_pmc(fetch_csv, write_csv, workload, out_path, command):
         w = per["WRITE_SIZE"][0].get(n, [])
         fb = (sum(f) / len(f) * 1024.0 / per["FETCH_SIZE"][1]) if f else 0.0
         wb = (sum(w) / len(w) * 1024.0 / per["WRITE_SIZE"][1]) if w else 0.0
-        stage = any(n.startswith(k) or k in n for k in STAGE_KERNELS)
+        stage = any(n.startswith(k) for k in STAGE_KERNELS)
         if stage:
             total += fb + wb
         rows.append((n, len(f), fb, wb, stage))
