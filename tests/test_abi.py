@@ -78,6 +78,14 @@ def test_workspace_size_grows_with_T(lib):
     assert st0 == st1 == 0 and 0 < n0 < n1
 
 
+def test_token_count_limit(lib):
+    # At most 2^22 tokens per call; negative counts are argument errors.
+    s = fake_layer()
+    assert ws_size(lib, s, 1 << 22)[0] == moe.MOE_OK
+    assert ws_size(lib, s, (1 << 22) + 1)[0] == moe.MOE_ERR_UNSUPPORTED
+    assert ws_size(lib, s, -1)[0] == moe.MOE_ERR_ARG
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("k", 0, moe.MOE_ERR_ARG), ("k", 9, moe.MOE_ERR_ARG), ("d", 0, moe.MOE_ERR_ARG),
     ("n_expert", -1, moe.MOE_ERR_ARG), ("shared_ff", -64, moe.MOE_ERR_ARG),

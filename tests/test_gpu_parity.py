@@ -426,6 +426,37 @@ def test_grouped_many_tiles():
     assert_close(y[tok], oracle.moe_forward(L, x[tok]), "bf16", "y")
 
 
+def test_max_tokens():
+    # The largest batch the library accepts, 2^22 tokens, on a small layer: 8M routed rows
+    # and 4M shared rows, so the grouping, the offsets, the M-tile map and every row index
+    # are at their largest.  Routing and grouping are compared on every token (bit-exact),
+    # the output on a seeded sample that includes the last token.  The same layer at 300
+    # tokens first.
+    ov = dict(d=64, n_expert=8, k=2, ff=64, shared_ff=64)
+    T = 1 << 22
+    L = layer_arrays("qwen", 0, **ov)
+    lay = dev_layer("qwen", **ov)
+    xs = synth.make_tokens(L, 300, seed=101)
+    assert_close(to_numpy_y(moe_mod().forward(lay, xdev(xs))), oracle.moe_forward(L, xs), "bf16", "y (300)")
+    say("max tokens", ov, T)
+    x = synth.make_tokens(L, T, seed=100)
+    xd = xdev(x)
+    idx, _, _ = moe_mod().route(lay, xd)
+    off, pt, pinv = moe_mod().permute(idx, L["n_expert"])
+    y = moe_mod().forward(lay, xd)
+    torch.cuda.synchronize()
+    ridx, _, _ = oracle.route(L, x)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    counts, roff, rpt, rinv = oracle.permute(ridx, L["n_expert"])
+    say("  counts", counts.tolist())
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(pt.cpu().numpy(), rpt) and np.array_equal(pinv.cpu().numpy(), rinv.reshape(-1))
+    tok = np.concatenate([np.sort(np.random.default_rng(13).choice(T - 1, 255, replace=False)), [T - 1]])
+    got = to_numpy_y(y[torch.from_numpy(tok).to(y.device)])
+    e = assert_close(got, oracle.moe_forward(L, x[tok]), "bf16", "y (sample)")
+    say(f"  rel err {e:.2e}")
+
+
 # ----------------------------------------------------------------------------- layer shell
 
 EPS = 1e-5
