@@ -44,22 +44,22 @@ namespace {
 
 constexpr int BM = kGroupTileM;  // rows per M-tile
 
-// 32 K of one wave's 64 x 64 tile: 4 A and 4 B fragments from LDS, 16 MFMAs.
+// 32 K of one wave's (16 MI) x 64 tile: MI A and 4 B fragments from LDS, 4 MI MFMAs.
 // Fragment layout of v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16 of its
 // 16-row block and the 8 K values of chunk (l / 16); A and B use the same chunk map, so
 // the order of K inside the 32 does not matter.
-template <int KW>
+template <int KW, int MI = 4>
 __device__ __forceinline__ void mfma_k32(const uint16_t* sa, const uint16_t* sb, int arow0,
-                                         const int (&brow)[4], int kc, floatx4 (&acc)[4][4]) {
+                                         const int (&brow)[4], int kc, floatx4 (&acc)[MI][4]) {
     const int lane = lane_id();
     const int fr = lane & 15, fc = lane >> 4;
-    bf16x8 af[4], bfr[4];
+    bf16x8 af[MI], bfr[4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) af[mi] = lds_frag<KW>(sa, arow0 + mi * 16 + fr, kc + fc);
+    for (int mi = 0; mi < MI; ++mi) af[mi] = lds_frag<KW>(sa, arow0 + mi * 16 + fr, kc + fc);
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) bfr[ni] = lds_frag<KW>(sb, brow[ni] + fr, kc + fc);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
@@ -569,47 +569,53 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 // =====================================================================================
-// Router GEMM: 4 waves, 128 x 128 block tile, register-staged double-buffered LDS.
+// Router GEMM: 4 waves, MT x 128 block tile (MT = 128, 64 or 32 token rows: the largest
+// that still gives every CU a block), register-staged double-buffered LDS.
 // =====================================================================================
 constexpr int RBN = 128;
 constexpr int RBK = 64;
 constexpr int kRThreads = 256;
 
+template <int MT>
 struct RSmem {
-    uint16_t a[2][BM * RBK];
+    uint16_t a[2][MT * RBK];
     uint16_t b[2][RBN * RBK];
 };
 
-// This thread's 4 rows (tile rows tid/8 + 32 i) at chunk tid%8.
-__device__ __forceinline__ void load_slice(const uint16_t* const (&rows)[4], int k0, uint4 (&r)[4]) {
+// This thread's N rows (tile rows tid/8 + 32 i) at chunk tid%8.
+template <int N>
+__device__ __forceinline__ void load_slice(const uint16_t* const (&rows)[N], int k0, uint4 (&r)[N]) {
     const int c = (threadIdx.x & 7) * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = ld16(rows[i] + k0 + c);
+    for (int i = 0; i < N; ++i) r[i] = ld16(rows[i] + k0 + c);
 }
 
-__device__ __forceinline__ void store_slice(uint16_t* lds, const uint4 (&r)[4]) {
+template <int N>
+__device__ __forceinline__ void store_slice(uint16_t* lds, const uint4 (&r)[N]) {
     const int c = threadIdx.x & 7;
     const int r0 = threadIdx.x >> 3;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(lds + swz<RBK>(r0 + 32 * i, c)) = r[i];
+    for (int i = 0; i < N; ++i) *reinterpret_cast<uint4*>(lds + swz<RBK>(r0 + 32 * i, c)) = r[i];
 }
 
 // One step on K-slice kt with buffer / register set B (compile-time, so register arrays
 // are never indexed dynamically).  Straight-line on purpose: the prefetch (slice kt+2,
 // clamped) and the store (slice kt+1; a dead store into the idle buffer on the last step)
 // are unconditional, and a scheduling fence keeps the prefetch above the store, so the
-// wait before the store leaves this step's prefetch in flight.
-template <int B>
-__device__ __forceinline__ void router_step(RSmem& sm, const uint16_t* const (&a_rows)[4],
+// wait before the store leaves this step's prefetch in flight.  NA: A rows per thread
+// (MT / 32); MI: A fragments per wave (MT / 32).
+template <int B, int MT>
+__device__ __forceinline__ void router_step(RSmem<MT>& sm, const uint16_t* const (&a_rows)[MT / 32],
                                             const uint16_t* const (&b_rows)[4], int kt, int nk, int arow0,
-                                            const int (&brow)[4], uint4 (&ra)[2][4], uint4 (&rb)[2][4],
-                                            floatx4 (&acc)[4][4]) {
+                                            const int (&brow)[4], uint4 (&ra)[2][MT / 32], uint4 (&rb)[2][4],
+                                            floatx4 (&acc)[MT / 32][4]) {
+    constexpr int MI = MT / 32;
     const int pre = min(kt + 2, nk - 1) * RBK;
     load_slice(a_rows, pre, ra[B]);
     load_slice(b_rows, pre, rb[B]);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_k32<RBK>(sm.a[B], sm.b[B], arow0, brow, 0, acc);
-    mfma_k32<RBK>(sm.a[B], sm.b[B], arow0, brow, 4, acc);
+    mfma_k32<RBK, MI>(sm.a[B], sm.b[B], arow0, brow, 0, acc);
+    mfma_k32<RBK, MI>(sm.a[B], sm.b[B], arow0, brow, 4, acc);
     store_slice(sm.a[B ^ 1], ra[B ^ 1]);
     store_slice(sm.b[B ^ 1], rb[B ^ 1]);
     __syncthreads();
@@ -617,32 +623,33 @@ __device__ __forceinline__ void router_step(RSmem& sm, const uint16_t* const (&a
 
 // Router logits of a large batch on MFMA: logits[t, e] = x[t] . W_r[e] (+ b[e]) for
 // e < E ("Qwen3.5-MoE Model Implementation", MoE routing; "Phase 19: MoE - gpt-oss-20b",
-// Router).
+// Router).  Waves in a 2 x 2 grid of (MT / 2) x 64 tiles.
+template <int MT>
 __global__ __launch_bounds__(kRThreads, 2) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                                    const uint16_t* __restrict__ w_router,
                                                                    const float* __restrict__ b_router,
                                                                    int T, int d, int E, int n_ntiles,
                                                                    float* __restrict__ logits, int ld) {
-    __shared__ RSmem sm;
-    const int m0 = (blockIdx.x / n_ntiles) * BM;
+    constexpr int NA = MT / 32, MI = MT / 32, WM = MT / 2;
+    __shared__ RSmem<MT> sm;
+    const int m0 = (blockIdx.x / n_ntiles) * MT;
     const int n0 = (blockIdx.x % n_ntiles) * RBN;
     const int r0 = threadIdx.x >> 3;
-    const uint16_t* a_rows[4];
+    const uint16_t* a_rows[NA];
     const uint16_t* b_rows[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        a_rows[i] = x + (size_t)min(m0 + r0 + 32 * i, T - 1) * d;
-        b_rows[i] = w_router + (size_t)min(n0 + r0 + 32 * i, E - 1) * d;
-    }
+    for (int i = 0; i < NA; ++i) a_rows[i] = x + (size_t)min(m0 + r0 + 32 * i, T - 1) * d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b_rows[i] = w_router + (size_t)min(n0 + r0 + 32 * i, E - 1) * d;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int wm = wave >> 1, wn = wave & 1;
     const int brow[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
-    floatx4 acc[4][4];
+    floatx4 acc[MI][4];
     zero(acc);
-    const uint16_t* const (&ar)[4] = a_rows;
+    const uint16_t* const (&ar)[NA] = a_rows;
     const uint16_t* const (&br)[4] = b_rows;
     const int nk = d / RBK;
-    uint4 ra[2][4], rb[2][4];
+    uint4 ra[2][NA], rb[2][4];
     load_slice(ar, 0, ra[0]);
     load_slice(br, 0, rb[0]);
     load_slice(ar, min(1, nk - 1) * RBK, ra[1]);
@@ -652,20 +659,20 @@ __global__ __launch_bounds__(kRThreads, 2) void router_mfma_kernel(const uint16_
     __syncthreads();
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
-        router_step<0>(sm, ar, br, kt, nk, wm * 64, brow, ra, rb, acc);
-        router_step<1>(sm, ar, br, kt + 1, nk, wm * 64, brow, ra, rb, acc);
+        router_step<0, MT>(sm, ar, br, kt, nk, wm * WM, brow, ra, rb, acc);
+        router_step<1, MT>(sm, ar, br, kt + 1, nk, wm * WM, brow, ra, rb, acc);
     }
-    if (kt < nk) router_step<0>(sm, ar, br, kt, nk, wm * 64, brow, ra, rb, acc);
+    if (kt < nk) router_step<0, MT>(sm, ar, br, kt, nk, wm * WM, brow, ra, rb, acc);
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
         const int n = n0 + wn * 64 + ni * 16 + (lane & 15);
         if (n >= E) continue;
         const float bias = b_router ? b_router[n] : 0.0f;
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int m = m0 + wm * 64 + mi * 16 + 4 * (lane >> 4) + i;
+                const int m = m0 + wm * WM + mi * 16 + 4 * (lane >> 4) + i;
                 if (m < T) logits[(size_t)m * ld + n] = acc[mi][ni][i] + bias;
             }
     }
@@ -676,10 +683,17 @@ __global__ __launch_bounds__(kRThreads, 2) void router_mfma_kernel(const uint16_
 hipError_t launch_router_mfma(const moe_layer& L, const void* x, int T, float* logits, int ld,
                               hipStream_t s) {
     const int nn = (L.n_expert + RBN - 1) / RBN;
-    const int nm = (T + BM - 1) / BM;
-    router_mfma_kernel<<<nm * nn, kRThreads, 0, s>>>(static_cast<const uint16_t*>(x),
-                                                     static_cast<const uint16_t*>(L.w_router), L.b_router,
-                                                     T, L.d, L.n_expert, nn, logits, ld);
+    // The tallest token tile that still makes one block per CU (256 CUs), else 32 rows.
+    const auto blocks = [&](int mt) { return ((T + mt - 1) / mt) * nn; };
+    const int mt = blocks(128) >= 256 ? 128 : blocks(64) >= 256 ? 64 : 32;
+    const auto* xs = static_cast<const uint16_t*>(x);
+    const auto* wr = static_cast<const uint16_t*>(L.w_router);
+    if (mt == 128)
+        router_mfma_kernel<128><<<blocks(128), kRThreads, 0, s>>>(xs, wr, L.b_router, T, L.d, L.n_expert, nn, logits, ld);
+    else if (mt == 64)
+        router_mfma_kernel<64><<<blocks(64), kRThreads, 0, s>>>(xs, wr, L.b_router, T, L.d, L.n_expert, nn, logits, ld);
+    else
+        router_mfma_kernel<32><<<blocks(32), kRThreads, 0, s>>>(xs, wr, L.b_router, T, L.d, L.n_expert, nn, logits, ld);
     return hipGetLastError();
 }
 
