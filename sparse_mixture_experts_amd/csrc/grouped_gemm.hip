@@ -32,8 +32,10 @@
 // kernel's long K loop.  Epilogues go through LDS so that every lane
 // stores whole 16-byte chunks of output rows.
 //
-// The router GEMM (128 tokens x 128 experts per block) keeps a 4-wave, register-staged
-// pipeline: with E = 256 experts a 256-wide tile would leave too few blocks.
+// The router GEMM (128, 64 or 32 tokens x 128 experts per block) keeps a 4-wave,
+// register-staged pipeline: with E = 256 experts a 256-wide tile would leave too few
+// blocks.  MXFP4 expert weights take the same loops with their B slices expanded from FP4
+// blocks into the ring (see grouped_mainloop_mx).
 #include "common.h"
 #include "internal.h"
 #include "mfma_dev.h"
