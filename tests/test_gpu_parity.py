@@ -209,6 +209,20 @@ def test_k_equals_E_dense_case():
     assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "f32", "k=E")
 
 
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_k_equals_E_bf16(path):
+    # Every expert selected by every token (k = E): each group holds all T rows, several
+    # M-tiles per expert on the grouped path; the shared expert on top.
+    L = dict(layer_arrays("qwen", d=256, n_expert=16, k=16, ff=128, shared_ff=64))
+    x = synth.make_tokens(L, 150, seed=14)
+    lay = _custom(L).with_path(path)
+    idx, _, _ = moe_mod().route(lay, xdev(x))
+    ridx, _, _ = oracle.route(L, x)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    y = moe_mod().forward(lay, xdev(x))
+    assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "bf16", f"k=E {path}")
+
+
 def test_one_expert_takes_every_token():
     L = dict(layer_arrays("qwen", d=256, n_expert=32, ff=128, shared_ff=64))
     L["w_router"] = np.zeros_like(L["w_router"])
