@@ -66,8 +66,9 @@ def log(*a):
 
 CALIB_BYTES = 256 << 20
 # Kernels of the timed stage (name prefixes; the grouped down kernel writes fp32 rows there).
-STAGE_KERNELS = ("expert_up_gemv_kernel", "expert_down_gemv_kernel", "plan_kernel",
-                 "gg_up_kernel", "gg_down_kernel<float", "splitk_reduce_kernel<float")
+STAGE_KERNELS = ("expert_up_gemv_kernel", "expert_down_gemv_kernel", "expert_up_gemv_mx_kernel",
+                 "expert_down_gemv_mx_kernel", "plan_kernel", "gg_up_kernel", "gg_down_kernel<float",
+                 "splitk_reduce_kernel<float")
 
 
 def kernel_source_hash():
