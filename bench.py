@@ -49,7 +49,8 @@ WORKLOADS = {
     "tiny_f32_t16": ("tiny_f32", 16),
 }
 DEFAULT = "qwen_decode_t64"
-DEFAULT_SWEEP = ["qwen_decode_t1", "qwen_decode_t8", "qwen_prefill_t8192"]
+DEFAULT_SWEEP = ["qwen_decode_t1", "qwen_decode_t8", "qwen_prefill_t8192", "gptoss_t1", "gptoss_t4096",
+                 "mixtral_t16", "mixtral_t16384"]
 
 
 def log(*a):
