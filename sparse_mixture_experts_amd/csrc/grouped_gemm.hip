@@ -509,10 +509,11 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
             const int n = n0 + h * kCols + c * kPer;
             if (m0 + ml < g.n && n < a.d) {
                 TY* dst = static_cast<TY*>(a.y) + ((size_t)ks * a.rows + g.row0 + m0 + ml) * a.d + n;
-                uint4 v;
-                if constexpr (kHalf) v = *reinterpret_cast<const uint4*>(sm.down_h + ml * kStride + c * kPer);
-                else v = *reinterpret_cast<const uint4*>(sm.down_f + ml * kStride + c * kPer);
-                *reinterpret_cast<uint4*>(dst) = v;
+                u32x4_t v;
+                if constexpr (kHalf) v = *reinterpret_cast<const u32x4_t*>(sm.down_h + ml * kStride + c * kPer);
+                else v = *reinterpret_cast<const u32x4_t*>(sm.down_f + ml * kStride + c * kPer);
+                // Streamed out: the rows are read again only by a later launch.
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
             }
         }
         if (h + 1 < kHalves) __syncthreads();
