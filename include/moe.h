@@ -112,9 +112,9 @@ typedef struct moe_layer {
     const void* w_gate;       /* SWIGLU: [E, ff, d]                                    */
     const void* w_up;         /* SWIGLU: [E, ff, d]                                    */
     const void* w_gate_up;    /* SWIGLU_OAI: [E, 2*ff, d], rows gate,up interleaved    */
-    const void* b_gate_up;    /* SWIGLU_OAI: [E, 2*ff]                                 */
+    const void* b_gate_up;    /* SWIGLU_OAI: [E, 2*ff]; must be NULL for SWIGLU        */
     const void* w_down;       /* [E, d, ff]                                            */
-    const void* b_down;       /* SWIGLU_OAI: [E, d] or NULL                            */
+    const void* b_down;       /* SWIGLU_OAI: [E, d] or NULL; must be NULL for SWIGLU   */
     const void* ws_gate;      /* shared expert: [shared_ff, d]                         */
     const void* ws_up;        /* shared expert: [shared_ff, d]                         */
     const void* ws_down;      /* shared expert: [d, shared_ff]                         */

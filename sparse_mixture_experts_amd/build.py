@@ -41,23 +41,38 @@ def _run(cmd):
     return r.stdout
 
 
-def build(verbose: bool = False, jobs: int | None = None, extra_flags=()) -> str:
+def build(verbose: bool = False, jobs: int | None = None, extra_flags=(), only=None) -> str:
+    """Compile every csrc/*.hip (or, with ``only``, just the named sources, reusing the
+    other objects from the last build) and link libsmoe.so.  Objects whose source no
+    longer exists are deleted."""
     srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
     out_dir = os.path.join(HERE, "_build")
     os.makedirs(out_dir, exist_ok=True)
     cc = hipcc()
-    objs = []
+
+    def obj_of(src):
+        return os.path.join(out_dir, os.path.basename(src)[:-4] + ".o")
+
+    wanted = {obj_of(s) for s in srcs}
+    for stale in glob.glob(os.path.join(out_dir, "*.o")):
+        if stale not in wanted:
+            os.remove(stale)
 
     def compile_one(src):
-        obj = os.path.join(out_dir, os.path.basename(src)[:-4] + ".o")
+        obj = obj_of(src)
         log = _run([cc, *HIP_FLAGS, *extra_flags, "-c", src, "-o", obj])
         if verbose and log.strip():
             print(log)
         return obj
 
+    todo = srcs
+    if only:
+        names = {n if n.endswith(".hip") else n + ".hip" for n in only}
+        todo = [s for s in srcs if os.path.basename(s) in names or not os.path.exists(obj_of(s))]
     jobs = jobs or min(16, os.cpu_count() or 4)
     with ThreadPoolExecutor(jobs) as pool:
-        objs = list(pool.map(compile_one, srcs))
+        list(pool.map(compile_one, todo))
+    objs = [obj_of(s) for s in srcs]
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs])
     os.replace(tmp, LIB)
@@ -67,4 +82,7 @@ def build(verbose: bool = False, jobs: int | None = None, extra_flags=()) -> str
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
+    # python -m sparse_mixture_experts_amd.build [-v] [source.hip ...]: with source names,
+    # recompile only those and relink.
+    names = [a for a in sys.argv[1:] if a != "-v"]
+    build(verbose="-v" in sys.argv, only=names or None)

@@ -93,6 +93,9 @@ moe_status check_layer(const moe_layer* L) {
         return MOE_ERR_ARG;
     if (!L->w_router || !L->w_down) return MOE_ERR_ARG;
     if (L->act == MOE_ACT_SWIGLU && (!L->w_gate || !L->w_up)) return MOE_ERR_ARG;
+    // Expert biases belong to the clamped variant only; a plain SwiGLU layer that carried
+    // one would see it on some kernel paths and not on others.
+    if (L->act == MOE_ACT_SWIGLU && (L->b_gate_up || L->b_down)) return MOE_ERR_ARG;
     if (L->act == MOE_ACT_SWIGLU_OAI && (!L->w_gate_up || !L->b_gate_up)) return MOE_ERR_ARG;
     if (L->shared_ff > 0 && (!L->ws_gate || !L->ws_up || !L->ws_down || !L->ws_gate_inp))
         return MOE_ERR_ARG;
@@ -282,7 +285,11 @@ moe_status moe_workspace_size(const moe_layer* L, int32_t T, size_t* bytes) {
     if (st != MOE_OK) return st;
     if ((st = check_tokens(T)) != MOE_OK) return st;
     if (!bytes) return MOE_ERR_ARG;
-    *bytes = layout_for(*L, T).total;
+    // The split-K planes exist only up to kDecodeMaxT tokens, so the layout of a smaller
+    // batch can be larger: the size covers every batch of at most T tokens.
+    const size_t own = layout_for(*L, T).total;
+    const size_t small = layout_for(*L, T < kDecodeMaxT ? T : kDecodeMaxT).total;
+    *bytes = own > small ? own : small;
     return MOE_OK;
 }
 
@@ -410,3 +417,4 @@ moe_status moe_forward_shell(const moe_layer* L, const void* h, int32_t T, const
 }
 
 }  // extern "C"
+

@@ -117,6 +117,32 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+def _want(t, name, dtype, shape=None, numel=None):
+    """Reject a tensor argument the kernels would read or write out of bounds: wrong
+    dtype, shape or element count, a non-contiguous view, or memory that is not on the
+    current HIP device."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {numel} needed")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda" or t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name}: on {t.device}, expected the current device "
+                         f"cuda:{torch.cuda.current_device()}")
+    return t
+
+
+def _want_ws(ws, layer, T):
+    torch = _torch()
+    return _want(ws, "ws", torch.uint8, numel=workspace_size(layer, T) if T > 0 else None)
+
+
 def _stream():
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -194,7 +220,8 @@ def route(layer: Layer, x, ws=None):
     """(topk_idx int32 [T,k], topk_w fp32 [T,k], shared_gate fp32 [T] or None)."""
     torch = _torch()
     T = x.shape[0]
-    ws = workspace(layer, T, x.device) if ws is None else ws
+    _want(x, "x", layer.torch_dtype, (T, layer.d))
+    ws = workspace(layer, T, x.device) if ws is None else _want_ws(ws, layer, T)
     idx = torch.empty((T, layer.k), dtype=torch.int32, device=x.device)
     w = torch.empty((T, layer.k), dtype=torch.float32, device=x.device)
     sg = torch.empty(T, dtype=torch.float32, device=x.device) if layer.shared_ff else None
@@ -207,13 +234,14 @@ def permute(topk_idx, n_expert: int):
     """(expert_offsets [E+1], perm_token [T*k], perm_inv [T*k]) int32."""
     torch = _torch()
     T, k = topk_idx.shape
+    _want(topk_idx, "topk_idx", torch.int32, (T, k))
     n = ctypes.c_size_t(0)
     _check(lib().moe_permute_workspace_size(T, k, n_expert, ctypes.byref(n)), "moe_permute_workspace_size")
     ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=topk_idx.device)
     off = torch.empty(n_expert + 1, dtype=torch.int32, device=topk_idx.device)
     pt = torch.empty(T * k, dtype=torch.int32, device=topk_idx.device)
     pi = torch.empty(T * k, dtype=torch.int32, device=topk_idx.device)
-    _check(lib().moe_permute(_ptr(topk_idx.contiguous()), T, k, n_expert, _ptr(off), _ptr(pt), _ptr(pi),
+    _check(lib().moe_permute(_ptr(topk_idx), T, k, n_expert, _ptr(off), _ptr(pt), _ptr(pi),
                              _ptr(ws), ws.numel(), _stream()), "moe_permute")
     return off, pt, pi
 
@@ -223,7 +251,10 @@ def expert_ffn(layer: Layer, x, expert_offsets, perm_token, ws=None):
     torch = _torch()
     T = x.shape[0]
     rows = T * layer.k + (T if layer.shared_ff else 0)
-    ws = workspace(layer, T, x.device) if ws is None else ws
+    _want(x, "x", layer.torch_dtype, (T, layer.d))
+    _want(expert_offsets, "expert_offsets", torch.int32, (layer.n_expert + 1,))
+    _want(perm_token, "perm_token", torch.int32, (T * layer.k,))
+    ws = workspace(layer, T, x.device) if ws is None else _want_ws(ws, layer, T)
     y = torch.empty((rows, layer.d), dtype=torch.float32, device=x.device)
     _check(lib().moe_expert_ffn(layer.ref(), _ptr(x), T, _ptr(expert_offsets), _ptr(perm_token),
                                 _ptr(y), _ptr(ws), ws.numel(), _stream()), "moe_expert_ffn")
@@ -233,6 +264,12 @@ def expert_ffn(layer: Layer, x, expert_offsets, perm_token, ws=None):
 def combine(layer: Layer, y_perm, perm_inv, topk_w, shared_gate):
     torch = _torch()
     T = topk_w.shape[0]
+    rows = T * layer.k + (T if layer.shared_ff else 0)
+    _want(topk_w, "topk_w", torch.float32, (T, layer.k))
+    _want(y_perm, "y_perm", torch.float32, (rows, layer.d))
+    _want(perm_inv, "perm_inv", torch.int32, (T * layer.k,))
+    if shared_gate is not None:
+        _want(shared_gate, "shared_gate", torch.float32, (T,))
     y = torch.empty((T, layer.d), dtype=layer.torch_dtype, device=topk_w.device)
     _check(lib().moe_combine(layer.ref(), _ptr(y_perm), _ptr(perm_inv), _ptr(topk_w), _ptr(shared_gate),
                              T, _ptr(y), _stream()), "moe_combine")
@@ -243,8 +280,10 @@ def forward(layer: Layer, x, ws=None, out=None):
     """The whole layer: y [T, d] in the layer dtype."""
     torch = _torch()
     T = x.shape[0]
-    ws = workspace(layer, T, x.device) if ws is None else ws
+    _want(x, "x", layer.torch_dtype, (T, layer.d))
+    ws = workspace(layer, T, x.device) if ws is None else _want_ws(ws, layer, T)
     y = torch.empty((T, layer.d), dtype=layer.torch_dtype, device=x.device) if out is None else out
+    _want(y, "out", layer.torch_dtype, (T, layer.d))
     _check(lib().moe_forward(layer.ref(), _ptr(x), T, _ptr(y), _ptr(ws), ws.numel(), _stream()),
            "moe_forward")
     return y
@@ -255,8 +294,12 @@ def forward_shell(layer: Layer, h, norm_w, eps: float = 1e-5, ws=None, out=None)
     itself (in-place residual update)."""
     torch = _torch()
     T = h.shape[0]
-    ws = workspace(layer, T, h.device) if ws is None else ws
+    _want(h, "h", layer.torch_dtype, (T, layer.d))
+    _want(norm_w, "norm_w", layer.torch_dtype, (layer.d,))
+    ws = workspace(layer, T, h.device) if ws is None else _want_ws(ws, layer, T)
     y = torch.empty((T, layer.d), dtype=layer.torch_dtype, device=h.device) if out is None else out
+    _want(y, "out", layer.torch_dtype, (T, layer.d))
     _check(lib().moe_forward_shell(layer.ref(), _ptr(h), T, _ptr(norm_w), float(eps), _ptr(y), _ptr(ws),
                                    ws.numel(), _stream()), "moe_forward_shell")
     return y
+

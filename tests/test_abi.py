@@ -12,6 +12,24 @@ from sparse_mixture_experts_amd import moe
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FAKE = 0x10000  # 64 KiB-aligned address; the library must never touch it in these tests
 
+# These tests call real entry points with fake device addresses, which every check must
+# reject before any launch.  On a machine where a GPU can be reached (/dev/kfd exists)
+# the module runs in a child process that sees no GPU (tests/conftest.py deselects the
+# tests here and keeps test_in_child_without_gpu), so a regressed check returns
+# MOE_ERR_DEVICE there instead of launching a kernel on a fake address.
+CHILD_ENV = "SMOE_ABI_CHILD"
+
+
+def test_in_child_without_gpu():
+    import subprocess
+    import sys
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="", ROCR_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
+    env[CHILD_ENV] = "1"
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", __file__],
+                       cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True,
+                       timeout=600)
+    assert r.returncode == 0, r.stdout[-4000:]
+
 
 def header_functions():
     src = open(os.path.join(ROOT, "include", "moe.h")).read()
@@ -195,9 +213,28 @@ def test_mxfp4_layer_checks(lib):
     assert ws_size(lib, fake_layer(**dict(mx, expert_format=7)), 4)[0] == moe.MOE_ERR_ARG
     assert ws_size(lib, fake_layer(**dict(mx, reserved0=1)), 4)[0] == moe.MOE_ERR_ARG
     assert ws_size(lib, fake_layer(**dict(mx, dtype=moe.MOE_F32)), 4)[0] == moe.MOE_ERR_UNSUPPORTED
-    assert ws_size(lib, fake_layer(**dict(mx, act=moe.MOE_ACT_SWIGLU, w_gate=FAKE, w_up=FAKE)), 4)[0] \
-        == moe.MOE_ERR_UNSUPPORTED
+    assert ws_size(lib, fake_layer(**dict(mx, act=moe.MOE_ACT_SWIGLU, w_gate=FAKE, w_up=FAKE, b_gate_up=None)),
+                   4)[0] == moe.MOE_ERR_UNSUPPORTED
     assert ws_size(lib, fake_layer(**dict(mx, path=moe.MOE_PATH_GROUPED)), 4)[0] == moe.MOE_OK
     assert ws_size(lib, fake_layer(**dict(mx, d=8192)), 4)[0] == moe.MOE_ERR_UNSUPPORTED  # K > 4096
     sh = dict(mx, shared_ff=64, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, ws_gate_inp=FAKE)
     assert ws_size(lib, fake_layer(**sh), 4)[0] == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_swiglu_rejects_expert_biases(lib):
+    # Expert biases belong to the clamped variant; a plain SwiGLU layer carrying one is an
+    # argument error, whichever kernel path the batch would take.
+    for field in ("b_down", "b_gate_up"):
+        s = fake_layer(**{field: FAKE})
+        assert fwd(lib, s) == moe.MOE_ERR_ARG, field
+        assert ws_size(lib, s, 4)[0] == moe.MOE_ERR_ARG, field
+        assert fwd(lib, fake_layer(path=moe.MOE_PATH_GROUPED, **{field: FAKE}), T=1000) == moe.MOE_ERR_ARG
+
+
+def test_workspace_size_covers_smaller_batches(lib):
+    # One size query covers every batch of at most T tokens (the decode-only split-K
+    # planes make some small batches' layouts larger than a slightly bigger batch's).
+    s = fake_layer(d=2048, n_expert=256, k=8)
+    sizes = [ws_size(lib, s, T)[1] for T in range(1, 200)]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:]))
+
