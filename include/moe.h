@@ -28,7 +28,8 @@
  *    the call returns without enqueuing work and without writing any output.
  *    T == 0 is a no-op that returns MOE_OK.
  *  - Results are deterministic: no floating-point atomics, fixed reduction orders.
- *  - The functions hold no state and may be called from several host threads.
+ *  - The functions hold no state and may be called from several host threads
+ *    (moe_forward_noalloc shares one scratch array per GPU; see there).
  */
 #ifndef SMOE_MOE_H
 #define SMOE_MOE_H
@@ -207,6 +208,25 @@ moe_status moe_forward(const moe_layer* L, const void* x, int32_t T, void* y, vo
  * Errors as moe_forward; MOE_ERR_ARG for a negative or non-finite eps. */
 moe_status moe_forward_shell(const moe_layer* L, const void* h, int32_t T, const void* norm_w, float eps,
                              void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the library's fixed device scratch array used by moe_forward_noalloc (one
+ * array per GPU, allocated when the library's code is loaded on that GPU and held until
+ * the process ends). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_forward without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same layer, same kernels and same results as moe_forward; the workspace is the fixed
+ * array above.  The call itself allocates and frees nothing.
+ *   x [T, d], y [T, d] in L->dtype; y must not alias x.
+ * Errors as moe_forward, plus MOE_ERR_WORKSPACE when the batch needs more workspace than
+ * MOE_NOALLOC_SCRATCH_BYTES (moe_workspace_size(L, T) reports the need; 64 MiB covers
+ * every batch of up to 64 tokens of the Qwen-, gpt-oss- and Mixtral-shaped layers), and
+ * MOE_ERR_DEVICE when the array's device address cannot be obtained.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (on different streams, or from several host threads without ordering) race and give
+ * undefined results.  Calls ordered on one stream are safe. */
+moe_status moe_forward_noalloc(const moe_layer* L, const void* x, int32_t T, void* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 namespace smoe {
@@ -418,3 +420,52 @@ moe_status moe_forward_shell(const moe_layer* L, const void* h, int32_t T, const
 
 }  // extern "C"
 
+// ------------------------------------------------------------------------------------
+// Allocation-free forward: the workspace is a fixed device array of this library.
+// ------------------------------------------------------------------------------------
+namespace smoe {
+namespace {
+
+// One copy per GPU, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel or a copy (on the host that name is only a stand-in); it uses the
+// device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device, looked up once per device
+// (with that device current); null if the lookup fails.
+void* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+}  // namespace smoe
+
+extern "C" moe_status moe_forward_noalloc(const moe_layer* L, const void* x, int32_t T, void* y, void* stream) {
+    moe_status st = check_layer(L);
+    if (st != MOE_OK) return st;
+    if ((st = check_tokens(T)) != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (!x || !y) return MOE_ERR_ARG;
+    if (x == y) return MOE_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16)) return MOE_ERR_UNSUPPORTED;
+    const Layout o = layout_for(*L, T);
+    if (o.total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    void* ws = scratch_on_current_device();
+    if (!ws) return MOE_ERR_DEVICE;
+    // Every workspace region is written before it is read within one forward (no kernel
+    // expects zeroed memory), so what an earlier call left in the array does not matter.
+    return forward_body(L, x, T, nullptr, y, ws, o, static_cast<hipStream_t>(stream));
+}

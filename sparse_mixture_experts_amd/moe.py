@@ -49,7 +49,9 @@ POINTER_FIELDS = [f for f, t in MoeLayer._fields_ if t is _P]
 ABI_VERSION = 3
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_forward_shell"]
+           "moe_forward", "moe_forward_shell", "moe_forward_noalloc"]
+# Bytes of the library's fixed scratch array behind moe_forward_noalloc.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeError(RuntimeError):
@@ -91,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.argtypes = [pl, vp, i32, vp, vp, sz, vp]
         L.moe_forward_shell.restype = i32
         L.moe_forward_shell.argtypes = [pl, vp, i32, vp, ctypes.c_float, vp, vp, sz, vp]
+        L.moe_forward_noalloc.restype = i32
+        L.moe_forward_noalloc.argtypes = [pl, vp, i32, vp, vp]
         if L.moe_abi_version() != ABI_VERSION:
             raise RuntimeError("libsmoe.so ABI version mismatch")
         _lib = L
@@ -303,3 +307,16 @@ def forward_shell(layer: Layer, h, norm_w, eps: float = 1e-5, ws=None, out=None)
                                    ws.numel(), _stream()), "moe_forward_shell")
     return y
 
+
+def forward_noalloc(layer: Layer, x, out=None):
+    """moe_forward_noalloc: the whole layer with the library's fixed scratch array as the
+    workspace (no workspace argument, nothing allocated by the call beyond ``out`` when
+    it is not given).  Raises MoeError (MOE_ERR_WORKSPACE) when the batch needs more than
+    NOALLOC_SCRATCH_BYTES of workspace."""
+    torch = _torch()
+    T = x.shape[0]
+    _want(x, "x", layer.torch_dtype, (T, layer.d))
+    y = torch.empty((T, layer.d), dtype=layer.torch_dtype, device=x.device) if out is None else out
+    _want(y, "out", layer.torch_dtype, (T, layer.d))
+    _check(lib().moe_forward_noalloc(layer.ref(), _ptr(x), T, _ptr(y), _stream()), "moe_forward_noalloc")
+    return y

@@ -46,7 +46,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -231,6 +231,25 @@ def test_swiglu_rejects_expert_biases(lib):
         assert fwd(lib, fake_layer(path=moe.MOE_PATH_GROUPED, **{field: FAKE}), T=1000) == moe.MOE_ERR_ARG
 
 
+def test_noalloc_argument_errors(lib):
+    # Every check of moe_forward_noalloc runs before the scratch array's address is looked
+    # up or anything is enqueued.
+    s = fake_layer()
+    L = ctypes.byref(s)
+    assert lib.moe_forward_noalloc(L, FAKE, 0, FAKE * 2, None) == moe.MOE_OK
+    assert lib.moe_forward_noalloc(L, FAKE, -1, FAKE * 2, None) == moe.MOE_ERR_ARG
+    assert lib.moe_forward_noalloc(L, None, 4, FAKE * 2, None) == moe.MOE_ERR_ARG
+    assert lib.moe_forward_noalloc(L, FAKE, 4, None, None) == moe.MOE_ERR_ARG
+    assert lib.moe_forward_noalloc(L, FAKE, 4, FAKE, None) == moe.MOE_ERR_ARG       # y aliases x
+    assert lib.moe_forward_noalloc(L, FAKE + 8, 4, FAKE * 2, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_forward_noalloc(None, FAKE, 4, FAKE * 2, None) == moe.MOE_ERR_ARG
+    assert lib.moe_forward_noalloc(ctypes.byref(fake_layer(k=0)), FAKE, 4, FAKE * 2, None) == moe.MOE_ERR_ARG
+    # A batch whose workspace exceeds the scratch array is refused.
+    big = 1 << 16
+    assert ws_size(lib, s, big)[1] > moe.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(L, FAKE, big, FAKE * 2, None) == moe.MOE_ERR_WORKSPACE
+
+
 def test_workspace_size_covers_smaller_batches(lib):
     # One size query covers every batch of at most T tokens (the decode-only split-K
     # planes make some small batches' layouts larger than a slightly bigger batch's).
@@ -238,3 +257,9 @@ def test_workspace_size_covers_smaller_batches(lib):
     sizes = [ws_size(lib, s, T)[1] for T in range(1, 200)]
     assert all(a <= b for a, b in zip(sizes, sizes[1:]))
 
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m, "MOE_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == moe.NOALLOC_SCRATCH_BYTES
