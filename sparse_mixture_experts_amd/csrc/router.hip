@@ -17,15 +17,24 @@ namespace smoe {
 namespace {
 
 // NR router rows per wave (rows 0..E-1 are experts, row E the shared gate vector),
-// looping over a chunk of tokens.  Writes logits[t * ld + row].
+// looping over a chunk of tokens.  Writes logits[t * ld + row].  The 1-D grid holds
+// n_groups row groups (4 waves each) times n_chunks token chunks, ordered so that every
+// token chunk of a row group runs on the same XCD (blocks go to the 8 XCDs round-robin by
+// id): each XCD then fetches its row groups' router rows into its own L2 once, instead of
+// every XCD fetching the whole router matrix.
+constexpr int kRouterXcds = 8;
+
 template <int KB, typename TT, int NR>
 __global__ __launch_bounds__(256) void router_gemv_kernel(
     const typename TT::storage* __restrict__ x, const typename TT::storage* __restrict__ w_router,
     const float* __restrict__ b_router, const typename TT::storage* __restrict__ w_sg, int T, int d,
-    int E, int n_rows, int tok_chunk, float* __restrict__ logits, int ld) {
-    const int row0 = (blockIdx.x * 4 + wave_id()) * NR;
+    int E, int n_rows, int tok_chunk, int n_chunks, float* __restrict__ logits, int ld) {
+    const int xcd = blockIdx.x % kRouterXcds, slot = blockIdx.x / kRouterXcds;
+    const int group = xcd + kRouterXcds * (slot / n_chunks), chunk = slot % n_chunks;
+    const int row0 = (group * 4 + wave_id()) * NR;
     if (row0 >= n_rows) return;
-    const int t0 = blockIdx.y * tok_chunk;
+    const int t0 = chunk * tok_chunk;
+    if (t0 >= T) return;
     router_rows_wave<KB, TT, NR>(x, w_router, b_router, w_sg, T, d, E, n_rows, row0, t0, min(T, t0 + tok_chunk),
                              logits, ld);
 }
@@ -171,7 +180,11 @@ hipError_t launch_router_t(const moe_layer& L, const void* x, int T, float* logi
     const int tok_chunk = T <= 256 ? kRouterNT : 64;
     const bool one_row = T <= 64;
     const int nr = one_row ? 1 : kRouterNR;
-    dim3 grid((n_rows + 4 * nr - 1) / (4 * nr), (T + tok_chunk - 1) / tok_chunk);
+    const int n_groups = (n_rows + 4 * nr - 1) / (4 * nr);
+    const int n_chunks = (T + tok_chunk - 1) / tok_chunk;
+    dim3 grid(n_groups, n_chunks);  // the normalising variant's 2-D grid
+    // The plain variant's 1-D grid: whole rounds of kRouterXcds row groups per chunk set.
+    const unsigned flat = (unsigned)(kRouterXcds * ((n_groups + kRouterXcds - 1) / kRouterXcds) * n_chunks);
     const S* xs = static_cast<const S*>(x);
     const S* wr = static_cast<const S*>(L.w_router);
     // The normalising variant works on chunks of kRouterNT tokens held in LDS.
@@ -187,9 +200,9 @@ hipError_t launch_router_t(const moe_layer& L, const void* x, int T, float* logi
                 xs, static_cast<const S*>(norm->w), norm->eps, static_cast<S*>(norm->xn), wr,   \
                 L.b_router, wsg, T, L.d, L.n_expert, n_rows, logits, ld);                     \
         else                                                                                   \
-            router_gemv_kernel<KB, TT, NR><<<grid, 256, 0, s>>>(xs, wr, L.b_router, wsg, T,     \
+            router_gemv_kernel<KB, TT, NR><<<flat, 256, 0, s>>>(xs, wr, L.b_router, wsg, T,     \
                                                                 L.d, L.n_expert, n_rows,       \
-                                                                tok_chunk, logits, ld);        \
+                                                                tok_chunk, n_chunks, logits, ld); \
     } while (0)
 #define SMOE_ROUTER_CASE(KB)                                                                   \
     case KB:                                                                                   \
