@@ -12,8 +12,8 @@
  * Experts (Mixtral)") and "Phase 19: MoE - gpt-oss-20b" (section 2, Router and
  * Experts: top-k before softmax with a router bias; interleaved, clamped
  * (up + 1) * gate * sigmoid(alpha * gate) experts with biases).  The grouped
- * evaluation (tokens grouped by expert, gathered, projected, scattered back) is the
- * one described on "Engine" (Cherenkov), section "Prefill".
+ * evaluation (each expert run once over the rows routed to it, the results returned to
+ * their tokens) follows "Engine" (Cherenkov), section "Prefill".
  *
  * Conventions (every entry point):
  *  - Every pointer argument and every pointer inside moe_layer is DEVICE memory
@@ -152,8 +152,8 @@ moe_status moe_route(const moe_layer* L, const void* x, int32_t T, int32_t* topk
 /* Workspace bytes needed by moe_permute. */
 moe_status moe_permute_workspace_size(int32_t T, int32_t k, int32_t E, size_t* bytes);
 
-/* Group the T*k (token, slot) pairs by expert ("Engine", Prefill: tokens grouped by
- * expert).
+/* Reorder the T*k (token, slot) pairs so that each expert's rows are contiguous
+ * ("Engine", section "Prefill").
  *   topk_idx        [T, k] int32 in, entries in [0, E), distinct within a row
  *   expert_offsets  [E+1] int32 out: exclusive prefix sum of per-expert counts
  *   perm_token      [T*k] int32 out: token of grouped row r (expert-major rows, tokens

@@ -26,10 +26,10 @@ The passages followed:
 * "Llama Forward Pass", section "Key Operations", RMSNorm, and "Qwen3.5-MoE Model
   Implementation", section "Architecture" (post-attention norm -> MoE FFN -> residual):
   the layer shell around the block (``moe_shell``).
-* "Engine" (Cherenkov), section "Prefill": tokens grouped by expert, gathered,
-  projected and scattered back -- the grouped evaluation below; section "Address
-  tables": the union of the experts a batch selects, with a zero weight where a row did
-  not select an expert.
+* "Engine" (Cherenkov), section "Prefill": each expert evaluated once over the rows
+  routed to it, the results returned to their tokens -- the grouped evaluation below;
+  section "Address tables": the union of the experts a batch selects, with a zero weight
+  where a row did not select an expert.
 
 Readings where the pages are silent (top-k tie-break and output order, router bias
 placement, permutation order inside an expert, ...) are listed with the design notes of
@@ -215,8 +215,8 @@ def shared_expert(L: dict, x) -> np.ndarray | None:
 # ----------------------------------------------------------------------------- grouping
 
 def permute(idx: np.ndarray, E: int):
-    """Expert grouping ("Engine", Prefill: tokens grouped by expert, gathered, projected
-    and scattered back).
+    """Expert grouping ("Engine", section "Prefill": the rows of each expert made
+    contiguous so that the expert is evaluated once over them).
 
     Returns counts[E], offsets[E+1] (exclusive prefix sum of counts), perm_token[T*k]
     (token of each grouped row) and perm_inv[T,k] (grouped row of (t, j)).
@@ -350,7 +350,9 @@ def moe_shell(L: dict, h, norm_w, eps: float) -> np.ndarray:
 def active_union(idx: np.ndarray, w: np.ndarray, E: int):
     """Union of experts selected by any row of a small batch, with the per-row weight
     map that holds zero where a row did not select the expert ("Engine", Address
-    tables).  Returns (experts ascending, wmap[n_active, T])."""
+    tables).  Returns (experts ascending, wmap[n_active, T]).  The page orders its table
+    by residency and then by largest weight; here the experts are in ascending id (a
+    reading: no output depends on the order of the union)."""
     active = np.unique(idx.reshape(-1))
     wmap = np.zeros((active.size, idx.shape[0]))
     pos = {int(e): i for i, e in enumerate(active)}

@@ -1,9 +1,9 @@
 // Grouped GEMMs of the expert FFNs on bf16 MFMA (the prefill path), and the dense router
 // GEMM of large batches.
 //
-// "Engine" (Cherenkov), Prefill: tokens are grouped by expert, gathered, projected and
-// scattered back; its kernels use token tiles, half-precision weights and float
-// accumulation.  Here every group (one expert's rows, or the shared expert over all
+// "Engine" (Cherenkov), section "Prefill", evaluates an expert once over all the tokens
+// routed to it, with token tiles, half-precision weights and float accumulation.  Here
+// every group (one expert's rows, or the shared expert over all
 // tokens) is cut into 128-row M-tiles; a block computes one 128-row tile against one
 // 256-row slice of the expert's weights with v_mfma_f32_16x16x32_bf16 and fp32
 // accumulation.

@@ -1,6 +1,9 @@
-// MXFP4 weight blocks ("Phase 19: MoE - gpt-oss-20b", section 3 and the measured tensor
-// layout): 16-byte blocks of 32 FP4 (E2M1) codes of consecutive inputs, low nibble first,
-// each block sharing one E8M0 scale byte; value = fp4(code) * 2^(scale - 127).
+// MXFP4 weight blocks.  "Phase 19: MoE - gpt-oss-20b", section 3 and the measured tensor
+// layout, gives 16-byte blocks of 32 FP4 codes with one E8M0 scale byte each and
+// value = fp4_lut[code] * 2^(scale - 127).  The page names the code table without printing
+// it and leaves the nibble order open; this library reads the codes as OCP Microscaling
+// E2M1 (0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives) with the low nibble of byte i
+// holding element 2i (readings of the page, not statements of it).
 #pragma once
 
 #include "common.h"

@@ -1,6 +1,6 @@
-// Expert grouping ("Engine" (Cherenkov), Prefill: tokens grouped by expert, gathered,
-// projected, scattered back) as a deterministic counting sort of the T*k (token, slot)
-// pairs by expert, tokens ascending inside each expert.
+// Expert grouping ("Engine" (Cherenkov), section "Prefill"): the T*k (token, slot) pairs
+// are reordered so that each expert's rows are contiguous, by a deterministic counting
+// sort with the tokens in ascending order inside each expert.
 //
 // Tokens are cut into chunks of 64.  For each chunk and expert an LDS 64-bit mask marks
 // the chunk's tokens that selected the expert (LDS atomic OR: order-free, so the
