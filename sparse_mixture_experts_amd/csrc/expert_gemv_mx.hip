@@ -15,6 +15,7 @@
 // grouped path.  Lane l takes blocks l, l+64, ... of a row.
 #include "gemv_items.h"
 #include "mxfp4_dev.h"
+#include "route_dev.h"
 
 namespace smoe {
 namespace {
@@ -62,6 +63,7 @@ constexpr int kMxUpNT = 2;    // group rows per up step
 constexpr int kMxDownNR = 4;  // output dims per down wave
 constexpr int kMxDownNT = 2;  // H rows per down step
 constexpr int kMxNB = 2;      // blocks per lane and row held at once (K up to 4096)
+constexpr int kToken1MxMaxWaves = 16;  // picks per token of the fused one-token kernels
 
 __device__ const uint16_t kZeroBf16 = 0;
 
@@ -276,7 +278,112 @@ __global__ __launch_bounds__(256) void expert_down_gemv_mx_kernel(MxArgs a, cons
     if (i0 < a.d) mx_down_item<NB>(a, g, i0);
 }
 
+// Token index of every hidden row of a one-token batch (hidden row j = pick j).
+__device__ const int32_t kTokenZero[kToken1MxMaxWaves] = {};
+
+// One token: the top-k and the up projection in one kernel.  Grid row j: every wave runs
+// the token's top-k on the router logits and takes pick j (hidden row j); block 0 of the
+// row records the pick for the down kernel.  No planning or grouping launch.
+template <int NB>
+__global__ __launch_bounds__(256) void token1_up_mx_kernel(MxArgs a, const float* __restrict__ logits, int E,
+                                                           int k, int mode, float scale,
+                                                           int32_t* __restrict__ idx, float* __restrict__ w) {
+    const int j = blockIdx.y;
+    const int f0 = (blockIdx.x * 4 + wave_id()) * kMxUnits;
+    if (f0 >= a.ff) return;  // never block 0's first wave, which records the pick
+    int my_i;
+    float my_w;
+    topk_wave(logits, E, k, mode, scale, &my_i, &my_w);
+    if (blockIdx.x == 0 && wave_id() == 0 && lane_id() == j) {
+        idx[j] = my_i;
+        w[j] = my_w;
+    }
+    const int e = __builtin_amdgcn_readlane(my_i, j);
+    MxArgs b = a;
+    b.perm_token = kTokenZero;
+    mx_up_item<NB>(b, Group{min(max(e, 0), E - 1), j, 1, 0}, f0);
+}
+
+// A few tokens: the down projection of every pick (MXFP4 W_d) and the weighted combine
+// in one kernel, as token1_down_combine_kernel does for dense experts.  Block (b, t) owns
+// output dims i0 = 4b .. i0+3 of token t; wave j takes pick j (expert idx[t*k+j], weight
+// w[t*k+j], bf16 hidden row perm_inv[t*k+j], or row j for one token without perm_inv) and
+// leaves its 4 sums (+ down bias) in LDS; 4 threads then add them in pick order.
+template <int NB>
+__global__ __launch_bounds__(kToken1MxMaxWaves * kWave) void token_down_combine_mx_kernel(
+    MxArgs a, const int32_t* __restrict__ idx, const float* __restrict__ w, const int32_t* __restrict__ perm_inv,
+    int E, int k, const uint16_t* __restrict__ residual, uint16_t* __restrict__ y) {
+    constexpr int NR = kMxDownNR, SH = 6 - ilog2(NR);
+    __shared__ float part[kToken1MxMaxWaves][NR];
+    __shared__ float wts[kToken1MxMaxWaves];
+    const int j = wave_id(), lane = lane_id();
+    const int i0 = blockIdx.x * NR, t = blockIdx.y;
+    // A pick without a valid hidden row contributes nothing (its weight is zero).
+    const int p = t * k + j;
+    const int ei = idx[p], r = perm_inv ? perm_inv[p] : j;
+    const bool ok = ei >= 0 && ei < E && r >= 0 && r < a.tk;
+    const int e = ok ? ei : 0, row = ok ? r : 0;
+    const float weight = ok ? w[p] : 0.0f;
+    const int nblk = a.ff / 32;
+    const uint8_t* wrow[NR];
+    const uint8_t* srow[NR];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+        const size_t R = (size_t)e * a.d + min(i0 + q, a.d - 1);
+        wrow[q] = a.w_down + R * nblk * 16;
+        srow[q] = a.s_down + R * nblk;
+    }
+    const uint8_t* const (&wc)[NR] = wrow;
+    const uint8_t* const (&sc)[NR] = srow;
+    uint4 codes[NR][NB];
+    uint32_t sbyte[NR][NB];
+    load_mx_rows<NR, NB>(wc, sc, nblk, codes, sbyte);
+    const int my_r = lane >> SH;
+    const uint16_t* bd = a.b_down ? a.b_down + (size_t)e * a.d + min(i0 + my_r, a.d - 1) : &kZeroBf16;
+    const float bias = bf16_to_f32(*bd);
+    const uint16_t* hr = a.H + (size_t)row * a.hstride;
+    uint4 hq[NB][1][4];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int b = lane + kWave * i;
+        const int bc = b < nblk ? b : 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hq[i][0][q] = ld16(hr + (size_t)bc * 32 + q * 8);
+    }
+    float acc[NR][1] = {};
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int b = lane + kWave * i;
+#pragma unroll
+        for (int q = 0; q < NR; ++q)
+            block_dot_bf16_rows<1>(opaque(codes[q][i]), mx_scale(sbyte[q][i], b, nblk), hq[i], acc[q]);
+    }
+    float v[NR];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) v[q] = acc[q][0];
+    const float sum = wave_reduce_scatter<NR>(v);
+    if ((lane & ((1 << SH) - 1)) == 0) part[j][my_r] = sum + bias;
+    if (lane == 0) wts[j] = weight;
+    __syncthreads();
+    const int tid = threadIdx.x;
+    if (tid < NR && i0 + tid < a.d) {
+        float o = 0.0f;
+        for (int jj = 0; jj < k; ++jj) o = fmaf(wts[jj], part[jj][tid], o);
+        const size_t at = (size_t)t * a.d + i0 + tid;
+        if (residual) o += bf16_to_f32(residual[at]);  // read before y is written: y may alias it
+        y[at] = f32_to_bf16(o);
+    }
+}
+
 int blocks_per_lane(int K) { return (K / 32 + kWave - 1) / kWave; }
+
+MxArgs mx_args(const moe_layer& L, const void* x, int T, const int32_t* perm_token, const Group* groups, float* H,
+               int hstride, float* y_perm) {
+    return MxArgs{static_cast<const uint16_t*>(x), perm_token, groups,
+                  static_cast<const uint8_t*>(L.w_gate_up), L.w_gate_up_scales, static_cast<const uint16_t*>(L.b_gate_up),
+                  static_cast<const uint8_t*>(L.w_down), L.w_down_scales, static_cast<const uint16_t*>(L.b_down),
+                  reinterpret_cast<uint16_t*>(H), y_perm, hstride, T, T * L.k, L.d, L.ff, L.oai_alpha, L.oai_limit};
+}
 
 }  // namespace
 
@@ -288,19 +395,55 @@ hipError_t launch_expert_gemv_mx(const moe_layer& L, const void* x, int T, const
                                  const Group* groups, const PlanMeta* meta, float* H, int hstride, float* y_perm,
                                  hipStream_t s) {
     if (!mx_fits(L)) return hipErrorInvalidValue;
-    MxArgs a{static_cast<const uint16_t*>(x), perm_token, groups,
-             static_cast<const uint8_t*>(L.w_gate_up), L.w_gate_up_scales, static_cast<const uint16_t*>(L.b_gate_up),
-             static_cast<const uint8_t*>(L.w_down), L.w_down_scales, static_cast<const uint16_t*>(L.b_down),
-             reinterpret_cast<uint16_t*>(H), y_perm, hstride, T, T * L.k, L.d, L.ff, L.oai_alpha, L.oai_limit};
-    const int gmax = max_groups(L.n_expert, T, L.k, false);
-    const dim3 gu((L.ff + 4 * kMxUnits - 1) / (4 * kMxUnits), gmax);
-    const dim3 gd((L.d + 4 * kMxDownNR - 1) / (4 * kMxDownNR), gmax);
-    if (blocks_per_lane(L.d) == 1) expert_up_gemv_mx_kernel<1><<<gu, 256, 0, s>>>(a, meta);
-    else expert_up_gemv_mx_kernel<2><<<gu, 256, 0, s>>>(a, meta);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = launch_expert_up_gemv_mx(L, x, T, perm_token, groups, meta, H, hstride, s);
     if (e != hipSuccess) return e;
+    const MxArgs a = mx_args(L, x, T, perm_token, groups, H, hstride, y_perm);
+    const int gmax = max_groups(L.n_expert, T, L.k, false);
+    const dim3 gd((L.d + 4 * kMxDownNR - 1) / (4 * kMxDownNR), gmax);
     if (blocks_per_lane(L.ff) == 1) expert_down_gemv_mx_kernel<1><<<gd, 256, 0, s>>>(a, meta);
     else expert_down_gemv_mx_kernel<2><<<gd, 256, 0, s>>>(a, meta);
+    return hipGetLastError();
+}
+
+hipError_t launch_expert_up_gemv_mx(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
+                                    const Group* groups, const PlanMeta* meta, float* H, int hstride,
+                                    hipStream_t s) {
+    if (!mx_fits(L)) return hipErrorInvalidValue;
+    const MxArgs a = mx_args(L, x, T, perm_token, groups, H, hstride, nullptr);
+    const int gmax = max_groups(L.n_expert, T, L.k, false);
+    const dim3 gu((L.ff + 4 * kMxUnits - 1) / (4 * kMxUnits), gmax);
+    if (blocks_per_lane(L.d) == 1) expert_up_gemv_mx_kernel<1><<<gu, 256, 0, s>>>(a, meta);
+    else expert_up_gemv_mx_kernel<2><<<gu, 256, 0, s>>>(a, meta);
+    return hipGetLastError();
+}
+
+bool token1_mx_fits(const moe_layer& L) { return mx_fits(L) && L.k <= kToken1MxMaxWaves && L.shared_ff == 0; }
+
+hipError_t launch_token1_up_mx(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,
+                               float* H, int hstride, hipStream_t s) {
+    if (!token1_mx_fits(L)) return hipErrorInvalidValue;
+    const MxArgs a = mx_args(L, x, 1, nullptr, nullptr, H, hstride, nullptr);
+    const dim3 gu((L.ff + 4 * kMxUnits - 1) / (4 * kMxUnits), L.k);
+    if (blocks_per_lane(L.d) == 1)
+        token1_up_mx_kernel<1><<<gu, 256, 0, s>>>(a, logits, L.n_expert, L.k, L.route, L.route_scale, idx, w);
+    else
+        token1_up_mx_kernel<2><<<gu, 256, 0, s>>>(a, logits, L.n_expert, L.k, L.route, L.route_scale, idx, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_token_down_combine_mx(const moe_layer& L, int T, const float* H, int hstride, const int32_t* idx,
+                                        const float* w, const int32_t* perm_inv, const void* residual, void* y,
+                                        hipStream_t s) {
+    if (!token1_mx_fits(L) || T < 1 || (!perm_inv && T != 1)) return hipErrorInvalidValue;
+    const MxArgs a = mx_args(L, nullptr, T, nullptr, nullptr, const_cast<float*>(H), hstride, nullptr);
+    const dim3 grid((L.d + kMxDownNR - 1) / kMxDownNR, T);
+    const dim3 block(L.k * kWave);
+    const auto* ro = static_cast<const uint16_t*>(residual);
+    auto* yo = static_cast<uint16_t*>(y);
+    if (blocks_per_lane(L.ff) == 1)
+        token_down_combine_mx_kernel<1><<<grid, block, 0, s>>>(a, idx, w, perm_inv, L.n_expert, L.k, ro, yo);
+    else
+        token_down_combine_mx_kernel<2><<<grid, block, 0, s>>>(a, idx, w, perm_inv, L.n_expert, L.k, ro, yo);
     return hipGetLastError();
 }
 

@@ -89,6 +89,19 @@ bool mx_fits(const moe_layer& L);
 hipError_t launch_expert_gemv_mx(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                                  const Group* groups, const PlanMeta* meta, float* H, int hstride, float* y_perm,
                                  hipStream_t s);
+// The MXFP4 up GEMV alone (bf16 H rows), and the one-token / few-token fused kernels of
+// the MXFP4 layer: top-k inside the up GEMV (one token; hidden row j = pick j), and the
+// down GEMVs of every pick with the weighted combine written straight to y (hidden rows
+// perm_inv[t*k+j], or row j for one token).  token1_mx_fits: k <= 16, no shared expert.
+hipError_t launch_expert_up_gemv_mx(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
+                                    const Group* groups, const PlanMeta* meta, float* H, int hstride,
+                                    hipStream_t s);
+bool token1_mx_fits(const moe_layer& L);
+hipError_t launch_token1_up_mx(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,
+                               float* H, int hstride, hipStream_t s);
+hipError_t launch_token_down_combine_mx(const moe_layer& L, int T, const float* H, int hstride, const int32_t* idx,
+                                        const float* w, const int32_t* perm_inv, const void* residual, void* y,
+                                        hipStream_t s);
 // Up GEMV alone (H rows), for callers that finish the layer themselves.
 hipError_t launch_expert_up_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                                  const Group* groups, const PlanMeta* meta, float* H, int hstride,

@@ -233,6 +233,12 @@ moe_status forward_body(const moe_layer* L, const void* x, int32_t T, const void
                                            shared ? logits + L->n_expert : nullptr, o.ld, residual, y, s));
         return MOE_OK;
     }
+    if (T == 1 && !grouped && !dense && token1_mx_fits(*L)) {
+        // The same three launches over MXFP4 expert weights.
+        SMOE_TRY(launch_token1_up_mx(*L, x, logits, idx, w, at<float>(ws, o.H), o.hstride, s));
+        SMOE_TRY(launch_token_down_combine_mx(*L, 1, at<float>(ws, o.H), o.hstride, idx, w, nullptr, residual, y, s));
+        return MOE_OK;
+    }
     const bool fused_route = T <= kPermChunk;
     if (fused_route) {
         SMOE_TRY(launch_decode_route(*L, logits, o.ld, T, idx, w, sg, offsets, perm_token, perm_inv,
@@ -251,6 +257,12 @@ moe_status forward_body(const moe_layer* L, const void* x, int32_t T, const void
                                        at<float>(ws, o.H), o.hstride, s));
         SMOE_TRY(launch_token_down_combine(*L, T, at<float>(ws, o.H), o.hstride, idx, w, perm_inv, sg, 1, residual,
                                            y, s));
+        return MOE_OK;
+    }
+    if (fused_route && !grouped && !dense && T <= kTokenDownMaxT && token1_mx_fits(*L)) {
+        SMOE_TRY(launch_expert_up_gemv_mx(*L, x, T, perm_token, at<Group>(ws, o.groups), at<PlanMeta>(ws, o.meta),
+                                          at<float>(ws, o.H), o.hstride, s));
+        SMOE_TRY(launch_token_down_combine_mx(*L, T, at<float>(ws, o.H), o.hstride, idx, w, perm_inv, residual, y, s));
         return MOE_OK;
     }
     const moe_status st = run_experts(*L, x, T, offsets, perm_token, y_rows, row_w, grouped, ws, o, fused_route, s);
