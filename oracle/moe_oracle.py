@@ -23,6 +23,9 @@ The passages followed:
   bias, weighted sum with the routing scores.
 * "Phase 19: MoE - gpt-oss-20b", section 3 and the tensor layout: MXFP4 expert weights
   (32 FP4 codes and one E8M0 scale per block), dequantised before use.
+* "Qwen3.5-MoE Model Implementation", numeric status (K-quant Q3_K experts) and "Engine",
+  Prefill (Q4 / Q2 / Q3 GEMMs): K-quant expert weights; the Q4_K block layout is not on
+  the pages and follows the GGUF definition (``q4k_dequant``).
 * "Llama Forward Pass", section "Key Operations", RMSNorm, and "Qwen3.5-MoE Model
   Implementation", section "Architecture" (post-attention norm -> MoE FFN -> residual):
   the layer shell around the block (``moe_shell``).
@@ -80,12 +83,51 @@ def mxfp4_dequant(blocks, scales) -> np.ndarray:
     return vals.reshape(b.shape[:-2] + (b.shape[-2] * 32,))
 
 
+# GGUF "K-quant" Q4_K super-block: 256 weights in 144 bytes.  The pages name K-quant
+# experts (Q3_K on "Qwen3.5-MoE Model Implementation", numeric status; Q4 / Q2 / Q3 GEMMs
+# on "Engine", Prefill) but print no block layout; the layout below is the GGUF Q4_K
+# definition, taken as a reading:
+#   bytes 0-1   d     fp16, multiplier of the sub-block scales
+#   bytes 2-3   dmin  fp16, multiplier of the sub-block mins
+#   bytes 4-15  eight 6-bit scales sc_j and eight 6-bit mins m_j of the 32-weight
+#               sub-blocks j = 0..7: for j < 4, sc_j and m_j are the low 6 bits of bytes
+#               4+j and 8+j; for j >= 4, the low 4 bits of sc_j / m_j are the low / high
+#               nibble of byte 12+(j-4), and their top 2 bits are the top 2 bits of byte
+#               4+(j-4) (for sc_j) and byte 8+(j-4) (for m_j)
+#   bytes 16-143  128 bytes of 4-bit quants in 4 runs of 32: byte l of run c holds the
+#               quant of weight 64c + l in its low nibble (sub-block 2c) and of weight
+#               64c + 32 + l in its high nibble (sub-block 2c + 1)
+#   weight = d * sc_j * q - dmin * m_j
+Q4K_BLOCK = 144
+Q4K_WEIGHTS = 256
+
+
+def q4k_dequant(blocks) -> np.ndarray:
+    """Q4_K weights (layout above): ``blocks[..., nsb, 144]`` uint8 -> fp64
+    ``[..., nsb * 256]`` (fp16 d and dmin widen exactly; every product is exact in fp64)."""
+    b = np.ascontiguousarray(blocks, dtype=np.uint8)
+    lead = b.shape[:-1]
+    d = b[..., 0:2].copy().view("<f2").astype(np.float64)[..., 0]
+    dmin = b[..., 2:4].copy().view("<f2").astype(np.float64)[..., 0]
+    lo6 = b[..., 4:12].astype(np.int64) & 63            # sc_0..3 then m_0..3
+    top2 = b[..., 4:12].astype(np.int64) >> 6           # upper bits of sc_4..7 then m_4..7
+    nib = b[..., 12:16].astype(np.int64)
+    sc = np.concatenate([lo6[..., 0:4], (nib & 15) | (top2[..., 0:4] << 4)], axis=-1)
+    mn = np.concatenate([lo6[..., 4:8], (nib >> 4) | (top2[..., 4:8] << 4)], axis=-1)
+    runs = b[..., 16:144].astype(np.int64).reshape(lead + (4, 32))
+    q = np.stack([runs & 15, runs >> 4], axis=-2).reshape(lead + (8, 32))  # sub-block 2c, 2c+1
+    vals = d[..., None, None] * sc[..., :, None] * q - dmin[..., None, None] * mn[..., :, None]
+    return vals.reshape(b.shape[:-2] + (b.shape[-2] * Q4K_WEIGHTS,))
+
+
 def _expert(L: dict, name: str, e: int) -> np.ndarray | None:
     t = L.get(name)
     if t is None:
         return None
     if L.get("expert_format") == "mxfp4" and name in ("w_gate_up", "w_down"):
         return mxfp4_dequant(t[e], L[name + "_scales"][e])
+    if L.get("expert_format") == "q4k" and name in ("w_gate", "w_up", "w_down"):
+        return q4k_dequant(t[e])
     return widen(t[e])
 
 

@@ -70,6 +70,7 @@ class LayerSpec:
     zipf_s: float = 1.1
     bias_std: float = 0.02          # expert biases of the clamped variant
     experts: str = "dense"          # "dense" | "mxfp4" (gate_up / down of the clamped variant)
+                                    # | "q4k" (gate / up / down of the SwiGLU variant)
 
 
 # The workloads.  Distributions: x ~ N(0,1); expert and shared weights ~ N(0, weight_std);
@@ -92,6 +93,9 @@ SPECS = {
                            router_bias_std=0.1, experts="mxfp4"),
     "mixtral": LayerSpec("mixtral", d=4096, n_expert=8, ff=14336, k=2, shared_ff=0,
                          dtype="bf16", router_std=1.0 / math.sqrt(4096)),
+    # The Qwen-shaped layer with Q4_K routed experts (the shared expert stays bf16).
+    "qwen_q4k": LayerSpec("qwen_q4k", d=2048, n_expert=256, ff=512, k=8, shared_ff=512,
+                          dtype="bf16", router_std=1.0 / math.sqrt(2048), experts="q4k"),
 }
 
 
@@ -168,6 +172,27 @@ def _mxfp4_stacked(seed: int, code: str, E: int, rows: int, K: int, std: float, 
     return blocks, scales
 
 
+def _q4k_stacked(seed: int, code: str, E: int, rows: int, K: int, std: float, experts=None):
+    """Q4_K tensors [E, rows, K/256, 144] uint8: per super-block the fp16 multipliers d and
+    dmin, then uniformly drawn bytes for the packed 6-bit scales / mins and the 4-bit quants
+    (every bit pattern is a valid block).  d is drawn around the value that gives weights of
+    standard deviation ~std (mean scale 31.5, quants of rms deviation 4.6, and the spread
+    of the sub-block offsets, about as large again) and dmin so that
+    d * sc * 7.5 and dmin * m balance on average."""
+    nsb = K // 256
+    out = np.zeros((E, rows, nsb, 144), dtype=np.uint8)
+    d0 = 0.55 * std / (31.5 * 4.61)
+    for e in (range(E) if experts is None else experts):
+        g = _rng(seed, _CODE[code], e)
+        blk = g.integers(0, 256, size=(rows, nsb, 144), dtype=np.uint8)
+        d = (d0 * np.exp2(g.uniform(-0.5, 0.5, size=(rows, nsb)))).astype(np.float16)
+        dmin = (7.5 * d0 * np.exp2(g.uniform(-0.5, 0.5, size=(rows, nsb)))).astype(np.float16)
+        blk[..., 0:2] = d[..., None].view(np.uint8).reshape(rows, nsb, 2)
+        blk[..., 2:4] = dmin[..., None].view(np.uint8).reshape(rows, nsb, 2)
+        out[e] = blk
+    return out
+
+
 def make_layer(sp: LayerSpec, seed: int = 0, experts=None) -> dict:
     """All parameters of one layer, in storage form (uint16 bf16 bits or float32).
 
@@ -188,7 +213,13 @@ def make_layer(sp: LayerSpec, seed: int = 0, experts=None) -> dict:
         L["b_router"] = zipf_router_bias(E, sp.k, sp.zipf_s)
     else:
         L["b_router"] = None
-    if sp.act == ACT_SWIGLU:
+    if sp.act == ACT_SWIGLU and sp.experts == "q4k":
+        if dt != "bf16" or d % 256 or ff % 256:
+            raise ValueError("Q4_K experts: bf16 layer, widths multiple of 256")
+        L["w_gate"] = _q4k_stacked(seed, "w_gate", E, ff, d, sp.weight_std, experts)
+        L["w_up"] = _q4k_stacked(seed, "w_up", E, ff, d, sp.weight_std, experts)
+        L["w_gate_up"] = L["b_gate_up"] = L["b_down"] = None
+    elif sp.act == ACT_SWIGLU:
         L["w_gate"] = _stacked(seed, "w_gate", E, (ff, d), sp.weight_std, dt, experts)
         L["w_up"] = _stacked(seed, "w_up", E, (ff, d), sp.weight_std, dt, experts)
         L["w_gate_up"] = L["b_gate_up"] = L["b_down"] = None
@@ -202,6 +233,8 @@ def make_layer(sp: LayerSpec, seed: int = 0, experts=None) -> dict:
             raise ValueError("MXFP4 experts: clamped variant, bf16, widths multiple of 32")
         for name, rows, K in (("w_gate_up", 2 * ff, d), ("w_down", d, ff)):
             L[name], L[name + "_scales"] = _mxfp4_stacked(seed, name, E, rows, K, sp.weight_std, experts)
+    elif sp.experts == "q4k":
+        L["w_down"] = _q4k_stacked(seed, "w_down", E, d, ff, sp.weight_std, experts)
     else:
         if sp.act == ACT_SWIGLU_OAI:
             L["w_gate_up"] = _stacked(seed, "w_gate_up", E, (2 * ff, d), sp.weight_std, dt, experts)

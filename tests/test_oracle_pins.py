@@ -412,3 +412,87 @@ def test_mxfp4_layer_equals_dequantised_bf16_layer():
     x = synth.make_tokens(L, 9, seed=4)
     assert np.array_equal(oracle.moe_forward(L, x), oracle.moe_forward(D, x))
     assert np.allclose(oracle.moe_forward(L, x), oracle.moe_forward_tokens(L, x), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- Q4_K
+
+def _pack_q4k(d, dmin, sc, mn, q):
+    """One Q4_K super-block from its fields, written bit by bit from the layout (fp16 d and
+    dmin; 6-bit sc[8], mn[8]; q[256] in 0..15, weight i in sub-block i // 32)."""
+    blk = np.zeros(144, dtype=np.uint8)
+    blk[0:2] = np.array([d], dtype="<f2").view(np.uint8)
+    blk[2:4] = np.array([dmin], dtype="<f2").view(np.uint8)
+    for j in range(8):
+        s, m = int(sc[j]), int(mn[j])
+        assert 0 <= s < 64 and 0 <= m < 64
+        if j < 4:
+            blk[4 + j] |= s            # low 6 bits of byte 4+j
+            blk[8 + j] |= m            # low 6 bits of byte 8+j
+        else:
+            blk[12 + j - 4] |= (s & 15) | ((m & 15) << 4)
+            blk[4 + j - 4] |= (s >> 4) << 6   # top 2 bits of byte 4+(j-4)
+            blk[8 + j - 4] |= (m >> 4) << 6   # top 2 bits of byte 8+(j-4)
+    for i in range(256):
+        c, within = divmod(i, 64)
+        half, l = divmod(within, 32)   # half 0: low nibble, 1: high nibble of byte l of run c
+        blk[16 + 32 * c + l] |= int(q[i]) << (4 * half)
+    return blk
+
+
+def test_q4k_block_from_bit_fields():
+    # Every scale and min distinct and most above 15, so a swapped nibble, a swapped
+    # scale/min or a misplaced top-bit split moves some weight.
+    sc = [17 + 6 * j for j in range(8)]            # 17 .. 59
+    mn = [60 - 7 * j for j in range(8)]            # 60 .. 11
+    q = [(7 * i + 3) % 16 for i in range(256)]
+    d, dmin = 0.5, 0.25                            # exact in fp16
+    blk = _pack_q4k(d, dmin, sc, mn, q)
+    v = oracle.q4k_dequant(blk[None, :])
+    assert v.shape == (256,)
+    for i in range(256):
+        j = i // 32
+        assert v[i] == d * sc[j] * q[i] - dmin * mn[j], i
+
+
+def test_q4k_fp16_multipliers_and_shape():
+    # d and dmin are IEEE half precision: numpy's float16 decodes them independently.
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        d = np.float16(rng.uniform(1e-5, 2.0))
+        dmin = np.float16(rng.uniform(1e-5, 2.0))
+        sc = rng.integers(0, 64, 8)
+        mn = rng.integers(0, 64, 8)
+        q = rng.integers(0, 16, 256)
+        blk = _pack_q4k(d, dmin, sc, mn, q)
+        v = oracle.q4k_dequant(blk[None, :])
+        expect = [float(d) * int(sc[i // 32]) * int(q[i]) - float(dmin) * int(mn[i // 32]) for i in range(256)]
+        assert np.array_equal(v, np.array(expect))
+    # Leading dimensions and several super-blocks per row.
+    blocks = np.stack([_pack_q4k(1.0, 0.0, [1] * 8, [0] * 8, [(i + r) % 16 for i in range(256)]) for r in range(6)])
+    v = oracle.q4k_dequant(blocks.reshape(2, 3, 144))
+    assert v.shape == (2, 768)
+    assert list(v[1, 256:260]) == [4.0, 5.0, 6.0, 7.0]   # row 1, second super-block (r = 4)
+
+
+def test_q4k_layer_equals_dequantised_bf16_layer():
+    # With power-of-two scales, no mins and fp16 multipliers that are powers of two, every
+    # Q4_K weight has at most 4 significant bits: exact in bf16, so the Q4_K layer must give
+    # exactly what the dense bf16 layer holding those weights gives.
+    sp = synth.spec("qwen_q4k", d=256, n_expert=5, ff=256, k=2, shared_ff=256)
+    L = synth.make_layer(sp, seed=7)
+    rng = np.random.default_rng(8)
+    for n in ("w_gate", "w_up", "w_down"):
+        t = L[n]
+        for idx in np.ndindex(t.shape[:-1]):
+            t[idx] = _pack_q4k(2.0 ** -int(rng.integers(9, 13)), 1.0, 2 ** rng.integers(0, 6, 8), [0] * 8,
+                               rng.integers(0, 16, 256))
+    D = dict(L)
+    D["expert_format"] = "dense"
+    for n in ("w_gate", "w_up", "w_down"):
+        deq = oracle.q4k_dequant(L[n])
+        D[n] = synth.f32_to_bf16_bits(deq.astype(np.float32))
+        assert np.array_equal(oracle.widen(D[n]), deq)
+    x = synth.make_tokens(L, 9, seed=4)
+    y = oracle.moe_forward(L, x)
+    assert np.array_equal(y, oracle.moe_forward(D, x))
+    assert np.max(np.abs(y - oracle.moe_forward_tokens(L, x))) <= 1e-12 * np.max(np.abs(y))

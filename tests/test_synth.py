@@ -70,3 +70,18 @@ def test_zipf_bias_realises_target_load():
     assert np.all(err <= 0.03 * q + 5 * sigma), np.max(err / q)
     assert np.all(err[:16] <= 0.03 * q[:16] + 3 * sigma[:16])
     assert np.all(share > 0)
+
+
+def test_q4k_layer_inputs():
+    L = synth.make_layer(synth.spec("qwen_q4k", d=512, n_expert=4, ff=256, shared_ff=256), seed=0)
+    assert L["w_gate"].shape == (4, 256, 2, 144) and L["w_gate"].dtype == np.uint8
+    assert L["w_down"].shape == (4, 512, 1, 144)
+    assert L["ws_gate"].dtype == np.uint16          # the shared expert stays bf16
+    d = L["w_gate"][..., 0:2].copy().view("<f2").astype(np.float64)
+    assert np.all(np.isfinite(d)) and np.all(d > 0)
+    import oracle
+    w = oracle.q4k_dequant(L["w_up"])
+    assert 0.01 < w.std() < 0.04
+    # The same seed gives the same bytes.
+    L2 = synth.make_layer(synth.spec("qwen_q4k", d=512, n_expert=4, ff=256, shared_ff=256), seed=0)
+    assert np.array_equal(L["w_down"], L2["w_down"])
