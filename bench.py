@@ -53,6 +53,9 @@ WORKLOADS = {
     "mixtral_t16": ("mixtral", 16),
     "mixtral_t16384": ("mixtral", 16384),
     "tiny_f32_t16": ("tiny_f32", 16),
+    "qwen_q4k_t1": ("qwen_q4k", 1),
+    "qwen_q4k_t64": ("qwen_q4k", 64),
+    "qwen_q4k_prefill_t8192": ("qwen_q4k_zipf", 8192),
 }
 DEFAULT = "qwen_decode_t64"
 DEFAULT_SWEEP = ["qwen_decode_t1", "qwen_decode_t8", "qwen_prefill_t8192", "tiny_f32_t16", "gptoss_t1",
@@ -182,9 +185,10 @@ def elem_bytes(L):
 
 def expert_weight_bytes(L):
     """Bytes of one routed expert's parameters (MXFP4: 16 code bytes and one scale byte
-    per 32 weights)."""
+    per 32 weights; Q4_K: 144 bytes per 256 weights)."""
     s, d, ff = elem_bytes(L), L["d"], L["ff"]
-    w = 3 * d * ff * 17 // 32 if L.get("expert_format") == "mxfp4" else 3 * d * ff * s
+    fmt = L.get("expert_format")
+    w = 3 * d * ff * 17 // 32 if fmt == "mxfp4" else 3 * d * ff * 144 // 256 if fmt == "q4k" else 3 * d * ff * s
     if L["act"] == "swiglu":
         return w
     b = 2 * ff * s + (d * s if L.get("b_down") is not None else 0)
@@ -233,8 +237,11 @@ def time_workload(name, steps, warmup, layer_cache, forward_only=False):
     L = layer_cache.get(spec_name)
     if L is None:
         t0 = time.time()
-        base = "qwen" if spec_name == "qwen_zipf" and "qwen" in layer_cache else None
-        if base:
+        if spec_name == "qwen_q4k_zipf":  # the Q4_K layer with the Zipf router bias
+            L = dict(layer_cache.get("qwen_q4k") or synth.make_layer(synth.spec("qwen_q4k"), seed=0))
+            L["b_router"] = synth.zipf_router_bias(L["n_expert"], L["k"], 1.1)
+            L["name"] = spec_name
+        elif spec_name == "qwen_zipf" and "qwen" in layer_cache:
             L = dict(layer_cache["qwen"])
             L["b_router"] = synth.zipf_router_bias(L["n_expert"], L["k"], 1.1)
             L["name"] = "qwen_zipf"

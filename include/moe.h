@@ -88,8 +88,18 @@ enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_GROUPED = 2 };
  *    Requires MOE_BF16, MOE_ACT_SWIGLU_OAI, no shared expert and d, ff <= 4096.  The
  *    GEMV path expands the blocks in registers; the grouped path expands each K-slice of
  *    a weight tile into LDS as bf16 for the bf16 MFMA (activations stay bf16).  Biases,
- *    router, x and y stay bf16. */
-enum { MOE_EXPERTS_DENSE = 0, MOE_EXPERTS_MXFP4 = 1 };
+ *    router, x and y stay bf16.
+ *  Q4K (K-quant experts named on "Qwen3.5-MoE Model Implementation", numeric status, and
+ *    "Engine", Prefill; the block layout is GGUF's Q4_K, not printed on the pages):
+ *    w_gate, w_up = [E, ff, d/256, 144] and w_down = [E, d, ff/256, 144] uint8 super-blocks
+ *    of 256 consecutive inputs each: fp16 d and dmin (bytes 0-3), eight packed 6-bit
+ *    scales and mins of the 32-input sub-blocks (bytes 4-15), 4-bit quants in 4 runs of 32
+ *    bytes (low nibble of byte l of run c = input 64c + l, high nibble = input 64c+32+l);
+ *    weight = d * scale_j * q - dmin * min_j.  Requires MOE_BF16, MOE_ACT_SWIGLU, d and ff
+ *    multiples of 256 and at most 4096, and NULL *_scales fields.  The shared expert, router,
+ *    x and y stay bf16.  The GEMV path multiplies the quants in registers; the grouped path
+ *    expands each K-slice of a weight tile into LDS as bf16 for the bf16 MFMA. */
+enum { MOE_EXPERTS_DENSE = 0, MOE_EXPERTS_MXFP4 = 1, MOE_EXPERTS_Q4K = 2 };
 
 /* One MoE layer.  Fixed layout: 9 int32, 3 float, then 12 pointers (offset 48), then
  * 2 int32 and 2 pointers (offset 144).  No field depends on a build flag.  All pointers

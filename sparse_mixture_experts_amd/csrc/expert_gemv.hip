@@ -154,12 +154,14 @@ __global__ __launch_bounds__(kToken1MaxWaves * kWave) void token1_down_combine_k
     }
 }
 
+// shared_only: one grid row, the shared expert's (grid row 0), for layers whose routed
+// experts run on other kernels.
 template <typename TT, bool OAI>
 hipError_t launch_up_t(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                        const Group* groups, const PlanMeta* meta, float* H, int hstride, const GemvPlan& plan,
-                       hipStream_t s) {
+                       hipStream_t s, bool shared_only = false) {
     const bool shared = L.shared_ff > 0;
-    const int gmax = max_groups(L.n_expert, T, L.k, shared);
+    const int gmax = shared_only ? 1 : max_groups(L.n_expert, T, L.k, shared);
     GemvUp u{x, perm_token, groups, L.w_gate, L.w_up, L.w_gate_up, L.b_gate_up,
              L.ws_gate, L.ws_up, H, hstride, T, T * L.k, L.d, L.ff, L.shared_ff, L.oai_alpha, L.oai_limit};
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
@@ -213,9 +215,9 @@ hipError_t launch_up_t(const moe_layer& L, const void* x, int T, const int32_t* 
 
 template <typename TT, bool OAI>
 hipError_t launch_down_t(const moe_layer& L, int T, const Group* groups, const PlanMeta* meta, const float* H,
-                         int hstride, float* y_perm, hipStream_t s) {
+                         int hstride, float* y_perm, hipStream_t s, bool shared_only = false) {
     const bool shared = L.shared_ff > 0;
-    const int gmax = max_groups(L.n_expert, T, L.k, shared);
+    const int gmax = shared_only ? 1 : max_groups(L.n_expert, T, L.k, shared);
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
     GemvDown dn{H, groups, L.w_down, L.b_down, L.ws_down, y_perm, hstride, T, T * L.k, L.d, L.ff, L.shared_ff};
     const bool dn_res = chunks(ffmax, TT::VEC) <= 8;
@@ -352,6 +354,10 @@ hipError_t launch_expert_gemv(const moe_layer& L, const void* x, int T, const in
         if (plan_offsets) return hipErrorInvalidValue;
         return launch_expert_gemv_mx(L, x, T, perm_token, groups, meta, H, hstride, y_perm, s);
     }
+    if (L.expert_format == MOE_EXPERTS_Q4K) {
+        if (plan_offsets) return hipErrorInvalidValue;
+        return launch_expert_gemv_q4k(L, x, T, perm_token, groups, meta, H, hstride, y_perm, s);
+    }
     const GemvPlan plan{plan_offsets, L.n_expert, groups, meta};
     const bool oai = L.act == MOE_ACT_SWIGLU_OAI;
     hipError_t e;
@@ -367,6 +373,19 @@ hipError_t launch_expert_gemv(const moe_layer& L, const void* x, int T, const in
                    : launch_down_t<BF16, false>(L, T, groups, meta, H, hstride, y_perm, s);
     return oai ? launch_down_t<F32, true>(L, T, groups, meta, H, hstride, y_perm, s)
                : launch_down_t<F32, false>(L, T, groups, meta, H, hstride, y_perm, s);
+}
+
+hipError_t launch_shared_gemv_up(const moe_layer& L, const void* x, int T, const Group* groups, const PlanMeta* meta,
+                                 float* H, int hstride, hipStream_t s) {
+    if (L.shared_ff <= 0 || L.dtype != MOE_BF16 || L.act != MOE_ACT_SWIGLU) return hipErrorInvalidValue;
+    const GemvPlan plan{nullptr, L.n_expert, nullptr, nullptr};
+    return launch_up_t<BF16, false>(L, x, T, nullptr, groups, meta, H, hstride, plan, s, true);
+}
+
+hipError_t launch_shared_gemv_down(const moe_layer& L, int T, const Group* groups, const PlanMeta* meta,
+                                   const float* H, int hstride, float* y_perm, hipStream_t s) {
+    if (L.shared_ff <= 0 || L.dtype != MOE_BF16 || L.act != MOE_ACT_SWIGLU) return hipErrorInvalidValue;
+    return launch_down_t<BF16, false>(L, T, groups, meta, H, hstride, y_perm, s, true);
 }
 
 hipError_t launch_expert_up_gemv(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
@@ -392,7 +411,9 @@ hipError_t launch_token1_up(const moe_layer& L, const void* x, const float* logi
                : launch_token1_up_t<F32, false>(L, x, logits, idx, w, H, hstride, s);
 }
 
-bool token1_fits(const moe_layer& L) { return L.k + (L.shared_ff > 0 ? 1 : 0) <= kToken1MaxWaves; }
+bool token1_fits(const moe_layer& L) {
+    return L.expert_format == MOE_EXPERTS_DENSE && L.k + (L.shared_ff > 0 ? 1 : 0) <= kToken1MaxWaves;
+}
 
 hipError_t launch_token_down_combine(const moe_layer& L, int T, const float* H, int hstride, const int32_t* idx,
                                      const float* w, const int32_t* perm_inv, const float* shared_gate,

@@ -417,7 +417,9 @@ hipError_t launch_expert_up_gemv_mx(const moe_layer& L, const void* x, int T, co
     return hipGetLastError();
 }
 
-bool token1_mx_fits(const moe_layer& L) { return mx_fits(L) && L.k <= kToken1MxMaxWaves && L.shared_ff == 0; }
+bool token1_mx_fits(const moe_layer& L) {
+    return L.expert_format == MOE_EXPERTS_MXFP4 && mx_fits(L) && L.k <= kToken1MxMaxWaves && L.shared_ff == 0;
+}
 
 hipError_t launch_token1_up_mx(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,
                                float* H, int hstride, hipStream_t s) {

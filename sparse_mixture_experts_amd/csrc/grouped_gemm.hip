@@ -35,11 +35,13 @@
 // The router GEMM (128, 64 or 32 tokens x 128 experts per block) keeps a 4-wave,
 // register-staged pipeline: with E = 256 experts a 256-wide tile would leave too few
 // blocks.  MXFP4 expert weights take the same loops with their B slices expanded from FP4
-// blocks into the ring (see grouped_mainloop_mx).
+// blocks into the ring, and Q4_K weights from their super-blocks (see
+// grouped_mainloop_regb).
 #include "common.h"
 #include "internal.h"
 #include "mfma_dev.h"
 #include "mxfp4_dev.h"
+#include "q4k_dev.h"
 
 namespace smoe {
 namespace {
@@ -151,6 +153,14 @@ __device__ __forceinline__ void issue_slice(GSmem<KW>& sm, const LoadPlan<KW>& p
     }
 }
 
+// The A segments of a slice only (B comes through registers): n 1 KB segments of this
+// wave, segment j at dst + (wave + 8 j) * 512 elements, fetched from src[j] + k0.
+__device__ __forceinline__ void issue_a_segments(uint16_t* dst, const uint16_t* const* src, int n, int k0) {
+    const int wave = threadIdx.x / kWave;
+    for (int j = 0; j < n; ++j)
+        __builtin_amdgcn_global_load_lds(src[j] + k0, (lds_ptr_t)(dst + (wave + 8 * j) * 512), 16, 0, 0);
+}
+
 // acc += A[wave rows] x B[rows brow[ni] + 0..15]^T over K.  Step kt: wait for this lane's
 // loads of slice kt, barrier (everyone's slice kt has landed and everyone has finished
 // step kt-1, whose stage the next issue reuses), compute slice kt, then issue slice kt+2
@@ -230,37 +240,105 @@ __device__ __forceinline__ void mx_store(GSmem<KW>& sm, int stage, const MxRegs<
         *reinterpret_cast<uint4*>(&sm.k.b[stage][swz<KW>(row, h * (KW / 16) + i)]) = fp4_word_bf16x8(r.w[i], scale);
 }
 
-// The main loop with B from MXFP4 blocks.  Slice s: A direct-loaded two steps ahead as
-// above; B loaded into registers two steps ahead and expanded into LDS at the end of step
-// s - 1 (its stage held slice s - 3, finished by every wave at the barrier of step s - 1).
-// The wait before each step allows the newest slice's loads (A and B registers) in
-// flight; the expansion itself waits for its registers, which also completes the A
-// loads issued before them.
+// Weight sources of the register-staged main loop: load(k0) fetches this thread's share
+// of the K-slice at k0 (thread t: tile row t / 2, half t & 1 of the slice) into registers;
+// store() expands it into the slice's bf16 LDS rows (the swizzled layout of the direct
+// loads).  kLoads: vector loads per thread per slice.
 template <int KW>
-__device__ __forceinline__ void grouped_mainloop_mx(GSmem<KW>& sm, const LoadPlan<KW>& p, const MxRow& mb, int K,
-                                                    int arow0, const int (&brow)[4], floatx4 (&acc)[4][4]) {
+struct MxSrc {
+    MxRow m;
+    using Regs = MxRegs<KW>;
+    static constexpr int kLoads = kMxLoads;
+    __device__ __forceinline__ Regs load(int k0) const { return mx_load<KW>(m, k0); }
+    __device__ __forceinline__ void store(GSmem<KW>& sm, int stage, const Regs& r) const { mx_store<KW>(sm, stage, r); }
+};
+
+// Q4_K weights (layout in q4k_dev.h).  A 64-wide slice is one quant run (two sub-blocks):
+// half h of a row takes sub-block 2c + h, i.e. nibble h of all 32 run bytes.  A 32-wide
+// slice is one sub-block j: half h takes its weights 16h .. 16h+15, i.e. bytes 16h .. of
+// run j / 2, nibble j & 1.  Either way the super-block's 16-byte header comes along.
+// `kbase` is the absolute input index of the call's K = 0 (split-K slices start inside a
+// super-block).
+template <int KW>
+struct Q4kRegs {
+    uint4 head;
+    uint4 q[KW == 64 ? 2 : 1];
+    int j;  // sub-block whose scale and min apply
+};
+
+template <int KW>
+struct Q4kSrc {
+    const uint8_t* row;  // this thread's B row, first super-block
+    int kbase;
+    using Regs = Q4kRegs<KW>;
+    static constexpr int kLoads = KW == 64 ? 3 : 2;
+    __device__ __forceinline__ Regs load(int k0) const {
+        const int k = kbase + k0, h = threadIdx.x & 1;
+        const int j = (k % kQ4kBlockWeights) / 32;
+        const uint8_t* blk = row + (size_t)(k / kQ4kBlockWeights) * kQ4kBlockBytes;
+        Regs r;
+        r.head = ld16(blk);
+        if constexpr (KW == 64) {
+            const uint8_t* run = blk + 16 + 32 * (j / 2);
+            r.q[0] = ld16(run);
+            r.q[1] = ld16(run + 16);
+            r.j = j + h;
+        } else {
+            static_assert(KW == 32, "Q4_K slices are one run or one sub-block wide");
+            r.q[0] = ld16(blk + 16 + 32 * (j / 2) + 16 * h);
+            r.j = j;
+        }
+        return r;
+    }
+    __device__ __forceinline__ void store(GSmem<KW>& sm, int stage, const Regs& r) const {
+        const int row_l = threadIdx.x >> 1, h = threadIdx.x & 1;
+        float a, b;
+        q4k_sub_scale(r.head, r.j, a, b);
+        const int shift = 4 * (r.j & 1);
+        constexpr int NC = KW / 16;  // 16-byte LDS chunks per thread
+#pragma unroll
+        for (int q = 0; q < NC; ++q) {
+            const uint4& v = r.q[q / 2];
+            const uint32_t w0 = (q & 1) ? v.z : v.x, w1 = (q & 1) ? v.w : v.y;
+            *reinterpret_cast<uint4*>(&sm.k.b[stage][swz<KW>(row_l, h * NC + q)]) = q4k_dequant8(w0, w1, shift, a, b);
+        }
+    }
+};
+
+// The main loop with B from a register-staged source.  Slice s: A direct-loaded two steps
+// ahead as in grouped_mainloop; B loaded into registers two steps ahead and expanded into
+// LDS at the end of step s - 1 (its stage held slice s - 3, finished by every wave at the
+// barrier of step s - 1).  The wait before each step allows the newest slice's loads (A
+// and B registers) in flight; the expansion itself waits for its registers, which also
+// completes the A loads issued before them.
+template <int KW, typename Src>
+__device__ __forceinline__ void grouped_mainloop_regb(GSmem<KW>& sm, const LoadPlan<KW>& p, const Src& src, int K,
+                                                      int arow0, const int (&brow)[4], floatx4 (&acc)[4][4]) {
     const int nk = K / KW;
-    issue_slice<KW, true>(sm, p, 0, 0);
-    const MxRegs<KW> first = mx_load<KW>(mb, 0);
-    issue_slice<KW, true>(sm, p, 1, min(1, nk - 1) * KW);
-    MxRegs<KW> nxt = mx_load<KW>(mb, min(1, nk - 1) * KW);
-    mx_store(sm, 0, first);
+    issue_a_segments(sm.k.a[0], p.src, Ring<KW>::kLoadsA, 0);
+    const typename Src::Regs first = src.load(0);
+    issue_a_segments(sm.k.a[1], p.src, Ring<KW>::kLoadsA, min(1, nk - 1) * KW);
+    typename Src::Regs nxt = src.load(min(1, nk - 1) * KW);
+    src.store(sm, 0, first);
     int st = 0;
     for (int kt = 0; kt < nk; ++kt) {
-        wait_vm_lgkm<Ring<KW>::kLoadsA + kMxLoads>();
+        wait_vm_lgkm<Ring<KW>::kLoadsA + Src::kLoads>();
         lds_barrier();
 #pragma unroll
         for (int kc = 0; kc < KW / 8; kc += 4) mfma_k32<KW>(sm.k.a[st], sm.k.b[st], arow0, brow, kc, acc);
         const int nx = st == 2 ? 0 : st + 1;   // (kt + 1) % 3
-        mx_store(sm, nx, nxt);                 // B of slice kt+1 (clamped re-load on the last step)
+        src.store(sm, nx, nxt);                // B of slice kt+1 (clamped re-load on the last step)
         const int pre = st == 0 ? 2 : st - 1;  // (kt + 2) % 3
-        issue_slice<KW, true>(sm, p, pre, min(kt + 2, nk - 1) * KW);
-        nxt = mx_load<KW>(mb, min(kt + 2, nk - 1) * KW);
+        issue_a_segments(sm.k.a[pre], p.src, Ring<KW>::kLoadsA, min(kt + 2, nk - 1) * KW);
+        nxt = src.load(min(kt + 2, nk - 1) * KW);
         st = nx;
     }
     wait_vm_lgkm<0>();
     __syncthreads();
 }
+
+// Storage of the routed experts' weights in the grouped kernels.
+constexpr int kWDense = 0, kWMx = 1, kWQ4k = 2;
 
 struct UpArgs {
     const uint16_t* x;
@@ -276,6 +354,8 @@ struct UpArgs {
     const uint16_t* ws_up;
     const uint8_t* mx_w;        // MXFP4 gate_up blocks [E, 2ff, d/32, 16], or null
     const uint8_t* mx_s;        // ... and scales [E, 2ff, d/32]
+    const uint8_t* q4_gate;     // Q4_K gate / up super-blocks [E, ff, d/256, 144], or null
+    const uint8_t* q4_up;
     uint16_t* H;                // bf16 [rows, hstride]
     int hstride, T, d, ff, ffs, n_ntiles;
     float alpha, limit;
@@ -292,6 +372,7 @@ struct DownArgs {
     const uint16_t* ws_down;  // [d, ffs]
     const uint8_t* mx_w;      // MXFP4 down blocks [E, d, ff/32, 16], or null
     const uint8_t* mx_s;      // ... and scales [E, d, ff/32]
+    const uint8_t* q4_down;   // Q4_K down super-blocks [E, d, ff/256, 144], or null
     const float* row_w;       // per grouped row weight, or null (unweighted)
     void* y;                  // [rows, d], bf16 or fp32; with ksplit > 1 fp32 [ksplit][rows][d]
     int hstride, d, ff, ffs, n_ntiles;
@@ -350,8 +431,10 @@ __device__ __forceinline__ bool locate(const PlanMeta* meta, const TileDesc* til
     return true;
 }
 
-// MX: gate_up weights as MXFP4 blocks (a.mx_w, a.mx_s; clamped variant, no shared expert).
-template <bool OAI, bool MX>
+// WF: storage of the routed gate/up weights.  kWMx: MXFP4 gate_up blocks (a.mx_w, a.mx_s;
+// clamped variant, no shared expert).  kWQ4k: Q4_K w_gate / w_up super-blocks (SwiGLU);
+// the shared expert's tiles stay on the bf16 direct loads.
+template <bool OAI, int WF>
 __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kernel(UpArgs a) {
     __shared__ GSmem<kUpKW> sm;
     Group g;
@@ -380,22 +463,35 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kerne
                                       : (up ? a.w_up : a.w_gate) + (size_t)g.e * a.ff * d;
         return base + (size_t)f * d;
     };
-    const LoadPlan<kUpKW> plan = make_plan<kUpKW, MX>(row_a, row_b);
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int wm = wave >> 2, wn = wave & 3;
     // Wave n-tiles 0,1 are gate units wn*32.., 2,3 the matching up units.
     const int brow[4] = {wn * 32, wn * 32 + 16, 128 + wn * 32, 128 + wn * 32 + 16};
     floatx4 acc[4][4];
     zero(acc);
-    if constexpr (MX) {
+    if constexpr (WF == kWMx) {
         // This thread's B row (tile row threadIdx.x / 2), in the interleaved gate_up rows.
+        const LoadPlan<kUpKW> plan = make_plan<kUpKW, true>(row_a, row_b);
         const int r = threadIdx.x >> 1;
         const int f = min(f0 + (r & 127), ffg - 1);
         const size_t R = (size_t)max(g.e, 0) * 2 * a.ff + 2 * f + (r >= 128 ? 1 : 0);
         const size_t nblk = d / 32;
-        const MxRow mb{a.mx_w + R * nblk * 16, a.mx_s + R * nblk};
-        grouped_mainloop_mx(sm, plan, mb, a.d, wm * 64, brow, acc);
+        const MxSrc<kUpKW> src{MxRow{a.mx_w + R * nblk * 16, a.mx_s + R * nblk}};
+        grouped_mainloop_regb(sm, plan, src, a.d, wm * 64, brow, acc);
+    } else if constexpr (WF == kWQ4k) {
+        if (!shared) {
+            const LoadPlan<kUpKW> plan = make_plan<kUpKW, true>(row_a, row_b);
+            const int r = threadIdx.x >> 1;
+            const int f = min(f0 + (r & 127), ffg - 1);
+            const uint8_t* base = r >= 128 ? a.q4_up : a.q4_gate;
+            const Q4kSrc<kUpKW> src{base + ((size_t)g.e * a.ff + f) * (d / kQ4kBlockWeights) * kQ4kBlockBytes, 0};
+            grouped_mainloop_regb(sm, plan, src, a.d, wm * 64, brow, acc);
+        } else {
+            const LoadPlan<kUpKW> plan = make_plan<kUpKW, false>(row_a, row_b);
+            grouped_mainloop(sm, plan, a.d, wm * 64, brow, acc);
+        }
     } else {
+        const LoadPlan<kUpKW> plan = make_plan<kUpKW, false>(row_a, row_b);
         grouped_mainloop(sm, plan, a.d, wm * 64, brow, acc);
     }
 
@@ -443,8 +539,9 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kerne
 // of every tile is cut into ksplit slices, one block each (N-tile-major: the slices of an
 // N-tile are consecutive block slots), and each block stores its raw fp32 sums to slice
 // plane ks of y; splitk_reduce_kernel adds the planes, the bias and the routing weight.
-// MX: down weights as MXFP4 blocks (a.mx_w, a.mx_s).
-template <typename TY, bool MX>
+// WF: storage of the routed down weights (kWMx: MXFP4 blocks a.mx_w, a.mx_s; kWQ4k: Q4_K
+// super-blocks a.q4_down, the shared expert's tiles on the bf16 direct loads).
+template <typename TY, int WF>
 __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_kernel(DownArgs a) {
     __shared__ GSmem<kDownKW> sm;
     Group g;
@@ -462,20 +559,32 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
         const int n = min(n0 + r, a.d - 1);  // partial last N-tile: re-read
         return (shared ? a.ws_down + (size_t)n * Kfull : a.w_down + ((size_t)g.e * a.d + n) * Kfull) + kb;
     };
-    const LoadPlan<kDownKW> plan = make_plan<kDownKW, MX>(row_a, row_b);
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int wm = wave >> 2, wn = wave & 3;
     const int brow[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
     floatx4 acc[4][4];
     zero(acc);
-    if constexpr (MX) {
+    if constexpr (WF == kWMx) {
         // This thread's B row (tile row threadIdx.x / 2) of W_d, from this split's first block.
+        const LoadPlan<kDownKW> plan = make_plan<kDownKW, true>(row_a, row_b);
         const int n = min(n0 + (int)(threadIdx.x >> 1), a.d - 1);
         const size_t R = (size_t)max(g.e, 0) * a.d + n;
         const size_t nblk = Kfull / 32;
-        const MxRow mb{a.mx_w + (R * nblk + kb / 32) * 16, a.mx_s + R * nblk + kb / 32};
-        grouped_mainloop_mx(sm, plan, mb, K, wm * 64, brow, acc);
+        const MxSrc<kDownKW> src{MxRow{a.mx_w + (R * nblk + kb / 32) * 16, a.mx_s + R * nblk + kb / 32}};
+        grouped_mainloop_regb(sm, plan, src, K, wm * 64, brow, acc);
+    } else if constexpr (WF == kWQ4k) {
+        if (!shared) {
+            const LoadPlan<kDownKW> plan = make_plan<kDownKW, true>(row_a, row_b);
+            const int n = min(n0 + (int)(threadIdx.x >> 1), a.d - 1);
+            const Q4kSrc<kDownKW> src{
+                a.q4_down + ((size_t)g.e * a.d + n) * (Kfull / kQ4kBlockWeights) * kQ4kBlockBytes, kb};
+            grouped_mainloop_regb(sm, plan, src, K, wm * 64, brow, acc);
+        } else {
+            const LoadPlan<kDownKW> plan = make_plan<kDownKW, false>(row_a, row_b);
+            grouped_mainloop(sm, plan, K, wm * 64, brow, acc);
+        }
     } else {
+        const LoadPlan<kDownKW> plan = make_plan<kDownKW, false>(row_a, row_b);
         grouped_mainloop(sm, plan, K, wm * 64, brow, acc);
     }
 
@@ -732,26 +841,36 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
     const int nn_up = (ffmax + 127) / 128;
     // MXFP4 experts: the clamped variant without a shared expert (checked by the caller);
     // w_gate_up / w_down hold the FP4 blocks, the *_scales fields their E8M0 scales.
+    // Q4_K experts: SwiGLU, w_gate / w_up / w_down hold the super-blocks (K multiple of 256).
     const bool mx = L.expert_format == MOE_EXPERTS_MXFP4;
+    const bool q4 = L.expert_format == MOE_EXPERTS_Q4K;
     if (mx && (L.act != MOE_ACT_SWIGLU_OAI || shared || L.d % 64 || L.ff % 32)) return hipErrorInvalidValue;
+    if (q4 && (L.act != MOE_ACT_SWIGLU || L.d % kQ4kBlockWeights || L.ff % kQ4kBlockWeights))
+        return hipErrorInvalidValue;
+    const auto* q4_gate = q4 ? static_cast<const uint8_t*>(L.w_gate) : nullptr;
+    const auto* q4_up = q4 ? static_cast<const uint8_t*>(L.w_up) : nullptr;
+    const auto* q4_down = q4 ? static_cast<const uint8_t*>(L.w_down) : nullptr;
     UpArgs u{static_cast<const uint16_t*>(x), perm_token, groups, meta, tiles,
              static_cast<const uint16_t*>(L.w_gate), static_cast<const uint16_t*>(L.w_up),
              static_cast<const uint16_t*>(L.w_gate_up), static_cast<const uint16_t*>(L.b_gate_up),
              static_cast<const uint16_t*>(L.ws_gate), static_cast<const uint16_t*>(L.ws_up),
-             mx ? static_cast<const uint8_t*>(L.w_gate_up) : nullptr, mx ? L.w_gate_up_scales : nullptr, H,
-             hstride, T, L.d, L.ff, L.shared_ff, nn_up, L.oai_alpha, L.oai_limit, kWalkWindow};
+             mx ? static_cast<const uint8_t*>(L.w_gate_up) : nullptr, mx ? L.w_gate_up_scales : nullptr, q4_gate,
+             q4_up, H, hstride, T, L.d, L.ff, L.shared_ff, nn_up, L.oai_alpha, L.oai_limit, kWalkWindow};
     const dim3 gu((unsigned)grid_blocks(mt, nn_up, kWalkWindow));
     if (mx)
-        gg_up_kernel<true, true><<<gu, kGThreads, 0, s>>>(u);
+        gg_up_kernel<true, kWMx><<<gu, kGThreads, 0, s>>>(u);
+    else if (q4)
+        gg_up_kernel<false, kWQ4k><<<gu, kGThreads, 0, s>>>(u);
     else if (L.act == MOE_ACT_SWIGLU_OAI)
-        gg_up_kernel<true, false><<<gu, kGThreads, 0, s>>>(u);
+        gg_up_kernel<true, kWDense><<<gu, kGThreads, 0, s>>>(u);
     else
-        gg_up_kernel<false, false><<<gu, kGThreads, 0, s>>>(u);
+        gg_up_kernel<false, kWDense><<<gu, kGThreads, 0, s>>>(u);
     const uint8_t* mx_dw = mx ? static_cast<const uint8_t*>(L.w_down) : nullptr;
     const uint8_t* mx_ds = mx ? L.w_down_scales : nullptr;
     const int nn = (L.d + GBN - 1) / GBN;
     const int rows = T * L.k + (shared ? T : 0);
     const auto* b_down = static_cast<const uint16_t*>(L.b_down);
+    const int wf = mx ? kWMx : q4 ? kWQ4k : kWDense;
     if (ksplit > 1) {
         // The reduce grid has a z-slice per tile row: min(BM, T*k) covers every row of a tile
         // (a group never holds more than the T*k routed rows).
@@ -759,11 +878,12 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
             (shared && (L.shared_ff / ksplit) % kDownKW) || L.ff % ksplit || L.shared_ff % ksplit)
             return hipErrorInvalidValue;
         DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down), nullptr,
-                    static_cast<const uint16_t*>(L.ws_down), mx_dw, mx_ds, nullptr, partial, hstride, L.d, L.ff,
-                    L.shared_ff, nn, ksplit, rows, kWalkWindow};
+                    static_cast<const uint16_t*>(L.ws_down), mx_dw, mx_ds, q4_down, nullptr, partial, hstride, L.d,
+                    L.ff, L.shared_ff, nn, ksplit, rows, kWalkWindow};
         const dim3 gs((unsigned)grid_blocks(mt, nn * ksplit, kWalkWindow));
-        if (mx) gg_down_kernel<float, true><<<gs, kGThreads, 0, s>>>(dn);
-        else gg_down_kernel<float, false><<<gs, kGThreads, 0, s>>>(dn);
+        if (wf == kWMx) gg_down_kernel<float, kWMx><<<gs, kGThreads, 0, s>>>(dn);
+        else if (wf == kWQ4k) gg_down_kernel<float, kWQ4k><<<gs, kGThreads, 0, s>>>(dn);
+        else gg_down_kernel<float, kWDense><<<gs, kGThreads, 0, s>>>(dn);
         const dim3 gr((unsigned)((L.d + 1023) / 1024), (unsigned)mt, (unsigned)min(BM, T * L.k));
         if (y_bf16)
             splitk_reduce_kernel<uint16_t><<<gr, 256, 0, s>>>(partial, ksplit, rows, meta, tiles, b_down, row_w,
@@ -774,16 +894,18 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
         return hipGetLastError();
     }
     DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down), b_down,
-                static_cast<const uint16_t*>(L.ws_down), mx_dw, mx_ds, row_w, y, hstride, L.d, L.ff, L.shared_ff,
-                nn, 1, rows, kWalkWindow};
+                static_cast<const uint16_t*>(L.ws_down), mx_dw, mx_ds, q4_down, row_w, y, hstride, L.d, L.ff,
+                L.shared_ff, nn, 1, rows, kWalkWindow};
     const dim3 gd((unsigned)grid_blocks(mt, nn, kWalkWindow));
-    if (mx) {
-        if (y_bf16) gg_down_kernel<uint16_t, true><<<gd, kGThreads, 0, s>>>(dn);
-        else gg_down_kernel<float, true><<<gd, kGThreads, 0, s>>>(dn);
-    } else {
-        if (y_bf16) gg_down_kernel<uint16_t, false><<<gd, kGThreads, 0, s>>>(dn);
-        else gg_down_kernel<float, false><<<gd, kGThreads, 0, s>>>(dn);
-    }
+#define SMOE_GG_DOWN(WF)                                                              \
+    do {                                                                              \
+        if (y_bf16) gg_down_kernel<uint16_t, WF><<<gd, kGThreads, 0, s>>>(dn);        \
+        else gg_down_kernel<float, WF><<<gd, kGThreads, 0, s>>>(dn);                  \
+    } while (0)
+    if (wf == kWMx) SMOE_GG_DOWN(kWMx);
+    else if (wf == kWQ4k) SMOE_GG_DOWN(kWQ4k);
+    else SMOE_GG_DOWN(kWDense);
+#undef SMOE_GG_DOWN
     return hipGetLastError();
 }
 

@@ -97,6 +97,17 @@ hipError_t launch_expert_up_gemv_mx(const moe_layer& L, const void* x, int T, co
                                     const Group* groups, const PlanMeta* meta, float* H, int hstride,
                                     hipStream_t s);
 bool token1_mx_fits(const moe_layer& L);
+// GEMVs over Q4_K routed experts (fp32 H and unweighted fp32 rows, as the dense GEMVs);
+// the bf16 shared expert runs on the dense kernels restricted to its grid row
+// (launch_shared_gemv_*).  q4k_fits: d and ff multiples of 256, at most 4096.
+bool q4k_fits(const moe_layer& L);
+hipError_t launch_expert_gemv_q4k(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
+                                  const Group* groups, const PlanMeta* meta, float* H, int hstride, float* y_perm,
+                                  hipStream_t s);
+hipError_t launch_shared_gemv_up(const moe_layer& L, const void* x, int T, const Group* groups, const PlanMeta* meta,
+                                 float* H, int hstride, hipStream_t s);
+hipError_t launch_shared_gemv_down(const moe_layer& L, int T, const Group* groups, const PlanMeta* meta,
+                                   const float* H, int hstride, float* y_perm, hipStream_t s);
 hipError_t launch_token1_up_mx(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,
                                float* H, int hstride, hipStream_t s);
 hipError_t launch_token_down_combine_mx(const moe_layer& L, int T, const float* H, int hstride, const int32_t* idx,

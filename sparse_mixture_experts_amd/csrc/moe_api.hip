@@ -104,12 +104,18 @@ moe_status check_layer(const moe_layer* L) {
     if (L->d % 64 || L->ff % 64 || L->shared_ff % 64) return MOE_ERR_UNSUPPORTED;
     if (L->n_expert > kMaxExperts || L->k > kMaxK) return MOE_ERR_UNSUPPORTED;
     if (L->path == MOE_PATH_GROUPED && L->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-    if (L->expert_format != MOE_EXPERTS_DENSE && L->expert_format != MOE_EXPERTS_MXFP4) return MOE_ERR_ARG;
+    if (L->expert_format != MOE_EXPERTS_DENSE && L->expert_format != MOE_EXPERTS_MXFP4 &&
+        L->expert_format != MOE_EXPERTS_Q4K)
+        return MOE_ERR_ARG;
     if (L->reserved0 != 0) return MOE_ERR_ARG;
     if (L->expert_format == MOE_EXPERTS_MXFP4) {
         if (!L->w_gate_up_scales || !L->w_down_scales) return MOE_ERR_ARG;
         if (L->dtype != MOE_BF16 || L->act != MOE_ACT_SWIGLU_OAI || L->shared_ff != 0 || !mx_fits(*L))
             return MOE_ERR_UNSUPPORTED;
+    }
+    if (L->expert_format == MOE_EXPERTS_Q4K) {
+        if (L->w_gate_up_scales || L->w_down_scales) return MOE_ERR_ARG;
+        if (L->dtype != MOE_BF16 || L->act != MOE_ACT_SWIGLU || !q4k_fits(*L)) return MOE_ERR_UNSUPPORTED;
     }
     const void* vec_ptrs[] = {L->w_router, L->w_gate, L->w_up, L->w_gate_up, L->w_down,
                               L->ws_gate, L->ws_up, L->ws_down, L->ws_gate_inp};
@@ -233,7 +239,8 @@ moe_status forward_body(const moe_layer* L, const void* x, int32_t T, const void
                                            shared ? logits + L->n_expert : nullptr, o.ld, residual, y, s));
         return MOE_OK;
     }
-    if (T == 1 && !grouped && !dense && token1_mx_fits(*L)) {
+    const bool mxfp4 = L->expert_format == MOE_EXPERTS_MXFP4;
+    if (T == 1 && !grouped && mxfp4 && token1_mx_fits(*L)) {
         // The same three launches over MXFP4 expert weights.
         SMOE_TRY(launch_token1_up_mx(*L, x, logits, idx, w, at<float>(ws, o.H), o.hstride, s));
         SMOE_TRY(launch_token_down_combine_mx(*L, 1, at<float>(ws, o.H), o.hstride, idx, w, nullptr, residual, y, s));
@@ -259,7 +266,7 @@ moe_status forward_body(const moe_layer* L, const void* x, int32_t T, const void
                                            y, s));
         return MOE_OK;
     }
-    if (fused_route && !grouped && !dense && T <= kTokenDownMaxT && token1_mx_fits(*L)) {
+    if (fused_route && !grouped && mxfp4 && T <= kTokenDownMaxT && token1_mx_fits(*L)) {
         SMOE_TRY(launch_expert_up_gemv_mx(*L, x, T, perm_token, at<Group>(ws, o.groups), at<PlanMeta>(ws, o.meta),
                                           at<float>(ws, o.H), o.hstride, s));
         SMOE_TRY(launch_token_down_combine_mx(*L, T, at<float>(ws, o.H), o.hstride, idx, w, perm_inv, residual, y, s));

@@ -19,12 +19,12 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_ROUTE_SOFTMAX_TOPK_RENORM, MOE_ROUTE_TOPK_SOFTMAX = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_SWIGLU_OAI = 0, 1
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_GROUPED = 0, 1, 2
-MOE_EXPERTS_DENSE, MOE_EXPERTS_MXFP4 = 0, 1
+MOE_EXPERTS_DENSE, MOE_EXPERTS_MXFP4, MOE_EXPERTS_Q4K = 0, 1, 2
 
 _ROUTE = {"softmax_topk_renorm": MOE_ROUTE_SOFTMAX_TOPK_RENORM, "topk_softmax": MOE_ROUTE_TOPK_SOFTMAX}
 _ACT = {"swiglu": MOE_ACT_SWIGLU, "swiglu_oai": MOE_ACT_SWIGLU_OAI}
 _PATH = {"auto": MOE_PATH_AUTO, "decode": MOE_PATH_DECODE, "grouped": MOE_PATH_GROUPED}
-_EXPERTS = {"dense": MOE_EXPERTS_DENSE, "mxfp4": MOE_EXPERTS_MXFP4}
+_EXPERTS = {"dense": MOE_EXPERTS_DENSE, "mxfp4": MOE_EXPERTS_MXFP4, "q4k": MOE_EXPERTS_Q4K}
 
 _P = ctypes.c_void_p
 

@@ -263,3 +263,18 @@ def test_noalloc_scratch_size_matches_header():
     m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
     assert m, "MOE_NOALLOC_SCRATCH_BYTES not found"
     assert int(m.group(1)) << int(m.group(2)) == moe.NOALLOC_SCRATCH_BYTES
+
+
+def test_q4k_layer_checks(lib):
+    q4 = dict(expert_format=moe.MOE_EXPERTS_Q4K, d=512, ff=256)
+    assert ws_size(lib, fake_layer(**q4), 4)[0] == moe.MOE_OK
+    assert ws_size(lib, fake_layer(**dict(q4, path=moe.MOE_PATH_GROUPED)), 4)[0] == moe.MOE_OK
+    assert ws_size(lib, fake_layer(**dict(q4, d=320)), 4)[0] == moe.MOE_ERR_UNSUPPORTED      # not a multiple of 256
+    assert ws_size(lib, fake_layer(**dict(q4, ff=192)), 4)[0] == moe.MOE_ERR_UNSUPPORTED
+    assert ws_size(lib, fake_layer(**dict(q4, d=8192)), 4)[0] == moe.MOE_ERR_UNSUPPORTED     # K > 4096
+    assert ws_size(lib, fake_layer(**dict(q4, dtype=moe.MOE_F32)), 4)[0] == moe.MOE_ERR_UNSUPPORTED
+    oai = dict(q4, act=moe.MOE_ACT_SWIGLU_OAI, w_gate_up=FAKE, b_gate_up=FAKE)
+    assert ws_size(lib, fake_layer(**oai), 4)[0] == moe.MOE_ERR_UNSUPPORTED
+    assert ws_size(lib, fake_layer(**dict(q4, w_down_scales=FAKE)), 4)[0] == moe.MOE_ERR_ARG
+    sh = dict(q4, shared_ff=256, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, ws_gate_inp=FAKE)
+    assert ws_size(lib, fake_layer(**sh), 4)[0] == moe.MOE_OK                                # bf16 shared expert

@@ -391,7 +391,8 @@ def test_full_qwen_prefill_zipf():
 @pytest.mark.parametrize("name,T,sample", [("gptoss", 1, None), ("gptoss", 4096, 256),
                                            ("mixtral", 16, None), ("mixtral", 16384, 256),
                                            ("gptoss_mx", 1, None), ("gptoss_mx", 64, None),
-                                           ("gptoss_mx", 1000, 128)])
+                                           ("gptoss_mx", 1000, 128), ("qwen_q4k", 1, None),
+                                           ("qwen_q4k", 64, None), ("qwen_q4k", 2048, 128)])
 def test_full_other_layers(name, T, sample):
     say("full", name, T)
     L, x = case(name, T)
@@ -615,3 +616,70 @@ def test_mxfp4_grouped_expert_ffn_rows():
     _, roff, rpt, _ = oracle.permute(ridx, L["n_expert"])
     assert np.array_equal(off.cpu().numpy(), roff) and np.array_equal(pt.cpu().numpy(), rpt)
     assert_close(to_numpy_y(yp), oracle.expert_rows(L, x, roff, rpt), "bf16", "rows")
+
+
+# ----------------------------------------------------------------------------- Q4_K experts
+
+# Rows of 8, 12 (a ragged lane group of 16) and 64 quant runs per lane group on the up
+# projection; 4 and 8 on the down projection; with and without a bf16 shared expert.
+Q4K_SMALL = [dict(d=512, n_expert=16, ff=256, shared_ff=256),
+             dict(d=768, n_expert=8, ff=512, k=2, shared_ff=0),
+             dict(d=4096, n_expert=4, ff=256, k=2, shared_ff=256)]
+Q4K_IDS = ["d512", "d768", "d4096"]
+
+
+@pytest.mark.parametrize("T", [1, 7, 100])
+@pytest.mark.parametrize("ov", Q4K_SMALL, ids=Q4K_IDS)
+def test_q4k_forward(ov, T):
+    say("q4k forward", ov, T)
+    L, x = case("qwen_q4k", T, **ov)
+    lay = dev_layer("qwen_q4k", **ov)
+    idx, _, _ = moe_mod().route(lay, xdev(x))
+    y = moe_mod().forward(lay, xdev(x))
+    torch.cuda.synchronize()
+    ridx, _, _ = oracle.route(L, x)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    e = assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "bf16", "y")
+    say(f"  rel err {e:.2e}")
+
+
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+@pytest.mark.parametrize("T", [1, 7, 100, 300])
+@pytest.mark.parametrize("ov", Q4K_SMALL, ids=Q4K_IDS)
+def test_q4k_forced_path(ov, T, path):
+    # Both kernel families at every batch size: the GEMVs with several rows per group, the
+    # grouped MFMA path with the super-blocks expanded into LDS (T=7: split-K down tiles).
+    say("q4k", path, ov, T)
+    L, x = case("qwen_q4k", T, **ov)
+    lay = dev_layer("qwen_q4k", **ov)
+    y = moe_mod().forward(lay.with_path(path), xdev(x))
+    torch.cuda.synchronize()
+    e = assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "bf16", "y")
+    say(f"  rel err {e:.2e}")
+
+
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_q4k_expert_ffn_rows(path):
+    # Unweighted expert rows (fp32) through the ABI, including the shared expert's rows.
+    ov = Q4K_SMALL[0]
+    L, x = case("qwen_q4k", 133, **ov)
+    lay = dev_layer("qwen_q4k", **ov).with_path(path)
+    idx, _, _ = moe_mod().route(lay, xdev(x))
+    off, pt, _ = moe_mod().permute(idx, L["n_expert"])
+    yp = moe_mod().expert_ffn(lay, xdev(x), off, pt)
+    torch.cuda.synchronize()
+    ridx, _, _ = oracle.route(L, x)
+    _, roff, rpt, _ = oracle.permute(ridx, L["n_expert"])
+    assert np.array_equal(off.cpu().numpy(), roff) and np.array_equal(pt.cpu().numpy(), rpt)
+    assert_close(to_numpy_y(yp), oracle.expert_rows(L, x, roff, rpt), "bf16", "rows")
+
+
+def test_q4k_shell():
+    ov = Q4K_SMALL[0]
+    for T in (1, 64, 100):
+        L, w, h = shell_case("qwen_q4k", T, **ov)
+        lay = dev_layer("qwen_q4k", **ov)
+        out = moe_mod().forward_shell(lay, xdev(h), xdev(w), EPS)
+        torch.cuda.synchronize()
+        ref = oracle.moe_shell(L, h, w, EPS)
+        assert_shell_close(to_numpy_y(out), ref, oracle.widen(h), "bf16", f"q4k shell T={T}")
