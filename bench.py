@@ -177,6 +177,54 @@ def summarize_pmc(fetch_csv, write_csv, workload, out_path, command, forwards):
     print(f"wrote {out_path}: {total / 1e6:.2f} MB per forward")
 
 
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def summarize_mfma(csv_path, workload, out_path, command):
+    """profiles/<workload>_mfma_counters.md from one rocprofv3 --pmc run of the three
+    MFMA_COUNTERS.  Per kernel (averages over its dispatches): the duration from the
+    dispatch timestamps; executed bf16 MFMA work (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts
+    units of 512 FLOPs, padding rows included) and its rate; the clock the chip ran at
+    (GRBM_GUI_ACTIVE, which sums the 8 XCDs' busy cycles, over the duration); and the
+    share of SIMD cycles whose MFMA unit was busy (SQ_VALU_MFMA_BUSY_CYCLES over
+    GRBM_GUI_ACTIVE / 8 x 1024 SIMDs)."""
+    import csv
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    span = collections.defaultdict(dict)
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            n = _short_kernel(r["Kernel_Name"])
+            vals[n][r["Counter_Name"]] += float(r["Counter_Value"])
+            span[n][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    lines = [f"# MFMA counters: {workload}", "",
+             "Command (from the repository root, one MI355X; the three counters in one run):", "", "```"]
+    lines += command.split("\n")
+    lines += ["```", "",
+              "Per dispatch (averages).  GFLOP executed = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (padding "
+              "rows of the 128-row M-tiles included); clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; "
+              "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs).  The rate is "
+              f"also given as a fraction of the {MFMA_BF16_PEAK / 1e15:.1f} PFLOP/s dense bf16 peak "
+              "(quoted at 2.4 GHz).", "",
+              "| kernel | dispatches | avg us | GFLOP executed | PFLOP/s | of peak | clock GHz | MFMA busy |",
+              "|---|---|---|---|---|---|---|---|"]
+    for n, d in sorted(vals.items(), key=lambda kv: -kv[1].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0)):
+        k = len(span[n])
+        mops = d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) / k
+        if mops <= 0:
+            continue
+        t = sum(span[n].values()) / k
+        grbm = d.get("GRBM_GUI_ACTIVE", 0.0) / k / N_XCD
+        busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / k / max(grbm * N_SIMD, 1.0)
+        rate = mops * 512 / t
+        lines.append(f"| `{n[:70]}` | {k} | {t * 1e6:.1f} | {mops * 512 / 1e9:.1f} | {rate / 1e15:.3f} | "
+                     f"{rate / MFMA_BF16_PEAK:.3f} | {grbm / t / 1e9:.2f} | {busy:.3f} |")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out_path}")
+
+
 # ----------------------------------------------------------------------------- work model
 
 def elem_bytes(L):
@@ -478,6 +526,9 @@ def main():
     ap.add_argument("--pmc-command", default="", help="command lines quoted in that summary")
     ap.add_argument("--pmc-forwards", type=int, default=0,
                     help="forwards (warm-up + timed) in each counter run, for --summarize-pmc")
+    ap.add_argument("--summarize-mfma", metavar="CSV",
+                    help="write profiles/<workload>_mfma_counters.md from a counter CSV of the three "
+                         "MFMA counters (no GPU); --pmc-command gives the command quoted in it")
     ap.add_argument("--forward-only", action="store_true",
                     help="time the forwards of --workload only (no sweep, routing, shell or stage "
                          "pass, no CPU baseline): the mode for rocprofv3 runs")
@@ -490,6 +541,11 @@ def main():
             raise SystemExit("--summarize-pmc needs --pmc-forwards (warm-up + timed steps of the runs)")
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
                       traffic_file(args.workload), args.pmc_command, args.pmc_forwards)
+        return
+
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.workload,
+                       os.path.join(ROOT, "profiles", f"{args.workload}_mfma_counters.md"), args.pmc_command)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void expert_up_gemv_kernel(GemvUp a, const Pla
     if constexpr (PLAN) {
         if (!plan_group(plan, a.ffs > 0, a.T, a.tk, g)) return;
     } else {
-        if (!gemv_group(a.groups, meta, a.ffs > 0, a.T, a.tk, g)) return;
+        if (!gemv_group(a.groups, meta, a.ffs > 0, a.T, a.tk, a.sh_rows, g)) return;
     }
     const int ffg = g.e < 0 ? a.ffs : a.ff;
     const int f0 = (blockIdx.x * 4 + wave_id()) * U;
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void expert_up_gemv_kernel(GemvUp a, const Pla
 template <int KB, typename TT, bool OAI, bool RESIDENT, int NR, bool EXACT, int NT>
 __global__ __launch_bounds__(256) void expert_down_gemv_kernel(GemvDown a, const PlanMeta* meta) {
     Group g;
-    if (!gemv_group(a.groups, meta, a.ffs > 0, a.T, a.tk, g)) return;
+    if (!gemv_group(a.groups, meta, a.ffs > 0, a.T, a.tk, a.sh_rows, g)) return;
     const int i0 = (blockIdx.x * 4 + wave_id()) * NR;
     if (i0 < a.d) down_item<KB, TT, OAI, RESIDENT, NR, NT, EXACT>(a, g, i0);
 }
@@ -154,16 +154,22 @@ __global__ __launch_bounds__(kToken1MaxWaves * kWave) void token1_down_combine_k
     }
 }
 
-// shared_only: one grid row, the shared expert's (grid row 0), for layers whose routed
-// experts run on other kernels.
+// shared_only: only the shared expert's grid rows, for layers whose routed experts run on
+// other kernels; its rows are then cut into chunks of kSharedRows rows (one grid row
+// each), so that the whole expert is not one grid row's serial loop over T tokens.
+constexpr int kSharedRows = 16;
+
 template <typename TT, bool OAI>
 hipError_t launch_up_t(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                        const Group* groups, const PlanMeta* meta, float* H, int hstride, const GemvPlan& plan,
                        hipStream_t s, bool shared_only = false) {
     const bool shared = L.shared_ff > 0;
-    const int gmax = shared_only ? 1 : max_groups(L.n_expert, T, L.k, shared);
+    const int sh_rows = shared_only ? kSharedRows : 0;
+    const int gmax = (shared_only ? 0 : max_groups(L.n_expert, T, L.k, false)) +
+                     (!shared ? 0 : shared_only ? (T + kSharedRows - 1) / kSharedRows : 1);
     GemvUp u{x, perm_token, groups, L.w_gate, L.w_up, L.w_gate_up, L.b_gate_up,
-             L.ws_gate, L.ws_up, H, hstride, T, T * L.k, L.d, L.ff, L.shared_ff, L.oai_alpha, L.oai_limit};
+             L.ws_gate, L.ws_up, H, hstride, T, T * L.k, L.d, L.ff, L.shared_ff, L.oai_alpha, L.oai_limit,
+             sh_rows};
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
     const bool up_res = chunks(L.d, TT::VEC) <= 8;
     // Rows longer than one 8-chunk batch stream in batches of 4 chunks per lane.  One
@@ -217,9 +223,12 @@ template <typename TT, bool OAI>
 hipError_t launch_down_t(const moe_layer& L, int T, const Group* groups, const PlanMeta* meta, const float* H,
                          int hstride, float* y_perm, hipStream_t s, bool shared_only = false) {
     const bool shared = L.shared_ff > 0;
-    const int gmax = shared_only ? 1 : max_groups(L.n_expert, T, L.k, shared);
+    const int sh_rows = shared_only ? kSharedRows : 0;
+    const int gmax = (shared_only ? 0 : max_groups(L.n_expert, T, L.k, false)) +
+                     (!shared ? 0 : shared_only ? (T + kSharedRows - 1) / kSharedRows : 1);
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
-    GemvDown dn{H, groups, L.w_down, L.b_down, L.ws_down, y_perm, hstride, T, T * L.k, L.d, L.ff, L.shared_ff};
+    GemvDown dn{H, groups, L.w_down, L.b_down, L.ws_down, y_perm, hstride, T, T * L.k, L.d, L.ff, L.shared_ff,
+                sh_rows};
     const bool dn_res = chunks(ffmax, TT::VEC) <= 8;
     // Fewer than 64 possible groups (T*k + shared below 64 rows): 4 rows per wave, for
     // more waves in flight.

@@ -259,7 +259,7 @@ __device__ __forceinline__ void mx_down_item(const MxArgs& a, const Group& g, in
 
 // Grid row y takes routed group y (there is no shared expert with MXFP4 experts).
 __device__ __forceinline__ bool mx_group(const MxArgs& a, const PlanMeta* meta, Group& g) {
-    return gemv_group(a.groups, meta, false, a.T, a.tk, g);
+    return gemv_group(a.groups, meta, false, a.T, a.tk, 0, g);
 }
 
 template <int NB>

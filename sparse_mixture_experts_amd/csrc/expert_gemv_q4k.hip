@@ -5,20 +5,26 @@
 // silu(gate . x) * (up . x) then down.  The weights are never expanded in memory: a lane
 // takes 64-weight units of a row (one 32-byte quant run of a super-block plus the block's
 // 16-byte header), 0.56 bytes per weight.  With U = K / 64 units per row, LPR lanes (U
-// rounded up to a power of two, at most 64) share a row and a wave covers 64 / LPR rows
-// at once, so short rows still occupy every lane.
+// rounded up to a power of two, at most 64) share a row and a wave covers P = 64 / LPR
+// rows at once, in NP passes.
 //
-// Up: the quants become bf16 pairs 128 + q (exact), which meet the bf16 activations in
-// v_dot2 (fp32 accumulation); per sub-block, sum q x = dot - 128 sum x, and the unit's
-// contribution is d sc (sum q x) - dmin m (sum x) for each of its two sub-blocks.  Down:
-// H is fp32 on this path, so the quants are widened to fp32 and meet H in FMAs.  Each
-// row's LPR partial sums meet in a butterfly over the LPR lanes.  The shared expert (bf16)
-// runs on the dense GEMV kernels.
+// A block (4 waves) serves one routed group.  Each wave loads its rows' units once and
+// turns the quants into bf16 pairs 128 + q (exact), kept in registers for every row of
+// the group.  The block stages the group's activations in LDS as bf16, up to 4 rows at a
+// time (x for the up kernel; for the down kernel H, fp32 in memory, rounded to bf16 as on
+// the grouped path), so the waves read them from LDS rather than each from the L2.  Per
+// row a lane dots its unit with the activations in v_dot2 (fp32 accumulation); per
+// sub-block, sum q x = dot - 128 sum x, and the unit's contribution is
+// d sc (sum q x) - dmin m (sum x) for each of its two sub-blocks.  Each weight row's LPR
+// partial sums meet in a butterfly over its LPR lanes.  The shared expert (bf16) runs on
+// the dense GEMV kernels.
 #include "internal.h"
 #include "q4k_dev.h"
 
 namespace smoe {
 namespace {
+
+constexpr int kQ4kStepRows = 4;  // activation rows staged in LDS per step (T > 1)
 
 struct Q4kArgs {
     const uint16_t* x;          // [T, d] bf16
@@ -57,238 +63,234 @@ __device__ __forceinline__ float segment_sum(float v) {
     return v;
 }
 
-// One unit (64 weights) of a row: the header and the 32-byte quant run.
-struct Q4kUnit {
-    uint4 head, q0, q1;
-};
-
-__device__ __forceinline__ Q4kUnit load_unit(const uint8_t* row, int unit) {
-    const uint8_t* blk = row + (size_t)(unit >> 2) * kQ4kBlockBytes;
-    const uint8_t* run = blk + 16 + 32 * (unit & 3);
-    return Q4kUnit{ld16(blk), ld16(run), ld16(run + 16)};
-}
-
-__device__ __forceinline__ uint32_t word_of(const Q4kUnit& u, int i) {
-    const uint4& q = i < 4 ? u.q0 : u.q1;
-    const int k = i & 3;
-    return k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w;
-}
-
 __device__ __forceinline__ uint32_t word4(const uint4& v, int k) {
     return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
 }
 
-// sum over the sub-block half H (0: weights 0..31 of the unit, 1: 32..63) of (128 + q) x,
-// x given as 4 16-byte pieces of 8 bf16.
-template <int H>
-__device__ __forceinline__ float q_dot_half(const Q4kUnit& u, const uint4 (&xs)[4]) {
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t w = word_of(u, i);
-        const uint4& xv = xs[i >> 1];
-        const uint32_t x01 = (i & 1) ? xv.z : xv.x, x23 = (i & 1) ? xv.w : xv.y;
-        acc = __builtin_amdgcn_fdot2_f32_bf16(q4k_pair<0, H>(w), __builtin_bit_cast(q4k_bf16x2_t, x01), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(q4k_pair<1, H>(w), __builtin_bit_cast(q4k_bf16x2_t, x23), acc, false);
-    }
-    return acc;
-}
-
-__device__ __forceinline__ float bf16_sum(const uint4 (&xs)[4]) {
-    const q4k_bf16x2_t one = __builtin_bit_cast(q4k_bf16x2_t, 0x3F803F80u);
-    float acc = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(q4k_bf16x2_t, word4(xs[k], c)), one, acc, false);
-    return acc;
-}
-
-template <int LPR>
-struct Lanes {
-    static constexpr int P = 64 / LPR;             // rows a wave covers at once
-    static constexpr int NR = P > 4 ? P : 4;       // rows per wave
-    static constexpr int NP = NR / P;              // passes
+// One unit of a row, decoded: lo[j] / hi[j] hold weights 2j, 2j+1 of the unit's first /
+// second sub-block as bf16 pairs 128 + q; sa, ma / sb, mb are d sc and dmin m of the two.
+struct Q4kDec {
+    uint32_t lo[16], hi[16];
+    float sa, ma, sb, mb;
 };
 
-// One wave: hidden units f0 .. f0 + NR/2 - 1 of routed group g.  Row r of the wave is the
-// gate (r even) or up (r odd) row of unit f0 + r / 2; in pass p, lane l serves row
-// p * P + l / LPR, unit l % LPR.  NT group rows per step.
-template <int LPR, int NT>
-__device__ __forceinline__ void q4k_up_item(const Q4kArgs& a, const Group& g, int f0) {
-    using LN = Lanes<LPR>;
-    constexpr int P = LN::P, NP = LN::NP;
-    const int lane = lane_id();
-    const int sr = lane / LPR, ul = lane % LPR;
-    const int units = a.d / 64;
-    const bool active = ul < units;
-    const int uc = active ? ul : 0;
-    const int nsb = a.d / kQ4kBlockWeights;
-    Q4kUnit w[NP];
-    float sa[NP], ma[NP], sb[NP], mb[NP];
-    int row_f[NP];
+__device__ __forceinline__ void load_unit(const uint8_t* row, int unit, uint4& head, uint4& q0, uint4& q1) {
+    const uint8_t* blk = row + (size_t)(unit >> 2) * kQ4kBlockBytes;
+    const uint8_t* run = blk + 16 + 32 * (unit & 3);
+    head = ld16(blk);
+    q0 = ld16(run);
+    q1 = ld16(run + 16);
+}
+
+// Byte l of the run holds weight l (low nibble) and 32 + l (high nibble): word i of the
+// run gives weights 4i .. 4i+3 of both sub-blocks.
+__device__ __forceinline__ void decode_unit(int unit, const uint4& head, const uint4& q0, const uint4& q1,
+                                            Q4kDec& u) {
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int r = p * P + sr;
-        const int f = min(f0 + r / 2, a.ff - 1);
-        row_f[p] = f0 + r / 2;
-        const uint8_t* base = (r & 1) ? a.w_up : a.w_gate;
-        w[p] = load_unit(base + ((size_t)g.e * a.ff + f) * nsb * kQ4kBlockBytes, uc);
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t w = word4(i < 4 ? q0 : q1, i & 3);
+        u.lo[2 * i] = __builtin_bit_cast(uint32_t, q4k_pair<0, 0>(w));
+        u.lo[2 * i + 1] = __builtin_bit_cast(uint32_t, q4k_pair<1, 0>(w));
+        u.hi[2 * i] = __builtin_bit_cast(uint32_t, q4k_pair<0, 1>(w));
+        u.hi[2 * i + 1] = __builtin_bit_cast(uint32_t, q4k_pair<1, 1>(w));
     }
+    const int c = unit & 3;
+    q4k_sub_scale(head, 2 * c, u.sa, u.ma);
+    q4k_sub_scale(head, 2 * c + 1, u.sb, u.mb);
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(q4k_bf16x2_t, a), __builtin_bit_cast(q4k_bf16x2_t, b),
+                                           acc, false);
+}
+
+// One unit's 64 activations as bf16 pairs: xa (elements 0..31), xb (32..63), and the sums
+// of each half.
+struct Q4kAct {
+    uint32_t xa[16], xb[16];
+    float sxa, sxb;
+};
+
+// LDS layout of a staged activation row: unit u's 16-byte chunk c sits at chunk position
+// c ^ (u & 7) of the unit's 128 bytes, so that the LPR lanes of a row (units 128 bytes
+// apart) read different banks.
+__device__ __forceinline__ int act_chunk(int u, int c) { return u * 8 + (c ^ (u & 7)); }
+
+__device__ __forceinline__ void read_act(const uint4* row, int unit, Q4kAct& x) {
+    const uint32_t one = 0x3F803F80u;  // bf16 pair (1, 1)
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int c = uc & 3;
-        q4k_sub_scale(w[p].head, 2 * c, sa[p], ma[p]);
-        q4k_sub_scale(w[p].head, 2 * c + 1, sb[p], mb[p]);
+    for (int c = 0; c < 8; ++c) {
+        const uint4 v = row[act_chunk(unit, c)];
+        uint32_t* dst = c < 4 ? x.xa : x.xb;
+        const int o = 4 * (c & 3);
+        dst[o] = v.x;
+        dst[o + 1] = v.y;
+        dst[o + 2] = v.z;
+        dst[o + 3] = v.w;
     }
-    for (int tb = 0; tb < g.n; tb += NT) {
-        const int nt = min(NT, g.n - tb);
-        uint4 xa[NT][4], xb[NT][4];
+    x.sxa = 0.0f;
+    x.sxb = 0.0f;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int row = g.row0 + min(tb + t, g.n - 1);
+    for (int j = 0; j < 16; ++j) {
+        x.sxa = dot2(x.xa[j], one, x.sxa);
+        x.sxb = dot2(x.xb[j], one, x.sxb);
+    }
+}
+
+// The unit's contribution to its row's dot product.
+__device__ __forceinline__ float unit_dot(const Q4kDec& u, const Q4kAct& x) {
+    float da = 0.0f, db = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        da = dot2(u.lo[j], x.xa[j], da);
+        db = dot2(u.hi[j], x.xb[j], db);
+    }
+    return u.sa * da + u.sb * db - (128.0f * u.sa + u.ma) * x.sxa - (128.0f * u.sb + u.mb) * x.sxb;
+}
+
+// Stage group rows tb .. tb+nt-1 in LDS as bf16 rows of K (layout act_chunk): x rows
+// (bf16, by token) or H rows (fp32, rounded to nearest even).
+template <bool FROM_H>
+__device__ __forceinline__ void stage_rows(const Q4kArgs& a, const Group& g, int tb, int nt, int K, uint4* lds) {
+    const int chunks = K / 8;  // 16-byte bf16 chunks per row
+    for (int i = threadIdx.x; i < nt * chunks; i += blockDim.x) {
+        const int t = i / chunks, ch = i - t * chunks;
+        const int row = g.row0 + tb + t;
+        uint4 v;
+        if constexpr (FROM_H) {
+            const float* src = a.H + (size_t)row * a.hstride + 8 * ch;
+            const float4 f0 = *reinterpret_cast<const float4*>(src);
+            const float4 f1 = *reinterpret_cast<const float4*>(src + 4);
+            q4k_bf16x2_t p0, p1, p2, p3;
+            p0[0] = (__bf16)f0.x;
+            p0[1] = (__bf16)f0.y;
+            p1[0] = (__bf16)f0.z;
+            p1[1] = (__bf16)f0.w;
+            p2[0] = (__bf16)f1.x;
+            p2[1] = (__bf16)f1.y;
+            p3[0] = (__bf16)f1.z;
+            p3[1] = (__bf16)f1.w;
+            v = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+        } else {
             int tok = a.T == 1 ? 0 : a.perm_token[row];
             tok = min(max(tok, 0), a.T - 1);
-            const uint16_t* xr = a.x + (size_t)tok * a.d + 64 * uc;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                xa[t][k] = ld16(xr + 8 * k);
-                xb[t][k] = ld16(xr + 32 + 8 * k);
-            }
+            v = ld16(a.x + (size_t)tok * a.d + 8 * ch);
         }
-        float acc[NP][NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const float sxa = bf16_sum(xa[t]), sxb = bf16_sum(xb[t]);
-#pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                const float da = q_dot_half<0>(w[p], xa[t]), db = q_dot_half<1>(w[p], xb[t]);
-                float v = sa[p] * da + sb[p] * db - (128.0f * sa[p] + ma[p]) * sxa - (128.0f * sb[p] + mb[p]) * sxb;
-                acc[p][t] = active ? v : 0.0f;
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < NP; ++p)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) acc[p][t] = segment_sum<LPR>(acc[p][t]);
-        // Gate of unit u and its up row: with P >= 2 the up row is the next sub-row (LPR
-        // lanes on); with P == 1 it is the next pass, in the same lane.
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-#pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                float gate = acc[p][t], up;
-                bool writer;
-                int f;
-                if constexpr (P >= 2) {
-                    up = __shfl(gate, (lane + LPR) & 63, kWave);
-                    writer = ul == 0 && (sr & 1) == 0;
-                    f = row_f[p];
-                } else {
-                    if (p & 1) continue;
-                    up = acc[p + 1][t];
-                    writer = lane == 0;
-                    f = row_f[p];
-                }
-                if (writer && t < nt && f < a.ff)
-                    a.H[(size_t)(g.row0 + tb + t) * a.hstride + f] = gate * sigmoidf_(gate) * up;
-            }
-        }
+        lds[t * chunks + act_chunk(ch >> 3, ch & 7)] = v;
     }
 }
 
-// One wave: output dims i0 .. i0 + NR - 1 of routed group g (row r = dim i0 + r), NT H
-// rows per step.
-template <int LPR, int NT>
-__device__ __forceinline__ void q4k_down_item(const Q4kArgs& a, const Group& g, int i0) {
-    using LN = Lanes<LPR>;
-    constexpr int P = LN::P, NP = LN::NP;
+template <int LPR, int NP>
+struct Lanes {
+    static constexpr int P = 64 / LPR;  // rows a wave covers at once
+    static constexpr int NR = P * NP;   // rows per wave
+};
+
+// Up: one wave owns hidden units f0 .. f0 + NR/2 - 1 of routed group g.  Row r of the
+// wave is the gate (r even) or up (r odd) row of unit f0 + r / 2; in pass p, lane l serves
+// row p * P + l / LPR, unit l % LPR.  With P >= 2 the up row is the next sub-row (LPR
+// lanes on); with P == 1 it is the next pass, in the same lane.
+template <int LPR, int NP, int NT>
+__global__ __launch_bounds__(256) void expert_up_gemv_q4k_kernel(Q4kArgs a) {
+    using LN = Lanes<LPR, NP>;
+    constexpr int P = LN::P, NR = LN::NR;
+    static_assert(P >= 2 || NP % 2 == 0, "gate and up rows pair up");
+    extern __shared__ uint4 act[];
+    Group g;
+    if (!q4k_group(a, g)) return;
+    const int f0 = (blockIdx.x * 4 + wave_id()) * (NR / 2);
     const int lane = lane_id();
     const int sr = lane / LPR, ul = lane % LPR;
-    const int units = a.ff / 64;
-    const bool active = ul < units;
+    const bool active = ul < a.d / 64;
     const int uc = active ? ul : 0;
-    const int nsb = a.ff / kQ4kBlockWeights;
-    Q4kUnit w[NP];
-    float sa[NP], ma[NP], sb[NP], mb[NP];
+    const int nsb = a.d / kQ4kBlockWeights;
+    Q4kDec w[NP];
+    {
+        uint4 hd[NP], q0[NP], q1[NP];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int i = min(i0 + p * P + sr, a.d - 1);
-        w[p] = load_unit(a.w_down + ((size_t)g.e * a.d + i) * nsb * kQ4kBlockBytes, uc);
-    }
+        for (int p = 0; p < NP; ++p) {
+            const int r = p * P + sr;
+            const int f = min(f0 + r / 2, a.ff - 1);
+            const uint8_t* base = (r & 1) ? a.w_up : a.w_gate;
+            load_unit(base + ((size_t)g.e * a.ff + f) * nsb * kQ4kBlockBytes, uc, hd[p], q0[p], q1[p]);
+        }
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int c = uc & 3;
-        q4k_sub_scale(w[p].head, 2 * c, sa[p], ma[p]);
-        q4k_sub_scale(w[p].head, 2 * c + 1, sb[p], mb[p]);
+        for (int p = 0; p < NP; ++p) decode_unit(uc, hd[p], q0[p], q1[p], w[p]);
     }
+    const int chunks = a.d / 8;
     for (int tb = 0; tb < g.n; tb += NT) {
         const int nt = min(NT, g.n - tb);
-        float4 ha[NT][8], hb[NT][8];
+        if (tb > 0) __syncthreads();  // every wave is done with the previous rows
+        stage_rows<false>(a, g, tb, nt, a.d, act);
+        __syncthreads();
+        if (f0 >= a.ff) continue;
+        for (int t = 0; t < nt; ++t) {
+            Q4kAct x;
+            read_act(act + t * chunks, uc, x);
+            float acc[NP];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const float* hr = a.H + (size_t)(g.row0 + min(tb + t, g.n - 1)) * a.hstride + 64 * uc;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                ha[t][k] = *reinterpret_cast<const float4*>(hr + 4 * k);
-                hb[t][k] = *reinterpret_cast<const float4*>(hr + 32 + 4 * k);
-            }
-        }
-        float acc[NP][NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            float sha = 0.0f, shb = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                sha += (ha[t][k].x + ha[t][k].y) + (ha[t][k].z + ha[t][k].w);
-                shb += (hb[t][k].x + hb[t][k].y) + (hb[t][k].z + hb[t][k].w);
-            }
+            for (int p = 0; p < NP; ++p) acc[p] = segment_sum<LPR>(active ? unit_dot(w[p], x) : 0.0f);
+            const size_t hrow = (size_t)(g.row0 + tb + t) * a.hstride;
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                float da = 0.0f, db = 0.0f;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const uint32_t wd = word_of(w[p], k);
-                    const uint32_t lo = wd & 0x0F0F0F0Fu, hi = (wd >> 4) & 0x0F0F0F0Fu;
-                    da = fmaf((float)(lo & 0xFFu), ha[t][k].x, da);
-                    da = fmaf((float)((lo >> 8) & 0xFFu), ha[t][k].y, da);
-                    da = fmaf((float)((lo >> 16) & 0xFFu), ha[t][k].z, da);
-                    da = fmaf((float)(lo >> 24), ha[t][k].w, da);
-                    db = fmaf((float)(hi & 0xFFu), hb[t][k].x, db);
-                    db = fmaf((float)((hi >> 8) & 0xFFu), hb[t][k].y, db);
-                    db = fmaf((float)((hi >> 16) & 0xFFu), hb[t][k].z, db);
-                    db = fmaf((float)(hi >> 24), hb[t][k].w, db);
+                const int f = f0 + (p * P + sr) / 2;
+                if constexpr (P >= 2) {
+                    const float up = __shfl(acc[p], (lane + LPR) & 63, kWave);
+                    if (ul == 0 && (sr & 1) == 0 && f < a.ff) a.H[hrow + f] = acc[p] * sigmoidf_(acc[p]) * up;
+                } else if ((p & 1) == 0) {
+                    if (lane == 0 && f < a.ff) a.H[hrow + f] = acc[p] * sigmoidf_(acc[p]) * acc[p + 1];
                 }
-                const float v = sa[p] * da - ma[p] * sha + sb[p] * db - mb[p] * shb;
-                acc[p][t] = active ? v : 0.0f;
             }
         }
-#pragma unroll
-        for (int p = 0; p < NP; ++p)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const float s = segment_sum<LPR>(acc[p][t]);
-                const int i = i0 + p * P + sr;
-                if (ul == 0 && t < nt && i < a.d) a.y[(size_t)(g.row0 + tb + t) * a.d + i] = s;
-            }
     }
 }
 
-template <int LPR, int NT>
-__global__ __launch_bounds__(256) void expert_up_gemv_q4k_kernel(Q4kArgs a) {
-    Group g;
-    if (!q4k_group(a, g)) return;
-    const int f0 = (blockIdx.x * 4 + wave_id()) * (Lanes<LPR>::NR / 2);
-    if (f0 < a.ff) q4k_up_item<LPR, NT>(a, g, f0);
-}
-
-template <int LPR, int NT>
+// Down: one wave owns output dims i0 .. i0 + NR - 1 of routed group g (dim i0 + p * P +
+// l / LPR in pass p).
+template <int LPR, int NP, int NT>
 __global__ __launch_bounds__(256) void expert_down_gemv_q4k_kernel(Q4kArgs a) {
+    using LN = Lanes<LPR, NP>;
+    constexpr int P = LN::P, NR = LN::NR;
+    extern __shared__ uint4 act[];
     Group g;
     if (!q4k_group(a, g)) return;
-    const int i0 = (blockIdx.x * 4 + wave_id()) * Lanes<LPR>::NR;
-    if (i0 < a.d) q4k_down_item<LPR, NT>(a, g, i0);
+    const int i0 = (blockIdx.x * 4 + wave_id()) * NR;
+    const int lane = lane_id();
+    const int sr = lane / LPR, ul = lane % LPR;
+    const bool active = ul < a.ff / 64;
+    const int uc = active ? ul : 0;
+    const int nsb = a.ff / kQ4kBlockWeights;
+    Q4kDec w[NP];
+    {
+        uint4 hd[NP], q0[NP], q1[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int i = min(i0 + p * P + sr, a.d - 1);
+            load_unit(a.w_down + ((size_t)g.e * a.d + i) * nsb * kQ4kBlockBytes, uc, hd[p], q0[p], q1[p]);
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) decode_unit(uc, hd[p], q0[p], q1[p], w[p]);
+    }
+    const int chunks = a.ff / 8;
+    for (int tb = 0; tb < g.n; tb += NT) {
+        const int nt = min(NT, g.n - tb);
+        if (tb > 0) __syncthreads();
+        stage_rows<true>(a, g, tb, nt, a.ff, act);
+        __syncthreads();
+        if (i0 >= a.d) continue;
+        for (int t = 0; t < nt; ++t) {
+            Q4kAct h;
+            read_act(act + t * chunks, uc, h);
+            const size_t yrow = (size_t)(g.row0 + tb + t) * a.d;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const float s = segment_sum<LPR>(active ? unit_dot(w[p], h) : 0.0f);
+                const int i = i0 + p * P + sr;
+                if (ul == 0 && i < a.d) a.y[yrow + i] = s;
+            }
+        }
+    }
 }
 
 // Lanes per row for a K axis: K / 64 units rounded up to a power of two (K <= 4096).
@@ -299,46 +301,40 @@ int lanes_per_row(int K) {
     return l;
 }
 
-template <int NT>
-hipError_t launch_q4k_t(const Q4kArgs& a, int gmax, hipStream_t s) {
-#define SMOE_Q4K_UP(LPR)                                                                                  \
-    case LPR: {                                                                                           \
-        const dim3 g((a.ff + 4 * (Lanes<LPR>::NR / 2) - 1) / (4 * (Lanes<LPR>::NR / 2)), gmax);          \
-        expert_up_gemv_q4k_kernel<LPR, NT><<<g, 256, 0, s>>>(a);                                          \
-        break;                                                                                            \
+// Passes per wave: rows per wave R = 8 for one token (more waves in flight) or 16 for
+// more (the decoded weights serve every row of the group), NP = R / P, at most 4 (128
+// registers of decoded weights).  P == 1 gives 4 passes, even as the up kernel needs.
+constexpr int q4k_passes(int P, bool many) {
+    const int r = many ? 16 : 8;
+    return r / P > 4 ? 4 : (r / P < 1 ? 1 : r / P);
+}
+
+template <int LPR, bool MANY>
+hipError_t launch_q4k_lpr(const Q4kArgs& a, int gmax, bool down, hipStream_t s) {
+    constexpr int NP = q4k_passes(64 / LPR, MANY);
+    constexpr int NT = MANY ? kQ4kStepRows : 1;
+    constexpr int NR = Lanes<LPR, NP>::NR;
+    if (!down) {
+        const int units_per_block = 4 * (NR / 2);
+        const dim3 grid((a.ff + units_per_block - 1) / units_per_block, gmax);
+        expert_up_gemv_q4k_kernel<LPR, NP, NT><<<grid, 256, NT * a.d * 2, s>>>(a);
+    } else {
+        const dim3 grid((a.d + 4 * NR - 1) / (4 * NR), gmax);
+        expert_down_gemv_q4k_kernel<LPR, NP, NT><<<grid, 256, NT * a.ff * 2, s>>>(a);
     }
-    switch (lanes_per_row(a.d)) {
-        SMOE_Q4K_UP(4)
-        SMOE_Q4K_UP(8)
-        SMOE_Q4K_UP(16)
-        SMOE_Q4K_UP(32)
-        SMOE_Q4K_UP(64)
-        default:
-            return hipErrorInvalidValue;
-    }
-#undef SMOE_Q4K_UP
     return hipGetLastError();
 }
 
-template <int NT>
-hipError_t launch_q4k_down_t(const Q4kArgs& a, int gmax, hipStream_t s) {
-#define SMOE_Q4K_DOWN(LPR)                                                                                \
-    case LPR: {                                                                                           \
-        const dim3 g((a.d + 4 * Lanes<LPR>::NR - 1) / (4 * Lanes<LPR>::NR), gmax);                        \
-        expert_down_gemv_q4k_kernel<LPR, NT><<<g, 256, 0, s>>>(a);                                        \
-        break;                                                                                            \
+template <bool MANY>
+hipError_t launch_q4k(const Q4kArgs& a, int gmax, bool down, hipStream_t s) {
+    switch (lanes_per_row(down ? a.ff : a.d)) {
+        case 4: return launch_q4k_lpr<4, MANY>(a, gmax, down, s);
+        case 8: return launch_q4k_lpr<8, MANY>(a, gmax, down, s);
+        case 16: return launch_q4k_lpr<16, MANY>(a, gmax, down, s);
+        case 32: return launch_q4k_lpr<32, MANY>(a, gmax, down, s);
+        case 64: return launch_q4k_lpr<64, MANY>(a, gmax, down, s);
+        default: return hipErrorInvalidValue;
     }
-    switch (lanes_per_row(a.ff)) {
-        SMOE_Q4K_DOWN(4)
-        SMOE_Q4K_DOWN(8)
-        SMOE_Q4K_DOWN(16)
-        SMOE_Q4K_DOWN(32)
-        SMOE_Q4K_DOWN(64)
-        default:
-            return hipErrorInvalidValue;
-    }
-#undef SMOE_Q4K_DOWN
-    return hipGetLastError();
 }
 
 }  // namespace
@@ -357,10 +353,10 @@ hipError_t launch_expert_gemv_q4k(const moe_layer& L, const void* x, int T, cons
                     static_cast<const uint8_t*>(L.w_down), H, y_perm, hstride, T, T * L.k, L.d, L.ff,
                     shared ? 1 : 0};
     const int routed = max_groups(L.n_expert, T, L.k, false);
-    hipError_t e = T == 1 ? launch_q4k_t<1>(a, routed, s) : launch_q4k_t<2>(a, routed, s);
+    hipError_t e = T == 1 ? launch_q4k<false>(a, routed, false, s) : launch_q4k<true>(a, routed, false, s);
     if (e != hipSuccess) return e;
     if (shared && (e = launch_shared_gemv_up(L, x, T, groups, meta, H, hstride, s)) != hipSuccess) return e;
-    e = T == 1 ? launch_q4k_down_t<1>(a, routed, s) : launch_q4k_down_t<2>(a, routed, s);
+    e = T == 1 ? launch_q4k<false>(a, routed, true, s) : launch_q4k<true>(a, routed, true, s);
     if (e != hipSuccess) return e;
     if (shared) return launch_shared_gemv_down(L, T, groups, meta, H, hstride, y_perm, s);
     return hipSuccess;

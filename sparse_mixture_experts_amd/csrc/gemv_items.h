@@ -32,6 +32,7 @@ struct GemvUp {
     float* H;
     int hstride, T, tk, d, ff, ffs;  // tk = T * k routed rows
     float alpha, limit;
+    int sh_rows;  // shared-expert rows per grid row (0: all T in one)
 };
 
 struct GemvDown {
@@ -42,25 +43,33 @@ struct GemvDown {
     const void* ws_down;  // [d, ffs]
     float* y;
     int hstride, T, tk, d, ff, ffs;
+    int sh_rows;  // shared-expert rows per grid row (0: all T in one)
 };
 
+// Grid rows of the shared expert: its T rows cut into chunks of sh_rows (0: one chunk).
+__device__ __forceinline__ int shared_grid_rows(bool has_shared, int T, int sh_rows) {
+    return !has_shared ? 0 : sh_rows > 0 ? (T + sh_rows - 1) / sh_rows : 1;
+}
+
 // Group of grid row blockIdx.y.  The shared expert (when there is one) is the last group
-// of the list and always holds rows tk .. tk+T-1; grid row 0 takes it, built here without
-// a load, so that its longer work starts first.  Grid row y > 0 (or y without a shared
-// expert) takes routed group y - 1 (or y).  The group entry and the group count are
-// loaded together, before the count is checked (the list has room for every grid row),
-// so the two reads cost one memory latency.  Returns false for rows past the count.
+// of the list and always holds rows tk .. tk+T-1; the first grid rows take it, in chunks
+// of sh_rows rows (built here without a load), so that its longer work starts first.  The
+// grid rows after them take routed groups 0, 1, ...  The group entry and the group count
+// are loaded together, before the count is checked (the list has room for every grid
+// row), so the two reads cost one memory latency.  Returns false for rows past the count.
 __device__ __forceinline__ bool gemv_group(const Group* groups, const PlanMeta* meta, bool has_shared,
-                                           int T, int tk, Group& g) {
+                                           int T, int tk, int sh_rows, Group& g) {
     const int y = blockIdx.y;
-    const int gi = has_shared ? max(y - 1, 0) : y;
+    const int n_sh = shared_grid_rows(has_shared, T, sh_rows);
+    const int gi = max(y - n_sh, 0);
     // Loaded on every row, so that nothing branches before the loads are issued; both
     // values are needed at the asm, so the compiler may not sink either load past a check.
     const Group cand = groups[gi];
     const int n_groups = meta->n_groups;
     asm volatile("" ::"s"(cand.e), "s"(cand.row0), "s"(cand.n), "s"(n_groups));
-    if (has_shared && y == 0) {
-        g = Group{-1, tk, T, 0};
+    if (y < n_sh) {
+        const int r0 = sh_rows > 0 ? y * sh_rows : 0;
+        g = Group{-1, tk + r0, sh_rows > 0 ? min(sh_rows, T - r0) : T, 0};
         return true;
     }
     if (gi >= n_groups - (has_shared ? 1 : 0)) return false;
@@ -218,8 +227,9 @@ __device__ __forceinline__ void up_item(const GemvUp& a, const Group& g, int f0)
     // loads so that waiting for it does not wait for them.
     auto step_tokens = [&](int tb) {
         const int r = min(tb + (lane & (NT - 1)), g.n - 1);
-        // Shared rows are the tokens in order; with one token every row is token 0.
-        const int tok = (shared || a.T == 1) ? r : a.perm_token[g.row0 + r];
+        // Shared rows are the tokens in order (row tk + t is token t); with one token
+        // every row is token 0.
+        const int tok = shared ? g.row0 - a.tk + r : a.T == 1 ? r : a.perm_token[g.row0 + r];
         return min(max(tok, 0), a.T - 1);
     };
     auto step = [&](int tb, int tok_v, const uint4 (&wv)[RESIDENT ? KB : 1][NR]) {
