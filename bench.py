@@ -356,6 +356,27 @@ def time_workload(name, steps, warmup, layer_cache, forward_only=False):
     torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) for a, b in ev)
 
+    graph_ms = None
+    if decode:
+        # The same forwards replayed from HIP graphs (one captured forward per weight copy
+        # and token batch pair), timed like the step: what a caller that captures the
+        # layer saves in launch work.  Reported beside the eager value, not as it.
+        graphs = []
+        for i in range(n_batches):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+        def replay(i):
+            graphs[i % n_batches].replay()
+
+        for i in range(warmup):
+            replay(i)
+        graph_ms = timed(replay, steps, warmup)
+        del graphs
+
     # Realised active experts per batch (from the library's own routing).
     U = []
     for x in xs:
@@ -400,6 +421,9 @@ def time_workload(name, steps, warmup, layer_cache, forward_only=False):
         "ms_p10": per[len(per) // 10], "ms_median": statistics.median(per), "ms_p90": per[(9 * len(per)) // 10],
         "active_experts_mean": U_mean, "stage_ms": stage_ms, "shell_ms_per_step": shell_ms,
     })
+    if graph_ms is not None:
+        res["graph_ms_per_step"] = graph_ms
+        res["graph_tokens_per_s"] = T / (graph_ms / 1e3)
     traffic = recorded_traffic(name)
     if decode:
         lb = layer_bytes(L, T, U_mean)
@@ -434,7 +458,8 @@ def time_workload(name, steps, warmup, layer_cache, forward_only=False):
                                  "algorithmic_flops": sf}
     log(f"[{name}] {ms_step * 1e3:.1f} us/step, {res['tokens_per_s']:.0f} tok/s, "
         f"roofline frac {res['roofline']['frac']:.3f}, stage {stage_ms * 1e3:.1f} us "
-        f"({res['stage_roofline']['frac']:.3f}), shell {shell_ms * 1e3:.1f} us/step")
+        f"({res['stage_roofline']['frac']:.3f}), shell {shell_ms * 1e3:.1f} us/step"
+        + (f", graph replay {res['graph_ms_per_step'] * 1e3:.1f} us/step" if "graph_ms_per_step" in res else ""))
     del layers, xs, ws, y, yp, plans
     torch.cuda.empty_cache()
     return res

@@ -44,16 +44,19 @@ __global__ __launch_bounds__(256) void expert_down_gemv_kernel(GemvDown a, const
     if (i0 < a.d) down_item<KB, TT, OAI, RESIDENT, NR, NT, EXACT>(a, g, i0);
 }
 
-// One token: routing and the up projection in one kernel.  Grid row 0 (with a shared
-// expert) is the shared expert, hidden row k, and starts streaming at once; grid row y
-// of a pick j = y - 1 (or y) runs the token's top-k on every wave (the same wave top-k as
-// the routing kernels) and takes its j-th pick, hidden row j.  Block 0 of each pick row
-// records the pick (idx[j], w[j]) for the down kernel.
+// One token: routing and the up projection in one kernel.  With shared_row, grid row 0
+// is the shared expert, hidden row k, and starts streaming at once (without it, the
+// shared expert's up GEMV ran in the router launch, or there is none); grid row y of a
+// pick j = y - 1 (or y) runs the token's top-k on every wave (the same wave top-k as the
+// routing kernels) and takes its j-th pick, hidden row j.  Block 0 of each pick row
+// records the pick (idx[j], w[j]) for the down kernel.  (One top-k per block, handed to
+// the other waves through LDS, measured no faster: the waves wait for the logits either
+// way, and the top-k's arithmetic is not what the kernel waits on.)
 template <int KB, typename TT, bool OAI, bool RESIDENT, int U, bool EXACT>
 __global__ __launch_bounds__(256) void token1_up_kernel(GemvUp a, const float* __restrict__ logits, int E,
                                                         int k, int mode, float scale, int32_t* __restrict__ idx,
-                                                        float* __restrict__ w) {
-    const bool has_shared = a.ffs > 0;
+                                                        float* __restrict__ w, int shared_row) {
+    const bool has_shared = a.ffs > 0 && shared_row;
     const int y = blockIdx.y;
     const int f0 = (blockIdx.x * 4 + wave_id()) * U;
     Group g;
@@ -75,6 +78,28 @@ __global__ __launch_bounds__(256) void token1_up_kernel(GemvUp a, const float* _
     const int ffg = g.e < 0 ? a.ffs : a.ff;
     // Every group holds the one token: one row per step.
     if (f0 < ffg) up_item<KB, TT, OAI, RESIDENT, U, EXACT, 1>(a, g, f0);
+}
+
+// One token with a shared expert: the router rows and the shared expert's up GEMV in one
+// launch (the shared expert does not depend on the routing, so its weights stream while
+// the router's do).  Blocks 0 .. n_sh-1 (a multiple of 8) run the shared expert's gate and
+// up rows, hidden row k; block n_sh + b runs router row group b as router_gemv_kernel does
+// for one token (rows 0..E-1 experts, row E the shared gate; row group b on XCD b % 8,
+// which n_sh being a multiple of 8 keeps).
+template <int KB, bool EXACT>
+__global__ __launch_bounds__(256) void token1_router_shared_kernel(GemvUp a, const uint16_t* __restrict__ w_router,
+                                                                   const float* __restrict__ b_router,
+                                                                   const uint16_t* __restrict__ w_sg, int E,
+                                                                   int n_sh, float* __restrict__ logits) {
+    if ((int)blockIdx.x < n_sh) {
+        const int f0 = (blockIdx.x * 4 + wave_id()) * kUpUnits;
+        if (f0 < a.ffs) up_item<KB, BF16, false, true, kUpUnits, EXACT, 1>(a, Group{-1, a.tk, 1, 0}, f0);
+        return;
+    }
+    const int row0 = (blockIdx.x - n_sh) * 4 + wave_id();
+    if (row0 > E) return;
+    router_rows_wave<KB, BF16, 1>(static_cast<const uint16_t*>(a.x), w_router, b_router, w_sg, 1, a.d, E, E + 1,
+                                  row0, 0, 1, logits, E + 1);
 }
 
 // A few tokens: the down projection of every pick and of the shared expert, and the
@@ -281,8 +306,8 @@ hipError_t launch_down_t(const moe_layer& L, int T, const Group* groups, const P
 
 template <typename TT, bool OAI>
 hipError_t launch_token1_up_t(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,
-                              float* H, int hstride, hipStream_t s) {
-    const bool shared = L.shared_ff > 0;
+                              float* H, int hstride, bool shared_done, hipStream_t s) {
+    const bool shared = L.shared_ff > 0 && !shared_done;
     GemvUp u{x, nullptr, nullptr, L.w_gate, L.w_up, L.w_gate_up, L.b_gate_up,
              L.ws_gate, L.ws_up, H, hstride, 1, L.k, L.d, L.ff, L.shared_ff, L.oai_alpha, L.oai_limit};
     const int ffmax = L.ff > L.shared_ff ? L.ff : L.shared_ff;
@@ -295,7 +320,7 @@ hipError_t launch_token1_up_t(const moe_layer& L, const void* x, const float* lo
     switch (kb) {
 #define SMOE_UP_LAUNCH(KB, RES, EX)                                                              \
     token1_up_kernel<KB, TT, OAI, RES, KB == 8 ? 1 : kUpUnits, EX>                               \
-        <<<gu, 256, 0, s>>>(u, logits, L.n_expert, L.k, L.route, L.route_scale, idx, w)
+        <<<gu, 256, 0, s>>>(u, logits, L.n_expert, L.k, L.route, L.route_scale, idx, w, shared ? 1 : 0)
 #define SMOE_UP_CASE(KB)                                                                       \
     case KB:                                                                                   \
         if (exact_k(L.d, TT::VEC, KB)) {                                                       \
@@ -410,14 +435,49 @@ hipError_t launch_expert_up_gemv(const moe_layer& L, const void* x, int T, const
 }
 
 hipError_t launch_token1_up(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,
-                            float* H, int hstride, hipStream_t s) {
+                            float* H, int hstride, bool shared_done, hipStream_t s) {
     if (!token1_fits(L)) return hipErrorInvalidValue;
     const bool oai = L.act == MOE_ACT_SWIGLU_OAI;
     if (L.dtype == MOE_BF16)
-        return oai ? launch_token1_up_t<BF16, true>(L, x, logits, idx, w, H, hstride, s)
-                   : launch_token1_up_t<BF16, false>(L, x, logits, idx, w, H, hstride, s);
-    return oai ? launch_token1_up_t<F32, true>(L, x, logits, idx, w, H, hstride, s)
-               : launch_token1_up_t<F32, false>(L, x, logits, idx, w, H, hstride, s);
+        return oai ? launch_token1_up_t<BF16, true>(L, x, logits, idx, w, H, hstride, shared_done, s)
+                   : launch_token1_up_t<BF16, false>(L, x, logits, idx, w, H, hstride, shared_done, s);
+    return oai ? launch_token1_up_t<F32, true>(L, x, logits, idx, w, H, hstride, shared_done, s)
+               : launch_token1_up_t<F32, false>(L, x, logits, idx, w, H, hstride, shared_done, s);
+}
+
+// The router and the shared expert in one launch: bf16 layers with a shared expert whose
+// rows take one register batch of at most 4 chunks per lane (the router kernel's batch).
+bool token1_router_shared_fits(const moe_layer& L) {
+    return token1_fits(L) && L.shared_ff > 0 && L.dtype == MOE_BF16 && pick_kb(L.d, BF16::VEC) <= 4 &&
+           chunks(L.d, BF16::VEC) <= 8;
+}
+
+hipError_t launch_token1_router_shared(const moe_layer& L, const void* x, float* logits, int ld, float* H,
+                                       int hstride, hipStream_t s) {
+    if (!token1_router_shared_fits(L) || ld != L.n_expert + 1) return hipErrorInvalidValue;
+    GemvUp u{x, nullptr, nullptr, L.w_gate, L.w_up, L.w_gate_up, L.b_gate_up,
+             L.ws_gate, L.ws_up, H, hstride, 1, L.k, L.d, L.ff, L.shared_ff, L.oai_alpha, L.oai_limit, 0};
+    const int n_sh = 8 * ((L.shared_ff + 4 * kUpUnits * 8 - 1) / (4 * kUpUnits * 8));
+    const int n_router = (L.n_expert + 1 + 3) / 4;
+    const dim3 grid(n_sh + n_router);
+    const auto* wr = static_cast<const uint16_t*>(L.w_router);
+    const auto* wsg = static_cast<const uint16_t*>(L.ws_gate_inp);
+    switch (pick_kb(L.d, BF16::VEC)) {
+#define SMOE_RS_CASE(KB)                                                                                   \
+    case KB:                                                                                              \
+        if (exact_k(L.d, BF16::VEC, KB))                                                                  \
+            token1_router_shared_kernel<KB, true><<<grid, 256, 0, s>>>(u, wr, L.b_router, wsg, L.n_expert, n_sh, logits); \
+        else                                                                                              \
+            token1_router_shared_kernel<KB, false><<<grid, 256, 0, s>>>(u, wr, L.b_router, wsg, L.n_expert, n_sh, logits); \
+        break;
+        SMOE_RS_CASE(1)
+        SMOE_RS_CASE(2)
+        SMOE_RS_CASE(4)
+        default:
+            return hipErrorInvalidValue;
+#undef SMOE_RS_CASE
+    }
+    return hipGetLastError();
 }
 
 bool token1_fits(const moe_layer& L) {

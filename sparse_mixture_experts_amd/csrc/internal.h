@@ -124,7 +124,12 @@ hipError_t launch_expert_up_gemv(const moe_layer& L, const void* x, int T, const
 // shared_gate[t * gate_ld]).  Both need k (+1 with a shared expert) <= 16.
 bool token1_fits(const moe_layer& L);
 hipError_t launch_token1_up(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,
-                            float* H, int hstride, hipStream_t s);
+                            float* H, int hstride, bool shared_done, hipStream_t s);
+// One token, bf16 with a shared expert: the router logits (ld = E + 1) and the shared
+// expert's up GEMV (hidden row k) in one launch; token1_up then runs with shared_done.
+bool token1_router_shared_fits(const moe_layer& L);
+hipError_t launch_token1_router_shared(const moe_layer& L, const void* x, float* logits, int ld, float* H,
+                                       int hstride, hipStream_t s);
 hipError_t launch_token_down_combine(const moe_layer& L, int T, const float* H, int hstride, const int32_t* idx,
                                      const float* w, const int32_t* perm_inv, const float* shared_gate,
                                      int gate_ld, const void* residual, void* y, hipStream_t s);

@@ -229,12 +229,18 @@ moe_status forward_body(const moe_layer* L, const void* x, int32_t T, const void
     // Grouped path: rows carry their routing weight and are stored in bf16.
     float* row_w = grouped ? at<float>(ws, o.row_w) : nullptr;
     void* y_rows = at<void>(ws, o.yperm);
-    SMOE_TRY(run_router(*L, norm ? residual : x, T, logits, o.ld, s, norm));
     const bool dense = L->expert_format == MOE_EXPERTS_DENSE;
+    // One token with a shared expert: its up GEMV streams in the router launch.
+    const bool router_shared = T == 1 && !grouped && dense && !norm && o.ld == L->n_expert + 1 &&
+                               token1_router_shared_fits(*L);
+    if (router_shared)
+        SMOE_TRY(launch_token1_router_shared(*L, x, logits, o.ld, at<float>(ws, o.H), o.hstride, s));
+    else
+        SMOE_TRY(run_router(*L, norm ? residual : x, T, logits, o.ld, s, norm));
     if (T == 1 && !grouped && dense && token1_fits(*L)) {
         // One token: top-k inside the up GEMV, then the down GEMVs and the combine in one
         // kernel (no grouping: hidden row j holds pick j).
-        SMOE_TRY(launch_token1_up(*L, x, logits, idx, w, at<float>(ws, o.H), o.hstride, s));
+        SMOE_TRY(launch_token1_up(*L, x, logits, idx, w, at<float>(ws, o.H), o.hstride, router_shared, s));
         SMOE_TRY(launch_token_down_combine(*L, 1, at<float>(ws, o.H), o.hstride, idx, w, nullptr,
                                            shared ? logits + L->n_expert : nullptr, o.ld, residual, y, s));
         return MOE_OK;
