@@ -359,7 +359,6 @@ struct UpArgs {
     uint16_t* H;                // bf16 [rows, hstride]
     int hstride, T, d, ff, ffs, n_ntiles;
     float alpha, limit;
-    int win;                    // N-tiles per window of the tile walk
 };
 
 struct DownArgs {
@@ -377,53 +376,41 @@ struct DownArgs {
     void* y;                  // [rows, d], bf16 or fp32; with ksplit > 1 fp32 [ksplit][rows][d]
     int hstride, d, ff, ffs, n_ntiles;
     int ksplit, rows;         // K slices per tile (each block sums K / ksplit), grouped rows
-    int win;                  // N-tiles (times ksplit) per window of the tile walk
 };
 
 // XCD-aware tile order.  Workgroups are dispatched to the 8 XCDs round-robin by block
 // id, and each XCD has its own L2.  Block b runs slot b / 8 of XCD b % 8; every XCD owns
 // a contiguous range of M-tiles (groups are contiguous in tile order, so an expert spans
-// at most a few XCDs).  The XCD cuts its range into groups of kGroupM M-tiles and the
-// N-tiles into windows of `win` N-tiles, and walks window by window: inside a window,
-// group by group, and inside a (window, group) pair N-tile by N-tile, each over the
-// group's M-tiles.  The blocks in flight on one XCD (32 to 64) then share a few gathered
-// A tiles and a few weight slices in its L2, and consecutive groups of one expert reuse
-// the window's weight slices while they are still in the L2 or the memory-side cache.
-// A single window over all N-tiles would, for wide experts (tens of N-tiles, several
-// groups per XCD), stream the expert's whole weight matrix once per group.
+// at most a few XCDs) and walks it in groups of kGroupM M-tiles: all N-tiles of a group,
+// N-tile by N-tile, each N-tile over the group's M-tiles.  The blocks in flight on one XCD
+// (32 to 64) then share a few gathered A tiles and a few weight slices in its L2.  With
+// a single M-tile per step of the walk, a layer with wide experts (tens of N-tiles) would
+// stream a different weight slice into every block and re-read each expert's weights
+// from HBM once per M-tile.  (A walk that instead runs every group of the XCD through a
+// window of 4 N-tiles before the next window measured no faster anywhere and fetched
+// twice the bytes on the 8-expert, 14336-wide layer.)
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
-constexpr int kWalkWindow = 4;  // N-tiles per window
 
-inline int grid_blocks(int max_mtiles, int n_ntiles, int win) {
-    const int per_xcd = (max_mtiles + kXcds - 1) / kXcds;
-    const int n_groups = (per_xcd + kGroupM - 1) / kGroupM;
-    const int n_windows = (n_ntiles + win - 1) / win;
-    return kXcds * n_windows * n_groups * kGroupM * win;
+inline int grid_blocks(int max_mtiles, int n_ntiles) {
+    return kXcds * ((max_mtiles + kXcds - 1) / kXcds) * n_ntiles;
 }
 
 // Resolve this block's (group, first row, N-tile).  Returns false if the block is idle.
-// Slots of one XCD: window w = slot / (n_groups * kGroupM * win); inside it, group
-// q = rem / (kGroupM * win) holds that XCD's M-tiles q*kGroupM .. +gm-1 (gm = kGroupM but
-// for the last group) and slot s of the pair takes N-tile w*win + s / gm of M-tile
-// s % gm.  The grid (grid_blocks with the tile bound) has at least as many slots per XCD
-// as the actual tile count needs, and covers every (M-tile, N-tile) pair exactly once.
+// Slots of one XCD: group q = slot / (kGroupM * n_ntiles) holds that XCD's M-tiles
+// q*kGroupM .. +gm-1 (gm = kGroupM but for the last group); inside it slot s takes N-tile
+// s / gm of M-tile s % gm.  The grid has ceil(max_mtiles / 8) * n_ntiles slots per XCD,
+// which covers every (M-tile, N-tile) pair of the XCD's range exactly once.
 __device__ __forceinline__ bool locate(const PlanMeta* meta, const TileDesc* tiles, const Group* groups,
-                                       int n_ntiles, int win, Group& g, int& m0, int& nt) {
+                                       int n_ntiles, Group& g, int& m0, int& nt) {
     const int n_tiles = meta->n_tiles;
     if (n_tiles <= 0) return false;
     const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
     const int per_xcd = (n_tiles + kXcds - 1) / kXcds;
-    const int n_groups = (per_xcd + kGroupM - 1) / kGroupM;
-    const int per_window = n_groups * kGroupM * win;
-    const int w = slot / per_window, rem = slot % per_window;
-    const int q = rem / (kGroupM * win), s = rem % (kGroupM * win);
+    const int q = slot / (kGroupM * n_ntiles), s = slot % (kGroupM * n_ntiles);
     const int gm = min(kGroupM, per_xcd - q * kGroupM);
-    const int wn = min(win, n_ntiles - w * win);
-    if (gm <= 0 || wn <= 0) return false;
-    const int nl = s / gm;
-    if (nl >= wn) return false;
-    nt = w * win + nl;
+    if (gm <= 0) return false;
+    nt = s / gm;
     const int mt = xcd * per_xcd + q * kGroupM + s % gm;
     if (nt >= n_ntiles || mt >= n_tiles) return false;
     g = groups[tiles[mt].group];
@@ -439,7 +426,7 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kerne
     __shared__ GSmem<kUpKW> sm;
     Group g;
     int m0, nt;
-    if (!locate(a.meta, a.tiles, a.groups, a.n_ntiles, a.win, g, m0, nt)) return;
+    if (!locate(a.meta, a.tiles, a.groups, a.n_ntiles, g, m0, nt)) return;
     const bool shared = g.e < 0;
     const int ffg = shared ? a.ffs : a.ff;
     const int f0 = nt * 128;
@@ -546,7 +533,7 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
     __shared__ GSmem<kDownKW> sm;
     Group g;
     int m0, nt;
-    if (!locate(a.meta, a.tiles, a.groups, a.n_ntiles * a.ksplit, a.win, g, m0, nt)) return;
+    if (!locate(a.meta, a.tiles, a.groups, a.n_ntiles * a.ksplit, g, m0, nt)) return;
     const int ks = nt % a.ksplit;
     nt /= a.ksplit;
     const bool shared = g.e < 0;
@@ -855,8 +842,8 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
              static_cast<const uint16_t*>(L.w_gate_up), static_cast<const uint16_t*>(L.b_gate_up),
              static_cast<const uint16_t*>(L.ws_gate), static_cast<const uint16_t*>(L.ws_up),
              mx ? static_cast<const uint8_t*>(L.w_gate_up) : nullptr, mx ? L.w_gate_up_scales : nullptr, q4_gate,
-             q4_up, H, hstride, T, L.d, L.ff, L.shared_ff, nn_up, L.oai_alpha, L.oai_limit, kWalkWindow};
-    const dim3 gu((unsigned)grid_blocks(mt, nn_up, kWalkWindow));
+             q4_up, H, hstride, T, L.d, L.ff, L.shared_ff, nn_up, L.oai_alpha, L.oai_limit};
+    const dim3 gu((unsigned)grid_blocks(mt, nn_up));
     if (mx)
         gg_up_kernel<true, kWMx><<<gu, kGThreads, 0, s>>>(u);
     else if (q4)
@@ -879,8 +866,8 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
             return hipErrorInvalidValue;
         DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down), nullptr,
                     static_cast<const uint16_t*>(L.ws_down), mx_dw, mx_ds, q4_down, nullptr, partial, hstride, L.d,
-                    L.ff, L.shared_ff, nn, ksplit, rows, kWalkWindow};
-        const dim3 gs((unsigned)grid_blocks(mt, nn * ksplit, kWalkWindow));
+                    L.ff, L.shared_ff, nn, ksplit, rows};
+        const dim3 gs((unsigned)grid_blocks(mt, nn * ksplit));
         if (wf == kWMx) gg_down_kernel<float, kWMx><<<gs, kGThreads, 0, s>>>(dn);
         else if (wf == kWQ4k) gg_down_kernel<float, kWQ4k><<<gs, kGThreads, 0, s>>>(dn);
         else gg_down_kernel<float, kWDense><<<gs, kGThreads, 0, s>>>(dn);
@@ -895,8 +882,8 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
     }
     DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down), b_down,
                 static_cast<const uint16_t*>(L.ws_down), mx_dw, mx_ds, q4_down, row_w, y, hstride, L.d, L.ff,
-                L.shared_ff, nn, 1, rows, kWalkWindow};
-    const dim3 gd((unsigned)grid_blocks(mt, nn, kWalkWindow));
+                L.shared_ff, nn, 1, rows};
+    const dim3 gd((unsigned)grid_blocks(mt, nn));
 #define SMOE_GG_DOWN(WF)                                                              \
     do {                                                                              \
         if (y_bf16) gg_down_kernel<uint16_t, WF><<<gd, kGThreads, 0, s>>>(dn);        \
