@@ -446,9 +446,13 @@ hipError_t launch_token1_up(const moe_layer& L, const void* x, const float* logi
 }
 
 // The router and the shared expert in one launch: bf16 layers with a shared expert whose
-// rows take one register batch of at most 4 chunks per lane (the router kernel's batch).
+// rows take one register batch of at most 4 chunks per lane (the router kernel's batch),
+// dense routed experts on the one-token kernels or Q4_K routed experts (whose shared
+// expert is bf16).
 bool token1_router_shared_fits(const moe_layer& L) {
-    return token1_fits(L) && L.shared_ff > 0 && L.dtype == MOE_BF16 && pick_kb(L.d, BF16::VEC) <= 4 &&
+    const bool experts_ok = L.expert_format == MOE_EXPERTS_DENSE ? token1_fits(L)
+                                                                  : L.expert_format == MOE_EXPERTS_Q4K;
+    return experts_ok && L.shared_ff > 0 && L.dtype == MOE_BF16 && pick_kb(L.d, BF16::VEC) <= 4 &&
            chunks(L.d, BF16::VEC) <= 8;
 }
 

@@ -20,6 +20,8 @@
 // the dense GEMV kernels.
 #include "internal.h"
 #include "q4k_dev.h"
+#include "route_dev.h"
+#include "rowdot.h"
 
 namespace smoe {
 namespace {
@@ -190,16 +192,13 @@ struct Lanes {
 // Up: one wave owns hidden units f0 .. f0 + NR/2 - 1 of routed group g.  Row r of the
 // wave is the gate (r even) or up (r odd) row of unit f0 + r / 2; in pass p, lane l serves
 // row p * P + l / LPR, unit l % LPR.  With P >= 2 the up row is the next sub-row (LPR
-// lanes on); with P == 1 it is the next pass, in the same lane.
+// lanes on); with P == 1 it is the next pass, in the same lane.  Every wave of the block
+// runs this with the same group (the staging barriers are the block's).
 template <int LPR, int NP, int NT>
-__global__ __launch_bounds__(256) void expert_up_gemv_q4k_kernel(Q4kArgs a) {
+__device__ __forceinline__ void q4k_up_body(const Q4kArgs& a, const Group& g, int f0, uint4* act) {
     using LN = Lanes<LPR, NP>;
     constexpr int P = LN::P, NR = LN::NR;
     static_assert(P >= 2 || NP % 2 == 0, "gate and up rows pair up");
-    extern __shared__ uint4 act[];
-    Group g;
-    if (!q4k_group(a, g)) return;
-    const int f0 = (blockIdx.x * 4 + wave_id()) * (NR / 2);
     const int lane = lane_id();
     const int sr = lane / LPR, ul = lane % LPR;
     const bool active = ul < a.d / 64;
@@ -244,6 +243,35 @@ __global__ __launch_bounds__(256) void expert_up_gemv_q4k_kernel(Q4kArgs a) {
             }
         }
     }
+}
+
+template <int LPR, int NP, int NT>
+__global__ __launch_bounds__(256) void expert_up_gemv_q4k_kernel(Q4kArgs a) {
+    extern __shared__ uint4 act[];
+    Group g;
+    if (!q4k_group(a, g)) return;
+    q4k_up_body<LPR, NP, NT>(a, g, (blockIdx.x * 4 + wave_id()) * (Lanes<LPR, NP>::NR / 2), act);
+}
+
+// One token: the top-k in front of the up GEMV.  Every wave of grid row j runs the wave
+// top-k of the routing kernels on the logits and takes pick j (hidden row j); block 0 of
+// the row records the pick (idx[j], w[j]) for the down kernel.
+template <int LPR, int NP>
+__global__ __launch_bounds__(256) void token1_up_q4k_kernel(Q4kArgs a, const float* __restrict__ logits, int E,
+                                                            int k, int mode, float scale,
+                                                            int32_t* __restrict__ idx, float* __restrict__ w) {
+    extern __shared__ uint4 act[];
+    const int j = blockIdx.y;
+    int my_i;
+    float my_w;
+    topk_wave(logits, E, k, mode, scale, &my_i, &my_w);
+    if (blockIdx.x == 0 && wave_id() == 0 && lane_id() == j) {
+        idx[j] = my_i;
+        w[j] = my_w;
+    }
+    const int e = __builtin_amdgcn_readlane(my_i, j);
+    q4k_up_body<LPR, NP, 1>(a, Group{min(max(e, 0), E - 1), j, 1, 0},
+                            (blockIdx.x * 4 + wave_id()) * (Lanes<LPR, NP>::NR / 2), act);
 }
 
 // Down: one wave owns output dims i0 .. i0 + NR - 1 of routed group g (dim i0 + p * P +
@@ -293,6 +321,106 @@ __global__ __launch_bounds__(256) void expert_down_gemv_q4k_kernel(Q4kArgs a) {
     }
 }
 
+// A few tokens: the down projection of every pick (Q4_K W_d) and of the shared expert
+// (bf16) with the weighted combine, in one kernel, as the dense and MXFP4 layers do.
+// Block (b, t) owns output dims i0 = NR b .. i0 + NR - 1 of token t.  Wave j < k takes
+// pick j: expert idx[t k + j], weight w[t k + j], hidden row perm_inv[t k + j] (row j for
+// one token); it stages that H row in its own LDS slice as bf16 (as the down GEMV does)
+// and serves its NR rows with the decoded units.  Wave k, with a shared expert, takes hidden
+// row T k + t with weight sigmoid(shared_gate[t gate_ld]) and streams the bf16 rows of the
+// shared W_d against the fp32 H row.  The waves leave their NR sums in LDS; NR threads then
+// add them in the combine's order (picks 0..k-1, then the shared expert).
+constexpr int kQ4kTokenMaxWaves = 16;
+
+template <int LPR, int NP, int KBS, bool EXS>
+__global__ __launch_bounds__(kQ4kTokenMaxWaves * kWave) void token_down_combine_q4k_kernel(
+    Q4kArgs a, const uint16_t* __restrict__ ws_down, int ffs, const int32_t* __restrict__ idx,
+    const float* __restrict__ w, const int32_t* __restrict__ perm_inv, const float* __restrict__ shared_gate,
+    int gate_ld, int E, int k, const uint16_t* __restrict__ residual, uint16_t* __restrict__ y) {
+    using LN = Lanes<LPR, NP>;
+    constexpr int P = LN::P, NR = LN::NR;
+    __shared__ float part[kQ4kTokenMaxWaves][NR];
+    __shared__ float wts[kQ4kTokenMaxWaves];
+    extern __shared__ uint4 act[];
+    const int j = wave_id(), lane = lane_id();
+    const int i0 = blockIdx.x * NR, t = blockIdx.y;
+    if (j < k) {
+        const int p = t * k + j;
+        const int ei = idx[p], r = perm_inv ? perm_inv[p] : j;
+        const bool ok = ei >= 0 && ei < E && r >= 0 && r < a.tk;  // else weight 0
+        const int e = ok ? ei : 0, row = ok ? r : 0;
+        const int sr = lane / LPR, ul = lane % LPR;
+        const bool active = ul < a.ff / 64;
+        const int uc = active ? ul : 0;
+        const int nsb = a.ff / kQ4kBlockWeights;
+        uint4 hd[NP], q0[NP], q1[NP];
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            const int i = min(i0 + q * P + sr, a.d - 1);
+            load_unit(a.w_down + ((size_t)e * a.d + i) * nsb * kQ4kBlockBytes, uc, hd[q], q0[q], q1[q]);
+        }
+        // This wave's H row as bf16 in its LDS slice (layout act_chunk); the wave reads back
+        // only what it wrote.
+        const int chunks = a.ff / 8;
+        uint4* mine = act + j * chunks;
+        const float* hr = a.H + (size_t)row * a.hstride;
+        for (int ch = lane; ch < chunks; ch += kWave) {
+            const float4 f0 = *reinterpret_cast<const float4*>(hr + 8 * ch);
+            const float4 f1 = *reinterpret_cast<const float4*>(hr + 8 * ch + 4);
+            q4k_bf16x2_t p0, p1, p2, p3;
+            p0[0] = (__bf16)f0.x;
+            p0[1] = (__bf16)f0.y;
+            p1[0] = (__bf16)f0.z;
+            p1[1] = (__bf16)f0.w;
+            p2[0] = (__bf16)f1.x;
+            p2[1] = (__bf16)f1.y;
+            p3[0] = (__bf16)f1.z;
+            p3[1] = (__bf16)f1.w;
+            mine[act_chunk(ch >> 3, ch & 7)] =
+                make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+        }
+        Q4kDec wd[NP];
+#pragma unroll
+        for (int q = 0; q < NP; ++q) decode_unit(uc, hd[q], q0[q], q1[q], wd[q]);
+        Q4kAct h;
+        read_act(mine, uc, h);
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            const float sum = segment_sum<LPR>(active ? unit_dot(wd[q], h) : 0.0f);
+            if (ul == 0) part[j][q * P + sr] = sum;
+        }
+        if (lane == 0) wts[j] = ok ? w[p] : 0.0f;
+    } else {
+        // The shared expert: NR bf16 rows of the shared W_d against hidden row T k + t.
+        constexpr int SH = 6 - ilog2(NR);
+        const uint16_t* wr[NR];
+#pragma unroll
+        for (int q = 0; q < NR; ++q) wr[q] = ws_down + (size_t)min(i0 + q, a.d - 1) * ffs;
+        const uint16_t* const (&wrc)[NR] = wr;
+        const float* ar[1] = {a.H + (size_t)(a.tk + t) * a.hstride};
+        const float* const (&arc)[1] = ar;
+        float acc[NR][1] = {};
+        rows_dot<NR, 1, KBS, BF16, F32, true, EXS>(wrc, arc, 1, ffs, acc);
+        float v[NR];
+#pragma unroll
+        for (int q = 0; q < NR; ++q) v[q] = acc[q][0];
+        const float sum = wave_reduce_scatter<NR>(v);
+        if ((lane & ((1 << SH) - 1)) == 0) part[j][lane >> SH] = sum;
+        if (lane == 0) wts[j] = 1.0f / (1.0f + expf(-shared_gate[(size_t)t * gate_ld]));
+    }
+    __syncthreads();
+    const int tid = threadIdx.x;
+    if (tid < NR && i0 + tid < a.d) {
+        const int nw = blockDim.x / kWave;
+        float o = 0.0f;
+        for (int jj = 0; jj < nw; ++jj) o = fmaf(wts[jj], part[jj][tid], o);
+        const size_t at = (size_t)t * a.d + i0 + tid;
+        if (residual) o += bf16_to_f32(residual[at]);  // read before y is written: y may alias it
+        y[at] = f32_to_bf16(o);
+    }
+}
+
 // Lanes per row for a K axis: K / 64 units rounded up to a power of two (K <= 4096).
 int lanes_per_row(int K) {
     const int u = K / 64;
@@ -337,29 +465,126 @@ hipError_t launch_q4k(const Q4kArgs& a, int gmax, bool down, hipStream_t s) {
     }
 }
 
+template <int LPR>
+hipError_t launch_token1_up_q4k_lpr(const Q4kArgs& a, const moe_layer& L, const float* logits, int32_t* idx,
+                                    float* w, hipStream_t s) {
+    constexpr int NP = q4k_passes(64 / LPR, false);
+    constexpr int units_per_block = 4 * (Lanes<LPR, NP>::NR / 2);
+    const dim3 grid((a.ff + units_per_block - 1) / units_per_block, L.k);
+    token1_up_q4k_kernel<LPR, NP><<<grid, 256, a.d * 2, s>>>(a, logits, L.n_expert, L.k, L.route, L.route_scale,
+                                                            idx, w);
+    return hipGetLastError();
+}
+
+template <int LPR>
+hipError_t launch_down_combine_q4k_lpr(const Q4kArgs& a, const moe_layer& L, int T, const int32_t* idx,
+                                       const float* w, const int32_t* perm_inv, const float* shared_gate,
+                                       int gate_ld, const void* residual, void* y, hipStream_t s) {
+    constexpr int NP = q4k_passes(64 / LPR, false);
+    constexpr int NR = Lanes<LPR, NP>::NR;
+    const bool shared = L.shared_ff > 0;
+    const dim3 grid((a.d + NR - 1) / NR, T);
+    const dim3 block((L.k + (shared ? 1 : 0)) * kWave);
+    const size_t lds = (size_t)L.k * a.ff * 2;
+    const auto* wsd = static_cast<const uint16_t*>(L.ws_down);
+    const auto* ro = static_cast<const uint16_t*>(residual);
+    auto* yo = static_cast<uint16_t*>(y);
+    const int ffs = shared ? L.shared_ff : kWave * BF16::VEC;
+    // Shared rows in batches of at most 2 chunks per lane, 1 for 16 rows per wave (the
+    // block may hold 16 waves, 128 registers each).
+    const int kbs = NR >= 16 || pick_kb(ffs, BF16::VEC) < 2 ? 1 : 2;
+    const bool ex = exact_k(ffs, BF16::VEC, kbs);
+#define SMOE_Q4K_DC(KBS, EX)                                                                           \
+    token_down_combine_q4k_kernel<LPR, NP, KBS, EX><<<grid, block, lds, s>>>(                           \
+        a, wsd, ffs, idx, w, perm_inv, shared ? shared_gate : nullptr, gate_ld, L.n_expert, L.k, ro, yo)
+    if constexpr (NR >= 16) {
+        if (ex) SMOE_Q4K_DC(1, true);
+        else SMOE_Q4K_DC(1, false);
+    } else if (kbs == 1) {
+        if (ex) SMOE_Q4K_DC(1, true);
+        else SMOE_Q4K_DC(1, false);
+    } else {
+        if (ex) SMOE_Q4K_DC(2, true);
+        else SMOE_Q4K_DC(2, false);
+    }
+#undef SMOE_Q4K_DC
+    return hipGetLastError();
+}
+
+Q4kArgs q4k_args(const moe_layer& L, const void* x, int T, const int32_t* perm_token, const Group* groups,
+                 const PlanMeta* meta, float* H, int hstride, float* y_perm) {
+    return Q4kArgs{static_cast<const uint16_t*>(x), perm_token, groups, meta,
+                   static_cast<const uint8_t*>(L.w_gate), static_cast<const uint8_t*>(L.w_up),
+                   static_cast<const uint8_t*>(L.w_down), H, y_perm, hstride, T, T * L.k, L.d, L.ff,
+                   L.shared_ff > 0 ? 1 : 0};
+}
+
 }  // namespace
 
 bool q4k_fits(const moe_layer& L) {
     return L.d % kQ4kBlockWeights == 0 && L.ff % kQ4kBlockWeights == 0 && L.d <= 4096 && L.ff <= 4096;
 }
 
+bool q4k_token_fits(const moe_layer& L) {
+    return L.expert_format == MOE_EXPERTS_Q4K && q4k_fits(L) &&
+           L.k + (L.shared_ff > 0 ? 1 : 0) <= kQ4kTokenMaxWaves && (size_t)L.k * L.ff * 2 <= (64u << 10);
+}
+
+hipError_t launch_expert_up_gemv_q4k(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
+                                     const Group* groups, const PlanMeta* meta, float* H, int hstride,
+                                     hipStream_t s) {
+    if (!q4k_fits(L)) return hipErrorInvalidValue;
+    const Q4kArgs a = q4k_args(L, x, T, perm_token, groups, meta, H, hstride, nullptr);
+    const int routed = max_groups(L.n_expert, T, L.k, false);
+    const hipError_t e = T == 1 ? launch_q4k<false>(a, routed, false, s) : launch_q4k<true>(a, routed, false, s);
+    if (e != hipSuccess || L.shared_ff <= 0) return e;
+    return launch_shared_gemv_up(L, x, T, groups, meta, H, hstride, s);
+}
+
 hipError_t launch_expert_gemv_q4k(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                                   const Group* groups, const PlanMeta* meta, float* H, int hstride, float* y_perm,
                                   hipStream_t s) {
-    if (!q4k_fits(L)) return hipErrorInvalidValue;
-    const bool shared = L.shared_ff > 0;
-    const Q4kArgs a{static_cast<const uint16_t*>(x), perm_token, groups, meta,
-                    static_cast<const uint8_t*>(L.w_gate), static_cast<const uint8_t*>(L.w_up),
-                    static_cast<const uint8_t*>(L.w_down), H, y_perm, hstride, T, T * L.k, L.d, L.ff,
-                    shared ? 1 : 0};
-    const int routed = max_groups(L.n_expert, T, L.k, false);
-    hipError_t e = T == 1 ? launch_q4k<false>(a, routed, false, s) : launch_q4k<true>(a, routed, false, s);
+    hipError_t e = launch_expert_up_gemv_q4k(L, x, T, perm_token, groups, meta, H, hstride, s);
     if (e != hipSuccess) return e;
-    if (shared && (e = launch_shared_gemv_up(L, x, T, groups, meta, H, hstride, s)) != hipSuccess) return e;
+    const Q4kArgs a = q4k_args(L, x, T, perm_token, groups, meta, H, hstride, y_perm);
+    const int routed = max_groups(L.n_expert, T, L.k, false);
     e = T == 1 ? launch_q4k<false>(a, routed, true, s) : launch_q4k<true>(a, routed, true, s);
     if (e != hipSuccess) return e;
-    if (shared) return launch_shared_gemv_down(L, T, groups, meta, H, hstride, y_perm, s);
+    if (L.shared_ff > 0) return launch_shared_gemv_down(L, T, groups, meta, H, hstride, y_perm, s);
     return hipSuccess;
+}
+
+hipError_t launch_token1_up_q4k(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,
+                                float* H, int hstride, hipStream_t s) {
+    if (!q4k_token_fits(L)) return hipErrorInvalidValue;
+    const Q4kArgs a = q4k_args(L, x, 1, nullptr, nullptr, nullptr, H, hstride, nullptr);
+    switch (lanes_per_row(L.d)) {
+        case 4: return launch_token1_up_q4k_lpr<4>(a, L, logits, idx, w, s);
+        case 8: return launch_token1_up_q4k_lpr<8>(a, L, logits, idx, w, s);
+        case 16: return launch_token1_up_q4k_lpr<16>(a, L, logits, idx, w, s);
+        case 32: return launch_token1_up_q4k_lpr<32>(a, L, logits, idx, w, s);
+        case 64: return launch_token1_up_q4k_lpr<64>(a, L, logits, idx, w, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_token_down_combine_q4k(const moe_layer& L, int T, const float* H, int hstride, const int32_t* idx,
+                                         const float* w, const int32_t* perm_inv, const float* shared_gate,
+                                         int gate_ld, const void* residual, void* y, hipStream_t s) {
+    if (!q4k_token_fits(L) || T < 1 || (!perm_inv && T != 1) || (L.shared_ff > 0 && !shared_gate))
+        return hipErrorInvalidValue;
+    const Q4kArgs a = q4k_args(L, nullptr, T, nullptr, nullptr, nullptr, const_cast<float*>(H), hstride, nullptr);
+    switch (lanes_per_row(L.ff)) {
+#define SMOE_DC_CASE(LPR) \
+    case LPR: return launch_down_combine_q4k_lpr<LPR>(a, L, T, idx, w, perm_inv, shared_gate, gate_ld, residual, y, s);
+        SMOE_DC_CASE(4)
+        SMOE_DC_CASE(8)
+        SMOE_DC_CASE(16)
+        SMOE_DC_CASE(32)
+        SMOE_DC_CASE(64)
+#undef SMOE_DC_CASE
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace smoe

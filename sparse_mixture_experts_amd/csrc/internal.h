@@ -104,6 +104,21 @@ bool q4k_fits(const moe_layer& L);
 hipError_t launch_expert_gemv_q4k(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                                   const Group* groups, const PlanMeta* meta, float* H, int hstride, float* y_perm,
                                   hipStream_t s);
+// The Q4_K up GEMVs alone (routed and shared H rows), and the one-token / few-token
+// kernels of the Q4_K layer: top-k inside the up GEMV (one token, routed picks only: the
+// shared expert's up runs in the router launch), and the down GEMVs of every pick and of
+// the shared expert with the weighted combine written straight to y (hidden rows
+// perm_inv[t*k+j], or row j for one token; shared row T*k + t, gate shared_gate[t*gate_ld]).
+// q4k_token_fits: k (+1 with a shared expert) <= 16 and k*ff*2 bytes of LDS <= 64 KB.
+bool q4k_token_fits(const moe_layer& L);
+hipError_t launch_expert_up_gemv_q4k(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
+                                     const Group* groups, const PlanMeta* meta, float* H, int hstride,
+                                     hipStream_t s);
+hipError_t launch_token1_up_q4k(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,
+                                float* H, int hstride, hipStream_t s);
+hipError_t launch_token_down_combine_q4k(const moe_layer& L, int T, const float* H, int hstride, const int32_t* idx,
+                                         const float* w, const int32_t* perm_inv, const float* shared_gate,
+                                         int gate_ld, const void* residual, void* y, hipStream_t s);
 hipError_t launch_shared_gemv_up(const moe_layer& L, const void* x, int T, const Group* groups, const PlanMeta* meta,
                                  float* H, int hstride, hipStream_t s);
 hipError_t launch_shared_gemv_down(const moe_layer& L, int T, const Group* groups, const PlanMeta* meta,

@@ -230,8 +230,9 @@ moe_status forward_body(const moe_layer* L, const void* x, int32_t T, const void
     float* row_w = grouped ? at<float>(ws, o.row_w) : nullptr;
     void* y_rows = at<void>(ws, o.yperm);
     const bool dense = L->expert_format == MOE_EXPERTS_DENSE;
+    const bool q4k_token = L->expert_format == MOE_EXPERTS_Q4K && !grouped && q4k_token_fits(*L);
     // One token with a shared expert: its up GEMV streams in the router launch.
-    const bool router_shared = T == 1 && !grouped && dense && !norm && o.ld == L->n_expert + 1 &&
+    const bool router_shared = T == 1 && !grouped && (dense || q4k_token) && !norm && o.ld == L->n_expert + 1 &&
                                token1_router_shared_fits(*L);
     if (router_shared)
         SMOE_TRY(launch_token1_router_shared(*L, x, logits, o.ld, at<float>(ws, o.H), o.hstride, s));
@@ -243,6 +244,14 @@ moe_status forward_body(const moe_layer* L, const void* x, int32_t T, const void
         SMOE_TRY(launch_token1_up(*L, x, logits, idx, w, at<float>(ws, o.H), o.hstride, router_shared, s));
         SMOE_TRY(launch_token_down_combine(*L, 1, at<float>(ws, o.H), o.hstride, idx, w, nullptr,
                                            shared ? logits + L->n_expert : nullptr, o.ld, residual, y, s));
+        return MOE_OK;
+    }
+    if (T == 1 && q4k_token && (router_shared || !shared)) {
+        // The same three launches over Q4_K routed experts (the shared expert's up ran in
+        // the router launch).
+        SMOE_TRY(launch_token1_up_q4k(*L, x, logits, idx, w, at<float>(ws, o.H), o.hstride, s));
+        SMOE_TRY(launch_token_down_combine_q4k(*L, 1, at<float>(ws, o.H), o.hstride, idx, w, nullptr,
+                                               shared ? logits + L->n_expert : nullptr, o.ld, residual, y, s));
         return MOE_OK;
     }
     const bool mxfp4 = L->expert_format == MOE_EXPERTS_MXFP4;
@@ -270,6 +279,13 @@ moe_status forward_body(const moe_layer* L, const void* x, int32_t T, const void
                                        at<float>(ws, o.H), o.hstride, s));
         SMOE_TRY(launch_token_down_combine(*L, T, at<float>(ws, o.H), o.hstride, idx, w, perm_inv, sg, 1, residual,
                                            y, s));
+        return MOE_OK;
+    }
+    if (fused_route && q4k_token && T <= kTokenDownMaxT) {
+        SMOE_TRY(launch_expert_up_gemv_q4k(*L, x, T, perm_token, at<Group>(ws, o.groups), at<PlanMeta>(ws, o.meta),
+                                           at<float>(ws, o.H), o.hstride, s));
+        SMOE_TRY(launch_token_down_combine_q4k(*L, T, at<float>(ws, o.H), o.hstride, idx, w, perm_inv, sg, 1,
+                                               residual, y, s));
         return MOE_OK;
     }
     if (fused_route && !grouped && mxfp4 && T <= kTokenDownMaxT && token1_mx_fits(*L)) {

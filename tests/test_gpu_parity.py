@@ -418,7 +418,7 @@ def test_full_qwen_prefill_zipf():
                                            ("mixtral", 16, None), ("mixtral", 16384, 512),
                                            ("gptoss_mx", 1, None), ("gptoss_mx", 64, None),
                                            ("gptoss_mx", 1000, 128), ("qwen_q4k", 1, None),
-                                           ("qwen_q4k", 64, None), ("qwen_q4k", 2048, 128)])
+                                           ("qwen_q4k", 8, None), ("qwen_q4k", 64, None), ("qwen_q4k", 2048, 128)])
 def test_full_other_layers(name, T, sample):
     say("full", name, T)
     L, x = case(name, T)
