@@ -37,6 +37,8 @@
 // blocks.  MXFP4 expert weights take the same loops with their B slices expanded from FP4
 // blocks into the ring, and Q4_K weights from their super-blocks (see
 // grouped_mainloop_regb).
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "mfma_dev.h"
@@ -201,55 +203,94 @@ struct MxRow {
     const uint8_t* scales;  // the row's first scale byte
 };
 
+// Vector loads into registers that the compiler does not track.  Its wait-count model
+// does not count the direct-to-LDS loads in flight, so a wait it places before the first
+// use of a register load drains those as well (vmcnt(0)), and the A slice meant to be two
+// steps ahead has to land within the step.  The register-staged loop issues B through
+// these and places its own waits (reg_wait), which name the number of younger loads.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void vload16(u32x4& dst, const void* p) {
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(p) : "memory");
+}
+__device__ __forceinline__ void vload8(u32x2& dst, const void* p) {
+    asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(dst) : "v"(p) : "memory");
+}
+__device__ __forceinline__ void vload_u8(uint32_t& dst, const void* p) {
+    asm volatile("global_load_ubyte %0, %1, off" : "=v"(dst) : "v"(p) : "memory");
+}
+// Wait until at most N of this wave's vector-memory operations are outstanding; the
+// registers named are tied to the wait, so no use of them moves above it.
+template <int N>
+__device__ __forceinline__ void reg_wait(u32x4& a, uint32_t& b) {
+    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void reg_wait(u32x2& a, uint32_t& b) {
+    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void reg_wait(u32x4& a, u32x4& b) {
+    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void reg_wait(u32x4& a, u32x4& b, u32x4& c) {
+    asm volatile("s_waitcnt vmcnt(%3)" : "+v"(a), "+v"(b), "+v"(c) : "n"(N) : "memory");
+}
+// A 16-byte LDS store the compiler does not see as one: it orders every LDS store it sees
+// after all direct-to-LDS loads in flight (vmcnt(0)), not knowing that the expanded B rows
+// and the loads' A stages never overlap.  The loop's wait before each barrier
+// (lgkmcnt(0)) completes these stores.
+__device__ __forceinline__ void lds_write16(uint16_t* dst, const uint4& v) {
+    const u32x4 d = {v.x, v.y, v.z, v.w};
+    asm volatile("ds_write_b128 %0, %1" ::"v"((__attribute__((address_space(3))) void*)dst), "v"(d) : "memory");
+}
+
 template <int KW>
 struct MxRegs {
-    uint32_t w[KW / 16];  // KW / 2 codes
-    uint32_t s;           // scale byte
+    typename std::conditional<KW == 64, u32x4, u32x2>::type w;  // KW / 2 codes
+    uint32_t s;                                                 // scale byte
 };
 constexpr int kMxLoads = 2;  // vector loads per thread per slice (codes, scale)
 
 template <int KW>
-__device__ __forceinline__ MxRegs<KW> mx_load(const MxRow& m, int k0) {
+__device__ __forceinline__ void mx_load(const MxRow& m, int k0, MxRegs<KW>& r) {
     const int h = threadIdx.x & 1;
-    MxRegs<KW> r;
     if constexpr (KW == 64) {  // two blocks per row slice: one each
         const int blk = k0 / 32 + h;
-        const uint4 q = ld16(m.codes + (size_t)blk * 16);
-        r.w[0] = q.x;
-        r.w[1] = q.y;
-        r.w[2] = q.z;
-        r.w[3] = q.w;
-        r.s = m.scales[blk];
+        vload16(r.w, m.codes + (size_t)blk * 16);
+        vload_u8(r.s, m.scales + blk);
     } else {  // one block per row slice: half of it each
         static_assert(KW == 32, "MXFP4 slices are one or two blocks wide");
         const int blk = k0 / 32;
-        const uint2 q = *reinterpret_cast<const uint2*>(m.codes + (size_t)blk * 16 + 8 * h);
-        r.w[0] = q.x;
-        r.w[1] = q.y;
-        r.s = m.scales[blk];
+        vload8(r.w, m.codes + (size_t)blk * 16 + 8 * h);
+        vload_u8(r.s, m.scales + blk);
     }
-    return r;
 }
 
 template <int KW>
 __device__ __forceinline__ void mx_store(GSmem<KW>& sm, int stage, const MxRegs<KW>& r) {
     const int row = threadIdx.x >> 1, h = threadIdx.x & 1;
-    const float scale = e8m0_scale(r.s);
+    const float scale = e8m0_scale(r.s & 0xFFu);
 #pragma unroll
     for (int i = 0; i < KW / 16; ++i)
-        *reinterpret_cast<uint4*>(&sm.k.b[stage][swz<KW>(row, h * (KW / 16) + i)]) = fp4_word_bf16x8(r.w[i], scale);
+        lds_write16(&sm.k.b[stage][swz<KW>(row, h * (KW / 16) + i)], fp4_word_bf16x8(r.w[i], scale));
 }
 
-// Weight sources of the register-staged main loop: load(k0) fetches this thread's share
-// of the K-slice at k0 (thread t: tile row t / 2, half t & 1 of the slice) into registers;
-// store() expands it into the slice's bf16 LDS rows (the swizzled layout of the direct
+// Weight sources of the register-staged main loop: load(k0, r) issues this thread's loads
+// of the K-slice at k0 (thread t: tile row t / 2, half t & 1 of the slice) into r;
+// ready<N>(r) waits for them with N younger vector-memory operations allowed in flight;
+// store() expands r into the slice's bf16 LDS rows (the swizzled layout of the direct
 // loads).  kLoads: vector loads per thread per slice.
 template <int KW>
 struct MxSrc {
     MxRow m;
     using Regs = MxRegs<KW>;
     static constexpr int kLoads = kMxLoads;
-    __device__ __forceinline__ Regs load(int k0) const { return mx_load<KW>(m, k0); }
+    __device__ __forceinline__ void load(int k0, Regs& r) const { mx_load<KW>(m, k0, r); }
+    template <int N>
+    __device__ __forceinline__ void ready(Regs& r) const { reg_wait<N>(r.w, r.s); }
     __device__ __forceinline__ void store(GSmem<KW>& sm, int stage, const Regs& r) const { mx_store<KW>(sm, stage, r); }
 };
 
@@ -261,8 +302,8 @@ struct MxSrc {
 // super-block).
 template <int KW>
 struct Q4kRegs {
-    uint4 head;
-    uint4 q[KW == 64 ? 2 : 1];
+    u32x4 head;
+    u32x4 q[KW == 64 ? 2 : 1];
     int j;  // sub-block whose scale and min apply
 };
 
@@ -272,35 +313,39 @@ struct Q4kSrc {
     int kbase;
     using Regs = Q4kRegs<KW>;
     static constexpr int kLoads = KW == 64 ? 3 : 2;
-    __device__ __forceinline__ Regs load(int k0) const {
+    __device__ __forceinline__ void load(int k0, Regs& r) const {
         const int k = kbase + k0, h = threadIdx.x & 1;
         const int j = (k % kQ4kBlockWeights) / 32;
         const uint8_t* blk = row + (size_t)(k / kQ4kBlockWeights) * kQ4kBlockBytes;
-        Regs r;
-        r.head = ld16(blk);
+        vload16(r.head, blk);
         if constexpr (KW == 64) {
             const uint8_t* run = blk + 16 + 32 * (j / 2);
-            r.q[0] = ld16(run);
-            r.q[1] = ld16(run + 16);
+            vload16(r.q[0], run);
+            vload16(r.q[1], run + 16);
             r.j = j + h;
         } else {
             static_assert(KW == 32, "Q4_K slices are one run or one sub-block wide");
-            r.q[0] = ld16(blk + 16 + 32 * (j / 2) + 16 * h);
+            vload16(r.q[0], blk + 16 + 32 * (j / 2) + 16 * h);
             r.j = j;
         }
-        return r;
+    }
+    template <int N>
+    __device__ __forceinline__ void ready(Regs& r) const {
+        if constexpr (KW == 64) reg_wait<N>(r.head, r.q[0], r.q[1]);
+        else reg_wait<N>(r.head, r.q[0]);
     }
     __device__ __forceinline__ void store(GSmem<KW>& sm, int stage, const Regs& r) const {
         const int row_l = threadIdx.x >> 1, h = threadIdx.x & 1;
         float a, b;
-        q4k_sub_scale(r.head, r.j, a, b);
+        const uint4 head = make_uint4(r.head[0], r.head[1], r.head[2], r.head[3]);
+        q4k_sub_scale(head, r.j, a, b);
         const int shift = 4 * (r.j & 1);
         constexpr int NC = KW / 16;  // 16-byte LDS chunks per thread
 #pragma unroll
         for (int q = 0; q < NC; ++q) {
-            const uint4& v = r.q[q / 2];
-            const uint32_t w0 = (q & 1) ? v.z : v.x, w1 = (q & 1) ? v.w : v.y;
-            *reinterpret_cast<uint4*>(&sm.k.b[stage][swz<KW>(row_l, h * NC + q)]) = q4k_dequant8(w0, w1, shift, a, b);
+            const u32x4& v = r.q[q / 2];
+            const uint32_t w0 = (q & 1) ? v[2] : v[0], w1 = (q & 1) ? v[3] : v[1];
+            lds_write16(&sm.k.b[stage][swz<KW>(row_l, h * NC + q)], q4k_dequant8(w0, w1, shift, a, b));
         }
     }
 };
@@ -308,32 +353,42 @@ struct Q4kSrc {
 // The main loop with B from a register-staged source.  Slice s: A direct-loaded two steps
 // ahead as in grouped_mainloop; B loaded into registers two steps ahead and expanded into
 // LDS at the end of step s - 1 (its stage held slice s - 3, finished by every wave at the
-// barrier of step s - 1).  The wait before each step allows the newest slice's loads (A
-// and B registers) in flight; the expansion itself waits for its registers, which also
-// completes the A loads issued before them.
+// barrier of step s - 1).  Each step issues its B loads, then its A segments, so the
+// expansion of slice s waits with slice s's A segments still in flight (kLoadsA younger
+// operations); the prologue's first expansion has A of slices 0 and 1 and B of slice 1
+// behind it.  The wait before each step allows the newest slice's loads (B registers and
+// A) in flight.  The B registers of the clamped re-load on the last step stay tied until
+// every load has drained.  (With the compiler's own waits, which drained every load at the
+// first use of the B registers: gpt-oss-shaped MXFP4 T=4096 1252 -> 1170 us per forward,
+// Q4_K prefill T=8192 1056 -> 1038 us.)
 template <int KW, typename Src>
 __device__ __forceinline__ void grouped_mainloop_regb(GSmem<KW>& sm, const LoadPlan<KW>& p, const Src& src, int K,
                                                       int arow0, const int (&brow)[4], floatx4 (&acc)[4][4]) {
+    constexpr int LA = Ring<KW>::kLoadsA;
     const int nk = K / KW;
-    issue_a_segments(sm.k.a[0], p.src, Ring<KW>::kLoadsA, 0);
-    const typename Src::Regs first = src.load(0);
-    issue_a_segments(sm.k.a[1], p.src, Ring<KW>::kLoadsA, min(1, nk - 1) * KW);
-    typename Src::Regs nxt = src.load(min(1, nk - 1) * KW);
+    typename Src::Regs first, nxt;
+    src.load(0, first);
+    issue_a_segments(sm.k.a[0], p.src, LA, 0);
+    src.load(min(1, nk - 1) * KW, nxt);
+    issue_a_segments(sm.k.a[1], p.src, LA, min(1, nk - 1) * KW);
+    src.template ready<2 * LA + Src::kLoads>(first);
     src.store(sm, 0, first);
     int st = 0;
     for (int kt = 0; kt < nk; ++kt) {
-        wait_vm_lgkm<Ring<KW>::kLoadsA + Src::kLoads>();
+        wait_vm_lgkm<LA + Src::kLoads>();
         lds_barrier();
 #pragma unroll
         for (int kc = 0; kc < KW / 8; kc += 4) mfma_k32<KW>(sm.k.a[st], sm.k.b[st], arow0, brow, kc, acc);
         const int nx = st == 2 ? 0 : st + 1;   // (kt + 1) % 3
+        src.template ready<LA>(nxt);
         src.store(sm, nx, nxt);                // B of slice kt+1 (clamped re-load on the last step)
+        src.load(min(kt + 2, nk - 1) * KW, nxt);
         const int pre = st == 0 ? 2 : st - 1;  // (kt + 2) % 3
-        issue_a_segments(sm.k.a[pre], p.src, Ring<KW>::kLoadsA, min(kt + 2, nk - 1) * KW);
-        nxt = src.load(min(kt + 2, nk - 1) * KW);
+        issue_a_segments(sm.k.a[pre], p.src, LA, min(kt + 2, nk - 1) * KW);
         st = nx;
     }
     wait_vm_lgkm<0>();
+    src.template ready<0>(nxt);
     __syncthreads();
 }
 
