@@ -221,22 +221,23 @@ __device__ __forceinline__ void vload_u8(uint32_t& dst, const void* p) {
     asm volatile("global_load_ubyte %0, %1, off" : "=v"(dst) : "v"(p) : "memory");
 }
 // Wait until at most N of this wave's vector-memory operations are outstanding; the
-// registers named are tied to the wait, so no use of them moves above it.
+// registers named are tied to the wait, so no use of them moves above it.  The assembly
+// names them in a comment ("tied ..."), which tests/test_asm_waits.py reads.
 template <int N>
 __device__ __forceinline__ void reg_wait(u32x4& a, uint32_t& b) {
-    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%2) ; tied %0 %1" : "+v"(a), "+v"(b) : "n"(N) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void reg_wait(u32x2& a, uint32_t& b) {
-    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%2) ; tied %0 %1" : "+v"(a), "+v"(b) : "n"(N) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void reg_wait(u32x4& a, u32x4& b) {
-    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%2) ; tied %0 %1" : "+v"(a), "+v"(b) : "n"(N) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void reg_wait(u32x4& a, u32x4& b, u32x4& c) {
-    asm volatile("s_waitcnt vmcnt(%3)" : "+v"(a), "+v"(b), "+v"(c) : "n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%3) ; tied %0 %1 %2" : "+v"(a), "+v"(b), "+v"(c) : "n"(N) : "memory");
 }
 // A 16-byte LDS store the compiler does not see as one: it orders every LDS store it sees
 // after all direct-to-LDS loads in flight (vmcnt(0)), not knowing that the expanded B rows
