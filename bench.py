@@ -59,7 +59,8 @@ WORKLOADS = {
 }
 DEFAULT = "qwen_decode_t64"
 DEFAULT_SWEEP = ["qwen_decode_t1", "qwen_decode_t8", "qwen_prefill_t8192", "tiny_f32_t16", "gptoss_t1",
-                 "gptoss_t4096", "gptoss_mx_t1", "gptoss_mx_t4096", "mixtral_t16", "mixtral_t16384"]
+                 "gptoss_t4096", "gptoss_mx_t1", "gptoss_mx_t4096", "mixtral_t16", "mixtral_t16384",
+                 "qwen_q4k_t1", "qwen_q4k_t64", "qwen_q4k_prefill_t8192"]
 
 
 def log(*a):
@@ -175,6 +176,58 @@ def summarize_pmc(fetch_csv, write_csv, workload, out_path, command, forwards):
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote {out_path}: {total / 1e6:.2f} MB per forward")
+
+
+def _is_library_kernel(name):
+    return not any(t in name for t in ("rocclr", "rocprim", "at::", "elementwise", "Functor"))
+
+
+def workload_title(workload):
+    from sparse_mixture_experts_amd import synth
+    spec_name, T = WORKLOADS[workload]
+    sp = synth.SPECS[spec_name.replace("_zipf", "")] if spec_name.endswith("_zipf") else synth.SPECS[spec_name]
+    zipf = spec_name.endswith("_zipf") or sp.router_bias == "zipf"
+    experts = {"dense": sp.dtype, "mxfp4": "MXFP4 experts", "q4k": "Q4_K routed experts"}[sp.experts]
+    return (f"{workload}: T={T}, d={sp.d}, E={sp.n_expert}, k={sp.k}, ff={sp.ff}, shared {sp.shared_ff}, "
+            f"{experts}, {sp.act}{', Zipf-skewed routing' if zipf else ''}")
+
+
+def summarize_stats(csv_path, log_path, workload, out_path, command):
+    """profiles/<workload>_kernel_stats.md from one `rocprofv3 --kernel-trace --stats` run of
+    this script in --forward-only mode: every library kernel with its calls, its mean
+    duration and its time per forward (total / forwards), their sum per forward, and the
+    same run's event-timed step for comparison."""
+    import csv
+    with open(log_path) as fh:
+        run = next(json.loads(l)["forward_only"] for l in fh if l.startswith('{"forward_only"'))
+    forwards = run["warmup"] + run["steps"]
+    rows, per_fwd = [], 0.0
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            if not _is_library_kernel(r["Name"]):
+                continue
+            tot = float(r["TotalDurationNs"]) / 1e3
+            per_fwd += tot / forwards
+            rows.append((_short_kernel(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, tot / forwards))
+    rows.sort(key=lambda x: -x[5])
+    step = run["ms_per_step"] * 1e3
+    lines = [f"# Kernel time per forward, {workload_title(workload)}", "",
+             "Command (from the repository root, one MI355X):", "", "```"]
+    lines += command.split("\n")
+    lines += ["```", "",
+              f"{forwards} forwards (warm-up + timed) of `moe_forward`; every library kernel of the run "
+              "belongs to one of them, so its time per forward is its total over the run / "
+              f"{forwards}.  Set-up copies and torch kernels are left out.", "",
+              "| kernel | calls | avg us | min us | max us | us per forward |", "|---|---|---|---|---|---|"]
+    for n, c, a, mn, mx, pf in rows:
+        lines.append(f"| `{n[:90]}` | {c} | {a:.2f} | {mn:.2f} | {mx:.2f} | {pf:.2f} |")
+    lines += ["", f"Sum of the forward's kernels: {per_fwd:.1f} us per forward.  Event-timed step of the "
+              f"same run (under the profiler): {step:.1f} us per forward; the kernels cover "
+              f"{per_fwd / step:.1%} of it (the rest is the gaps between launches)."]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out_path}: kernels {per_fwd:.1f} us of {step:.1f} us per forward")
 
 
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
@@ -338,6 +391,7 @@ def time_workload(name, steps, warmup, layer_cache, forward_only=False):
     # Timed region: exactly `steps` forwards back to back; nothing else is enqueued.
     ms_step = timed(step, steps, warmup)
     res = {"workload": name, "T": T, "layer": spec_name, "dtype": L["dtype"], "ms_per_step": ms_step,
+           "steps": steps, "warmup": warmup,
            "tokens_per_s": T / (ms_step / 1e3), "weight_copies": n_copies, "token_batches": n_batches}
     if forward_only:
         log(f"[{name}] {ms_step * 1e3:.1f} us/step ({warmup + steps} forwards)")
@@ -551,6 +605,9 @@ def main():
     ap.add_argument("--pmc-command", default="", help="command lines quoted in that summary")
     ap.add_argument("--pmc-forwards", type=int, default=0,
                     help="forwards (warm-up + timed) in each counter run, for --summarize-pmc")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "RUN_LOG"),
+                    help="write profiles/<workload>_kernel_stats.md from a rocprofv3 kernel-stats CSV of a "
+                         "--forward-only run and that run's output (no GPU)")
     ap.add_argument("--summarize-mfma", metavar="CSV",
                     help="write profiles/<workload>_mfma_counters.md from a counter CSV of the three "
                          "MFMA counters (no GPU); --pmc-command gives the command quoted in it")
@@ -566,6 +623,11 @@ def main():
             raise SystemExit("--summarize-pmc needs --pmc-forwards (warm-up + timed steps of the runs)")
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
                       traffic_file(args.workload), args.pmc_command, args.pmc_forwards)
+        return
+
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.workload,
+                        os.path.join(ROOT, "profiles", f"{args.workload}_kernel_stats.md"), args.pmc_command)
         return
 
     if args.summarize_mfma:
