@@ -192,7 +192,20 @@ def workload_title(workload):
             f"{experts}, {sp.act}{', Zipf-skewed routing' if zipf else ''}")
 
 
-def summarize_stats(csv_path, log_path, workload, out_path, command):
+def bench_step_ms(bench_json, workload):
+    """ms_per_step of a workload in a default bench.py output line (top level or sweep)."""
+    with open(bench_json) as fh:
+        line = [l for l in fh if l.startswith("{")][-1]
+    d = json.loads(line)
+    if d["config"]["workload"] == workload:
+        return d["ms_per_step"]
+    for r in d.get("sweep", []):
+        if r["workload"] == workload:
+            return r["ms_per_step"]
+    return None
+
+
+def summarize_stats(csv_path, log_path, workload, out_path, command, bench_json=None):
     """profiles/<workload>_kernel_stats.md from one `rocprofv3 --kernel-trace --stats` run of
     this script in --forward-only mode: every library kernel with its calls, its mean
     duration and its time per forward (total / forwards), their sum per forward, and the
@@ -223,8 +236,15 @@ def summarize_stats(csv_path, log_path, workload, out_path, command):
     for n, c, a, mn, mx, pf in rows:
         lines.append(f"| `{n[:90]}` | {c} | {a:.2f} | {mn:.2f} | {mx:.2f} | {pf:.2f} |")
     lines += ["", f"Sum of the forward's kernels: {per_fwd:.1f} us per forward.  Event-timed step of the "
-              f"same run (under the profiler): {step:.1f} us per forward; the kernels cover "
-              f"{per_fwd / step:.1%} of it (the rest is the gaps between launches)."]
+              f"same run (under the profiler): {step:.1f} us per forward; kernels / step = "
+              f"{per_fwd / step:.1%}.  (Below 100%: gaps between launches, which at one token are mostly "
+              "the profiler's own work per dispatch; above: the kernels' own timestamps run a little "
+              "longer than the events around the whole step.)"]
+    plain = bench_step_ms(bench_json, workload) if bench_json else None
+    if plain:
+        lines += ["", f"The same forward without the profiler (`python bench.py`, default run, "
+                  f"{os.path.basename(bench_json)}): {plain * 1e3:.1f} us per step; kernels / step = "
+                  f"{per_fwd / (plain * 1e3):.1%}."]
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote {out_path}: kernels {per_fwd:.1f} us of {step:.1f} us per forward")
@@ -510,9 +530,15 @@ def time_workload(name, steps, warmup, layer_cache, forward_only=False):
                                  "frac": sf / (stage_ms / 1e3) / peak,
                                  "kernel": "moe_expert_ffn (plan + up + down, fp32 rows)",
                                  "algorithmic_flops": sf}
+    if stage_ms > ms_step:
+        # The forward took a fused path (one or a few tokens) whose kernels are not the
+        # stage's; a stage slower than the whole step measures nothing the forward runs.
+        res["stage_roofline"] = None
+        res["stage_note"] = "moe_forward runs fused kernels here; the separate stage call is slower than the step"
+    stage_frac = f"{res['stage_roofline']['frac']:.3f}" if res["stage_roofline"] else "not the forward's kernels"
     log(f"[{name}] {ms_step * 1e3:.1f} us/step, {res['tokens_per_s']:.0f} tok/s, "
         f"roofline frac {res['roofline']['frac']:.3f}, stage {stage_ms * 1e3:.1f} us "
-        f"({res['stage_roofline']['frac']:.3f}), shell {shell_ms * 1e3:.1f} us/step"
+        f"({stage_frac}), shell {shell_ms * 1e3:.1f} us/step"
         + (f", graph replay {res['graph_ms_per_step'] * 1e3:.1f} us/step" if "graph_ms_per_step" in res else ""))
     del layers, xs, ws, y, yp, plans
     torch.cuda.empty_cache()
@@ -608,6 +634,7 @@ def main():
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "RUN_LOG"),
                     help="write profiles/<workload>_kernel_stats.md from a rocprofv3 kernel-stats CSV of a "
                          "--forward-only run and that run's output (no GPU)")
+    ap.add_argument("--bench-json", help="a default bench.py output, quoted by --summarize-stats")
     ap.add_argument("--summarize-mfma", metavar="CSV",
                     help="write profiles/<workload>_mfma_counters.md from a counter CSV of the three "
                          "MFMA counters (no GPU); --pmc-command gives the command quoted in it")
@@ -627,7 +654,8 @@ def main():
 
     if args.summarize_stats:
         summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.workload,
-                        os.path.join(ROOT, "profiles", f"{args.workload}_kernel_stats.md"), args.pmc_command)
+                        os.path.join(ROOT, "profiles", f"{args.workload}_kernel_stats.md"), args.pmc_command,
+                        args.bench_json)
         return
 
     if args.summarize_mfma:
