@@ -250,6 +250,33 @@ def summarize_stats(csv_path, log_path, workload, out_path, command, bench_json=
     print(f"wrote {out_path}: kernels {per_fwd:.1f} us of {step:.1f} us per forward")
 
 
+def summarize_counters(csv_path, workload, out_path, command, title):
+    """profiles/<workload>_<title>.md: every counter of one rocprofv3 --pmc run, averaged
+    per dispatch for each library kernel, with the mean dispatch duration."""
+    import csv
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    span = collections.defaultdict(dict)
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            if not _is_library_kernel(r["Kernel_Name"]):
+                continue
+            n = _short_kernel(r["Kernel_Name"])
+            vals[n][r["Counter_Name"]] += float(r["Counter_Value"])
+            span[n][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    names = sorted({c for d in vals.values() for c in d})
+    lines = [f"# Counters ({title}): {workload_title(workload)}", "", "Command (from the repository root, one MI355X):",
+             "", "```"] + command.split("\n") + ["```", "", "Per dispatch (averages over the run's dispatches of each kernel).", "",
+             "| kernel | dispatches | avg us | " + " | ".join(names) + " |", "|---|---|---|" + "---|" * len(names)]
+    for n, d in sorted(vals.items(), key=lambda kv: -sum(span[kv[0]].values())):
+        k = len(span[n])
+        t = sum(span[n].values()) / k
+        lines.append(f"| `{n[:70]}` | {k} | {t * 1e6:.1f} | " + " | ".join(f"{d.get(c, 0.0) / k:.4g}" for c in names) + " |")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out_path}")
+
+
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
 N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 
@@ -635,6 +662,8 @@ def main():
                     help="write profiles/<workload>_kernel_stats.md from a rocprofv3 kernel-stats CSV of a "
                          "--forward-only run and that run's output (no GPU)")
     ap.add_argument("--bench-json", help="a default bench.py output, quoted by --summarize-stats")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("CSV", "TITLE"),
+                    help="write profiles/<workload>_<TITLE>.md: every counter of one --pmc run per kernel (no GPU)")
     ap.add_argument("--summarize-mfma", metavar="CSV",
                     help="write profiles/<workload>_mfma_counters.md from a counter CSV of the three "
                          "MFMA counters (no GPU); --pmc-command gives the command quoted in it")
@@ -656,6 +685,12 @@ def main():
         summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.workload,
                         os.path.join(ROOT, "profiles", f"{args.workload}_kernel_stats.md"), args.pmc_command,
                         args.bench_json)
+        return
+
+    if args.summarize_counters:
+        csv_path, title = args.summarize_counters
+        summarize_counters(csv_path, args.workload, os.path.join(ROOT, "profiles", f"{args.workload}_{title}.md"),
+                           args.pmc_command, title.replace("_", " "))
         return
 
     if args.summarize_mfma:
