@@ -429,24 +429,29 @@ int lanes_per_row(int K) {
     return l;
 }
 
-// Passes per wave: rows per wave R = 8 for one token (more waves in flight) or 16 for
-// more (the decoded weights serve every row of the group), NP = R / P, at most 4 (128
-// registers of decoded weights).  P == 1 gives 4 passes, even as the up kernel needs.
-constexpr int q4k_passes(int P, bool many) {
-    const int r = many ? 16 : 8;
+// Passes per wave: NP = R / P, at most 4 (128 registers of decoded weights), for R rows
+// per wave: 8 for one token; for more, 4 in the up kernel and 16 in the down kernel.  (Up
+// kernel at the Qwen shape, K = 2048: 4 rows per wave hold 64 registers of decoded weights
+// and leave about four waves per SIMD to hide the weight loads; 8 rows, two waves per
+// SIMD, ran the T=64 forward at 180 us against 169 us, 2 rows at 182 us.)  P == 1 gives
+// 4 passes, even as the up kernel needs.
+constexpr int q4k_passes(int P, bool many, bool down = false) {
+    const int r = many ? (down ? 16 : 4) : 8;
     return r / P > 4 ? 4 : (r / P < 1 ? 1 : r / P);
 }
 
 template <int LPR, bool MANY>
 hipError_t launch_q4k_lpr(const Q4kArgs& a, int gmax, bool down, hipStream_t s) {
-    constexpr int NP = q4k_passes(64 / LPR, MANY);
     constexpr int NT = MANY ? kQ4kStepRows : 1;
-    constexpr int NR = Lanes<LPR, NP>::NR;
     if (!down) {
+        constexpr int NP = q4k_passes(64 / LPR, MANY, false);
+        constexpr int NR = Lanes<LPR, NP>::NR;
         const int units_per_block = 4 * (NR / 2);
         const dim3 grid((a.ff + units_per_block - 1) / units_per_block, gmax);
         expert_up_gemv_q4k_kernel<LPR, NP, NT><<<grid, 256, NT * a.d * 2, s>>>(a);
     } else {
+        constexpr int NP = q4k_passes(64 / LPR, MANY, true);
+        constexpr int NR = Lanes<LPR, NP>::NR;
         const dim3 grid((a.d + 4 * NR - 1) / (4 * NR), gmax);
         expert_down_gemv_q4k_kernel<LPR, NP, NT><<<grid, 256, NT * a.ff * 2, s>>>(a);
     }
