@@ -54,6 +54,7 @@ WORKLOADS = {
     "mixtral_t16384": ("mixtral", 16384),
     "tiny_f32_t16": ("tiny_f32", 16),
     "qwen_q4k_t1": ("qwen_q4k", 1),
+    "qwen_q4k_t8": ("qwen_q4k", 8),
     "qwen_q4k_t64": ("qwen_q4k", 64),
     "qwen_q4k_prefill_t8192": ("qwen_q4k_zipf", 8192),
 }

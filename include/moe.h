@@ -98,9 +98,10 @@ enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_GROUPED = 2 };
  *    weight = d * scale_j * q - dmin * min_j.  Requires MOE_BF16, MOE_ACT_SWIGLU, d and ff
  *    multiples of 256 and at most 4096, and NULL *_scales fields.  The shared expert, router,
  *    x and y stay bf16.  The GEMV path decodes the quants in registers and meets them with
- *    activations held as bf16 (the hidden rows H rounded to bf16, as on the grouped path);
- *    the grouped path expands each K-slice of a weight tile into LDS as bf16 for the bf16
- *    MFMA. */
+ *    activations held as bf16 (the hidden rows H rounded to bf16, as on the grouped path;
+ *    also the shared expert's, when it is as wide as the routed experts and runs in the same
+ *    GEMVs); the grouped path expands each K-slice of a weight tile into LDS as bf16 for
+ *    the bf16 MFMA. */
 enum { MOE_EXPERTS_DENSE = 0, MOE_EXPERTS_MXFP4 = 1, MOE_EXPERTS_Q4K = 2 };
 
 /* One MoE layer.  Fixed layout: 9 int32, 3 float, then 12 pointers (offset 48), then

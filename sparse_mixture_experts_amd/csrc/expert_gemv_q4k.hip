@@ -8,17 +8,22 @@
 // rounded up to a power of two, at most 64) share a row and a wave covers P = 64 / LPR
 // rows at once, in NP passes.
 //
-// A block (4 waves) serves one routed group.  Each wave loads its rows' units once and
-// turns the quants into bf16 pairs 128 + q (exact), kept in registers for every row of
-// the group.  The block stages the group's activations in LDS as bf16, up to 4 rows at a
-// time (x for the up kernel; for the down kernel H, fp32 in memory, rounded to bf16 as on
-// the grouped path), so the waves read them from LDS rather than each from the L2.  Per
-// row a lane dots its unit with the activations in v_dot2 (fp32 accumulation); per
-// sub-block, sum q x = dot - 128 sum x, and the unit's contribution is
-// d sc (sum q x) - dmin m (sum x) for each of its two sub-blocks.  Each weight row's LPR
-// partial sums meet in a butterfly over its LPR lanes.  The shared expert (bf16) runs on
-// the dense GEMV kernels.
-#include "internal.h"
+// A block (4 waves) serves one group.  Each wave loads its rows' units once and turns the
+// quants into bf16 pairs 128 + q (exact), kept in registers for every row of the group.
+// The block stages the group's activations in LDS as bf16, up to 4 rows at a time (x for
+// the up kernel; for the down kernel H, fp32 in memory, rounded to bf16 as on the grouped
+// path), so the waves read them from LDS rather than each from the L2.  Per row a lane
+// dots its unit with the activations in v_dot2 (fp32 accumulation); per sub-block,
+// sum q x = dot - 128 sum x, and the unit's contribution is d sc (sum q x) - dmin m (sum x)
+// for each of its two sub-blocks.  Each weight row's LPR partial sums meet in a butterfly
+// over its LPR lanes.
+//
+// A bf16 shared expert as wide as the routed experts runs in the same launches: its units
+// are the 64 weights themselves as bf16 pairs, with multiplier 1 and offset term 0, and the
+// first grid rows take it in chunks of kQ4kSharedRows tokens (the other rows the routed
+// groups), so its longer blocks start first.  A shared expert of another width runs on the
+// dense GEMV kernels.
+#include "gemv_items.h"
 #include "q4k_dev.h"
 #include "route_dev.h"
 #include "rowdot.h"
@@ -26,7 +31,8 @@
 namespace smoe {
 namespace {
 
-constexpr int kQ4kStepRows = 4;  // activation rows staged in LDS per step (T > 1)
+constexpr int kQ4kStepRows = 4;     // activation rows staged in LDS per step (T > 1)
+constexpr int kQ4kSharedRows = 16;  // tokens per grid row of a fused shared expert
 
 struct Q4kArgs {
     const uint16_t* x;          // [T, d] bf16
@@ -36,14 +42,19 @@ struct Q4kArgs {
     const uint8_t* w_gate;      // [E, ff, d/256, 144]
     const uint8_t* w_up;
     const uint8_t* w_down;      // [E, d, ff/256, 144]
+    const uint16_t* ws_gate;    // shared expert, bf16 [ff, d] (fuse_shared)
+    const uint16_t* ws_up;
+    const uint16_t* ws_down;    // bf16 [d, ff]
     float* H;                   // fp32 [rows, hstride]
     float* y;                   // fp32 [rows, d]
-    int hstride, T, tk, d, ff, has_shared;
+    int hstride, T, tk, d, ff, has_shared, fuse_shared;
 };
 
-// Routed group of grid row blockIdx.y (the shared expert, last in the list, is not taken
-// here).  The entry and the count are loaded before the count is checked.
+// Group of grid row blockIdx.y.  With fuse_shared the first grid rows take the shared
+// expert in chunks (gemv_group); otherwise the shared expert, last in the list, is not
+// taken here.  The entry and the count are loaded before the count is checked.
 __device__ __forceinline__ bool q4k_group(const Q4kArgs& a, Group& g) {
+    if (a.fuse_shared) return gemv_group(a.groups, a.meta, true, a.T, a.tk, kQ4kSharedRows, g);
     const int gi = blockIdx.y;
     const Group cand = a.groups[gi];
     const int n_groups = a.meta->n_groups;
@@ -101,6 +112,28 @@ __device__ __forceinline__ void decode_unit(int unit, const uint4& head, const u
     q4k_sub_scale(head, 2 * c + 1, u.sb, u.mb);
 }
 
+// A unit of a bf16 row (the shared expert): lo / hi take the 64 weights as they are, with
+// multiplier 1 and offset 128 * 1 - 128 = 0, so unit_dot gives the plain dot product.
+__device__ __forceinline__ void load_bf16_unit(const uint16_t* row, int unit, Q4kDec& u) {
+    const uint16_t* p = row + 64 * unit;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint4 a = ld16(p + 8 * c), b = ld16(p + 32 + 8 * c);
+        u.lo[4 * c] = a.x;
+        u.lo[4 * c + 1] = a.y;
+        u.lo[4 * c + 2] = a.z;
+        u.lo[4 * c + 3] = a.w;
+        u.hi[4 * c] = b.x;
+        u.hi[4 * c + 1] = b.y;
+        u.hi[4 * c + 2] = b.z;
+        u.hi[4 * c + 3] = b.w;
+    }
+    u.sa = 1.0f;
+    u.sb = 1.0f;
+    u.ma = -128.0f;
+    u.mb = -128.0f;
+}
+
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(q4k_bf16x2_t, a), __builtin_bit_cast(q4k_bf16x2_t, b),
                                            acc, false);
@@ -118,6 +151,12 @@ struct Q4kAct {
 // apart) read different banks.
 __device__ __forceinline__ int act_chunk(int u, int c) { return u * 8 + (c ^ (u & 7)); }
 
+// LDS bytes of nt staged rows of K activations.
+constexpr size_t q4k_stage_bytes(int K, int nt) { return (size_t)nt * (size_t)K * 2; }
+
+// The unit's activations and the sums of its two halves (each lane adds its own: sums
+// staged once per row by one thread per sub-block ran slower, the staging being what the
+// kernels wait on).
 __device__ __forceinline__ void read_act(const uint4* row, int unit, Q4kAct& x) {
     const uint32_t one = 0x3F803F80u;  // bf16 pair (1, 1)
 #pragma unroll
@@ -150,8 +189,26 @@ __device__ __forceinline__ float unit_dot(const Q4kDec& u, const Q4kAct& x) {
     return u.sa * da + u.sb * db - (128.0f * u.sa + u.ma) * x.sxa - (128.0f * u.sb + u.mb) * x.sxb;
 }
 
+// 8 fp32 values as a 16-byte chunk of bf16 (rounded to nearest even).
+__device__ __forceinline__ uint4 bf16_chunk(const float* src) {
+    const float4 f0 = *reinterpret_cast<const float4*>(src);
+    const float4 f1 = *reinterpret_cast<const float4*>(src + 4);
+    q4k_bf16x2_t p0, p1, p2, p3;
+    p0[0] = (__bf16)f0.x;
+    p0[1] = (__bf16)f0.y;
+    p1[0] = (__bf16)f0.z;
+    p1[1] = (__bf16)f0.w;
+    p2[0] = (__bf16)f1.x;
+    p2[1] = (__bf16)f1.y;
+    p3[0] = (__bf16)f1.z;
+    p3[1] = (__bf16)f1.w;
+    return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                      __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+}
+
 // Stage group rows tb .. tb+nt-1 in LDS as bf16 rows of K (layout act_chunk): x rows
-// (bf16, by token) or H rows (fp32, rounded to nearest even).
+// (bf16, by token; the shared expert's row r is token r - tk) or H rows (fp32, rounded to
+// nearest even).
 template <bool FROM_H>
 __device__ __forceinline__ void stage_rows(const Q4kArgs& a, const Group& g, int tb, int nt, int K, uint4* lds) {
     const int chunks = K / 8;  // 16-byte bf16 chunks per row
@@ -160,22 +217,9 @@ __device__ __forceinline__ void stage_rows(const Q4kArgs& a, const Group& g, int
         const int row = g.row0 + tb + t;
         uint4 v;
         if constexpr (FROM_H) {
-            const float* src = a.H + (size_t)row * a.hstride + 8 * ch;
-            const float4 f0 = *reinterpret_cast<const float4*>(src);
-            const float4 f1 = *reinterpret_cast<const float4*>(src + 4);
-            q4k_bf16x2_t p0, p1, p2, p3;
-            p0[0] = (__bf16)f0.x;
-            p0[1] = (__bf16)f0.y;
-            p1[0] = (__bf16)f0.z;
-            p1[1] = (__bf16)f0.w;
-            p2[0] = (__bf16)f1.x;
-            p2[1] = (__bf16)f1.y;
-            p3[0] = (__bf16)f1.z;
-            p3[1] = (__bf16)f1.w;
-            v = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+            v = bf16_chunk(a.H + (size_t)row * a.hstride + 8 * ch);
         } else {
-            int tok = a.T == 1 ? 0 : a.perm_token[row];
+            int tok = a.T == 1 ? 0 : g.e < 0 ? row - a.tk : a.perm_token[row];
             tok = min(max(tok, 0), a.T - 1);
             v = ld16(a.x + (size_t)tok * a.d + 8 * ch);
         }
@@ -189,15 +233,14 @@ struct Lanes {
     static constexpr int NR = P * NP;   // rows per wave
 };
 
-// Up: one wave owns hidden units f0 .. f0 + NR/2 - 1 of routed group g.  Row r of the
+// Up: one wave owns hidden units f0 .. f0 + NR/2 - 1 of group g.  Row r of the
 // wave is the gate (r even) or up (r odd) row of unit f0 + r / 2; in pass p, lane l serves
 // row p * P + l / LPR, unit l % LPR.  With P >= 2 the up row is the next sub-row (LPR
 // lanes on); with P == 1 it is the next pass, in the same lane.  Every wave of the block
 // runs this with the same group (the staging barriers are the block's).
 template <int LPR, int NP, int NT>
 __device__ __forceinline__ void q4k_up_body(const Q4kArgs& a, const Group& g, int f0, uint4* act) {
-    using LN = Lanes<LPR, NP>;
-    constexpr int P = LN::P, NR = LN::NR;
+    constexpr int P = Lanes<LPR, NP>::P;
     static_assert(P >= 2 || NP % 2 == 0, "gate and up rows pair up");
     const int lane = lane_id();
     const int sr = lane / LPR, ul = lane % LPR;
@@ -205,7 +248,14 @@ __device__ __forceinline__ void q4k_up_body(const Q4kArgs& a, const Group& g, in
     const int uc = active ? ul : 0;
     const int nsb = a.d / kQ4kBlockWeights;
     Q4kDec w[NP];
-    {
+    if (g.e < 0) {  // the shared expert (bf16 rows)
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int r = p * P + sr;
+            const int f = min(f0 + r / 2, a.ff - 1);
+            load_bf16_unit(((r & 1) ? a.ws_up : a.ws_gate) + (size_t)f * a.d, uc, w[p]);
+        }
+    } else {
         uint4 hd[NP], q0[NP], q1[NP];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -274,8 +324,8 @@ __global__ __launch_bounds__(256) void token1_up_q4k_kernel(Q4kArgs a, const flo
                             (blockIdx.x * 4 + wave_id()) * (Lanes<LPR, NP>::NR / 2), act);
 }
 
-// Down: one wave owns output dims i0 .. i0 + NR - 1 of routed group g (dim i0 + p * P +
-// l / LPR in pass p).
+// Down: one wave owns output dims i0 .. i0 + NR - 1 of group g (dim i0 + p * P + l / LPR
+// in pass p).
 template <int LPR, int NP, int NT>
 __global__ __launch_bounds__(256) void expert_down_gemv_q4k_kernel(Q4kArgs a) {
     using LN = Lanes<LPR, NP>;
@@ -290,7 +340,11 @@ __global__ __launch_bounds__(256) void expert_down_gemv_q4k_kernel(Q4kArgs a) {
     const int uc = active ? ul : 0;
     const int nsb = a.ff / kQ4kBlockWeights;
     Q4kDec w[NP];
-    {
+    if (g.e < 0) {  // the shared expert (bf16 rows)
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            load_bf16_unit(a.ws_down + (size_t)min(i0 + p * P + sr, a.d - 1) * a.ff, uc, w[p]);
+    } else {
         uint4 hd[NP], q0[NP], q1[NP];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -364,22 +418,7 @@ __global__ __launch_bounds__(kQ4kTokenMaxWaves * kWave) void token_down_combine_
         const int chunks = a.ff / 8;
         uint4* mine = act + j * chunks;
         const float* hr = a.H + (size_t)row * a.hstride;
-        for (int ch = lane; ch < chunks; ch += kWave) {
-            const float4 f0 = *reinterpret_cast<const float4*>(hr + 8 * ch);
-            const float4 f1 = *reinterpret_cast<const float4*>(hr + 8 * ch + 4);
-            q4k_bf16x2_t p0, p1, p2, p3;
-            p0[0] = (__bf16)f0.x;
-            p0[1] = (__bf16)f0.y;
-            p1[0] = (__bf16)f0.z;
-            p1[1] = (__bf16)f0.w;
-            p2[0] = (__bf16)f1.x;
-            p2[1] = (__bf16)f1.y;
-            p3[0] = (__bf16)f1.z;
-            p3[1] = (__bf16)f1.w;
-            mine[act_chunk(ch >> 3, ch & 7)] =
-                make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
-        }
+        for (int ch = lane; ch < chunks; ch += kWave) mine[act_chunk(ch >> 3, ch & 7)] = bf16_chunk(hr + 8 * ch);
         Q4kDec wd[NP];
 #pragma unroll
         for (int q = 0; q < NP; ++q) decode_unit(uc, hd[q], q0[q], q1[q], wd[q]);
@@ -448,12 +487,12 @@ hipError_t launch_q4k_lpr(const Q4kArgs& a, int gmax, bool down, hipStream_t s) 
         constexpr int NR = Lanes<LPR, NP>::NR;
         const int units_per_block = 4 * (NR / 2);
         const dim3 grid((a.ff + units_per_block - 1) / units_per_block, gmax);
-        expert_up_gemv_q4k_kernel<LPR, NP, NT><<<grid, 256, NT * a.d * 2, s>>>(a);
+        expert_up_gemv_q4k_kernel<LPR, NP, NT><<<grid, 256, q4k_stage_bytes(a.d, NT), s>>>(a);
     } else {
         constexpr int NP = q4k_passes(64 / LPR, MANY, true);
         constexpr int NR = Lanes<LPR, NP>::NR;
         const dim3 grid((a.d + 4 * NR - 1) / (4 * NR), gmax);
-        expert_down_gemv_q4k_kernel<LPR, NP, NT><<<grid, 256, NT * a.ff * 2, s>>>(a);
+        expert_down_gemv_q4k_kernel<LPR, NP, NT><<<grid, 256, q4k_stage_bytes(a.ff, NT), s>>>(a);
     }
     return hipGetLastError();
 }
@@ -476,7 +515,7 @@ hipError_t launch_token1_up_q4k_lpr(const Q4kArgs& a, const moe_layer& L, const 
     constexpr int NP = q4k_passes(64 / LPR, false);
     constexpr int units_per_block = 4 * (Lanes<LPR, NP>::NR / 2);
     const dim3 grid((a.ff + units_per_block - 1) / units_per_block, L.k);
-    token1_up_q4k_kernel<LPR, NP><<<grid, 256, a.d * 2, s>>>(a, logits, L.n_expert, L.k, L.route, L.route_scale,
+    token1_up_q4k_kernel<LPR, NP><<<grid, 256, q4k_stage_bytes(a.d, 1), s>>>(a, logits, L.n_expert, L.k, L.route, L.route_scale,
                                                             idx, w);
     return hipGetLastError();
 }
@@ -490,7 +529,7 @@ hipError_t launch_down_combine_q4k_lpr(const Q4kArgs& a, const moe_layer& L, int
     const bool shared = L.shared_ff > 0;
     const dim3 grid((a.d + NR - 1) / NR, T);
     const dim3 block((L.k + (shared ? 1 : 0)) * kWave);
-    const size_t lds = (size_t)L.k * a.ff * 2;
+    const size_t lds = q4k_stage_bytes(a.ff, L.k);
     const auto* wsd = static_cast<const uint16_t*>(L.ws_down);
     const auto* ro = static_cast<const uint16_t*>(residual);
     auto* yo = static_cast<uint16_t*>(y);
@@ -516,12 +555,21 @@ hipError_t launch_down_combine_q4k_lpr(const Q4kArgs& a, const moe_layer& L, int
     return hipGetLastError();
 }
 
+// The shared expert rides in the Q4_K launches when it is as wide as the routed experts.
+bool q4k_fuse_shared(const moe_layer& L) { return L.shared_ff > 0 && L.shared_ff == L.ff; }
+
 Q4kArgs q4k_args(const moe_layer& L, const void* x, int T, const int32_t* perm_token, const Group* groups,
                  const PlanMeta* meta, float* H, int hstride, float* y_perm) {
     return Q4kArgs{static_cast<const uint16_t*>(x), perm_token, groups, meta,
                    static_cast<const uint8_t*>(L.w_gate), static_cast<const uint8_t*>(L.w_up),
-                   static_cast<const uint8_t*>(L.w_down), H, y_perm, hstride, T, T * L.k, L.d, L.ff,
-                   L.shared_ff > 0 ? 1 : 0};
+                   static_cast<const uint8_t*>(L.w_down), static_cast<const uint16_t*>(L.ws_gate),
+                   static_cast<const uint16_t*>(L.ws_up), static_cast<const uint16_t*>(L.ws_down), H, y_perm,
+                   hstride, T, T * L.k, L.d, L.ff, L.shared_ff > 0 ? 1 : 0, q4k_fuse_shared(L) ? 1 : 0};
+}
+
+// Grid rows of a Q4_K GEMV launch: every routed group, and the fused shared expert's chunks.
+int q4k_grid_rows(const moe_layer& L, int T) {
+    return max_groups(L.n_expert, T, L.k, false) + (q4k_fuse_shared(L) ? (T + kQ4kSharedRows - 1) / kQ4kSharedRows : 0);
 }
 
 }  // namespace
@@ -532,7 +580,7 @@ bool q4k_fits(const moe_layer& L) {
 
 bool q4k_token_fits(const moe_layer& L) {
     return L.expert_format == MOE_EXPERTS_Q4K && q4k_fits(L) &&
-           L.k + (L.shared_ff > 0 ? 1 : 0) <= kQ4kTokenMaxWaves && (size_t)L.k * L.ff * 2 <= (64u << 10);
+           L.k + (L.shared_ff > 0 ? 1 : 0) <= kQ4kTokenMaxWaves && q4k_stage_bytes(L.ff, L.k) <= (64u << 10);
 }
 
 hipError_t launch_expert_up_gemv_q4k(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
@@ -540,9 +588,9 @@ hipError_t launch_expert_up_gemv_q4k(const moe_layer& L, const void* x, int T, c
                                      hipStream_t s) {
     if (!q4k_fits(L)) return hipErrorInvalidValue;
     const Q4kArgs a = q4k_args(L, x, T, perm_token, groups, meta, H, hstride, nullptr);
-    const int routed = max_groups(L.n_expert, T, L.k, false);
-    const hipError_t e = T == 1 ? launch_q4k<false>(a, routed, false, s) : launch_q4k<true>(a, routed, false, s);
-    if (e != hipSuccess || L.shared_ff <= 0) return e;
+    const int rows = q4k_grid_rows(L, T);
+    const hipError_t e = T == 1 ? launch_q4k<false>(a, rows, false, s) : launch_q4k<true>(a, rows, false, s);
+    if (e != hipSuccess || L.shared_ff <= 0 || a.fuse_shared) return e;
     return launch_shared_gemv_up(L, x, T, groups, meta, H, hstride, s);
 }
 
@@ -552,11 +600,10 @@ hipError_t launch_expert_gemv_q4k(const moe_layer& L, const void* x, int T, cons
     hipError_t e = launch_expert_up_gemv_q4k(L, x, T, perm_token, groups, meta, H, hstride, s);
     if (e != hipSuccess) return e;
     const Q4kArgs a = q4k_args(L, x, T, perm_token, groups, meta, H, hstride, y_perm);
-    const int routed = max_groups(L.n_expert, T, L.k, false);
-    e = T == 1 ? launch_q4k<false>(a, routed, true, s) : launch_q4k<true>(a, routed, true, s);
-    if (e != hipSuccess) return e;
-    if (L.shared_ff > 0) return launch_shared_gemv_down(L, T, groups, meta, H, hstride, y_perm, s);
-    return hipSuccess;
+    const int rows = q4k_grid_rows(L, T);
+    e = T == 1 ? launch_q4k<false>(a, rows, true, s) : launch_q4k<true>(a, rows, true, s);
+    if (e != hipSuccess || L.shared_ff <= 0 || a.fuse_shared) return e;
+    return launch_shared_gemv_down(L, T, groups, meta, H, hstride, y_perm, s);
 }
 
 hipError_t launch_token1_up_q4k(const moe_layer& L, const void* x, const float* logits, int32_t* idx, float* w,

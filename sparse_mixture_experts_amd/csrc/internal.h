@@ -98,8 +98,10 @@ hipError_t launch_expert_up_gemv_mx(const moe_layer& L, const void* x, int T, co
                                     hipStream_t s);
 bool token1_mx_fits(const moe_layer& L);
 // GEMVs over Q4_K routed experts (fp32 H and unweighted fp32 rows, as the dense GEMVs);
-// the bf16 shared expert runs on the dense kernels restricted to its grid row
-// (launch_shared_gemv_*).  q4k_fits: d and ff multiples of 256, at most 4096.
+// a bf16 shared expert as wide as the routed experts runs in the same launches (its H rows
+// rounded to bf16 for the down GEMV, as the routed ones), one of another width on the dense
+// kernels restricted to its grid row (launch_shared_gemv_*).  q4k_fits: d and ff multiples
+// of 256, at most 4096.
 bool q4k_fits(const moe_layer& L);
 hipError_t launch_expert_gemv_q4k(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                                   const Group* groups, const PlanMeta* meta, float* H, int hstride, float* y_perm,
@@ -109,7 +111,8 @@ hipError_t launch_expert_gemv_q4k(const moe_layer& L, const void* x, int T, cons
 // shared expert's up runs in the router launch), and the down GEMVs of every pick and of
 // the shared expert with the weighted combine written straight to y (hidden rows
 // perm_inv[t*k+j], or row j for one token; shared row T*k + t, gate shared_gate[t*gate_ld]).
-// q4k_token_fits: k (+1 with a shared expert) <= 16 and k*ff*2 bytes of LDS <= 64 KB.
+// q4k_token_fits: k (+1 with a shared expert) <= 16 and k staged H rows (ff bf16 and ff/32
+// fp32 sums each) within 64 KB of LDS.
 bool q4k_token_fits(const moe_layer& L);
 hipError_t launch_expert_up_gemv_q4k(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                                      const Group* groups, const PlanMeta* meta, float* H, int hstride,

@@ -647,11 +647,13 @@ def test_mxfp4_grouped_expert_ffn_rows():
 # ----------------------------------------------------------------------------- Q4_K experts
 
 # Rows of 8, 12 (a ragged lane group of 16) and 64 quant runs per lane group on the up
-# projection; 4 and 8 on the down projection; with and without a bf16 shared expert.
+# projection; 4 and 8 on the down projection; a bf16 shared expert as wide as the routed
+# experts (served by the Q4_K GEMVs), one twice as wide (dense GEMVs), and none.
 Q4K_SMALL = [dict(d=512, n_expert=16, ff=256, shared_ff=256),
              dict(d=768, n_expert=8, ff=512, k=2, shared_ff=0),
-             dict(d=4096, n_expert=4, ff=256, k=2, shared_ff=256)]
-Q4K_IDS = ["d512", "d768", "d4096"]
+             dict(d=4096, n_expert=4, ff=256, k=2, shared_ff=256),
+             dict(d=512, n_expert=16, ff=256, shared_ff=512)]
+Q4K_IDS = ["d512", "d768", "d4096", "d512_sh512"]
 
 
 @pytest.mark.parametrize("T", [1, 7, 100])
