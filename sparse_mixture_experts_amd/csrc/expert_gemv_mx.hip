@@ -109,10 +109,11 @@ __device__ __forceinline__ float mx_scale(uint32_t sbyte, int b, int nblk) {
 }
 
 // One wave: hidden units f0, f0+1 of routed group g (interleaved rows 2f0 .. 2f0+3), every
-// row of the group, kMxUpNT rows per step.
-template <int NB>
+// row of the group, NT rows per step (1 for a one-token group, whose second row would repeat
+// the first).
+template <int NB, int NT = kMxUpNT>
 __device__ __forceinline__ void mx_up_item(const MxArgs& a, const Group& g, int f0) {
-    constexpr int NR = 2 * kMxUnits, NT = kMxUpNT, N = NR * NT;
+    constexpr int NR = 2 * kMxUnits, N = NR * NT;
     constexpr int SH = 6 - ilog2(N);
     const int nblk = a.d / 32;
     const size_t row_blocks = (size_t)nblk;
@@ -141,7 +142,7 @@ __device__ __forceinline__ void mx_up_item(const MxArgs& a, const Group& g, int 
     uint32_t sbyte[NR][NB];
     load_mx_rows<NR, NB>(wc, sc, nblk, codes, sbyte);
     // After the reduction lane l holds value v = t * NR + r = l >> SH; the up row of gate
-    // row r sits one value on, 1 << SH lanes higher in the same 16-lane row.
+    // row r sits one value on, 1 << SH lanes higher (in the same 16-lane row for NT = 2).
     const int my_t = (lane >> SH) / NR, my_r = (lane >> SH) % NR;
     const int my_f = f0 + my_r / 2;
     const bool writer = (my_r & 1) == 0 && (lane & ((1 << SH) - 1)) == 0 && my_f < a.ff;
@@ -186,8 +187,12 @@ __device__ __forceinline__ void mx_up_item(const MxArgs& a, const Group& g, int 
 #pragma unroll
             for (int r = 0; r < NR; ++r) v[t * NR + r] = acc[r][t];
         const float sum = wave_reduce_scatter<N>(v);
-        const float up = __int_as_float(
-            __builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x100 + (1 << SH), 0xF, 0xF, false));
+        float up;
+        if constexpr (SH < 4)  // inside a 16-lane row: a DPP row shift
+            up = __int_as_float(
+                __builtin_amdgcn_update_dpp(0, __float_as_int(sum), 0x100 + (1 << SH), 0xF, 0xF, false));
+        else
+            up = __shfl(sum, (lane + (1 << SH)) & 63, kWave);
         if (writer && my_t < nt) {
             float gv = fminf(sum + bf16_lo(bpair), a.limit);
             float uv = fminf(fmaxf(up + bf16_hi(bpair), -a.limit), a.limit);
@@ -301,7 +306,7 @@ __global__ __launch_bounds__(256) void token1_up_mx_kernel(MxArgs a, const float
     const int e = __builtin_amdgcn_readlane(my_i, j);
     MxArgs b = a;
     b.perm_token = kTokenZero;
-    mx_up_item<NB>(b, Group{min(max(e, 0), E - 1), j, 1, 0}, f0);
+    mx_up_item<NB, 1>(b, Group{min(max(e, 0), E - 1), j, 1, 0}, f0);
 }
 
 // A few tokens: the down projection of every pick (MXFP4 W_d) and the weighted combine
