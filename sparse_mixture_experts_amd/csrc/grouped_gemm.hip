@@ -142,17 +142,23 @@ __device__ __forceinline__ LoadPlan<KW> make_plan(RowA row_a, RowB row_b) {
     return p;
 }
 
-template <int KW, bool A_ONLY = false>
-__device__ __forceinline__ void issue_slice(GSmem<KW>& sm, const LoadPlan<KW>& p, int stage, int k0) {
+// The direct loads of one K-slice (from src[j] + k0) into ring stage (a_stage, b_stage).
+template <int KW>
+__device__ __forceinline__ void issue_stage(uint16_t* a_stage, uint16_t* b_stage, const uint16_t* const* src, int k0) {
     using R = Ring<KW>;
     const int wave = threadIdx.x / kWave;
 #pragma unroll
-    for (int j = 0; j < (A_ONLY ? R::kLoadsA : R::kLoads); ++j) {
+    for (int j = 0; j < R::kLoads; ++j) {
         const bool is_a = j < R::kLoadsA;
         const int seg = wave + 8 * (is_a ? j : j - R::kLoadsA);
-        uint16_t* dst = is_a ? &sm.k.a[stage][seg * 512] : &sm.k.b[stage][seg * 512];  // 1 KB
-        __builtin_amdgcn_global_load_lds(p.src[j] + k0, (lds_ptr_t)dst, 16, 0, 0);
+        uint16_t* dst = is_a ? a_stage + seg * 512 : b_stage + seg * 512;  // 1 KB
+        __builtin_amdgcn_global_load_lds(src[j] + k0, (lds_ptr_t)dst, 16, 0, 0);
     }
+}
+
+template <int KW>
+__device__ __forceinline__ void issue_slice(GSmem<KW>& sm, const LoadPlan<KW>& p, int stage, int k0) {
+    issue_stage<KW>(sm.k.a[stage], sm.k.b[stage], p.src, k0);
 }
 
 // The A segments of a slice only (B comes through registers): n 1 KB segments of this
@@ -161,6 +167,30 @@ __device__ __forceinline__ void issue_a_segments(uint16_t* dst, const uint16_t* 
     const int wave = threadIdx.x / kWave;
     for (int j = 0; j < n; ++j)
         __builtin_amdgcn_global_load_lds(src[j] + k0, (lds_ptr_t)(dst + (wave + 8 * j) * 512), 16, 0, 0);
+}
+
+// Fragments of 32 K of one wave's 64 x 64 tile, read from LDS apart from their MFMAs.
+struct Frags {
+    bf16x8 a[4], b[4];
+};
+
+template <int KW>
+__device__ __forceinline__ void read_frags(const uint16_t* sa, const uint16_t* sb, int arow0, const int (&brow)[4],
+                                           int kc, Frags& f) {
+    const int lane = lane_id();
+    const int fr = lane & 15, fc = lane >> 4;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) f.a[mi] = lds_frag<KW>(sa, arow0 + mi * 16 + fr, kc + fc);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) f.b[ni] = lds_frag<KW>(sb, brow[ni] + fr, kc + fc);
+}
+
+__device__ __forceinline__ void mfma_frags(const Frags& f, floatx4 (&acc)[4][4]) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
 }
 
 // acc += A[wave rows] x B[rows brow[ni] + 0..15]^T over K.  Step kt: wait for this lane's
@@ -172,8 +202,8 @@ __device__ __forceinline__ void issue_a_segments(uint16_t* dst, const uint16_t* 
 // barrier instead of queueing behind the direct loads' LDS writes.  Ends with all loads
 // drained and a barrier, so the caller may reuse the LDS.
 template <int KW>
-__device__ __forceinline__ void grouped_mainloop(GSmem<KW>& sm, const LoadPlan<KW>& p, int K, int arow0,
-                                                 const int (&brow)[4], floatx4 (&acc)[4][4]) {
+__device__ __forceinline__ void grouped_mainloop_plain(GSmem<KW>& sm, const LoadPlan<KW>& p, int K, int arow0,
+                                                       const int (&brow)[4], floatx4 (&acc)[4][4]) {
     const int nk = K / KW;
     issue_slice(sm, p, 0, 0);
     issue_slice(sm, p, 1, min(1, nk - 1) * KW);
@@ -186,6 +216,101 @@ __device__ __forceinline__ void grouped_mainloop(GSmem<KW>& sm, const LoadPlan<K
         const int pre = st == 0 ? 2 : st - 1;  // (kt + 2) % 3
         issue_slice(sm, p, pre, min(kt + 2, nk - 1) * KW);
         st = st == 2 ? 0 : st + 1;
+    }
+    wait_vm_lgkm<0>();
+    __syncthreads();
+}
+
+// 32-wide slices in M halves: A rows 0-31 of the wave tile (lo) with all four B fragments,
+// then A rows 32-63 (hi) with the same B.  b0 / b1 hold the B fragments of alternate slices.
+struct HalfFrags {
+    bf16x8 lo[2], hi[2], b0[4], b1[4];
+};
+
+template <int KW>
+__device__ __forceinline__ void read_half_lo(GSmem<KW>& sm, int stg, int arow0, const int (&brow)[4], HalfFrags& h,
+                                             bf16x8 (&b)[4]) {
+    const int lane = lane_id();
+    const int fr = lane & 15, fc = lane >> 4;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) h.lo[mi] = lds_frag<KW>(sm.k.a[stg], arow0 + mi * 16 + fr, fc);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) b[ni] = lds_frag<KW>(sm.k.b[stg], brow[ni] + fr, fc);
+}
+
+__device__ __forceinline__ void mfma_half(const bf16x8 (&a)[2], const bf16x8 (&b)[4], floatx4 (&acc)[4][4], int m0) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+            acc[m0 + mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], b[ni], acc[m0 + mi][ni], 0, 0, 0);
+}
+
+// Step kt of a 32-wide loop: B fragments of slice kt in bc, those of slice kt+1 go to bn.
+template <int KW>
+__device__ __forceinline__ void half_step(GSmem<KW>& sm, const LoadPlan<KW>& p, int kt, int nk, int& st, int arow0,
+                                          const int (&brow)[4], HalfFrags& h, bf16x8 (&bc)[4], bf16x8 (&bn)[4],
+                                          floatx4 (&acc)[4][4]) {
+    const int lane = lane_id();
+    const int fr = lane & 15, fc = lane >> 4;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) h.hi[mi] = lds_frag<KW>(sm.k.a[st], arow0 + (mi + 2) * 16 + fr, fc);
+    mfma_half(h.lo, bc, acc, 0);
+    wait_vm_lgkm<Ring<KW>::kLoads>();  // slice kt+1 has landed, this wave's reads of slice kt are done
+    lds_barrier();
+    const int nx = st == 2 ? 0 : st + 1;
+    read_half_lo(sm, nx, arow0, brow, h, bn);
+    mfma_half(h.hi, bc, acc, 2);
+    issue_slice(sm, p, st, min(kt + 3, nk - 1) * KW);
+    st = nx;
+}
+
+// The same product with each step straddling the barrier, in two halves: the fragments of
+// a step's second half are read while its first half's MFMAs run, and after the barrier the
+// next slice's first-half fragments while the second half's MFMAs run, so no wave meets the
+// barrier with its LDS reads still to issue and none waits at the top of a step for reads
+// it has just issued.  64-wide slices split into their two 32-wide K halves; 32-wide slices
+// into M halves (A rows 0-31 with all B fragments, then A rows 32-63 with the same B, so the
+// next slice's B fragments take a second set of registers).  The stage of slice kt is
+// overwritten (by slice kt + 3) only after the barrier that follows every wave's last read
+// of it; the slices stay two ahead.  Each accumulator still takes the slices, and the halves
+// of a slice, in K order, so the sums are those of grouped_mainloop_plain.
+template <int KW>
+__device__ __forceinline__ void grouped_mainloop(GSmem<KW>& sm, const LoadPlan<KW>& p, int K, int arow0,
+                                                 const int (&brow)[4], floatx4 (&acc)[4][4]) {
+    static_assert(KW == 32 || KW == 64, "slice width");
+    constexpr int NL = Ring<KW>::kLoads;
+    const int nk = K / KW;
+    issue_slice(sm, p, 0, 0);
+    issue_slice(sm, p, 1, min(1, nk - 1) * KW);
+    wait_vm_lgkm<NL>();
+    lds_barrier();
+    int st = 0;
+    if constexpr (KW == 64) {
+        Frags f0, f1;
+        read_frags<KW>(sm.k.a[0], sm.k.b[0], arow0, brow, 0, f0);
+        issue_slice(sm, p, 2, min(2, nk - 1) * KW);
+        for (int kt = 0; kt < nk; ++kt) {
+            read_frags<KW>(sm.k.a[st], sm.k.b[st], arow0, brow, 4, f1);
+            mfma_frags(f0, acc);
+            wait_vm_lgkm<NL>();  // slice kt+1 has landed, this wave's reads of slice kt are done
+            lds_barrier();
+            const int nx = st == 2 ? 0 : st + 1;  // (kt + 1) % 3; past the last slice, a clamped re-load
+            read_frags<KW>(sm.k.a[nx], sm.k.b[nx], arow0, brow, 0, f0);
+            mfma_frags(f1, acc);
+            issue_slice(sm, p, st, min(kt + 3, nk - 1) * KW);
+            st = nx;
+        }
+    } else {
+        HalfFrags h;
+        read_half_lo(sm, 0, arow0, brow, h, h.b0);
+        issue_slice(sm, p, 2, min(2, nk - 1) * KW);
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            half_step(sm, p, kt, nk, st, arow0, brow, h, h.b0, h.b1, acc);
+            half_step(sm, p, kt + 1, nk, st, arow0, brow, h, h.b1, h.b0, acc);
+        }
+        if (kt < nk) half_step(sm, p, kt, nk, st, arow0, brow, h, h.b0, h.b1, acc);
     }
     wait_vm_lgkm<0>();
     __syncthreads();
@@ -622,9 +747,9 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
             const Q4kSrc<kDownKW> src{
                 a.q4_down + ((size_t)g.e * a.d + n) * (Kfull / kQ4kBlockWeights) * kQ4kBlockBytes, kb};
             grouped_mainloop_regb(sm, plan, src, K, wm * 64, brow, acc);
-        } else {
+        } else {  // the plain loop: the second set of B registers would cost this kernel occupancy
             const LoadPlan<kDownKW> plan = make_plan<kDownKW, false>(row_a, row_b);
-            grouped_mainloop(sm, plan, K, wm * 64, brow, acc);
+            grouped_mainloop_plain(sm, plan, K, wm * 64, brow, acc);
         }
     } else {
         const LoadPlan<kDownKW> plan = make_plan<kDownKW, false>(row_a, row_b);
