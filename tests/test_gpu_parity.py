@@ -379,6 +379,29 @@ def test_grouped_token_permutation_bitwise(name, ov, T):
     assert torch.equal(yp, y[pt])
 
 
+# The same on the decode path: each hidden and output row is a fixed-order sum over its
+# own token's activations (rows of a group are served one by one from the same decoded
+# weights, and the cross-lane reductions pair lanes the same way for every row), so a
+# permuted batch of the same size gives the permuted output, bit for bit.
+@pytest.mark.parametrize("name,ov,T", [
+    ("qwen", dict(d=512, n_expert=64, ff=192, shared_ff=128), 8),
+    ("qwen", dict(d=512, n_expert=64, ff=192, shared_ff=128), 50),
+    ("gptoss_mx", dict(d=320, n_expert=16, ff=192), 8),
+    ("gptoss_mx", dict(d=320, n_expert=16, ff=192), 50),
+    ("qwen_q4k", dict(d=512, n_expert=16, ff=256, shared_ff=256), 8),
+    ("qwen_q4k", dict(d=512, n_expert=16, ff=256, shared_ff=256), 50),
+], ids=lambda v: v if isinstance(v, str) else (str(v) if isinstance(v, int) else ""))
+def test_decode_token_permutation_bitwise(name, ov, T):
+    say("decode permutation", name, ov, T)
+    L, x = case(name, T, **ov)
+    lay = dev_layer(name, path="decode", **ov)
+    perm = np.random.default_rng(6).permutation(T)
+    y = moe_mod().forward(lay, xdev(x))
+    yp = moe_mod().forward(lay, xdev(np.ascontiguousarray(x[perm])))
+    torch.cuda.synchronize()
+    assert torch.equal(yp, y[torch.as_tensor(perm, device=y.device)])
+
+
 # ----------------------------------------------------------------------------- full sizes
 
 @pytest.mark.parametrize("T", [1, 8, 64])
