@@ -763,7 +763,8 @@ def main():
                    "layer_hbm_frac": main_res.get("layer_hbm_frac"),
                    "active_experts_mean": main_res["active_experts_mean"],
                    "ms_median": main_res["ms_median"], "ms_p10": main_res["ms_p10"],
-                   "ms_p90": main_res["ms_p90"], "shell_ms_per_step": main_res["shell_ms_per_step"]},
+                   "ms_p90": main_res["ms_p90"], "shell_ms_per_step": main_res["shell_ms_per_step"],
+                   "graph_ms_per_step": main_res.get("graph_ms_per_step")},
         "roofline": main_res["roofline"],
         "stage_roofline": main_res["stage_roofline"],
         "cpu_baseline": cpu,
