@@ -108,6 +108,7 @@ struct GSmem {
         uint16_t down_h[BM * kDownStageH];
         float down_f[BM * kDownStageF];
     };
+    float row_w[BM];  // down epilogue: the tile rows' routing weights
 };
 
 // Blocks that fit one CU's 160 KB of LDS (at most 2).
@@ -730,6 +731,10 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int wm = wave >> 2, wn = wave & 3;
     const int brow[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
+    // The routing weight of tile row threadIdx.x, loaded now so that its latency hides behind
+    // the main loop; it goes to LDS after the loop, where the epilogue reads it.
+    float my_rw = 1.0f;
+    if (a.row_w && threadIdx.x < BM) my_rw = a.row_w[g.row0 + min(m0 + (int)threadIdx.x, g.n - 1)];
     floatx4 acc[4][4];
     zero(acc);
     if constexpr (WF == kWMx) {
@@ -756,14 +761,13 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
         grouped_mainloop(sm, plan, K, wm * 64, brow, acc);
     }
 
+    if (threadIdx.x < BM) sm.row_w[threadIdx.x] = my_rw;
+    __syncthreads();
     float rw[4][4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = min(m0 + wm * 64 + mi * 16 + 4 * (lane >> 4) + i, g.n - 1);
-            rw[mi][i] = a.row_w ? a.row_w[g.row0 + m] : 1.0f;
-        }
+        for (int i = 0; i < 4; ++i) rw[mi][i] = sm.row_w[wm * 64 + mi * 16 + 4 * (lane >> 4) + i];
     constexpr bool kHalf = sizeof(TY) == 2;
     // bf16: the whole 128 x 256 tile is staged at once; fp32: two 128-column halves (the
     // waves with wn < 2, then the others), each followed by coalesced 16-byte stores.
