@@ -175,20 +175,23 @@ struct Frags {
     bf16x8 a[4], b[4];
 };
 
-template <int KW>
+// MI: the wave's 16-row fragments that hold tile rows (the others are padding past the
+// group's last row, skipped).
+template <int KW, int MI = 4>
 __device__ __forceinline__ void read_frags(const uint16_t* sa, const uint16_t* sb, int arow0, const int (&brow)[4],
                                            int kc, Frags& f) {
     const int lane = lane_id();
     const int fr = lane & 15, fc = lane >> 4;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) f.a[mi] = lds_frag<KW>(sa, arow0 + mi * 16 + fr, kc + fc);
+    for (int mi = 0; mi < MI; ++mi) f.a[mi] = lds_frag<KW>(sa, arow0 + mi * 16 + fr, kc + fc);
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) f.b[ni] = lds_frag<KW>(sb, brow[ni] + fr, kc + fc);
 }
 
+template <int MI = 4>
 __device__ __forceinline__ void mfma_frags(const Frags& f, floatx4 (&acc)[4][4]) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
@@ -276,7 +279,7 @@ __device__ __forceinline__ void half_step(GSmem<KW>& sm, const LoadPlan<KW>& p, 
 // overwritten (by slice kt + 3) only after the barrier that follows every wave's last read
 // of it; the slices stay two ahead.  Each accumulator still takes the slices, and the halves
 // of a slice, in K order, so the sums are those of grouped_mainloop_plain.
-template <int KW>
+template <int KW, int MI = 4>
 __device__ __forceinline__ void grouped_mainloop(GSmem<KW>& sm, const LoadPlan<KW>& p, int K, int arow0,
                                                  const int (&brow)[4], floatx4 (&acc)[4][4]) {
     static_assert(KW == 32 || KW == 64, "slice width");
@@ -289,16 +292,16 @@ __device__ __forceinline__ void grouped_mainloop(GSmem<KW>& sm, const LoadPlan<K
     int st = 0;
     if constexpr (KW == 64) {
         Frags f0, f1;
-        read_frags<KW>(sm.k.a[0], sm.k.b[0], arow0, brow, 0, f0);
+        read_frags<KW, MI>(sm.k.a[0], sm.k.b[0], arow0, brow, 0, f0);
         issue_slice(sm, p, 2, min(2, nk - 1) * KW);
         for (int kt = 0; kt < nk; ++kt) {
-            read_frags<KW>(sm.k.a[st], sm.k.b[st], arow0, brow, 4, f1);
-            mfma_frags(f0, acc);
+            read_frags<KW, MI>(sm.k.a[st], sm.k.b[st], arow0, brow, 4, f1);
+            mfma_frags<MI>(f0, acc);
             wait_vm_lgkm<NL>();  // slice kt+1 has landed, this wave's reads of slice kt are done
             lds_barrier();
             const int nx = st == 2 ? 0 : st + 1;  // (kt + 1) % 3; past the last slice, a clamped re-load
-            read_frags<KW>(sm.k.a[nx], sm.k.b[nx], arow0, brow, 0, f0);
-            mfma_frags(f1, acc);
+            read_frags<KW, MI>(sm.k.a[nx], sm.k.b[nx], arow0, brow, 0, f0);
+            mfma_frags<MI>(f1, acc);
             issue_slice(sm, p, st, min(kt + 3, nk - 1) * KW);
             st = nx;
         }
@@ -660,8 +663,18 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kerne
             grouped_mainloop(sm, plan, a.d, wm * 64, brow, acc);
         }
     } else {
+        // 16-row fragments of this wave's 64 rows that hold group rows: the rest of a partial
+        // tile is padding, whose MFMAs and fragment reads are skipped (its loads are not:
+        // every wave issues its share of each slice).
         const LoadPlan<kUpKW> plan = make_plan<kUpKW, false>(row_a, row_b);
-        grouped_mainloop(sm, plan, a.d, wm * 64, brow, acc);
+        const int live = __builtin_amdgcn_readfirstlane(min(max((g.n - m0 - wm * 64 + 15) / 16, 0), 4));
+        switch (live) {
+            case 4: grouped_mainloop<kUpKW, 4>(sm, plan, a.d, wm * 64, brow, acc); break;
+            case 3: grouped_mainloop<kUpKW, 3>(sm, plan, a.d, wm * 64, brow, acc); break;
+            case 2: grouped_mainloop<kUpKW, 2>(sm, plan, a.d, wm * 64, brow, acc); break;
+            case 1: grouped_mainloop<kUpKW, 1>(sm, plan, a.d, wm * 64, brow, acc); break;
+            default: grouped_mainloop<kUpKW, 0>(sm, plan, a.d, wm * 64, brow, acc); break;
+        }
     }
 
     // Epilogue: lane holds D[4*(lane/16) + i][lane%16] of each 16x16 tile.  Activation,
