@@ -231,9 +231,11 @@ struct HalfFrags {
     bf16x8 lo[2], hi[2], b0[4], b1[4];
 };
 
-template <int KW>
+// MI (0, 2 or 4): the wave's live 16-row fragments, as in read_frags; 2 keeps the lo half.
+template <int KW, int MI = 4>
 __device__ __forceinline__ void read_half_lo(GSmem<KW>& sm, int stg, int arow0, const int (&brow)[4], HalfFrags& h,
                                              bf16x8 (&b)[4]) {
+    if constexpr (MI == 0) return;
     const int lane = lane_id();
     const int fr = lane & 15, fc = lane >> 4;
 #pragma unroll
@@ -251,20 +253,22 @@ __device__ __forceinline__ void mfma_half(const bf16x8 (&a)[2], const bf16x8 (&b
 }
 
 // Step kt of a 32-wide loop: B fragments of slice kt in bc, those of slice kt+1 go to bn.
-template <int KW>
+template <int KW, int MI = 4>
 __device__ __forceinline__ void half_step(GSmem<KW>& sm, const LoadPlan<KW>& p, int kt, int nk, int& st, int arow0,
                                           const int (&brow)[4], HalfFrags& h, bf16x8 (&bc)[4], bf16x8 (&bn)[4],
                                           floatx4 (&acc)[4][4]) {
     const int lane = lane_id();
     const int fr = lane & 15, fc = lane >> 4;
+    if constexpr (MI == 4) {
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) h.hi[mi] = lds_frag<KW>(sm.k.a[st], arow0 + (mi + 2) * 16 + fr, fc);
-    mfma_half(h.lo, bc, acc, 0);
+        for (int mi = 0; mi < 2; ++mi) h.hi[mi] = lds_frag<KW>(sm.k.a[st], arow0 + (mi + 2) * 16 + fr, fc);
+    }
+    if constexpr (MI >= 2) mfma_half(h.lo, bc, acc, 0);
     wait_vm_lgkm<Ring<KW>::kLoads>();  // slice kt+1 has landed, this wave's reads of slice kt are done
     lds_barrier();
     const int nx = st == 2 ? 0 : st + 1;
-    read_half_lo(sm, nx, arow0, brow, h, bn);
-    mfma_half(h.hi, bc, acc, 2);
+    read_half_lo<KW, MI>(sm, nx, arow0, brow, h, bn);
+    if constexpr (MI == 4) mfma_half(h.hi, bc, acc, 2);
     issue_slice(sm, p, st, min(kt + 3, nk - 1) * KW);
     st = nx;
 }
@@ -306,15 +310,16 @@ __device__ __forceinline__ void grouped_mainloop(GSmem<KW>& sm, const LoadPlan<K
             st = nx;
         }
     } else {
+        static_assert(MI == 0 || MI == 2 || MI == 4, "32-wide slices skip whole 32-row halves");
         HalfFrags h;
-        read_half_lo(sm, 0, arow0, brow, h, h.b0);
+        read_half_lo<KW, MI>(sm, 0, arow0, brow, h, h.b0);
         issue_slice(sm, p, 2, min(2, nk - 1) * KW);
         int kt = 0;
         for (; kt + 1 < nk; kt += 2) {
-            half_step(sm, p, kt, nk, st, arow0, brow, h, h.b0, h.b1, acc);
-            half_step(sm, p, kt + 1, nk, st, arow0, brow, h, h.b1, h.b0, acc);
+            half_step<KW, MI>(sm, p, kt, nk, st, arow0, brow, h, h.b0, h.b1, acc);
+            half_step<KW, MI>(sm, p, kt + 1, nk, st, arow0, brow, h, h.b1, h.b0, acc);
         }
-        if (kt < nk) half_step(sm, p, kt, nk, st, arow0, brow, h, h.b0, h.b1, acc);
+        if (kt < nk) half_step<KW, MI>(sm, p, kt, nk, st, arow0, brow, h, h.b0, h.b1, acc);
     }
     wait_vm_lgkm<0>();
     __syncthreads();
@@ -770,8 +775,18 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
             grouped_mainloop_plain(sm, plan, K, wm * 64, brow, acc);
         }
     } else {
+        // As in the up kernel, padding rows past the group's last row run no MFMAs, here by
+        // whole 32-row halves of the wave's 64 rows (bf16 rows only: the three instances
+        // would take the fp32-row kernel past 128 VGPRs, i.e. to one block per CU).
         const LoadPlan<kDownKW> plan = make_plan<kDownKW, false>(row_a, row_b);
-        grouped_mainloop(sm, plan, K, wm * 64, brow, acc);
+        if constexpr (sizeof(TY) == 2) {
+            const int live = __builtin_amdgcn_readfirstlane(min(max((g.n - m0 - wm * 64 + 15) / 16, 0), 4));
+            if (live > 2) grouped_mainloop<kDownKW, 4>(sm, plan, K, wm * 64, brow, acc);
+            else if (live > 0) grouped_mainloop<kDownKW, 2>(sm, plan, K, wm * 64, brow, acc);
+            else grouped_mainloop<kDownKW, 0>(sm, plan, K, wm * 64, brow, acc);
+        } else {
+            grouped_mainloop(sm, plan, K, wm * 64, brow, acc);
+        }
     }
 
     if (threadIdx.x < BM) sm.row_w[threadIdx.x] = my_rw;
