@@ -496,7 +496,8 @@ struct Q4kSrc {
 // every load has drained.  (With the compiler's own waits, which drained every load at the
 // first use of the B registers: gpt-oss-shaped MXFP4 T=4096 1252 -> 1170 us per forward,
 // Q4_K prefill T=8192 1056 -> 1038 us.)
-template <int KW, typename Src>
+// MI: the wave's live 16-row fragments (as in read_frags; the rest are padding).
+template <int KW, int MI = 4, typename Src>
 __device__ __forceinline__ void grouped_mainloop_regb(GSmem<KW>& sm, const LoadPlan<KW>& p, const Src& src, int K,
                                                       int arow0, const int (&brow)[4], floatx4 (&acc)[4][4]) {
     constexpr int LA = Ring<KW>::kLoadsA;
@@ -512,8 +513,14 @@ __device__ __forceinline__ void grouped_mainloop_regb(GSmem<KW>& sm, const LoadP
     for (int kt = 0; kt < nk; ++kt) {
         wait_vm_lgkm<LA + Src::kLoads>();
         lds_barrier();
+        if constexpr (MI > 0) {
 #pragma unroll
-        for (int kc = 0; kc < KW / 8; kc += 4) mfma_k32<KW>(sm.k.a[st], sm.k.b[st], arow0, brow, kc, acc);
+            for (int kc = 0; kc < KW / 8; kc += 4) {
+                Frags f;
+                read_frags<KW, MI>(sm.k.a[st], sm.k.b[st], arow0, brow, kc, f);
+                mfma_frags<MI>(f, acc);
+            }
+        }
         const int nx = st == 2 ? 0 : st + 1;   // (kt + 1) % 3
         src.template ready<LA>(nxt);
         src.store(sm, nx, nxt);                // B of slice kt+1 (clamped re-load on the last step)
@@ -608,6 +615,41 @@ __device__ __forceinline__ bool locate(const PlanMeta* meta, const TileDesc* til
     return true;
 }
 
+// 16-row fragments of wave row wm's 64 tile rows that hold group rows (0 .. 4); the rest of
+// a partial tile is padding, whose MFMAs and fragment reads are skipped (its loads are not:
+// every wave issues its share of each slice).
+__device__ __forceinline__ int up_live(const Group& g, int m0, int wm) {
+    return __builtin_amdgcn_readfirstlane(min(max((g.n - m0 - wm * 64 + 15) / 16, 0), 4));
+}
+
+// The register-staged loop with the padded fragments skipped.
+template <int KW, typename Src>
+__device__ __forceinline__ void regb_live(GSmem<KW>& sm, const LoadPlan<KW>& p, const Src& src, int K, int live,
+                                          int arow0, const int (&brow)[4], floatx4 (&acc)[4][4]) {
+    switch (live) {
+        case 4: grouped_mainloop_regb<KW, 4>(sm, p, src, K, arow0, brow, acc); break;
+        case 3: grouped_mainloop_regb<KW, 3>(sm, p, src, K, arow0, brow, acc); break;
+        case 2: grouped_mainloop_regb<KW, 2>(sm, p, src, K, arow0, brow, acc); break;
+        case 1: grouped_mainloop_regb<KW, 1>(sm, p, src, K, arow0, brow, acc); break;
+        default: grouped_mainloop_regb<KW, 0>(sm, p, src, K, arow0, brow, acc); break;
+    }
+}
+
+// Down kernel, register-staged B: padded fragments skipped by whole 32-row halves for bf16
+// rows; fp32 rows keep the one full loop (more instances would cost that kernel its second
+// block per CU).
+template <typename TY, typename Src>
+__device__ __forceinline__ void down_regb(GSmem<kDownKW>& sm, const LoadPlan<kDownKW>& p, const Src& src, int K,
+                                          int live, int arow0, const int (&brow)[4], floatx4 (&acc)[4][4]) {
+    if constexpr (sizeof(TY) == 2) {
+        if (live > 2) grouped_mainloop_regb<kDownKW, 4>(sm, p, src, K, arow0, brow, acc);
+        else if (live > 0) grouped_mainloop_regb<kDownKW, 2>(sm, p, src, K, arow0, brow, acc);
+        else grouped_mainloop_regb<kDownKW, 0>(sm, p, src, K, arow0, brow, acc);
+    } else {
+        grouped_mainloop_regb<kDownKW, 4>(sm, p, src, K, arow0, brow, acc);
+    }
+}
+
 // WF: storage of the routed gate/up weights.  kWMx: MXFP4 gate_up blocks (a.mx_w, a.mx_s;
 // clamped variant, no shared expert).  kWQ4k: Q4_K w_gate / w_up super-blocks (SwiGLU);
 // the shared expert's tiles stay on the bf16 direct loads.
@@ -654,7 +696,7 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kerne
         const size_t R = (size_t)max(g.e, 0) * 2 * a.ff + 2 * f + (r >= 128 ? 1 : 0);
         const size_t nblk = d / 32;
         const MxSrc<kUpKW> src{MxRow{a.mx_w + R * nblk * 16, a.mx_s + R * nblk}};
-        grouped_mainloop_regb(sm, plan, src, a.d, wm * 64, brow, acc);
+        regb_live<kUpKW>(sm, plan, src, a.d, up_live(g, m0, wm), wm * 64, brow, acc);
     } else if constexpr (WF == kWQ4k) {
         if (!shared) {
             const LoadPlan<kUpKW> plan = make_plan<kUpKW, true>(row_a, row_b);
@@ -662,18 +704,14 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kerne
             const int f = min(f0 + (r & 127), ffg - 1);
             const uint8_t* base = r >= 128 ? a.q4_up : a.q4_gate;
             const Q4kSrc<kUpKW> src{base + ((size_t)g.e * a.ff + f) * (d / kQ4kBlockWeights) * kQ4kBlockBytes, 0};
-            grouped_mainloop_regb(sm, plan, src, a.d, wm * 64, brow, acc);
+            regb_live<kUpKW>(sm, plan, src, a.d, up_live(g, m0, wm), wm * 64, brow, acc);
         } else {
             const LoadPlan<kUpKW> plan = make_plan<kUpKW, false>(row_a, row_b);
             grouped_mainloop(sm, plan, a.d, wm * 64, brow, acc);
         }
     } else {
-        // 16-row fragments of this wave's 64 rows that hold group rows: the rest of a partial
-        // tile is padding, whose MFMAs and fragment reads are skipped (its loads are not:
-        // every wave issues its share of each slice).
         const LoadPlan<kUpKW> plan = make_plan<kUpKW, false>(row_a, row_b);
-        const int live = __builtin_amdgcn_readfirstlane(min(max((g.n - m0 - wm * 64 + 15) / 16, 0), 4));
-        switch (live) {
+        switch (up_live(g, m0, wm)) {
             case 4: grouped_mainloop<kUpKW, 4>(sm, plan, a.d, wm * 64, brow, acc); break;
             case 3: grouped_mainloop<kUpKW, 3>(sm, plan, a.d, wm * 64, brow, acc); break;
             case 2: grouped_mainloop<kUpKW, 2>(sm, plan, a.d, wm * 64, brow, acc); break;
@@ -762,14 +800,14 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
         const size_t R = (size_t)max(g.e, 0) * a.d + n;
         const size_t nblk = Kfull / 32;
         const MxSrc<kDownKW> src{MxRow{a.mx_w + (R * nblk + kb / 32) * 16, a.mx_s + R * nblk + kb / 32}};
-        grouped_mainloop_regb(sm, plan, src, K, wm * 64, brow, acc);
+        down_regb<TY>(sm, plan, src, K, up_live(g, m0, wm), wm * 64, brow, acc);
     } else if constexpr (WF == kWQ4k) {
         if (!shared) {
             const LoadPlan<kDownKW> plan = make_plan<kDownKW, true>(row_a, row_b);
             const int n = min(n0 + (int)(threadIdx.x >> 1), a.d - 1);
             const Q4kSrc<kDownKW> src{
                 a.q4_down + ((size_t)g.e * a.d + n) * (Kfull / kQ4kBlockWeights) * kQ4kBlockBytes, kb};
-            grouped_mainloop_regb(sm, plan, src, K, wm * 64, brow, acc);
+            down_regb<TY>(sm, plan, src, K, up_live(g, m0, wm), wm * 64, brow, acc);
         } else {  // the plain loop: the second set of B registers would cost this kernel occupancy
             const LoadPlan<kDownKW> plan = make_plan<kDownKW, false>(row_a, row_b);
             grouped_mainloop_plain(sm, plan, K, wm * 64, brow, acc);
@@ -780,7 +818,7 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
         // would take the fp32-row kernel past 128 VGPRs, i.e. to one block per CU).
         const LoadPlan<kDownKW> plan = make_plan<kDownKW, false>(row_a, row_b);
         if constexpr (sizeof(TY) == 2) {
-            const int live = __builtin_amdgcn_readfirstlane(min(max((g.n - m0 - wm * 64 + 15) / 16, 0), 4));
+            const int live = up_live(g, m0, wm);
             if (live > 2) grouped_mainloop<kDownKW, 4>(sm, plan, K, wm * 64, brow, acc);
             else if (live > 0) grouped_mainloop<kDownKW, 2>(sm, plan, K, wm * 64, brow, acc);
             else grouped_mainloop<kDownKW, 0>(sm, plan, K, wm * 64, brow, acc);
