@@ -105,7 +105,7 @@ enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_GROUPED = 2 };
 enum { MOE_EXPERTS_DENSE = 0, MOE_EXPERTS_MXFP4 = 1, MOE_EXPERTS_Q4K = 2 };
 
 /* One MoE layer.  Fixed layout: 9 int32, 3 float, then 12 pointers (offset 48), then
- * 2 int32 and 2 pointers (offset 144).  No field depends on a build flag.  All pointers
+ * 2 int32 and 3 pointers (offset 144).  No field depends on a build flag.  All pointers
  * are device memory, 16-byte aligned (b_router, b_gate_up, b_down and the MXFP4 scales:
  * element-aligned suffices). */
 typedef struct moe_layer {
@@ -137,6 +137,11 @@ typedef struct moe_layer {
     int32_t reserved0;        /* 0                                                     */
     const uint8_t* w_gate_up_scales;  /* MXFP4: [E, 2*ff, d/32] E8M0, else NULL        */
     const uint8_t* w_down_scales;     /* MXFP4: [E, d, ff/32] E8M0, else NULL          */
+    const void* grouped_pack;         /* MXFP4, Q4K: the grouped path's copy of the
+                                         routed experts' weights written by
+                                         moe_grouped_pack, or NULL (the grouped kernels
+                                         then read the blocks above); must be NULL for
+                                         dense experts                                 */
 } moe_layer;
 
 /* ABI version of this header (bumped on any layout or signature change). */
@@ -226,6 +231,27 @@ moe_status moe_forward_shell(const moe_layer* L, const void* h, int32_t T, const
  * array per GPU, allocated when the library's code is loaded on that GPU and held until
  * the process ends). */
 #define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* The grouped (MFMA) path's copy of MXFP4 or Q4K routed-expert weights.  Each K-slice
+ * of a weight tile that the grouped kernels expand is stored as contiguous runs, in the
+ * order the threads of a block read them, so a wave's loads cover whole cache lines; in
+ * the checkpoint layouts (rows of 16-byte MXFP4 blocks, "Phase 19: MoE - gpt-oss-20b",
+ * section 3; rows of 144-byte Q4_K super-blocks) every thread reads a few bytes of a
+ * different row.  Same codes, scales and headers, so results are bit for bit those of the
+ * checkpoint layout.  The decode GEMVs keep reading the checkpoint layout, which suits
+ * their whole-row reads.
+ * moe_grouped_pack_size writes the copy's size to *bytes (host): about the size of the
+ * routed experts' gate/up and down weights in their format.  Errors: MOE_ERR_ARG /
+ * MOE_ERR_UNSUPPORTED as for moe_forward; MOE_ERR_UNSUPPORTED for dense experts (they
+ * have no grouped copy).
+ * moe_grouped_pack enqueues on `stream` the kernels that write the copy to `dst` (device,
+ * 16-byte aligned, at least that size; it must not overlap the layer's weights).  The
+ * caller owns `dst`; store it in moe_layer.grouped_pack for the calls that should use it
+ * and keep it alive while they run.  L->grouped_pack itself is ignored here.  Errors as
+ * moe_grouped_pack_size, plus MOE_ERR_ARG for a null dst, MOE_ERR_UNSUPPORTED for a
+ * misaligned one, MOE_ERR_WORKSPACE when `bytes` is below the size, and MOE_ERR_DEVICE. */
+moe_status moe_grouped_pack_size(const moe_layer* L, size_t* bytes);
+moe_status moe_grouped_pack(const moe_layer* L, void* dst, size_t bytes, void* stream);
 
 /* moe_forward without a caller workspace, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).

@@ -37,6 +37,7 @@
 // blocks.  MXFP4 expert weights take the same loops with their B slices expanded from FP4
 // blocks into the ring, and Q4_K weights from their super-blocks (see
 // grouped_mainloop_regb).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -331,10 +332,15 @@ __device__ __forceinline__ void grouped_mainloop(GSmem<KW>& sm, const LoadPlan<K
 // of the N-tile, half threadIdx.x & 1 of the slice's KW codes (KW / 4 bytes) and the
 // block's scale -- and one step later expands it with gfx950's scaled FP4 conversion into
 // the slice's bf16 LDS rows (same swizzled layout as the direct loads).  The weights then
-// cost 0.53 bytes each from memory instead of 2.
+// cost 0.53 bytes each from memory instead of 2.  The thread's piece of slice s sits at
+// codes + s * cstride and its scale at scales + s * sstride: in the checkpoint layout
+// (rows of blocks) each thread of a wave reads another row, one cache line per row for a
+// few bytes of it; in the grouped copy (mx_pack_layout) the pieces of one slice of one
+// tile are contiguous, in thread order, so a wave reads whole lines.
 struct MxRow {
-    const uint8_t* codes;   // the row's first block
-    const uint8_t* scales;  // the row's first scale byte
+    const uint8_t* codes;   // this thread's piece of slice 0
+    const uint8_t* scales;  // the scale byte of that piece
+    int cstride, sstride;   // bytes between the pieces of consecutive slices
 };
 
 // Vector loads into registers that the compiler does not track.  Its wait-count model
@@ -391,17 +397,11 @@ constexpr int kMxLoads = 2;  // vector loads per thread per slice (codes, scale)
 
 template <int KW>
 __device__ __forceinline__ void mx_load(const MxRow& m, int k0, MxRegs<KW>& r) {
-    const int h = threadIdx.x & 1;
-    if constexpr (KW == 64) {  // two blocks per row slice: one each
-        const int blk = k0 / 32 + h;
-        vload16(r.w, m.codes + (size_t)blk * 16);
-        vload_u8(r.s, m.scales + blk);
-    } else {  // one block per row slice: half of it each
-        static_assert(KW == 32, "MXFP4 slices are one or two blocks wide");
-        const int blk = k0 / 32;
-        vload8(r.w, m.codes + (size_t)blk * 16 + 8 * h);
-        vload_u8(r.s, m.scales + blk);
-    }
+    static_assert(KW == 64 || KW == 32, "MXFP4 slices are one or two blocks wide");
+    const int sl = k0 / KW;
+    if constexpr (KW == 64) vload16(r.w, m.codes + (size_t)sl * m.cstride);  // one whole block
+    else vload8(r.w, m.codes + (size_t)sl * m.cstride);                      // half a block
+    vload_u8(r.s, m.scales + (size_t)sl * m.sstride);
 }
 
 template <int KW>
@@ -429,58 +429,66 @@ struct MxSrc {
     __device__ __forceinline__ void store(GSmem<KW>& sm, int stage, const Regs& r) const { mx_store<KW>(sm, stage, r); }
 };
 
-// Q4_K weights (layout in q4k_dev.h).  A 64-wide slice is one quant run (two sub-blocks):
-// half h of a row takes sub-block 2c + h, i.e. nibble h of all 32 run bytes.  A 32-wide
-// slice is one sub-block j: half h takes its weights 16h .. 16h+15, i.e. bytes 16h .. of
-// run j / 2, nibble j & 1.  Either way the super-block's 16-byte header comes along.
-// `kbase` is the absolute input index of the call's K = 0 (split-K slices start inside a
-// super-block).
+// Q4_K weights (layout in q4k_dev.h).  Half h of a row takes 16 quant bytes and the
+// super-block's 16-byte header per slice.  A 64-wide slice is one quant run c: its bytes
+// 16h .. 16h+15, whose low nibbles are inputs 16h .. of the slice (sub-block 2c) and high
+// nibbles inputs 32 + 16h .. (sub-block 2c + 1).  A 32-wide slice is one sub-block j: its
+// weights 16h .. 16h+15, i.e. bytes 16h .. of run j / 2, nibble j & 1.  `kbase` is the
+// absolute input index of the call's K = 0 (split-K slices start inside a super-block).
+// Checkpoint layout: each thread's row is a run of 144-byte super-blocks, so the threads
+// of a wave read 32 rows, a line or two per row for 32 bytes of it.  Grouped copy
+// (q4k_pack_layout): per tile and super-block, the 256 tile rows' headers (16 bytes each)
+// and then the four runs, each as 256 rows of 32 bytes, so a wave reads whole lines.
 template <int KW>
 struct Q4kRegs {
     u32x4 head;
-    u32x4 q[KW == 64 ? 2 : 1];
-    int j;  // sub-block whose scale and min apply
+    u32x4 q;
+    int j;  // sub-block of the low nibbles (64-wide) or of the slice (32-wide)
 };
 
 template <int KW>
 struct Q4kSrc {
-    const uint8_t* row;  // this thread's B row, first super-block
+    const uint8_t* base;  // checkpoint: this thread's B row; grouped copy: the tile's first group
     int kbase;
+    bool packed;
     using Regs = Q4kRegs<KW>;
-    static constexpr int kLoads = KW == 64 ? 3 : 2;
+    static constexpr int kLoads = 2;
+    static_assert(KW == 64 || KW == 32, "Q4_K slices are one run or one sub-block wide");
     __device__ __forceinline__ void load(int k0, Regs& r) const {
-        const int k = kbase + k0, h = threadIdx.x & 1;
-        const int j = (k % kQ4kBlockWeights) / 32;
-        const uint8_t* blk = row + (size_t)(k / kQ4kBlockWeights) * kQ4kBlockBytes;
-        vload16(r.head, blk);
-        if constexpr (KW == 64) {
-            const uint8_t* run = blk + 16 + 32 * (j / 2);
-            vload16(r.q[0], run);
-            vload16(r.q[1], run + 16);
-            r.j = j + h;
+        const int k = kbase + k0, h = threadIdx.x & 1, row = threadIdx.x >> 1;
+        const int j = (k % kQ4kBlockWeights) / 32, c = j / 2;
+        const size_t sb = (size_t)(k / kQ4kBlockWeights);
+        const uint8_t *head, *quant;
+        if (packed) {
+            const uint8_t* grp = base + sb * (kGThreads / 2) * kQ4kBlockBytes;
+            head = grp + row * 16;
+            quant = grp + (kGThreads / 2) * 16 + (size_t)c * (kGThreads / 2) * 32 + row * 32 + 16 * h;
         } else {
-            static_assert(KW == 32, "Q4_K slices are one run or one sub-block wide");
-            vload16(r.q[0], blk + 16 + 32 * (j / 2) + 16 * h);
-            r.j = j;
+            head = base + sb * kQ4kBlockBytes;
+            quant = head + 16 + 32 * c + 16 * h;
         }
+        vload16(r.head, head);
+        vload16(r.q, quant);
+        r.j = j;
     }
     template <int N>
-    __device__ __forceinline__ void ready(Regs& r) const {
-        if constexpr (KW == 64) reg_wait<N>(r.head, r.q[0], r.q[1]);
-        else reg_wait<N>(r.head, r.q[0]);
-    }
+    __device__ __forceinline__ void ready(Regs& r) const { reg_wait<N>(r.head, r.q); }
     __device__ __forceinline__ void store(GSmem<KW>& sm, int stage, const Regs& r) const {
         const int row_l = threadIdx.x >> 1, h = threadIdx.x & 1;
-        float a, b;
         const uint4 head = make_uint4(r.head[0], r.head[1], r.head[2], r.head[3]);
+        float a, b;
         q4k_sub_scale(head, r.j, a, b);
-        const int shift = 4 * (r.j & 1);
-        constexpr int NC = KW / 16;  // 16-byte LDS chunks per thread
-#pragma unroll
-        for (int q = 0; q < NC; ++q) {
-            const u32x4& v = r.q[q / 2];
-            const uint32_t w0 = (q & 1) ? v[2] : v[0], w1 = (q & 1) ? v[3] : v[1];
-            lds_write16(&sm.k.b[stage][swz<KW>(row_l, h * NC + q)], q4k_dequant8(w0, w1, shift, a, b));
+        if constexpr (KW == 64) {
+            float a1, b1;
+            q4k_sub_scale(head, r.j + 1, a1, b1);
+            lds_write16(&sm.k.b[stage][swz<KW>(row_l, 2 * h)], q4k_dequant8(r.q[0], r.q[1], 0, a, b));
+            lds_write16(&sm.k.b[stage][swz<KW>(row_l, 2 * h + 1)], q4k_dequant8(r.q[2], r.q[3], 0, a, b));
+            lds_write16(&sm.k.b[stage][swz<KW>(row_l, 4 + 2 * h)], q4k_dequant8(r.q[0], r.q[1], 4, a1, b1));
+            lds_write16(&sm.k.b[stage][swz<KW>(row_l, 5 + 2 * h)], q4k_dequant8(r.q[2], r.q[3], 4, a1, b1));
+        } else {
+            const int shift = 4 * (r.j & 1);
+            lds_write16(&sm.k.b[stage][swz<KW>(row_l, 2 * h)], q4k_dequant8(r.q[0], r.q[1], shift, a, b));
+            lds_write16(&sm.k.b[stage][swz<KW>(row_l, 2 * h + 1)], q4k_dequant8(r.q[2], r.q[3], shift, a, b));
         }
     }
 };
@@ -556,6 +564,8 @@ struct UpArgs {
     uint16_t* H;                // bf16 [rows, hstride]
     int hstride, T, d, ff, ffs, n_ntiles;
     float alpha, limit;
+    int mx_packed;              // mx_w / mx_s point into the grouped copy (mx_pack_layout)
+    int q4_packed;              // q4_gate points at the grouped copy's up region (q4k_pack_layout)
 };
 
 struct DownArgs {
@@ -573,6 +583,7 @@ struct DownArgs {
     void* y;                  // [rows, d], bf16 or fp32; with ksplit > 1 fp32 [ksplit][rows][d]
     int hstride, d, ff, ffs, n_ntiles;
     int ksplit, rows;         // K slices per tile (each block sums K / ksplit), grouped rows
+    int mx_packed;            // mx_w / mx_s, or q4_down, point into the grouped copy
 };
 
 // XCD-aware tile order.  Workgroups are dispatched to the 8 XCDs round-robin by block
@@ -691,19 +702,33 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kerne
     if constexpr (WF == kWMx) {
         // This thread's B row (tile row threadIdx.x / 2), in the interleaved gate_up rows.
         const LoadPlan<kUpKW> plan = make_plan<kUpKW, true>(row_a, row_b);
-        const int r = threadIdx.x >> 1;
-        const int f = min(f0 + (r & 127), ffg - 1);
-        const size_t R = (size_t)max(g.e, 0) * 2 * a.ff + 2 * f + (r >= 128 ? 1 : 0);
-        const size_t nblk = d / 32;
-        const MxSrc<kUpKW> src{MxRow{a.mx_w + R * nblk * 16, a.mx_s + R * nblk}};
+        const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
+        MxRow m;
+        if (a.mx_packed) {
+            const size_t tile = (size_t)max(g.e, 0) * ((a.ff + 127) / 128) + nt, slices = d / kUpKW;
+            m = MxRow{a.mx_w + (tile * slices * kGThreads + threadIdx.x) * 16, a.mx_s + tile * slices * kGThreads + threadIdx.x,
+                      kGThreads * 16, kGThreads};
+        } else {
+            const int f = min(f0 + (r & 127), ffg - 1);
+            const size_t R = (size_t)max(g.e, 0) * 2 * a.ff + 2 * f + (r >= 128 ? 1 : 0);
+            const size_t nblk = d / 32;
+            m = MxRow{a.mx_w + (R * nblk + h) * 16, a.mx_s + R * nblk + h, 32, 2};
+        }
+        const MxSrc<kUpKW> src{m};
         regb_live<kUpKW>(sm, plan, src, a.d, up_live(g, m0, wm), wm * 64, brow, acc);
     } else if constexpr (WF == kWQ4k) {
         if (!shared) {
             const LoadPlan<kUpKW> plan = make_plan<kUpKW, true>(row_a, row_b);
             const int r = threadIdx.x >> 1;
-            const int f = min(f0 + (r & 127), ffg - 1);
-            const uint8_t* base = r >= 128 ? a.q4_up : a.q4_gate;
-            const Q4kSrc<kUpKW> src{base + ((size_t)g.e * a.ff + f) * (d / kQ4kBlockWeights) * kQ4kBlockBytes, 0};
+            const size_t nsb = d / kQ4kBlockWeights;
+            const uint8_t* base;
+            if (a.q4_packed) {
+                base = a.q4_gate + ((size_t)g.e * ((a.ff + 127) / 128) + nt) * nsb * (kGThreads / 2) * kQ4kBlockBytes;
+            } else {
+                const int f = min(f0 + (r & 127), ffg - 1);
+                base = (r >= 128 ? a.q4_up : a.q4_gate) + ((size_t)g.e * a.ff + f) * nsb * kQ4kBlockBytes;
+            }
+            const Q4kSrc<kUpKW> src{base, 0, a.q4_packed != 0};
             regb_live<kUpKW>(sm, plan, src, a.d, up_live(g, m0, wm), wm * 64, brow, acc);
         } else {
             const LoadPlan<kUpKW> plan = make_plan<kUpKW, false>(row_a, row_b);
@@ -796,17 +821,32 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
     if constexpr (WF == kWMx) {
         // This thread's B row (tile row threadIdx.x / 2) of W_d, from this split's first block.
         const LoadPlan<kDownKW> plan = make_plan<kDownKW, true>(row_a, row_b);
-        const int n = min(n0 + (int)(threadIdx.x >> 1), a.d - 1);
-        const size_t R = (size_t)max(g.e, 0) * a.d + n;
-        const size_t nblk = Kfull / 32;
-        const MxSrc<kDownKW> src{MxRow{a.mx_w + (R * nblk + kb / 32) * 16, a.mx_s + R * nblk + kb / 32}};
+        const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
+        MxRow m;
+        if (a.mx_packed) {
+            const size_t tile = (size_t)max(g.e, 0) * a.n_ntiles + nt, slices = Kfull / kDownKW;
+            const size_t first = tile * slices + kb / kDownKW;  // this split's first slice
+            m = MxRow{a.mx_w + (first * GBN + r) * 16 + 8 * h, a.mx_s + first * GBN + r, GBN * 16, GBN};
+        } else {
+            const int n = min(n0 + r, a.d - 1);
+            const size_t R = (size_t)max(g.e, 0) * a.d + n;
+            const size_t nblk = Kfull / 32;
+            m = MxRow{a.mx_w + (R * nblk + kb / 32) * 16 + 8 * h, a.mx_s + R * nblk + kb / 32, 16, 1};
+        }
+        const MxSrc<kDownKW> src{m};
         down_regb<TY>(sm, plan, src, K, up_live(g, m0, wm), wm * 64, brow, acc);
     } else if constexpr (WF == kWQ4k) {
         if (!shared) {
             const LoadPlan<kDownKW> plan = make_plan<kDownKW, true>(row_a, row_b);
-            const int n = min(n0 + (int)(threadIdx.x >> 1), a.d - 1);
-            const Q4kSrc<kDownKW> src{
-                a.q4_down + ((size_t)g.e * a.d + n) * (Kfull / kQ4kBlockWeights) * kQ4kBlockBytes, kb};
+            const size_t nsb = Kfull / kQ4kBlockWeights;
+            const uint8_t* base;
+            if (a.mx_packed) {
+                base = a.q4_down + ((size_t)g.e * a.n_ntiles + nt) * nsb * GBN * kQ4kBlockBytes;
+            } else {
+                const int n = min(n0 + (int)(threadIdx.x >> 1), a.d - 1);
+                base = a.q4_down + ((size_t)g.e * a.d + n) * nsb * kQ4kBlockBytes;
+            }
+            const Q4kSrc<kDownKW> src{base, kb, a.mx_packed != 0};
             down_regb<TY>(sm, plan, src, K, up_live(g, m0, wm), wm * 64, brow, acc);
         } else {  // the plain loop: the second set of B registers would cost this kernel occupancy
             const LoadPlan<kDownKW> plan = make_plan<kDownKW, false>(row_a, row_b);
@@ -1043,6 +1083,83 @@ __global__ __launch_bounds__(kRThreads, 2) void router_mfma_kernel(const uint16_
     }
 }
 
+// The grouped copy of MXFP4 expert weights (moe_grouped_pack), one thread per 16-byte
+// block.  Up: piece i = ((e * NTu + nt) * Su + s) * 512 + t holds the block that thread t
+// of the up kernel's block for N-tile nt reads in slice s (tile row r = t / 2: gate unit
+// nt * 128 + r for r < 128, else up unit nt * 128 + r - 128, clamped to the last unit;
+// block 2s + t % 2 of that row), its scale byte at the same index.  Down: piece
+// i = ((e * NTd + nt) * Sd + s) * 256 + r holds block s of output row nt * 256 + r
+// (clamped to the last row).  Units and rows past the matrix repeat the last one, as the
+// kernels' own clamps do.
+__global__ __launch_bounds__(256) void mx_pack_up_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ sc,
+                                                         int ff, int d, long long pieces, int ntu, int su,
+                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const size_t nblk = d / 32;
+    for (long long i = blockIdx.x * 256ll + threadIdx.x; i < pieces; i += (long long)gridDim.x * 256) {
+        const int t = (int)(i % kGThreads);
+        long long rest = i / kGThreads;
+        const int sl = (int)(rest % su);
+        rest /= su;
+        const int nt = (int)(rest % ntu);
+        const long long e = rest / ntu;
+        const int r = t >> 1;
+        const int f = min(nt * 128 + (r & 127), ff - 1);
+        const size_t R = (size_t)e * 2 * ff + 2 * f + (r >= 128 ? 1 : 0);
+        const size_t blk = R * nblk + 2 * sl + (t & 1);
+        *reinterpret_cast<uint4*>(codes + (size_t)i * 16) = *reinterpret_cast<const uint4*>(w + blk * 16);
+        scales[i] = sc[blk];
+    }
+}
+
+__global__ __launch_bounds__(256) void mx_pack_down_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ sc,
+                                                           int ff, int d, long long pieces, int ntd, int sd,
+                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const size_t nblk = ff / 32;
+    for (long long i = blockIdx.x * 256ll + threadIdx.x; i < pieces; i += (long long)gridDim.x * 256) {
+        const int r = (int)(i % GBN);
+        long long rest = i / GBN;
+        const int sl = (int)(rest % sd);
+        rest /= sd;
+        const int nt = (int)(rest % ntd);
+        const long long e = rest / ntd;
+        const int n = min(nt * GBN + r, d - 1);
+        const size_t blk = ((size_t)e * d + n) * nblk + sl;
+        *reinterpret_cast<uint4*>(codes + (size_t)i * 16) = *reinterpret_cast<const uint4*>(w + blk * 16);
+        scales[i] = sc[blk];
+    }
+}
+
+// The grouped copy of Q4_K expert weights, one thread per (tile row, super-block): per
+// (expert, N-tile, super-block) group of 256 tile rows, the rows' 16-byte headers, then
+// quant run c (c = 0..3) of every row as 32 bytes.  Up tiles: rows 0..127 are gate units
+// nt * 128 + r, rows 128..255 the up units (clamped to the last unit); down tiles: output
+// rows nt * 256 + r (clamped to the last row).
+__global__ __launch_bounds__(256) void q4k_pack_kernel(const uint8_t* __restrict__ w_a, const uint8_t* __restrict__ w_b,
+                                                       int rows, int tile_rows, int half, long long items, int nt_n,
+                                                       int nsb, uint8_t* __restrict__ out) {
+    for (long long i = blockIdx.x * 256ll + threadIdx.x; i < items; i += (long long)gridDim.x * 256) {
+        const int r = (int)(i % GBN);
+        long long rest = i / GBN;
+        const int sb = (int)(rest % nsb);
+        rest /= nsb;
+        const int nt = (int)(rest % nt_n);
+        const long long e = rest / nt_n;
+        // half > 0: rows >= half come from w_b (the up units of an up tile)
+        const bool second = half > 0 && r >= half;
+        const int local = half > 0 ? (second ? r - half : r) : r;
+        const int n = min(nt * tile_rows + local, rows - 1);
+        const uint8_t* src = (second ? w_b : w_a) + (((size_t)e * rows + n) * nsb + sb) * kQ4kBlockBytes;
+        uint8_t* grp = out + (((size_t)e * nt_n + nt) * nsb + sb) * GBN * kQ4kBlockBytes;
+        *reinterpret_cast<uint4*>(grp + r * 16) = *reinterpret_cast<const uint4*>(src);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint8_t* dst = grp + GBN * 16 + (size_t)c * GBN * 32 + r * 32;
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src + 16 + 32 * c);
+            *reinterpret_cast<uint4*>(dst + 16) = *reinterpret_cast<const uint4*>(src + 32 + 32 * c);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_router_mfma(const moe_layer& L, const void* x, int T, float* logits, int ld,
@@ -1069,6 +1186,66 @@ int grouped_max_mtiles(int E, int T, int k, bool shared) {
     return (int)b;
 }
 
+MxPackLayout mx_pack_layout(const moe_layer& L) {
+    MxPackLayout p{};
+    p.ntu = (L.ff + 127) / 128;
+    p.su = L.d / kUpKW;
+    p.ntd = (L.d + GBN - 1) / GBN;
+    p.sd = L.ff / kDownKW;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) / 256 * 256;
+        return at;
+    };
+    const size_t E = (size_t)L.n_expert;
+    p.up_codes = take(E * p.ntu * p.su * kGThreads * 16);
+    p.up_scales = take(E * p.ntu * p.su * kGThreads);
+    p.dn_codes = take(E * p.ntd * p.sd * GBN * 16);
+    p.dn_scales = take(E * p.ntd * p.sd * GBN);
+    p.total = off;
+    return p;
+}
+
+Q4kPackLayout q4k_pack_layout(const moe_layer& L) {
+    Q4kPackLayout p{};
+    p.ntu = (L.ff + 127) / 128;
+    p.ntd = (L.d + GBN - 1) / GBN;
+    const size_t group = (size_t)GBN * kQ4kBlockBytes, E = (size_t)L.n_expert;
+    const size_t up = E * p.ntu * (L.d / kQ4kBlockWeights) * group;
+    p.up = 0;
+    p.dn = (up + 255) / 256 * 256;
+    p.total = p.dn + E * p.ntd * (L.ff / kQ4kBlockWeights) * group;
+    return p;
+}
+
+hipError_t launch_q4k_pack(const moe_layer& L, void* dst, hipStream_t s) {
+    const Q4kPackLayout p = q4k_pack_layout(L);
+    uint8_t* base = static_cast<uint8_t*>(dst);
+    const int nsb_u = L.d / kQ4kBlockWeights, nsb_d = L.ff / kQ4kBlockWeights;
+    const long long up = (long long)L.n_expert * p.ntu * nsb_u * GBN;
+    const long long dn = (long long)L.n_expert * p.ntd * nsb_d * GBN;
+    auto blocks = [](long long n) { return (unsigned)std::min<long long>((n + 255) / 256, 8192); };
+    q4k_pack_kernel<<<blocks(up), 256, 0, s>>>(static_cast<const uint8_t*>(L.w_gate), static_cast<const uint8_t*>(L.w_up),
+                                               L.ff, 128, 128, up, p.ntu, nsb_u, base + p.up);
+    q4k_pack_kernel<<<blocks(dn), 256, 0, s>>>(static_cast<const uint8_t*>(L.w_down), nullptr, L.d, GBN, 0, dn, p.ntd,
+                                               nsb_d, base + p.dn);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_pack(const moe_layer& L, void* dst, hipStream_t s) {
+    const MxPackLayout p = mx_pack_layout(L);
+    uint8_t* base = static_cast<uint8_t*>(dst);
+    const long long up = (long long)L.n_expert * p.ntu * p.su * kGThreads;
+    const long long dn = (long long)L.n_expert * p.ntd * p.sd * GBN;
+    auto blocks = [](long long n) { return (unsigned)std::min<long long>((n + 255) / 256, 8192); };
+    mx_pack_up_kernel<<<blocks(up), 256, 0, s>>>(static_cast<const uint8_t*>(L.w_gate_up), L.w_gate_up_scales, L.ff,
+                                                 L.d, up, p.ntu, p.su, base + p.up_codes, base + p.up_scales);
+    mx_pack_down_kernel<<<blocks(dn), 256, 0, s>>>(static_cast<const uint8_t*>(L.w_down), L.w_down_scales, L.ff, L.d,
+                                                   dn, p.ntd, p.sd, base + p.dn_codes, base + p.dn_scales);
+    return hipGetLastError();
+}
+
 hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const int32_t* perm_token,
                               const Group* groups, const PlanMeta* meta, const TileDesc* tiles,
                               uint16_t* H, int hstride, const float* row_w, void* y, bool y_bf16,
@@ -1085,15 +1262,27 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
     if (mx && (L.act != MOE_ACT_SWIGLU_OAI || shared || L.d % 64 || L.ff % 32)) return hipErrorInvalidValue;
     if (q4 && (L.act != MOE_ACT_SWIGLU || L.d % kQ4kBlockWeights || L.ff % kQ4kBlockWeights))
         return hipErrorInvalidValue;
-    const auto* q4_gate = q4 ? static_cast<const uint8_t*>(L.w_gate) : nullptr;
-    const auto* q4_up = q4 ? static_cast<const uint8_t*>(L.w_up) : nullptr;
-    const auto* q4_down = q4 ? static_cast<const uint8_t*>(L.w_down) : nullptr;
+    // With the grouped copy (MXFP4 or Q4_K), both GEMMs read their weight slices from it.
+    const bool packed = (mx || q4) && L.grouped_pack;
+    const uint8_t* pack = static_cast<const uint8_t*>(L.grouped_pack);
+    const Q4kPackLayout pq = q4 && packed ? q4k_pack_layout(L) : Q4kPackLayout{};
+    const auto* q4_gate = q4 ? (packed ? pack + pq.up : static_cast<const uint8_t*>(L.w_gate)) : nullptr;
+    const auto* q4_up = q4 && !packed ? static_cast<const uint8_t*>(L.w_up) : nullptr;
+    const auto* q4_down = q4 ? (packed ? pack + pq.dn : static_cast<const uint8_t*>(L.w_down)) : nullptr;
     UpArgs u{static_cast<const uint16_t*>(x), perm_token, groups, meta, tiles,
              static_cast<const uint16_t*>(L.w_gate), static_cast<const uint16_t*>(L.w_up),
              static_cast<const uint16_t*>(L.w_gate_up), static_cast<const uint16_t*>(L.b_gate_up),
              static_cast<const uint16_t*>(L.ws_gate), static_cast<const uint16_t*>(L.ws_up),
              mx ? static_cast<const uint8_t*>(L.w_gate_up) : nullptr, mx ? L.w_gate_up_scales : nullptr, q4_gate,
              q4_up, H, hstride, T, L.d, L.ff, L.shared_ff, nn_up, L.oai_alpha, L.oai_limit};
+    const bool mx_packed = mx && packed;
+    const MxPackLayout pk = mx_packed ? mx_pack_layout(L) : MxPackLayout{};
+    if (mx_packed) {
+        u.mx_w = pack + pk.up_codes;
+        u.mx_s = pack + pk.up_scales;
+        u.mx_packed = 1;
+    }
+    u.q4_packed = q4 && packed ? 1 : 0;
     const dim3 gu((unsigned)grid_blocks(mt, nn_up));
     if (mx)
         gg_up_kernel<true, kWMx><<<gu, kGThreads, 0, s>>>(u);
@@ -1103,8 +1292,8 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
         gg_up_kernel<true, kWDense><<<gu, kGThreads, 0, s>>>(u);
     else
         gg_up_kernel<false, kWDense><<<gu, kGThreads, 0, s>>>(u);
-    const uint8_t* mx_dw = mx ? static_cast<const uint8_t*>(L.w_down) : nullptr;
-    const uint8_t* mx_ds = mx ? L.w_down_scales : nullptr;
+    const uint8_t* mx_dw = mx_packed ? pack + pk.dn_codes : mx ? static_cast<const uint8_t*>(L.w_down) : nullptr;
+    const uint8_t* mx_ds = mx_packed ? pack + pk.dn_scales : mx ? L.w_down_scales : nullptr;
     const int nn = (L.d + GBN - 1) / GBN;
     const int rows = T * L.k + (shared ? T : 0);
     const auto* b_down = static_cast<const uint16_t*>(L.b_down);
@@ -1117,7 +1306,7 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
             return hipErrorInvalidValue;
         DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down), nullptr,
                     static_cast<const uint16_t*>(L.ws_down), mx_dw, mx_ds, q4_down, nullptr, partial, hstride, L.d,
-                    L.ff, L.shared_ff, nn, ksplit, rows};
+                    L.ff, L.shared_ff, nn, ksplit, rows, packed ? 1 : 0};
         const dim3 gs((unsigned)grid_blocks(mt, nn * ksplit));
         if (wf == kWMx) gg_down_kernel<float, kWMx><<<gs, kGThreads, 0, s>>>(dn);
         else if (wf == kWQ4k) gg_down_kernel<float, kWQ4k><<<gs, kGThreads, 0, s>>>(dn);
@@ -1133,7 +1322,7 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
     }
     DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down), b_down,
                 static_cast<const uint16_t*>(L.ws_down), mx_dw, mx_ds, q4_down, row_w, y, hstride, L.d, L.ff,
-                L.shared_ff, nn, 1, rows};
+                L.shared_ff, nn, 1, rows, packed ? 1 : 0};
     const dim3 gd((unsigned)grid_blocks(mt, nn));
 #define SMOE_GG_DOWN(WF)                                                              \
     do {                                                                              \

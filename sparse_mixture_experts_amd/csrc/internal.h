@@ -67,6 +67,27 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
 hipError_t launch_plan(const int32_t* offsets, int E, int T, int k, bool shared, int tile_m,
                        Group* groups, PlanMeta* meta, TileDesc* tiles, hipStream_t s);
 int grouped_max_mtiles(int E, int T, int k, bool shared);
+// The grouped copy of MXFP4 expert weights (moe_grouped_pack): byte offsets of its four
+// regions (256-aligned) and its tile and slice counts.  Up: NTu N-tiles of 128 hidden units
+// (256 gate/up rows) times Su = d/64 slices, 512 16-byte blocks and 512 scale bytes per
+// (expert, N-tile, slice).  Down: NTd N-tiles of 256 output rows times Sd = ff/32 slices,
+// 256 blocks and 256 scale bytes each.
+struct MxPackLayout {
+    size_t up_codes, up_scales, dn_codes, dn_scales, total;
+    int ntu, su, ntd, sd;
+};
+MxPackLayout mx_pack_layout(const moe_layer& L);
+hipError_t launch_mx_pack(const moe_layer& L, void* dst, hipStream_t s);
+// The grouped copy of Q4_K expert weights: up region (NTu N-tiles of 128 units x d/256
+// super-blocks) at `up`, down region (NTd N-tiles of 256 rows x ff/256) at `dn`; each
+// (expert, N-tile, super-block) group holds 256 rows' 16-byte headers, then quant run
+// c = 0..3 of every row as 32 bytes (256 x 144 bytes in all).
+struct Q4kPackLayout {
+    size_t up, dn, total;
+    int ntu, ntd;
+};
+Q4kPackLayout q4k_pack_layout(const moe_layer& L);
+hipError_t launch_q4k_pack(const moe_layer& L, void* dst, hipStream_t s);
 // Grouped up + down.  ksplit > 1: the down projection cuts each tile's K axis into that
 // many slices, summing them through `partial` (fp32, ksplit * rows * d floats).
 hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const int32_t* perm_token,

@@ -108,6 +108,8 @@ moe_status check_layer(const moe_layer* L) {
         L->expert_format != MOE_EXPERTS_Q4K)
         return MOE_ERR_ARG;
     if (L->reserved0 != 0) return MOE_ERR_ARG;
+    if (L->grouped_pack && L->expert_format == MOE_EXPERTS_DENSE) return MOE_ERR_ARG;
+    if (!aligned(L->grouped_pack, 16)) return MOE_ERR_UNSUPPORTED;
     if (L->expert_format == MOE_EXPERTS_MXFP4) {
         if (!L->w_gate_up_scales || !L->w_down_scales) return MOE_ERR_ARG;
         if (L->dtype != MOE_BF16 || L->act != MOE_ACT_SWIGLU_OAI || L->shared_ff != 0 || !mx_fits(*L))
@@ -310,7 +312,7 @@ using namespace smoe;
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 3; }
+int32_t moe_abi_version(void) { return 4; }
 
 const char* moe_status_string(moe_status s) {
     switch (s) {
@@ -321,6 +323,27 @@ const char* moe_status_string(moe_status s) {
         case MOE_ERR_DEVICE: return "HIP launch failed";
         default: return "unknown status";
     }
+}
+
+moe_status moe_grouped_pack_size(const moe_layer* L, size_t* bytes) {
+    const moe_status st = check_layer(L);
+    if (st != MOE_OK) return st;
+    if (!bytes) return MOE_ERR_ARG;
+    if (L->expert_format == MOE_EXPERTS_MXFP4) *bytes = mx_pack_layout(*L).total;
+    else if (L->expert_format == MOE_EXPERTS_Q4K) *bytes = q4k_pack_layout(*L).total;
+    else return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status moe_grouped_pack(const moe_layer* L, void* dst, size_t bytes, void* stream) {
+    size_t need = 0;
+    const moe_status st = moe_grouped_pack_size(L, &need);
+    if (st != MOE_OK) return st;
+    if (!dst) return MOE_ERR_ARG;
+    if (!aligned(dst, 16)) return MOE_ERR_UNSUPPORTED;
+    if (bytes < need) return MOE_ERR_WORKSPACE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    return status_of(L->expert_format == MOE_EXPERTS_MXFP4 ? launch_mx_pack(*L, dst, s) : launch_q4k_pack(*L, dst, s));
 }
 
 moe_status moe_workspace_size(const moe_layer* L, int32_t T, size_t* bytes) {

@@ -41,15 +41,16 @@ class MoeLayer(ctypes.Structure):
         ("w_gate_up", _P), ("b_gate_up", _P), ("w_down", _P), ("b_down", _P),
         ("ws_gate", _P), ("ws_up", _P), ("ws_down", _P), ("ws_gate_inp", _P),
         ("expert_format", ctypes.c_int32), ("reserved0", ctypes.c_int32),
-        ("w_gate_up_scales", _P), ("w_down_scales", _P),
+        ("w_gate_up_scales", _P), ("w_down_scales", _P), ("grouped_pack", _P),
     ]
 
 
 POINTER_FIELDS = [f for f, t in MoeLayer._fields_ if t is _P]
-ABI_VERSION = 3
+ABI_VERSION = 4
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_forward_shell", "moe_forward_noalloc"]
+           "moe_forward", "moe_forward_shell", "moe_forward_noalloc", "moe_grouped_pack_size",
+           "moe_grouped_pack"]
 # Bytes of the library's fixed scratch array behind moe_forward_noalloc.
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -95,6 +96,10 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_shell.argtypes = [pl, vp, i32, vp, ctypes.c_float, vp, vp, sz, vp]
         L.moe_forward_noalloc.restype = i32
         L.moe_forward_noalloc.argtypes = [pl, vp, i32, vp, vp]
+        L.moe_grouped_pack_size.restype = i32
+        L.moe_grouped_pack_size.argtypes = [pl, ctypes.POINTER(sz)]
+        L.moe_grouped_pack.restype = i32
+        L.moe_grouped_pack.argtypes = [pl, vp, sz, vp]
         if L.moe_abi_version() != ABI_VERSION:
             raise RuntimeError("libsmoe.so ABI version mismatch")
         _lib = L
@@ -192,6 +197,23 @@ class Layer:
                    L["act"], L.get("route_scale", 1.0), L.get("oai_alpha", 1.702),
                    L.get("oai_limit", 7.0), path=path, expert_format=L.get("expert_format", "dense"),
                    **tensors)
+
+    def with_grouped_pack(self) -> "Layer":
+        """A copy of this MXFP4 or Q4_K layer whose grouped kernels read the grouped copy of the
+        expert weights (moe_grouped_pack), written now on the current stream into a new
+        device buffer that the returned layer holds."""
+        torch = _torch()
+        n = ctypes.c_size_t(0)
+        _check(lib().moe_grouped_pack_size(self.ref(), ctypes.byref(n)), "moe_grouped_pack_size")
+        dev = self.tensors["w_down"].device
+        buf = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+        _check(lib().moe_grouped_pack(self.ref(), _ptr(buf), n.value, _stream()), "moe_grouped_pack")
+        other = Layer.__new__(Layer)
+        other.__dict__.update(self.__dict__)
+        other.tensors = dict(self.tensors, grouped_pack=buf)
+        other.struct = MoeLayer.from_buffer_copy(self.struct)
+        other.struct.grouped_pack = _ptr(buf)
+        return other
 
     def with_path(self, path: str) -> "Layer":
         other = Layer.__new__(Layer)

@@ -46,7 +46,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     assert sorted(moe.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -59,7 +59,8 @@ def test_struct_layout(lib):
     assert moe.MoeLayer.expert_format.offset == 144
     assert moe.MoeLayer.w_gate_up_scales.offset == 152
     assert moe.MoeLayer.w_down_scales.offset == 160
-    assert ctypes.sizeof(moe.MoeLayer) == 168
+    assert moe.MoeLayer.grouped_pack.offset == 168
+    assert ctypes.sizeof(moe.MoeLayer) == 176
 
 
 def fake_layer(**kw):
@@ -219,6 +220,45 @@ def test_mxfp4_layer_checks(lib):
     assert ws_size(lib, fake_layer(**dict(mx, d=8192)), 4)[0] == moe.MOE_ERR_UNSUPPORTED  # K > 4096
     sh = dict(mx, shared_ff=64, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, ws_gate_inp=FAKE)
     assert ws_size(lib, fake_layer(**sh), 4)[0] == moe.MOE_ERR_UNSUPPORTED
+
+
+def pack_size(lib, s):
+    n = ctypes.c_size_t(0)
+    return lib.moe_grouped_pack_size(ctypes.byref(s), ctypes.byref(n)), n.value
+
+
+def test_grouped_pack_checks(lib):
+    # The grouped copy exists for MXFP4 and Q4_K layers only; its size follows the tile counts
+    # (up: ceil(ff/128) N-tiles x d/64 slices x 512 blocks of 17 bytes; down: ceil(d/256)
+    # x ff/32 x 256), each region rounded up to 256 bytes.
+    mx = dict(expert_format=moe.MOE_EXPERTS_MXFP4, act=moe.MOE_ACT_SWIGLU_OAI, w_gate_up=FAKE,
+              b_gate_up=FAKE, w_gate_up_scales=FAKE * 5, w_down_scales=FAKE * 6)
+    s = fake_layer(**mx)
+    st, n = pack_size(lib, s)
+    E, d, ff = 8, 256, 512
+    up = E * ((ff + 127) // 128) * (d // 64) * 512
+    dn = E * ((d + 255) // 256) * (ff // 32) * 256
+    r256 = lambda b: (b + 255) // 256 * 256
+    assert st == moe.MOE_OK and n == r256(16 * up) + r256(up) + r256(16 * dn) + r256(dn)
+    assert pack_size(lib, fake_layer())[0] == moe.MOE_ERR_UNSUPPORTED          # dense experts
+    assert lib.moe_grouped_pack(ctypes.byref(fake_layer()), FAKE * 7, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_grouped_pack(ctypes.byref(s), None, 1 << 40, None) == moe.MOE_ERR_ARG
+    assert lib.moe_grouped_pack(ctypes.byref(s), FAKE * 7 + 4, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_grouped_pack(ctypes.byref(s), FAKE * 7, n - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_grouped_pack(None, FAKE * 7, n, None) == moe.MOE_ERR_ARG
+    # The field: MXFP4 only, 16-byte aligned.
+    assert ws_size(lib, fake_layer(**dict(mx, grouped_pack=FAKE * 7)), 4)[0] == moe.MOE_OK
+    assert ws_size(lib, fake_layer(**dict(mx, grouped_pack=FAKE * 7 + 8)), 4)[0] == moe.MOE_ERR_UNSUPPORTED
+    assert ws_size(lib, fake_layer(grouped_pack=FAKE * 7), 4)[0] == moe.MOE_ERR_ARG
+    assert fwd(lib, fake_layer(grouped_pack=FAKE * 7)) == moe.MOE_ERR_ARG
+    # Q4_K: per (expert, N-tile, super-block) 256 rows of 144 bytes; up tiles of 128 units
+    # over d/256 super-blocks, down tiles of 256 rows over ff/256.
+    q4 = fake_layer(expert_format=moe.MOE_EXPERTS_Q4K, d=512, ff=256)
+    st, n = pack_size(lib, q4)
+    up = 8 * 2 * 2 * 256 * 144
+    assert st == moe.MOE_OK and n == r256(up) + 8 * 2 * 1 * 256 * 144
+    assert ws_size(lib, fake_layer(expert_format=moe.MOE_EXPERTS_Q4K, d=512, ff=256, grouped_pack=FAKE * 7),
+                   4)[0] == moe.MOE_OK
 
 
 def test_swiglu_rejects_expert_biases(lib):

@@ -667,6 +667,79 @@ def test_mxfp4_grouped_expert_ffn_rows():
     assert_close(to_numpy_y(yp), oracle.expert_rows(L, x, roff, rpt), "bf16", "rows")
 
 
+def mx_pack_expected(L):
+    """The grouped copy of an MXFP4 layer's expert weights, built with numpy from the
+    checkpoint arrays: regions [up codes | up scales | down codes | down scales], each
+    256-byte aligned.  Up piece ((e * NTu + nt) * Su + s) * 512 + t is block 2s + t % 2 of
+    gate_up row 2f (t / 2 < 128) or 2f + 1 (else), f = min(nt * 128 + (t / 2) % 128, ff - 1);
+    down piece ((e * NTd + nt) * Sd + s) * 256 + r is block s of W_d row min(nt * 256 + r,
+    d - 1).  Returns [(offset, bytes)] per region."""
+    E, d, ff = L["n_expert"], L["d"], L["ff"]
+    ntu, su, ntd, sdn = -(-ff // 128), d // 64, -(-d // 256), ff // 32
+    t = np.arange(512)
+    r = t // 2
+    f = np.minimum(np.arange(ntu)[:, None] * 128 + (r % 128)[None, :], ff - 1)
+    R = 2 * f + (r >= 128)[None, :]                                   # [ntu, 512]
+    blk = 2 * np.arange(su)[:, None] + (t % 2)[None, :]               # [su, 512]
+    up_c = L["w_gate_up"][:, R[:, None, :], blk[None, :, :]]          # [E, ntu, su, 512, 16]
+    up_s = L["w_gate_up_scales"][:, R[:, None, :], blk[None, :, :]]   # [E, ntu, su, 512]
+    n = np.minimum(np.arange(ntd)[:, None] * 256 + np.arange(256)[None, :], d - 1)  # [ntd, 256]
+    sl = np.arange(sdn)
+    dn_c = L["w_down"][:, n[:, None, :], sl[None, :, None]]           # [E, ntd, sdn, 256, 16]
+    dn_s = L["w_down_scales"][:, n[:, None, :], sl[None, :, None]]    # [E, ntd, sdn, 256]
+    out, off = [], 0
+    for a in (up_c, up_s, dn_c, dn_s):
+        b = np.ascontiguousarray(a, dtype=np.uint8).reshape(-1)
+        out.append((off, b))
+        off += -(-b.size // 256) * 256
+    assert up_c.shape == (E, ntu, su, 512, 16) and dn_c.shape == (E, ntd, sdn, 256, 16)
+    return out, off
+
+
+@pytest.mark.parametrize("ov", MX_SMALL, ids=["d320", "d4096"])
+def test_mxfp4_grouped_pack_layout(ov):
+    # moe_grouped_pack writes, byte for byte, the layout described above (partial N-tiles
+    # of both GEMMs included: ff = 192 leaves half an up tile, d = 320 a partial down tile).
+    say("mxfp4 grouped pack layout", ov)
+    L, _ = case("gptoss_mx", 1, **ov)
+    lay = dev_layer("gptoss_mx", **ov).with_grouped_pack()
+    torch.cuda.synchronize()
+    got = lay.tensors["grouped_pack"].cpu().numpy()
+    regions, total = mx_pack_expected(L)
+    assert got.size == total
+    for off, want in regions:
+        assert np.array_equal(got[off:off + want.size], want), off
+
+
+@pytest.mark.parametrize("T", [7, 100, 300])
+@pytest.mark.parametrize("ov", MX_SMALL, ids=["d320", "d4096"])
+def test_mxfp4_grouped_pack_forward(ov, T):
+    # The grouped path on the grouped copy: bit for bit the output of the checkpoint layout
+    # (same codes, scales and sums; T = 7 takes split-K down tiles), and within tolerance of
+    # the oracle.
+    say("mxfp4 grouped forward, grouped copy", ov, T)
+    L, x = case("gptoss_mx", T, **ov)
+    lay = dev_layer("gptoss_mx", **ov).with_path("grouped")
+    y0 = moe_mod().forward(lay, xdev(x))
+    y1 = moe_mod().forward(lay.with_grouped_pack(), xdev(x))
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert_close(to_numpy_y(y1), oracle.moe_forward(L, x), "bf16", "y")
+
+
+def test_mxfp4_full_grouped_pack():
+    # The full gpt-oss-shaped MXFP4 layer at 4096 tokens as the benchmark runs it (grouped
+    # copy), on a seeded sample of tokens.
+    T, sample = 4096, 128
+    say("full gptoss_mx grouped copy", T)
+    L, x = case("gptoss_mx", T)
+    lay = dev_layer("gptoss_mx").with_grouped_pack()
+    y = to_numpy_y(moe_mod().forward(lay, xdev(x)))
+    tok = np.sort(np.random.default_rng(11).choice(T, sample, replace=False))
+    e = assert_close(y[tok], oracle.moe_forward(L, x[tok]), "bf16", "y")
+    say(f"  rel err {e:.2e}")
+
+
 # ----------------------------------------------------------------------------- Q4_K experts
 
 # Rows of 8, 12 (a ragged lane group of 16) and 64 quant runs per lane group on the up
@@ -734,3 +807,74 @@ def test_q4k_shell():
         torch.cuda.synchronize()
         ref = oracle.moe_shell(L, h, w, EPS)
         assert_shell_close(to_numpy_y(out), ref, oracle.widen(h), "bf16", f"q4k shell T={T}")
+
+
+def q4k_pack_expected(L):
+    """The grouped copy of a Q4_K layer's routed experts, built with numpy from the
+    checkpoint super-blocks: up region then down region (256-byte aligned).  Group
+    (e, nt, sb) of 256 tile rows: the rows' 16-byte headers, then quant run c = 0..3 of each
+    row as 32 bytes.  Up tile row r: gate unit min(nt * 128 + r, ff - 1) for r < 128, else
+    the up unit min(nt * 128 + r - 128, ff - 1); down tile row r: W_d row min(nt * 256 + r,
+    d - 1).  Returns [(offset, bytes)] and the total size."""
+    E, d, ff = L["n_expert"], L["d"], L["ff"]
+
+    def groups(mats, tile_rows, n_rows, n_tiles):
+        r = np.arange(256)
+        half = len(mats) == 2
+        local = r % 128 if half else r
+        n = np.minimum(np.arange(n_tiles)[:, None] * tile_rows + local[None, :], n_rows - 1)  # [nt, 256]
+        blocks = [m.reshape(E, n_rows, -1, 144) for m in mats]
+        out = np.empty((E, n_tiles, blocks[0].shape[2], 256, 144), np.uint8)
+        for t in range(n_tiles):
+            for rr in range(256):
+                src = blocks[1] if half and rr >= 128 else blocks[0]
+                out[:, t, :, rr, :] = src[:, n[t, rr], :, :]
+        head = out[..., :16].reshape(out.shape[:3] + (-1,))                        # 256 x 16 B
+        runs = out[..., 16:].reshape(out.shape[:4] + (4, 32)).transpose(0, 1, 2, 4, 3, 5)
+        return np.concatenate([head, runs.reshape(out.shape[:3] + (-1,))], axis=3).reshape(-1)
+
+    up = groups([L["w_gate"], L["w_up"]], 128, ff, -(-ff // 128))
+    dn = groups([L["w_down"]], 256, d, -(-d // 256))
+    off_dn = -(-up.size // 256) * 256
+    return [(0, up), (off_dn, dn)], off_dn + dn.size
+
+
+@pytest.mark.parametrize("ov", Q4K_SMALL[:3], ids=Q4K_IDS[:3])
+def test_q4k_grouped_pack_layout(ov):
+    say("q4k grouped pack layout", ov)
+    L, _ = case("qwen_q4k", 1, **ov)
+    lay = dev_layer("qwen_q4k", **ov).with_grouped_pack()
+    torch.cuda.synchronize()
+    got = lay.tensors["grouped_pack"].cpu().numpy()
+    regions, total = q4k_pack_expected(L)
+    assert got.size == total
+    for off, want in regions:
+        assert np.array_equal(got[off:off + want.size], want), off
+
+
+@pytest.mark.parametrize("T", [7, 100, 300])
+@pytest.mark.parametrize("ov", Q4K_SMALL, ids=Q4K_IDS)
+def test_q4k_grouped_pack_forward(ov, T):
+    # The grouped path on the grouped copy: bit for bit the output of the checkpoint layout
+    # (T = 7 takes split-K down tiles), and within tolerance of the oracle.
+    say("q4k grouped forward, grouped copy", ov, T)
+    L, x = case("qwen_q4k", T, **ov)
+    lay = dev_layer("qwen_q4k", **ov).with_path("grouped")
+    y0 = moe_mod().forward(lay, xdev(x))
+    y1 = moe_mod().forward(lay.with_grouped_pack(), xdev(x))
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert_close(to_numpy_y(y1), oracle.moe_forward(L, x), "bf16", "y")
+
+
+def test_q4k_full_grouped_pack():
+    # The full Qwen-shaped Q4_K layer at 2048 tokens with the grouped copy, on a seeded
+    # sample of tokens.
+    T, sample = 2048, 128
+    say("full qwen_q4k grouped copy", T)
+    L, x = case("qwen_q4k", T)
+    lay = dev_layer("qwen_q4k").with_grouped_pack()
+    y = to_numpy_y(moe_mod().forward(lay, xdev(x)))
+    tok = np.sort(np.random.default_rng(11).choice(T, sample, replace=False))
+    e = assert_close(y[tok], oracle.moe_forward(L, x[tok]), "bf16", "y")
+    say(f"  rel err {e:.2e}")
