@@ -429,66 +429,75 @@ struct MxSrc {
     __device__ __forceinline__ void store(GSmem<KW>& sm, int stage, const Regs& r) const { mx_store<KW>(sm, stage, r); }
 };
 
-// Q4_K weights (layout in q4k_dev.h).  Half h of a row takes 16 quant bytes and the
-// super-block's 16-byte header per slice.  A 64-wide slice is one quant run c: its bytes
-// 16h .. 16h+15, whose low nibbles are inputs 16h .. of the slice (sub-block 2c) and high
-// nibbles inputs 32 + 16h .. (sub-block 2c + 1).  A 32-wide slice is one sub-block j: its
-// weights 16h .. 16h+15, i.e. bytes 16h .. of run j / 2, nibble j & 1.  `kbase` is the
-// absolute input index of the call's K = 0 (split-K slices start inside a super-block).
-// Checkpoint layout: each thread's row is a run of 144-byte super-blocks, so the threads
-// of a wave read 32 rows, a line or two per row for 32 bytes of it.  Grouped copy
-// (q4k_pack_layout): per tile and super-block, the 256 tile rows' headers (16 bytes each)
-// and then the four runs, each as 256 rows of 32 bytes, so a wave reads whole lines.
+// Q4_K weights (layout in q4k_dev.h).  A 64-wide slice is one quant run c (two
+// sub-blocks): half h of a row takes sub-block 2c + h, i.e. nibble h of all 32 run bytes.
+// A 32-wide slice is one sub-block j: half h takes its weights 16h .. 16h+15, i.e. bytes
+// 16h .. of run j / 2, nibble j & 1.  Either way the super-block's 16-byte header comes
+// along.  `kbase` is the absolute input index of the call's K = 0 (split-K slices start
+// inside a super-block).  Checkpoint layout: each thread's row is a run of 144-byte
+// super-blocks, so the threads of a wave read 32 rows, a line or two per row for 48 bytes
+// of it.  Grouped copy (q4k_pack_layout): per tile and super-block, the 256 tile rows'
+// headers (16 bytes each) and then the four runs, each as 256 rows of 32 bytes, so a wave
+// reads whole lines.
 template <int KW>
 struct Q4kRegs {
     u32x4 head;
-    u32x4 q;
-    int j;  // sub-block of the low nibbles (64-wide) or of the slice (32-wide)
+    u32x4 q[KW == 64 ? 2 : 1];
+    int j;  // sub-block whose scale and min apply
 };
 
+// Addresses: the header of super-block sb at head0 + sb * hs, quant run c of it at that
+// header + qoff + c * cs.  Checkpoint: head0 = the thread's row, hs = 144, qoff = 16,
+// cs = 32.  Grouped copy: head0 = the tile's first group + row * 16, hs = 256 * 144,
+// qoff = 256 * 16 + row * 16 (the run rows follow the 256 headers), cs = 256 * 32.  A
+// 32-wide slice adds 16h to qoff (its half of the run).
 template <int KW>
 struct Q4kSrc {
-    const uint8_t* base;  // checkpoint: this thread's B row; grouped copy: the tile's first group
+    const uint8_t* head0;
+    int qoff, hs, cs;
     int kbase;
-    bool packed;
     using Regs = Q4kRegs<KW>;
-    static constexpr int kLoads = 2;
+    static constexpr int kLoads = KW == 64 ? 3 : 2;
     static_assert(KW == 64 || KW == 32, "Q4_K slices are one run or one sub-block wide");
+    __device__ __forceinline__ static Q4kSrc make(const uint8_t* tile_or_row, bool packed, int kbase) {
+        const int row = threadIdx.x >> 1, half = KW == 32 ? 16 * (threadIdx.x & 1) : 0;
+        if (packed)
+            return Q4kSrc{tile_or_row + row * 16, (kGThreads / 2) * 16 + row * 16 + half, (kGThreads / 2) * kQ4kBlockBytes,
+                          (kGThreads / 2) * 32, kbase};
+        return Q4kSrc{tile_or_row, 16 + half, kQ4kBlockBytes, 32, kbase};
+    }
     __device__ __forceinline__ void load(int k0, Regs& r) const {
-        const int k = kbase + k0, h = threadIdx.x & 1, row = threadIdx.x >> 1;
-        const int j = (k % kQ4kBlockWeights) / 32, c = j / 2;
-        const size_t sb = (size_t)(k / kQ4kBlockWeights);
-        const uint8_t *head, *quant;
-        if (packed) {
-            const uint8_t* grp = base + sb * (kGThreads / 2) * kQ4kBlockBytes;
-            head = grp + row * 16;
-            quant = grp + (kGThreads / 2) * 16 + (size_t)c * (kGThreads / 2) * 32 + row * 32 + 16 * h;
-        } else {
-            head = base + sb * kQ4kBlockBytes;
-            quant = head + 16 + 32 * c + 16 * h;
-        }
+        const int k = kbase + k0, h = threadIdx.x & 1;
+        const int j = (k % kQ4kBlockWeights) / 32;
+        const uint8_t* head = head0 + (size_t)(k / kQ4kBlockWeights) * hs;
+        const uint8_t* run = head + qoff + (j / 2) * cs;
         vload16(r.head, head);
-        vload16(r.q, quant);
-        r.j = j;
+        if constexpr (KW == 64) {
+            vload16(r.q[0], run);
+            vload16(r.q[1], run + 16);
+            r.j = j + h;
+        } else {
+            vload16(r.q[0], run);
+            r.j = j;
+        }
     }
     template <int N>
-    __device__ __forceinline__ void ready(Regs& r) const { reg_wait<N>(r.head, r.q); }
+    __device__ __forceinline__ void ready(Regs& r) const {
+        if constexpr (KW == 64) reg_wait<N>(r.head, r.q[0], r.q[1]);
+        else reg_wait<N>(r.head, r.q[0]);
+    }
     __device__ __forceinline__ void store(GSmem<KW>& sm, int stage, const Regs& r) const {
         const int row_l = threadIdx.x >> 1, h = threadIdx.x & 1;
-        const uint4 head = make_uint4(r.head[0], r.head[1], r.head[2], r.head[3]);
         float a, b;
+        const uint4 head = make_uint4(r.head[0], r.head[1], r.head[2], r.head[3]);
         q4k_sub_scale(head, r.j, a, b);
-        if constexpr (KW == 64) {
-            float a1, b1;
-            q4k_sub_scale(head, r.j + 1, a1, b1);
-            lds_write16(&sm.k.b[stage][swz<KW>(row_l, 2 * h)], q4k_dequant8(r.q[0], r.q[1], 0, a, b));
-            lds_write16(&sm.k.b[stage][swz<KW>(row_l, 2 * h + 1)], q4k_dequant8(r.q[2], r.q[3], 0, a, b));
-            lds_write16(&sm.k.b[stage][swz<KW>(row_l, 4 + 2 * h)], q4k_dequant8(r.q[0], r.q[1], 4, a1, b1));
-            lds_write16(&sm.k.b[stage][swz<KW>(row_l, 5 + 2 * h)], q4k_dequant8(r.q[2], r.q[3], 4, a1, b1));
-        } else {
-            const int shift = 4 * (r.j & 1);
-            lds_write16(&sm.k.b[stage][swz<KW>(row_l, 2 * h)], q4k_dequant8(r.q[0], r.q[1], shift, a, b));
-            lds_write16(&sm.k.b[stage][swz<KW>(row_l, 2 * h + 1)], q4k_dequant8(r.q[2], r.q[3], shift, a, b));
+        const int shift = 4 * (r.j & 1);
+        constexpr int NC = KW / 16;  // 16-byte LDS chunks per thread
+#pragma unroll
+        for (int q = 0; q < NC; ++q) {
+            const u32x4& v = r.q[q / 2];
+            const uint32_t w0 = (q & 1) ? v[2] : v[0], w1 = (q & 1) ? v[3] : v[1];
+            lds_write16(&sm.k.b[stage][swz<KW>(row_l, h * NC + q)], q4k_dequant8(w0, w1, shift, a, b));
         }
     }
 };
@@ -728,7 +737,7 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kerne
                 const int f = min(f0 + (r & 127), ffg - 1);
                 base = (r >= 128 ? a.q4_up : a.q4_gate) + ((size_t)g.e * a.ff + f) * nsb * kQ4kBlockBytes;
             }
-            const Q4kSrc<kUpKW> src{base, 0, a.q4_packed != 0};
+            const Q4kSrc<kUpKW> src = Q4kSrc<kUpKW>::make(base, a.q4_packed != 0, 0);
             regb_live<kUpKW>(sm, plan, src, a.d, up_live(g, m0, wm), wm * 64, brow, acc);
         } else {
             const LoadPlan<kUpKW> plan = make_plan<kUpKW, false>(row_a, row_b);
@@ -846,7 +855,7 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
                 const int n = min(n0 + (int)(threadIdx.x >> 1), a.d - 1);
                 base = a.q4_down + ((size_t)g.e * a.d + n) * nsb * kQ4kBlockBytes;
             }
-            const Q4kSrc<kDownKW> src{base, kb, a.mx_packed != 0};
+            const Q4kSrc<kDownKW> src = Q4kSrc<kDownKW>::make(base, a.mx_packed != 0, kb);
             down_regb<TY>(sm, plan, src, K, up_live(g, m0, wm), wm * 64, brow, acc);
         } else {  // the plain loop: the second set of B registers would cost this kernel occupancy
             const LoadPlan<kDownKW> plan = make_plan<kDownKW, false>(row_a, row_b);

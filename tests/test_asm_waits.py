@@ -165,3 +165,10 @@ def test_grouped_kernels_keep_pending_registers_untouched(tmp_path):
         assert bad == [], f"{name}: pending registers touched: {bad[:5]}"
     # The MXFP4 and Q4_K variants of the up and down kernels use the untracked loads.
     assert total_loads >= 8
+    # Two down blocks of 512 threads share a CU only at 128 VGPRs or fewer (512 per SIMD
+    # lane, four waves per SIMD): one register more halves the kernel's occupancy.
+    text = out.read_text()
+    for m in re.finditer(r"\.amdhsa_kernel (\S*gg_down_kernel\S*)", text):
+        vgpr = int(re.search(r"\.amdhsa_next_free_vgpr\s+(\d+)", text[m.start():m.start() + 5000]).group(1))
+        assert vgpr <= 128, f"{m.group(1)}: {vgpr} VGPRs"
+        assert ".amdhsa_private_segment_fixed_size 0" in text[m.start():m.start() + 5000], m.group(1)
