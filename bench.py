@@ -150,8 +150,8 @@ def summarize_pmc(fetch_csv, write_csv, workload, out_path, command, forwards):
     kernels = sorted(set(per["FETCH_SIZE"][0]) | set(per["WRITE_SIZE"][0]))
     rows, total = [], 0.0
     for n in kernels:
-        if "rocclr" in n or "rocprim" in n or "at::" in n or "elementwise" in n.lower():
-            continue  # runtime copies and torch's own kernels (input set-up), not the layer
+        if not _is_library_kernel(n) or "elementwise" in n.lower():
+            continue  # runtime copies, torch's own kernels, load-time packing: not the layer
         f = per["FETCH_SIZE"][0].get(n, [])
         w = per["WRITE_SIZE"][0].get(n, [])
         fb = (sum(f) * 1024.0 / per["FETCH_SIZE"][1]) if f else 0.0
@@ -180,7 +180,10 @@ def summarize_pmc(fetch_csv, write_csv, workload, out_path, command, forwards):
 
 
 def _is_library_kernel(name):
-    return not any(t in name for t in ("rocclr", "rocprim", "at::", "elementwise", "Functor"))
+    """A kernel of the forward: not the runtime's copies, not torch's own kernels (input
+    set-up), and not the kernels that write the grouped copy of MXFP4 / Q4_K weights
+    (moe_grouped_pack, once per layer at load time)."""
+    return not any(t in name for t in ("rocclr", "rocprim", "at::", "elementwise", "Functor", "_pack_"))
 
 
 def workload_title(workload):
@@ -232,7 +235,8 @@ def summarize_stats(csv_path, log_path, workload, out_path, command, bench_json=
     lines += ["```", "",
               f"{forwards} forwards (warm-up + timed) of `moe_forward`; every library kernel of the run "
               "belongs to one of them, so its time per forward is its total over the run / "
-              f"{forwards}.  Set-up copies and torch kernels are left out.", "",
+              f"{forwards}.  Set-up copies, torch kernels and the load-time packing of MXFP4 / "
+              "Q4_K weights (moe_grouped_pack) are left out.", "",
               "| kernel | calls | avg us | min us | max us | us per forward |", "|---|---|---|---|---|---|"]
     for n, c, a, mn, mx, pf in rows:
         lines.append(f"| `{n[:90]}` | {c} | {a:.2f} | {mn:.2f} | {mx:.2f} | {pf:.2f} |")
