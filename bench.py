@@ -419,9 +419,10 @@ def time_workload(name, steps, warmup, layer_cache, forward_only=False):
         layers.append(moe.Layer(L["d"], L["n_expert"], L["ff"], L["k"], L["shared_ff"], L["dtype"],
                                 L["route"], L["act"], L["route_scale"], L["oai_alpha"],
                                 L["oai_limit"], expert_format=L.get("expert_format", "dense"), **tens))
-    if L.get("expert_format") in ("mxfp4", "q4k"):
-        # MXFP4 and Q4_K layers carry the grouped path's copy of their expert weights,
-        # written once at load time (moe_grouped_pack), as a deployment would.
+    if L["dtype"] == "bf16":
+        # bf16 layers carry the grouped path's copy of their expert weights (MXFP4 / Q4_K
+        # blocks, or dense down weights), written once at load time (moe_grouped_pack), as a
+        # deployment would.
         layers = [lay.with_grouped_pack() for lay in layers]
         lay0 = layers[0]
         torch.cuda.synchronize()

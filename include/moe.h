@@ -137,11 +137,10 @@ typedef struct moe_layer {
     int32_t reserved0;        /* 0                                                     */
     const uint8_t* w_gate_up_scales;  /* MXFP4: [E, 2*ff, d/32] E8M0, else NULL        */
     const uint8_t* w_down_scales;     /* MXFP4: [E, d, ff/32] E8M0, else NULL          */
-    const void* grouped_pack;         /* MXFP4, Q4K: the grouped path's copy of the
-                                         routed experts' weights written by
-                                         moe_grouped_pack, or NULL (the grouped kernels
-                                         then read the blocks above); must be NULL for
-                                         dense experts                                 */
+    const void* grouped_pack;         /* the grouped path's copy of expert weights
+                                         written by moe_grouped_pack, or NULL (the
+                                         grouped kernels then read the fields above);
+                                         bf16 layers only                              */
 } moe_layer;
 
 /* ABI version of this header (bumped on any layout or signature change). */
@@ -232,18 +231,22 @@ moe_status moe_forward_shell(const moe_layer* L, const void* h, int32_t T, const
  * the process ends). */
 #define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
-/* The grouped (MFMA) path's copy of MXFP4 or Q4K routed-expert weights.  Each K-slice
- * of a weight tile that the grouped kernels expand is stored as contiguous runs, in the
- * order the threads of a block read them, so a wave's loads cover whole cache lines; in
- * the checkpoint layouts (rows of 16-byte MXFP4 blocks, "Phase 19: MoE - gpt-oss-20b",
- * section 3; rows of 144-byte Q4_K super-blocks) every thread reads a few bytes of a
- * different row.  Same codes, scales and headers, so results are bit for bit those of the
- * checkpoint layout.  The decode GEMVs keep reading the checkpoint layout, which suits
- * their whole-row reads.
+/* The grouped (MFMA) path's copy of expert weights ("Engine" (Cherenkov), Prefill: the
+ * experts evaluated as tiled GEMMs).  Each K-slice of a weight tile that the grouped
+ * kernels load is stored as contiguous runs, in the order the threads of a block read
+ * them, so a wave's loads cover whole cache lines; in the checkpoint layouts a slice is a
+ * few bytes of every row.  What is copied:
+ *  - MXFP4 and Q4K: the routed experts' gate_up / gate, up and down blocks (rows of
+ *    16-byte MXFP4 blocks, "Phase 19: MoE - gpt-oss-20b", section 3; rows of 144-byte
+ *    Q4_K super-blocks), codes, scales and headers unchanged;
+ *  - dense bf16 experts: the down weights only (routed and shared), whose 32-input slices
+ *    are half a cache line of each row in place; the up weights' 64-input slices already
+ *    cover whole lines and are read in place.
+ * Same values, so results are bit for bit those of the checkpoint layout.  The decode
+ * GEMVs keep reading the checkpoint layout, which suits their whole-row reads.
  * moe_grouped_pack_size writes the copy's size to *bytes (host): about the size of the
- * routed experts' gate/up and down weights in their format.  Errors: MOE_ERR_ARG /
- * MOE_ERR_UNSUPPORTED as for moe_forward; MOE_ERR_UNSUPPORTED for dense experts (they
- * have no grouped copy).
+ * copied weights.  Errors: MOE_ERR_ARG / MOE_ERR_UNSUPPORTED as for moe_forward;
+ * MOE_ERR_UNSUPPORTED for fp32 layers (they have no grouped path).
  * moe_grouped_pack enqueues on `stream` the kernels that write the copy to `dst` (device,
  * 16-byte aligned, at least that size; it must not overlap the layer's weights).  The
  * caller owns `dst`; store it in moe_layer.grouped_pack for the calls that should use it

@@ -119,9 +119,13 @@ constexpr int blocks_per_cu() { return sizeof(GSmem<KW>) * 2 <= 160 * 1024 ? 2 :
 // Source pointers of this lane's direct loads: A segments w + 8j, B segments w + 8j
 // (segment s holds tile rows s * kRowsPerSeg ..).  row_a / row_b map a tile row to its
 // global row.
+// Slice s of load j starts at src[j] + s * KW * mul (mul_a for the A loads, mul_b for B):
+// mul 1 for row-major operands, the row count for operands stored slice-major (the bf16
+// hidden rows H of the grouped path; the grouped copy of dense W_d).
 template <int KW>
 struct LoadPlan {
     const uint16_t* src[Ring<KW>::kLoads];
+    int mul_a, mul_b;
 };
 
 // A_ONLY: B comes from MXFP4 blocks through registers (mx_load / mx_store), so only the A
@@ -130,6 +134,8 @@ template <int KW, bool A_ONLY = false, typename RowA, typename RowB>
 __device__ __forceinline__ LoadPlan<KW> make_plan(RowA row_a, RowB row_b) {
     using R = Ring<KW>;
     LoadPlan<KW> p;
+    p.mul_a = 1;
+    p.mul_b = 1;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
 #pragma unroll
     for (int j = 0; j < R::kLoads; ++j) {
@@ -160,15 +166,19 @@ __device__ __forceinline__ void issue_stage(uint16_t* a_stage, uint16_t* b_stage
 
 template <int KW>
 __device__ __forceinline__ void issue_slice(GSmem<KW>& sm, const LoadPlan<KW>& p, int stage, int k0) {
-    issue_stage<KW>(sm.k.a[stage], sm.k.b[stage], p.src, k0);
+    const uint16_t* srcs[Ring<KW>::kLoads];
+#pragma unroll
+    for (int j = 0; j < Ring<KW>::kLoads; ++j)
+        srcs[j] = p.src[j] + (size_t)k0 * (j < Ring<KW>::kLoadsA ? p.mul_a : p.mul_b);
+    issue_stage<KW>(sm.k.a[stage], sm.k.b[stage], srcs, 0);
 }
 
 // The A segments of a slice only (B comes through registers): n 1 KB segments of this
 // wave, segment j at dst + (wave + 8 j) * 512 elements, fetched from src[j] + k0.
-__device__ __forceinline__ void issue_a_segments(uint16_t* dst, const uint16_t* const* src, int n, int k0) {
+__device__ __forceinline__ void issue_a_segments(uint16_t* dst, const uint16_t* const* src, int n, int k0, int mul) {
     const int wave = threadIdx.x / kWave;
     for (int j = 0; j < n; ++j)
-        __builtin_amdgcn_global_load_lds(src[j] + k0, (lds_ptr_t)(dst + (wave + 8 * j) * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src[j] + (size_t)k0 * mul, (lds_ptr_t)(dst + (wave + 8 * j) * 512), 16, 0, 0);
 }
 
 // Fragments of 32 K of one wave's 64 x 64 tile, read from LDS apart from their MFMAs.
@@ -521,9 +531,9 @@ __device__ __forceinline__ void grouped_mainloop_regb(GSmem<KW>& sm, const LoadP
     const int nk = K / KW;
     typename Src::Regs first, nxt;
     src.load(0, first);
-    issue_a_segments(sm.k.a[0], p.src, LA, 0);
+    issue_a_segments(sm.k.a[0], p.src, LA, 0, p.mul_a);
     src.load(min(1, nk - 1) * KW, nxt);
-    issue_a_segments(sm.k.a[1], p.src, LA, min(1, nk - 1) * KW);
+    issue_a_segments(sm.k.a[1], p.src, LA, min(1, nk - 1) * KW, p.mul_a);
     src.template ready<2 * LA + Src::kLoads>(first);
     src.store(sm, 0, first);
     int st = 0;
@@ -543,7 +553,7 @@ __device__ __forceinline__ void grouped_mainloop_regb(GSmem<KW>& sm, const LoadP
         src.store(sm, nx, nxt);                // B of slice kt+1 (clamped re-load on the last step)
         src.load(min(kt + 2, nk - 1) * KW, nxt);
         const int pre = st == 0 ? 2 : st - 1;  // (kt + 2) % 3
-        issue_a_segments(sm.k.a[pre], p.src, LA, min(kt + 2, nk - 1) * KW);
+        issue_a_segments(sm.k.a[pre], p.src, LA, min(kt + 2, nk - 1) * KW, p.mul_a);
         st = nx;
     }
     wait_vm_lgkm<0>();
@@ -570,11 +580,12 @@ struct UpArgs {
     const uint8_t* mx_s;        // ... and scales [E, 2ff, d/32]
     const uint8_t* q4_gate;     // Q4_K gate / up super-blocks [E, ff, d/256, 144], or null
     const uint8_t* q4_up;
-    uint16_t* H;                // bf16 [rows, hstride]
+    uint16_t* H;                // bf16 hidden rows, slice-major: [hstride / 32][h_rows][32]
     int hstride, T, d, ff, ffs, n_ntiles;
     float alpha, limit;
     int mx_packed;              // mx_w / mx_s point into the grouped copy (mx_pack_layout)
     int q4_packed;              // q4_gate points at the grouped copy's up region (q4k_pack_layout)
+    int h_rows;                 // rows of H (T * k, plus T with a shared expert)
 };
 
 struct DownArgs {
@@ -593,6 +604,8 @@ struct DownArgs {
     int hstride, d, ff, ffs, n_ntiles;
     int ksplit, rows;         // K slices per tile (each block sums K / ksplit), grouped rows
     int mx_packed;            // mx_w / mx_s, or q4_down, point into the grouped copy
+    const uint16_t* wd_pack;  // dense bf16: routed W_d in the grouped copy (dense_pack_layout), or null
+    const uint16_t* wsd_pack; // ... and the shared expert's W_d, or null
 };
 
 // XCD-aware tile order.  Workgroups are dispatched to the 8 XCDs round-robin by block
@@ -783,14 +796,17 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kerne
         }
     }
     __syncthreads();
-    // 128 rows x 16 chunks; 512 threads = 32 rows per pass.
+    // 128 rows x 16 chunks; 512 threads = 32 rows per pass.  H is slice-major (32 columns
+    // per slice, the down kernel's K-slice): chunk c goes to slice (f0 + 8c) / 32, so a
+    // wave's 4 rows x 64 bytes per slice are contiguous.
     const int c = threadIdx.x & 15;
+    const int f = f0 + c * 8;
+    uint16_t* hs = a.H + ((size_t)(f / 32) * a.h_rows + g.row0 + m0) * 32 + f % 32;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int ml = (threadIdx.x >> 4) + 32 * p;
-        if (m0 + ml < g.n && f0 + c * 8 < ffg)
-            *reinterpret_cast<uint4*>(a.H + (size_t)(g.row0 + m0 + ml) * a.hstride + f0 + c * 8) =
-                *reinterpret_cast<const uint4*>(sm.up + ml * kUpStage + c * 8);
+        if (m0 + ml < g.n && f < ffg)
+            *reinterpret_cast<uint4*>(hs + (size_t)ml * 32) = *reinterpret_cast<const uint4*>(sm.up + ml * kUpStage + c * 8);
     }
 }
 
@@ -813,8 +829,16 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
     const int K = Kfull / a.ksplit;  // the host picks ksplit so that slices are whole K-steps
     const int kb = ks * K;
     const int n0 = nt * GBN;
-    auto row_a = [&](int r) { return a.H + (size_t)(g.row0 + min(m0 + r, g.n - 1)) * a.hstride + kb; };
+    // H is slice-major: slice s of row m at H + (s * rows + m) * 32; this split starts at slice kb / 32.
+    auto row_a = [&](int r) { return a.H + ((size_t)(kb / kDownKW) * a.rows + g.row0 + min(m0 + r, g.n - 1)) * kDownKW; };
+    // Dense weights in the grouped copy: slice s of N-tile nt is 256 rows x 32 contiguous, so
+    // row r of this split's first slice sits at ((tile * slices + kb / 32) * 256 + r) * 32.
+    const uint16_t* wpack = shared ? a.wsd_pack : a.wd_pack;
     auto row_b = [&](int r) {
+        if (wpack) {
+            const size_t tile = shared ? (size_t)nt : (size_t)g.e * a.n_ntiles + nt;
+            return wpack + ((tile * (Kfull / kDownKW) + kb / kDownKW) * GBN + r) * kDownKW;
+        }
         const int n = min(n0 + r, a.d - 1);  // partial last N-tile: re-read
         return (shared ? a.ws_down + (size_t)n * Kfull : a.w_down + ((size_t)g.e * a.d + n) * Kfull) + kb;
     };
@@ -829,7 +853,8 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
     zero(acc);
     if constexpr (WF == kWMx) {
         // This thread's B row (tile row threadIdx.x / 2) of W_d, from this split's first block.
-        const LoadPlan<kDownKW> plan = make_plan<kDownKW, true>(row_a, row_b);
+        LoadPlan<kDownKW> plan = make_plan<kDownKW, true>(row_a, row_b);
+        plan.mul_a = a.rows;
         const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
         MxRow m;
         if (a.mx_packed) {
@@ -846,7 +871,8 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
         down_regb<TY>(sm, plan, src, K, up_live(g, m0, wm), wm * 64, brow, acc);
     } else if constexpr (WF == kWQ4k) {
         if (!shared) {
-            const LoadPlan<kDownKW> plan = make_plan<kDownKW, true>(row_a, row_b);
+            LoadPlan<kDownKW> plan = make_plan<kDownKW, true>(row_a, row_b);
+            plan.mul_a = a.rows;
             const size_t nsb = Kfull / kQ4kBlockWeights;
             const uint8_t* base;
             if (a.mx_packed) {
@@ -858,14 +884,17 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
             const Q4kSrc<kDownKW> src = Q4kSrc<kDownKW>::make(base, a.mx_packed != 0, kb);
             down_regb<TY>(sm, plan, src, K, up_live(g, m0, wm), wm * 64, brow, acc);
         } else {  // the plain loop: the second set of B registers would cost this kernel occupancy
-            const LoadPlan<kDownKW> plan = make_plan<kDownKW, false>(row_a, row_b);
+            LoadPlan<kDownKW> plan = make_plan<kDownKW, false>(row_a, row_b);
+            plan.mul_a = a.rows;
             grouped_mainloop_plain(sm, plan, K, wm * 64, brow, acc);
         }
     } else {
         // As in the up kernel, padding rows past the group's last row run no MFMAs, here by
         // whole 32-row halves of the wave's 64 rows (bf16 rows only: the three instances
         // would take the fp32-row kernel past 128 VGPRs, i.e. to one block per CU).
-        const LoadPlan<kDownKW> plan = make_plan<kDownKW, false>(row_a, row_b);
+        LoadPlan<kDownKW> plan = make_plan<kDownKW, false>(row_a, row_b);
+        plan.mul_a = a.rows;
+        plan.mul_b = wpack ? GBN : 1;
         if constexpr (sizeof(TY) == 2) {
             const int live = up_live(g, m0, wm);
             if (live > 2) grouped_mainloop<kDownKW, 4>(sm, plan, K, wm * 64, brow, acc);
@@ -1169,6 +1198,28 @@ __global__ __launch_bounds__(256) void q4k_pack_kernel(const uint8_t* __restrict
     }
 }
 
+// The grouped copy of dense bf16 down weights (moe_grouped_pack): piece
+// i = ((tile * slices + s) * 256 + r) holds the 32 inputs 32s .. 32s+31 of output row
+// min(nt * 256 + r, d - 1) of the tile's expert, where tile = e * NTd + nt; one thread per
+// piece (64 bytes).
+__global__ __launch_bounds__(256) void dense_down_pack_kernel(const uint16_t* __restrict__ w, int d, int K,
+                                                              long long pieces, int ntd, uint16_t* __restrict__ out) {
+    const int slices = K / kDownKW;
+    for (long long i = blockIdx.x * 256ll + threadIdx.x; i < pieces; i += (long long)gridDim.x * 256) {
+        const int r = (int)(i % GBN);
+        long long rest = i / GBN;
+        const int sl = (int)(rest % slices);
+        rest /= slices;
+        const int nt = (int)(rest % ntd);
+        const long long e = rest / ntd;
+        const int n = min(nt * GBN + r, d - 1);
+        const uint4* src = reinterpret_cast<const uint4*>(w + ((size_t)e * d + n) * K + (size_t)sl * kDownKW);
+        uint4* dst = reinterpret_cast<uint4*>(out + (size_t)i * kDownKW);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = src[q];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_router_mfma(const moe_layer& L, const void* x, int T, float* logits, int ld,
@@ -1214,6 +1265,31 @@ MxPackLayout mx_pack_layout(const moe_layer& L) {
     p.dn_scales = take(E * p.ntd * p.sd * GBN);
     p.total = off;
     return p;
+}
+
+DensePackLayout dense_pack_layout(const moe_layer& L) {
+    DensePackLayout p{};
+    p.ntd = (L.d + GBN - 1) / GBN;
+    const size_t routed = (size_t)L.n_expert * p.ntd * GBN * L.ff * 2;
+    p.dn = 0;
+    p.sh = (routed + 255) / 256 * 256;
+    p.total = p.sh + (size_t)p.ntd * GBN * L.shared_ff * 2;
+    return p;
+}
+
+hipError_t launch_dense_pack(const moe_layer& L, void* dst, hipStream_t s) {
+    const DensePackLayout p = dense_pack_layout(L);
+    uint8_t* base = static_cast<uint8_t*>(dst);
+    auto blocks = [](long long n) { return (unsigned)std::min<long long>((n + 255) / 256, 8192); };
+    const long long routed = (long long)L.n_expert * p.ntd * (L.ff / kDownKW) * GBN;
+    dense_down_pack_kernel<<<blocks(routed), 256, 0, s>>>(static_cast<const uint16_t*>(L.w_down), L.d, L.ff, routed,
+                                                          p.ntd, reinterpret_cast<uint16_t*>(base + p.dn));
+    if (L.shared_ff > 0) {
+        const long long sh = (long long)p.ntd * (L.shared_ff / kDownKW) * GBN;
+        dense_down_pack_kernel<<<blocks(sh), 256, 0, s>>>(static_cast<const uint16_t*>(L.ws_down), L.d, L.shared_ff, sh,
+                                                          p.ntd, reinterpret_cast<uint16_t*>(base + p.sh));
+    }
+    return hipGetLastError();
 }
 
 Q4kPackLayout q4k_pack_layout(const moe_layer& L) {
@@ -1272,7 +1348,12 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
     if (q4 && (L.act != MOE_ACT_SWIGLU || L.d % kQ4kBlockWeights || L.ff % kQ4kBlockWeights))
         return hipErrorInvalidValue;
     // With the grouped copy (MXFP4 or Q4_K), both GEMMs read their weight slices from it.
-    const bool packed = (mx || q4) && L.grouped_pack;
+    const bool packed = L.grouped_pack != nullptr;
+    const DensePackLayout pdn = packed && !mx && !q4 ? dense_pack_layout(L) : DensePackLayout{};
+    const uint16_t* wd_pack = packed && !mx && !q4 ? reinterpret_cast<const uint16_t*>(
+                                                         static_cast<const uint8_t*>(L.grouped_pack) + pdn.dn) : nullptr;
+    const uint16_t* wsd_pack = wd_pack && shared ? reinterpret_cast<const uint16_t*>(
+                                                       static_cast<const uint8_t*>(L.grouped_pack) + pdn.sh) : nullptr;
     const uint8_t* pack = static_cast<const uint8_t*>(L.grouped_pack);
     const Q4kPackLayout pq = q4 && packed ? q4k_pack_layout(L) : Q4kPackLayout{};
     const auto* q4_gate = q4 ? (packed ? pack + pq.up : static_cast<const uint8_t*>(L.w_gate)) : nullptr;
@@ -1292,6 +1373,7 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
         u.mx_packed = 1;
     }
     u.q4_packed = q4 && packed ? 1 : 0;
+    u.h_rows = T * L.k + (shared ? T : 0);
     const dim3 gu((unsigned)grid_blocks(mt, nn_up));
     if (mx)
         gg_up_kernel<true, kWMx><<<gu, kGThreads, 0, s>>>(u);
@@ -1315,7 +1397,7 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
             return hipErrorInvalidValue;
         DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down), nullptr,
                     static_cast<const uint16_t*>(L.ws_down), mx_dw, mx_ds, q4_down, nullptr, partial, hstride, L.d,
-                    L.ff, L.shared_ff, nn, ksplit, rows, packed ? 1 : 0};
+                    L.ff, L.shared_ff, nn, ksplit, rows, (mx || q4) && packed ? 1 : 0, wd_pack, wsd_pack};
         const dim3 gs((unsigned)grid_blocks(mt, nn * ksplit));
         if (wf == kWMx) gg_down_kernel<float, kWMx><<<gs, kGThreads, 0, s>>>(dn);
         else if (wf == kWQ4k) gg_down_kernel<float, kWQ4k><<<gs, kGThreads, 0, s>>>(dn);
@@ -1331,7 +1413,7 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
     }
     DownArgs dn{H, groups, meta, tiles, static_cast<const uint16_t*>(L.w_down), b_down,
                 static_cast<const uint16_t*>(L.ws_down), mx_dw, mx_ds, q4_down, row_w, y, hstride, L.d, L.ff,
-                L.shared_ff, nn, 1, rows, packed ? 1 : 0};
+                L.shared_ff, nn, 1, rows, (mx || q4) && packed ? 1 : 0, wd_pack, wsd_pack};
     const dim3 gd((unsigned)grid_blocks(mt, nn));
 #define SMOE_GG_DOWN(WF)                                                              \
     do {                                                                              \

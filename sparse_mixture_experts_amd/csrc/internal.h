@@ -88,6 +88,15 @@ struct Q4kPackLayout {
 };
 Q4kPackLayout q4k_pack_layout(const moe_layer& L);
 hipError_t launch_q4k_pack(const moe_layer& L, void* dst, hipStream_t s);
+// The grouped copy of dense bf16 down weights: routed W_d at `dn` as [E][NTd][ff/32][256][32]
+// (NTd N-tiles of 256 output rows, 32-input slices; rows past d repeat the last), the
+// shared expert's at `sh` as [NTd][shared_ff/32][256][32].
+struct DensePackLayout {
+    size_t dn, sh, total;
+    int ntd;
+};
+DensePackLayout dense_pack_layout(const moe_layer& L);
+hipError_t launch_dense_pack(const moe_layer& L, void* dst, hipStream_t s);
 // Grouped up + down.  ksplit > 1: the down projection cuts each tile's K axis into that
 // many slices, summing them through `partial` (fp32, ksplit * rows * d floats).
 hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const int32_t* perm_token,

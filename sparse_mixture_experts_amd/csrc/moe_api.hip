@@ -108,7 +108,7 @@ moe_status check_layer(const moe_layer* L) {
         L->expert_format != MOE_EXPERTS_Q4K)
         return MOE_ERR_ARG;
     if (L->reserved0 != 0) return MOE_ERR_ARG;
-    if (L->grouped_pack && L->expert_format == MOE_EXPERTS_DENSE) return MOE_ERR_ARG;
+    if (L->grouped_pack && L->expert_format == MOE_EXPERTS_DENSE && L->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (!aligned(L->grouped_pack, 16)) return MOE_ERR_UNSUPPORTED;
     if (L->expert_format == MOE_EXPERTS_MXFP4) {
         if (!L->w_gate_up_scales || !L->w_down_scales) return MOE_ERR_ARG;
@@ -331,7 +331,8 @@ moe_status moe_grouped_pack_size(const moe_layer* L, size_t* bytes) {
     if (!bytes) return MOE_ERR_ARG;
     if (L->expert_format == MOE_EXPERTS_MXFP4) *bytes = mx_pack_layout(*L).total;
     else if (L->expert_format == MOE_EXPERTS_Q4K) *bytes = q4k_pack_layout(*L).total;
-    else return MOE_ERR_UNSUPPORTED;
+    else if (L->dtype == MOE_BF16) *bytes = dense_pack_layout(*L).total;
+    else return MOE_ERR_UNSUPPORTED;  // fp32 layers never take the grouped path
     return MOE_OK;
 }
 
@@ -343,7 +344,10 @@ moe_status moe_grouped_pack(const moe_layer* L, void* dst, size_t bytes, void* s
     if (!aligned(dst, 16)) return MOE_ERR_UNSUPPORTED;
     if (bytes < need) return MOE_ERR_WORKSPACE;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    return status_of(L->expert_format == MOE_EXPERTS_MXFP4 ? launch_mx_pack(*L, dst, s) : launch_q4k_pack(*L, dst, s));
+    const hipError_t e = L->expert_format == MOE_EXPERTS_MXFP4 ? launch_mx_pack(*L, dst, s)
+                         : L->expert_format == MOE_EXPERTS_Q4K ? launch_q4k_pack(*L, dst, s)
+                                                                : launch_dense_pack(*L, dst, s);
+    return status_of(e);
 }
 
 moe_status moe_workspace_size(const moe_layer* L, int32_t T, size_t* bytes) {

@@ -199,7 +199,7 @@ class Layer:
                    **tensors)
 
     def with_grouped_pack(self) -> "Layer":
-        """A copy of this MXFP4 or Q4_K layer whose grouped kernels read the grouped copy of the
+        """A copy of this bf16 layer whose grouped kernels read the grouped copy of the
         expert weights (moe_grouped_pack), written now on the current stream into a new
         device buffer that the returned layer holds."""
         torch = _torch()

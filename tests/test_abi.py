@@ -228,7 +228,7 @@ def pack_size(lib, s):
 
 
 def test_grouped_pack_checks(lib):
-    # The grouped copy exists for MXFP4 and Q4_K layers only; its size follows the tile counts
+    # The grouped copy exists for MXFP4, Q4_K and dense bf16 layers; its size follows the tile counts
     # (up: ceil(ff/128) N-tiles x d/64 slices x 512 blocks of 17 bytes; down: ceil(d/256)
     # x ff/32 x 256), each region rounded up to 256 bytes.
     mx = dict(expert_format=moe.MOE_EXPERTS_MXFP4, act=moe.MOE_ACT_SWIGLU_OAI, w_gate_up=FAKE,
@@ -240,8 +240,9 @@ def test_grouped_pack_checks(lib):
     dn = E * ((d + 255) // 256) * (ff // 32) * 256
     r256 = lambda b: (b + 255) // 256 * 256
     assert st == moe.MOE_OK and n == r256(16 * up) + r256(up) + r256(16 * dn) + r256(dn)
-    assert pack_size(lib, fake_layer())[0] == moe.MOE_ERR_UNSUPPORTED          # dense experts
-    assert lib.moe_grouped_pack(ctypes.byref(fake_layer()), FAKE * 7, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    f32 = fake_layer(dtype=moe.MOE_F32)                                # no grouped path in fp32
+    assert pack_size(lib, f32)[0] == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_grouped_pack(ctypes.byref(f32), FAKE * 7, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_grouped_pack(ctypes.byref(s), None, 1 << 40, None) == moe.MOE_ERR_ARG
     assert lib.moe_grouped_pack(ctypes.byref(s), FAKE * 7 + 4, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_grouped_pack(ctypes.byref(s), FAKE * 7, n - 1, None) == moe.MOE_ERR_WORKSPACE
@@ -249,8 +250,14 @@ def test_grouped_pack_checks(lib):
     # The field: MXFP4 only, 16-byte aligned.
     assert ws_size(lib, fake_layer(**dict(mx, grouped_pack=FAKE * 7)), 4)[0] == moe.MOE_OK
     assert ws_size(lib, fake_layer(**dict(mx, grouped_pack=FAKE * 7 + 8)), 4)[0] == moe.MOE_ERR_UNSUPPORTED
-    assert ws_size(lib, fake_layer(grouped_pack=FAKE * 7), 4)[0] == moe.MOE_ERR_ARG
-    assert fwd(lib, fake_layer(grouped_pack=FAKE * 7)) == moe.MOE_ERR_ARG
+    assert ws_size(lib, fake_layer(dtype=moe.MOE_F32, grouped_pack=FAKE * 7), 4)[0] == moe.MOE_ERR_UNSUPPORTED
+    assert fwd(lib, fake_layer(dtype=moe.MOE_F32, grouped_pack=FAKE * 7)) == moe.MOE_ERR_UNSUPPORTED
+    # Dense bf16: the down weights only, routed [E][ceil(d/256)][ff/32][256][32] bf16, then the
+    # shared expert's [ceil(d/256)][shared_ff/32][256][32].
+    assert pack_size(lib, fake_layer()) == (moe.MOE_OK, 8 * 1 * 256 * 512 * 2)
+    sh = fake_layer(d=320, shared_ff=128, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, ws_gate_inp=FAKE)
+    assert pack_size(lib, sh) == (moe.MOE_OK, r256(8 * 2 * 256 * 512 * 2) + 2 * 256 * 128 * 2)
+    assert ws_size(lib, fake_layer(grouped_pack=FAKE * 7), 4)[0] == moe.MOE_OK
     # Q4_K: per (expert, N-tile, super-block) 256 rows of 144 bytes; up tiles of 128 units
     # over d/256 super-blocks, down tiles of 256 rows over ff/256.
     q4 = fake_layer(expert_format=moe.MOE_EXPERTS_Q4K, d=512, ff=256)

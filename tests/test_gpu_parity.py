@@ -435,6 +435,10 @@ def test_full_qwen_prefill_zipf():
     say("  counts min/median/max", counts.min(), int(np.median(counts)), counts.max())
     e = assert_close(to_numpy_y(y), oracle.moe_forward(L, x), "bf16", "y")
     say(f"  rel err {e:.2e}")
+    # As benchmarked: with the grouped copy of the down weights, bit for bit the same.
+    y_pack = moe_mod().forward(lay.with_grouped_pack(), xdev(x))
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_pack.view(torch.int16))
 
 
 @pytest.mark.parametrize("name,T,sample", [("gptoss", 1, None), ("gptoss", 4096, 256),
@@ -591,6 +595,83 @@ def test_full_qwen_shell(T):
     ref = oracle.moe_shell(L, h, w, EPS)
     e = assert_shell_close(to_numpy_y(out), ref, oracle.widen(h), "bf16", "shell")
     say(f"  block part rel err {e:.2e}")
+
+
+# ----------------------------------------------------------------------------- grouped copy, dense
+
+def dense_pack_expected(L):
+    """The grouped copy of a dense bf16 layer (its down weights), built with numpy: routed
+    W_d as [E][NTd][ff/32][256][32] (NTd = ceil(d/256); tile row r of N-tile nt is output
+    row min(nt * 256 + r, d - 1); slice s holds inputs 32s .. 32s+31), then, 256-byte
+    aligned, the shared expert's W_d as [NTd][shared_ff/32][256][32]."""
+    d = L["d"]
+    ntd = -(-d // 256)
+    n = np.minimum(np.arange(ntd)[:, None] * 256 + np.arange(256)[None, :], d - 1)   # [NTd, 256]
+
+    def part(w):  # w [E, d, K] -> [E, NTd, K/32, 256, 32]
+        E, _, K = w.shape
+        return w.reshape(E, d, K // 32, 32)[:, n].transpose(0, 1, 3, 2, 4)
+
+    routed = np.ascontiguousarray(part(L["w_down"])).reshape(-1)
+    out = [(0, routed)]
+    if L["shared_ff"]:
+        out.append((-(-routed.size * 2 // 256) * 256 // 2, np.ascontiguousarray(part(L["ws_down"][None])).reshape(-1)))
+    total = out[-1][0] + out[-1][1].size
+    return out, total
+
+
+DENSE_PACK = [("qwen", dict(d=512, n_expert=64, ff=192, shared_ff=128)),
+              ("gptoss", dict(d=320, n_expert=16, ff=192)),
+              ("mixtral", dict(d=512, ff=1024))]
+
+
+@pytest.mark.parametrize("name,ov", DENSE_PACK, ids=["qwen", "gptoss_d320", "mixtral"])
+def test_dense_grouped_pack_layout(name, ov):
+    # Byte for byte the layout above (d = 320 leaves a partial N-tile).
+    say("dense grouped pack layout", name, ov)
+    L, _ = case(name, 1, **ov)
+    lay = dev_layer(name, **ov).with_grouped_pack()
+    torch.cuda.synchronize()
+    got = lay.tensors["grouped_pack"].view(torch.int16).cpu().numpy().view(np.uint16)
+    regions, total = dense_pack_expected(L)
+    assert got.size == total
+    for off, want in regions:
+        assert np.array_equal(got[off:off + want.size], want), off
+
+
+@pytest.mark.parametrize("T", [7, 100, 300])
+@pytest.mark.parametrize("name,ov", DENSE_PACK, ids=["qwen", "gptoss_d320", "mixtral"])
+def test_dense_grouped_pack_forward(name, ov, T):
+    # The grouped path (forced; T = 7 takes split-K down tiles) on the grouped copy: bit for
+    # bit the output of the weights in place, and within tolerance of the oracle; and the
+    # expert stage's fp32 rows (the other down-kernel instance) bit for bit too.
+    say("dense grouped forward, grouped copy", name, ov, T)
+    L, x = case(name, T, **ov)
+    lay = dev_layer(name, **ov).with_path("grouped")
+    pk = lay.with_grouped_pack()
+    y0 = moe_mod().forward(lay, xdev(x))
+    y1 = moe_mod().forward(pk, xdev(x))
+    idx, _, _ = moe_mod().route(lay, xdev(x))
+    off, pt, _ = moe_mod().permute(idx, L["n_expert"])
+    r0 = moe_mod().expert_ffn(lay, xdev(x), off, pt)
+    r1 = moe_mod().expert_ffn(pk, xdev(x), off, pt)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert torch.equal(r0, r1)
+    assert_close(to_numpy_y(y1), oracle.moe_forward(L, x), "bf16", "y")
+
+
+@pytest.mark.parametrize("name,T", [("gptoss", 4096), ("mixtral", 16384)])
+def test_full_dense_grouped_pack(name, T):
+    # The full layers as benchmarked: with the grouped copy, bit for bit the output of the
+    # weights in place (which test_full_other_layers checks against the oracle).
+    say("full dense grouped copy", name, T)
+    L, x = case(name, T)
+    lay = dev_layer(name)
+    y0 = moe_mod().forward(lay, xdev(x))
+    y1 = moe_mod().forward(lay.with_grouped_pack(), xdev(x))
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
 
 
 # ----------------------------------------------------------------------------- MXFP4 experts
