@@ -151,7 +151,11 @@ __device__ __forceinline__ LoadPlan<KW> make_plan(RowA row_a, RowB row_b) {
 }
 
 // The direct loads of one K-slice (from src[j] + k0) into ring stage (a_stage, b_stage).
-template <int KW>
+// NTB: the weight (B) loads are non-temporal -- for launches whose every weight slice is read
+// by one block only (batches of at most 128 tokens: no group has a second M-tile), where the
+// streaming loads reach a higher HBM rate; with several M-tiles per expert they would evict
+// the slices the later M-tiles re-read from L2.
+template <int KW, bool NTB = false>
 __device__ __forceinline__ void issue_stage(uint16_t* a_stage, uint16_t* b_stage, const uint16_t* const* src, int k0) {
     using R = Ring<KW>;
     const int wave = threadIdx.x / kWave;
@@ -160,17 +164,18 @@ __device__ __forceinline__ void issue_stage(uint16_t* a_stage, uint16_t* b_stage
         const bool is_a = j < R::kLoadsA;
         const int seg = wave + 8 * (is_a ? j : j - R::kLoadsA);
         uint16_t* dst = is_a ? a_stage + seg * 512 : b_stage + seg * 512;  // 1 KB
-        __builtin_amdgcn_global_load_lds(src[j] + k0, (lds_ptr_t)dst, 16, 0, 0);
+        if (NTB && !is_a) __builtin_amdgcn_global_load_lds(src[j] + k0, (lds_ptr_t)dst, 16, 0, 2);  // nt
+        else __builtin_amdgcn_global_load_lds(src[j] + k0, (lds_ptr_t)dst, 16, 0, 0);
     }
 }
 
-template <int KW>
+template <int KW, bool NTB = false>
 __device__ __forceinline__ void issue_slice(GSmem<KW>& sm, const LoadPlan<KW>& p, int stage, int k0) {
     const uint16_t* srcs[Ring<KW>::kLoads];
 #pragma unroll
     for (int j = 0; j < Ring<KW>::kLoads; ++j)
         srcs[j] = p.src[j] + (size_t)k0 * (j < Ring<KW>::kLoadsA ? p.mul_a : p.mul_b);
-    issue_stage<KW>(sm.k.a[stage], sm.k.b[stage], srcs, 0);
+    issue_stage<KW, NTB>(sm.k.a[stage], sm.k.b[stage], srcs, 0);
 }
 
 // The A segments of a slice only (B comes through registers): n 1 KB segments of this
@@ -216,12 +221,12 @@ __device__ __forceinline__ void mfma_frags(const Frags& f, floatx4 (&acc)[4][4])
 // a probe of this loop (L2-resident operands): the fragment reads start right after the
 // barrier instead of queueing behind the direct loads' LDS writes.  Ends with all loads
 // drained and a barrier, so the caller may reuse the LDS.
-template <int KW>
+template <int KW, bool NTB = false>
 __device__ __forceinline__ void grouped_mainloop_plain(GSmem<KW>& sm, const LoadPlan<KW>& p, int K, int arow0,
                                                        const int (&brow)[4], floatx4 (&acc)[4][4]) {
     const int nk = K / KW;
-    issue_slice(sm, p, 0, 0);
-    issue_slice(sm, p, 1, min(1, nk - 1) * KW);
+    issue_slice<KW, NTB>(sm, p, 0, 0);
+    issue_slice<KW, NTB>(sm, p, 1, min(1, nk - 1) * KW);
     int st = 0;
     for (int kt = 0; kt < nk; ++kt) {
         wait_vm_lgkm<Ring<KW>::kLoads>();
@@ -229,7 +234,7 @@ __device__ __forceinline__ void grouped_mainloop_plain(GSmem<KW>& sm, const Load
 #pragma unroll
         for (int kc = 0; kc < KW / 8; kc += 4) mfma_k32<KW>(sm.k.a[st], sm.k.b[st], arow0, brow, kc, acc);
         const int pre = st == 0 ? 2 : st - 1;  // (kt + 2) % 3
-        issue_slice(sm, p, pre, min(kt + 2, nk - 1) * KW);
+        issue_slice<KW, NTB>(sm, p, pre, min(kt + 2, nk - 1) * KW);
         st = st == 2 ? 0 : st + 1;
     }
     wait_vm_lgkm<0>();
@@ -264,7 +269,7 @@ __device__ __forceinline__ void mfma_half(const bf16x8 (&a)[2], const bf16x8 (&b
 }
 
 // Step kt of a 32-wide loop: B fragments of slice kt in bc, those of slice kt+1 go to bn.
-template <int KW, int MI = 4>
+template <int KW, int MI = 4, bool NTB = false>
 __device__ __forceinline__ void half_step(GSmem<KW>& sm, const LoadPlan<KW>& p, int kt, int nk, int& st, int arow0,
                                           const int (&brow)[4], HalfFrags& h, bf16x8 (&bc)[4], bf16x8 (&bn)[4],
                                           floatx4 (&acc)[4][4]) {
@@ -280,7 +285,7 @@ __device__ __forceinline__ void half_step(GSmem<KW>& sm, const LoadPlan<KW>& p, 
     const int nx = st == 2 ? 0 : st + 1;
     read_half_lo<KW, MI>(sm, nx, arow0, brow, h, bn);
     if constexpr (MI == 4) mfma_half(h.hi, bc, acc, 2);
-    issue_slice(sm, p, st, min(kt + 3, nk - 1) * KW);
+    issue_slice<KW, NTB>(sm, p, st, min(kt + 3, nk - 1) * KW);
     st = nx;
 }
 
@@ -294,21 +299,21 @@ __device__ __forceinline__ void half_step(GSmem<KW>& sm, const LoadPlan<KW>& p, 
 // overwritten (by slice kt + 3) only after the barrier that follows every wave's last read
 // of it; the slices stay two ahead.  Each accumulator still takes the slices, and the halves
 // of a slice, in K order, so the sums are those of grouped_mainloop_plain.
-template <int KW, int MI = 4>
+template <int KW, int MI = 4, bool NTB = false>
 __device__ __forceinline__ void grouped_mainloop(GSmem<KW>& sm, const LoadPlan<KW>& p, int K, int arow0,
                                                  const int (&brow)[4], floatx4 (&acc)[4][4]) {
     static_assert(KW == 32 || KW == 64, "slice width");
     constexpr int NL = Ring<KW>::kLoads;
     const int nk = K / KW;
-    issue_slice(sm, p, 0, 0);
-    issue_slice(sm, p, 1, min(1, nk - 1) * KW);
+    issue_slice<KW, NTB>(sm, p, 0, 0);
+    issue_slice<KW, NTB>(sm, p, 1, min(1, nk - 1) * KW);
     wait_vm_lgkm<NL>();
     lds_barrier();
     int st = 0;
     if constexpr (KW == 64) {
         Frags f0, f1;
         read_frags<KW, MI>(sm.k.a[0], sm.k.b[0], arow0, brow, 0, f0);
-        issue_slice(sm, p, 2, min(2, nk - 1) * KW);
+        issue_slice<KW, NTB>(sm, p, 2, min(2, nk - 1) * KW);
         for (int kt = 0; kt < nk; ++kt) {
             read_frags<KW, MI>(sm.k.a[st], sm.k.b[st], arow0, brow, 4, f1);
             mfma_frags<MI>(f0, acc);
@@ -317,20 +322,20 @@ __device__ __forceinline__ void grouped_mainloop(GSmem<KW>& sm, const LoadPlan<K
             const int nx = st == 2 ? 0 : st + 1;  // (kt + 1) % 3; past the last slice, a clamped re-load
             read_frags<KW, MI>(sm.k.a[nx], sm.k.b[nx], arow0, brow, 0, f0);
             mfma_frags<MI>(f1, acc);
-            issue_slice(sm, p, st, min(kt + 3, nk - 1) * KW);
+            issue_slice<KW, NTB>(sm, p, st, min(kt + 3, nk - 1) * KW);
             st = nx;
         }
     } else {
         static_assert(MI == 0 || MI == 2 || MI == 4, "32-wide slices skip whole 32-row halves");
         HalfFrags h;
         read_half_lo<KW, MI>(sm, 0, arow0, brow, h, h.b0);
-        issue_slice(sm, p, 2, min(2, nk - 1) * KW);
+        issue_slice<KW, NTB>(sm, p, 2, min(2, nk - 1) * KW);
         int kt = 0;
         for (; kt + 1 < nk; kt += 2) {
-            half_step<KW, MI>(sm, p, kt, nk, st, arow0, brow, h, h.b0, h.b1, acc);
-            half_step<KW, MI>(sm, p, kt + 1, nk, st, arow0, brow, h, h.b1, h.b0, acc);
+            half_step<KW, MI, NTB>(sm, p, kt, nk, st, arow0, brow, h, h.b0, h.b1, acc);
+            half_step<KW, MI, NTB>(sm, p, kt + 1, nk, st, arow0, brow, h, h.b1, h.b0, acc);
         }
-        if (kt < nk) half_step<KW, MI>(sm, p, kt, nk, st, arow0, brow, h, h.b0, h.b1, acc);
+        if (kt < nk) half_step<KW, MI, NTB>(sm, p, kt, nk, st, arow0, brow, h, h.b0, h.b1, acc);
     }
     wait_vm_lgkm<0>();
     __syncthreads();
@@ -686,7 +691,7 @@ __device__ __forceinline__ void down_regb(GSmem<kDownKW>& sm, const LoadPlan<kDo
 // WF: storage of the routed gate/up weights.  kWMx: MXFP4 gate_up blocks (a.mx_w, a.mx_s;
 // clamped variant, no shared expert).  kWQ4k: Q4_K w_gate / w_up super-blocks (SwiGLU);
 // the shared expert's tiles stay on the bf16 direct loads.
-template <bool OAI, int WF>
+template <bool OAI, int WF, bool NTB>
 __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kernel(UpArgs a) {
     __shared__ GSmem<kUpKW> sm;
     Group g;
@@ -754,16 +759,16 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kerne
             regb_live<kUpKW>(sm, plan, src, a.d, up_live(g, m0, wm), wm * 64, brow, acc);
         } else {
             const LoadPlan<kUpKW> plan = make_plan<kUpKW, false>(row_a, row_b);
-            grouped_mainloop(sm, plan, a.d, wm * 64, brow, acc);
+            grouped_mainloop<kUpKW, 4, NTB>(sm, plan, a.d, wm * 64, brow, acc);
         }
     } else {
         const LoadPlan<kUpKW> plan = make_plan<kUpKW, false>(row_a, row_b);
         switch (up_live(g, m0, wm)) {
-            case 4: grouped_mainloop<kUpKW, 4>(sm, plan, a.d, wm * 64, brow, acc); break;
-            case 3: grouped_mainloop<kUpKW, 3>(sm, plan, a.d, wm * 64, brow, acc); break;
-            case 2: grouped_mainloop<kUpKW, 2>(sm, plan, a.d, wm * 64, brow, acc); break;
-            case 1: grouped_mainloop<kUpKW, 1>(sm, plan, a.d, wm * 64, brow, acc); break;
-            default: grouped_mainloop<kUpKW, 0>(sm, plan, a.d, wm * 64, brow, acc); break;
+            case 4: grouped_mainloop<kUpKW, 4, NTB>(sm, plan, a.d, wm * 64, brow, acc); break;
+            case 3: grouped_mainloop<kUpKW, 3, NTB>(sm, plan, a.d, wm * 64, brow, acc); break;
+            case 2: grouped_mainloop<kUpKW, 2, NTB>(sm, plan, a.d, wm * 64, brow, acc); break;
+            case 1: grouped_mainloop<kUpKW, 1, NTB>(sm, plan, a.d, wm * 64, brow, acc); break;
+            default: grouped_mainloop<kUpKW, 0, NTB>(sm, plan, a.d, wm * 64, brow, acc); break;
         }
     }
 
@@ -816,7 +821,7 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kUpKW>()) void gg_up_kerne
 // plane ks of y; splitk_reduce_kernel adds the planes, the bias and the routing weight.
 // WF: storage of the routed down weights (kWMx: MXFP4 blocks a.mx_w, a.mx_s; kWQ4k: Q4_K
 // super-blocks a.q4_down, the shared expert's tiles on the bf16 direct loads).
-template <typename TY, int WF>
+template <typename TY, int WF, bool NTB>
 __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_kernel(DownArgs a) {
     __shared__ GSmem<kDownKW> sm;
     Group g;
@@ -886,7 +891,7 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
         } else {  // the plain loop: the second set of B registers would cost this kernel occupancy
             LoadPlan<kDownKW> plan = make_plan<kDownKW, false>(row_a, row_b);
             plan.mul_a = a.rows;
-            grouped_mainloop_plain(sm, plan, K, wm * 64, brow, acc);
+            grouped_mainloop_plain<kDownKW, NTB>(sm, plan, K, wm * 64, brow, acc);
         }
     } else {
         // As in the up kernel, padding rows past the group's last row run no MFMAs, here by
@@ -897,11 +902,11 @@ __global__ __launch_bounds__(kGThreads, blocks_per_cu<kDownKW>()) void gg_down_k
         plan.mul_b = wpack ? GBN : 1;
         if constexpr (sizeof(TY) == 2) {
             const int live = up_live(g, m0, wm);
-            if (live > 2) grouped_mainloop<kDownKW, 4>(sm, plan, K, wm * 64, brow, acc);
-            else if (live > 0) grouped_mainloop<kDownKW, 2>(sm, plan, K, wm * 64, brow, acc);
-            else grouped_mainloop<kDownKW, 0>(sm, plan, K, wm * 64, brow, acc);
+            if (live > 2) grouped_mainloop<kDownKW, 4, NTB>(sm, plan, K, wm * 64, brow, acc);
+            else if (live > 0) grouped_mainloop<kDownKW, 2, NTB>(sm, plan, K, wm * 64, brow, acc);
+            else grouped_mainloop<kDownKW, 0, NTB>(sm, plan, K, wm * 64, brow, acc);
         } else {
-            grouped_mainloop(sm, plan, K, wm * 64, brow, acc);
+            grouped_mainloop<kDownKW, 4, NTB>(sm, plan, K, wm * 64, brow, acc);
         }
     }
 
@@ -1375,14 +1380,18 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
     u.q4_packed = q4 && packed ? 1 : 0;
     u.h_rows = T * L.k + (shared ? T : 0);
     const dim3 gu((unsigned)grid_blocks(mt, nn_up));
-    if (mx)
-        gg_up_kernel<true, kWMx><<<gu, kGThreads, 0, s>>>(u);
-    else if (q4)
-        gg_up_kernel<false, kWQ4k><<<gu, kGThreads, 0, s>>>(u);
-    else if (L.act == MOE_ACT_SWIGLU_OAI)
-        gg_up_kernel<true, kWDense><<<gu, kGThreads, 0, s>>>(u);
-    else
-        gg_up_kernel<false, kWDense><<<gu, kGThreads, 0, s>>>(u);
+    // A group holds at most T rows: up to 128 tokens every weight slice is read by one block.
+    const bool ntb = T <= BM;
+#define SMOE_GG_UP(OAI, WF)                                                          \
+    do {                                                                             \
+        if (ntb) gg_up_kernel<OAI, WF, true><<<gu, kGThreads, 0, s>>>(u);            \
+        else gg_up_kernel<OAI, WF, false><<<gu, kGThreads, 0, s>>>(u);               \
+    } while (0)
+    if (mx) SMOE_GG_UP(true, kWMx);
+    else if (q4) SMOE_GG_UP(false, kWQ4k);
+    else if (L.act == MOE_ACT_SWIGLU_OAI) SMOE_GG_UP(true, kWDense);
+    else SMOE_GG_UP(false, kWDense);
+#undef SMOE_GG_UP
     const uint8_t* mx_dw = mx_packed ? pack + pk.dn_codes : mx ? static_cast<const uint8_t*>(L.w_down) : nullptr;
     const uint8_t* mx_ds = mx_packed ? pack + pk.dn_scales : mx ? L.w_down_scales : nullptr;
     const int nn = (L.d + GBN - 1) / GBN;
@@ -1399,9 +1408,15 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
                     static_cast<const uint16_t*>(L.ws_down), mx_dw, mx_ds, q4_down, nullptr, partial, hstride, L.d,
                     L.ff, L.shared_ff, nn, ksplit, rows, (mx || q4) && packed ? 1 : 0, wd_pack, wsd_pack};
         const dim3 gs((unsigned)grid_blocks(mt, nn * ksplit));
-        if (wf == kWMx) gg_down_kernel<float, kWMx><<<gs, kGThreads, 0, s>>>(dn);
-        else if (wf == kWQ4k) gg_down_kernel<float, kWQ4k><<<gs, kGThreads, 0, s>>>(dn);
-        else gg_down_kernel<float, kWDense><<<gs, kGThreads, 0, s>>>(dn);
+#define SMOE_GG_SPLIT(WF)                                                            \
+    do {                                                                             \
+        if (ntb) gg_down_kernel<float, WF, true><<<gs, kGThreads, 0, s>>>(dn);       \
+        else gg_down_kernel<float, WF, false><<<gs, kGThreads, 0, s>>>(dn);          \
+    } while (0)
+        if (wf == kWMx) SMOE_GG_SPLIT(kWMx);
+        else if (wf == kWQ4k) SMOE_GG_SPLIT(kWQ4k);
+        else SMOE_GG_SPLIT(kWDense);
+#undef SMOE_GG_SPLIT
         const dim3 gr((unsigned)((L.d + 1023) / 1024), (unsigned)mt, (unsigned)min(BM, T * L.k));
         if (y_bf16)
             splitk_reduce_kernel<uint16_t><<<gr, 256, 0, s>>>(partial, ksplit, rows, meta, tiles, b_down, row_w,
@@ -1417,8 +1432,10 @@ hipError_t launch_grouped_ffn(const moe_layer& L, const void* x, int T, const in
     const dim3 gd((unsigned)grid_blocks(mt, nn));
 #define SMOE_GG_DOWN(WF)                                                              \
     do {                                                                              \
-        if (y_bf16) gg_down_kernel<uint16_t, WF><<<gd, kGThreads, 0, s>>>(dn);        \
-        else gg_down_kernel<float, WF><<<gd, kGThreads, 0, s>>>(dn);                  \
+        if (y_bf16 && ntb) gg_down_kernel<uint16_t, WF, true><<<gd, kGThreads, 0, s>>>(dn);   \
+        else if (y_bf16) gg_down_kernel<uint16_t, WF, false><<<gd, kGThreads, 0, s>>>(dn);    \
+        else if (ntb) gg_down_kernel<float, WF, true><<<gd, kGThreads, 0, s>>>(dn);           \
+        else gg_down_kernel<float, WF, false><<<gd, kGThreads, 0, s>>>(dn);                   \
     } while (0)
     if (wf == kWMx) SMOE_GG_DOWN(kWMx);
     else if (wf == kWQ4k) SMOE_GG_DOWN(kWQ4k);
