@@ -72,9 +72,10 @@ enum { MOE_ROUTE_SOFTMAX_TOPK_RENORM = 0, MOE_ROUTE_TOPK_SOFTMAX = 1 };
 enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 };
 
 /* Kernel path.  AUTO: the grouped MFMA path for T > 64, and also for smaller batches
- * (bf16) whose expected rows per active expert reach 4, taking E * (1 - (1 - k/E)^T)
- * distinct experts as for uniform routing; else the decode GEMV path.  DECODE / GROUPED
- * force one path at any T (GROUPED requires MOE_BF16). */
+ * (bf16) whose expected rows per active expert reach 4 (2 for dense experts whose gate and
+ * up weights take 16 MB or more), taking E * (1 - (1 - k/E)^T) distinct experts as for
+ * uniform routing; else the decode GEMV path.  DECODE / GROUPED force one path at any T
+ * (GROUPED requires MOE_BF16). */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_GROUPED = 2 };
 
 /* Storage of the routed experts' gate_up and down weights.

@@ -18,6 +18,12 @@ constexpr int kDecodeMaxT = 64;  // MOE_PATH_AUTO takes the grouped path above t
 // ... and at or below it when the expected rows per active expert reach this many: the
 // GEMVs' per-row arithmetic then outgrows their weight stream, MFMA tiles do not.
 constexpr double kGroupedMinRows = 4.0;
+// Dense experts whose gate/up weights reach 16 MB take the grouped path from 2 expected rows
+// per active expert: each expert's tiles then run long enough that streaming its weights once
+// per N-tile beats once per row pair (Mixtral-shaped T=8 546 -> 435 us, gpt-oss-shaped T=16
+// 274 -> 259 us; the Qwen-shaped layer's 4 MB experts at T=64 stay faster on the GEMVs).
+constexpr double kGroupedMinRowsWide = 2.0;
+constexpr double kWideExpertBytes = 16.0 * (1 << 20);
 // Split-K of the grouped down projection at decode-sized batches: at most this many K
 // slices per tile, chosen to bring the expected down blocks up to two per CU (256 CUs).
 constexpr int kMaxKSplit = 4;
@@ -153,7 +159,9 @@ bool use_grouped(const moe_layer& L, int T) {
     if (L.path == MOE_PATH_GROUPED) return true;
     if (L.path != MOE_PATH_AUTO) return false;
     if (T > kDecodeMaxT) return true;
-    return (double)T * L.k >= kGroupedMinRows * expected_active(L.n_expert, L.k, T);
+    const double rows = (double)T * L.k / expected_active(L.n_expert, L.k, T);
+    const bool wide = L.expert_format == MOE_EXPERTS_DENSE && 2.0 * L.ff * L.d * 2 >= kWideExpertBytes;
+    return rows >= (wide ? kGroupedMinRowsWide : kGroupedMinRows);
 }
 
 // Large bf16 batches compute the router logits on MFMA (experts only; top-k then forms
