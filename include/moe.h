@@ -71,7 +71,8 @@ enum { MOE_ROUTE_SOFTMAX_TOPK_RENORM = 0, MOE_ROUTE_TOPK_SOFTMAX = 1 };
  *    y = W_d h + b_d (the down bias is inside the routing-weighted sum). */
 enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLU_OAI = 1 };
 
-/* Kernel path.  AUTO: the grouped MFMA path for T > 64, and also for smaller batches
+/* Kernel path.  AUTO: the grouped MFMA path for T > 64 (Q4K experts: T > 128, or from 65
+ * tokens once the expected rows per active expert reach 8), and also for smaller batches
  * (bf16) whose expected rows per active expert reach 4 (2 for dense experts whose gate and
  * up weights take 16 MB or more), taking E * (1 - (1 - k/E)^T) distinct experts as for
  * uniform routing; else the decode GEMV path.  DECODE / GROUPED force one path at any T

@@ -24,6 +24,12 @@ constexpr double kGroupedMinRows = 4.0;
 // 274 -> 259 us; the Qwen-shaped layer's 4 MB experts at T=64 stay faster on the GEMVs).
 constexpr double kGroupedMinRowsWide = 2.0;
 constexpr double kWideExpertBytes = 16.0 * (1 << 20);
+// Q4_K experts keep the GEMVs up to this many tokens while the expected rows per active expert
+// stay below 8: the GEMVs decode each quant once per step, the grouped kernels expand every
+// weight of a tile into LDS (Qwen-shaped: T=96 209 vs 260 us, T=128 244 vs 264 us; grouped
+// faster from T=192, 304 vs 315 us).
+constexpr int kDecodeMaxTQ4k = 128;
+constexpr double kQ4kGroupedMinRows = 8.0;
 // Split-K of the grouped down projection at decode-sized batches: at most this many K
 // slices per tile, chosen to bring the expected down blocks up to two per CU (256 CUs).
 constexpr int kMaxKSplit = 4;
@@ -158,8 +164,9 @@ bool use_grouped(const moe_layer& L, int T) {
     if (L.dtype != MOE_BF16) return false;
     if (L.path == MOE_PATH_GROUPED) return true;
     if (L.path != MOE_PATH_AUTO) return false;
-    if (T > kDecodeMaxT) return true;
     const double rows = (double)T * L.k / expected_active(L.n_expert, L.k, T);
+    if (T > kDecodeMaxT)
+        return !(L.expert_format == MOE_EXPERTS_Q4K && T <= kDecodeMaxTQ4k && rows < kQ4kGroupedMinRows);
     const bool wide = L.expert_format == MOE_EXPERTS_DENSE && 2.0 * L.ff * L.d * 2 >= kWideExpertBytes;
     return rows >= (wide ? kGroupedMinRowsWide : kGroupedMinRows);
 }
